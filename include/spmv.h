@@ -1,0 +1,200 @@
+/*
+ * spmv.h -- C ABI of libspmv.so: load-balanced CSR sparse matrix-vector
+ * multiplication y = alpha*A*x + beta*y on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operation (the pages this library is written from):
+ *  - CSR storage: "New Row-grouped CSR format for storing the sparse matrices
+ *    on GPU with implementation in CUDA" (arXiv 1012.2270), Section 3 and its
+ *    Fig. 1: row pointers with M+1 entries whose last entry is nnz; values and
+ *    column indices with nnz entries each, stored row after row; 32-bit
+ *    integer indices (its peak-performance estimate, Table 1).
+ *  - The product itself: the same page, Section 3 (sequential CSR loop), and
+ *    "A Programming Model for GPU Load Balancing" (Osama, Porumbescu, Owens,
+ *    PPoPP'23), Section 4.3, Listing 3 (sum of a row's atoms, then y[row]).
+ *  - The alpha/beta form: "Accelerating Sparse Approximate Matrix
+ *    Multiplication on GPUs" (arXiv 2103.13042), background section, which
+ *    states its product in the BLAS form C = alpha*A*B + beta*C.
+ *  - Load balance: the PPoPP'23 page, Section 5.2.1 (merge-path: every row
+ *    and every nonzero is one unit of work; the units are split evenly and
+ *    each worker finds its start by a 2-D binary search) and Sidebar 1 (the
+ *    segmented fix-up of rows split between workers); Sections 5.2.2 and 4.2
+ *    (warp/block-mapped and thread-mapped schedules); and "OpSparse: a Highly
+ *    Optimized Framework for Sparse General Matrix Multiplication on GPUs"
+ *    (arXiv 2206.07244), Section 5.1 (two-pass binning with shared-memory
+ *    counters, exclusive sum, and the all-rows-in-one-bin fast path) and its
+ *    advice to allocate all metadata with one allocation.
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer named "device" is a device (HBM) pointer owned by the
+ *    caller; every pointer named "host" is ordinary host memory.
+ *  - Indices are 0-based int32. Values and vectors are fp32 or fp64
+ *    (all of one plan use the same dtype).
+ *  - No function throws; each returns an spmv_status_t. On failure nothing
+ *    stays allocated and *out handles are set to NULL. spmv_last_error()
+ *    gives a thread-local text with the detail of the last failure.
+ *  - beta == 0 means y is write-only: it is never read, so it may hold NaN.
+ *  - Nothing here allocates after spmv_plan returns, except spmv_plan_* calls
+ *    that are documented as copying to host.
+ */
+#ifndef SPMV_H_
+#define SPMV_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spmv_status {
+  SPMV_SUCCESS = 0,
+  SPMV_ERR_INVALID_ARG = 1,    /* null/aliased pointer, negative size, bad enum */
+  SPMV_ERR_UNSUPPORTED = 2,    /* sizes beyond the int32 item model, see spmv_plan */
+  SPMV_ERR_ALLOC = 3,          /* the one workspace hipMalloc failed */
+  SPMV_ERR_HIP = 4,            /* a HIP launch or runtime call failed */
+  SPMV_ERR_INVALID_PLAN = 5,   /* NULL, destroyed or foreign handle */
+  SPMV_ERR_INVALID_MATRIX = 6  /* row_ptr (or, when validated, col_idx) malformed */
+} spmv_status_t;
+
+typedef enum spmv_dtype { SPMV_F32 = 0, SPMV_F64 = 1 } spmv_dtype_t;
+
+/* Execution schedules.
+ *  MERGE : merge-path over the M + nnz work items (PPoPP'23 page, Sec. 5.2.1),
+ *          one partition of T items per 64-lane wavefront, plus a carry fix-up.
+ *  BINNED: rows grouped into row-length bins (OpSparse, Sec. 5.1); each bin
+ *          runs a thread-, lane-group-, wavefront- or workgroup-per-row variant
+ *          (PPoPP'23 page, Secs. 4.2 and 5.2.2), longest bins dispatched first.
+ *  AUTO  : the planner picks one of the two from the row-length statistics. */
+typedef enum spmv_strategy {
+  SPMV_STRATEGY_AUTO = 0,
+  SPMV_STRATEGY_MERGE = 1,
+  SPMV_STRATEGY_BINNED = 2
+} spmv_strategy_t;
+
+#define SPMV_MAX_BINS 8
+
+typedef struct spmv_plan_st* spmv_plan_t;
+
+/* Optional planning parameters (spmv_plan_ex). Zero-initialise and set only
+ * what you need; a zero field means "library default". Results never depend
+ * on these values, only speed does. */
+typedef struct spmv_plan_options {
+  int32_t strategy;           /* spmv_strategy_t; 0 = AUTO (env SPMV_STRATEGY
+                                 = auto|merge|binned overrides AUTO) */
+  int32_t items_per_thread;   /* merge-path items per lane: 4, 8 or 16;
+                                 T = 64 * items_per_thread items per wavefront */
+  int32_t n_bins;             /* 1..SPMV_MAX_BINS; 0 = default bins */
+  int32_t validate_columns;   /* 1: also check 0 <= col_idx < N at plan time
+                                 (one pass over col_idx); env SPMV_VALIDATE=1 */
+  int64_t bin_max_len[SPMV_MAX_BINS];
+                              /* inclusive upper row length of bins 0..n_bins-2,
+                                 strictly increasing; the last bin is unbounded */
+  int32_t bin_lanes[SPMV_MAX_BINS];
+                              /* lanes per row of each bin: 1,2,4,...,64, or 256
+                                 (one 256-thread workgroup per row) */
+} spmv_plan_options_t;
+
+typedef struct spmv_plan_info {
+  int64_t M, N, nnz;
+  int32_t dtype;              /* spmv_dtype_t */
+  int32_t strategy;           /* the schedule spmv_exec runs (never AUTO) */
+  int32_t items_per_thread;
+  int32_t items_per_wave;     /* T */
+  int64_t n_partitions;       /* P = ceil((M + nnz) / T) */
+  int32_t n_bins;
+  int32_t bin_identity;       /* 1: every row fell in one bin, no row-id array */
+  int64_t bin_max_len[SPMV_MAX_BINS];
+  int32_t bin_lanes[SPMV_MAX_BINS];
+  int64_t bin_count[SPMV_MAX_BINS];
+  int64_t max_row_len;
+  int64_t n_empty_rows;
+  int64_t workspace_bytes;    /* size of the plan's single device allocation */
+} spmv_plan_info_t;
+
+/* Build a plan for the CSR matrix A (M x N, nnz stored entries).
+ *
+ * row_ptr  device int32[M+1]; row_ptr[0] == 0, non-decreasing,
+ *          row_ptr[M] == nnz (RgCSR page, Sec. 3). Checked on the device;
+ *          a violation returns SPMV_ERR_INVALID_MATRIX.
+ * col_idx  device int32[nnz], each in [0, N). Any order within a row;
+ *          repeated columns add up. Checked only with validate_columns.
+ * values   device fp32[nnz] or fp64[nnz] per dtype.
+ * stream   the HIP stream the planning kernels run on (0 = null stream).
+ *
+ * Ownership: the plan borrows row_ptr, col_idx and values; they must stay
+ * allocated until spmv_destroy, and row_ptr must stay unchanged (the plan's
+ * partition and bins are derived from it). col_idx and values may change
+ * between spmv_exec calls. The plan owns exactly one device allocation, made
+ * here and freed by spmv_destroy.
+ *
+ * Work: row-length statistics and per-workgroup bin counts kept in LDS, an
+ * exclusive scan of the bin counts, a stable scatter of row ids into bins,
+ * and one merge-path binary search per wavefront partition; then one
+ * device-to-host copy of a small statistics block and one stream
+ * synchronisation. Returns SPMV_ERR_UNSUPPORTED if M + nnz > 2^31 - 1.
+ * M == 0 or nnz == 0 is allowed. */
+spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                        const int32_t* row_ptr, const int32_t* col_idx,
+                        const void* values, spmv_dtype_t dtype,
+                        hipStream_t stream);
+
+/* spmv_plan with explicit options (NULL = defaults). */
+spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const void* values, spmv_dtype_t dtype,
+                           const spmv_plan_options_t* options,
+                           hipStream_t stream);
+
+/* y = alpha * A * x + beta * y.
+ *
+ * x  device array of N elements of the plan's dtype.
+ * y  device array of M elements; read only when beta != 0. Must not alias x.
+ * alpha, beta are converted once to the plan's dtype.
+ *
+ * Asynchronous: only enqueues kernels on stream; never allocates, frees or
+ * synchronises. Rows with no entries give exactly beta*y (0 when beta == 0).
+ * For a fixed plan the result is bitwise reproducible (no float atomics).
+ * One plan must not run concurrently on two streams (its carry buffer is
+ * per plan); distinct plans are independent. */
+spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
+                        double alpha, double beta, hipStream_t stream);
+
+/* spmv_exec that also records ev_begin just before and ev_end just after the
+ * dominant kernel (the merge-path main kernel or the fused binned kernel), on
+ * the same stream, so a caller can time that kernel alone. Either event may
+ * be NULL. */
+spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y,
+                               double alpha, double beta, hipStream_t stream,
+                               hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* Release the plan's workspace (hipFree, which synchronises the device).
+ * NULL is a no-op; a destroyed or foreign handle gives SPMV_ERR_INVALID_PLAN
+ * as long as its memory has not been reused. */
+spmv_status_t spmv_destroy(spmv_plan_t plan);
+
+/* Switch a live plan between MERGE and BINNED (both are always built). */
+spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
+
+/* Fill *info (host struct). */
+spmv_status_t spmv_plan_info(spmv_plan_t plan, spmv_plan_info_t* info);
+
+/* Copy the merge-path split coordinates to host arrays of cap >= P+1 entries:
+ * rows_host[p] = rows whose end item precedes diagonal min(p*T, M+nnz),
+ * nnz_host[p] = nonzeros before it. Synchronous (stream-ordered on the null
+ * stream after the plan's work). */
+spmv_status_t spmv_plan_copy_splits(spmv_plan_t plan, int32_t* rows_host,
+                                    int32_t* nnz_host, int64_t cap);
+
+/* Copy the binning result to host: bins_host[M] (row ids grouped by bin,
+ * ascending within a bin; the identity when bin_identity is set) and
+ * offsets_host[n_bins+1]. Synchronous. */
+spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
+                                  int64_t bins_cap, int64_t* offsets_host);
+
+const char* spmv_status_string(spmv_status_t status);
+const char* spmv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPMV_H_ */

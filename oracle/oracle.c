@@ -1,0 +1,195 @@
+/*
+ * oracle.c -- plain, sequential CPU reference for the CSR SpMV path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this code. The product library
+ * (libspmv.so) shares no code, header, table or helper with it.
+ *
+ * Every function is the plain definition written out, in the order the pages
+ * state it, with no blocking, fusion or reordering:
+ *
+ *  oracle_spmv_f32 / _f64 / _rows_*:
+ *      CSR SpMV, "New Row-grouped CSR format for storing the sparse matrices
+ *      on GPU with implementation in CUDA" (arXiv 1012.2270), Section 3: rows
+ *      stored one after another, row r's entries between rowPointers[r] and
+ *      rowPointers[r+1], each entry one multiply and one add into the row's
+ *      sum; "A Programming Model for GPU Load Balancing" (PPoPP'23),
+ *      Section 4.3 Listing 3: sum over the row's atoms, then write y[row].
+ *      The alpha/beta update follows the BLAS form C = alpha*A*B + beta*C
+ *      stated in "Accelerating Sparse Approximate Matrix Multiplication on
+ *      GPUs" (arXiv 2103.13042), background section. The sum runs in fp64,
+ *      sequentially in storage order; fp32 products are exact in fp64.
+ *      Also returned: scale[i] = sum_k |a_ik * x_k|, the magnitude the
+ *      acceptance bound is measured against.
+ *      Pinned by tests/test_oracle.py: dense brute force on tiny matrices,
+ *      identity, diagonal, integer row sums, the 2-D Laplacian closed forms,
+ *      power-of-two linearity, empty rows, and the worked CSR example.
+ *
+ *  oracle_merge_splits:
+ *      merge-path partition, PPoPP'23 page, Section 5.2.1: every nonzero and
+ *      every row counts as one unit of work; units are split evenly. Written
+ *      as a walk over the units in order (row r's nonzeros, then row r's
+ *      end), recording how many row ends and nonzeros precede each multiple
+ *      of T. Pinned by a hand-worked table on the worked CSR example and by
+ *      invariants that hold for any correct split.
+ *
+ *  oracle_bins:
+ *      two-pass binning, "OpSparse" (arXiv 2206.07244), Section 5.1: count
+ *      rows per bin, exclusive sum of the counts, then place row ids. Written
+ *      sequentially (so the order within a bin is ascending). Pinned by
+ *      histogram, permutation and ordering checks against numpy.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+
+/* ---- SpMV: y_ref = alpha * (A x) + beta * y_old, fp64 ------------------- */
+
+static double row_sum_f32(const int32_t* row_ptr, const int32_t* col_idx,
+                          const float* values, const float* x, int64_t i,
+                          double* scale) {
+  double t = 0.0, s = 0.0;
+  for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+    double p = (double)values[k] * (double)x[col_idx[k]];
+    t = t + p;
+    s = s + fabs(p);
+  }
+  *scale = s;
+  return t;
+}
+
+static double row_sum_f64(const int32_t* row_ptr, const int32_t* col_idx,
+                          const double* values, const double* x, int64_t i,
+                          double* scale) {
+  double t = 0.0, s = 0.0;
+  for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+    double p = values[k] * x[col_idx[k]];
+    t = t + p;
+    s = s + fabs(p);
+  }
+  *scale = s;
+  return t;
+}
+
+/* beta == 0 means y_old is not read (it may be NULL). */
+int oracle_spmv_f32(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
+                    const float* values, const float* x, double alpha,
+                    double beta, const float* y_old, double* ref,
+                    double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    double t = row_sum_f32(row_ptr, col_idx, values, x, i, &scale[i]);
+    ref[i] = alpha * t + (beta != 0.0 ? beta * (double)y_old[i] : 0.0);
+  }
+  return 0;
+}
+
+int oracle_spmv_f64(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
+                    const double* values, const double* x, double alpha,
+                    double beta, const double* y_old, double* ref,
+                    double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    double t = row_sum_f64(row_ptr, col_idx, values, x, i, &scale[i]);
+    ref[i] = alpha * t + (beta != 0.0 ? beta * y_old[i] : 0.0);
+  }
+  return 0;
+}
+
+/* The same definition evaluated only on the rows listed in rows[0..n). */
+int oracle_spmv_rows_f32(const int32_t* row_ptr, const int32_t* col_idx,
+                         const float* values, const float* x, double alpha,
+                         double beta, const float* y_old, const int64_t* rows,
+                         int64_t n, double* ref, double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t q = 0; q < n; ++q) {
+    int64_t i = rows[q];
+    double t = row_sum_f32(row_ptr, col_idx, values, x, i, &scale[q]);
+    ref[q] = alpha * t + (beta != 0.0 ? beta * (double)y_old[i] : 0.0);
+  }
+  return 0;
+}
+
+int oracle_spmv_rows_f64(const int32_t* row_ptr, const int32_t* col_idx,
+                         const double* values, const double* x, double alpha,
+                         double beta, const double* y_old, const int64_t* rows,
+                         int64_t n, double* ref, double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t q = 0; q < n; ++q) {
+    int64_t i = rows[q];
+    double t = row_sum_f64(row_ptr, col_idx, values, x, i, &scale[q]);
+    ref[q] = alpha * t + (beta != 0.0 ? beta * y_old[i] : 0.0);
+  }
+  return 0;
+}
+
+/* ---- merge-path split coordinates by walking the work units ------------- */
+
+/* Writes P+1 entries, P = ceil((M + nnz) / T). Entry p holds the number of
+ * row ends (split_row) and nonzeros (split_nz) among the first min(p*T, W)
+ * units, W = M + nnz. Returns P, or -1 on bad arguments. */
+int64_t oracle_merge_splits(int64_t M, int64_t nnz, const int32_t* row_ptr,
+                            int64_t T, int32_t* split_row, int32_t* split_nz) {
+  if (T <= 0 || M < 0 || nnz < 0) return -1;
+  int64_t W = M + nnz;
+  int64_t P = (W + T - 1) / T;
+  int64_t rows_done = 0, nz_done = 0, units = 0, p = 0;
+  split_row[0] = 0;
+  split_nz[0] = 0;
+  p = 1;
+  for (int64_t r = 0; r < M; ++r) {
+    for (int64_t k = row_ptr[r]; k < row_ptr[r + 1]; ++k) {
+      nz_done += 1;                       /* unit: nonzero k of row r */
+      units += 1;
+      if (units == p * T) {
+        split_row[p] = (int32_t)rows_done;
+        split_nz[p] = (int32_t)nz_done;
+        p += 1;
+      }
+    }
+    rows_done += 1;                       /* unit: end of row r */
+    units += 1;
+    if (units == p * T) {
+      split_row[p] = (int32_t)rows_done;
+      split_nz[p] = (int32_t)nz_done;
+      p += 1;
+    }
+  }
+  if (p == P) {                           /* short last partition */
+    split_row[P] = (int32_t)rows_done;
+    split_nz[P] = (int32_t)nz_done;
+  }
+  return P;
+}
+
+/* ---- two-pass binning by row length ------------------------------------ */
+
+/* Bin of a row of length L: the first b < n_bins-1 with L <= max_len[b],
+ * otherwise the last bin. counts[n_bins], offsets[n_bins+1], bins[M]. */
+int oracle_bins(int64_t M, const int32_t* row_ptr, int32_t n_bins,
+                const int64_t* max_len, int64_t* counts, int64_t* offsets,
+                int32_t* bins) {
+  if (n_bins < 1 || n_bins > 64) return -1;
+  for (int32_t b = 0; b < n_bins; ++b) counts[b] = 0;
+  /* pass 1: count rows per bin */
+  for (int64_t r = 0; r < M; ++r) {
+    int64_t L = (int64_t)row_ptr[r + 1] - row_ptr[r];
+    int32_t b = 0;
+    while (b < n_bins - 1 && L > max_len[b]) ++b;
+    counts[b] += 1;
+  }
+  /* exclusive sum of the counts */
+  offsets[0] = 0;
+  for (int32_t b = 0; b < n_bins; ++b) offsets[b + 1] = offsets[b] + counts[b];
+  /* pass 2: place row ids */
+  int64_t fill[64];
+  for (int32_t b = 0; b < n_bins; ++b) fill[b] = offsets[b];
+  for (int64_t r = 0; r < M; ++r) {
+    int64_t L = (int64_t)row_ptr[r + 1] - row_ptr[r];
+    int32_t b = 0;
+    while (b < n_bins - 1 && L > max_len[b]) ++b;
+    bins[fill[b]] = (int32_t)r;
+    fill[b] += 1;
+  }
+  return 0;
+}
