@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSR SpMV hot path on one MI355X.
+
+One step = one spmv_exec (y = alpha*A*x + beta*y, the whole hot path: the
+merge-path kernel and its carry fix-up, or the fused binned kernel) over the
+workload resident in HBM. Before every step a 1 GiB buffer is zero-filled on
+the same stream, which evicts L2 and the 256 MiB Infinity Cache, so every
+step reads the matrix from HBM (``--no-flush`` times warm steps instead).
+Each step's exec is bracketed by HIP events, and the dominant kernel by its
+own pair of HIP events recorded by the library on the same stream.
+
+Prints ONE JSON line. ``value`` is GFLOP/s (2 * nnz per step) over the mean
+event-timed exec duration; ``roofline`` prices the dominant kernel against
+MI355X's 8 TB/s HBM peak with the compulsory bytes (row_ptr, col_idx,
+values, x, y) per launch; ``cpu_baseline`` times the CPU oracle on the host.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "CSR SpMV GFLOP/s and achieved HBM GB/s (% of peak) on 1 MI355X"
+WORKLOADS = {
+    "tiny": "tiny fp32 CSR, 2,000 x 2,000, 5..15 entries per row",
+    "laplacian": "fp64 5-point 2-D Laplacian, 2048 x 2048 grid (4,194,304 rows)",
+    "powerlaw": "fp32 power-law rows (exponent 2.1, 1..100,000), 4,000,000^2, alpha 1.5 beta 0.5",
+    "bimodal": "fp32 bimodal rows, 1,000,000^2: 1,000 x 50,000 + 5% empty + 3 per row",
+    "banded": "fp32 banded decay matrix, 32,000,000 rows, 24..40 entries within |i-j| <= 1000",
+}
+KERNEL_SOURCES = ["merge_kernels.hip", "binned_kernels.hip", "device_common.hpp", "internal.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "load_balanced_csr_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e: int):
+        self.hip.hipEventDestroy(e)
+
+
+def compulsory_bytes(w) -> int:
+    s = w.values.dtype.itemsize
+    b = 4 * (w.M + 1) + w.nnz * (4 + s) + w.N * s + w.M * s
+    if w.beta != 0.0:
+        b += w.M * s          # y is read as well as written
+    return b
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken with the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get("%s/%s" % (workload, kernel))
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float, y_gpu):
+    """The oracle as it stands, on one host core, repeated on the whole
+    workload until the budget is spent (at least once). Its result also
+    checks the GPU's first exec (every row, the acceptance bound)."""
+    import oracle
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 50:
+            break
+    t = statistics.median(times)
+    ok, worst, _ = oracle.within_tolerance(y_gpu, ref, scale, w.alpha, w.beta, w.y0,
+                                           row_ptr=w.row_ptr)
+    res = {"value": round(2.0 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
+           "kind": "oracle",
+           "sample": "whole workload (%d nnz), %d runs, median %.1f ms, fp64 accumulation"
+                     % (w.nnz, len(times), t * 1e3),
+           "GBps": round(compulsory_bytes(w) / t / 1e9, 3)}
+    return res, bool(ok), worst
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="laplacian", choices=list(WORKLOADS))
+    ap.add_argument("--strategy", default="auto", choices=["auto", "merge", "binned"])
+    ap.add_argument("--items-per-thread", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import load_balanced_csr_amd as lb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    print("[bench] generating %s" % args.workload, file=sys.stderr, flush=True)
+    w = synth.CONFIGS[args.workload]()
+    dt = torch.float32 if w.values.dtype == np.float32 else torch.float64
+
+    rp = torch.from_numpy(w.row_ptr).to(dev)
+    col = torch.from_numpy(w.col_idx).to(dev)
+    val = torch.from_numpy(w.values).to(dev)
+    x = torch.from_numpy(w.x).to(dev)
+    y0 = torch.from_numpy(w.y0).to(dev) if w.y0 is not None else None
+    y = torch.empty(w.M, dtype=dt, device=dev)
+    torch.cuda.synchronize()
+
+    # planning cost (separate from the steps): median of 3 plan/destroy cycles
+    plan_ms = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        p = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
+                    items_per_thread=args.items_per_thread)
+        plan_ms.append((time.perf_counter() - t0) * 1e3)
+        p.destroy()
+    plan = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
+                   items_per_thread=args.items_per_thread)
+    info = plan.info
+
+    # first exec on fresh inputs; the cpu_baseline leg checks it against the oracle
+    if y0 is not None:
+        y.copy_(y0)
+    else:
+        y.fill_(float("nan"))
+    plan(x, y, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    y_first = y.cpu().numpy()
+
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hip = HipEvents()
+    K, W = args.steps, args.warmup
+    kb = [hip.create() for _ in range(K)]
+    ke = [hip.create() for _ in range(K)]
+    xb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    xe = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    if y0 is not None:
+        y.copy_(y0)
+
+    for _ in range(W):
+        if flush is not None:
+            flush.zero_()
+        plan(x, y, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush.zero_()
+        xb[i].record()
+        lb.spmv_exec_events(plan.handle, x, y, w.alpha, w.beta, kb[i], ke[i])
+        xe[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    exec_ms = [xb[i].elapsed_time(xe[i]) for i in range(K)]
+    kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
+    for e in kb + ke:
+        hip.destroy(e)
+    mean_exec = statistics.fmean(exec_ms)
+    mean_kern = statistics.fmean(kern_ms)
+    Bc = compulsory_bytes(w)
+    gflops = 2.0 * w.nnz / (mean_exec * 1e-3) / 1e9
+    gbps_exec = Bc / (mean_exec * 1e-3) / 1e9
+    kernel = "merge_spmv_kernel" if info["strategy"] == "merge" else "binned_spmv_kernel"
+    achieved = Bc / (mean_kern * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(gflops, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(mean_exec, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if dt == torch.float32 else "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
+                   "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha, "beta": w.beta,
+                   "seed": w.seed, "strategy": info["strategy"],
+                   "items_per_wave": info["items_per_wave"],
+                   "cache": "warm" if flush is None else "1 GiB flush before every step"},
+        "achieved_GBps": round(gbps_exec, 2),
+        "pct_hbm_peak": round(100.0 * gbps_exec / HBM_PEAK_GBPS, 2),
+        "compulsory_bytes": Bc,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "kernel_ms": round(mean_kern, 5),
+                     "traffic": load_traffic(args.workload, kernel)},
+        "exec_ms_median": round(statistics.median(exec_ms), 5),
+        "exec_ms_min": round(min(exec_ms), 5),
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "plan_ms": round(statistics.median(plan_ms), 3),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    plan.destroy()
+    ok = True
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"], ok, worst = cpu_baseline(w, args.cpu_seconds, y_first)
+        out["parity"] = {"ok": ok, "worst_over_bound": round(worst, 5),
+                         "checked": "first exec vs the oracle, every row"}
+    print(json.dumps(out), flush=True)
+    if not ok:
+        sys.exit(3)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,6 +46,8 @@
 extern "C" {
 #endif
 
+#define SPMV_API __attribute__((visibility("default")))
+
 typedef enum spmv_status {
   SPMV_SUCCESS = 0,
   SPMV_ERR_INVALID_ARG = 1,    /* null/aliased pointer, negative size, bad enum */
@@ -133,13 +135,13 @@ typedef struct spmv_plan_info {
  * device-to-host copy of a small statistics block and one stream
  * synchronisation. Returns SPMV_ERR_UNSUPPORTED if M + nnz > 2^31 - 1.
  * M == 0 or nnz == 0 is allowed. */
-spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+SPMV_API spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                         const int32_t* row_ptr, const int32_t* col_idx,
                         const void* values, spmv_dtype_t dtype,
                         hipStream_t stream);
 
 /* spmv_plan with explicit options (NULL = defaults). */
-spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+SPMV_API spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                            const int32_t* row_ptr, const int32_t* col_idx,
                            const void* values, spmv_dtype_t dtype,
                            const spmv_plan_options_t* options,
@@ -156,43 +158,43 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
  * For a fixed plan the result is bitwise reproducible (no float atomics).
  * One plan must not run concurrently on two streams (its carry buffer is
  * per plan); distinct plans are independent. */
-spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
+SPMV_API spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
                         double alpha, double beta, hipStream_t stream);
 
 /* spmv_exec that also records ev_begin just before and ev_end just after the
  * dominant kernel (the merge-path main kernel or the fused binned kernel), on
  * the same stream, so a caller can time that kernel alone. Either event may
  * be NULL. */
-spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y,
+SPMV_API spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y,
                                double alpha, double beta, hipStream_t stream,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 
 /* Release the plan's workspace (hipFree, which synchronises the device).
  * NULL is a no-op; a destroyed or foreign handle gives SPMV_ERR_INVALID_PLAN
  * as long as its memory has not been reused. */
-spmv_status_t spmv_destroy(spmv_plan_t plan);
+SPMV_API spmv_status_t spmv_destroy(spmv_plan_t plan);
 
 /* Switch a live plan between MERGE and BINNED (both are always built). */
-spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
+SPMV_API spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
 
 /* Fill *info (host struct). */
-spmv_status_t spmv_plan_info(spmv_plan_t plan, spmv_plan_info_t* info);
+SPMV_API spmv_status_t spmv_plan_info(spmv_plan_t plan, spmv_plan_info_t* info);
 
 /* Copy the merge-path split coordinates to host arrays of cap >= P+1 entries:
  * rows_host[p] = rows whose end item precedes diagonal min(p*T, M+nnz),
  * nnz_host[p] = nonzeros before it. Synchronous (stream-ordered on the null
  * stream after the plan's work). */
-spmv_status_t spmv_plan_copy_splits(spmv_plan_t plan, int32_t* rows_host,
+SPMV_API spmv_status_t spmv_plan_copy_splits(spmv_plan_t plan, int32_t* rows_host,
                                     int32_t* nnz_host, int64_t cap);
 
 /* Copy the binning result to host: bins_host[M] (row ids grouped by bin,
  * ascending within a bin; the identity when bin_identity is set) and
  * offsets_host[n_bins+1]. Synchronous. */
-spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
+SPMV_API spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
                                   int64_t bins_cap, int64_t* offsets_host);
 
-const char* spmv_status_string(spmv_status_t status);
-const char* spmv_last_error(void);
+SPMV_API const char* spmv_status_string(spmv_status_t status);
+SPMV_API const char* spmv_last_error(void);
 
 #ifdef __cplusplus
 }

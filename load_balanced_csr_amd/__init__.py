@@ -1,0 +1,17 @@
+"""Load-balanced CSR sparse matrix-vector multiplication for AMD MI355X.
+
+y = alpha * A x + beta * y with A in CSR (int32 row_ptr/col_idx, fp32 or fp64
+values), computed by hand-written gfx950 HIP kernels in libspmv.so: a
+merge-path schedule over rows + nonzeros with a carry fix-up, and a binned
+schedule (thread / lane-group / wavefront / workgroup per row). This package
+is a thin ctypes binding over the C ABI declared in include/spmv.h.
+"""
+from .binding import (EXPORTED, LIB_PATH, Plan, PlanOptions, SpmvError, load, make_options,
+                      spmv_destroy, spmv_exec, spmv_exec_events, spmv_last_error, spmv_plan,
+                      spmv_plan_copy_bins, spmv_plan_copy_splits, spmv_plan_info,
+                      spmv_plan_set_strategy, spmv_status_string)
+
+__all__ = ["EXPORTED", "LIB_PATH", "Plan", "PlanOptions", "SpmvError", "load", "make_options",
+           "spmv_destroy", "spmv_exec", "spmv_exec_events", "spmv_last_error", "spmv_plan",
+           "spmv_plan_copy_bins", "spmv_plan_copy_splits", "spmv_plan_info",
+           "spmv_plan_set_strategy", "spmv_status_string"]

@@ -1,0 +1,265 @@
+"""ctypes binding of libspmv.so (the C ABI in include/spmv.h).
+
+Argument marshalling only: tensors become device pointers and sizes, the
+current torch stream becomes the hipStream_t, statuses become exceptions.
+Every step of planning and execution runs in the library's HIP kernels.
+There is no fallback: if libspmv.so cannot be built or loaded, the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime libspmv.so binds to (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspmv.so")
+
+SPMV_SUCCESS = 0
+STATUS_NAMES = {0: "SUCCESS", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALLOC", 4: "HIP",
+                5: "INVALID_PLAN", 6: "INVALID_MATRIX"}
+SPMV_F32, SPMV_F64 = 0, 1
+STRATEGY = {"auto": 0, "merge": 1, "binned": 2}
+STRATEGY_NAME = {v: k for k, v in STRATEGY.items()}
+MAX_BINS = 8
+
+EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_exec", "spmv_exec_events", "spmv_destroy",
+            "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
+            "spmv_plan_copy_bins", "spmv_status_string", "spmv_last_error")
+
+
+class SpmvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS_NAMES.get(status, status), detail))
+
+
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("strategy", ctypes.c_int32), ("items_per_thread", ctypes.c_int32),
+                ("n_bins", ctypes.c_int32), ("validate_columns", ctypes.c_int32),
+                ("bin_max_len", ctypes.c_int64 * MAX_BINS),
+                ("bin_lanes", ctypes.c_int32 * MAX_BINS)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("strategy", ctypes.c_int32),
+                ("items_per_thread", ctypes.c_int32), ("items_per_wave", ctypes.c_int32),
+                ("n_partitions", ctypes.c_int64), ("n_bins", ctypes.c_int32),
+                ("bin_identity", ctypes.c_int32), ("bin_max_len", ctypes.c_int64 * MAX_BINS),
+                ("bin_lanes", ctypes.c_int32 * MAX_BINS),
+                ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
+                ("n_empty_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(build_if_missing: bool = True):
+    """Load libspmv.so (building it with hipcc first if it is not there)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise OSError("libspmv.so is not built: " + LIB_PATH)
+        from . import build as _build
+        _build.build(force=False)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, p, d = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+    st = ctypes.c_int
+    lib.spmv_plan.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p]
+    lib.spmv_plan_ex.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32,
+                                 ctypes.POINTER(PlanOptions), p]
+    lib.spmv_exec.argtypes = [p, p, p, d, d, p]
+    lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
+    lib.spmv_destroy.argtypes = [p]
+    lib.spmv_plan_set_strategy.argtypes = [p, i32]
+    lib.spmv_plan_info.argtypes = [p, ctypes.POINTER(PlanInfo)]
+    lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
+    lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
+    for name in EXPORTED:
+        if name not in ("spmv_status_string", "spmv_last_error"):
+            getattr(lib, name).restype = st
+    lib.spmv_status_string.argtypes = [st]
+    lib.spmv_status_string.restype = ctypes.c_char_p
+    lib.spmv_last_error.argtypes = []
+    lib.spmv_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != SPMV_SUCCESS:
+        raise SpmvError(status, where, load().spmv_last_error().decode(errors="replace"))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr() if t.numel() else None
+
+
+def _dtype_code(values: torch.Tensor) -> int:
+    return SPMV_F32 if values.dtype == torch.float32 else SPMV_F64
+
+
+def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
+                 validate_columns: bool = False) -> PlanOptions:
+    """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored."""
+    o = PlanOptions()
+    o.strategy = STRATEGY[strategy]
+    o.items_per_thread = items_per_thread
+    o.validate_columns = int(bool(validate_columns))
+    if bins:
+        o.n_bins = len(bins)
+        for k, (ml, lanes) in enumerate(bins):
+            o.bin_max_len[k] = ml if ml is not None else 0
+            o.bin_lanes[k] = lanes
+    return o
+
+
+def spmv_plan(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor, M: int,
+              N: int, options: Optional[PlanOptions] = None, stream=None) -> int:
+    """Plan handle for the CSR matrix (device int32 row_ptr/col_idx, fp32/fp64
+    values). The tensors are borrowed: keep them alive until spmv_destroy."""
+    lib = load()
+    nnz = int(col_idx.numel())
+    h = ctypes.c_void_p()
+    args = (ctypes.byref(h), M, N, nnz, _dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
+            _dev_ptr(col_idx, "col_idx", (torch.int32,)),
+            _dev_ptr(values, "values", (torch.float32, torch.float64)), _dtype_code(values))
+    if options is None:
+        _check(lib.spmv_plan(*args, _stream(stream)), "spmv_plan")
+    else:
+        _check(lib.spmv_plan_ex(*args, ctypes.byref(options), _stream(stream)), "spmv_plan_ex")
+    return h.value
+
+
+def spmv_exec(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
+              beta: float = 0.0, stream=None) -> None:
+    """y = alpha * A x + beta * y, enqueued on the stream (asynchronous)."""
+    dts = (torch.float32, torch.float64)
+    _check(load().spmv_exec(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts), float(alpha),
+                            float(beta), _stream(stream)), "spmv_exec")
+
+
+def spmv_exec_events(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float, beta: float,
+                     ev_begin: int, ev_end: int, stream=None) -> None:
+    """spmv_exec recording two hipEvent_t handles around the dominant kernel."""
+    dts = (torch.float32, torch.float64)
+    _check(load().spmv_exec_events(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts),
+                                   float(alpha), float(beta), _stream(stream), ev_begin, ev_end),
+           "spmv_exec_events")
+
+
+def spmv_destroy(plan: Optional[int]) -> None:
+    _check(load().spmv_destroy(plan), "spmv_destroy")
+
+
+def spmv_plan_set_strategy(plan: int, strategy: str) -> None:
+    _check(load().spmv_plan_set_strategy(plan, STRATEGY[strategy]), "spmv_plan_set_strategy")
+
+
+def spmv_plan_info(plan: int) -> dict:
+    info = PlanInfo()
+    _check(load().spmv_plan_info(plan, ctypes.byref(info)), "spmv_plan_info")
+    nb = info.n_bins
+    return {"M": info.M, "N": info.N, "nnz": info.nnz,
+            "dtype": "f32" if info.dtype == SPMV_F32 else "f64",
+            "strategy": STRATEGY_NAME[info.strategy], "items_per_thread": info.items_per_thread,
+            "items_per_wave": info.items_per_wave, "n_partitions": info.n_partitions,
+            "n_bins": nb, "bin_identity": bool(info.bin_identity),
+            "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
+            "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
+            "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes}
+
+
+def spmv_plan_copy_splits(plan: int):
+    import numpy as np
+    P = spmv_plan_info(plan)["n_partitions"]
+    rows = np.empty(P + 1, dtype=np.int32)
+    nz = np.empty(P + 1, dtype=np.int32)
+    _check(load().spmv_plan_copy_splits(plan, rows.ctypes.data, nz.ctypes.data, P + 1),
+           "spmv_plan_copy_splits")
+    return rows, nz
+
+
+def spmv_plan_copy_bins(plan: int):
+    import numpy as np
+    info = spmv_plan_info(plan)
+    M = info["M"]
+    bins = np.empty(max(M, 1), dtype=np.int32)
+    offsets = np.empty(info["n_bins"] + 1, dtype=np.int64)
+    _check(load().spmv_plan_copy_bins(plan, bins.ctypes.data, M, offsets.ctypes.data),
+           "spmv_plan_copy_bins")
+    return bins[:M], offsets
+
+
+def spmv_status_string(status: int) -> str:
+    return load().spmv_status_string(status).decode()
+
+
+def spmv_last_error() -> str:
+    return load().spmv_last_error().decode(errors="replace")
+
+
+class Plan:
+    """A planned CSR matrix: ``Plan(row_ptr, col_idx, values, (M, N))``, then
+    ``plan(x, y, alpha, beta)``. Holds references to the borrowed tensors."""
+
+    def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
+                 items_per_thread: int = 0, bins=None, validate_columns: bool = False,
+                 stream=None):
+        self.M, self.N = int(shape[0]), int(shape[1])
+        self._keep = (row_ptr, col_idx, values)
+        opts = None
+        if strategy != "auto" or items_per_thread or bins or validate_columns:
+            opts = make_options(strategy, items_per_thread, bins, validate_columns)
+        self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
+
+    def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):
+        spmv_exec(self.handle, x, y, alpha, beta, stream)
+        return y
+
+    def set_strategy(self, strategy: str):
+        spmv_plan_set_strategy(self.handle, strategy)
+
+    @property
+    def info(self) -> dict:
+        return spmv_plan_info(self.handle)
+
+    def splits(self):
+        return spmv_plan_copy_splits(self.handle)
+
+    def bins(self):
+        return spmv_plan_copy_bins(self.handle)
+
+    def destroy(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            spmv_destroy(h)
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

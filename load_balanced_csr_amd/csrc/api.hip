@@ -1,0 +1,491 @@
+// C ABI of libspmv.so (declared in include/spmv.h): argument checks, the
+// plan's single workspace allocation, planning launches, strategy choice and
+// the exec launches. No computation of the SpMV happens on the host.
+#include "spmv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+
+#include "internal.hpp"
+
+using namespace spmv;
+
+namespace {
+
+constexpr uint64_t kMagic = 0x53504d5650414e31ull;  // "SPMVPAN1"
+constexpr int64_t kInt32Max = 2147483647ll;
+
+thread_local std::string g_last_error;
+
+spmv_status_t fail(spmv_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+spmv_status_t fail(spmv_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+spmv_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(SPMV_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : dflt;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Default row-length bins: inclusive upper lengths and lanes per row.
+const int64_t kDefaultMaxLen[kMaxBins - 1] = {2, 8, 16, 32, 128, 512, 4096};
+const int32_t kDefaultLanes[kMaxBins] = {1, 2, 4, 8, 16, 32, 64, 256};
+
+}  // namespace
+
+struct spmv_plan_st {
+  uint64_t magic;
+  int64_t M, N, nnz;
+  spmv_dtype_t dtype;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* values;
+
+  int32_t strategy;
+  int32_t ipt, T;
+  int64_t P;
+  int32_t xcd_remap;
+
+  BinEdges edges;
+  int32_t lanes[kMaxBins];
+  int64_t bin_offset[kMaxBins + 1];
+  int32_t identity;
+  int64_t max_len, n_empty;
+  int32_t n_launch;
+  BinLaunch launch[kMaxBins];
+  int32_t binned_blocks;
+
+  void* ws;
+  size_t ws_bytes;
+  int64_t* stats;
+  int32_t* counts;
+  int32_t* wg_max;
+  int32_t* wg_empty;
+  int32_t* split_row;
+  int32_t* split_nz;
+  int32_t* carry_row;
+  void* carry_val;
+  int32_t* bins;
+};
+
+namespace {
+
+// Live plans. A handle is only dereferenced after it is found here, so a
+// destroyed or foreign handle is rejected without touching its memory.
+std::mutex g_plans_mu;
+std::unordered_set<const spmv_plan_st*> g_plans;
+
+spmv_status_t check_plan(spmv_plan_t p) {
+  if (!p) return fail(SPMV_ERR_INVALID_PLAN, "plan is NULL");
+  {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    if (!g_plans.count(p)) return fail(SPMV_ERR_INVALID_PLAN, "not a live plan handle");
+  }
+  if (p->magic != kMagic) return fail(SPMV_ERR_INVALID_PLAN, "corrupted plan handle");
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t check_options(const spmv_plan_options_t* o) {
+  if (!o) return SPMV_SUCCESS;
+  if (o->strategy < 0 || o->strategy > SPMV_STRATEGY_BINNED)
+    return fail(SPMV_ERR_INVALID_ARG, "options.strategy %d unknown", o->strategy);
+  if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 8 &&
+      o->items_per_thread != 16)
+    return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 8 or 16");
+  if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
+    return fail(SPMV_ERR_INVALID_ARG, "options.n_bins must be in [0, %d]", SPMV_MAX_BINS);
+  if (o->n_bins > 0) {
+    for (int b = 0; b < o->n_bins; ++b) {
+      const int g = o->bin_lanes[b];
+      if (!(g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32 || g == 64 || g == 256))
+        return fail(SPMV_ERR_INVALID_ARG, "options.bin_lanes[%d] = %d not allowed", b, g);
+    }
+    for (int b = 0; b + 1 < o->n_bins; ++b) {
+      if (o->bin_max_len[b] < 0 || (b > 0 && o->bin_max_len[b] <= o->bin_max_len[b - 1]))
+        return fail(SPMV_ERR_INVALID_ARG, "options.bin_max_len must increase strictly");
+    }
+  }
+  return SPMV_SUCCESS;
+}
+
+// Lay out the binned grid: bins with the longest rows first.
+void build_binned_launch(spmv_plan_st* p) {
+  p->n_launch = 0;
+  int32_t next = 0;
+  for (int b = p->edges.n_bins - 1; b >= 0; --b) {
+    const int64_t rows = p->bin_offset[b + 1] - p->bin_offset[b];
+    if (rows == 0) continue;
+    BinLaunch& L = p->launch[p->n_launch++];
+    L.lanes = p->lanes[b];
+    L.row_begin = (int32_t)p->bin_offset[b];
+    L.n_rows = (int32_t)rows;
+    const int64_t per = L.lanes >= kBlock ? 1 : kBlock / L.lanes;
+    L.n_blocks = (int32_t)((rows + per - 1) / per);
+    L.block_begin = next;
+    next += L.n_blocks;
+  }
+  p->binned_blocks = next;
+}
+
+// The schedule used when none is forced. Merge-path is the general case;
+// rows that are all short and of similar length (one bin) run binned.
+int32_t choose_strategy(const spmv_plan_st*) {
+  const char* env = std::getenv("SPMV_STRATEGY");
+  if (env && !std::strcmp(env, "merge")) return SPMV_STRATEGY_MERGE;
+  if (env && !std::strcmp(env, "binned")) return SPMV_STRATEGY_BINNED;
+  return SPMV_STRATEGY_MERGE;
+}
+
+template <typename V>
+spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, double beta,
+                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t err = hipSuccess;
+  if (p->strategy == SPMV_STRATEGY_MERGE) {
+    MergeArgs<V> a;
+    a.row_ptr = p->row_ptr;
+    a.col_idx = p->col_idx;
+    a.val = static_cast<const V*>(p->values);
+    a.x = static_cast<const V*>(x);
+    a.y = static_cast<V*>(y);
+    a.split_row = p->split_row;
+    a.split_nz = p->split_nz;
+    a.carry_row = p->carry_row;
+    a.carry_val = static_cast<V*>(p->carry_val);
+    a.alpha = (V)alpha;
+    a.beta = (V)beta;
+    a.beta_nonzero = beta != 0.0;
+    a.P = (int32_t)p->P;
+    a.M = (int32_t)p->M;
+    a.xcd_remap = p->xcd_remap;
+    err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
+  } else {
+    BinnedArgs<V> a;
+    std::memset(&a, 0, sizeof a);
+    a.row_ptr = p->row_ptr;
+    a.col_idx = p->col_idx;
+    a.val = static_cast<const V*>(p->values);
+    a.x = static_cast<const V*>(x);
+    a.y = static_cast<V*>(y);
+    a.bins = p->bins;
+    a.alpha = (V)alpha;
+    a.beta = (V)beta;
+    a.beta_nonzero = beta != 0.0;
+    a.identity = p->identity;
+    a.n_launch = p->n_launch;
+    a.xcd_remap = p->xcd_remap;
+    for (int i = 0; i < p->n_launch; ++i) a.bin[i] = p->launch[i];
+    err = launch_binned<V>(a, p->binned_blocks, stream, ev0, ev1);
+  }
+  if (err != hipSuccess) return hip_fail(err, "spmv_exec launch");
+  return SPMV_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                           const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                           spmv_dtype_t dtype, const spmv_plan_options_t* options,
+                           hipStream_t stream) {
+  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (M < 0 || N < 0 || nnz < 0)
+    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
+                (long long)N, (long long)nnz);
+  if (dtype != SPMV_F32 && dtype != SPMV_F64)
+    return fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (M > 0 && !row_ptr) return fail(SPMV_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (nnz > 0 && (!col_idx || !values))
+    return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
+  if (M == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "M = 0 needs nnz = 0");
+  if (N == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "N = 0 needs nnz = 0");
+  if (nnz > kInt32Max || M >= kInt32Max || N > kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
+  if (M + nnz > kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "M + nnz = %lld exceeds 2^31 - 1 work units",
+                (long long)(M + nnz));
+  spmv_status_t st = check_options(options);
+  if (st != SPMV_SUCCESS) return st;
+
+  spmv_plan_st* p = new (std::nothrow) spmv_plan_st;
+  if (!p) return fail(SPMV_ERR_ALLOC, "host allocation of the plan failed");
+  std::memset(p, 0, sizeof *p);
+  p->M = M;
+  p->N = N;
+  p->nnz = nnz;
+  p->dtype = dtype;
+  p->row_ptr = row_ptr;
+  p->col_idx = col_idx;
+  p->values = values;
+  p->xcd_remap = env_int("SPMV_XCD_REMAP", 1) != 0;
+
+  const int forced = options ? options->strategy : 0;
+  p->ipt = options && options->items_per_thread ? options->items_per_thread
+                                                 : env_int("SPMV_ITEMS_PER_THREAD", 8);
+  if (p->ipt != 4 && p->ipt != 8 && p->ipt != 16) p->ipt = 8;
+  p->T = kWave * p->ipt;
+  const int64_t W = M + nnz;
+  p->P = (W + p->T - 1) / p->T;
+
+  if (options && options->n_bins > 0) {
+    p->edges.n_bins = options->n_bins;
+    for (int b = 0; b + 1 < options->n_bins; ++b) p->edges.max_len[b] = options->bin_max_len[b];
+    for (int b = 0; b < options->n_bins; ++b) p->lanes[b] = options->bin_lanes[b];
+  } else {
+    p->edges.n_bins = kMaxBins;
+    for (int b = 0; b + 1 < kMaxBins; ++b) p->edges.max_len[b] = kDefaultMaxLen[b];
+    for (int b = 0; b < kMaxBins; ++b) p->lanes[b] = kDefaultLanes[b];
+  }
+  const bool validate_cols =
+      (options && options->validate_columns) || env_int("SPMV_VALIDATE", 0) != 0;
+
+  // ---- the one workspace allocation -------------------------------------------
+  const size_t vs = dtype == SPMV_F32 ? 4 : 8;
+  const int64_t n_wg = (M + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t o_stats = take(sizeof(int64_t) * kStatCount);
+  const size_t o_counts = take(sizeof(int32_t) * kMaxBins * n_wg);
+  const size_t o_wgmax = take(sizeof(int32_t) * n_wg);
+  const size_t o_wgemp = take(sizeof(int32_t) * n_wg);
+  const size_t o_srow = take(sizeof(int32_t) * (p->P + 1));
+  const size_t o_snz = take(sizeof(int32_t) * (p->P + 1));
+  const size_t o_crow = take(sizeof(int32_t) * p->P);
+  const size_t o_cval = take(vs * p->P);
+  const size_t o_bins = take(sizeof(int32_t) * M);
+  p->ws_bytes = off;
+  if (env_int("SPMV_TEST_FAIL_ALLOC", 0)) {
+    delete p;
+    return fail(SPMV_ERR_ALLOC, "workspace allocation failed (forced by SPMV_TEST_FAIL_ALLOC)");
+  }
+  hipError_t err = hipMalloc(&p->ws, p->ws_bytes);
+  if (err != hipSuccess) {
+    delete p;
+    (void)hipGetLastError();
+    return fail(SPMV_ERR_ALLOC, "hipMalloc(%zu) failed: %s", off, hipGetErrorString(err));
+  }
+  char* base = static_cast<char*>(p->ws);
+  p->stats = reinterpret_cast<int64_t*>(base + o_stats);
+  p->counts = reinterpret_cast<int32_t*>(base + o_counts);
+  p->wg_max = reinterpret_cast<int32_t*>(base + o_wgmax);
+  p->wg_empty = reinterpret_cast<int32_t*>(base + o_wgemp);
+  p->split_row = reinterpret_cast<int32_t*>(base + o_srow);
+  p->split_nz = reinterpret_cast<int32_t*>(base + o_snz);
+  p->carry_row = reinterpret_cast<int32_t*>(base + o_crow);
+  p->carry_val = base + o_cval;
+  p->bins = reinterpret_cast<int32_t*>(base + o_bins);
+
+  // ---- planning kernels, one read-back, one synchronisation ---------------------
+  int64_t host_stats[kStatCount] = {0};
+  auto bail = [&](spmv_status_t s) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(p->ws);
+    delete p;
+    return s;
+  };
+  if ((err = launch_clear_stats(p->stats, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: clear"));
+  if ((err = launch_bin_count(row_ptr, M, nnz, p->edges, p->counts, p->wg_max, p->wg_empty,
+                              p->stats, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: bin count"));
+  if ((err = launch_bin_scan(M, p->edges, p->counts, p->wg_max, p->wg_empty, p->stats,
+                             stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: bin scan"));
+  if ((err = launch_bin_scatter(row_ptr, M, p->edges, p->counts, p->stats, p->bins, stream)) !=
+      hipSuccess)
+    return bail(hip_fail(err, "plan: bin scatter"));
+  if (p->P > 0 && (err = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row,
+                                             p->split_nz, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: split search"));
+  if (validate_cols &&
+      (err = launch_check_columns(col_idx, nnz, N, p->stats, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: column check"));
+  if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: stats copy"));
+  if ((err = hipStreamSynchronize(stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: synchronize"));
+
+  if (host_stats[kStatError] & 1)
+    return bail(fail(SPMV_ERR_INVALID_MATRIX,
+                     "row_ptr is not a CSR row pointer array (row_ptr[0] = 0, "
+                     "non-decreasing, row_ptr[M] = nnz)"));
+  if (host_stats[kStatError] & 2)
+    return bail(fail(SPMV_ERR_INVALID_MATRIX, "a column index is outside [0, N)"));
+
+  p->max_len = host_stats[kStatMaxLen];
+  p->n_empty = host_stats[kStatEmpty];
+  for (int b = 0; b <= p->edges.n_bins; ++b)
+    p->bin_offset[b] = M > 0 ? host_stats[kStatBinOffset + b] : 0;
+  p->identity = M == 0 || host_stats[kStatNonEmptyBins] <= 1;
+  build_binned_launch(p);
+  if ((int64_t)p->binned_blocks * kBlock > 0xffffffffll)
+    return bail(fail(SPMV_ERR_UNSUPPORTED, "binned grid exceeds 2^32 work-items"));
+
+  p->strategy = forced ? forced : choose_strategy(p);
+  if (env_int("SPMV_LOG", 0))
+    std::fprintf(stderr,
+                 "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s T=%d P=%lld "
+                 "max_len=%lld empty=%lld bins=%d identity=%d ws=%zu\n",
+                 (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
+                 p->strategy == SPMV_STRATEGY_MERGE ? "merge" : "binned", p->T,
+                 (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
+                 p->edges.n_bins, p->identity, p->ws_bytes);
+  p->magic = kMagic;
+  {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    g_plans.insert(p);
+  }
+  *out = p;
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                        const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                        spmv_dtype_t dtype, hipStream_t stream) {
+  return spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, nullptr, stream);
+}
+
+spmv_status_t spmv_exec_events(spmv_plan_t p, const void* x, void* y, double alpha,
+                               double beta, hipStream_t stream, hipEvent_t ev_begin,
+                               hipEvent_t ev_end) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (p->M > 0 && !y) return fail(SPMV_ERR_INVALID_ARG, "y is NULL");
+  if (p->N > 0 && p->nnz > 0 && !x) return fail(SPMV_ERR_INVALID_ARG, "x is NULL");
+  if (x && y && x == y) return fail(SPMV_ERR_INVALID_ARG, "x and y must not alias");
+  if (p->M == 0) return SPMV_SUCCESS;
+  return p->dtype == SPMV_F32
+             ? exec_typed<float>(p, x, y, alpha, beta, stream, ev_begin, ev_end)
+             : exec_typed<double>(p, x, y, alpha, beta, stream, ev_begin, ev_end);
+}
+
+spmv_status_t spmv_exec(spmv_plan_t p, const void* x, void* y, double alpha, double beta,
+                        hipStream_t stream) {
+  return spmv_exec_events(p, x, y, alpha, beta, stream, nullptr, nullptr);
+}
+
+spmv_status_t spmv_destroy(spmv_plan_t p) {
+  if (!p) return SPMV_SUCCESS;
+  {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    if (!g_plans.erase(p)) return fail(SPMV_ERR_INVALID_PLAN, "not a live plan handle");
+  }
+  p->magic = 0;
+  hipError_t err = hipFree(p->ws);
+  delete p;
+  if (err != hipSuccess) return hip_fail(err, "spmv_destroy: hipFree");
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan_set_strategy(spmv_plan_t p, spmv_strategy_t strategy) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (strategy == SPMV_STRATEGY_AUTO) p->strategy = choose_strategy(p);
+  else if (strategy == SPMV_STRATEGY_MERGE || strategy == SPMV_STRATEGY_BINNED)
+    p->strategy = strategy;
+  else return fail(SPMV_ERR_INVALID_ARG, "unknown strategy %d", (int)strategy);
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (!info) return fail(SPMV_ERR_INVALID_ARG, "info is NULL");
+  std::memset(info, 0, sizeof *info);
+  info->M = p->M;
+  info->N = p->N;
+  info->nnz = p->nnz;
+  info->dtype = p->dtype;
+  info->strategy = p->strategy;
+  info->items_per_thread = p->ipt;
+  info->items_per_wave = p->T;
+  info->n_partitions = p->P;
+  info->n_bins = p->edges.n_bins;
+  info->bin_identity = p->identity;
+  for (int b = 0; b < p->edges.n_bins; ++b) {
+    info->bin_max_len[b] = b + 1 < p->edges.n_bins ? p->edges.max_len[b] : -1;
+    info->bin_lanes[b] = p->lanes[b];
+    info->bin_count[b] = p->bin_offset[b + 1] - p->bin_offset[b];
+  }
+  info->max_row_len = p->max_len;
+  info->n_empty_rows = p->n_empty;
+  info->workspace_bytes = (int64_t)p->ws_bytes;
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan_copy_splits(spmv_plan_t p, int32_t* rows_host, int32_t* nnz_host,
+                                    int64_t cap) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (!rows_host || !nnz_host) return fail(SPMV_ERR_INVALID_ARG, "host buffer is NULL");
+  if (cap < p->P + 1) return fail(SPMV_ERR_INVALID_ARG, "cap < P + 1");
+  if (p->P == 0) {
+    rows_host[0] = 0;
+    nnz_host[0] = 0;
+    return SPMV_SUCCESS;
+  }
+  hipError_t err = hipMemcpy(rows_host, p->split_row, sizeof(int32_t) * (p->P + 1),
+                             hipMemcpyDeviceToHost);
+  if (err == hipSuccess)
+    err = hipMemcpy(nnz_host, p->split_nz, sizeof(int32_t) * (p->P + 1), hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return hip_fail(err, "spmv_plan_copy_splits");
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan_copy_bins(spmv_plan_t p, int32_t* bins_host, int64_t bins_cap,
+                                  int64_t* offsets_host) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if ((!bins_host && p->M > 0) || !offsets_host)
+    return fail(SPMV_ERR_INVALID_ARG, "host buffer is NULL");
+  if (bins_cap < p->M) return fail(SPMV_ERR_INVALID_ARG, "bins_cap < M");
+  for (int b = 0; b <= p->edges.n_bins; ++b) offsets_host[b] = p->bin_offset[b];
+  if (p->M == 0) return SPMV_SUCCESS;
+  if (p->identity) {
+    for (int64_t i = 0; i < p->M; ++i) bins_host[i] = (int32_t)i;
+    return SPMV_SUCCESS;
+  }
+  hipError_t err = hipMemcpy(bins_host, p->bins, sizeof(int32_t) * p->M, hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return hip_fail(err, "spmv_plan_copy_bins");
+  return SPMV_SUCCESS;
+}
+
+const char* spmv_status_string(spmv_status_t s) {
+  switch (s) {
+    case SPMV_SUCCESS: return "success";
+    case SPMV_ERR_INVALID_ARG: return "invalid argument";
+    case SPMV_ERR_UNSUPPORTED: return "unsupported size";
+    case SPMV_ERR_ALLOC: return "device allocation failed";
+    case SPMV_ERR_HIP: return "HIP runtime error";
+    case SPMV_ERR_INVALID_PLAN: return "invalid plan handle";
+    case SPMV_ERR_INVALID_MATRIX: return "malformed CSR matrix";
+  }
+  return "unknown status";
+}
+
+const char* spmv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Binned CSR SpMV for gfx950: rows grouped by length, each bin run by the
+// row mapping that suits its length, all bins in ONE launch.
+//
+// Row mappings: thread-mapped (one lane per row) and warp/block-mapped (a
+// group of lanes, a wavefront, or a workgroup strides a row's nonzeros and
+// reduces), "A Programming Model for GPU Load Balancing" (PPoPP'23),
+// Sections 4.2 and 5.2.2; the scalar and vector CSR kernels that "New
+// Row-grouped CSR format..." (arXiv 1012.2270) Section 3 discusses. Rows come
+// grouped by the plan's bins ("OpSparse", arXiv 2206.07244, Section 5.1);
+// OpSparse launches the kernels of the bins with the largest rows first so
+// the short-row work fills the machine behind them.
+//
+// MI355X mapping: instead of one kernel per bin on several streams, the bins
+// are segments of a single grid. Workgroups are dispatched in index order,
+// and the segments are ordered longest rows first, so the long-row
+// workgroups start first; there is no inter-kernel gap. Inside a segment the
+// workgroup index is renumbered so each XCD walks a contiguous run of rows.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace spmv {
+namespace {
+
+template <typename V>
+__device__ __forceinline__ void store_row(const BinnedArgs<V>& a, int r, V acc) {
+  V out = a.alpha * acc;
+  if (a.beta_nonzero) out = fma(a.beta, a.y[r], out);
+  a.y[r] = out;
+}
+
+// G lanes per row (G = 1, 2, ..., 64), 256 / G rows per workgroup.
+template <typename V, int G>
+__device__ __forceinline__ void group_rows(const BinnedArgs<V>& a, const BinLaunch& L,
+                                           int tile) {
+  constexpr int kRows = kBlock / G;
+  const int grp = threadIdx.x / G, gl = threadIdx.x % G;
+  const int idx = tile * kRows + grp;
+  if (idx >= L.n_rows) return;  // whole groups leave together
+  const int r = a.identity ? L.row_begin + idx : a.bins[L.row_begin + idx];
+  const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
+  V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
+  int k = s + gl;
+  for (; k + 3 * G < e; k += 4 * G) {
+    const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + G);
+    const int c2 = ld_stream(a.col_idx + k + 2 * G), c3 = ld_stream(a.col_idx + k + 3 * G);
+    const V v0 = ld_stream(a.val + k), v1 = ld_stream(a.val + k + G);
+    const V v2 = ld_stream(a.val + k + 2 * G), v3 = ld_stream(a.val + k + 3 * G);
+    acc0 = fma(v0, a.x[c0], acc0);
+    acc1 = fma(v1, a.x[c1], acc1);
+    acc2 = fma(v2, a.x[c2], acc2);
+    acc3 = fma(v3, a.x[c3], acc3);
+  }
+  for (; k < e; k += G) acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
+  V acc = (acc0 + acc1) + (acc2 + acc3);
+  if (G > 1) acc = group_sum<G>(acc);
+  if (gl == 0) store_row(a, r, acc);
+}
+
+// One 256-thread workgroup per row.
+template <typename V>
+__device__ __forceinline__ void block_row(const BinnedArgs<V>& a, const BinLaunch& L,
+                                          int tile) {
+  __shared__ V s_part[kWavesPerBlock];
+  const int r = a.identity ? L.row_begin + tile : a.bins[L.row_begin + tile];
+  const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
+  V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
+  int k = s + (int)threadIdx.x;
+  for (; k + 3 * kBlock < e; k += 4 * kBlock) {
+    const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + kBlock);
+    const int c2 = ld_stream(a.col_idx + k + 2 * kBlock);
+    const int c3 = ld_stream(a.col_idx + k + 3 * kBlock);
+    const V v0 = ld_stream(a.val + k), v1 = ld_stream(a.val + k + kBlock);
+    const V v2 = ld_stream(a.val + k + 2 * kBlock), v3 = ld_stream(a.val + k + 3 * kBlock);
+    acc0 = fma(v0, a.x[c0], acc0);
+    acc1 = fma(v1, a.x[c1], acc1);
+    acc2 = fma(v2, a.x[c2], acc2);
+    acc3 = fma(v3, a.x[c3], acc3);
+  }
+  for (; k < e; k += kBlock)
+    acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
+  V acc = group_sum<kWave>((acc0 + acc1) + (acc2 + acc3));
+  if (lane_id() == 0) s_part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) store_row(a, r, (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
+}
+
+template <typename V>
+__global__ __launch_bounds__(kBlock) void binned_spmv_kernel(const BinnedArgs<V> a) {
+  const int b = blockIdx.x;
+  int d = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxBins; ++k) d += (k < a.n_launch && b >= a.bin[k].block_begin) ? 1 : 0;
+  d = __builtin_amdgcn_readfirstlane(d);
+  const BinLaunch L = a.bin[d];
+  const int tile = a.xcd_remap ? xcd_tile(b, L.block_begin, L.n_blocks) : b - L.block_begin;
+  switch (L.lanes) {
+    case 1: group_rows<V, 1>(a, L, tile); break;
+    case 2: group_rows<V, 2>(a, L, tile); break;
+    case 4: group_rows<V, 4>(a, L, tile); break;
+    case 8: group_rows<V, 8>(a, L, tile); break;
+    case 16: group_rows<V, 16>(a, L, tile); break;
+    case 32: group_rows<V, 32>(a, L, tile); break;
+    case 64: group_rows<V, 64>(a, L, tile); break;
+    default: block_row<V>(a, L, tile); break;
+  }
+}
+
+}  // namespace
+
+template <typename V>
+hipError_t launch_binned(const BinnedArgs<V>& a, int total_blocks, hipStream_t s,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  if (total_blocks <= 0) return hipSuccess;
+  hipError_t err;
+  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+  hipLaunchKernelGGL((binned_spmv_kernel<V>), dim3(total_blocks), dim3(kBlock), 0, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
+  return hipSuccess;
+}
+
+template hipError_t launch_binned<float>(const BinnedArgs<float>&, int, hipStream_t, hipEvent_t,
+                                         hipEvent_t);
+template hipError_t launch_binned<double>(const BinnedArgs<double>&, int, hipStream_t,
+                                          hipEvent_t, hipEvent_t);
+
+}  // namespace spmv

@@ -1,0 +1,105 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels
+// (plan_kernels.hip, merge_kernels.hip, binned_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spmv {
+
+constexpr int kWave = 64;             // CDNA4 wavefront
+constexpr int kBlock = 256;           // threads per workgroup (4 waves)
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
+constexpr int kMaxBins = 8;
+constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
+
+// Layout of the statistics block the plan copies back to the host (int64).
+enum StatSlot : int {
+  kStatMaxLen = 0,
+  kStatEmpty = 1,
+  kStatError = 2,          // bit 0: row_ptr malformed, bit 1: column out of range
+  kStatNonEmptyBins = 3,
+  kStatBinOffset = 4,      // kMaxBins + 1 entries
+  kStatCount = kStatBinOffset + kMaxBins + 1
+};
+
+struct BinEdges {
+  int32_t n_bins;
+  int32_t pad;
+  int64_t max_len[kMaxBins];   // inclusive upper row length of bins 0..n_bins-2
+};
+
+// ---- plan kernels -----------------------------------------------------------
+hipError_t launch_bin_count(const int32_t* row_ptr, int64_t M, int64_t nnz,
+                            const BinEdges& edges, int32_t* counts, int32_t* wg_max,
+                            int32_t* wg_empty, int64_t* stats, hipStream_t s);
+hipError_t launch_bin_scan(int64_t M, const BinEdges& edges, int32_t* counts,
+                           const int32_t* wg_max, const int32_t* wg_empty,
+                           int64_t* stats, hipStream_t s);
+hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges& edges,
+                              const int32_t* offsets, const int64_t* stats,
+                              int32_t* bins, hipStream_t s);
+hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
+                               int64_t P, int32_t* split_row, int32_t* split_nz,
+                               hipStream_t s);
+hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
+                                int64_t* stats, hipStream_t s);
+hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
+
+// ---- merge-path exec ----------------------------------------------------------
+template <typename V>
+struct MergeArgs {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const V* val;
+  const V* x;
+  V* y;
+  const int32_t* split_row;
+  const int32_t* split_nz;
+  int32_t* carry_row;
+  V* carry_val;
+  V alpha;
+  V beta;
+  int32_t beta_nonzero;
+  int32_t P;
+  int32_t M;
+  int32_t xcd_remap;
+};
+
+template <typename V>
+hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,
+                        hipEvent_t ev1);
+
+// ---- binned exec ----------------------------------------------------------------
+struct BinLaunch {
+  int32_t block_begin;   // first workgroup of this bin in the fused grid
+  int32_t n_blocks;
+  int32_t row_begin;     // first entry of this bin in the row-id array
+  int32_t n_rows;
+  int32_t lanes;         // lanes per row: 1..64 (power of two) or 256
+  int32_t pad[3];
+};
+
+template <typename V>
+struct BinnedArgs {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const V* val;
+  const V* x;
+  V* y;
+  const int32_t* bins;   // row ids grouped by bin; unused when identity
+  V alpha;
+  V beta;
+  int32_t beta_nonzero;
+  int32_t identity;
+  int32_t n_launch;
+  int32_t xcd_remap;
+  BinLaunch bin[kMaxBins];
+};
+
+template <typename V>
+hipError_t launch_binned(const BinnedArgs<V>& a, int total_blocks, hipStream_t s,
+                         hipEvent_t ev0, hipEvent_t ev1);
+
+}  // namespace spmv

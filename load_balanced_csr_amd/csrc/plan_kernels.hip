@@ -1,0 +1,269 @@
+// Planning kernels: row-length statistics and bins counted in LDS, the
+// exclusive scan of the bin counts, the stable scatter of row ids into bins,
+// and the merge-path split search (one binary search per wavefront
+// partition).
+//
+// Binning follows "OpSparse: a Highly Optimized Framework for Sparse General
+// Matrix Multiplication on GPUs" (arXiv 2206.07244), Section 5.1: a first
+// pass counts the rows of every bin with shared-memory (here LDS) counters
+// and tracks the longest row the same way, an exclusive sum turns the counts
+// into offsets, and a second pass writes the row ids; when every row falls
+// into one bin the second pass is skipped and row ids are used directly.
+// Here the counts are kept per workgroup and scanned bin-major, so the
+// offsets are deterministic and rows stay in ascending order inside a bin,
+// without any global atomics.
+//
+// The split search follows "A Programming Model for GPU Load Balancing"
+// (Osama, Porumbescu, Owens, PPoPP'23), Section 5.2.1: rows and nonzeros are
+// units of equal cost, taken in order (a row's nonzeros, then the row's
+// end); a worker's start is found by a binary search along its diagonal.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace spmv {
+namespace {
+
+__device__ __forceinline__ int bin_of(int64_t L, const BinEdges& e) {
+  int b = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxBins - 1; ++k)
+    b += (k < e.n_bins - 1 && L > e.max_len[k]) ? 1 : 0;
+  return b;
+}
+
+__global__ __launch_bounds__(64) void clear_stats_kernel(int64_t* stats) {
+  if (threadIdx.x < kStatCount) stats[threadIdx.x] = 0;
+}
+
+// Pass 1: per-workgroup bin counts, longest row and empty rows, kept in LDS;
+// also checks that row_ptr is a valid CSR row pointer array.
+__global__ __launch_bounds__(kBlock) void bin_count_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, BinEdges edges,
+    int32_t* __restrict__ counts, int32_t* __restrict__ wg_max,
+    int32_t* __restrict__ wg_empty, int64_t* stats) {
+  __shared__ int32_t s_cnt[kMaxBins];
+  __shared__ int32_t s_max, s_empty;
+  const int tid = threadIdx.x;
+  if (tid < kMaxBins) s_cnt[tid] = 0;
+  if (tid == 0) { s_max = 0; s_empty = 0; }
+  __syncthreads();
+  int my_max = 0, my_empty = 0;
+  bool bad = false;
+  const int64_t first = (int64_t)blockIdx.x * kBinRowsPerBlock;
+#pragma unroll
+  for (int k = 0; k < kBinRowsPerBlock / kBlock; ++k) {
+    const int64_t r = first + k * kBlock + tid;
+    if (r < M) {
+      const int32_t a = row_ptr[r], b = row_ptr[r + 1];
+      const int32_t L = b - a;
+      bad |= (L < 0) | (r == 0 && a != 0) | (r == M - 1 && b != nnz);
+      atomicAdd(&s_cnt[bin_of(L, edges)], 1);
+      my_max = max(my_max, L);
+      my_empty += (L == 0);
+    }
+  }
+  // reduce in the wave first, then one LDS atomic per wave
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    my_max = max(my_max, __shfl_xor(my_max, o, kWave));
+    my_empty += __shfl_xor(my_empty, o, kWave);
+  }
+  if (lane_id() == 0) {
+    atomicMax(&s_max, my_max);
+    atomicAdd(&s_empty, my_empty);
+  }
+  if (bad) atomicOr((unsigned long long*)&stats[kStatError], 1ull);
+  __syncthreads();
+  if (tid < edges.n_bins) counts[(int64_t)tid * gridDim.x + blockIdx.x] = s_cnt[tid];
+  if (tid == 0) {
+    wg_max[blockIdx.x] = s_max;
+    wg_empty[blockIdx.x] = s_empty;
+  }
+}
+
+// Exclusive scan, in place, of the bin-major [bin][workgroup] counts by one
+// workgroup; also reduces the longest row and the empty-row count.
+__global__ __launch_bounds__(1024) void bin_scan_kernel(
+    int32_t M, int32_t n_wg, int32_t n_bins, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ wg_max, const int32_t* __restrict__ wg_empty,
+    int64_t* __restrict__ stats) {
+  __shared__ int32_t s_wave[16];
+  __shared__ int32_t s_max[16];
+  __shared__ int64_t s_emp[16];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int64_t E = (int64_t)n_bins * n_wg;
+  const int64_t per = (E + 1023) / 1024;
+  const int64_t beg = min(E, (int64_t)tid * per), end = min(E, beg + per);
+  int32_t local = 0;
+  for (int64_t i = beg; i < end; ++i) local += counts[i];
+  int32_t v = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  if (lane == kWave - 1) s_wave[wave] = v;
+  int32_t mx = 0;
+  int64_t emp = 0;
+  for (int w = tid; w < n_wg; w += 1024) {
+    mx = max(mx, wg_max[w]);
+    emp += wg_empty[w];
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o, kWave));
+    emp += __shfl_xor(emp, o, kWave);
+  }
+  if (lane == 0) { s_max[wave] = mx; s_emp[wave] = emp; }
+  __syncthreads();
+  int32_t wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += s_wave[w];
+  int32_t run = v - local + wave_base;
+  for (int64_t i = beg; i < end; ++i) {
+    const int32_t c = counts[i];
+    counts[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t m = 0;
+    int64_t e = 0;
+    for (int w = 0; w < 16; ++w) { m = max(m, s_max[w]); e += s_emp[w]; }
+    stats[kStatMaxLen] = m;
+    stats[kStatEmpty] = e;
+    int nonempty = 0;
+    for (int b = 0; b < n_bins; ++b) {
+      const int64_t off = counts[(int64_t)b * n_wg];
+      const int64_t nxt = b + 1 < n_bins ? counts[(int64_t)(b + 1) * n_wg] : M;
+      stats[kStatBinOffset + b] = off;
+      nonempty += nxt > off;
+    }
+    stats[kStatBinOffset + n_bins] = M;
+    stats[kStatNonEmptyBins] = nonempty;
+  }
+}
+
+// Pass 2: stable scatter of row ids into their bins. Ranks inside a wave come
+// from ballots, ranks across the 4 waves and the 4 passes from LDS counters.
+__global__ __launch_bounds__(kBlock) void bin_scatter_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t M, BinEdges edges,
+    const int32_t* __restrict__ offsets, const int64_t* __restrict__ stats,
+    int32_t* __restrict__ bins) {
+  if (stats[kStatNonEmptyBins] <= 1) return;  // one bin: ids are the identity
+  __shared__ int32_t s_base[kMaxBins];
+  __shared__ int32_t s_wcnt[kWavesPerBlock][kMaxBins];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  if (tid < edges.n_bins) s_base[tid] = offsets[(int64_t)tid * gridDim.x + blockIdx.x];
+  __syncthreads();
+  const int64_t first = (int64_t)blockIdx.x * kBinRowsPerBlock;
+  for (int pass = 0; pass < kBinRowsPerBlock / kBlock; ++pass) {
+    const int64_t r = first + pass * kBlock + tid;
+    const bool valid = r < M;
+    const int bin = valid ? bin_of((int64_t)row_ptr[r + 1] - row_ptr[r], edges) : -1;
+    int rank = 0;
+    for (int b = 0; b < edges.n_bins; ++b) {
+      const uint64_t mask = __ballot(bin == b);
+      if (bin == b) rank = lanes_below(mask);
+      if (lane == 0) s_wcnt[wave][b] = __popcll(mask);
+    }
+    __syncthreads();
+    if (valid) {
+      int pos = s_base[bin] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][bin];
+      bins[pos] = (int32_t)r;
+    }
+    __syncthreads();
+    if (tid < edges.n_bins) {
+      int add = 0;
+      for (int w = 0; w < kWavesPerBlock; ++w) add += s_wcnt[w][tid];
+      s_base[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
+// Split coordinates of every partition boundary p: at diagonal
+// d = min(p*T, M+nnz), rows_ended = max{ i : row_ptr[i] + i <= d } and
+// nonzeros = d - rows_ended.
+__global__ __launch_bounds__(kBlock) void split_search_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int32_t T, int32_t P,
+    int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p > P) return;
+  const int64_t W = (int64_t)M + nnz;
+  const int64_t d = min(p * T, W);
+  int64_t lo = max((int64_t)0, d - nnz), hi = min(d, (int64_t)M);
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)row_ptr[mid] + mid <= d) lo = mid; else hi = mid - 1;
+  }
+  split_row[p] = (int32_t)lo;
+  split_nz[p] = (int32_t)(d - lo);
+}
+
+__global__ __launch_bounds__(kBlock) void check_columns_kernel(
+    const int32_t* __restrict__ col_idx, int64_t nnz, int64_t N, int64_t* stats) {
+  bool bad = false;
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
+       k += (int64_t)gridDim.x * kBlock) {
+    const int32_t c = col_idx[k];
+    bad |= (c < 0) | ((int64_t)c >= N);
+  }
+  if (bad) atomicOr((unsigned long long*)&stats[kStatError], 2ull);
+}
+
+int n_blocks(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_clear_stats(int64_t* stats, hipStream_t s) {
+  hipLaunchKernelGGL(clear_stats_kernel, dim3(1), dim3(64), 0, s, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bin_count(const int32_t* row_ptr, int64_t M, int64_t nnz,
+                            const BinEdges& edges, int32_t* counts, int32_t* wg_max,
+                            int32_t* wg_empty, int64_t* stats, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(bin_count_kernel, dim3(n_blocks(M, kBinRowsPerBlock)), dim3(kBlock), 0, s,
+                     row_ptr, (int32_t)M, (int32_t)nnz, edges, counts, wg_max, wg_empty, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bin_scan(int64_t M, const BinEdges& edges, int32_t* counts,
+                           const int32_t* wg_max, const int32_t* wg_empty, int64_t* stats,
+                           hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(1024), 0, s, (int32_t)M,
+                     n_blocks(M, kBinRowsPerBlock), edges.n_bins, counts, wg_max, wg_empty,
+                     stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges& edges,
+                              const int32_t* offsets, const int64_t* stats, int32_t* bins,
+                              hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(bin_scatter_kernel, dim3(n_blocks(M, kBinRowsPerBlock)), dim3(kBlock), 0,
+                     s, row_ptr, (int32_t)M, edges, offsets, stats, bins);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
+                               int64_t P, int32_t* split_row, int32_t* split_nz,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(split_search_kernel, dim3(n_blocks(P + 1, kBlock)), dim3(kBlock), 0, s,
+                     row_ptr, (int32_t)M, (int32_t)nnz, T, (int32_t)P, split_row, split_nz);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
+                                int64_t* stats, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(n_blocks(nnz, kBlock), 8192);
+  hipLaunchKernelGGL(check_columns_kernel, dim3(blocks), dim3(kBlock), 0, s, col_idx, nnz, N,
+                     stats);
+  return hipGetLastError();
+}
+
+}  // namespace spmv

@@ -1,0 +1,71 @@
+"""Helpers for the GPU tests: move a workload to the device, run the C ABI
+through the binding, compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import load_balanced_csr_amd as lb
+
+# (strategy, items_per_thread, bins) variants every parity case runs through
+VARIANTS = {
+    "merge4": ("merge", 4, None),
+    "merge8": ("merge", 8, None),
+    "merge16": ("merge", 16, None),
+    "binned": ("binned", 0, None),
+    # other bin edges: correctness must not depend on them
+    "binned_alt": ("binned", 0, [(1, 1), (6, 4), (40, 16), (900, 64), (None, 256)]),
+    "binned_one": ("binned", 0, [(None, 8)]),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+class DevMatrix:
+    def __init__(self, row_ptr, col_idx, values, M, N):
+        self.M, self.N = M, N
+        self.row_ptr_h, self.col_h, self.val_h = row_ptr, col_idx, values
+        self.rp, self.col, self.val = dev(row_ptr), dev(col_idx), dev(values)
+
+    @classmethod
+    def of(cls, w):
+        return cls(w.row_ptr, w.col_idx, w.values, w.M, w.N)
+
+    def plan(self, variant="merge8", **kw):
+        strategy, ipt, bins = VARIANTS[variant] if variant else ("auto", 0, None)
+        return lb.Plan(self.rp, self.col, self.val, (self.M, self.N), strategy=strategy,
+                       items_per_thread=ipt, bins=bins, **kw)
+
+
+def run(plan, x_h, alpha, beta, y0_h=None, dtype=np.float32):
+    """One exec; y starts as y0 (beta != 0) or NaN (beta == 0, must not be read)."""
+    x = dev(x_h)
+    M = plan.M
+    if beta != 0.0:
+        y = dev(y0_h)
+    else:
+        y = torch.full((M,), float("nan"), dtype=torch.float32 if dtype == np.float32
+                       else torch.float64, device="cuda")
+    plan(x, y, alpha, beta)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check(y, row_ptr, col_idx, values, x, alpha, beta, y0=None, what=""):
+    ref, scale = oracle.spmv(row_ptr, col_idx, values, x, alpha, beta, y0)
+    ok, worst, idx = oracle.within_tolerance(y, ref, scale, alpha, beta, y0, row_ptr=row_ptr)
+    if not ok:
+        L = int(row_ptr[idx + 1] - row_ptr[idx]) if idx >= 0 else -1
+        raise AssertionError("%s: row %d (len %d) y=%r ref=%r scale=%r worst=%.3g" %
+                             (what, idx, L, y[idx], ref[idx], scale[idx], worst))
+    return worst

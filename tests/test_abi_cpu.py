@@ -1,0 +1,92 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+arguments before touching the device (CPU only: no GPU call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import load_balanced_csr_amd as lb
+from load_balanced_csr_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "spmv.h")).read()
+    return sorted(set(re.findall(r"SPMV_API\s+[\w\s\*]+?\b(spmv_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lb.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s, text in [(0, "success"), (1, "invalid argument"), (5, "invalid plan handle"),
+                    (6, "malformed CSR matrix")]:
+        assert lb.spmv_status_string(s) == text
+
+
+def _plan_raw(M, N, nnz, rp=0x1000, col=0x2000, val=0x3000, dtype=0, out=True):
+    lib = lb.load()
+    h = ctypes.c_void_p(0xdead)
+    st = lib.spmv_plan(ctypes.byref(h) if out else None, M, N, nnz, rp, col, val, dtype, None)
+    return st, h.value
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1, N=5, nnz=0), 1),
+    (dict(M=5, N=-1, nnz=0), 1),
+    (dict(M=5, N=5, nnz=-3), 1),
+    (dict(M=5, N=5, nnz=3, dtype=7), 1),
+    (dict(M=5, N=5, nnz=3, rp=None), 1),
+    (dict(M=5, N=5, nnz=3, col=None), 1),
+    (dict(M=5, N=5, nnz=3, val=None), 1),
+    (dict(M=0, N=5, nnz=3), 1),
+    (dict(M=5, N=0, nnz=3), 1),
+    (dict(M=5, N=5, nnz=3, out=False), 1),
+    (dict(M=2 ** 31, N=5, nnz=3), 2),
+    (dict(M=2 ** 30, N=5, nnz=2 ** 30 + 5), 2),
+])
+def test_plan_rejects_bad_arguments(args, status):
+    st, h = _plan_raw(**args)
+    assert st == status, lb.spmv_last_error()
+    if args.get("out", True):
+        assert h is None  # *out set to NULL on failure
+
+
+def test_plan_alloc_failure_is_reported(monkeypatch):
+    monkeypatch.setenv("SPMV_TEST_FAIL_ALLOC", "1")
+    st, h = _plan_raw(M=10, N=10, nnz=20)
+    assert st == 3 and h is None
+    assert "SPMV_TEST_FAIL_ALLOC" in lb.spmv_last_error()
+
+
+def test_bad_options_rejected():
+    lib = lb.load()
+    h = ctypes.c_void_p()
+    for kw in (dict(items_per_thread=5), dict(strategy="merge", bins=[(4, 3), (0, 64)]),
+               dict(bins=[(8, 1), (4, 2), (0, 64)])):
+        o = lb.make_options(**kw)
+        st = lib.spmv_plan_ex(ctypes.byref(h), 10, 10, 20, 0x1000, 0x2000, 0x3000, 0,
+                              ctypes.byref(o), None)
+        assert st == 1, kw
+
+
+def test_exec_and_destroy_reject_foreign_handles():
+    lib = lb.load()
+    assert lib.spmv_exec(None, 0x10, 0x20, 1.0, 0.0, None) == 5
+    assert lib.spmv_exec(0x12345678, 0x10, 0x20, 1.0, 0.0, None) == 5
+    assert lib.spmv_destroy(0x12345678) == 5
+    assert lib.spmv_destroy(None) == 0
+    info = binding.PlanInfo()
+    assert lib.spmv_plan_info(0x12345678, ctypes.byref(info)) == 5
+    with pytest.raises(lb.SpmvError) as e:
+        lb.spmv_plan_info(0x12345678)
+    assert e.value.status == 5
