@@ -88,6 +88,13 @@ typedef struct spmv_plan_options {
   int32_t n_bins;             /* 1..SPMV_MAX_BINS; 0 = default bins */
   int32_t validate_columns;   /* 1: also check 0 <= col_idx < N at plan time
                                  (one pass over col_idx); env SPMV_VALIDATE=1 */
+  int32_t merge_reduce;       /* how a merge-path partition sums its rows:
+                                 0 auto, 1 walk (exact merge-path split, per-lane
+                                 walk, carries + fix-up), 2 stream (only when every
+                                 row has <= T/4 entries: partitions end at row
+                                 starts, no carries) */
+  int32_t stream_lanes;       /* stream reduction: lanes per row, 1..64 power
+                                 of two; 0 = from the mean row length */
   int64_t bin_max_len[SPMV_MAX_BINS];
                               /* inclusive upper row length of bins 0..n_bins-2,
                                  strictly increasing; the last bin is unbounded */
@@ -103,6 +110,8 @@ typedef struct spmv_plan_info {
   int32_t items_per_thread;
   int32_t items_per_wave;     /* T */
   int64_t n_partitions;       /* P = ceil((M + nnz) / T) */
+  int32_t merge_reduce;       /* 1 walk, 2 stream */
+  int32_t stream_lanes;
   int32_t n_bins;
   int32_t bin_identity;       /* 1: every row fell in one bin, no row-id array */
   int64_t bin_max_len[SPMV_MAX_BINS];

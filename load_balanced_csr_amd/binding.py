@@ -39,6 +39,7 @@ class SpmvError(RuntimeError):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("strategy", ctypes.c_int32), ("items_per_thread", ctypes.c_int32),
                 ("n_bins", ctypes.c_int32), ("validate_columns", ctypes.c_int32),
+                ("merge_reduce", ctypes.c_int32), ("stream_lanes", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS)]
 
@@ -47,7 +48,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("nnz", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("strategy", ctypes.c_int32),
                 ("items_per_thread", ctypes.c_int32), ("items_per_wave", ctypes.c_int32),
-                ("n_partitions", ctypes.c_int64), ("n_bins", ctypes.c_int32),
+                ("n_partitions", ctypes.c_int64), ("merge_reduce", ctypes.c_int32),
+                ("stream_lanes", ctypes.c_int32), ("n_bins", ctypes.c_int32),
                 ("bin_identity", ctypes.c_int32), ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
                 ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
@@ -122,13 +124,20 @@ def _dtype_code(values: torch.Tensor) -> int:
     return SPMV_F32 if values.dtype == torch.float32 else SPMV_F64
 
 
+MERGE_REDUCE = {"auto": 0, "walk": 1, "stream": 2}
+MERGE_REDUCE_NAME = {1: "walk", 2: "stream"}
+
+
 def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
-                 validate_columns: bool = False) -> PlanOptions:
+                 validate_columns: bool = False, merge_reduce: str = "auto",
+                 stream_lanes: int = 0) -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored."""
     o = PlanOptions()
     o.strategy = STRATEGY[strategy]
     o.items_per_thread = items_per_thread
     o.validate_columns = int(bool(validate_columns))
+    o.merge_reduce = MERGE_REDUCE[merge_reduce]
+    o.stream_lanes = stream_lanes
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -187,6 +196,8 @@ def spmv_plan_info(plan: int) -> dict:
             "dtype": "f32" if info.dtype == SPMV_F32 else "f64",
             "strategy": STRATEGY_NAME[info.strategy], "items_per_thread": info.items_per_thread,
             "items_per_wave": info.items_per_wave, "n_partitions": info.n_partitions,
+            "merge_reduce": MERGE_REDUCE_NAME.get(info.merge_reduce, "none"),
+            "stream_lanes": info.stream_lanes,
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
@@ -228,12 +239,14 @@ class Plan:
 
     def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
-                 stream=None):
+                 merge_reduce: str = "auto", stream_lanes: int = 0, stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
-        if strategy != "auto" or items_per_thread or bins or validate_columns:
-            opts = make_options(strategy, items_per_thread, bins, validate_columns)
+        if (strategy != "auto" or items_per_thread or bins or validate_columns
+                or merge_reduce != "auto" or stream_lanes):
+            opts = make_options(strategy, items_per_thread, bins, validate_columns,
+                                merge_reduce, stream_lanes)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):

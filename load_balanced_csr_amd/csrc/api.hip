@@ -66,6 +66,8 @@ struct spmv_plan_st {
   int32_t ipt, T;
   int64_t P;
   int32_t xcd_remap;
+  int32_t merge_reduce;     // 1 walk, 2 stream
+  int32_t stream_lanes;
 
   BinEdges edges;
   int32_t lanes[kMaxBins];
@@ -113,6 +115,11 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
   if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 8 &&
       o->items_per_thread != 16)
     return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 8 or 16");
+  if (o->merge_reduce < 0 || o->merge_reduce > 2)
+    return fail(SPMV_ERR_INVALID_ARG, "options.merge_reduce %d unknown", o->merge_reduce);
+  if (o->stream_lanes != 0 && (o->stream_lanes < 1 || o->stream_lanes > 64 ||
+                               (o->stream_lanes & (o->stream_lanes - 1))))
+    return fail(SPMV_ERR_INVALID_ARG, "options.stream_lanes must be a power of two <= 64");
   if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
     return fail(SPMV_ERR_INVALID_ARG, "options.n_bins must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins > 0) {
@@ -177,7 +184,10 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.beta_nonzero = beta != 0.0;
     a.P = (int32_t)p->P;
     a.M = (int32_t)p->M;
+    a.nnz = (int32_t)p->nnz;
     a.xcd_remap = p->xcd_remap;
+    a.stream = p->merge_reduce == 2;
+    a.stream_lanes = p->stream_lanes;
     err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
   } else {
     BinnedArgs<V> a;
@@ -220,6 +230,9 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   if (nnz > 0 && (!col_idx || !values))
     return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
   if (M == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "M = 0 needs nnz = 0");
+  if ((reinterpret_cast<uintptr_t>(row_ptr) | reinterpret_cast<uintptr_t>(col_idx) |
+       reinterpret_cast<uintptr_t>(values)) & 15)
+    return fail(SPMV_ERR_INVALID_ARG, "row_ptr, col_idx and values must be 16-byte aligned");
   if (N == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "N = 0 needs nnz = 0");
   if (nnz > kInt32Max || M >= kInt32Max || N > kInt32Max)
     return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
@@ -344,13 +357,38 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   if ((int64_t)p->binned_blocks * kBlock > 0xffffffffll)
     return bail(fail(SPMV_ERR_UNSUPPORTED, "binned grid exceeds 2^32 work-items"));
 
+  // merge-path reduction: stream when every row fits a quarter partition
+  {
+    const bool eligible = p->max_len <= p->T / 4;
+    int req = options ? options->merge_reduce : 0;
+    if (req == 0) {
+      const char* e = std::getenv("SPMV_MERGE_REDUCE");
+      if (e && !std::strcmp(e, "walk")) req = 1;
+      else if (e && !std::strcmp(e, "stream")) req = 2;
+    }
+    if (req == 2 && !eligible)
+      return bail(fail(SPMV_ERR_INVALID_ARG,
+                       "stream reduction needs every row <= T/4 = %d entries (longest: %lld)",
+                       p->T / 4, (long long)p->max_len));
+    p->merge_reduce = req ? req : (eligible ? 2 : 1);
+    int g = options ? options->stream_lanes : 0;
+    if (g == 0) g = env_int("SPMV_STREAM_LANES", 0);
+    if (g == 0) {
+      const double avg = M > 0 ? (double)nnz / (double)M : 0.0;
+      g = 1;
+      while (g < 64 && 2.0 * g <= avg / 4.0) g *= 2;
+    }
+    if (g < 1 || g > 64 || (g & (g - 1))) g = 1;
+    p->stream_lanes = g;
+  }
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))
     std::fprintf(stderr,
-                 "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s T=%d P=%lld "
-                 "max_len=%lld empty=%lld bins=%d identity=%d ws=%zu\n",
+                 "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d T=%d "
+                 "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu\n",
                  (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
-                 p->strategy == SPMV_STRATEGY_MERGE ? "merge" : "binned", p->T,
+                 p->strategy == SPMV_STRATEGY_MERGE ? "merge" : "binned",
+                 p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->T,
                  (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
                  p->edges.n_bins, p->identity, p->ws_bytes);
   p->magic = kMagic;
@@ -423,6 +461,8 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->items_per_thread = p->ipt;
   info->items_per_wave = p->T;
   info->n_partitions = p->P;
+  info->merge_reduce = p->merge_reduce;
+  info->stream_lanes = p->stream_lanes;
   info->n_bins = p->edges.n_bins;
   info->bin_identity = p->identity;
   for (int b = 0; b < p->edges.n_bins; ++b) {

@@ -56,6 +56,192 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// 16-byte vectors for quad loads.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive values of type V (one 16-byte load for fp32, two for fp64).
+template <typename V> struct Quad;
+template <> struct Quad<float> {
+  f32x4 v;
+  __device__ __forceinline__ float operator[](int j) const { return v[j]; }
+  __device__ __forceinline__ void set(int j, float a) { v[j] = a; }
+};
+template <> struct Quad<double> {
+  f64x2 lo, hi;
+  __device__ __forceinline__ double operator[](int j) const { return j < 2 ? lo[j] : hi[j - 2]; }
+  __device__ __forceinline__ void set(int j, double a) {
+    if (j < 2) lo[j] = a; else hi[j - 2] = a;
+  }
+};
+
+// Elements [4q, 4q + 4) of a 16-byte aligned array of n elements, streamed.
+// SAFE = false: the caller guarantees 4q + 3 < n (one or two 16-byte loads).
+// SAFE = true: elements at or past n read as 0 and nothing past the array is
+// touched (element-wise loads); used only by the wave that holds the array's
+// last, partial quad, so the fast path has no per-lane branch.
+template <bool SAFE>
+__device__ __forceinline__ i32x4 load_quad(const int32_t* a, int q, int n) {
+  if (!SAFE) return ld_stream(reinterpret_cast<const i32x4*>(a) + q);
+  i32x4 r = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * q + j < n) r[j] = a[4 * q + j];
+  return r;
+}
+template <bool SAFE>
+__device__ __forceinline__ Quad<float> load_quad(const float* a, int q, int n) {
+  Quad<float> r;
+  if (!SAFE) {
+    r.v = ld_stream(reinterpret_cast<const f32x4*>(a) + q);
+  } else {
+    r.v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j < n) r.v[j] = a[4 * q + j];
+  }
+  return r;
+}
+template <bool SAFE>
+__device__ __forceinline__ Quad<double> load_quad(const double* a, int q, int n) {
+  Quad<double> r;
+  if (!SAFE) {
+    r.lo = ld_stream(reinterpret_cast<const f64x2*>(a) + 2 * q);
+    r.hi = ld_stream(reinterpret_cast<const f64x2*>(a) + 2 * q + 1);
+  } else {
+    r.lo = f64x2{0.0, 0.0};
+    r.hi = f64x2{0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j < n) r.set(j, a[4 * q + j]);
+  }
+  return r;
+}
+__device__ __forceinline__ void store_quad(float* lds, int i, const Quad<float>& v) {
+  *reinterpret_cast<f32x4*>(lds + 4 * i) = v.v;
+}
+__device__ __forceinline__ void store_quad(double* lds, int i, const Quad<double>& v) {
+  reinterpret_cast<f64x2*>(lds + 4 * i)[0] = v.lo;
+  reinterpret_cast<f64x2*>(lds + 4 * i)[1] = v.hi;
+}
+
+// Stage, with 16-byte loads, the row ends and the products of one partition:
+//   ends[4 * (q - qr0) + j] = row_ptr[4q + j] - sub     for quads [qr0, qr0 + nqr)
+//   prods[4 * (q - qn0) + j] = val[k] * x[col[k]], k = 4q + j, for [qn0, qn0 + nqn)
+// row_ptr (m elements), col and val (nnz elements) are 16-byte aligned.
+// Entries of the edge quads outside the caller's range are valid matrix
+// entries (or 0 past the end of an array), so every gather stays inside x.
+//
+// Fast path: NR row rounds and NN nonzero rounds of 64 quads each, fixed at
+// compile time, lane quads clamped into range (a clamped lane repeats the
+// last quad, which costs no extra cache lines), so the code is straight-line
+// and every load is issued before the first use.
+template <typename V, int NR, int NN>
+__device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, int qr0, int nqr,
+                                           int sub, const int32_t* __restrict__ col,
+                                           const V* __restrict__ val,
+                                           const V* __restrict__ x, int qn0, int nqn,
+                                           int32_t* ends, V* prods) {
+  const int lane = lane_id();
+  i32x4 e[NR > 0 ? NR : 1];
+  i32x4 c[NN > 0 ? NN : 1];
+  Quad<V> v[NN > 0 ? NN : 1];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) e[r] = load_quad<false>(row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
+#pragma unroll
+  for (int r = 0; r < NN; ++r) {
+    const int q = qn0 + min(lane + kWave * r, nqn - 1);
+    c[r] = load_quad<false>(col, q, 0);
+    v[r] = load_quad<false>(val, q, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < NN; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
+  // clamped lanes rewrite the last quad with the same values: unconditional
+  // stores keep the loads from being sunk into (and serialised by) branches
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    *reinterpret_cast<i32x4*>(ends + 4 * min(lane + kWave * r, nqr - 1)) = e[r] - sub;
+#pragma unroll
+  for (int r = 0; r < NN; ++r) store_quad(prods, min(lane + kWave * r, nqn - 1), v[r]);
+}
+
+// Slow path for the one partition that reaches an array's last, partial
+// quad: element-wise guarded loads, exec-masked rounds.
+template <typename V, int RQR, int RQN>
+__device__ __noinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int m, int qr0,
+                                        int nqr, int sub, const int32_t* __restrict__ col,
+                                        const V* __restrict__ val, const V* __restrict__ x,
+                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods) {
+  const int lane = lane_id();
+  for (int r = 0; r < RQR; ++r)
+    if (lane + kWave * r < nqr) {
+      const i32x4 e = load_quad<true>(row_ptr, qr0 + lane + kWave * r, m);
+      *reinterpret_cast<i32x4*>(ends + 4 * (lane + kWave * r)) = e - sub;
+    }
+  for (int r = 0; r < RQN; ++r)
+    if (lane + kWave * r < nqn) {
+      const i32x4 c = load_quad<true>(col, qn0 + lane + kWave * r, nnz);
+      Quad<V> v = load_quad<true>(val, qn0 + lane + kWave * r, nnz);
+      for (int j = 0; j < 4; ++j) v.set(j, v[j] * x[c[j]]);
+      store_quad(prods, lane + kWave * r, v);
+    }
+}
+
+template <typename V, int NR, int RQN>
+__device__ __forceinline__ void stage_dispatch_nn(const int32_t* row_ptr, int qr0, int nqr,
+                                                  int sub, const int32_t* col, const V* val,
+                                                  const V* x, int qn0, int nqn, int32_t* ends,
+                                                  V* prods) {
+  const int rounds = (nqn + kWave - 1) / kWave;
+  if (rounds == 0)
+    stage_fast<V, NR, 0>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+  else if (rounds == 1 || RQN < 2)
+    stage_fast<V, NR, 1>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+  else if (rounds == 2 || RQN < 3)
+    stage_fast<V, NR, (RQN < 2 ? 1 : 2)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods);
+  else if (rounds == 3 || RQN < 4)
+    stage_fast<V, NR, (RQN < 3 ? 1 : 3)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods);
+  else if (rounds == 4 || RQN < 5)
+    stage_fast<V, NR, (RQN < 4 ? 1 : 4)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods);
+  else if (rounds == 5 || RQN < 6)
+    stage_fast<V, NR, (RQN < 5 ? 1 : 5)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods);
+  else
+    stage_fast<V, NR, (RQN < 6 ? 1 : 6)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods);
+}
+
+// Stage one partition (see stage_fast). RQR / RQN bound the rounds.
+template <typename V, int RQR, int RQN>
+__device__ __forceinline__ void stage_partition(const int32_t* __restrict__ row_ptr, int m,
+                                                int qr0, int nqr, int sub,
+                                                const int32_t* __restrict__ col,
+                                                const V* __restrict__ val,
+                                                const V* __restrict__ x, int nnz, int qn0,
+                                                int nqn, int32_t* ends, V* prods) {
+  static_assert(RQN <= 6, "at most 6 nonzero rounds");
+  // does this partition reach an array's last, partial quad? (wave-uniform)
+  const bool tail = (nqr > 0 && (m & 3) && qr0 + nqr - 1 == (m - 1) >> 2) ||
+                    (nqn > 0 && (nnz & 3) && qn0 + nqn - 1 == (nnz - 1) >> 2);
+  if (tail) {
+    stage_safe<V, RQR, RQN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends, prods);
+    return;
+  }
+  const int rrounds = (nqr + kWave - 1) / kWave;
+  if (rrounds == 0)
+    stage_dispatch_nn<V, 0, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+  else if (rrounds == 1 || RQR < 2)
+    stage_dispatch_nn<V, 1, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+  else
+    stage_dispatch_nn<V, RQR, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+}
+
 // Segmented inclusive scan across the wave: lanes with equal `key` that are
 // contiguous form a segment (keys must be non-decreasing across lanes).
 template <typename V>

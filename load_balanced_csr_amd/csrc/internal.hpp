@@ -64,7 +64,10 @@ struct MergeArgs {
   int32_t beta_nonzero;
   int32_t P;
   int32_t M;
+  int32_t nnz;
   int32_t xcd_remap;
+  int32_t stream;        // 1: rows never cross partitions (all rows <= T/4)
+  int32_t stream_lanes;  // lanes per row in the stream reduction
 };
 
 template <typename V>

@@ -33,8 +33,9 @@ namespace {
 template <typename V, int IPT>
 __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a) {
   constexpr int T = kWave * IPT;
-  __shared__ int32_t s_end[kWavesPerBlock][T];
-  __shared__ V s_val[kWavesPerBlock][T];
+  constexpr int RQ = (T / 4 + 2 + kWave - 1) / kWave;   // quad rounds per array
+  __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
+  __shared__ __attribute__((aligned(16))) V s_val[kWavesPerBlock][T + 8];
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -42,38 +43,25 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   const int p = blk * kWavesPerBlock + wave;
   if (p >= a.P) return;
 
-  int32_t* re = s_end[wave];   // re[k]: local nonzero offset where row r0+k ends
-  V* vb = s_val[wave];         // [0, nrows): row sums; [T - nnzc, T): products
-
   const int r0 = a.split_row[p], r1 = a.split_row[p + 1];
   const int n0 = a.split_nz[p], n1 = a.split_nz[p + 1];
   const int nrows = r1 - r0, nnzc = n1 - n0, total = nrows + nnzc;
 
-  // ---- 1. stage row ends and products -------------------------------------
-  if (nrows > 0) {
-    int32_t e[IPT];
-#pragma unroll
-    for (int m = 0; m < IPT; ++m) e[m] = a.row_ptr[r0 + 1 + min(lane + kWave * m, nrows - 1)];
-#pragma unroll
-    for (int m = 0; m < IPT; ++m)
-      if (lane + kWave * m < nrows) re[lane + kWave * m] = e[m] - n0;
-  }
-  V* prod = vb + (T - nnzc);
-  if (nnzc > 0) {
-    int32_t c[IPT];
-    V v[IPT];
-#pragma unroll
-    for (int m = 0; m < IPT; ++m) {
-      const int k = n0 + min(lane + kWave * m, nnzc - 1);
-      c[m] = ld_stream(a.col_idx + k);
-      v[m] = ld_stream(a.val + k);
-    }
-#pragma unroll
-    for (int m = 0; m < IPT; ++m) v[m] *= a.x[c[m]];
-#pragma unroll
-    for (int m = 0; m < IPT; ++m)
-      if (lane + kWave * m < nnzc) prod[lane + kWave * m] = v[m];
-  }
+  // ---- 1. stage row ends and products with 16-byte loads ---------------------
+  // re[k]: local nonzero offset where row r0+k ends (row_ptr[r0+1+k] - n0).
+  // vb holds the finished rows' sums at [0, nrows) and, at its far end, the
+  // products of the quads covering [n0, n1): nrows + nnzc <= T keeps the two
+  // regions apart.
+  const int qr0 = (r0 + 1) >> 2;
+  const int nqr = nrows > 0 ? ((r1 >> 2) - qr0 + 1) : 0;
+  const int qn0 = n0 >> 2;
+  const int nqn = nnzc > 0 ? (((n1 - 1) >> 2) - qn0 + 1) : 0;
+  int32_t* re = s_end[wave] + ((r0 + 1) & 3);
+  V* vb = s_val[wave];
+  V* prod_q = vb + (T + 8 - 4 * nqn);
+  V* prod = prod_q + (n0 & 3);
+  stage_partition<V, RQ, RQ>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x, a.nnz,
+                             qn0, nqn, s_end[wave], prod_q);
   wave_sync();
 
   // ---- 2. per-lane start by binary search, then walk IPT units --------------
@@ -125,6 +113,66 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   }
 }
 
+// Stream reduction, used when every row holds at most T/4 entries. The
+// partitions keep the merge-path row coordinate (rows ended before the
+// diagonal) but start their nonzeros at that row's start, so no row crosses a
+// partition: a partition owns rows [r0, r1) whole and nonzeros
+// [row_ptr[r0], row_ptr[r1]), at most T + T/4 of them (the row cut by the
+// diagonal moves forward entirely). There are no carries and no fix-up.
+// After staging the products in LDS, groups of G lanes each sum one row
+// (strided by G, then a butterfly), 64 / G rows per round.
+template <typename V, int IPT>
+__global__ __launch_bounds__(kBlock) void merge_stream_kernel(const MergeArgs<V> a) {
+  constexpr int T = kWave * IPT;
+  constexpr int CAP = T + T / 4;           // nonzeros one partition can hold
+  constexpr int RQN = (CAP / 4 + 2 + kWave - 1) / kWave;
+  constexpr int RQR = (T / 4 + 2 + kWave - 1) / kWave;
+  __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
+  __shared__ __attribute__((aligned(16))) V s_prod[kWavesPerBlock][CAP + 8];
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
+  const int p = blk * kWavesPerBlock + wave;
+  if (p >= a.P) return;
+  const int r0 = a.split_row[p], r1 = a.split_row[p + 1];
+  const int nrows = r1 - r0;
+  if (nrows == 0) return;
+  const int n0 = a.row_ptr[r0];
+  const int nnzc = a.row_ptr[r1] - n0;
+
+  // ---- stage row ends and products with 16-byte loads ------------------------
+  const int qr0 = (r0 + 1) >> 2;
+  const int nqr = (r1 >> 2) - qr0 + 1;
+  const int qn0 = n0 >> 2;
+  const int nqn = nnzc > 0 ? (((n0 + nnzc - 1) >> 2) - qn0 + 1) : 0;
+  int32_t* re = s_end[wave] + ((r0 + 1) & 3);  // re[k]: local end of row r0 + k
+  V* prod = s_prod[wave] + (n0 & 3);
+  stage_partition<V, RQR, RQN>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
+                               a.nnz, qn0, nqn, s_end[wave], s_prod[wave]);
+  wave_sync();
+
+  // ---- G lanes per row ---------------------------------------------------------
+  const int G = a.stream_lanes;
+  const int gl = lane & (G - 1);
+  const int rows_per_round = kWave / G;
+  const int grp = lane / G;
+  for (int base = 0; base < nrows; base += rows_per_round) {
+    const int k = base + grp;
+    V acc = V(0);
+    if (k < nrows) {
+      const int s = k > 0 ? re[k - 1] : 0, t = re[k];
+      for (int i = s + gl; i < t; i += G) acc += prod[i];
+    }
+    for (int o = G >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (k < nrows && gl == 0) {
+      V out = a.alpha * acc;
+      if (a.beta_nonzero) out = fma(a.beta, ld_stream(a.y + r0 + k), out);
+      st_stream(a.y + r0 + k, out);
+    }
+  }
+}
+
 // Adds alpha * sum(carries) to every row that partitions left open. One wave
 // handles 64 consecutive partitions; a row's carries are contiguous, so they
 // form a segment of equal keys. The wave that holds a segment's first carry
@@ -172,7 +220,10 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
 template <typename V, int IPT>
 hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
+  if (a.stream)
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -192,7 +243,7 @@ hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_
   }
   if (err != hipSuccess) return err;
   if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-  if (a.P > 1) {
+  if (a.P > 1 && !a.stream) {
     const int64_t chunks = ((int64_t)a.P + kWave - 1) / kWave;
     const int blocks = (int)((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL((merge_fixup_kernel<V>), dim3(blocks), dim3(kBlock), 0, s,

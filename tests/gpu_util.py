@@ -8,15 +8,22 @@ import torch
 import oracle
 import load_balanced_csr_amd as lb
 
-# (strategy, items_per_thread, bins) variants every parity case runs through
+# plan options of the schedule variants every parity case runs through
 VARIANTS = {
-    "merge4": ("merge", 4, None),
-    "merge8": ("merge", 8, None),
-    "merge16": ("merge", 16, None),
-    "binned": ("binned", 0, None),
+    # merge-path; the reduction is "stream" where every row fits T/4, else "walk"
+    "merge4": dict(strategy="merge", items_per_thread=4),
+    "merge8": dict(strategy="merge", items_per_thread=8),
+    "merge16": dict(strategy="merge", items_per_thread=16),
+    # merge-path with the exact split and per-lane walk on every matrix
+    "merge8_walk": dict(strategy="merge", items_per_thread=8, merge_reduce="walk"),
+    # stream reduction with other lane-group widths (ignored when walk applies)
+    "merge8_g1": dict(strategy="merge", items_per_thread=8, stream_lanes=1),
+    "merge16_g16": dict(strategy="merge", items_per_thread=16, stream_lanes=16),
+    "binned": dict(strategy="binned"),
     # other bin edges: correctness must not depend on them
-    "binned_alt": ("binned", 0, [(1, 1), (6, 4), (40, 16), (900, 64), (None, 256)]),
-    "binned_one": ("binned", 0, [(None, 8)]),
+    "binned_alt": dict(strategy="binned",
+                       bins=[(1, 1), (6, 4), (40, 16), (900, 64), (None, 256)]),
+    "binned_one": dict(strategy="binned", bins=[(None, 8)]),
 }
 
 
@@ -42,9 +49,9 @@ class DevMatrix:
         return cls(w.row_ptr, w.col_idx, w.values, w.M, w.N)
 
     def plan(self, variant="merge8", **kw):
-        strategy, ipt, bins = VARIANTS[variant] if variant else ("auto", 0, None)
-        return lb.Plan(self.rp, self.col, self.val, (self.M, self.N), strategy=strategy,
-                       items_per_thread=ipt, bins=bins, **kw)
+        opts = dict(VARIANTS[variant]) if variant else {}
+        opts.update(kw)
+        return lb.Plan(self.rp, self.col, self.val, (self.M, self.N), **opts)
 
 
 def run(plan, x_h, alpha, beta, y0_h=None, dtype=np.float32):

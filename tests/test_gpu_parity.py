@@ -129,7 +129,23 @@ def test_zero_rows_is_noop():
     plan.destroy()
 
 
-@pytest.mark.parametrize("variant", ["merge8", "binned"])
+def test_reduction_mode_choice():
+    """stream where every row fits a quarter partition, walk otherwise; a
+    forced stream on a matrix with a longer row is refused."""
+    w = synth.laplacian(n=64)
+    m = DevMatrix.of(w)
+    info = m.plan("merge8").info
+    assert info["merge_reduce"] == "stream" and info["stream_lanes"] == 1
+    assert m.plan("merge8_walk").info["merge_reduce"] == "walk"
+    w = _csr([3] * 50 + [129] + [3] * 50, 200, 3)       # 129 > 512 / 4
+    m = DevMatrix.of(w)
+    assert m.plan("merge8").info["merge_reduce"] == "walk"
+    with pytest.raises(lb.SpmvError) as e:
+        m.plan("merge8", merge_reduce="stream")
+    assert e.value.status == 1
+
+
+@pytest.mark.parametrize("variant", ["merge8", "merge8_walk", "binned"])
 def test_deterministic_and_alpha_scaling(variant):
     w = synth.powerlaw(M=40_000, max_len=20_000)
     m = DevMatrix.of(w)
@@ -203,7 +219,6 @@ def test_splits_match_oracle(ipt, golden):
 
 @pytest.mark.parametrize("variant", ["binned", "binned_alt", "binned_one"])
 def test_bins_match_oracle(variant, golden):
-    bins_opt = VARIANTS[variant][2]
     for name, rp in _split_cases(golden):
         M, nnz = rp.size - 1, int(rp[-1])
         m = DevMatrix(rp, np.zeros(nnz, np.int32), np.zeros(nnz, np.float32), M,
@@ -220,7 +235,6 @@ def test_bins_match_oracle(variant, golden):
         assert info["n_empty_rows"] == int((np.diff(rp) == 0).sum())
         assert info["bin_identity"] == (int((ocnt > 0).sum()) <= 1)
         plan.destroy()
-    del bins_opt
 
 
 def test_malformed_inputs_are_rejected():
