@@ -2,12 +2,18 @@
 """Benchmark of the CSR SpMV hot path on one MI355X.
 
 One step = one spmv_exec (y = alpha*A*x + beta*y, the whole hot path: the
-merge-path kernel and its carry fix-up, or the fused binned kernel) over the
-workload resident in HBM. Before every step a 1 GiB buffer is zero-filled on
-the same stream, which evicts L2 and the 256 MiB Infinity Cache, so every
-step reads the matrix from HBM (``--no-flush`` times warm steps instead).
-Each step's exec is bracketed by HIP events, and the dominant kernel by its
-own pair of HIP events recorded by the library on the same stream.
+merge-path kernel and, where rows cross partitions, its carry fix-up, or the
+fused binned kernel) over the workload resident in HBM. Before every step a
+1 GiB buffer is zero-filled on the same stream, which evicts L2 and the
+256 MiB Infinity Cache, so every step reads the matrix from HBM
+(``--no-flush`` times warm steps instead).
+
+Timed region: K steps, each exec bracketed by a pair of HIP events (torch
+events on the stream the library launches on) -> ``value`` and
+``ms_per_step``. A second pass of K steps records HIP events that the
+library places around its dominant kernel alone (spmv_exec_events) ->
+``roofline.achieved``; keeping them out of the first pass keeps their
+overhead out of ``value``.
 
 Prints ONE JSON line. ``value`` is GFLOP/s (2 * nnz per step) over the mean
 event-timed exec duration; ``roofline`` prices the dominant kernel against
@@ -122,6 +128,22 @@ def cpu_baseline(w, budget_s: float, y_gpu):
     return res, bool(ok), worst
 
 
+def calibrate_copy(mib: int, steps: int):
+    """A plain copy kernel of known size (torch's device copy): reads and
+    writes exactly mib MiB per launch. Under rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE its per-dispatch counter values give the factor that turns
+    those counters into bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,7 +155,12 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, args.steps)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -196,18 +223,25 @@ def main():
         if flush is not None:
             flush.zero_()
         plan(x, y, w.alpha, w.beta)
+    # timed region: K steps, events around each exec only
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
             flush.zero_()
         xb[i].record()
-        lb.spmv_exec_events(plan.handle, x, y, w.alpha, w.beta, kb[i], ke[i])
+        plan(x, y, w.alpha, w.beta)
         xe[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
     exec_ms = [xb[i].elapsed_time(xe[i]) for i in range(K)]
+
+    # second pass: the library's events around its dominant kernel
+    for i in range(K):
+        if flush is not None:
+            flush.zero_()
+        lb.spmv_exec_events(plan.handle, x, y, w.alpha, w.beta, kb[i], ke[i])
+    torch.cuda.synchronize()
     kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
     for e in kb + ke:
         hip.destroy(e)
@@ -216,7 +250,10 @@ def main():
     Bc = compulsory_bytes(w)
     gflops = 2.0 * w.nnz / (mean_exec * 1e-3) / 1e9
     gbps_exec = Bc / (mean_exec * 1e-3) / 1e9
-    kernel = "merge_spmv_kernel" if info["strategy"] == "merge" else "binned_spmv_kernel"
+    if info["strategy"] == "binned":
+        kernel = "binned_spmv_kernel"
+    else:
+        kernel = "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
     achieved = Bc / (mean_kern * 1e-3) / 1e9
 
     out = {
@@ -235,6 +272,7 @@ def main():
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
                    "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha, "beta": w.beta,
                    "seed": w.seed, "strategy": info["strategy"],
+                   "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
                    "items_per_wave": info["items_per_wave"],
                    "cache": "warm" if flush is None else "1 GiB flush before every step"},
         "achieved_GBps": round(gbps_exec, 2),
