@@ -91,10 +91,16 @@ typedef struct spmv_plan_options {
   int32_t merge_reduce;       /* how a merge-path partition sums its rows:
                                  0 auto, 1 walk (exact merge-path split, per-lane
                                  walk, carries + fix-up), 2 stream (only when every
-                                 row has <= T/4 entries: partitions end at row
+                                 row has <= T/8 entries: partitions end at row
                                  starts, no carries) */
   int32_t stream_lanes;       /* stream reduction: lanes per row, 1..64 power
                                  of two; 0 = from the mean row length */
+  int32_t x_window;           /* stream reduction: 0 auto, 1 off, 2 on. On, each
+                                 workgroup copies the span of x its entries use
+                                 into LDS when the span fits (kWindowBytes) and
+                                 gathers from there; otherwise from HBM. Needs a
+                                 16-byte aligned x at exec time (else off) */
+  int32_t pad0;
   int64_t bin_max_len[SPMV_MAX_BINS];
                               /* inclusive upper row length of bins 0..n_bins-2,
                                  strictly increasing; the last bin is unbounded */
@@ -112,6 +118,8 @@ typedef struct spmv_plan_info {
   int64_t n_partitions;       /* P = ceil((M + nnz) / T) */
   int32_t merge_reduce;       /* 1 walk, 2 stream */
   int32_t stream_lanes;
+  int32_t x_window;           /* 1 when the stream kernel uses the LDS x window */
+  int32_t pad0;
   int32_t n_bins;
   int32_t bin_identity;       /* 1: every row fell in one bin, no row-id array */
   int64_t bin_max_len[SPMV_MAX_BINS];
@@ -135,7 +143,10 @@ typedef struct spmv_plan_info {
  * Ownership: the plan borrows row_ptr, col_idx and values; they must stay
  * allocated until spmv_destroy, and row_ptr must stay unchanged (the plan's
  * partition and bins are derived from it). col_idx and values may change
- * between spmv_exec calls. The plan owns exactly one device allocation, made
+ * between spmv_exec calls (the plan samples col_idx once to choose a kernel
+ * variant; results never depend on that choice). row_ptr, col_idx and values
+ * must be 16-byte aligned (any hipMalloc allocation is), else
+ * SPMV_ERR_INVALID_ARG. The plan owns exactly one device allocation, made
  * here and freed by spmv_destroy.
  *
  * Work: row-length statistics and per-workgroup bin counts kept in LDS, an

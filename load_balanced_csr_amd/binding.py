@@ -40,6 +40,7 @@ class PlanOptions(ctypes.Structure):
     _fields_ = [("strategy", ctypes.c_int32), ("items_per_thread", ctypes.c_int32),
                 ("n_bins", ctypes.c_int32), ("validate_columns", ctypes.c_int32),
                 ("merge_reduce", ctypes.c_int32), ("stream_lanes", ctypes.c_int32),
+                ("x_window", ctypes.c_int32), ("pad0", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS)]
 
@@ -49,7 +50,8 @@ class PlanInfo(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("strategy", ctypes.c_int32),
                 ("items_per_thread", ctypes.c_int32), ("items_per_wave", ctypes.c_int32),
                 ("n_partitions", ctypes.c_int64), ("merge_reduce", ctypes.c_int32),
-                ("stream_lanes", ctypes.c_int32), ("n_bins", ctypes.c_int32),
+                ("stream_lanes", ctypes.c_int32), ("x_window", ctypes.c_int32),
+                ("pad0", ctypes.c_int32), ("n_bins", ctypes.c_int32),
                 ("bin_identity", ctypes.c_int32), ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
                 ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
@@ -130,7 +132,7 @@ MERGE_REDUCE_NAME = {1: "walk", 2: "stream"}
 
 def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
-                 stream_lanes: int = 0) -> PlanOptions:
+                 stream_lanes: int = 0, x_window: str = "auto") -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored."""
     o = PlanOptions()
     o.strategy = STRATEGY[strategy]
@@ -138,6 +140,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.validate_columns = int(bool(validate_columns))
     o.merge_reduce = MERGE_REDUCE[merge_reduce]
     o.stream_lanes = stream_lanes
+    o.x_window = {"auto": 0, "off": 1, "on": 2}[x_window]
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -197,7 +200,7 @@ def spmv_plan_info(plan: int) -> dict:
             "strategy": STRATEGY_NAME[info.strategy], "items_per_thread": info.items_per_thread,
             "items_per_wave": info.items_per_wave, "n_partitions": info.n_partitions,
             "merge_reduce": MERGE_REDUCE_NAME.get(info.merge_reduce, "none"),
-            "stream_lanes": info.stream_lanes,
+            "stream_lanes": info.stream_lanes, "x_window": bool(info.x_window),
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
@@ -239,14 +242,15 @@ class Plan:
 
     def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
-                 merge_reduce: str = "auto", stream_lanes: int = 0, stream=None):
+                 merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
+                 stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
-                or merge_reduce != "auto" or stream_lanes):
+                or merge_reduce != "auto" or stream_lanes or x_window != "auto"):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
-                                merge_reduce, stream_lanes)
+                                merge_reduce, stream_lanes, x_window)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):

@@ -68,6 +68,7 @@ struct spmv_plan_st {
   int32_t xcd_remap;
   int32_t merge_reduce;     // 1 walk, 2 stream
   int32_t stream_lanes;
+  int32_t x_window;
 
   BinEdges edges;
   int32_t lanes[kMaxBins];
@@ -86,9 +87,11 @@ struct spmv_plan_st {
   int32_t* wg_empty;
   int32_t* split_row;
   int32_t* split_nz;
+  int32_t* row_bounds;
   int32_t* carry_row;
   void* carry_val;
   int32_t* bins;
+  int32_t* win_span;
 };
 
 namespace {
@@ -115,6 +118,8 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
   if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 8 &&
       o->items_per_thread != 16)
     return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 8 or 16");
+  if (o->x_window < 0 || o->x_window > 2)
+    return fail(SPMV_ERR_INVALID_ARG, "options.x_window %d unknown", o->x_window);
   if (o->merge_reduce < 0 || o->merge_reduce > 2)
     return fail(SPMV_ERR_INVALID_ARG, "options.merge_reduce %d unknown", o->merge_reduce);
   if (o->stream_lanes != 0 && (o->stream_lanes < 1 || o->stream_lanes > 64 ||
@@ -177,6 +182,7 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.y = static_cast<V*>(y);
     a.split_row = p->split_row;
     a.split_nz = p->split_nz;
+    a.row_bounds = p->row_bounds;
     a.carry_row = p->carry_row;
     a.carry_val = static_cast<V*>(p->carry_val);
     a.alpha = (V)alpha;
@@ -188,6 +194,9 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.xcd_remap = p->xcd_remap;
     a.stream = p->merge_reduce == 2;
     a.stream_lanes = p->stream_lanes;
+    // the window's 16-byte direct-to-LDS loads need a 16-byte aligned x
+    a.x_window = p->x_window && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    a.win_span = p->win_span;
     err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
   } else {
     BinnedArgs<V> a;
@@ -285,9 +294,11 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   const size_t o_wgemp = take(sizeof(int32_t) * n_wg);
   const size_t o_srow = take(sizeof(int32_t) * (p->P + 1));
   const size_t o_snz = take(sizeof(int32_t) * (p->P + 1));
+  const size_t o_rb = take(sizeof(int32_t) * 2 * (p->P + 1));
   const size_t o_crow = take(sizeof(int32_t) * p->P);
   const size_t o_cval = take(vs * p->P);
   const size_t o_bins = take(sizeof(int32_t) * M);
+  const size_t o_wins = take(sizeof(int32_t) * 2 * ((p->P + kWavesPerBlock - 1) / kWavesPerBlock));
   p->ws_bytes = off;
   if (env_int("SPMV_TEST_FAIL_ALLOC", 0)) {
     delete p;
@@ -306,9 +317,11 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   p->wg_empty = reinterpret_cast<int32_t*>(base + o_wgemp);
   p->split_row = reinterpret_cast<int32_t*>(base + o_srow);
   p->split_nz = reinterpret_cast<int32_t*>(base + o_snz);
+  p->row_bounds = reinterpret_cast<int32_t*>(base + o_rb);
   p->carry_row = reinterpret_cast<int32_t*>(base + o_crow);
   p->carry_val = base + o_cval;
   p->bins = reinterpret_cast<int32_t*>(base + o_bins);
+  p->win_span = reinterpret_cast<int32_t*>(base + o_wins);
 
   // ---- planning kernels, one read-back, one synchronisation ---------------------
   int64_t host_stats[kStatCount] = {0};
@@ -330,8 +343,13 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
       hipSuccess)
     return bail(hip_fail(err, "plan: bin scatter"));
   if (p->P > 0 && (err = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row,
-                                             p->split_nz, stream)) != hipSuccess)
+                                             p->split_nz, p->row_bounds, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: split search"));
+  if (p->P > 0 && nnz > 0 &&
+      (err = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
+                                 p->win_span, p->stats, stream)) !=
+          hipSuccess)
+    return bail(hip_fail(err, "plan: window spans"));
   if (validate_cols &&
       (err = launch_check_columns(col_idx, nnz, N, p->stats, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: column check"));
@@ -357,9 +375,9 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   if ((int64_t)p->binned_blocks * kBlock > 0xffffffffll)
     return bail(fail(SPMV_ERR_UNSUPPORTED, "binned grid exceeds 2^32 work-items"));
 
-  // merge-path reduction: stream when every row fits a quarter partition
+  // merge-path reduction: stream when every row fits an eighth of a partition
   {
-    const bool eligible = p->max_len <= p->T / 4;
+    const bool eligible = p->max_len <= p->T / 8;
     int req = options ? options->merge_reduce : 0;
     if (req == 0) {
       const char* e = std::getenv("SPMV_MERGE_REDUCE");
@@ -368,8 +386,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     }
     if (req == 2 && !eligible)
       return bail(fail(SPMV_ERR_INVALID_ARG,
-                       "stream reduction needs every row <= T/4 = %d entries (longest: %lld)",
-                       p->T / 4, (long long)p->max_len));
+                       "stream reduction needs every row <= T/8 = %d entries (longest: %lld)",
+                       p->T / 8, (long long)p->max_len));
     p->merge_reduce = req ? req : (eligible ? 2 : 1);
     int g = options ? options->stream_lanes : 0;
     if (g == 0) g = env_int("SPMV_STREAM_LANES", 0);
@@ -380,15 +398,25 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     }
     if (g < 1 || g > 64 || (g & (g - 1))) g = 1;
     p->stream_lanes = g;
+    // x window: where at least half of the stream workgroups' column spans fit
+    int xw = options ? options->x_window : 0;
+    if (xw == 0) {
+      const int e = env_int("SPMV_X_WINDOW", -1);
+      if (e == 0) xw = 1;
+      else if (e == 1) xw = 2;
+    }
+    const bool fits = host_stats[kStatWindowSamples] > 0 &&
+                      2 * host_stats[kStatWindowFits] >= host_stats[kStatWindowSamples];
+    p->x_window = p->merge_reduce == 2 && (xw == 2 || (xw == 0 && fits));
   }
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))
     std::fprintf(stderr,
-                 "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d T=%d "
+                 "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d xwin=%d T=%d "
                  "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu\n",
                  (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
                  p->strategy == SPMV_STRATEGY_MERGE ? "merge" : "binned",
-                 p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->T,
+                 p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->x_window, p->T,
                  (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
                  p->edges.n_bins, p->identity, p->ws_bytes);
   p->magic = kMagic;
@@ -463,6 +491,7 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->n_partitions = p->P;
   info->merge_reduce = p->merge_reduce;
   info->stream_lanes = p->stream_lanes;
+  info->x_window = p->x_window;
   info->n_bins = p->edges.n_bins;
   info->bin_identity = p->identity;
   for (int b = 0; b < p->edges.n_bins; ++b) {

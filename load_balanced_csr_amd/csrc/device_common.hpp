@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <limits.h>
+
 #include "internal.hpp"
 
 namespace spmv {
@@ -20,6 +22,23 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// gfx950 direct-to-LDS load: this lane's 16 bytes at g land at
+// lds_wave_base + 16 * lane (lds_wave_base must be wave-uniform). The load is
+// counted by vmcnt like any vector load; the compiler does not track the LDS
+// write, so readers wait with wait_vmem() and a barrier. (The builtin exists
+// only for the device target; the host pass never runs this code.)
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+}
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -58,6 +77,7 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
 
 // 16-byte vectors for quad loads.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 
@@ -137,12 +157,45 @@ __device__ __forceinline__ void store_quad(double* lds, int i, const Quad<double
 // compile time, lane quads clamped into range (a clamped lane repeats the
 // last quad, which costs no extra cache lines), so the code is straight-line
 // and every load is issued before the first use.
-template <typename V, int NR, int NN>
+// Optional x window shared by the 4 waves of a workgroup. The plan records,
+// per workgroup, the span [lo, lo + len) of the columns its entries use
+// (len = 0 when the span does not fit kWindowBytes). At kernel start every
+// thread issues its share of the coalesced loads of x[lo, lo + len) together
+// with its partition's own loads; the values go to LDS, one __syncthreads(),
+// and the gathers read LDS. A random 64-lane global gather costs about one L1
+// line lookup per lane; an LDS gather a few bank cycles. A lane whose column
+// falls outside the recorded span (col_idx changed after planning) makes its
+// wave gather from HBM instead, so results never depend on the window.
+template <typename V>
+struct XWindow {
+  static constexpr int kCap = kWindowBytes / sizeof(V);
+  static constexpr int kIters = kCap / kBlock;
+  V* lds;        // kCap entries
+  int lo, len;   // block-uniform
+  V t[kIters];   // this thread's share, in flight until commit()
+
+  __device__ __forceinline__ void issue(const V* __restrict__ x) {
+    if (len > 0) {
+#pragma unroll
+      for (int j = 0; j < kIters; ++j) t[j] = x[lo + min((int)threadIdx.x + kBlock * j, len - 1)];
+    }
+  }
+  // every thread of the block calls this exactly once
+  __device__ __forceinline__ void commit() {
+    if (len > 0) {
+#pragma unroll
+      for (int j = 0; j < kIters; ++j) lds[min((int)threadIdx.x + kBlock * j, len - 1)] = t[j];
+    }
+    __syncthreads();
+  }
+};
+
+template <typename V, int NR, int NN, bool WIN>
 __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, int qr0, int nqr,
                                            int sub, const int32_t* __restrict__ col,
                                            const V* __restrict__ val,
                                            const V* __restrict__ x, int qn0, int nqn,
-                                           int32_t* ends, V* prods) {
+                                           int32_t* ends, V* prods, XWindow<V>& w) {
   const int lane = lane_id();
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
@@ -155,10 +208,27 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
     c[r] = load_quad<false>(col, q, 0);
     v[r] = load_quad<false>(val, q, 0);
   }
+  bool from_lds = false;
+  if (WIN) {
+    w.commit();
+    bool inside = true;
 #pragma unroll
-  for (int r = 0; r < NN; ++r)
+    for (int r = 0; r < NN; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
+      for (int j = 0; j < 4; ++j) inside &= (unsigned)(c[r][j] - w.lo) < (unsigned)w.len;
+    from_lds = __ballot(!inside) == 0;
+  }
+  if (from_lds) {
+#pragma unroll
+    for (int r = 0; r < NN; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * w.lds[c[r][j] - w.lo]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < NN; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
+  }
   // clamped lanes rewrite the last quad with the same values: unconditional
   // stores keep the loads from being sunk into (and serialised by) branches
 #pragma unroll
@@ -170,12 +240,14 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
 
 // Slow path for the one partition that reaches an array's last, partial
 // quad: element-wise guarded loads, exec-masked rounds.
-template <typename V, int RQR, int RQN>
-__device__ __noinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int m, int qr0,
+template <typename V, int RQR, int RQN, bool WIN>
+__device__ __forceinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int m, int qr0,
                                         int nqr, int sub, const int32_t* __restrict__ col,
                                         const V* __restrict__ val, const V* __restrict__ x,
-                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods) {
+                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods,
+                                        XWindow<V>& w) {
   const int lane = lane_id();
+  if (WIN) w.commit();  // joins the block's barrier; this wave gathers from HBM
   for (int r = 0; r < RQR; ++r)
     if (lane + kWave * r < nqr) {
       const i32x4 e = load_quad<true>(row_ptr, qr0 + lane + kWave * r, m);
@@ -190,56 +262,61 @@ __device__ __noinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int
     }
 }
 
-template <typename V, int NR, int RQN>
+template <typename V, int NR, int RQN, bool WIN>
 __device__ __forceinline__ void stage_dispatch_nn(const int32_t* row_ptr, int qr0, int nqr,
                                                   int sub, const int32_t* col, const V* val,
                                                   const V* x, int qn0, int nqn, int32_t* ends,
-                                                  V* prods) {
+                                                  V* prods, XWindow<V>& w) {
   const int rounds = (nqn + kWave - 1) / kWave;
   if (rounds == 0)
-    stage_fast<V, NR, 0>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, 0, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, w);
   else if (rounds == 1 || RQN < 2)
-    stage_fast<V, NR, 1>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, 1, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, w);
   else if (rounds == 2 || RQN < 3)
-    stage_fast<V, NR, (RQN < 2 ? 1 : 2)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods);
+    stage_fast<V, NR, (RQN < 2 ? 1 : 2), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods, w);
   else if (rounds == 3 || RQN < 4)
-    stage_fast<V, NR, (RQN < 3 ? 1 : 3)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods);
+    stage_fast<V, NR, (RQN < 3 ? 1 : 3), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods, w);
   else if (rounds == 4 || RQN < 5)
-    stage_fast<V, NR, (RQN < 4 ? 1 : 4)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods);
+    stage_fast<V, NR, (RQN < 4 ? 1 : 4), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods, w);
   else if (rounds == 5 || RQN < 6)
-    stage_fast<V, NR, (RQN < 5 ? 1 : 5)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods);
+    stage_fast<V, NR, (RQN < 5 ? 1 : 5), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods, w);
   else
-    stage_fast<V, NR, (RQN < 6 ? 1 : 6)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods);
+    stage_fast<V, NR, (RQN < 6 ? 1 : 6), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                         prods, w);
 }
 
 // Stage one partition (see stage_fast). RQR / RQN bound the rounds.
-template <typename V, int RQR, int RQN>
+template <typename V, int RQR, int RQN, bool WIN>
 __device__ __forceinline__ void stage_partition(const int32_t* __restrict__ row_ptr, int m,
                                                 int qr0, int nqr, int sub,
                                                 const int32_t* __restrict__ col,
                                                 const V* __restrict__ val,
                                                 const V* __restrict__ x, int nnz, int qn0,
-                                                int nqn, int32_t* ends, V* prods) {
+                                                int nqn, int32_t* ends, V* prods,
+                                                XWindow<V>& w) {
   static_assert(RQN <= 6, "at most 6 nonzero rounds");
   // does this partition reach an array's last, partial quad? (wave-uniform)
   const bool tail = (nqr > 0 && (m & 3) && qr0 + nqr - 1 == (m - 1) >> 2) ||
                     (nqn > 0 && (nnz & 3) && qn0 + nqn - 1 == (nnz - 1) >> 2);
   if (tail) {
-    stage_safe<V, RQR, RQN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends, prods);
+    stage_safe<V, RQR, RQN, WIN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends,
+                                 prods, w);
     return;
   }
   const int rrounds = (nqr + kWave - 1) / kWave;
   if (rrounds == 0)
-    stage_dispatch_nn<V, 0, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, 0, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                      prods, w);
   else if (rrounds == 1 || RQR < 2)
-    stage_dispatch_nn<V, 1, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, 1, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                      prods, w);
   else
-    stage_dispatch_nn<V, RQR, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, RQR, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
+                                        prods, w);
 }
 
 // Segmented inclusive scan across the wave: lanes with equal `key` that are

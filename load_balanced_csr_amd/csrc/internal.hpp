@@ -13,6 +13,7 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
 constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
+constexpr int kWindowBytes = 12288;      // LDS x window of a stream workgroup
 
 // Layout of the statistics block the plan copies back to the host (int64).
 enum StatSlot : int {
@@ -20,7 +21,9 @@ enum StatSlot : int {
   kStatEmpty = 1,
   kStatError = 2,          // bit 0: row_ptr malformed, bit 1: column out of range
   kStatNonEmptyBins = 3,
-  kStatBinOffset = 4,      // kMaxBins + 1 entries
+  kStatWindowFits = 4,     // stream workgroups whose columns fit the x window
+  kStatWindowSamples = 5,  // stream workgroups examined
+  kStatBinOffset = 6,      // kMaxBins + 1 entries
   kStatCount = kStatBinOffset + kMaxBins + 1
 };
 
@@ -42,10 +45,23 @@ hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges&
                               int32_t* bins, hipStream_t s);
 hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
                                int64_t P, int32_t* split_row, int32_t* split_nz,
+                               int32_t* row_bounds, hipStream_t s);
+hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
+                                int64_t* stats, hipStream_t s);
+hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
+hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
+                               int32_t elem_bytes, int32_t* win_span, int64_t* stats,
                                hipStream_t s);
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
+hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* split_row, int64_t P, int32_t cap,
+                               int32_t* win_span, hipStream_t s);
+hipError_t launch_window_sample(const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* split_row, int64_t P, int32_t cap,
+                                int64_t* stats, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>
@@ -57,6 +73,7 @@ struct MergeArgs {
   V* y;
   const int32_t* split_row;
   const int32_t* split_nz;
+  const int32_t* row_bounds;  // per boundary p: {split_row[p], row_ptr[split_row[p]]}
   int32_t* carry_row;
   V* carry_val;
   V alpha;
@@ -66,8 +83,10 @@ struct MergeArgs {
   int32_t M;
   int32_t nnz;
   int32_t xcd_remap;
-  int32_t stream;        // 1: rows never cross partitions (all rows <= T/4)
+  int32_t stream;        // 1: rows never cross partitions (all rows <= T/8)
   int32_t stream_lanes;  // lanes per row in the stream reduction
+  int32_t x_window;      // 1: stream kernel with the workgroup's x window in LDS
+  const int32_t* win_span;  // per stream workgroup: first column, span (0: no window)
 };
 
 template <typename V>

@@ -60,8 +60,10 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   V* vb = s_val[wave];
   V* prod_q = vb + (T + 8 - 4 * nqn);
   V* prod = prod_q + (n0 & 3);
-  stage_partition<V, RQ, RQ>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x, a.nnz,
-                             qn0, nqn, s_end[wave], prod_q);
+  XWindow<V> nowin;
+  nowin.len = 0;
+  stage_partition<V, RQ, RQ, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
+                                    a.nnz, qn0, nqn, s_end[wave], prod_q, nowin);
   wave_sync();
 
   // ---- 2. per-lane start by binary search, then walk IPT units --------------
@@ -113,43 +115,168 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   }
 }
 
-// Stream reduction, used when every row holds at most T/4 entries. The
+// Stream reduction, used when every row holds at most T/8 entries. The
 // partitions keep the merge-path row coordinate (rows ended before the
 // diagonal) but start their nonzeros at that row's start, so no row crosses a
 // partition: a partition owns rows [r0, r1) whole and nonzeros
-// [row_ptr[r0], row_ptr[r1]), at most T + T/4 of them (the row cut by the
+// [row_ptr[r0], row_ptr[r1]); rows + nonzeros <= T + T/8 (the row cut by the
 // diagonal moves forward entirely). There are no carries and no fix-up.
-// After staging the products in LDS, groups of G lanes each sum one row
-// (strided by G, then a butterfly), 64 / G rows per round.
-template <typename V, int IPT>
-__global__ __launch_bounds__(kBlock) void merge_stream_kernel(const MergeArgs<V> a) {
+//
+// The kernel is bound by latency x occupancy, so it keeps one small LDS
+// buffer per wave: products at the front, row ends (int32) at the back.
+// With WIN, each workgroup first fetches the span of x its entries use
+// (recorded by the plan) straight into LDS with direct-to-LDS 16-byte loads,
+// which need no registers and overlap the partition's own loads; the gathers
+// then read LDS. Groups of G lanes sum each row (strided by G, then a
+// butterfly), 64 / G rows per round.
+template <typename V, int NR, int NN, bool WIN>
+__device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int nqr, int n0,
+                                             int qn0, int nqn, int32_t* ends, V* prods,
+                                             const V* xs, int wlo, int wlen) {
+  const int lane = lane_id();
+  i32x4 e[NR > 0 ? NR : 1];
+  i32x4 c[NN > 0 ? NN : 1];
+  Quad<V> v[NN > 0 ? NN : 1];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    e[r] = load_quad<false>(a.row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
+#pragma unroll
+  for (int r = 0; r < NN; ++r) {
+    const int q = qn0 + min(lane + kWave * r, nqn - 1);
+    c[r] = load_quad<false>(a.col_idx, q, 0);
+    v[r] = load_quad<false>(a.val, q, 0);
+  }
+  bool from_lds = false;
+  if (WIN) {
+    // the window's direct-to-LDS loads are not tracked by the compiler:
+    // wait for every load of this wave, then for the other waves
+    wait_vmem();
+    __syncthreads();
+    bool inside = wlen > 0;
+#pragma unroll
+    for (int r = 0; r < NN; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) inside &= (unsigned)(c[r][j] - wlo) < (unsigned)wlen;
+    from_lds = __ballot(!inside) == 0;
+  }
+  if (from_lds) {
+#pragma unroll
+    for (int r = 0; r < NN; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * xs[c[r][j] - wlo]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < NN; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * a.x[c[r][j]]);
+  }
+  // clamped lanes rewrite the last quad with the same values: unconditional
+  // stores keep the loads from being sunk into (and serialised by) branches
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    *reinterpret_cast<i32x4*>(ends + 4 * min(lane + kWave * r, nqr - 1)) = e[r] - n0;
+#pragma unroll
+  for (int r = 0; r < NN; ++r) store_quad(prods, min(lane + kWave * r, nqn - 1), v[r]);
+}
+
+template <typename V, int NR, int RQN, bool WIN>
+__device__ __forceinline__ void stream_stage_nn(const MergeArgs<V>& a, int qr0, int nqr, int n0,
+                                                int qn0, int nqn, int32_t* ends, V* prods,
+                                                const V* xs, int wlo, int wlen) {
+  const int rounds = (nqn + kWave - 1) / kWave;
+  if (rounds == 0)
+    stream_stage<V, NR, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo, wlen);
+  else if (rounds == 1 || RQN < 2)
+    stream_stage<V, NR, (RQN < 1 ? 0 : 1), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
+                                               wlen);
+  else if (rounds == 2 || RQN < 3)
+    stream_stage<V, NR, 2, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo, wlen);
+  else if (rounds == 3 || RQN < 4)
+    stream_stage<V, NR, (RQN < 3 ? 2 : 3), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
+                                               wlen);
+  else if (rounds == 4 || RQN < 5)
+    stream_stage<V, NR, (RQN < 4 ? 2 : 4), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
+                                               wlen);
+  else
+    stream_stage<V, NR, (RQN < 5 ? 2 : 5), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
+                                               wlen);
+}
+
+// (second launch bound: at least 8 waves per SIMD, i.e. at most 64 VGPRs)
+template <typename V, int IPT, bool WIN>
+__global__ __launch_bounds__(kBlock, 8) void merge_stream_kernel(const MergeArgs<V> a) {
   constexpr int T = kWave * IPT;
-  constexpr int CAP = T + T / 4;           // nonzeros one partition can hold
+  constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
+  constexpr int BUF = CAP + 16;             // per-wave buffer, elements of V
   constexpr int RQN = (CAP / 4 + 2 + kWave - 1) / kWave;
   constexpr int RQR = (T / 4 + 2 + kWave - 1) / kWave;
-  __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
-  __shared__ __attribute__((aligned(16))) V s_prod[kWavesPerBlock][CAP + 8];
+  constexpr int WCHUNKS = kWindowBytes / 16;  // 16-byte chunks of the x window
+  constexpr int E = 16 / sizeof(V);           // elements per chunk
+  static_assert(RQN <= 5, "at most 5 nonzero rounds");
+  __shared__ __attribute__((aligned(16))) V s_buf[kWavesPerBlock][BUF];
+  __shared__ __attribute__((aligned(16))) V s_x[WIN ? WCHUNKS * E : E];
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
   const int p = blk * kWavesPerBlock + wave;
-  if (p >= a.P) return;
-  const int r0 = a.split_row[p], r1 = a.split_row[p + 1];
+  // one descriptor read: {r0, row_ptr[r0]} and {r1, row_ptr[r1]}
+  int r0 = 0, r1 = 0, n0 = 0, n1 = 0;
+  if (p < a.P) {
+    const i32x2 b0 = reinterpret_cast<const i32x2*>(a.row_bounds)[p];
+    const i32x2 b1 = reinterpret_cast<const i32x2*>(a.row_bounds)[p + 1];
+    r0 = b0[0];
+    n0 = b0[1];
+    r1 = b1[0];
+    n1 = b1[1];
+  }
   const int nrows = r1 - r0;
-  if (nrows == 0) return;
-  const int n0 = a.row_ptr[r0];
-  const int nnzc = a.row_ptr[r1] - n0;
+  // with the window every wave must reach the block's barrier
+  if (!WIN && nrows == 0) return;
 
-  // ---- stage row ends and products with 16-byte loads ------------------------
+  int wlo = 0, wlen = 0;
+  if (WIN) {
+    // x[wlo, wlo + wlen): chunk aligned and inside x (the plan guarantees it)
+    wlo = a.win_span[2 * blk];
+    wlen = a.win_span[2 * blk + 1];
+    const int nch = wlen / E;
+#pragma unroll
+    for (int r = 0; r < (WCHUNKS + kBlock - 1) / kBlock; ++r) {
+      const int first = kBlock * r + kWave * wave;     // this wave's first chunk
+      if (first < nch && first + lane < nch) lds_dma16(a.x + wlo + E * (first + lane), s_x + E * first);
+    }
+  }
+
+  const int nnzc = n1 - n0;
   const int qr0 = (r0 + 1) >> 2;
-  const int nqr = (r1 >> 2) - qr0 + 1;
+  const int nqr = nrows > 0 ? (r1 >> 2) - qr0 + 1 : 0;
   const int qn0 = n0 >> 2;
   const int nqn = nnzc > 0 ? (((n0 + nnzc - 1) >> 2) - qn0 + 1) : 0;
-  int32_t* re = s_end[wave] + ((r0 + 1) & 3);  // re[k]: local end of row r0 + k
-  V* prod = s_prod[wave] + (n0 & 3);
-  stage_partition<V, RQR, RQN>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
-                               a.nnz, qn0, nqn, s_end[wave], s_prod[wave]);
+  V* buf = s_buf[wave];
+  // products of quads [qn0, qn0 + nqn) at the front, row-end quads at the back
+  int32_t* ends_q = reinterpret_cast<int32_t*>(buf + BUF) - 4 * nqr;
+  const int32_t* re = ends_q + ((r0 + 1) & 3);   // re[k]: local end of row r0 + k
+  const V* prod = buf + (n0 & 3);
+
+  const bool tail = (nqr > 0 && ((a.M + 1) & 3) && qr0 + nqr - 1 == a.M >> 2) ||
+                    (nqn > 0 && (a.nnz & 3) && qn0 + nqn - 1 == (a.nnz - 1) >> 2);
+  if (tail) {
+    if (WIN) {
+      wait_vmem();
+      __syncthreads();
+    }
+    XWindow<V> nowin;
+    nowin.len = 0;
+    stage_safe<V, RQR, RQN, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
+                                   a.nnz, qn0, nqn, ends_q, buf, nowin);
+  } else if (nqr == 0) {
+    stream_stage<V, 0, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+  } else if (nqr <= kWave || RQR < 2) {
+    stream_stage_nn<V, 1, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+  } else {
+    stream_stage_nn<V, RQR, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+  }
+  if (nrows == 0) return;
   wave_sync();
 
   // ---- G lanes per row ---------------------------------------------------------
@@ -167,8 +294,8 @@ __global__ __launch_bounds__(kBlock) void merge_stream_kernel(const MergeArgs<V>
     for (int o = G >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
     if (k < nrows && gl == 0) {
       V out = a.alpha * acc;
-      if (a.beta_nonzero) out = fma(a.beta, ld_stream(a.y + r0 + k), out);
-      st_stream(a.y + r0 + k, out);
+      if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
+      a.y[r0 + k] = out;   // cached store: L2 merges the partial lines of neighbours
     }
   }
 }
@@ -220,8 +347,10 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
 template <typename V, int IPT>
 hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (a.stream)
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
+  if (a.stream && a.x_window)
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true>), dim3(blocks), dim3(kBlock), 0, s, a);
+  else if (a.stream)
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, false>), dim3(blocks), dim3(kBlock), 0, s, a);
   else
     hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();

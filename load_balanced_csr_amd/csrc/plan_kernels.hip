@@ -20,6 +20,8 @@
 #include "device_common.hpp"
 #include "internal.hpp"
 
+#include <limits.h>
+
 namespace spmv {
 namespace {
 
@@ -185,9 +187,12 @@ __global__ __launch_bounds__(kBlock) void bin_scatter_kernel(
 // Split coordinates of every partition boundary p: at diagonal
 // d = min(p*T, M+nnz), rows_ended = max{ i : row_ptr[i] + i <= d } and
 // nonzeros = d - rows_ended.
+// Also writes, per boundary, the row and that row's first nonzero, the
+// boundaries of the stream reduction (rows never cross its partitions).
 __global__ __launch_bounds__(kBlock) void split_search_kernel(
     const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int32_t T, int32_t P,
-    int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz) {
+    int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz,
+    int32_t* __restrict__ row_bounds) {
   const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (p > P) return;
   const int64_t W = (int64_t)M + nnz;
@@ -199,6 +204,8 @@ __global__ __launch_bounds__(kBlock) void split_search_kernel(
   }
   split_row[p] = (int32_t)lo;
   split_nz[p] = (int32_t)(d - lo);
+  row_bounds[2 * p] = (int32_t)lo;
+  row_bounds[2 * p + 1] = row_ptr[lo];
 }
 
 __global__ __launch_bounds__(kBlock) void check_columns_kernel(
@@ -210,6 +217,57 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
     bad |= (c < 0) | ((int64_t)c >= N);
   }
   if (bad) atomicOr((unsigned long long*)&stats[kStatError], 2ull);
+}
+
+// For each group of 4 consecutive partitions (one stream workgroup), taken
+// as whole rows [split_row[4g], split_row[4g + 4]): the first column its
+// entries use and the span up to the last one, or span 0 when the span is
+// cap entries or more. The range is widened to whole 16-byte quads, as the
+// exec kernel stages it, so the few neighbouring-row entries of the edge
+// quads are inside the span too; the span itself is widened to whole 16-byte
+// chunks of x (e elements each), which the exec kernel copies with 16-byte
+// direct-to-LDS loads, and dropped if that would reach past x. Also counts the groups whose span fits. Only chooses
+// and prepares a kernel variant: the exec kernel checks every column against
+// the span again.
+__global__ __launch_bounds__(kBlock) void window_span_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ split_row, int32_t P, int32_t nnz, int32_t N, int32_t e,
+    int32_t cap, int32_t* __restrict__ win_span, int64_t* stats) {
+  __shared__ int32_t s_lo[kWavesPerBlock], s_hi[kWavesPerBlock];
+  const int g = blockIdx.x;
+  const int p0 = g * kWavesPerBlock, p1 = min(p0 + kWavesPerBlock, P);
+  int k0 = row_ptr[split_row[p0]], k1 = row_ptr[split_row[p1]];
+  if (k1 > k0) {
+    k0 &= ~3;
+    k1 = min((k1 + 3) & ~3, nnz);
+  }
+  int lo = INT_MAX, hi = INT_MIN;
+  for (int k = k0 + threadIdx.x; k < k1; k += kBlock) {
+    const int c = col_idx[k];
+    lo = min(lo, c);
+    hi = max(hi, c);
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o, kWave));
+    hi = max(hi, __shfl_xor(hi, o, kWave));
+  }
+  if (lane_id() == 0) {
+    s_lo[threadIdx.x / kWave] = lo;
+    s_hi[threadIdx.x / kWave] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWavesPerBlock; ++w) {
+      lo = min(lo, s_lo[w]);
+      hi = max(hi, s_hi[w]);
+    }
+    const int alo = lo & ~(e - 1), ahi = hi | (e - 1);
+    const bool fits = hi >= lo && ahi < N && ahi - alo < cap;
+    win_span[2 * g] = fits ? alo : 0;
+    win_span[2 * g + 1] = fits ? ahi - alo + 1 : 0;
+    if (fits) atomicAdd((unsigned long long*)&stats[kStatWindowFits], 1ull);
+    atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
+  }
 }
 
 int n_blocks(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
@@ -251,9 +309,22 @@ hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges&
 
 hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
                                int64_t P, int32_t* split_row, int32_t* split_nz,
-                               hipStream_t s) {
+                               int32_t* row_bounds, hipStream_t s) {
   hipLaunchKernelGGL(split_search_kernel, dim3(n_blocks(P + 1, kBlock)), dim3(kBlock), 0, s,
-                     row_ptr, (int32_t)M, (int32_t)nnz, T, (int32_t)P, split_row, split_nz);
+                     row_ptr, (int32_t)M, (int32_t)nnz, T, (int32_t)P, split_row, split_nz,
+                     row_bounds);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
+                               int32_t elem_bytes, int32_t* win_span, int64_t* stats,
+                               hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  const int64_t groups = (P + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
+                     col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
+                     kWindowBytes / elem_bytes, win_span, stats);
   return hipGetLastError();
 }
 

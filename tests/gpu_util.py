@@ -10,7 +10,7 @@ import load_balanced_csr_amd as lb
 
 # plan options of the schedule variants every parity case runs through
 VARIANTS = {
-    # merge-path; the reduction is "stream" where every row fits T/4, else "walk"
+    # merge-path; the reduction is "stream" where every row fits T/8, else "walk"
     "merge4": dict(strategy="merge", items_per_thread=4),
     "merge8": dict(strategy="merge", items_per_thread=8),
     "merge16": dict(strategy="merge", items_per_thread=16),
@@ -19,6 +19,11 @@ VARIANTS = {
     # stream reduction with other lane-group widths (ignored when walk applies)
     "merge8_g1": dict(strategy="merge", items_per_thread=8, stream_lanes=1),
     "merge16_g16": dict(strategy="merge", items_per_thread=16, stream_lanes=16),
+    # stream reduction with the workgroup's x window forced on / off (a block
+    # whose column span does not fit still gathers from HBM)
+    "merge8_xwin": dict(strategy="merge", items_per_thread=8, x_window="on"),
+    "merge4_xwin": dict(strategy="merge", items_per_thread=4, x_window="on", stream_lanes=2),
+    "merge8_noxwin": dict(strategy="merge", items_per_thread=8, x_window="off"),
     "binned": dict(strategy="binned"),
     # other bin edges: correctness must not depend on them
     "binned_alt": dict(strategy="binned",

@@ -90,3 +90,12 @@ def test_exec_and_destroy_reject_foreign_handles():
     with pytest.raises(lb.SpmvError) as e:
         lb.spmv_plan_info(0x12345678)
     assert e.value.status == 5
+
+
+def test_library_has_no_undefined_symbols_of_its_own():
+    """Every kernel the library launches has its host stub linked in (a
+    device-only builtin in a kernel body once made the host pass drop them)."""
+    import subprocess
+    out = subprocess.check_output(["nm", "-D", "--undefined-only", lb.LIB_PATH]).decode()
+    own = [l for l in out.splitlines() if "spmv" in l]
+    assert not own, own[:5]

@@ -137,7 +137,14 @@ def test_reduction_mode_choice():
     info = m.plan("merge8").info
     assert info["merge_reduce"] == "stream" and info["stream_lanes"] == 1
     assert m.plan("merge8_walk").info["merge_reduce"] == "walk"
-    w = _csr([3] * 50 + [129] + [3] * 50, 200, 3)       # 129 > 512 / 4
+    m = DevMatrix.of(synth.banded(M=50_000, half_band=500))
+    info = m.plan("merge8").info
+    assert info["merge_reduce"] == "stream" and info["x_window"]
+    assert not m.plan("merge8_noxwin").info["x_window"]
+    m = DevMatrix.of(synth.powerlaw(M=50_000, max_len=60))
+    info = m.plan("merge8").info
+    assert info["merge_reduce"] == "stream" and not info["x_window"]
+    w = _csr([3] * 50 + [65] + [3] * 50, 200, 3)        # 65 > 512 / 8
     m = DevMatrix.of(w)
     assert m.plan("merge8").info["merge_reduce"] == "walk"
     with pytest.raises(lb.SpmvError) as e:
