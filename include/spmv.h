@@ -83,8 +83,12 @@ typedef struct spmv_plan_st* spmv_plan_t;
 typedef struct spmv_plan_options {
   int32_t strategy;           /* spmv_strategy_t; 0 = AUTO (env SPMV_STRATEGY
                                  = auto|merge|binned overrides AUTO) */
-  int32_t items_per_thread;   /* merge-path items per lane: 4, 8 or 16;
-                                 T = 64 * items_per_thread items per wavefront */
+  int32_t items_per_thread;   /* merge-path items per lane: 4, 7, 8 or 16;
+                                 T = 64 * items_per_thread items per wavefront.
+                                 0: env SPMV_ITEMS_PER_THREAD, else chosen from
+                                 the row lengths: 4 when every row has <= 32
+                                 entries and the mean is < 12, 8 when every row
+                                 has <= 64, otherwise 16 (fp32) or 8 (fp64) */
   int32_t n_bins;             /* 1..SPMV_MAX_BINS; 0 = default bins */
   int32_t validate_columns;   /* 1: also check 0 <= col_idx < N at plan time
                                  (one pass over col_idx); env SPMV_VALIDATE=1 */

@@ -69,6 +69,7 @@ struct spmv_plan_st {
   int32_t merge_reduce;     // 1 walk, 2 stream
   int32_t stream_lanes;
   int32_t x_window;
+  int32_t win_waves;        // partitions (waves) per window workgroup
 
   BinEdges edges;
   int32_t lanes[kMaxBins];
@@ -115,9 +116,9 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
   if (!o) return SPMV_SUCCESS;
   if (o->strategy < 0 || o->strategy > SPMV_STRATEGY_BINNED)
     return fail(SPMV_ERR_INVALID_ARG, "options.strategy %d unknown", o->strategy);
-  if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 8 &&
-      o->items_per_thread != 16)
-    return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 8 or 16");
+  if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 7 &&
+      o->items_per_thread != 8 && o->items_per_thread != 16)
+    return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 7, 8 or 16");
   if (o->x_window < 0 || o->x_window > 2)
     return fail(SPMV_ERR_INVALID_ARG, "options.x_window %d unknown", o->x_window);
   if (o->merge_reduce < 0 || o->merge_reduce > 2)
@@ -197,6 +198,7 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     // the window's 16-byte direct-to-LDS loads need a 16-byte aligned x
     a.x_window = p->x_window && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
     a.win_span = p->win_span;
+    a.win_waves = p->win_waves;
     err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
   } else {
     BinnedArgs<V> a;
@@ -264,10 +266,16 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   p->xcd_remap = env_int("SPMV_XCD_REMAP", 1) != 0;
 
   const int forced = options ? options->strategy : 0;
+  // items per lane: given, or chosen from the row lengths once they are
+  // counted (the partition arrays are sized for the smallest candidate, 4)
   p->ipt = options && options->items_per_thread ? options->items_per_thread
-                                                 : env_int("SPMV_ITEMS_PER_THREAD", 8);
-  if (p->ipt != 4 && p->ipt != 8 && p->ipt != 16) p->ipt = 8;
+                                                 : env_int("SPMV_ITEMS_PER_THREAD", 0);
+  const bool auto_ipt = p->ipt != 4 && p->ipt != 7 && p->ipt != 8 && p->ipt != 16;
+  if (auto_ipt) p->ipt = 4;
   p->T = kWave * p->ipt;
+  // waves sharing one x window (env SPMV_WIN_WAVES: 4, 8 or 16)
+  p->win_waves = env_int("SPMV_WIN_WAVES", 4);
+  if (p->win_waves != 4 && p->win_waves != 8 && p->win_waves != 16) p->win_waves = 4;
   const int64_t W = M + nnz;
   p->P = (W + p->T - 1) / p->T;
 
@@ -342,12 +350,30 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   if ((err = launch_bin_scatter(row_ptr, M, p->edges, p->counts, p->stats, p->bins, stream)) !=
       hipSuccess)
     return bail(hip_fail(err, "plan: bin scatter"));
+  if (auto_ipt) {
+    // row lengths decide T: short rows (every row <= 32, mean < 12) take
+    // T = 256, rows up to 64 take T = 512 (both then use the stream
+    // reduction); longer rows take the walk with T = 1024 (fp32) or 512
+    if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
+                              stream)) != hipSuccess ||
+        (err = hipStreamSynchronize(stream)) != hipSuccess)
+      return bail(hip_fail(err, "plan: row-length read-back"));
+    if (!(host_stats[kStatError] & 1)) {
+      const int64_t max_len = host_stats[kStatMaxLen];
+      const double avg = M > 0 ? (double)nnz / (double)M : 0.0;
+      if (max_len <= 32 && avg < 12.0) p->ipt = 4;
+      else if (max_len <= 64) p->ipt = 8;
+      else p->ipt = dtype == SPMV_F32 ? 16 : 8;
+      p->T = kWave * p->ipt;
+      p->P = (W + p->T - 1) / p->T;
+    }
+  }
   if (p->P > 0 && (err = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row,
                                              p->split_nz, p->row_bounds, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: split search"));
   if (p->P > 0 && nnz > 0 &&
       (err = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
-                                 p->win_span, p->stats, stream)) !=
+                                 p->win_waves, p->win_span, p->stats, stream)) !=
           hipSuccess)
     return bail(hip_fail(err, "plan: window spans"));
   if (validate_cols &&
@@ -393,8 +419,9 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     if (g == 0) g = env_int("SPMV_STREAM_LANES", 0);
     if (g == 0) {
       const double avg = M > 0 ? (double)nnz / (double)M : 0.0;
+      // about four or more products per lane of a row's group
       g = 1;
-      while (g < 64 && 2.0 * g <= avg / 4.0) g *= 2;
+      while (g < 64 && 2.0 * g <= avg / 8.0) g *= 2;
     }
     if (g < 1 || g > 64 || (g & (g - 1))) g = 1;
     p->stream_lanes = g;
@@ -407,7 +434,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     }
     const bool fits = host_stats[kStatWindowSamples] > 0 &&
                       2 * host_stats[kStatWindowFits] >= host_stats[kStatWindowSamples];
-    p->x_window = p->merge_reduce == 2 && (xw == 2 || (xw == 0 && fits));
+    // (no nonzeros: nothing to gather, and the span table is not computed)
+    p->x_window = p->merge_reduce == 2 && nnz > 0 && (xw == 2 || (xw == 0 && fits));
   }
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))

@@ -49,19 +49,13 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
+// Per group of `group` consecutive partitions: {first column, length} of the
+// chunk-aligned column span of the group's quads when it fits kWindowBytes,
+// else {0, 0}; counts groups and fitting groups in stats.
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t* win_span, int64_t* stats,
-                               hipStream_t s);
-hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
-                                int64_t* stats, hipStream_t s);
-hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
-hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
-                               const int32_t* split_row, int64_t P, int32_t cap,
-                               int32_t* win_span, hipStream_t s);
-hipError_t launch_window_sample(const int32_t* row_ptr, const int32_t* col_idx,
-                                const int32_t* split_row, int64_t P, int32_t cap,
-                                int64_t* stats, hipStream_t s);
+                               int32_t elem_bytes, int32_t group, int32_t* win_span,
+                               int64_t* stats, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>
@@ -87,6 +81,7 @@ struct MergeArgs {
   int32_t stream_lanes;  // lanes per row in the stream reduction
   int32_t x_window;      // 1: stream kernel with the workgroup's x window in LDS
   const int32_t* win_span;  // per stream workgroup: first column, span (0: no window)
+  int32_t win_waves;        // waves per workgroup of the window kernel (4, 8, 16)
 };
 
 template <typename V>

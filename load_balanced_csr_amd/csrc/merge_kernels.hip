@@ -202,9 +202,39 @@ __device__ __forceinline__ void stream_stage_nn(const MergeArgs<V>& a, int qr0, 
                                                wlen);
 }
 
-// (second launch bound: at least 8 waves per SIMD, i.e. at most 64 VGPRs)
-template <typename V, int IPT, bool WIN>
-__global__ __launch_bounds__(kBlock, 8) void merge_stream_kernel(const MergeArgs<V> a) {
+// Reduction of a staged stream partition: groups of G lanes sum each row
+// (strided by G, then a butterfly), 64 / G rows per round; alpha and beta are
+// applied once per row. re[k] is the local end of row r0 + k, prod[i] the
+// product of the partition's nonzero i.
+template <typename V>
+__device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int nrows,
+                                              const int32_t* re, const V* prod) {
+  const int lane = lane_id();
+  const int G = a.stream_lanes;
+  const int gl = lane & (G - 1);
+  const int rows_per_round = kWave / G;
+  const int grp = lane / G;
+  for (int base = 0; base < nrows; base += rows_per_round) {
+    const int k = base + grp;
+    V acc = V(0);
+    if (k < nrows) {
+      const int s = k > 0 ? re[k - 1] : 0, t = re[k];
+      for (int i = s + gl; i < t; i += G) acc += prod[i];
+    }
+    for (int o = G >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (k < nrows && gl == 0) {
+      V out = a.alpha * acc;
+      if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
+      a.y[r0 + k] = out;   // cached store: L2 merges the partial lines of neighbours
+    }
+  }
+}
+
+// WPB waves per workgroup (4, or 8 / 16 with the window: the wider the
+// workgroup, the less x each partition fetches into LDS). Second launch
+// bound: at least 8 waves per SIMD, i.e. at most 64 VGPRs.
+template <typename V, int IPT, bool WIN, int WPB>
+__global__ __launch_bounds__(WPB * kWave, 8) void merge_stream_kernel(const MergeArgs<V> a) {
   constexpr int T = kWave * IPT;
   constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
   constexpr int BUF = CAP + 16;             // per-wave buffer, elements of V
@@ -213,13 +243,13 @@ __global__ __launch_bounds__(kBlock, 8) void merge_stream_kernel(const MergeArgs
   constexpr int WCHUNKS = kWindowBytes / 16;  // 16-byte chunks of the x window
   constexpr int E = 16 / sizeof(V);           // elements per chunk
   static_assert(RQN <= 5, "at most 5 nonzero rounds");
-  __shared__ __attribute__((aligned(16))) V s_buf[kWavesPerBlock][BUF];
+  __shared__ __attribute__((aligned(16))) V s_buf[WPB][BUF];
   __shared__ __attribute__((aligned(16))) V s_x[WIN ? WCHUNKS * E : E];
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  const int p = blk * kWavesPerBlock + wave;
+  const int p = blk * WPB + wave;
   // one descriptor read: {r0, row_ptr[r0]} and {r1, row_ptr[r1]}
   int r0 = 0, r1 = 0, n0 = 0, n1 = 0;
   if (p < a.P) {
@@ -241,8 +271,8 @@ __global__ __launch_bounds__(kBlock, 8) void merge_stream_kernel(const MergeArgs
     wlen = a.win_span[2 * blk + 1];
     const int nch = wlen / E;
 #pragma unroll
-    for (int r = 0; r < (WCHUNKS + kBlock - 1) / kBlock; ++r) {
-      const int first = kBlock * r + kWave * wave;     // this wave's first chunk
+    for (int r = 0; r < (WCHUNKS + WPB * kWave - 1) / (WPB * kWave); ++r) {
+      const int first = WPB * kWave * r + kWave * wave;   // this wave's first chunk
       if (first < nch && first + lane < nch) lds_dma16(a.x + wlo + E * (first + lane), s_x + E * first);
     }
   }
@@ -279,25 +309,7 @@ __global__ __launch_bounds__(kBlock, 8) void merge_stream_kernel(const MergeArgs
   if (nrows == 0) return;
   wave_sync();
 
-  // ---- G lanes per row ---------------------------------------------------------
-  const int G = a.stream_lanes;
-  const int gl = lane & (G - 1);
-  const int rows_per_round = kWave / G;
-  const int grp = lane / G;
-  for (int base = 0; base < nrows; base += rows_per_round) {
-    const int k = base + grp;
-    V acc = V(0);
-    if (k < nrows) {
-      const int s = k > 0 ? re[k - 1] : 0, t = re[k];
-      for (int i = s + gl; i < t; i += G) acc += prod[i];
-    }
-    for (int o = G >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    if (k < nrows && gl == 0) {
-      V out = a.alpha * acc;
-      if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
-      a.y[r0 + k] = out;   // cached store: L2 merges the partial lines of neighbours
-    }
-  }
+  stream_reduce(a, r0, nrows, re, prod);
 }
 
 // Adds alpha * sum(carries) to every row that partitions left open. One wave
@@ -344,14 +356,26 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
   }
 }
 
+template <typename V, int IPT, int WPB>
+void launch_window(const MergeArgs<V>& a, hipStream_t s) {
+  hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true, WPB>), dim3((a.P + WPB - 1) / WPB),
+                     dim3(WPB * kWave), 0, s, a);
+}
+
 template <typename V, int IPT>
 hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (a.stream && a.x_window)
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true>), dim3(blocks), dim3(kBlock), 0, s, a);
-  else if (a.stream)
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, false>), dim3(blocks), dim3(kBlock), 0, s, a);
-  else
+  if (a.stream && a.x_window) {
+    switch (a.win_waves) {
+      case 4: launch_window<V, IPT, 4>(a, s); break;
+      case 8: launch_window<V, IPT, 8>(a, s); break;
+      case 16: launch_window<V, IPT, 16>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (a.stream) {
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, false, kWavesPerBlock>), dim3(blocks),
+                       dim3(kBlock), 0, s, a);
+  } else
     hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
@@ -366,6 +390,7 @@ hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_
   if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
   switch (ipt) {
     case 4: err = launch_main<V, 4>(a, s); break;
+    case 7: err = launch_main<V, 7>(a, s); break;
     case 8: err = launch_main<V, 8>(a, s); break;
     case 16: err = launch_main<V, 16>(a, s); break;
     default: return hipErrorInvalidValue;

@@ -232,10 +232,10 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
 __global__ __launch_bounds__(kBlock) void window_span_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ split_row, int32_t P, int32_t nnz, int32_t N, int32_t e,
-    int32_t cap, int32_t* __restrict__ win_span, int64_t* stats) {
+    int32_t cap, int32_t group, int32_t* __restrict__ win_span, int64_t* stats) {
   __shared__ int32_t s_lo[kWavesPerBlock], s_hi[kWavesPerBlock];
   const int g = blockIdx.x;
-  const int p0 = g * kWavesPerBlock, p1 = min(p0 + kWavesPerBlock, P);
+  const int p0 = g * group, p1 = min(p0 + group, P);
   int k0 = row_ptr[split_row[p0]], k1 = row_ptr[split_row[p1]];
   if (k1 > k0) {
     k0 &= ~3;
@@ -318,13 +318,13 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t* win_span, int64_t* stats,
-                               hipStream_t s) {
+                               int32_t elem_bytes, int32_t group, int32_t* win_span,
+                               int64_t* stats, hipStream_t s) {
   if (P <= 0) return hipSuccess;
-  const int64_t groups = (P + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t groups = (P + group - 1) / group;
   hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
                      col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
-                     kWindowBytes / elem_bytes, win_span, stats);
+                     kWindowBytes / elem_bytes, group, win_span, stats);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ VARIANTS = {
     "merge8_xwin": dict(strategy="merge", items_per_thread=8, x_window="on"),
     "merge4_xwin": dict(strategy="merge", items_per_thread=4, x_window="on", stream_lanes=2),
     "merge8_noxwin": dict(strategy="merge", items_per_thread=8, x_window="off"),
+    "merge7": dict(strategy="merge", items_per_thread=7),
+    "merge7_xwin": dict(strategy="merge", items_per_thread=7, x_window="on", stream_lanes=4),
     "binned": dict(strategy="binned"),
     # other bin edges: correctness must not depend on them
     "binned_alt": dict(strategy="binned",

@@ -21,7 +21,7 @@ def test_full_size_parity(name):
     dt = w.values.dtype.type
     ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
     m = DevMatrix.of(w)
-    for variant in (None, "merge8", "merge8_walk", "merge8_xwin", "binned"):
+    for variant in (None, "merge8", "merge8_walk", "merge8_xwin", "merge7", "binned"):
         log("run", name, variant or "auto", "M=%d nnz=%d" % (w.M, w.nnz))
         plan = m.plan(variant)
         y = run(plan, w.x, w.alpha, w.beta, w.y0, dt)

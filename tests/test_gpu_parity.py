@@ -102,6 +102,43 @@ def test_long_rows_and_partition_edges(variant):
         _case(w, variant, 1.5, 0.5, what="edges%d" % len(lengths))
 
 
+def _jumping_bands(M, N, dtype, seed):
+    """Rows i hold columns c(i) + {-40, -20, -5, 0, 3, 17, 31} (inside [0, N)),
+    where c(i) follows i, jumps forward by N/2, back below the start, then
+    returns: column spans of workgroups that straddle a jump do not fit the
+    x window, so those gather from global x."""
+    offs = np.array([-40, -20, -5, 0, 3, 17, 31])
+    i = np.arange(M)
+    c = np.where(i < M // 4, i, np.where(i < M // 2, i + N // 2,
+                 np.where(i < 3 * M // 4, i // 8, i)))
+    cols = c[:, None] + offs[None, :]
+    ok = (cols >= 0) & (cols < N)
+    L = ok.sum(1)
+    row_ptr = np.zeros(M + 1, dtype=np.int32)
+    np.cumsum(L, out=row_ptr[1:])
+    col_idx = cols[ok].astype(np.int32)
+    values = synth.uniform(int(row_ptr[-1]), seed, synth.S_VAL, dtype)
+    x = synth.uniform(N, seed, synth.S_X, dtype)
+    return row_ptr, col_idx, values, x
+
+
+@pytest.mark.parametrize("variant", ["merge7_xwin", "merge8_xwin", "merge4_xwin"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+def test_window_with_jumping_bands(variant, dtype):
+    M, N = 400_000, 900_000
+    rp, ci, va, x = _jumping_bands(M, N, dtype, 31)
+    m = DevMatrix(rp, ci, va, M, N)
+    plan = m.plan(variant)
+    info = plan.info
+    log("case jumps", variant, info["merge_reduce"], info["x_window"])
+    assert info["merge_reduce"] == "stream" and info["x_window"], info
+    y0 = synth.uniform(M, 32, synth.S_Y, dtype)
+    for a, b in ((1.0, 0.0), (-1.5, 0.5)):
+        y = run(plan, x, a, b, y0 if b != 0 else None, dtype)
+        check(y, rp, ci, va, x, a, b, y0 if b != 0 else None, what="jumps/%s" % variant)
+    plan.destroy()
+
+
 @pytest.mark.parametrize("variant", ALL)
 def test_no_entries(variant):
     # every row empty: y = beta * y exactly (0 with beta = 0, y not read)
