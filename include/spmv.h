@@ -101,9 +101,12 @@ typedef struct spmv_plan_options {
                                  of two; 0 = from the mean row length */
   int32_t x_window;           /* stream reduction: 0 auto, 1 off, 2 on. On, each
                                  workgroup copies the span of x its entries use
-                                 into LDS when the span fits (kWindowBytes) and
-                                 gathers from there; otherwise from HBM. Needs a
-                                 16-byte aligned x at exec time (else off) */
+                                 into LDS when the span fits the LDS its staging
+                                 buffers leave (so that 32 waves still fit a
+                                 CU; none for fp64 with items_per_thread >= 8)
+                                 and gathers from there; otherwise from HBM.
+                                 Needs a 16-byte aligned x at exec time (else
+                                 off) */
   int32_t pad0;
   int64_t bin_max_len[SPMV_MAX_BINS];
                               /* inclusive upper row length of bins 0..n_bins-2,

@@ -97,6 +97,11 @@ struct spmv_plan_st {
 
 namespace {
 
+// The stream kernel's x window for these parameters (0: none).
+int window_bytes(int ipt, int vbytes, int wpb) {
+  return stream_window_bytes(ipt, vbytes, wpb);
+}
+
 // Live plans. A handle is only dereferenced after it is found here, so a
 // destroyed or foreign handle is rejected without touching its memory.
 std::mutex g_plans_mu;
@@ -373,7 +378,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     return bail(hip_fail(err, "plan: split search"));
   if (p->P > 0 && nnz > 0 &&
       (err = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
-                                 p->win_waves, p->win_span, p->stats, stream)) !=
+                                 p->win_waves, window_bytes(p->ipt, (int)vs, p->win_waves),
+                                 p->win_span, p->stats, stream)) !=
           hipSuccess)
     return bail(hip_fail(err, "plan: window spans"));
   if (validate_cols &&
@@ -435,7 +441,9 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     const bool fits = host_stats[kStatWindowSamples] > 0 &&
                       2 * host_stats[kStatWindowFits] >= host_stats[kStatWindowSamples];
     // (no nonzeros: nothing to gather, and the span table is not computed)
-    p->x_window = p->merge_reduce == 2 && nnz > 0 && (xw == 2 || (xw == 0 && fits));
+    p->x_window = p->merge_reduce == 2 && nnz > 0 &&
+                  window_bytes(p->ipt, (int)vs, p->win_waves) > 0 &&
+                  (xw == 2 || (xw == 0 && fits));
   }
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))

@@ -39,6 +39,27 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0);
 #endif
 }
+// Wait until at most N vector memory instructions of this wave are in
+// flight (they retire in order: everything older than the last N is done);
+// LDS, scalar and export counters are not waited for. gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+// The same, and every LDS access of this wave done (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+#endif
+}
+// Keeps the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void memory_order_point() { asm volatile("" ::: "memory"); }
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {

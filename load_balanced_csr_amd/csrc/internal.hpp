@@ -13,7 +13,28 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
 constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
-constexpr int kWindowBytes = 12288;      // LDS x window of a stream workgroup
+constexpr int kWindowBytes = 12288;      // cap of the staged x window (register form)
+
+// Waves per SIMD the stream kernel's register budget allows: 8 (at most 64
+// VGPRs) up to T = 448; larger partitions need more registers than that, and
+// spilling would cost more than the waves given up.
+constexpr int stream_min_waves(int vbytes, int ipt, bool win) {
+  return ipt >= 16 ? 4 : ipt < 8 ? 8 : vbytes == 4 ? 7 : win ? 6 : 8;
+}
+
+// LDS of the stream kernel. Its staging buffer per wave holds the T + T/8
+// units of one partition (+16 for quad alignment). The x window of a
+// workgroup of wpb waves takes what is left of the workgroup's share of the
+// CU's 160 KiB at the occupancy the registers allow, minus 512 bytes of
+// allocation slack; below 2 KiB it is not worth a barrier and is 0.
+constexpr int stream_buf_elems(int ipt) { return kWave * ipt + kWave * ipt / 8 + 16; }
+constexpr int stream_window_raw(int ipt, int vbytes, int wpb) {
+  return (163840 * wpb / (4 * stream_min_waves(vbytes, ipt, true)) - 512 -
+          wpb * stream_buf_elems(ipt) * vbytes) / 16 * 16;
+}
+constexpr int stream_window_bytes(int ipt, int vbytes, int wpb) {
+  return stream_window_raw(ipt, vbytes, wpb) >= 2048 ? stream_window_raw(ipt, vbytes, wpb) : 0;
+}
 
 // Layout of the statistics block the plan copies back to the host (int64).
 enum StatSlot : int {
@@ -50,12 +71,12 @@ hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
 // Per group of `group` consecutive partitions: {first column, length} of the
-// chunk-aligned column span of the group's quads when it fits kWindowBytes,
+// chunk-aligned column span of the group's quads when it fits cap_bytes,
 // else {0, 0}; counts groups and fitting groups in stats.
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t group, int32_t* win_span,
-                               int64_t* stats, hipStream_t s);
+                               int32_t elem_bytes, int32_t group, int32_t cap_bytes,
+                               int32_t* win_span, int64_t* stats, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>

@@ -132,26 +132,38 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
 template <typename V, int NR, int NN, bool WIN>
 __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int nqr, int n0,
                                              int qn0, int nqn, int32_t* ends, V* prods,
-                                             const V* xs, int wlo, int wlen) {
+                                             const V* xs, const int* win_meta) {
+  int wlo = 0, wlen = 0;
   const int lane = lane_id();
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
   Quad<V> v[NN > 0 ? NN : 1];
+  // row ends, then all column quads, then all value quads: the gathers wait
+  // only for the columns
 #pragma unroll
   for (int r = 0; r < NR; ++r)
     e[r] = load_quad<false>(a.row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
 #pragma unroll
-  for (int r = 0; r < NN; ++r) {
-    const int q = qn0 + min(lane + kWave * r, nqn - 1);
-    c[r] = load_quad<false>(a.col_idx, q, 0);
-    v[r] = load_quad<false>(a.val, q, 0);
-  }
+  for (int r = 0; r < NN; ++r) c[r] = load_quad<false>(a.col_idx, qn0 + min(lane + kWave * r, nqn - 1), 0);
+#pragma unroll
+  for (int r = 0; r < NN; ++r) v[r] = load_quad<false>(a.val, qn0 + min(lane + kWave * r, nqn - 1), 0);
   bool from_lds = false;
   if (WIN) {
-    // the window's direct-to-LDS loads are not tracked by the compiler:
-    // wait for every load of this wave, then for the other waves
-    wait_vmem();
-    __syncthreads();
+    // The window's direct-to-LDS loads went out before this partition's
+    // NR + NN + NN * (sizeof(V) / 4) loads (the caller orders them), and
+    // vector loads retire in order: once no more than that many are in
+    // flight, this wave's share of the window has landed. The barrier then
+    // covers the other waves' shares; the partition's own loads stay in
+    // flight across it (no fence: nothing but the window is shared), and the
+    // columns are only looked at after it.
+    // The window bounds are read back from LDS after the barrier, so the
+    // column checks cannot be hoisted above it.
+    memory_order_point();
+    wait_vmcnt_lds<NR + NN + NN * (int)(sizeof(V) / 4)>();
+    __builtin_amdgcn_s_barrier();
+    memory_order_point();
+    wlo = win_meta[0];
+    wlen = win_meta[1];
     bool inside = wlen > 0;
 #pragma unroll
     for (int r = 0; r < NN; ++r)
@@ -182,24 +194,24 @@ __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int
 template <typename V, int NR, int RQN, bool WIN>
 __device__ __forceinline__ void stream_stage_nn(const MergeArgs<V>& a, int qr0, int nqr, int n0,
                                                 int qn0, int nqn, int32_t* ends, V* prods,
-                                                const V* xs, int wlo, int wlen) {
+                                                const V* xs, const int* win_meta) {
   const int rounds = (nqn + kWave - 1) / kWave;
   if (rounds == 0)
-    stream_stage<V, NR, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo, wlen);
+    stream_stage<V, NR, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
   else if (rounds == 1 || RQN < 2)
-    stream_stage<V, NR, (RQN < 1 ? 0 : 1), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
-                                               wlen);
+    stream_stage<V, NR, (RQN < 1 ? 0 : 1), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+                                               win_meta);
   else if (rounds == 2 || RQN < 3)
-    stream_stage<V, NR, 2, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo, wlen);
+    stream_stage<V, NR, 2, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
   else if (rounds == 3 || RQN < 4)
-    stream_stage<V, NR, (RQN < 3 ? 2 : 3), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
-                                               wlen);
+    stream_stage<V, NR, (RQN < 3 ? 2 : 3), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+                                               win_meta);
   else if (rounds == 4 || RQN < 5)
-    stream_stage<V, NR, (RQN < 4 ? 2 : 4), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
-                                               wlen);
+    stream_stage<V, NR, (RQN < 4 ? 2 : 4), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+                                               win_meta);
   else
-    stream_stage<V, NR, (RQN < 5 ? 2 : 5), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, wlo,
-                                               wlen);
+    stream_stage<V, NR, (RQN < 5 ? 2 : 5), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+                                               win_meta);
 }
 
 // Reduction of a staged stream partition: groups of G lanes sum each row
@@ -231,16 +243,18 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
 }
 
 // WPB waves per workgroup (4, or 8 / 16 with the window: the wider the
-// workgroup, the less x each partition fetches into LDS). Second launch
-// bound: at least 8 waves per SIMD, i.e. at most 64 VGPRs.
+// workgroup, the less x each partition fetches into LDS).
 template <typename V, int IPT, bool WIN, int WPB>
-__global__ __launch_bounds__(WPB * kWave, 8) void merge_stream_kernel(const MergeArgs<V> a) {
+__global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN)) void merge_stream_kernel(
+    const MergeArgs<V> a) {
   constexpr int T = kWave * IPT;
   constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
-  constexpr int BUF = CAP + 16;             // per-wave buffer, elements of V
+  constexpr int BUF = stream_buf_elems(IPT);  // per-wave buffer, elements of V
   constexpr int RQN = (CAP / 4 + 2 + kWave - 1) / kWave;
   constexpr int RQR = (T / 4 + 2 + kWave - 1) / kWave;
-  constexpr int WCHUNKS = kWindowBytes / 16;  // 16-byte chunks of the x window
+  // 16-byte chunks of the x window
+  constexpr int WCHUNKS = WIN ? stream_window_bytes(IPT, sizeof(V), WPB) / 16 : 1;
+  static_assert(!WIN || WCHUNKS > 0, "window kernel instantiated without window room");
   constexpr int E = 16 / sizeof(V);           // elements per chunk
   static_assert(RQN <= 5, "at most 5 nonzero rounds");
   __shared__ __attribute__((aligned(16))) V s_buf[WPB][BUF];
@@ -264,17 +278,23 @@ __global__ __launch_bounds__(WPB * kWave, 8) void merge_stream_kernel(const Merg
   // with the window every wave must reach the block's barrier
   if (!WIN && nrows == 0) return;
 
-  int wlo = 0, wlen = 0;
+  __shared__ int s_win[2];
   if (WIN) {
     // x[wlo, wlo + wlen): chunk aligned and inside x (the plan guarantees it)
-    wlo = a.win_span[2 * blk];
-    wlen = a.win_span[2 * blk + 1];
+    const int wlo = a.win_span[2 * blk];
+    const int wlen = a.win_span[2 * blk + 1];
+    if (threadIdx.x == 0) {
+      s_win[0] = wlo;
+      s_win[1] = wlen;
+    }
     const int nch = wlen / E;
 #pragma unroll
     for (int r = 0; r < (WCHUNKS + WPB * kWave - 1) / (WPB * kWave); ++r) {
       const int first = WPB * kWave * r + kWave * wave;   // this wave's first chunk
       if (first < nch && first + lane < nch) lds_dma16(a.x + wlo + E * (first + lane), s_x + E * first);
     }
+    // the staging loads must be issued after these (the window wait counts them)
+    memory_order_point();
   }
 
   const int nnzc = n1 - n0;
@@ -300,11 +320,11 @@ __global__ __launch_bounds__(WPB * kWave, 8) void merge_stream_kernel(const Merg
     stage_safe<V, RQR, RQN, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
                                    a.nnz, qn0, nqn, ends_q, buf, nowin);
   } else if (nqr == 0) {
-    stream_stage<V, 0, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+    stream_stage<V, 0, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   } else if (nqr <= kWave || RQR < 2) {
-    stream_stage_nn<V, 1, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+    stream_stage_nn<V, 1, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   } else {
-    stream_stage_nn<V, RQR, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, wlo, wlen);
+    stream_stage_nn<V, RQR, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   }
   if (nrows == 0) return;
   wave_sync();
@@ -357,9 +377,13 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
 }
 
 template <typename V, int IPT, int WPB>
-void launch_window(const MergeArgs<V>& a, hipStream_t s) {
-  hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true, WPB>), dim3((a.P + WPB - 1) / WPB),
-                     dim3(WPB * kWave), 0, s, a);
+hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
+  if constexpr (stream_window_bytes(IPT, sizeof(V), WPB) > 0) {
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true, WPB>), dim3((a.P + WPB - 1) / WPB),
+                       dim3(WPB * kWave), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;   // the plan never asks for it
 }
 
 template <typename V, int IPT>
@@ -367,9 +391,9 @@ hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
   if (a.stream && a.x_window) {
     switch (a.win_waves) {
-      case 4: launch_window<V, IPT, 4>(a, s); break;
-      case 8: launch_window<V, IPT, 8>(a, s); break;
-      case 16: launch_window<V, IPT, 16>(a, s); break;
+      case 4: return launch_window<V, IPT, 4>(a, s);
+      case 8: return launch_window<V, IPT, 8>(a, s);
+      case 16: return launch_window<V, IPT, 16>(a, s);
       default: return hipErrorInvalidValue;
     }
   } else if (a.stream) {

@@ -318,13 +318,13 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t group, int32_t* win_span,
-                               int64_t* stats, hipStream_t s) {
-  if (P <= 0) return hipSuccess;
+                               int32_t elem_bytes, int32_t group, int32_t cap_bytes,
+                               int32_t* win_span, int64_t* stats, hipStream_t s) {
+  if (P <= 0 || cap_bytes <= 0) return hipSuccess;
   const int64_t groups = (P + group - 1) / group;
   hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
                      col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
-                     kWindowBytes / elem_bytes, group, win_span, stats);
+                     cap_bytes / elem_bytes, group, win_span, stats);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ VARIANTS = {
     "merge8_noxwin": dict(strategy="merge", items_per_thread=8, x_window="off"),
     "merge7": dict(strategy="merge", items_per_thread=7),
     "merge7_xwin": dict(strategy="merge", items_per_thread=7, x_window="on", stream_lanes=4),
+    "merge16_xwin": dict(strategy="merge", items_per_thread=16, x_window="on", stream_lanes=8),
     "binned": dict(strategy="binned"),
     # other bin edges: correctness must not depend on them
     "binned_alt": dict(strategy="binned",
