@@ -120,12 +120,43 @@ def cpu_baseline(w, budget_s: float, y_gpu):
     t = statistics.median(times)
     ok, worst, _ = oracle.within_tolerance(y_gpu, ref, scale, w.alpha, w.beta, w.y0,
                                            row_ptr=w.row_ptr)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     res = {"value": round(2.0 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
-           "kind": "oracle",
+           "kind": "oracle", "cpu": cpu, "host_cpus": os.cpu_count(),
            "sample": "whole workload (%d nnz), %d runs, median %.1f ms, fp64 accumulation"
                      % (w.nnz, len(times), t * 1e3),
            "GBps": round(compulsory_bytes(w) / t / 1e9, 3)}
     return res, bool(ok), worst
+
+
+def read_ceiling(lb, torch, flush, gib: int = 2, reps: int = 10):
+    """GB/s of the library's streaming-read probe over a 2 GiB buffer (each
+    wavefront reads 4 KiB once), flushed and event-timed like the steps:
+    the achievable read bandwidth to put beside the SpMV's."""
+    buf = torch.ones(gib << 28, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ts = []
+    for r in range(reps + 2):
+        if flush is not None:
+            flush.zero_()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        lb.spmv_read_probe(buf, sink)
+        b_.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(a_.elapsed_time(b_))
+    nbytes = buf.numel() * 4
+    del buf
+    return round(nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
 
 
 def calibrate_copy(mib: int, steps: int):
@@ -188,9 +219,9 @@ def main():
     y = torch.empty(w.M, dtype=dt, device=dev)
     torch.cuda.synchronize()
 
-    # planning cost (separate from the steps): median of 3 plan/destroy cycles
+    # planning cost (separate from the steps): median of 5 plan/destroy cycles
     plan_ms = []
-    for _ in range(3):
+    for _ in range(5):
         t0 = time.perf_counter()
         p = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
                     items_per_thread=args.items_per_thread)
@@ -245,6 +276,25 @@ def main():
     kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
     for e in kb + ke:
         hip.destroy(e)
+    # beta = 0: every call must reproduce the first one bit for bit
+    deterministic = None
+    if w.beta == 0.0:
+        deterministic = bool(np.array_equal(y.cpu().numpy().view(np.uint8),
+                                            y_first.view(np.uint8)))
+
+    # secondary figure: warm steps (no flush), events around each exec
+    warm_ms = []
+    for i in range(min(K, 20)):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        plan(x, y, w.alpha, w.beta)
+        b_.record()
+        warm_ms.append((a_, b_))
+    torch.cuda.synchronize()
+    warm_ms = [a_.elapsed_time(b_) for a_, b_ in warm_ms]
+
+    # achievable streaming-read bandwidth on this GPU, same flush and timing
+    ceiling = read_ceiling(lb, torch, flush)
     mean_exec = statistics.fmean(exec_ms)
     mean_kern = statistics.fmean(kern_ms)
     Bc = compulsory_bytes(w)
@@ -285,6 +335,13 @@ def main():
                      "traffic": load_traffic(args.workload, kernel)},
         "exec_ms_median": round(statistics.median(exec_ms), 5),
         "exec_ms_min": round(min(exec_ms), 5),
+        "exec_ms_max": round(max(exec_ms), 5),
+        "warm_exec_ms_median": round(statistics.median(warm_ms), 5),
+        "warm_pct_hbm_peak": round(100.0 * Bc / (statistics.median(warm_ms) * 1e-3) / 1e9
+                                   / HBM_PEAK_GBPS, 2),
+        "read_ceiling_GBps": ceiling,
+        "pct_of_read_ceiling": round(100.0 * gbps_exec / ceiling, 2) if ceiling else None,
+        "deterministic": deterministic,
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "plan_ms": round(statistics.median(plan_ms), 3),
         "kernel_source_hash": kernel_source_hash(),
@@ -294,10 +351,11 @@ def main():
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"], ok, worst = cpu_baseline(w, args.cpu_seconds, y_first)
+        out["cpu_baseline"]["gpu_speedup"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
         out["parity"] = {"ok": ok, "worst_over_bound": round(worst, 5),
                          "checked": "first exec vs the oracle, every row"}
     print(json.dumps(out), flush=True)
-    if not ok:
+    if not ok or deterministic is False:
         sys.exit(3)
 
 

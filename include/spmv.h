@@ -220,6 +220,18 @@ SPMV_API spmv_status_t spmv_plan_copy_splits(spmv_plan_t plan, int32_t* rows_hos
 SPMV_API spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
                                   int64_t bins_cap, int64_t* offsets_host);
 
+/* Measurement aid, not part of the SpMV: enqueue one streaming read of
+ * `bytes` bytes at device pointer `data` (16-byte aligned, bytes a multiple
+ * of 16, at most 2^31 - 1 workgroups' worth) on `stream`, with each 64-lane
+ * wavefront loading one 4 KiB block once. Timed by the caller, it gives the
+ * device's achievable read bandwidth for the same kind of access the SpMV
+ * kernels make. `sink` is a device int32 that keeps the loads live: the
+ * xor of a 4 KiB block is written there only if it equals 0x5bd1e995 (never,
+ * for buffers of equal words). Asynchronous; SPMV_ERR_INVALID_ARG on a bad
+ * pointer or size. */
+SPMV_API spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink,
+                                       hipStream_t stream);
+
 SPMV_API const char* spmv_status_string(spmv_status_t status);
 SPMV_API const char* spmv_last_error(void);
 

@@ -9,9 +9,9 @@ is a thin ctypes binding over the C ABI declared in include/spmv.h.
 from .binding import (EXPORTED, LIB_PATH, Plan, PlanOptions, SpmvError, load, make_options,
                       spmv_destroy, spmv_exec, spmv_exec_events, spmv_last_error, spmv_plan,
                       spmv_plan_copy_bins, spmv_plan_copy_splits, spmv_plan_info,
-                      spmv_plan_set_strategy, spmv_status_string)
+                      spmv_plan_set_strategy, spmv_read_probe, spmv_status_string)
 
 __all__ = ["EXPORTED", "LIB_PATH", "Plan", "PlanOptions", "SpmvError", "load", "make_options",
            "spmv_destroy", "spmv_exec", "spmv_exec_events", "spmv_last_error", "spmv_plan",
            "spmv_plan_copy_bins", "spmv_plan_copy_splits", "spmv_plan_info",
-           "spmv_plan_set_strategy", "spmv_status_string"]
+           "spmv_plan_set_strategy", "spmv_read_probe", "spmv_status_string"]

@@ -27,7 +27,7 @@ MAX_BINS = 8
 
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
-            "spmv_plan_copy_bins", "spmv_status_string", "spmv_last_error")
+            "spmv_plan_copy_bins", "spmv_read_probe", "spmv_status_string", "spmv_last_error")
 
 
 class SpmvError(RuntimeError):
@@ -84,6 +84,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_info.argtypes = [p, ctypes.POINTER(PlanInfo)]
     lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
     lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
+    lib.spmv_read_probe.argtypes = [p, i64, p, p]
     for name in EXPORTED:
         if name not in ("spmv_status_string", "spmv_last_error"):
             getattr(lib, name).restype = st
@@ -181,6 +182,15 @@ def spmv_exec_events(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float, 
     _check(load().spmv_exec_events(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts),
                                    float(alpha), float(beta), _stream(stream), ev_begin, ev_end),
            "spmv_exec_events")
+
+
+def spmv_read_probe(data: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One streaming read of the whole (16-byte multiple) device tensor `data`;
+    `sink` is a device int32 tensor (measurement aid, see the header)."""
+    if not (data.is_cuda and sink.is_cuda and sink.dtype == torch.int32):
+        raise ValueError("spmv_read_probe needs device tensors and an int32 sink")
+    _check(load().spmv_read_probe(data.data_ptr(), data.numel() * data.element_size(),
+                                  sink.data_ptr(), _stream(stream)), "spmv_read_probe")
 
 
 def spmv_destroy(plan: Optional[int]) -> None:

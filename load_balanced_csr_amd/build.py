@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspmv.so")
-SOURCES = ["api.hip", "plan_kernels.hip", "merge_kernels.hip", "binned_kernels.hip"]
+SOURCES = ["api.hip", "plan_kernels.hip", "merge_kernels.hip", "binned_kernels.hip",
+           "probe_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -470,6 +470,18 @@ spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   return spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, nullptr, stream);
 }
 
+spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink, hipStream_t stream) {
+  if (!data || !sink || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(data) & 15) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(SPMV_ERR_INVALID_ARG, "read probe: data must be 16-byte aligned, bytes a "
+                                      "multiple of 16, sink 4-byte aligned");
+  // a key no 4 KiB block of the callers' buffers (ones, zeros) folds to
+  const hipError_t err =
+      launch_read_probe(data, bytes, 0x5bd1e995, static_cast<int32_t*>(sink), stream);
+  if (err != hipSuccess) return hip_fail(err, "read probe launch");
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_exec_events(spmv_plan_t p, const void* x, void* y, double alpha,
                                double beta, hipStream_t stream, hipEvent_t ev_begin,
                                hipEvent_t ev_end) {

@@ -105,6 +105,11 @@ struct MergeArgs {
   int32_t win_waves;        // waves per workgroup of the window kernel (4, 8, 16)
 };
 
+// Streaming read of `bytes` (multiple of 16) at data; the xor of each 4 KiB
+// block is stored to the 4-byte sink only when it equals key.
+hipError_t launch_read_probe(const void* data, int64_t bytes, int32_t key, int32_t* sink,
+                             hipStream_t s);
+
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,
                         hipEvent_t ev1);

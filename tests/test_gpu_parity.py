@@ -310,3 +310,13 @@ def test_malformed_inputs_are_rejected():
     with pytest.raises(lb.SpmvError) as e:
         lb.spmv_exec(h, x, torch.empty(w.M, device="cuda"), 1.0, 0.0)
     assert e.value.status == 5
+
+
+def test_read_probe_runs_and_leaves_the_sink():
+    buf = torch.ones(1 << 22, dtype=torch.int32, device="cuda")   # 16 MiB
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    lb.spmv_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    with pytest.raises(lb.SpmvError):
+        lb.spmv_read_probe(buf[1:], sink)       # 4-byte offset: misaligned
