@@ -354,6 +354,38 @@ __device__ __forceinline__ V wave_segscan(V v, int key) {
   return v;
 }
 
+// DPP lane permutations inside a row of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over aligned groups of G lanes, G in {1, 2, 4, 8, 16}, with DPP moves
+// (no LDS traffic); every lane of the group gets the total. After the two
+// quad steps all lanes of a quad hold its sum, so mirroring 8 (16) lanes
+// pairs each lane with one of the other quad (other half).
+template <int G, typename V>
+__device__ __forceinline__ V group_sum_dpp(V v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "DPP groups up to 16");
+  if (G >= 2) v += dpp_move<kDppQuadXor1>(v);
+  if (G >= 4) v += dpp_move<kDppQuadXor2>(v);
+  if (G >= 8) v += dpp_move<kDppRowHalfMirror>(v);
+  if (G >= 16) v += dpp_move<kDppRowMirror>(v);
+  return v;
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64); every lane of
 // the group gets the total.
 template <int G, typename V>

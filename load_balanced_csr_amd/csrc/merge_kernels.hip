@@ -138,15 +138,16 @@ __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
   Quad<V> v[NN > 0 ? NN : 1];
-  // row ends, then all column quads, then all value quads: the gathers wait
-  // only for the columns
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-    e[r] = load_quad<false>(a.row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
+  // all column quads, then all value quads, then the row ends (needed last,
+  // for the LDS store): the gathers wait only for the columns, and nothing
+  // computed from the row ends sits in front of the other loads
 #pragma unroll
   for (int r = 0; r < NN; ++r) c[r] = load_quad<false>(a.col_idx, qn0 + min(lane + kWave * r, nqn - 1), 0);
 #pragma unroll
   for (int r = 0; r < NN; ++r) v[r] = load_quad<false>(a.val, qn0 + min(lane + kWave * r, nqn - 1), 0);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    e[r] = load_quad<false>(a.row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
   bool from_lds = false;
   if (WIN) {
     // The window's direct-to-LDS loads went out before this partition's
@@ -214,13 +215,54 @@ __device__ __forceinline__ void stream_stage_nn(const MergeArgs<V>& a, int qr0, 
                                                win_meta);
 }
 
-// Reduction of a staged stream partition: groups of G lanes sum each row
-// (strided by G, then a butterfly), 64 / G rows per round; alpha and beta are
-// applied once per row. re[k] is the local end of row r0 + k, prod[i] the
-// product of the partition's nonzero i.
+// Reduction of a staged stream partition: groups of G lanes sum each row,
+// 64 / G rows per round; alpha and beta are applied once per row. re[k] is
+// the local end of row r0 + k, prod[i] the product of the partition's
+// nonzero i. With one lane per row the lane sums its row in order; in wider
+// groups each lane reads U products per iteration (strided by G), all in
+// flight together; reads past the row end reread the row's last product and
+// add 0. The group's partial sums meet by DPP moves.
+template <typename V, int G>
+__device__ __forceinline__ void stream_reduce_g(const MergeArgs<V>& a, int r0, int nrows,
+                                                const int32_t* re, const V* prod) {
+  constexpr int U = G <= 4 ? 8 : 4;
+  const int lane = lane_id();
+  const int gl = lane & (G - 1);
+  constexpr int RPR = kWave / G;   // rows per round
+  const int grp = lane / G;
+  for (int base = 0; base < nrows; base += RPR) {
+    const int k = base + grp;
+    V acc = V(0);
+    if (k < nrows) {
+      const int s = k > 0 ? re[k - 1] : 0, t = re[k];
+      if (G == 1) {
+        // one lane per row (short rows): the plain loop is cheapest
+        for (int i = s; i < t; ++i) acc += prod[i];
+      } else {
+      for (int i = s + gl; i < t; i += U * G) {
+        V p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) p[u] = prod[min(i + u * G, t - 1)];
+        V part = p[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) part += i + u * G < t ? p[u] : V(0);
+        acc += part;
+      }
+      }
+    }
+    acc = group_sum_dpp<G>(acc);
+    if (k < nrows && gl == 0) {
+      V out = a.alpha * acc;
+      if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
+      a.y[r0 + k] = out;   // cached store: L2 merges the partial lines of neighbours
+    }
+  }
+}
+
+// Wider groups (32, 64 lanes per row): shuffles for the butterfly.
 template <typename V>
-__device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int nrows,
-                                              const int32_t* re, const V* prod) {
+__device__ __forceinline__ void stream_reduce_wide(const MergeArgs<V>& a, int r0, int nrows,
+                                                   const int32_t* re, const V* prod) {
   const int lane = lane_id();
   const int G = a.stream_lanes;
   const int gl = lane & (G - 1);
@@ -237,8 +279,21 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
     if (k < nrows && gl == 0) {
       V out = a.alpha * acc;
       if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
-      a.y[r0 + k] = out;   // cached store: L2 merges the partial lines of neighbours
+      a.y[r0 + k] = out;
     }
+  }
+}
+
+template <typename V>
+__device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int nrows,
+                                              const int32_t* re, const V* prod) {
+  switch (a.stream_lanes) {
+    case 1: stream_reduce_g<V, 1>(a, r0, nrows, re, prod); break;
+    case 2: stream_reduce_g<V, 2>(a, r0, nrows, re, prod); break;
+    case 4: stream_reduce_g<V, 4>(a, r0, nrows, re, prod); break;
+    case 8: stream_reduce_g<V, 8>(a, r0, nrows, re, prod); break;
+    case 16: stream_reduce_g<V, 16>(a, r0, nrows, re, prod); break;
+    default: stream_reduce_wide(a, r0, nrows, re, prod); break;
   }
 }
 

@@ -19,6 +19,8 @@ VARIANTS = {
     # stream reduction with other lane-group widths (ignored when walk applies)
     "merge8_g1": dict(strategy="merge", items_per_thread=8, stream_lanes=1),
     "merge16_g16": dict(strategy="merge", items_per_thread=16, stream_lanes=16),
+    "merge8_g64": dict(strategy="merge", items_per_thread=8, stream_lanes=64),
+    "merge4_g8": dict(strategy="merge", items_per_thread=4, stream_lanes=8),
     # stream reduction with the workgroup's x window forced on / off (a block
     # whose column span does not fit still gathers from HBM)
     "merge8_xwin": dict(strategy="merge", items_per_thread=8, x_window="on"),
