@@ -301,7 +301,7 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
 // workgroup, the less x each partition fetches into LDS).
 template <typename V, int IPT, bool WIN, int WPB>
 __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN)) void merge_stream_kernel(
-    const MergeArgs<V> a) {
+    const MergeArgs<V> a, const int32_t* __restrict__ rb) {
   constexpr int T = kWave * IPT;
   constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
   constexpr int BUF = stream_buf_elems(IPT);  // per-wave buffer, elements of V
@@ -319,15 +319,16 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
   const int p = blk * WPB + wave;
-  // one descriptor read: {r0, row_ptr[r0]} and {r1, row_ptr[r1]}
+  // one descriptor read, {r0, row_ptr[r0]} and {r1, row_ptr[r1]}: a uniform
+  // read of a table nothing in the kernel writes, so it is a scalar load
+  // (neighbouring waves share scalar cache lines; the vector memory path
+  // carries only the matrix)
   int r0 = 0, r1 = 0, n0 = 0, n1 = 0;
   if (p < a.P) {
-    const i32x2 b0 = reinterpret_cast<const i32x2*>(a.row_bounds)[p];
-    const i32x2 b1 = reinterpret_cast<const i32x2*>(a.row_bounds)[p + 1];
-    r0 = b0[0];
-    n0 = b0[1];
-    r1 = b1[0];
-    n1 = b1[1];
+    r0 = rb[2 * p];
+    n0 = rb[2 * p + 1];
+    r1 = rb[2 * p + 2];
+    n1 = rb[2 * p + 3];
   }
   const int nrows = r1 - r0;
   // with the window every wave must reach the block's barrier
@@ -435,7 +436,7 @@ template <typename V, int IPT, int WPB>
 hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
   if constexpr (stream_window_bytes(IPT, sizeof(V), WPB) > 0) {
     hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true, WPB>), dim3((a.P + WPB - 1) / WPB),
-                       dim3(WPB * kWave), 0, s, a);
+                       dim3(WPB * kWave), 0, s, a, a.row_bounds);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;   // the plan never asks for it
@@ -453,7 +454,7 @@ hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
     }
   } else if (a.stream) {
     hipLaunchKernelGGL((merge_stream_kernel<V, IPT, false, kWavesPerBlock>), dim3(blocks),
-                       dim3(kBlock), 0, s, a);
+                       dim3(kBlock), 0, s, a, a.row_bounds);
   } else
     hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
