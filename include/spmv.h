@@ -100,13 +100,16 @@ typedef struct spmv_plan_options {
   int32_t stream_lanes;       /* stream reduction: lanes per row, 1..64 power
                                  of two; 0 = from the mean row length */
   int32_t x_window;           /* stream reduction: 0 auto, 1 off, 2 on. On, each
-                                 workgroup copies the span of x its entries use
-                                 into LDS when the span fits the LDS its staging
-                                 buffers leave (so that 32 waves still fit a
-                                 CU; none for fp64 with items_per_thread >= 8)
-                                 and gathers from there; otherwise from HBM.
-                                 Needs a 16-byte aligned x at exec time (else
-                                 off) */
+                                 workgroup of 4 partitions copies the x entries
+                                 its quads use into LDS, as one column interval
+                                 or, when the columns form separate bands (a
+                                 stencil), up to three, when they fit the LDS
+                                 the staging buffers leave at full occupancy
+                                 (none for fp64 with items_per_thread >= 8),
+                                 and gathers from there; a wave with a column
+                                 outside them gathers from global x. Auto: on
+                                 when at least half the workgroups fit. Needs a
+                                 16-byte aligned x at exec time (else off) */
   int32_t pad0;
   int64_t bin_max_len[SPMV_MAX_BINS];
                               /* inclusive upper row length of bins 0..n_bins-2,
@@ -125,7 +128,8 @@ typedef struct spmv_plan_info {
   int64_t n_partitions;       /* P = ceil((M + nnz) / T) */
   int32_t merge_reduce;       /* 1 walk, 2 stream */
   int32_t stream_lanes;
-  int32_t x_window;           /* 1 when the stream kernel uses the LDS x window */
+  int32_t x_window;           /* stream kernel's LDS x window: 0 none, 1 one
+                                 column interval, 3 up to three */
   int32_t pad0;
   int32_t n_bins;
   int32_t bin_identity;       /* 1: every row fell in one bin, no row-id array */

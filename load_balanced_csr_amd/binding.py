@@ -211,6 +211,7 @@ def spmv_plan_info(plan: int) -> dict:
             "items_per_wave": info.items_per_wave, "n_partitions": info.n_partitions,
             "merge_reduce": MERGE_REDUCE_NAME.get(info.merge_reduce, "none"),
             "stream_lanes": info.stream_lanes, "x_window": bool(info.x_window),
+            "x_window_intervals": info.x_window,
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,

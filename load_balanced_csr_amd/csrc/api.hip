@@ -69,7 +69,6 @@ struct spmv_plan_st {
   int32_t merge_reduce;     // 1 walk, 2 stream
   int32_t stream_lanes;
   int32_t x_window;
-  int32_t win_waves;        // partitions (waves) per window workgroup
 
   BinEdges edges;
   int32_t lanes[kMaxBins];
@@ -201,9 +200,8 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.stream = p->merge_reduce == 2;
     a.stream_lanes = p->stream_lanes;
     // the window's 16-byte direct-to-LDS loads need a 16-byte aligned x
-    a.x_window = p->x_window && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    a.x_window = (reinterpret_cast<uintptr_t>(x) & 15) == 0 ? p->x_window : 0;
     a.win_span = p->win_span;
-    a.win_waves = p->win_waves;
     err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
   } else {
     BinnedArgs<V> a;
@@ -278,9 +276,6 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   const bool auto_ipt = p->ipt != 4 && p->ipt != 7 && p->ipt != 8 && p->ipt != 16;
   if (auto_ipt) p->ipt = 4;
   p->T = kWave * p->ipt;
-  // waves sharing one x window (env SPMV_WIN_WAVES: 4, 8 or 16)
-  p->win_waves = env_int("SPMV_WIN_WAVES", 4);
-  if (p->win_waves != 4 && p->win_waves != 8 && p->win_waves != 16) p->win_waves = 4;
   const int64_t W = M + nnz;
   p->P = (W + p->T - 1) / p->T;
 
@@ -311,7 +306,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   const size_t o_crow = take(sizeof(int32_t) * p->P);
   const size_t o_cval = take(vs * p->P);
   const size_t o_bins = take(sizeof(int32_t) * M);
-  const size_t o_wins = take(sizeof(int32_t) * 2 * ((p->P + kWavesPerBlock - 1) / kWavesPerBlock));
+  const int64_t win_ints = (int64_t)kWinTable * ((p->P + kWavesPerBlock - 1) / kWavesPerBlock);
+  const size_t o_wins = take(sizeof(int32_t) * win_ints);
   p->ws_bytes = off;
   if (env_int("SPMV_TEST_FAIL_ALLOC", 0)) {
     delete p;
@@ -378,8 +374,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     return bail(hip_fail(err, "plan: split search"));
   if (p->P > 0 && nnz > 0 &&
       (err = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
-                                 p->win_waves, window_bytes(p->ipt, (int)vs, p->win_waves),
-                                 p->win_span, p->stats, stream)) !=
+                                 kWavesPerBlock, window_bytes(p->ipt, (int)vs, kWavesPerBlock),
+                                 p->win_span, win_ints, p->stats, stream)) !=
           hipSuccess)
     return bail(hip_fail(err, "plan: window spans"));
   if (validate_cols &&
@@ -438,12 +434,17 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
       if (e == 0) xw = 1;
       else if (e == 1) xw = 2;
     }
-    const bool fits = host_stats[kStatWindowSamples] > 0 &&
-                      2 * host_stats[kStatWindowFits] >= host_stats[kStatWindowSamples];
-    // (no nonzeros: nothing to gather, and the span table is not computed)
-    p->x_window = p->merge_reduce == 2 && nnz > 0 &&
-                  window_bytes(p->ipt, (int)vs, p->win_waves) > 0 &&
-                  (xw == 2 || (xw == 0 && fits));
+    // x window: one interval where at least half of the stream workgroups'
+    // columns fit one, else up to three where at least half fit those (no
+    // nonzeros: nothing to gather, and the span table is not computed)
+    const int64_t S = host_stats[kStatWindowSamples];
+    const int64_t F1 = host_stats[kStatWindowFits], FM = host_stats[kStatWindowFitsMulti];
+    const bool room = p->merge_reduce == 2 && nnz > 0 &&
+                      window_bytes(p->ipt, (int)vs, kWavesPerBlock) > 0;
+    p->x_window = 0;
+    if (room && xw == 2) p->x_window = FM > F1 ? kWinIntervals : 1;
+    else if (room && xw == 0 && S > 0 && 2 * F1 >= S) p->x_window = 1;
+    else if (room && xw == 0 && S > 0 && 2 * FM >= S) p->x_window = kWinIntervals;
   }
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))

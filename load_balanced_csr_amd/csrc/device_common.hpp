@@ -96,6 +96,16 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// Streamed load of a T at byte offset off from base. With a wave-uniform
+// base (held in scalar registers) and a 32-bit offset the load takes the
+// scalar-base address form: one VGPR per address instead of a 64-bit pair,
+// and loads of several arrays at the same offset share it.
+template <typename T>
+__device__ __forceinline__ T ld_stream_at(const void* base, uint32_t off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const T*>(static_cast<const char*>(base) + off));
+}
+
 // 16-byte vectors for quad loads.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));

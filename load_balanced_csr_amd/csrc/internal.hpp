@@ -14,12 +14,15 @@ constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
 constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
 constexpr int kWindowBytes = 12288;      // cap of the staged x window (register form)
+constexpr int kWinIntervals = 3;         // column intervals of one x window
+constexpr int kWinTable = 8;             // int32 per window: {lo, len} x 3, total, 0
 
 // Waves per SIMD the stream kernel's register budget allows: 8 (at most 64
-// VGPRs) up to T = 448; larger partitions need more registers than that, and
-// spilling would cost more than the waves given up.
+// VGPRs) up to T = 448; larger partitions, and fp64 with the x window, need
+// more registers than that, and spilling would cost more than the waves
+// given up.
 constexpr int stream_min_waves(int vbytes, int ipt, bool win) {
-  return ipt >= 16 ? 4 : ipt < 8 ? 8 : vbytes == 4 ? 7 : win ? 6 : 8;
+  return ipt >= 16 ? (vbytes == 8 && win ? 3 : 4) : ipt < 8 ? 8 : vbytes == 4 ? 7 : win ? 5 : 8;
 }
 
 // LDS of the stream kernel. Its staging buffer per wave holds the T + T/8
@@ -42,9 +45,10 @@ enum StatSlot : int {
   kStatEmpty = 1,
   kStatError = 2,          // bit 0: row_ptr malformed, bit 1: column out of range
   kStatNonEmptyBins = 3,
-  kStatWindowFits = 4,     // stream workgroups whose columns fit the x window
+  kStatWindowFits = 4,     // stream workgroups whose columns fit one x interval
   kStatWindowSamples = 5,  // stream workgroups examined
-  kStatBinOffset = 6,      // kMaxBins + 1 entries
+  kStatWindowFitsMulti = 6,  // ... that fit kWinIntervals intervals
+  kStatBinOffset = 7,      // kMaxBins + 1 entries
   kStatCount = kStatBinOffset + kMaxBins + 1
 };
 
@@ -70,13 +74,16 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
-// Per group of `group` consecutive partitions: {first column, length} of the
-// chunk-aligned column span of the group's quads when it fits cap_bytes,
-// else {0, 0}; counts groups and fitting groups in stats.
+// Per group of `group` consecutive partitions: up to kWinIntervals
+// chunk-aligned column intervals covering the group's quads within
+// cap_bytes (kWinTable int32 per group, win_span holds win_span_ints);
+// counts groups and fitting groups in stats. hipErrorInvalidValue, and no
+// launch, when the table does not hold every group.
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
                                int32_t elem_bytes, int32_t group, int32_t cap_bytes,
-                               int32_t* win_span, int64_t* stats, hipStream_t s);
+                               int32_t* win_span, int64_t win_span_ints, int64_t* stats,
+                               hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>
@@ -100,9 +107,8 @@ struct MergeArgs {
   int32_t xcd_remap;
   int32_t stream;        // 1: rows never cross partitions (all rows <= T/8)
   int32_t stream_lanes;  // lanes per row in the stream reduction
-  int32_t x_window;      // 1: stream kernel with the workgroup's x window in LDS
-  const int32_t* win_span;  // per stream workgroup: first column, span (0: no window)
-  int32_t win_waves;        // waves per workgroup of the window kernel (4, 8, 16)
+  int32_t x_window;      // stream kernel's x window: 0 none, 1 one interval, 3 up to three
+  const int32_t* win_span;  // per stream workgroup: kWinTable int32 (window intervals)
 };
 
 // Streaming read of `bytes` (multiple of 16) at data; the xor of each 4 KiB

@@ -129,11 +129,30 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
 // which need no registers and overlap the partition's own loads; the gathers
 // then read LDS. Groups of G lanes sum each row (strided by G, then a
 // butterfly), 64 / G rows per round.
-template <typename V, int NR, int NN, bool WIN>
+// An x window of up to three column intervals, packed in LDS in column
+// order. The bounds are wave-uniform (scalar registers); an unused interval
+// has length 0.
+struct WindowBounds {
+  int lo[kWinIntervals], len[kWinIntervals];
+  // LDS slot of column col, or -1 when no interval holds it: the column
+  // belongs to the last non-empty interval starting at or below it.
+  template <int WK>
+  __device__ __forceinline__ int slot(int col) const {
+    if (WK == 1) return (unsigned)(col - lo[0]) < (unsigned)len[0] ? col - lo[0] : -1;
+    const bool a1 = len[1] > 0 && col >= lo[1];
+    const bool a2 = len[2] > 0 && col >= lo[2];
+    const int l = a2 ? lo[2] : a1 ? lo[1] : lo[0];
+    const int n = a2 ? len[2] : a1 ? len[1] : len[0];
+    const int base = a2 ? len[0] + len[1] : a1 ? len[0] : 0;
+    return (unsigned)(col - l) < (unsigned)n ? base + (col - l) : -1;
+  }
+};
+
+template <typename V, int NR, int NN, int WK>
 __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int nqr, int n0,
                                              int qn0, int nqn, int32_t* ends, V* prods,
                                              const V* xs, const int* win_meta) {
-  int wlo = 0, wlen = 0;
+  constexpr bool WIN = WK > 0;
   const int lane = lane_id();
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
@@ -141,13 +160,26 @@ __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int
   // all column quads, then all value quads, then the row ends (needed last,
   // for the LDS store): the gathers wait only for the columns, and nothing
   // computed from the row ends sits in front of the other loads
+  // (partition-relative 32-bit byte offsets from wave-uniform bases)
+  const int32_t* cb = a.col_idx + 4 * (int64_t)qn0;
+  const V* vb = a.val + 4 * (int64_t)qn0;
+  const int32_t* eb = a.row_ptr + 4 * (int64_t)qr0;
 #pragma unroll
-  for (int r = 0; r < NN; ++r) c[r] = load_quad<false>(a.col_idx, qn0 + min(lane + kWave * r, nqn - 1), 0);
+  for (int r = 0; r < NN; ++r)
+    c[r] = ld_stream_at<i32x4>(cb, 16u * (uint32_t)min(lane + kWave * r, nqn - 1));
 #pragma unroll
-  for (int r = 0; r < NN; ++r) v[r] = load_quad<false>(a.val, qn0 + min(lane + kWave * r, nqn - 1), 0);
+  for (int r = 0; r < NN; ++r) {
+    const uint32_t off = 16u * (uint32_t)min(lane + kWave * r, nqn - 1);
+    if constexpr (sizeof(V) == 4) {
+      v[r].v = ld_stream_at<f32x4>(vb, off);
+    } else {
+      v[r].lo = ld_stream_at<f64x2>(vb, 2 * off);
+      v[r].hi = ld_stream_at<f64x2>(vb, 2 * off + 16);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < NR; ++r)
-    e[r] = load_quad<false>(a.row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
+    e[r] = ld_stream_at<i32x4>(eb, 16u * (uint32_t)min(lane + kWave * r, nqr - 1));
   bool from_lds = false;
   if (WIN) {
     // The window's direct-to-LDS loads went out before this partition's
@@ -163,21 +195,26 @@ __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int
     wait_vmcnt_lds<NR + NN + NN * (int)(sizeof(V) / 4)>();
     __builtin_amdgcn_s_barrier();
     memory_order_point();
-    wlo = win_meta[0];
-    wlen = win_meta[1];
-    bool inside = wlen > 0;
+    WindowBounds w;
+#pragma unroll
+    for (int k = 0; k < kWinIntervals; ++k) {
+      w.lo[k] = k < WK ? __builtin_amdgcn_readfirstlane(win_meta[2 * k]) : 0;
+      w.len[k] = k < WK ? __builtin_amdgcn_readfirstlane(win_meta[2 * k + 1]) : 0;
+    }
+    bool inside = true;
 #pragma unroll
     for (int r = 0; r < NN; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) inside &= (unsigned)(c[r][j] - wlo) < (unsigned)wlen;
+      for (int j = 0; j < 4; ++j) inside &= w.slot<WK>(c[r][j]) >= 0;
     from_lds = __ballot(!inside) == 0;
+    if (from_lds) {
+#pragma unroll
+      for (int r = 0; r < NN; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * xs[w.slot<WK>(c[r][j])]);
+    }
   }
-  if (from_lds) {
-#pragma unroll
-    for (int r = 0; r < NN; ++r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * xs[c[r][j] - wlo]);
-  } else {
+  if (!from_lds) {
 #pragma unroll
     for (int r = 0; r < NN; ++r)
 #pragma unroll
@@ -192,26 +229,26 @@ __device__ __forceinline__ void stream_stage(const MergeArgs<V>& a, int qr0, int
   for (int r = 0; r < NN; ++r) store_quad(prods, min(lane + kWave * r, nqn - 1), v[r]);
 }
 
-template <typename V, int NR, int RQN, bool WIN>
+template <typename V, int NR, int RQN, int WK>
 __device__ __forceinline__ void stream_stage_nn(const MergeArgs<V>& a, int qr0, int nqr, int n0,
                                                 int qn0, int nqn, int32_t* ends, V* prods,
                                                 const V* xs, const int* win_meta) {
   const int rounds = (nqn + kWave - 1) / kWave;
   if (rounds == 0)
-    stream_stage<V, NR, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
+    stream_stage<V, NR, 0, WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
   else if (rounds == 1 || RQN < 2)
-    stream_stage<V, NR, (RQN < 1 ? 0 : 1), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+    stream_stage<V, NR, (RQN < 1 ? 0 : 1), WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
                                                win_meta);
   else if (rounds == 2 || RQN < 3)
-    stream_stage<V, NR, 2, WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
+    stream_stage<V, NR, 2, WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs, win_meta);
   else if (rounds == 3 || RQN < 4)
-    stream_stage<V, NR, (RQN < 3 ? 2 : 3), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+    stream_stage<V, NR, (RQN < 3 ? 2 : 3), WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
                                                win_meta);
   else if (rounds == 4 || RQN < 5)
-    stream_stage<V, NR, (RQN < 4 ? 2 : 4), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+    stream_stage<V, NR, (RQN < 4 ? 2 : 4), WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
                                                win_meta);
   else
-    stream_stage<V, NR, (RQN < 5 ? 2 : 5), WIN>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
+    stream_stage<V, NR, (RQN < 5 ? 2 : 5), WK>(a, qr0, nqr, n0, qn0, nqn, ends, prods, xs,
                                                win_meta);
 }
 
@@ -297,11 +334,12 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
   }
 }
 
-// WPB waves per workgroup (4, or 8 / 16 with the window: the wider the
-// workgroup, the less x each partition fetches into LDS).
-template <typename V, int IPT, bool WIN, int WPB>
-__global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN)) void merge_stream_kernel(
+// WK: x window of 0, 1 or kWinIntervals column intervals; WPB waves per
+// workgroup.
+template <typename V, int IPT, int WK, int WPB>
+__global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 0)) void merge_stream_kernel(
     const MergeArgs<V> a, const int32_t* __restrict__ rb) {
+  constexpr bool WIN = WK > 0;
   constexpr int T = kWave * IPT;
   constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
   constexpr int BUF = stream_buf_elems(IPT);  // per-wave buffer, elements of V
@@ -334,20 +372,36 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN))
   // with the window every wave must reach the block's barrier
   if (!WIN && nrows == 0) return;
 
-  __shared__ int s_win[2];
+  __shared__ int s_win[kWinTable];
   if (WIN) {
-    // x[wlo, wlo + wlen): chunk aligned and inside x (the plan guarantees it)
-    const int wlo = a.win_span[2 * blk];
-    const int wlen = a.win_span[2 * blk + 1];
+    // the window's intervals: chunk aligned and inside x (the plan guarantees
+    // it), packed one after the other in LDS
+    const int32_t* ws = a.win_span + (int64_t)kWinTable * blk;
+    const int lo0 = ws[0], len0 = ws[1];
+    const int lo1 = WK > 1 ? ws[2] : 0, len1 = WK > 1 ? ws[3] : 0;
+    const int lo2 = WK > 1 ? ws[4] : 0, len2 = WK > 1 ? ws[5] : 0;
     if (threadIdx.x == 0) {
-      s_win[0] = wlo;
-      s_win[1] = wlen;
+      s_win[0] = lo0;
+      s_win[1] = len0;
+      if (WK > 1) {
+        s_win[2] = lo1;
+        s_win[3] = len1;
+        s_win[4] = lo2;
+        s_win[5] = len2;
+      }
     }
-    const int nch = wlen / E;
+    const int c1 = len0 / E, c2 = c1 + len1 / E;         // first chunk of intervals 1, 2
+    const int nch = c2 + len2 / E;
 #pragma unroll
     for (int r = 0; r < (WCHUNKS + WPB * kWave - 1) / (WPB * kWave); ++r) {
       const int first = WPB * kWave * r + kWave * wave;   // this wave's first chunk
-      if (first < nch && first + lane < nch) lds_dma16(a.x + wlo + E * (first + lane), s_x + E * first);
+      const int ch = first + lane;
+      if (first < nch && ch < nch) {
+        const int src = WK == 1 ? lo0 + E * ch
+                        : ch >= c2 ? lo2 + E * (ch - c2)
+                        : ch >= c1 ? lo1 + E * (ch - c1) : lo0 + E * ch;
+        lds_dma16(a.x + src, s_x + E * first);
+      }
     }
     // the staging loads must be issued after these (the window wait counts them)
     memory_order_point();
@@ -376,11 +430,11 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WIN))
     stage_safe<V, RQR, RQN, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
                                    a.nnz, qn0, nqn, ends_q, buf, nowin);
   } else if (nqr == 0) {
-    stream_stage<V, 0, 0, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
+    stream_stage<V, 0, 0, WK>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   } else if (nqr <= kWave || RQR < 2) {
-    stream_stage_nn<V, 1, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
+    stream_stage_nn<V, 1, RQN, WK>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   } else {
-    stream_stage_nn<V, RQR, RQN, WIN>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
+    stream_stage_nn<V, RQR, RQN, WK>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   }
   if (nrows == 0) return;
   wave_sync();
@@ -432,10 +486,11 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
   }
 }
 
-template <typename V, int IPT, int WPB>
+template <typename V, int IPT, int WK>
 hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
+  constexpr int WPB = kWavesPerBlock;
   if constexpr (stream_window_bytes(IPT, sizeof(V), WPB) > 0) {
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, true, WPB>), dim3((a.P + WPB - 1) / WPB),
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, WK, WPB>), dim3((a.P + WPB - 1) / WPB),
                        dim3(WPB * kWave), 0, s, a, a.row_bounds);
     return hipGetLastError();
   }
@@ -445,15 +500,12 @@ hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
 template <typename V, int IPT>
 hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (a.stream && a.x_window) {
-    switch (a.win_waves) {
-      case 4: return launch_window<V, IPT, 4>(a, s);
-      case 8: return launch_window<V, IPT, 8>(a, s);
-      case 16: return launch_window<V, IPT, 16>(a, s);
-      default: return hipErrorInvalidValue;
-    }
+  if (a.stream && a.x_window == 1) {
+    return launch_window<V, IPT, 1>(a, s);
+  } else if (a.stream && a.x_window > 1) {
+    return launch_window<V, IPT, kWinIntervals>(a, s);
   } else if (a.stream) {
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, false, kWavesPerBlock>), dim3(blocks),
+    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, 0, kWavesPerBlock>), dim3(blocks),
                        dim3(kBlock), 0, s, a, a.row_bounds);
   } else
     hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);

@@ -219,22 +219,30 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
   if (bad) atomicOr((unsigned long long*)&stats[kStatError], 2ull);
 }
 
-// For each group of 4 consecutive partitions (one stream workgroup), taken
-// as whole rows [split_row[4g], split_row[4g + 4]): the first column its
-// entries use and the span up to the last one, or span 0 when the span is
-// cap entries or more. The range is widened to whole 16-byte quads, as the
-// exec kernel stages it, so the few neighbouring-row entries of the edge
-// quads are inside the span too; the span itself is widened to whole 16-byte
-// chunks of x (e elements each), which the exec kernel copies with 16-byte
-// direct-to-LDS loads, and dropped if that would reach past x. Also counts the groups whose span fits. Only chooses
-// and prepares a kernel variant: the exec kernel checks every column against
-// the span again.
+// x window of each group of `group` consecutive stream partitions: up to
+// kWinIntervals column intervals that together cover every column of the
+// group's nonzero quads (the range widened to whole 16-byte quads, as the
+// exec kernel stages it), each widened to whole 16-byte chunks of x (e
+// elements) and kept inside x's full chunks, their total within cap entries.
+// One interval (the whole span) when that fits; otherwise the span is cut
+// into 256 buckets, the runs of buckets that hold columns become the
+// intervals (at most kWinIntervals runs), tightened to the exact min and max
+// column of each run. Writes win_span[8g ..]: {lo, len} per interval (len 0:
+// unused), then the total length and 0. Counts the groups whose columns fit
+// one interval and those that fit the intervals. This only prepares a
+// kernel variant: the exec kernel checks every column against the intervals
+// again and gathers from global x when one is outside.
 __global__ __launch_bounds__(kBlock) void window_span_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ split_row, int32_t P, int32_t nnz, int32_t N, int32_t e,
     int32_t cap, int32_t group, int32_t* __restrict__ win_span, int64_t* stats) {
+  constexpr int NB = kBlock;            // buckets
   __shared__ int32_t s_lo[kWavesPerBlock], s_hi[kWavesPerBlock];
+  __shared__ int32_t s_flag[NB], s_run[NB];
+  __shared__ int32_t s_rlo[NB], s_rhi[NB];
+  __shared__ int32_t s_nrun;
   const int g = blockIdx.x;
+  const int t = threadIdx.x;
   const int p0 = g * group, p1 = min(p0 + group, P);
   int k0 = row_ptr[split_row[p0]], k1 = row_ptr[split_row[p1]];
   if (k1 > k0) {
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
     k1 = min((k1 + 3) & ~3, nnz);
   }
   int lo = INT_MAX, hi = INT_MIN;
-  for (int k = k0 + threadIdx.x; k < k1; k += kBlock) {
+  for (int k = k0 + t; k < k1; k += kBlock) {
     const int c = col_idx[k];
     lo = min(lo, c);
     hi = max(hi, c);
@@ -252,20 +260,85 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
     hi = max(hi, __shfl_xor(hi, o, kWave));
   }
   if (lane_id() == 0) {
-    s_lo[threadIdx.x / kWave] = lo;
-    s_hi[threadIdx.x / kWave] = hi;
+    s_lo[t / kWave] = lo;
+    s_hi[t / kWave] = hi;
+  }
+  s_flag[t] = 0;
+  s_rlo[t] = INT_MAX;
+  s_rhi[t] = INT_MIN;
+  __syncthreads();
+  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
+  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
+  int32_t* out = win_span + (int64_t)kWinTable * g;
+  const int last_full = (N / e) * e - 1;   // last column of x's full chunks
+  // (lo, hi) are block-uniform from here on
+  if (hi < lo) {
+    if (t < kWinTable) out[t] = 0;
+    if (t == 0) atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
+    return;
+  }
+  const int alo = lo & ~(e - 1), ahi = hi | (e - 1);
+  if (ahi <= last_full && ahi - alo < cap) {            // one interval
+    if (t < kWinTable) out[t] = t == 0 ? alo : (t == 1 || t == 2 * kWinIntervals) ? ahi - alo + 1 : 0;
+    if (t == 0) {
+      atomicAdd((unsigned long long*)&stats[kStatWindowFits], 1ull);
+      atomicAdd((unsigned long long*)&stats[kStatWindowFitsMulti], 1ull);
+      atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
+    }
+    return;
+  }
+  // buckets of width w over [lo, hi]; mark the ones that hold a column
+  const int64_t span = (int64_t)hi - lo + 1;
+  const int w = (int)((span + NB - 1) / NB);
+  for (int k = k0 + t; k < k1; k += kBlock) s_flag[(int)(((int64_t)col_idx[k] - lo) / w)] = 1;
+  __syncthreads();
+  // runs of marked buckets: run id by a block scan of the run starts
+  const int start = s_flag[t] && (t == 0 || !s_flag[t - 1]);
+  s_run[t] = start;
+  __syncthreads();
+  for (int o = 1; o < NB; o <<= 1) {
+    const int v = t >= o ? s_run[t - o] : 0;
+    __syncthreads();
+    s_run[t] += v;
+    __syncthreads();
+  }
+  if (t == NB - 1) s_nrun = s_run[t];
+  __syncthreads();
+  const int nrun = s_nrun;
+  if (nrun <= kWinIntervals) {
+    // exact min / max column of each run (run id of bucket b: s_run[b] - 1)
+    for (int k = k0 + t; k < k1; k += kBlock) {
+      const int c = col_idx[k];
+      const int r = s_run[(int)(((int64_t)c - lo) / w)] - 1;
+      atomicMin(&s_rlo[r], c);
+      atomicMax(&s_rhi[r], c);
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kWavesPerBlock; ++w) {
-      lo = min(lo, s_lo[w]);
-      hi = max(hi, s_hi[w]);
+  if (t == 0) {
+    int ilo[kWinIntervals], ilen[kWinIntervals], n = 0, total = 0;
+    bool ok = nrun <= kWinIntervals;
+    for (int r = 0; ok && r < nrun; ++r) {
+      int a = s_rlo[r] & ~(e - 1), b = s_rhi[r] | (e - 1);
+      if (b > last_full) ok = false;               // a column in x's last partial chunk
+      if (n > 0 && a <= ilo[n - 1] + ilen[n - 1]) {   // touches the previous one: merge
+        a = ilo[n - 1];
+        total -= ilen[n - 1];
+        --n;
+      }
+      ilo[n] = a;
+      ilen[n] = b - a + 1;
+      total += ilen[n];
+      ++n;
     }
-    const int alo = lo & ~(e - 1), ahi = hi | (e - 1);
-    const bool fits = hi >= lo && ahi < N && ahi - alo < cap;
-    win_span[2 * g] = fits ? alo : 0;
-    win_span[2 * g + 1] = fits ? ahi - alo + 1 : 0;
-    if (fits) atomicAdd((unsigned long long*)&stats[kStatWindowFits], 1ull);
+    ok = ok && total <= cap;
+    for (int k = 0; k < kWinIntervals; ++k) {
+      out[2 * k] = ok && k < n ? ilo[k] : 0;
+      out[2 * k + 1] = ok && k < n ? ilen[k] : 0;
+    }
+    out[2 * kWinIntervals] = ok ? total : 0;
+    for (int k = 2 * kWinIntervals + 1; k < kWinTable; ++k) out[k] = 0;
+    if (ok) atomicAdd((unsigned long long*)&stats[kStatWindowFitsMulti], 1ull);
     atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
   }
 }
@@ -319,9 +392,12 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
                                int32_t elem_bytes, int32_t group, int32_t cap_bytes,
-                               int32_t* win_span, int64_t* stats, hipStream_t s) {
+                               int32_t* win_span, int64_t win_span_ints, int64_t* stats,
+                               hipStream_t s) {
   if (P <= 0 || cap_bytes <= 0) return hipSuccess;
+  if (group <= 0) return hipErrorInvalidValue;
   const int64_t groups = (P + group - 1) / group;
+  if (groups * kWinTable > win_span_ints) return hipErrorInvalidValue;
   hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
                      col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
                      cap_bytes / elem_bytes, group, win_span, stats);

@@ -141,6 +141,29 @@ def test_window_with_jumping_bands(variant, dtype):
     plan.destroy()
 
 
+@pytest.mark.parametrize("dtype,variant", [(np.float32, None), (np.float32, "merge7_xwin"),
+                                           (np.float32, "merge8_xwin"), (np.float64, None),
+                                           (np.float64, "merge8_xwin")],
+                         ids=["f32-auto", "f32-merge7", "f32-merge8", "f64-auto", "f64-merge8"])
+def test_window_three_bands(variant, dtype):
+    """5-point stencil on a 2048 x 2048 grid: a workgroup's columns sit in
+    three bands (rows above, own, below) 2048 apart, too wide together for one
+    window interval but short each: the three-interval window is chosen."""
+    w = synth.laplacian(n=2048)
+    va, x = w.values.astype(dtype), w.x.astype(dtype)
+    m = DevMatrix(w.row_ptr, w.col_idx, va, w.M, w.N)
+    plan = m.plan(variant)
+    info = plan.info
+    log("case bands", variant, info["items_per_thread"], info["x_window_intervals"])
+    assert info["merge_reduce"] == "stream" and info["x_window_intervals"] == 3, info
+    y0 = synth.uniform(w.M, 33, synth.S_Y, dtype)
+    for a, b in ((1.0, 0.0), (-1.5, 0.5)):
+        y = run(plan, x, a, b, y0 if b != 0 else None, dtype)
+        check(y, w.row_ptr, w.col_idx, va, x, a, b, y0 if b != 0 else None,
+              what="bands/%s" % variant)
+    plan.destroy()
+
+
 @pytest.mark.parametrize("variant", ALL)
 def test_no_entries(variant):
     # every row empty: y = beta * y exactly (0 with beta = 0, y not read)
