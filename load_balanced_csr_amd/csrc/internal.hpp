@@ -15,7 +15,7 @@ constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
 constexpr int kWindowBytes = 12288;      // cap of the staged x window (register form)
 constexpr int kWinIntervals = 3;         // column intervals of one x window
-constexpr int kWinTable = 8;             // int32 per window: {lo, len} x 3, total, 0
+constexpr int kWinTable = 8;             // int32 per window: {lo, len} x 3, total, flags
 
 // Waves per SIMD the stream kernel's register budget allows: 8 (at most 64
 // VGPRs) up to T = 448; larger partitions, and fp64 with the x window, need

@@ -228,14 +228,14 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
 // into 256 buckets, the runs of buckets that hold columns become the
 // intervals (at most kWinIntervals runs), tightened to the exact min and max
 // column of each run. Writes win_span[8g ..]: {lo, len} per interval (len 0:
-// unused), then the total length and 0. Counts the groups whose columns fit
-// one interval and those that fit the intervals. This only prepares a
+// unused), then the total length and flags (bit 0: the columns fit one
+// interval, bit 1: they fit the intervals). This only prepares a
 // kernel variant: the exec kernel checks every column against the intervals
 // again and gathers from global x when one is outside.
 __global__ __launch_bounds__(kBlock) void window_span_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ split_row, int32_t P, int32_t nnz, int32_t N, int32_t e,
-    int32_t cap, int32_t group, int32_t* __restrict__ win_span, int64_t* stats) {
+    int32_t cap, int32_t group, int32_t* __restrict__ win_span) {
   constexpr int NB = kBlock;            // buckets
   __shared__ int32_t s_lo[kWavesPerBlock], s_hi[kWavesPerBlock];
   __shared__ int32_t s_flag[NB], s_run[NB];
@@ -274,23 +274,19 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
   // (lo, hi) are block-uniform from here on
   if (hi < lo) {
     if (t < kWinTable) out[t] = 0;
-    if (t == 0) atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
     return;
   }
   const int alo = lo & ~(e - 1), ahi = hi | (e - 1);
   if (ahi <= last_full && ahi - alo < cap) {            // one interval
-    if (t < kWinTable) out[t] = t == 0 ? alo : (t == 1 || t == 2 * kWinIntervals) ? ahi - alo + 1 : 0;
-    if (t == 0) {
-      atomicAdd((unsigned long long*)&stats[kStatWindowFits], 1ull);
-      atomicAdd((unsigned long long*)&stats[kStatWindowFitsMulti], 1ull);
-      atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
-    }
+    if (t < kWinTable)
+      out[t] = t == 0 ? alo : (t == 1 || t == 2 * kWinIntervals) ? ahi - alo + 1
+                        : t == kWinTable - 1 ? 3 : 0;
     return;
   }
-  // buckets of width w over [lo, hi]; mark the ones that hold a column
-  const int64_t span = (int64_t)hi - lo + 1;
-  const int w = (int)((span + NB - 1) / NB);
-  for (int k = k0 + t; k < k1; k += kBlock) s_flag[(int)(((int64_t)col_idx[k] - lo) / w)] = 1;
+  // buckets of width w over [lo, hi] (hi - lo < 2^31: columns are int32 and
+  // non-negative); mark the ones that hold a column
+  const unsigned w = ((unsigned)(hi - lo) + NB) / NB;
+  for (int k = k0 + t; k < k1; k += kBlock) s_flag[(unsigned)(col_idx[k] - lo) / w] = 1;
   __syncthreads();
   // runs of marked buckets: run id by a block scan of the run starts
   const int start = s_flag[t] && (t == 0 || !s_flag[t - 1]);
@@ -306,12 +302,33 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
   __syncthreads();
   const int nrun = s_nrun;
   if (nrun <= kWinIntervals) {
-    // exact min / max column of each run (run id of bucket b: s_run[b] - 1)
+    // exact min / max column of each run (run id of bucket b: s_run[b] - 1),
+    // per lane, then per wave, then one LDS atomic per wave and run
+    int rlo[kWinIntervals], rhi[kWinIntervals];
+#pragma unroll
+    for (int q = 0; q < kWinIntervals; ++q) {
+      rlo[q] = INT_MAX;
+      rhi[q] = INT_MIN;
+    }
     for (int k = k0 + t; k < k1; k += kBlock) {
       const int c = col_idx[k];
-      const int r = s_run[(int)(((int64_t)c - lo) / w)] - 1;
-      atomicMin(&s_rlo[r], c);
-      atomicMax(&s_rhi[r], c);
+      const int r = s_run[(unsigned)(c - lo) / w] - 1;
+#pragma unroll
+      for (int q = 0; q < kWinIntervals; ++q) {
+        rlo[q] = r == q ? min(rlo[q], c) : rlo[q];
+        rhi[q] = r == q ? max(rhi[q], c) : rhi[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kWinIntervals; ++q) {
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        rlo[q] = min(rlo[q], __shfl_xor(rlo[q], o, kWave));
+        rhi[q] = max(rhi[q], __shfl_xor(rhi[q], o, kWave));
+      }
+      if (lane_id() == 0 && q < nrun) {
+        atomicMin(&s_rlo[q], rlo[q]);
+        atomicMax(&s_rhi[q], rhi[q]);
+      }
     }
   }
   __syncthreads();
@@ -337,9 +354,37 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
       out[2 * k + 1] = ok && k < n ? ilen[k] : 0;
     }
     out[2 * kWinIntervals] = ok ? total : 0;
-    for (int k = 2 * kWinIntervals + 1; k < kWinTable; ++k) out[k] = 0;
-    if (ok) atomicAdd((unsigned long long*)&stats[kStatWindowFitsMulti], 1ull);
-    atomicAdd((unsigned long long*)&stats[kStatWindowSamples], 1ull);
+    for (int k = 2 * kWinIntervals + 1; k < kWinTable - 1; ++k) out[k] = 0;
+    out[kWinTable - 1] = ok ? 2 : 0;
+  }
+}
+
+// Sums the window table's flags into the statistics block: groups examined,
+// groups that fit one interval, groups that fit the intervals. A grid-stride
+// pass with one global atomic per workgroup and counter (thousands of groups
+// each adding to one address would serialise on it).
+__global__ __launch_bounds__(kBlock) void window_count_kernel(const int32_t* __restrict__ win_span,
+                                                              int32_t groups, int64_t* stats) {
+  __shared__ int s_sum[3][kWavesPerBlock];
+  int cnt[3] = {0, 0, 0};   // groups, fit one interval, fit the intervals
+  for (int g = blockIdx.x * kBlock + threadIdx.x; g < groups; g += gridDim.x * kBlock) {
+    const int f = win_span[(int64_t)kWinTable * g + kWinTable - 1];
+    cnt[0] += 1;
+    cnt[1] += f & 1;
+    cnt[2] += (f >> 1) & 1;
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    for (int o = kWave / 2; o > 0; o >>= 1) cnt[q] += __shfl_xor(cnt[q], o, kWave);
+    if (lane_id() == 0) s_sum[q][threadIdx.x / kWave] = cnt[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    const int q = threadIdx.x;
+    unsigned long long sum = 0;
+    for (int i = 0; i < kWavesPerBlock; ++i) sum += (unsigned)s_sum[q][i];
+    const int slot = q == 0 ? kStatWindowSamples : q == 1 ? kStatWindowFits : kStatWindowFitsMulti;
+    atomicAdd((unsigned long long*)&stats[slot], sum);
   }
 }
 
@@ -400,7 +445,11 @@ hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
   if (groups * kWinTable > win_span_ints) return hipErrorInvalidValue;
   hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
                      col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
-                     cap_bytes / elem_bytes, group, win_span, stats);
+                     cap_bytes / elem_bytes, group, win_span);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(window_count_kernel, dim3((int)std::min<int64_t>(n_blocks(groups, kBlock), 64)),
+                     dim3(kBlock), 0, s, win_span, (int32_t)groups, stats);
   return hipGetLastError();
 }
 
