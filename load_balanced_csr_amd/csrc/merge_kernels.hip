@@ -338,7 +338,7 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
 // workgroup.
 template <typename V, int IPT, int WK, int WPB>
 __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 0)) void merge_stream_kernel(
-    const MergeArgs<V> a, const int32_t* __restrict__ rb) {
+    const MergeArgs<V> a, const int32_t* __restrict__ rb, const int32_t* __restrict__ wt) {
   constexpr bool WIN = WK > 0;
   constexpr int T = kWave * IPT;
   constexpr int CAP = T + T / 8;            // rows + nonzeros of one partition
@@ -375,8 +375,8 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 
   __shared__ int s_win[kWinTable];
   if (WIN) {
     // the window's intervals: chunk aligned and inside x (the plan guarantees
-    // it), packed one after the other in LDS
-    const int32_t* ws = a.win_span + (int64_t)kWinTable * blk;
+    // it), packed one after the other in LDS; like the bounds, a scalar read
+    const int32_t* ws = wt + (int64_t)kWinTable * blk;
     const int lo0 = ws[0], len0 = ws[1];
     const int lo1 = WK > 1 ? ws[2] : 0, len1 = WK > 1 ? ws[3] : 0;
     const int lo2 = WK > 1 ? ws[4] : 0, len2 = WK > 1 ? ws[5] : 0;
@@ -491,7 +491,7 @@ hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
   constexpr int WPB = kWavesPerBlock;
   if constexpr (stream_window_bytes(IPT, sizeof(V), WPB) > 0) {
     hipLaunchKernelGGL((merge_stream_kernel<V, IPT, WK, WPB>), dim3((a.P + WPB - 1) / WPB),
-                       dim3(WPB * kWave), 0, s, a, a.row_bounds);
+                       dim3(WPB * kWave), 0, s, a, a.row_bounds, a.win_span);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;   // the plan never asks for it
@@ -506,7 +506,7 @@ hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
     return launch_window<V, IPT, kWinIntervals>(a, s);
   } else if (a.stream) {
     hipLaunchKernelGGL((merge_stream_kernel<V, IPT, 0, kWavesPerBlock>), dim3(blocks),
-                       dim3(kBlock), 0, s, a, a.row_bounds);
+                       dim3(kBlock), 0, s, a, a.row_bounds, a.win_span);
   } else
     hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();

@@ -51,6 +51,10 @@ class OracleLib:
             f = getattr(lib, name)
             f.argtypes = [p, p, p, p, d, d, p, p, i64, p, p]
             f.restype = ctypes.c_int
+        for name in ("oracle_spmm_f32", "oracle_spmm_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [i64, p, p, p, i64, p, i64, d, d, p, i64, p, p]
+            f.restype = ctypes.c_int
         lib.oracle_merge_splits.argtypes = [i64, i64, p, i64, p, p]
         lib.oracle_merge_splits.restype = i64
         lib.oracle_bins.argtypes = [i64, p, i32, p, p, p, p]
@@ -97,6 +101,34 @@ class OracleLib:
         f = self.lib.oracle_spmv_rows_f32 if dt == np.float32 else self.lib.oracle_spmv_rows_f64
         rc = f(_ptr(rp), _ptr(col), _ptr(val), _ptr(xx), float(alpha), float(beta), _ptr(yo),
                _ptr(rows), rows.size, _ptr(ref), _ptr(scale))
+        assert rc == 0
+        return ref, scale
+
+    def spmm(self, row_ptr, col_idx, values, X, alpha: float = 1.0, beta: float = 0.0,
+             Y_old=None) -> Tuple[np.ndarray, np.ndarray]:
+        """ref = alpha*A*X + beta*Y_old (M x k) in fp64, and scale[i, c] =
+        sum_e |a_ie * X[col_e, c]|. X is N x k, Y_old M x k (row-major, any
+        row stride); their dtype must match ``values``."""
+        values = np.asarray(values)
+        dt = values.dtype
+        if dt not in (np.float32, np.float64):
+            raise TypeError("values must be float32 or float64")
+        if beta != 0.0 and Y_old is None:
+            raise ValueError("beta != 0 needs Y_old")
+        rp, col, val = _c(row_ptr, np.int32), _c(col_idx, np.int32), _c(values, dt)
+        XX = _c(X, dt)
+        if XX.ndim != 2:
+            raise ValueError("X must be 2-D")
+        k = XX.shape[1]
+        yo = _c(Y_old, dt) if beta != 0.0 else None
+        if yo is not None and yo.shape[1] != k:
+            raise ValueError("Y_old must have k columns")
+        M = rp.size - 1
+        ref = np.empty((M, k), dtype=np.float64)
+        scale = np.empty((M, k), dtype=np.float64)
+        f = self.lib.oracle_spmm_f32 if dt == np.float32 else self.lib.oracle_spmm_f64
+        rc = f(M, _ptr(rp), _ptr(col), _ptr(val), k, _ptr(XX), k, float(alpha), float(beta),
+               _ptr(yo), k, _ptr(ref), _ptr(scale))
         assert rc == 0
         return ref, scale
 
@@ -154,6 +186,10 @@ def spmv_rows(*args, **kw):
     return _default().spmv_rows(*args, **kw)
 
 
+def spmm(*args, **kw):
+    return _default().spmm(*args, **kw)
+
+
 def merge_splits(*args, **kw):
     return _default().merge_splits(*args, **kw)
 
@@ -183,7 +219,8 @@ def within_tolerance(y, ref, scale, alpha: float, beta: float, y_old=None,
 
     |y_i - ref_i| <= rtol * (|alpha| * scale_i + |beta| * |y_old_i|) for every
     row, and rows with no entries (when row_ptr is given) must equal
-    fl(beta * y_old_i) exactly (0 when beta == 0). Values compare as values,
+    fl(beta * y_old_i) exactly (0 when beta == 0). y may also be M x k (one
+    column per right-hand side); the rule then holds per element. Values compare as values,
     so -0 equals +0. NaN in y is a failure unless ref is NaN there."""
     y = np.asarray(y)
     if rtol is None:
@@ -199,6 +236,8 @@ def within_tolerance(y, ref, scale, alpha: float, beta: float, y_old=None,
     if row_ptr is not None:
         rp = np.asarray(row_ptr)
         empty = (rp[1:] - rp[:-1]) == 0
+        if y.ndim == 2:                      # M x k (multi-vector): per row
+            empty = empty[:, None]
         if beta != 0.0:
             want = (np.asarray(y_old, dtype=y.dtype) * y.dtype.type(beta)).astype(np.float64)
         else:

@@ -25,6 +25,19 @@
  *      identity, diagonal, integer row sums, the 2-D Laplacian closed forms,
  *      power-of-two linearity, empty rows, and the worked CSR example.
  *
+ *  oracle_spmm_f32 / _f64:
+ *      multi-vector SpMV (SpMM), PPoPP'23 page, Section 5.3, Listing 4: the
+ *      SpMV of Listing 3 with one more loop over the columns of the dense
+ *      matrix, each output column the sum over a row's atoms of the value
+ *      times the dense entry in the atom's column index row and that output
+ *      column (the extracted listing garbles that index; reading in the
+ *      design notes). The dense matrices are row-major with leading
+ *      dimensions ldx / ldy; the same fp64 sum in storage order per column,
+ *      the same alpha/beta update and the same scale as the SpMV above.
+ *      Pinned by tests/pins.py: numpy's dense product on tiny non-square
+ *      inputs, identity, 2-D Laplacian closed forms per column, and exact
+ *      alpha/beta arithmetic.
+ *
  *  oracle_merge_splits:
  *      merge-path partition, PPoPP'23 page, Section 5.2.1: every nonzero and
  *      every row counts as one unit of work; units are split evenly. Written
@@ -92,6 +105,49 @@ int oracle_spmv_f64(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
   for (int64_t i = 0; i < M; ++i) {
     double t = row_sum_f64(row_ptr, col_idx, values, x, i, &scale[i]);
     ref[i] = alpha * t + (beta != 0.0 ? beta * y_old[i] : 0.0);
+  }
+  return 0;
+}
+
+/* ---- SpMM: Y_ref = alpha * (A X) + beta * Y_old, k columns, fp64 --------- */
+
+/* ref and scale are M x k, row-major with leading dimension k. */
+int oracle_spmm_f32(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
+                    const float* values, int64_t k, const float* X, int64_t ldx,
+                    double alpha, double beta, const float* Y_old, int64_t ldy,
+                    double* ref, double* scale) {
+  if (beta != 0.0 && Y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t c = 0; c < k; ++c) {
+      double t = 0.0, s = 0.0;
+      for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+        double p = (double)values[e] * (double)X[(int64_t)col_idx[e] * ldx + c];
+        t = t + p;
+        s = s + fabs(p);
+      }
+      ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * (double)Y_old[i * ldy + c] : 0.0);
+      scale[i * k + c] = s;
+    }
+  }
+  return 0;
+}
+
+int oracle_spmm_f64(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
+                    const double* values, int64_t k, const double* X, int64_t ldx,
+                    double alpha, double beta, const double* Y_old, int64_t ldy,
+                    double* ref, double* scale) {
+  if (beta != 0.0 && Y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t c = 0; c < k; ++c) {
+      double t = 0.0, s = 0.0;
+      for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+        double p = values[e] * X[(int64_t)col_idx[e] * ldx + c];
+        t = t + p;
+        s = s + fabs(p);
+      }
+      ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * Y_old[i * ldy + c] : 0.0);
+      scale[i * k + c] = s;
+    }
   }
   return 0;
 }

@@ -268,6 +268,83 @@ def pin_bins(o):
             assert np.all(np.diff(seg) > 0), "ascending within a bin"
 
 
+def _dense_matmat_ascending(A, X):
+    """Y[i, c] = sum over j ascending of A_ij * X_jc in fp64, by hand, and the
+    matching sums of |A_ij * X_jc|."""
+    M, N = A.shape
+    k = X.shape[1]
+    Y = np.empty((M, k), dtype=np.float64)
+    S = np.empty((M, k), dtype=np.float64)
+    for c in range(k):
+        Y[:, c], S[:, c] = _dense_matvec_ascending(A, X[:, c])
+    return Y, S
+
+
+def pin_spmm_dense(o):
+    """CSR times a dense N x k matrix equals the dense product bit for bit
+    (ascending sums) on tiny random non-square inputs with M, N, k distinct,
+    and numpy's matrix product within fp64 rounding."""
+    rng = np.random.default_rng(17)
+    for trial in range(12):
+        M, N, k = int(rng.integers(1, 30)), int(rng.integers(1, 30)), int(rng.integers(1, 9))
+        while len({M, N, k}) < 3:
+            N += 1
+            k = k + 1 if k == M or k == N else k
+        dt = F32 if trial % 2 == 0 else F64
+        A = np.where(rng.random((M, N)) < 0.3, rng.uniform(-1, 1, (M, N)), 0.0).astype(dt)
+        A[rng.random(M) < 0.2, :] = 0
+        X = rng.uniform(-1, 1, (N, k)).astype(dt)
+        rp, col, val = _csr_from_dense(A)
+        ref, scale = o.spmm(rp, col, val, X)
+        want, wscale = _dense_matmat_ascending(A, X)
+        assert np.array_equal(ref, want), ("spmm dense", trial)
+        assert np.array_equal(scale, wscale), ("spmm scale", trial)
+        mm = A.astype(np.float64) @ X.astype(np.float64)
+        assert np.allclose(ref, mm, rtol=0, atol=1e-12 * max(1, N)), ("spmm vs matmul", trial)
+
+
+def pin_spmm_identity_and_laplacian(o):
+    """A = I gives Y = alpha X + beta Y_old (dyadic alpha, beta: exact); for
+    the 5-point Laplacian, column c of X equal to (c + 1) everywhere gives
+    column c of Y equal to (c + 1) * (4 - neighbours)."""
+    rng = np.random.default_rng(18)
+    for dt in (F32, F64):
+        n, k = 97, 5
+        rp = np.arange(n + 1, dtype=np.int32)
+        X = rng.uniform(-1, 1, (n, k)).astype(dt)
+        Y0 = rng.uniform(-1, 1, (n, k)).astype(dt)
+        ref, _ = o.spmm(rp, np.arange(n, dtype=np.int32), np.ones(n, dtype=dt), X, 2.0, -0.5, Y0)
+        want = 2.0 * X.astype(np.float64) - 0.5 * Y0.astype(np.float64)
+        assert np.array_equal(ref, want), "spmm identity"
+    g = 12
+    rp, col, val = _laplacian(g)
+    r, c = np.divmod(np.arange(g * g), g)
+    nbrs = 4 - (r == 0) - (r == g - 1) - (c == 0) - (c == g - 1)
+    k = 6
+    X = np.tile(np.arange(1, k + 1, dtype=np.float64), (g * g, 1))
+    ref, _ = o.spmm(rp, col, val, X)
+    want = (4 - nbrs)[:, None].astype(np.float64) * np.arange(1, k + 1)[None, :]
+    assert np.array_equal(ref, want), "spmm laplacian"
+
+
+def pin_spmm_alpha_beta(o):
+    """alpha = -2 scales exactly; beta = 0 does not read Y_old (NaN there is
+    harmless); empty rows give exactly beta * Y_old in every column."""
+    for dt in (F32, F64):
+        rp, col, val, x, _ = _small_random(19, dt=dt)
+        rng = np.random.default_rng(20)
+        X = rng.uniform(-1, 1, (x.size, 3)).astype(dt)
+        Y0 = rng.uniform(-1, 1, (rp.size - 1, 3)).astype(dt)
+        base, _ = o.spmm(rp, col, val, X)
+        r2, _ = o.spmm(rp, col, val, X, -2.0, 0.0, np.full(Y0.shape, np.nan, dtype=dt))
+        assert np.array_equal(r2, -2.0 * base), "spmm alpha / beta = 0"
+        rb, _ = o.spmm(rp, col, val, X, 1.0, 0.5, Y0)
+        empty = np.diff(rp) == 0
+        assert np.array_equal(rb[empty], 0.5 * Y0[empty].astype(np.float64)), "spmm empty rows"
+        assert not np.array_equal(rb, base), "spmm beta term present"
+
+
 ALL_PINS = [pin_dense_bruteforce, pin_identity, pin_diagonal, pin_integer_row_sums,
             pin_laplacian_closed_forms, pin_alpha_beta, pin_scale, pin_rows_subset,
-            pin_merge_splits, pin_bins]
+            pin_merge_splits, pin_bins, pin_spmm_dense, pin_spmm_identity_and_laplacian,
+            pin_spmm_alpha_beta]

@@ -30,6 +30,14 @@ MUTANTS = [
      "      if (units == p * T + 1) {\n        split_row[p] = (int32_t)rows_done;\n        split_nz[p] = (int32_t)nz_done;\n        p += 1;\n      }\n    }\n    rows_done"),
     ("bin edge exclusive", "while (b < n_bins - 1 && L > max_len[b]) ++b;\n    counts[b] += 1;",
      "while (b < n_bins - 1 && L >= max_len[b]) ++b;\n    counts[b] += 1;"),
+    ("spmm X read column-major", "double p = (double)values[e] * (double)X[(int64_t)col_idx[e] * ldx + c];",
+     "double p = (double)values[e] * (double)X[c * ldx + col_idx[e]];"),
+    ("spmm first column only", "double p = values[e] * X[(int64_t)col_idx[e] * ldx + c];",
+     "double p = values[e] * X[(int64_t)col_idx[e] * ldx];"),
+    ("spmm beta row stride", "ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * (double)Y_old[i * ldy + c] : 0.0);",
+     "ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * (double)Y_old[i + c] : 0.0);"),
+    ("spmm alpha dropped", "ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * Y_old[i * ldy + c] : 0.0);",
+     "ref[i * k + c] = t + (beta != 0.0 ? beta * Y_old[i * ldy + c] : 0.0);"),
     ("bins reversed order", "bins[fill[b]] = (int32_t)r;", "bins[offsets[b + 1] - 1 - (fill[b] - offsets[b])] = (int32_t)r;"),
 ]
 
