@@ -200,6 +200,33 @@ SPMV_API spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y
                                double alpha, double beta, hipStream_t stream,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 
+/* Multi-vector SpMV (SpMM) over the same plan: Y = alpha * A * X + beta * Y
+ * for k right-hand sides. "A Programming Model for GPU Load Balancing"
+ * (PPoPP'23), Section 5.3, Listing 4: the SpMV with a loop over the dense
+ * matrix's columns, column c of Y from column c of X.
+ *
+ * X  device array, N x k row-major of the plan's dtype: X[j*ldx + c]; ldx >= k.
+ * Y  device array, M x k row-major: Y[i*ldy + c]; ldy >= k; read only when
+ *    beta != 0. X and Y must not overlap; both aligned to the element size.
+ * workspace, workspace_bytes: device memory of at least
+ *    spmv_spmm_workspace_size(plan, k) bytes for the k-wide carries of rows
+ *    cut between partitions (0 bytes, NULL allowed, when the plan's
+ *    partitions end at row ends: merge_reduce = stream). Owned by the caller;
+ *    its contents need no initialisation and are scratch after the call.
+ * k = 0 or M = 0 does nothing. k > 64 runs in column blocks of 64.
+ *
+ * Uses the plan's merge-path partitions whatever its SpMV strategy.
+ * Asynchronous like spmv_exec (no allocation, no synchronisation);
+ * bitwise reproducible for a fixed plan and k; the plan's carry-row array
+ * is shared with spmv_exec, so one plan must not run either call
+ * concurrently on two streams. SPMV_ERR_INVALID_ARG on a bad size, pointer,
+ * overlap or short workspace. */
+SPMV_API spmv_status_t spmv_spmm_workspace_size(spmv_plan_t plan, int64_t k, size_t* bytes);
+SPMV_API spmv_status_t spmv_exec_multi(spmv_plan_t plan, int64_t k, const void* X,
+                                       int64_t ldx, void* Y, int64_t ldy, double alpha,
+                                       double beta, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Release the plan's workspace (hipFree, which synchronises the device).
  * NULL is a no-op; a destroyed or foreign handle gives SPMV_ERR_INVALID_PLAN
  * as long as its memory has not been reused. */

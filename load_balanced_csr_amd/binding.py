@@ -27,7 +27,8 @@ MAX_BINS = 8
 
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
-            "spmv_plan_copy_bins", "spmv_read_probe", "spmv_status_string", "spmv_last_error")
+            "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
+            "spmv_exec_multi", "spmv_status_string", "spmv_last_error")
 
 
 class SpmvError(RuntimeError):
@@ -85,6 +86,8 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
     lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
     lib.spmv_read_probe.argtypes = [p, i64, p, p]
+    lib.spmv_spmm_workspace_size.argtypes = [p, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.spmv_exec_multi.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p]
     for name in EXPORTED:
         if name not in ("spmv_status_string", "spmv_last_error"):
             getattr(lib, name).restype = st
@@ -109,7 +112,8 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _dev_ptr(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[int]:
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtypes,
+             contiguous: bool = True) -> Optional[int]:
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -118,7 +122,7 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[int]:
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
     if not t.is_cuda:
         raise ValueError("%s must be a device (cuda) tensor" % name)
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t.data_ptr() if t.numel() else None
 
@@ -182,6 +186,40 @@ def spmv_exec_events(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float, 
     _check(load().spmv_exec_events(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts),
                                    float(alpha), float(beta), _stream(stream), ev_begin, ev_end),
            "spmv_exec_events")
+
+
+def spmv_spmm_workspace_size(plan: int, k: int) -> int:
+    """Bytes of device workspace spmv_exec_multi needs for k right-hand sides."""
+    n = ctypes.c_size_t(0)
+    _check(load().spmv_spmm_workspace_size(plan, int(k), ctypes.byref(n)),
+           "spmv_spmm_workspace_size")
+    return int(n.value)
+
+
+def _row_major(t: torch.Tensor, name: str):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be a 2-D row-major tensor (unit column stride)" % name)
+    return max(int(t.stride(0)), int(t.shape[1]))
+
+
+def spmv_exec_multi(plan: int, X: torch.Tensor, Y: torch.Tensor, alpha: float = 1.0,
+                    beta: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """Y = alpha * A X + beta * Y for the k = X.shape[1] columns of X (N x k)
+    and Y (M x k), both row-major; ``workspace`` is a device tensor of at
+    least spmv_spmm_workspace_size(plan, k) bytes (None when that is 0)."""
+    dts = (torch.float32, torch.float64)
+    if X.shape[1] != Y.shape[1]:
+        raise ValueError("X and Y must have the same number of columns")
+    ldx, ldy = _row_major(X, "X"), _row_major(Y, "Y")
+    ws, wsb = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(load().spmv_exec_multi(plan, int(X.shape[1]), _dev_ptr(X, "X", dts, False), ldx,
+                                  _dev_ptr(Y, "Y", dts, False), ldy, float(alpha), float(beta), ws,
+                                  wsb, _stream(stream)), "spmv_exec_multi")
 
 
 def spmv_read_probe(data: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
@@ -267,6 +305,20 @@ class Plan:
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):
         spmv_exec(self.handle, x, y, alpha, beta, stream)
         return y
+
+    def exec_multi(self, X, Y, alpha: float = 1.0, beta: float = 0.0, workspace=None,
+                   stream=None):
+        """Y = alpha * A X + beta * Y (X: N x k, Y: M x k, row-major). Without
+        a workspace the plan keeps one of the needed size (a torch tensor)."""
+        if workspace is None:
+            need = spmv_spmm_workspace_size(self.handle, int(X.shape[1]))
+            if need > 0:
+                ws = getattr(self, "_ws", None)
+                if ws is None or ws.numel() < need or ws.device != Y.device:
+                    self._ws = torch.empty(need, dtype=torch.uint8, device=Y.device)
+                workspace = self._ws
+        spmv_exec_multi(self.handle, X, Y, alpha, beta, workspace, stream)
+        return Y
 
     def set_strategy(self, strategy: str):
         spmv_plan_set_strategy(self.handle, strategy)

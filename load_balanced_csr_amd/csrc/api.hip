@@ -225,9 +225,92 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
   return SPMV_SUCCESS;
 }
 
+size_t spmm_workspace(const spmv_plan_st* p, int64_t k) {
+  if (p->merge_reduce == 2 || p->P <= 0 || k <= 0) return 0;
+  const size_t vs = p->dtype == SPMV_F32 ? 4 : 8;
+  return align256((size_t)p->P * (size_t)std::min<int64_t>(k, kWave) * vs);
+}
+
+template <typename V>
+spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t ldx, void* Y,
+                               int64_t ldy, double alpha, double beta, void* workspace,
+                               hipStream_t stream) {
+  SpmmArgs<V> a;
+  std::memset(&a, 0, sizeof a);
+  a.row_ptr = p->row_ptr;
+  a.col_idx = p->col_idx;
+  a.val = static_cast<const V*>(p->values);
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.split_row = p->split_row;
+  a.split_nz = p->split_nz;
+  a.row_bounds = p->row_bounds;
+  a.carry_row = p->carry_row;
+  a.carry_vec = static_cast<V*>(workspace);
+  a.alpha = (V)alpha;
+  a.beta = (V)beta;
+  a.beta_nonzero = beta != 0.0;
+  a.P = (int32_t)p->P;
+  a.M = (int32_t)p->M;
+  a.nnz = (int32_t)p->nnz;
+  a.T = p->T;
+  a.cap = spmm_stage_cap(p->T);
+  a.stream = p->merge_reduce == 2;
+  a.xcd_remap = p->xcd_remap;
+  for (int64_t kb = 0; kb < k; kb += kWave) {
+    a.k = (int32_t)std::min<int64_t>(kWave, k - kb);
+    a.X = static_cast<const V*>(X) + kb;
+    a.Y = static_cast<V*>(Y) + kb;
+    const hipError_t err = launch_spmm<V>(a, stream);
+    if (err != hipSuccess) return hip_fail(err, "spmv_exec_multi launch");
+  }
+  return SPMV_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+spmv_status_t spmv_spmm_workspace_size(spmv_plan_t p, int64_t k, size_t* bytes) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (!bytes) return fail(SPMV_ERR_INVALID_ARG, "bytes is NULL");
+  if (k < 0) return fail(SPMV_ERR_INVALID_ARG, "k = %lld < 0", (long long)k);
+  *bytes = spmm_workspace(p, k);
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_exec_multi(spmv_plan_t p, int64_t k, const void* X, int64_t ldx, void* Y,
+                              int64_t ldy, double alpha, double beta, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (k < 0) return fail(SPMV_ERR_INVALID_ARG, "k = %lld < 0", (long long)k);
+  if (k == 0 || p->M == 0) return SPMV_SUCCESS;
+  if (ldx < k || ldy < k)
+    return fail(SPMV_ERR_INVALID_ARG, "ldx = %lld and ldy = %lld must be >= k = %lld",
+                (long long)ldx, (long long)ldy, (long long)k);
+  if (!Y) return fail(SPMV_ERR_INVALID_ARG, "Y is NULL");
+  if (p->nnz > 0 && !X) return fail(SPMV_ERR_INVALID_ARG, "X is NULL");
+  const size_t vs = p->dtype == SPMV_F32 ? 4 : 8;
+  if ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y)) % vs)
+    return fail(SPMV_ERR_INVALID_ARG, "X and Y must be aligned to the element size");
+  // byte ranges [X, X + ((N-1) ldx + k) vs) and [Y, Y + ((M-1) ldy + k) vs)
+  if (X && p->N > 0 && p->nnz > 0) {
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(X);
+    const uintptr_t x1 = x0 + (uintptr_t)(((p->N - 1) * ldx + k) * (int64_t)vs);
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(Y);
+    const uintptr_t y1 = y0 + (uintptr_t)(((p->M - 1) * ldy + k) * (int64_t)vs);
+    if (x0 < y1 && y0 < x1) return fail(SPMV_ERR_INVALID_ARG, "X and Y overlap");
+  }
+  const size_t need = spmm_workspace(p, k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SPMV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return p->dtype == SPMV_F32
+             ? exec_multi_typed<float>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream)
+             : exec_multi_typed<double>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream);
+}
 
 spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                            const int32_t* row_ptr, const int32_t* col_idx, const void* values,

@@ -120,6 +120,44 @@ template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,
                         hipEvent_t ev1);
 
+// ---- multi-vector exec (SpMM) -------------------------------------------------------
+// Y = alpha * A X + beta * Y, X N x k and Y M x k row-major (k <= 64 per
+// launch), over the plan's merge-path partitions.
+template <typename V>
+struct SpmmArgs {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const V* val;
+  const V* X;
+  V* Y;
+  int64_t ldx, ldy;          // row strides of X and Y, elements
+  const int32_t* split_row;
+  const int32_t* split_nz;
+  const int32_t* row_bounds;
+  int32_t* carry_row;        // P (not stream)
+  V* carry_vec;              // P x k (not stream)
+  V alpha;
+  V beta;
+  int32_t beta_nonzero;
+  int32_t k;
+  int32_t P;
+  int32_t M;
+  int32_t nnz;
+  int32_t T;
+  int32_t cap;               // staged entries per array and wave
+  int32_t stream;            // 1: partitions end at row ends (no carries)
+  int32_t xcd_remap;
+};
+
+// Staging room per array for partitions of T units (at most T + T/8 rows or
+// nonzeros, plus quad alignment).
+constexpr int spmm_stage_cap(int T) { return T + T / 8 + 8; }
+// Dynamic LDS of one SpMM workgroup.
+size_t spmm_lds_bytes(int vbytes, int T);
+
+template <typename V>
+hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s);
+
 // ---- binned exec ----------------------------------------------------------------
 struct BinLaunch {
   int32_t block_begin;   // first workgroup of this bin in the fused grid

@@ -245,6 +245,6 @@ def within_tolerance(y, ref, scale, alpha: float, beta: float, y_old=None,
         bad |= empty & (yd != want)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(lim > 0, err / np.where(lim > 0, lim, 1.0), np.where(err > 0, np.inf, 0.0))
-    ratio = np.where(nan_ok, 0.0, ratio)
+    ratio = np.where(nan_ok, 0.0, ratio).ravel()   # worst: flat index
     worst = int(np.argmax(ratio)) if ratio.size else -1
     return (not bool(bad.any())), (float(ratio[worst]) if worst >= 0 else 0.0), worst
