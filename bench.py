@@ -48,6 +48,7 @@ WORKLOADS = {
     "banded": "fp32 banded decay matrix, 32,000,000 rows, 24..40 entries within |i-j| <= 1000",
 }
 KERNEL_SOURCES = ["merge_kernels.hip", "binned_kernels.hip", "device_common.hpp", "internal.hpp"]
+# (the SpMM kernel, spmm_kernels.hip, has no committed counter table)
 
 
 def kernel_source_hash() -> str:
@@ -195,6 +196,135 @@ def calibrate_copy(mib: int, steps: int):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": steps}), flush=True)
 
 
+METRIC_SPMM = "CSR SpMM (k right-hand sides) GFLOP/s and achieved HBM GB/s (% of peak) on 1 MI355X"
+
+
+def spmm_bytes(w, k: int) -> int:
+    """Compulsory bytes of Y = alpha*A*X + beta*Y: the matrix once, X (N x k)
+    and Y (M x k) once each (Y twice when beta != 0)."""
+    s = w.values.dtype.itemsize
+    b = 4 * (w.M + 1) + w.nnz * (4 + s) + w.N * k * s + w.M * k * s
+    if w.beta != 0.0:
+        b += w.M * k * s
+    return b
+
+
+def run_spmm(args, w, torch, lb, dev):
+    """SpMM mode (--rhs K > 1): one step = one spmv_exec_multi over the
+    workload with K dense right-hand sides, flushed and event-timed like the
+    SpMV steps. Prints one JSON line of its own metric."""
+    import synth
+    k = args.rhs
+    dt = torch.float32 if w.values.dtype == np.float32 else torch.float64
+    npdt = w.values.dtype
+    rp = torch.from_numpy(w.row_ptr).to(dev)
+    col = torch.from_numpy(w.col_idx).to(dev)
+    val = torch.from_numpy(w.values).to(dev)
+    Xh = synth.uniform(w.N * k, w.seed, synth.S_X, npdt).reshape(w.N, k)
+    Y0h = (synth.uniform(w.M * k, w.seed, synth.S_Y, npdt).reshape(w.M, k)
+           if w.beta != 0.0 else None)
+    X = torch.from_numpy(Xh).to(dev)
+    Y = torch.empty((w.M, k), dtype=dt, device=dev)
+    Y0 = torch.from_numpy(Y0h).to(dev) if Y0h is not None else None
+    plan = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
+                   items_per_thread=args.items_per_thread)
+    info = plan.info
+    need = lb.spmv_spmm_workspace_size(plan.handle, k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+
+    def step(ev0=None, ev1=None):
+        lb.spmv_exec_multi(plan.handle, X, Y, w.alpha, w.beta, ws, None, ev0, ev1)
+
+    if Y0 is not None:
+        Y.copy_(Y0)
+    else:
+        Y.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    Y_first = Y.cpu().numpy()
+    flush = None if args.no_flush else CacheFlush(torch, dev)
+    hip = HipEvents()
+    K, W = args.steps, args.warmup
+    if Y0 is not None:
+        Y.copy_(Y0)
+    for _ in range(W):
+        if flush is not None:
+            flush()
+        step()
+    kb = [hip.create() for _ in range(K)]
+    ke = [hip.create() for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush()
+        step(kb[i], ke[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
+    for e in kb + ke:
+        hip.destroy(e)
+    deterministic = None
+    if w.beta == 0.0:
+        deterministic = bool(np.array_equal(Y.cpu().numpy().view(np.uint8),
+                                            Y_first.view(np.uint8)))
+    mean_ms = statistics.fmean(ms)
+    Bc = spmm_bytes(w, k)
+    gbps = Bc / (mean_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC_SPMM,
+        "value": round(2.0 * w.nnz * k / (mean_ms * 1e-3) / 1e9, 3),
+        "unit": "GFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if dt == torch.float32 else "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
+                   "rhs": k, "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha,
+                   "beta": w.beta, "seed": w.seed, "merge_reduce": info["merge_reduce"],
+                   "items_per_wave": info["items_per_wave"],
+                   "cache": "warm" if flush is None else
+                   "flushed before every step (1 GiB fill + 1 GiB cached read)"},
+        "achieved_GBps": round(gbps, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "compulsory_bytes": Bc,
+        "roofline": {"bound": "hbm", "kernel": "spmm_merge_kernel", "achieved": round(gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel_ms": round(mean_ms, 5),
+                     "traffic": None,
+                     "timed": "events around the exec's launches (main kernel%s)"
+                              % ("" if info["merge_reduce"] == "stream" else " + carry fix-up")},
+        "exec_ms_median": round(statistics.median(ms), 5),
+        "deterministic": deterministic,
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "workspace_bytes": need,
+    }
+    plan.destroy()
+    ok = True
+    if not args.no_cpu:
+        import oracle
+        print("[bench] cpu oracle baseline (spmm)", file=sys.stderr, flush=True)
+        times = []
+        t_end = time.perf_counter() + args.cpu_seconds
+        while True:
+            t1 = time.perf_counter()
+            ref, scale = oracle.spmm(w.row_ptr, w.col_idx, w.values, Xh, w.alpha, w.beta, Y0h)
+            times.append(time.perf_counter() - t1)
+            if time.perf_counter() > t_end or len(times) >= 20:
+                break
+        t = statistics.median(times)
+        ok, worst, _ = oracle.within_tolerance(Y_first, ref, scale, w.alpha, w.beta, Y0h,
+                                               row_ptr=w.row_ptr)
+        out["cpu_baseline"] = {"value": round(2.0 * w.nnz * k / t / 1e9, 4), "unit": "GFLOP/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "whole workload with %d right-hand sides, %d runs, "
+                                         "median %.1f ms" % (k, len(times), t * 1e3)}
+        out["parity"] = {"ok": bool(ok), "worst_over_bound": round(worst, 5),
+                         "checked": "first exec vs the oracle, every element"}
+    print(json.dumps(out), flush=True)
+    if not ok or deterministic is False:
+        sys.exit(3)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +336,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--rhs", type=int, default=1, metavar="K",
+                    help="K > 1: time the multi-vector form (SpMM) with K right-hand sides")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -229,6 +361,8 @@ def main():
     dev = torch.device("cuda:0")
     print("[bench] generating %s" % args.workload, file=sys.stderr, flush=True)
     w = synth.CONFIGS[args.workload]()
+    if args.rhs > 1:
+        return run_spmm(args, w, torch, lb, dev)
     dt = torch.float32 if w.values.dtype == np.float32 else torch.float64
 
     rp = torch.from_numpy(w.row_ptr).to(dev)

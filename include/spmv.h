@@ -227,6 +227,15 @@ SPMV_API spmv_status_t spmv_exec_multi(spmv_plan_t plan, int64_t k, const void* 
                                        double beta, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/* spmv_exec_multi that also records ev_begin before its first launch and
+ * ev_end after its last (main kernel and, for plans whose partitions cut
+ * rows, the carry fix-up), on the same stream. Either event may be NULL. */
+SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const void* X,
+                                              int64_t ldx, void* Y, int64_t ldy, double alpha,
+                                              double beta, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream,
+                                              hipEvent_t ev_begin, hipEvent_t ev_end);
+
 /* Release the plan's workspace (hipFree, which synchronises the device).
  * NULL is a no-op; a destroyed or foreign handle gives SPMV_ERR_INVALID_PLAN
  * as long as its memory has not been reused. */

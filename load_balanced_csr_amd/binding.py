@@ -28,7 +28,8 @@ MAX_BINS = 8
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
-            "spmv_exec_multi", "spmv_status_string", "spmv_last_error")
+            "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
+            "spmv_last_error")
 
 
 class SpmvError(RuntimeError):
@@ -88,6 +89,8 @@ def load(build_if_missing: bool = True):
     lib.spmv_read_probe.argtypes = [p, i64, p, p]
     lib.spmv_spmm_workspace_size.argtypes = [p, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.spmv_exec_multi.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p]
+    lib.spmv_exec_multi_events.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p,
+                                           p, p]
     for name in EXPORTED:
         if name not in ("spmv_status_string", "spmv_last_error"):
             getattr(lib, name).restype = st
@@ -204,10 +207,13 @@ def _row_major(t: torch.Tensor, name: str):
 
 def spmv_exec_multi(plan: int, X: torch.Tensor, Y: torch.Tensor, alpha: float = 1.0,
                     beta: float = 0.0, workspace: Optional[torch.Tensor] = None,
-                    stream=None) -> None:
+                    stream=None, ev_begin: Optional[int] = None,
+                    ev_end: Optional[int] = None) -> None:
     """Y = alpha * A X + beta * Y for the k = X.shape[1] columns of X (N x k)
     and Y (M x k), both row-major; ``workspace`` is a device tensor of at
-    least spmv_spmm_workspace_size(plan, k) bytes (None when that is 0)."""
+    least spmv_spmm_workspace_size(plan, k) bytes (None when that is 0).
+    ev_begin / ev_end: optional hipEvent_t handles recorded around the
+    launches."""
     dts = (torch.float32, torch.float64)
     if X.shape[1] != Y.shape[1]:
         raise ValueError("X and Y must have the same number of columns")
@@ -217,9 +223,10 @@ def spmv_exec_multi(plan: int, X: torch.Tensor, Y: torch.Tensor, alpha: float = 
         if not workspace.is_cuda:
             raise ValueError("workspace must be a device tensor")
         ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(load().spmv_exec_multi(plan, int(X.shape[1]), _dev_ptr(X, "X", dts, False), ldx,
-                                  _dev_ptr(Y, "Y", dts, False), ldy, float(alpha), float(beta), ws,
-                                  wsb, _stream(stream)), "spmv_exec_multi")
+    _check(load().spmv_exec_multi_events(plan, int(X.shape[1]), _dev_ptr(X, "X", dts, False),
+                                         ldx, _dev_ptr(Y, "Y", dts, False), ldy, float(alpha),
+                                         float(beta), ws, wsb, _stream(stream), ev_begin,
+                                         ev_end), "spmv_exec_multi")
 
 
 def spmv_read_probe(data: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -234,7 +234,7 @@ size_t spmm_workspace(const spmv_plan_st* p, int64_t k) {
 template <typename V>
 spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t ldx, void* Y,
                                int64_t ldy, double alpha, double beta, void* workspace,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   SpmmArgs<V> a;
   std::memset(&a, 0, sizeof a);
   a.row_ptr = p->row_ptr;
@@ -257,13 +257,18 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
   a.cap = spmm_stage_cap(p->T);
   a.stream = p->merge_reduce == 2;
   a.xcd_remap = p->xcd_remap;
+  hipError_t err = hipSuccess;
+  if (ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess)
+    return hip_fail(err, "spmv_exec_multi event");
   for (int64_t kb = 0; kb < k; kb += kWave) {
     a.k = (int32_t)std::min<int64_t>(kWave, k - kb);
     a.X = static_cast<const V*>(X) + kb;
     a.Y = static_cast<V*>(Y) + kb;
-    const hipError_t err = launch_spmm<V>(a, stream);
-    if (err != hipSuccess) return hip_fail(err, "spmv_exec_multi launch");
+    if ((err = launch_spmm<V>(a, stream)) != hipSuccess)
+      return hip_fail(err, "spmv_exec_multi launch");
   }
+  if (ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess)
+    return hip_fail(err, "spmv_exec_multi event");
   return SPMV_SUCCESS;
 }
 
@@ -280,9 +285,10 @@ spmv_status_t spmv_spmm_workspace_size(spmv_plan_t p, int64_t k, size_t* bytes) 
   return SPMV_SUCCESS;
 }
 
-spmv_status_t spmv_exec_multi(spmv_plan_t p, int64_t k, const void* X, int64_t ldx, void* Y,
-                              int64_t ldy, double alpha, double beta, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+spmv_status_t spmv_exec_multi_events(spmv_plan_t p, int64_t k, const void* X, int64_t ldx,
+                                     void* Y, int64_t ldy, double alpha, double beta,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     hipEvent_t ev_begin, hipEvent_t ev_end) {
   spmv_status_t st = check_plan(p);
   if (st != SPMV_SUCCESS) return st;
   if (k < 0) return fail(SPMV_ERR_INVALID_ARG, "k = %lld < 0", (long long)k);
@@ -308,8 +314,17 @@ spmv_status_t spmv_exec_multi(spmv_plan_t p, int64_t k, const void* X, int64_t l
     return fail(SPMV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   return p->dtype == SPMV_F32
-             ? exec_multi_typed<float>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream)
-             : exec_multi_typed<double>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream);
+             ? exec_multi_typed<float>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream,
+                                       ev_begin, ev_end)
+             : exec_multi_typed<double>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream,
+                                        ev_begin, ev_end);
+}
+
+spmv_status_t spmv_exec_multi(spmv_plan_t p, int64_t k, const void* X, int64_t ldx, void* Y,
+                              int64_t ldy, double alpha, double beta, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return spmv_exec_multi_events(p, k, X, ldx, Y, ldy, alpha, beta, workspace, workspace_bytes,
+                                stream, nullptr, nullptr);
 }
 
 spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
