@@ -252,6 +252,7 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
   a.beta_nonzero = beta != 0.0;
   a.P = (int32_t)p->P;
   a.M = (int32_t)p->M;
+  a.N = (int32_t)p->N;
   a.nnz = (int32_t)p->nnz;
   a.T = p->T;
   a.cap = spmm_stage_cap(p->T);

@@ -142,6 +142,7 @@ struct SpmmArgs {
   int32_t k;
   int32_t P;
   int32_t M;
+  int32_t N;
   int32_t nnz;
   int32_t T;
   int32_t cap;               // staged entries per array and wave

@@ -11,12 +11,14 @@
 // the same page): a partition is T units, each nonzero and each row end one
 // unit. MI355X mapping (not the page's): one 64-lane wavefront per
 // partition, split into S = 64 / KL slots of KL lanes; lane l of a slot
-// holds output column l. The partition's units are cut again, merge-path
+// holds output columns [VE l, VE l + VE), VE = 16 bytes' worth when X and Y
+// allow 16-byte accesses (else 1). The partition's units are cut again, merge-path
 // style, into S equal runs, one per slot, so every slot does the same work
 // however long the rows are. A slot walks its run in order; per batch of 8
 // nonzeros it first issues all their X-row loads (KL consecutive elements
 // per nonzero: one coalesced access per slot), then adds the products,
-// finishing rows as their ends come by. A row wholly inside one run is
+// finishing rows as their ends come by (one 16-byte load per lane and
+// nonzero). A row wholly inside one run is
 // written by that slot; the pieces of rows cut between runs are combined in
 // slot order afterwards, and a row cut at the partition's end leaves a
 // k-wide carry that the fix-up kernel adds, in partition order. No float
@@ -29,49 +31,95 @@
 namespace spmv {
 namespace {
 
-constexpr int kSpmmBatch = 8;
+constexpr int kSpmmBatch = 4;
 
-// LDS of one wave (bytes): head / tail vectors (64 V each), the staged row
-// pointers and column indices (cap int32 each, 16-byte aligned), and the
+// LDS of one wave (bytes): the staged row pointers, column indices and
+// values (cap entries each, 16-byte aligned); once the walk is done the same
+// bytes hold the head / tail vectors (64 lanes x 16 bytes each) and the
 // per-slot records (5 x 64 int32).
-__host__ __device__ constexpr int spmm_wave_lds(int vbytes, int cap) {
-  return (2 * kWave * vbytes + 2 * cap * 4 + 5 * kWave * 4 + 15) / 16 * 16;
+constexpr int kSpmmRecordBytes = 2 * kWave * 16 + 5 * kWave * 4;
+__host__ __device__ constexpr int spmm_wave_lds(int cap, int vbytes) {
+  return 2 * cap * 4 + cap * vbytes > kSpmmRecordBytes ? 2 * cap * 4 + cap * vbytes
+                                                       : kSpmmRecordBytes;
 }
 
-// a[beg, beg + cnt) (int32, n elements in all) into dst so that a[beg + t]
-// lands at dst[(beg & 3) + t]. 16-byte loads where the quad lies inside the
-// array, element loads for the array's last, partial quad. dst is 16-byte
-// aligned with room for cnt + 7 entries.
-__device__ __forceinline__ void stage_i32(int32_t* dst, const int32_t* a, int beg, int cnt,
-                                          int n) {
-  if (cnt <= 0) return;
-  const int q0 = beg >> 2;
-  const int nq = ((beg + cnt - 1) >> 2) - q0 + 1;
-  for (int t = lane_id(); t < nq; t += kWave) {
-    const int q = q0 + t;
-    i32x4 v;
-    if (4 * q + 3 < n) {
-      v = ld_stream(reinterpret_cast<const i32x4*>(a) + q);
-    } else {
+// VE consecutive elements of V (a 16-byte vector when VE * sizeof(V) = 16).
+template <typename V, int VE>
+struct Vec {
+  V v[VE];
+};
+template <typename V, int VE>
+__device__ __forceinline__ Vec<V, VE> vec_load(const V* p) {
+  Vec<V, VE> r;
+  if constexpr (VE * sizeof(V) == 16) {
+    typedef V v4 __attribute__((ext_vector_type(VE)));
+    const v4 t = *reinterpret_cast<const v4*>(p);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = 4 * q + j < n ? a[4 * q + j] : 0;
-    }
-    *reinterpret_cast<i32x4*>(dst + 4 * t) = v;
+    for (int q = 0; q < VE; ++q) r.v[q] = t[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < VE; ++q) r.v[q] = p[q];
+  }
+  return r;
+}
+
+// a[beg, beg + cnt) (int32 words, n in the array) into LDS dst so that
+// a[beg + t] lands at dst[(beg & 3) + t]: whole 16-byte quads by direct-to-LDS
+// loads (no registers; all in flight together), the array's last, partial
+// quad by element loads. dst is 16-byte aligned with room for cnt + 7
+// entries. The caller waits for the loads (vmcnt 0) and syncs the wave
+// before reading dst.
+__device__ __forceinline__ void stage_dma(int32_t* dst, const int32_t* a, int64_t beg, int cnt,
+                                          int64_t n) {
+  if (cnt <= 0) return;
+  const int lane = lane_id();
+  const int64_t q0 = beg >> 2;
+  const int nq = (int)(((beg + cnt - 1) >> 2) - q0 + 1);
+  for (int r = 0; kWave * r < nq; ++r) {
+    const int t = kWave * r + lane;
+    const int64_t q = q0 + t;
+    if (t < nq && 4 * q + 3 < n) lds_dma16(a + 4 * q, dst + 4 * kWave * r);
+  }
+  const int64_t ql = q0 + nq - 1;
+  if (4 * ql + 3 >= n && lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[4 * (nq - 1) + j] = 4 * ql + j < n ? a[4 * ql + j] : 0;
   }
 }
 
-template <typename V>
-__device__ __forceinline__ void spmm_store(const SpmmArgs<V>& a, int row, int col, V acc) {
+// Y[row, col .. col + VE) = alpha * acc + beta * Y (Y not read when beta = 0)
+template <typename V, int VE>
+__device__ __forceinline__ void spmm_store(const SpmmArgs<V>& a, int row, int col,
+                                           const Vec<V, VE>& acc) {
   V* yp = a.Y + (int64_t)row * a.ldy + col;
-  V out = a.alpha * acc;
-  if (a.beta_nonzero) out = fma(a.beta, *yp, out);
-  *yp = out;
+  Vec<V, VE> out;
+  if (a.beta_nonzero) {
+    const Vec<V, VE> old = vec_load<V, VE>(yp);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) out.v[q] = fma(a.beta, old.v[q], a.alpha * acc.v[q]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < VE; ++q) out.v[q] = a.alpha * acc.v[q];
+  }
+  if constexpr (VE * sizeof(V) == 16) {
+    typedef V v4 __attribute__((ext_vector_type(VE)));
+    v4 t;
+#pragma unroll
+    for (int q = 0; q < VE; ++q) t[q] = out.v[q];
+    *reinterpret_cast<v4*>(yp) = t;
+  } else {
+#pragma unroll
+    for (int q = 0; q < VE; ++q) yp[q] = out.v[q];
+  }
 }
 
-template <typename V, int KL>
+// OFF32: X spans less than 4 GiB, so a row's address is the wave-uniform
+// base plus a 32-bit byte offset (one VGPR per address instead of two).
+template <typename V, int KL, int VE, bool OFF32>
 __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a) {
   constexpr int S = kWave / KL;   // slots per wave
   constexpr int B = kSpmmBatch;
+  typedef Vec<V, VE> VV;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
 
   const int lane = lane_id();
@@ -98,23 +146,29 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   }
   const int R = r1 - r0, nloc = n1 - n0, tot = R + nloc;
 
-  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(sizeof(V), a.cap);
-  V* head_vec = reinterpret_cast<V*>(base);
-  V* tail_vec = head_vec + kWave;
-  int32_t* s_rp = reinterpret_cast<int32_t*>(tail_vec + kWave);
+  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V));
+  int32_t* s_rp = reinterpret_cast<int32_t*>(base);
   int32_t* s_col = s_rp + a.cap;
-  int32_t* rec = s_col + a.cap;   // [5][64]: head ends, tail owned, used, head row, tail row
+  int32_t* s_val = s_col + a.cap;   // cap entries of V, staged as int32 words
 
-  // row pointers rp[r0 .. r1] (row r1's start ends the last closed row) and
-  // the partition's column indices
-  stage_i32(s_rp, a.row_ptr, r0, R + 1, a.M + 1);
-  stage_i32(s_col, a.col_idx, n0, nloc, a.nnz);
+  // row pointers rp[r0 .. r1] (row r1's start ends the last closed row), the
+  // partition's column indices and values: coalesced 16-byte loads
+  constexpr int W = sizeof(V) / 4;   // int32 words per value
+  stage_dma(s_rp, a.row_ptr, r0, R + 1, a.M + 1);
+  stage_dma(s_col, a.col_idx, n0, nloc, a.nnz);
+  stage_dma(s_val, reinterpret_cast<const int32_t*>(a.val), (int64_t)W * n0, W * nloc,
+            (int64_t)W * a.nnz);
+  wait_vmem();
   wave_sync();
+  memory_order_point();
   const int32_t* rpl = s_rp + (r0 & 3);    // rpl[i] = row_ptr[r0 + i]
   const int32_t* coll = s_col + (n0 & 3);  // coll[t] = col_idx[n0 + t]
+  const V* vall = reinterpret_cast<const V*>(s_val + ((W * n0) & 3));   // vall[t] = val[n0 + t]
+  // (W * n0 may wrap in int32 for fp64; its low two bits are still right)
 
-  const int s = lane / KL, cl = lane % KL;
-  const bool colok = cl < a.k;
+  const int s = lane / KL;
+  const int col = (lane % KL) * VE;          // first output column of this lane
+  const bool colok = col < a.k;
   const int D = (tot + S - 1) / S;
   const int d0 = min(s * D, tot), d1 = min(d0 + D, tot);
   // merge-path coordinate of unit d: rows whose end unit comes before d
@@ -136,54 +190,71 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   // (slot 0 always: earlier partitions' pieces come in as carries)
   bool owned = s == 0 || rpl[i] - n0 >= jbeg;
   bool head_ends = false;
-  V acc = V(0), head = V(0);
+  VV acc, head;
+#pragma unroll
+  for (int q = 0; q < VE; ++q) acc.v[q] = head.v[q] = V(0);
   int e = i < R ? rpl[i + 1] - n0 : INT_MAX;   // local end of row i
+  const char* xbase = reinterpret_cast<const char*>(a.X);
+  const uint32_t xrow_bytes = (uint32_t)a.ldx * (uint32_t)sizeof(V);
 
-  for (int jb = jbeg; jb < jend; jb += B) {
-    V xv[B], vv[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int jj = jb + u;
-      const bool ok = jj < jend;
-      const int c = ok ? coll[jj] : 0;
-      vv[u] = ok ? a.val[n0 + jj] : V(0);
-      xv[u] = ok && colok ? a.X[(int64_t)c * a.ldx + cl] : V(0);
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int jj = jb + u;
-      while (i < iend && e == jj) {   // rows ending before nonzero jj
-        if (owned) {
-          if (colok) spmm_store(a, r0 + i, cl, acc);
-        } else {
-          head = acc;
-          head_ends = true;
-        }
-        owned = true;
-        acc = V(0);
-        ++i;
-        e = i < R ? rpl[i + 1] - n0 : INT_MAX;
+  // rows ending at unit position jj (before nonzero jj): written when this
+  // slot holds all of them, else kept as the head piece
+  auto finish_rows = [&](int jj) {
+    while (i < iend && e == jj) {
+      if (owned) {
+        if (colok) spmm_store<V, VE>(a, r0 + i, col, acc);
+      } else {
+        head = acc;
+        head_ends = true;
       }
-      if (jj < jend) acc = fma(vv[u], xv[u], acc);
+      owned = true;
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc.v[q] = V(0);
+      ++i;
+      e = i < R ? rpl[i + 1] - n0 : INT_MAX;
+    }
+  };
+
+  // lanes past k read column 0 of the same X rows (in bounds; never stored)
+  const int lcol = colok ? col : 0;
+  const V* xcol = a.X + lcol;
+  const uint32_t xcol_bytes = (uint32_t)lcol * (uint32_t)sizeof(V);
+  for (int jb = jbeg; jb < jend; jb += B) {
+    // the batch's column indices first (LDS), then every X-row load: past the
+    // run's end a lane re-reads its last nonzero's row and adds 0 for it
+    int cs[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) cs[u] = coll[min(jb + u, jend - 1)];
+    VV xv[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (OFF32)
+        xv[u] = vec_load<V, VE>(
+            reinterpret_cast<const V*>(xbase + ((uint32_t)cs[u] * xrow_bytes + xcol_bytes)));
+      else
+        xv[u] = vec_load<V, VE>(xcol + (int64_t)cs[u] * a.ldx);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int jj = jb + u;
+      finish_rows(jj);
+      const V v = jj < jend ? vall[min(jj, jend - 1)] : V(0);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc.v[q] = fma(v, xv[u].v[q], acc.v[q]);
     }
   }
-  while (i < iend) {                   // rows ending at the run's end
-    if (owned) {
-      if (colok) spmm_store(a, r0 + i, cl, acc);
-    } else {
-      head = acc;
-      head_ends = true;
-    }
-    owned = true;
-    acc = V(0);
-    ++i;
-  }
+  finish_rows(jend);
 
   // records: the piece of the first row (when another slot started it and it
-  // ended here) and the piece of the row open at the run's end
+  // ended here) and the piece of the row open at the run's end, over the
+  // staging area (every lane is done reading it)
+  wave_sync();
+  VV* head_vec = reinterpret_cast<VV*>(base);                 // [64] (16 bytes each)
+  VV* tail_vec = reinterpret_cast<VV*>(base + kWave * 16);    // [64]
+  int32_t* rec = reinterpret_cast<int32_t*>(base + 2 * kWave * 16);   // [5][64]
   head_vec[lane] = head;
   tail_vec[lane] = acc;
-  if (cl == 0) {
+  if (lane % KL == 0) {
     rec[s] = head_ends;
     rec[kWave + s] = owned;
     rec[2 * kWave + s] = d0 < d1;
@@ -194,23 +265,33 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   if (lane < KL) {
     // slot order: a running piece of the current cut row
     bool run = false;
-    V rv = V(0);
+    VV rv;
+#pragma unroll
+    for (int q = 0; q < VE; ++q) rv.v[q] = V(0);
     for (int t = 0; t < S; ++t) {
       if (!rec[2 * kWave + t]) break;   // only trailing slots are empty
+      const VV hv = head_vec[t * KL + lane];
+      const VV tv = tail_vec[t * KL + lane];
       if (rec[t]) {
-        const V v = (run ? rv : V(0)) + head_vec[t * KL + cl];
-        if (colok) spmm_store(a, r0 + rec[3 * kWave + t], cl, v);
+        VV v;
+#pragma unroll
+        for (int q = 0; q < VE; ++q) v.v[q] = (run ? rv.v[q] : V(0)) + hv.v[q];
+        if (colok) spmm_store<V, VE>(a, r0 + rec[3 * kWave + t], col, v);
         run = false;
       }
       if (rec[kWave + t]) {
         run = true;
-        rv = tail_vec[t * KL + cl];
+        rv = tv;
       } else {
-        rv += tail_vec[t * KL + cl];
+#pragma unroll
+        for (int q = 0; q < VE; ++q) rv.v[q] += tv.v[q];
       }
     }
     if (!a.stream) {
-      if (colok) a.carry_vec[(int64_t)p * a.k + cl] = run ? rv : V(0);
+      if (colok) {
+#pragma unroll
+        for (int q = 0; q < VE; ++q) a.carry_vec[(int64_t)p * a.k + col + q] = run ? rv.v[q] : V(0);
+      }
       if (lane == 0) a.carry_row[p] = r1;
     }
   }
@@ -233,32 +314,49 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   *yp = fma(a.alpha, sum, *yp);
 }
 
-template <typename V, int KL>
+template <typename V, int KL, int VE>
 hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  const size_t lds = (size_t)kWavesPerBlock * spmm_wave_lds(sizeof(V), a.cap);
-  hipLaunchKernelGGL((spmm_merge_kernel<V, KL>), dim3(blocks), dim3(kBlock), lds, s, a);
+  const size_t lds = (size_t)kWavesPerBlock * spmm_wave_lds(a.cap, sizeof(V));
+  // bytes from X to the end of its last row's k columns
+  const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
+  if (xspan < (1ull << 32))
+    hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, true>), dim3(blocks), dim3(kBlock), lds, s, a);
+  else
+    hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, false>), dim3(blocks), dim3(kBlock), lds, s,
+                       a);
   return hipGetLastError();
+}
+
+// lanes per slot: the smallest power of two covering k columns, VE per lane
+template <typename V, int VE>
+hipError_t launch_ve(const SpmmArgs<V>& a, hipStream_t s) {
+  const int lanes = (a.k + VE - 1) / VE;
+  if (lanes <= 1) return launch_kl<V, 1, VE>(a, s);
+  if (lanes <= 2) return launch_kl<V, 2, VE>(a, s);
+  if (lanes <= 4) return launch_kl<V, 4, VE>(a, s);
+  if (lanes <= 8) return launch_kl<V, 8, VE>(a, s);
+  if (lanes <= 16) return launch_kl<V, 16, VE>(a, s);
+  if (lanes <= 32) return launch_kl<V, 32, VE>(a, s);
+  return launch_kl<V, 64, VE>(a, s);
 }
 
 }  // namespace
 
 size_t spmm_lds_bytes(int vbytes, int T) {
-  return (size_t)kWavesPerBlock * spmm_wave_lds(vbytes, spmm_stage_cap(T));
+  return (size_t)kWavesPerBlock * spmm_wave_lds(spmm_stage_cap(T), vbytes);
 }
 
 template <typename V>
 hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s) {
   if (a.P <= 0 || a.k <= 0) return hipSuccess;
   if (a.k > kWave || a.cap < spmm_stage_cap(a.T)) return hipErrorInvalidValue;
-  hipError_t err;
-  if (a.k <= 1) err = launch_kl<V, 1>(a, s);
-  else if (a.k <= 2) err = launch_kl<V, 2>(a, s);
-  else if (a.k <= 4) err = launch_kl<V, 4>(a, s);
-  else if (a.k <= 8) err = launch_kl<V, 8>(a, s);
-  else if (a.k <= 16) err = launch_kl<V, 16>(a, s);
-  else if (a.k <= 32) err = launch_kl<V, 32>(a, s);
-  else err = launch_kl<V, 64>(a, s);
+  // 16-byte lanes when every row of X and Y starts 16-byte aligned and k
+  // fills whole vectors; otherwise one element per lane
+  constexpr int VE = 16 / sizeof(V);
+  const bool vec = a.k % VE == 0 && a.ldx % VE == 0 && a.ldy % VE == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.X) | reinterpret_cast<uintptr_t>(a.Y)) & 15) == 0;
+  hipError_t err = vec ? launch_ve<V, VE>(a, s) : launch_ve<V, 1>(a, s);
   if (err != hipSuccess || a.stream || a.P <= 1) return err;
   hipLaunchKernelGGL((spmm_fixup_kernel<V>), dim3((a.P + kWavesPerBlock - 1) / kWavesPerBlock),
                      dim3(kBlock), 0, s, a);
