@@ -48,12 +48,12 @@ WORKLOADS = {
     "banded": "fp32 banded decay matrix, 32,000,000 rows, 24..40 entries within |i-j| <= 1000",
 }
 KERNEL_SOURCES = ["merge_kernels.hip", "binned_kernels.hip", "device_common.hpp", "internal.hpp"]
-# (the SpMM kernel, spmm_kernels.hip, has no committed counter table)
+SPMM_SOURCES = ["spmm_kernels.hip", "device_common.hpp", "internal.hpp"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "load_balanced_csr_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -91,7 +91,7 @@ def compulsory_bytes(w) -> int:
     return b
 
 
-def load_traffic(workload: str, kernel: str):
+def load_traffic(workload: str, kernel: str, files=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken with the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -100,7 +100,7 @@ def load_traffic(workload: str, kernel: str):
     with open(path) as f:
         table = json.load(f)
     rec = table.get("%s/%s" % (workload, kernel))
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -290,13 +290,15 @@ def run_spmm(args, w, torch, lb, dev):
         "roofline": {"bound": "hbm", "kernel": "spmm_merge_kernel", "achieved": round(gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel_ms": round(mean_ms, 5),
-                     "traffic": None,
+                     "traffic": load_traffic("%s_k%d" % (args.workload, k), "spmm_merge_kernel",
+                                             SPMM_SOURCES),
                      "timed": "events around the exec's launches (main kernel%s)"
                               % ("" if info["merge_reduce"] == "stream" else " + carry fix-up")},
         "exec_ms_median": round(statistics.median(ms), 5),
         "deterministic": deterministic,
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "workspace_bytes": need,
+        "kernel_source_hash": kernel_source_hash(SPMM_SOURCES),
     }
     plan.destroy()
     ok = True
