@@ -297,6 +297,98 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   }
 }
 
+// The same product for plans whose partitions hold whole rows (every row
+// <= T/8 entries, the stream layout). Rows go to slots instead of equal
+// runs: G slots share a row when the partition has fewer rows than slots
+// (G the largest power of two with rows * G <= slots), each taking every
+// G-th of the row's nonzeros in batches of 8 (all X-row loads first), and
+// meet by cross-lane adds. A round finishes S / G rows at once, so Y rows
+// are written together (coalesced) and no slot walks a row end alone.
+template <typename V, int KL, int VE, bool OFF32>
+__global__ __launch_bounds__(kBlock) void spmm_rows_kernel(const SpmmArgs<V> a) {
+  constexpr int S = kWave / KL;   // slots per wave
+  constexpr int B = 8;
+  typedef Vec<V, VE> VV;
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
+  const int p = blk * kWavesPerBlock + wave;
+  if (p >= a.P) return;
+  const int r0 = a.row_bounds[2 * p];
+  const int n0 = a.row_bounds[2 * p + 1];
+  const int r1 = a.row_bounds[2 * p + 2];
+  const int n1 = a.row_bounds[2 * p + 3];
+  const int R = r1 - r0, nloc = n1 - n0;
+  if (R == 0) return;
+
+  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V));
+  int32_t* s_rp = reinterpret_cast<int32_t*>(base);
+  int32_t* s_col = s_rp + a.cap;
+  int32_t* s_val = s_col + a.cap;
+  constexpr int W = sizeof(V) / 4;
+  stage_dma(s_rp, a.row_ptr, r0, R + 1, a.M + 1);
+  stage_dma(s_col, a.col_idx, n0, nloc, a.nnz);
+  stage_dma(s_val, reinterpret_cast<const int32_t*>(a.val), (int64_t)W * n0, W * nloc,
+            (int64_t)W * a.nnz);
+  wait_vmem();
+  wave_sync();
+  memory_order_point();
+  const int32_t* rpl = s_rp + (r0 & 3);
+  const int32_t* coll = s_col + (n0 & 3);
+  const V* vall = reinterpret_cast<const V*>(s_val + ((W * n0) & 3));
+
+  const int s = lane / KL;
+  const int col = (lane % KL) * VE;
+  const bool colok = col < a.k;
+  const int lcol = colok ? col : 0;
+  const char* xbase = reinterpret_cast<const char*>(a.X);
+  const uint32_t xrow_bytes = (uint32_t)a.ldx * (uint32_t)sizeof(V);
+  const uint32_t xcol_bytes = (uint32_t)lcol * (uint32_t)sizeof(V);
+  const V* xcol = a.X + lcol;
+
+  int G = 1;
+  while (G < S && R * (2 * G) <= S) G *= 2;
+  const int rpr = S / G;                 // rows per round
+  const int part = s % G, grp = s / G;
+  for (int rb = 0; rb < R; rb += rpr) {
+    const int rr = rb + grp;
+    const bool live = rr < R;
+    const int ra = live ? rpl[rr] - n0 : 0;
+    const int re = live ? rpl[rr + 1] - n0 : 0;
+    VV acc;
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc.v[q] = V(0);
+    for (int jb = ra + part; jb < re; jb += G * B) {
+      int cs[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) cs[u] = coll[min(jb + G * u, re - 1)];
+      VV xv[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (OFF32)
+          xv[u] = vec_load<V, VE>(
+              reinterpret_cast<const V*>(xbase + ((uint32_t)cs[u] * xrow_bytes + xcol_bytes)));
+        else
+          xv[u] = vec_load<V, VE>(xcol + (int64_t)cs[u] * a.ldx);
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int jj = jb + G * u;
+        const V v = jj < re ? vall[min(jj, re - 1)] : V(0);
+#pragma unroll
+        for (int q = 0; q < VE; ++q) acc.v[q] = fma(v, xv[u].v[q], acc.v[q]);
+      }
+    }
+    for (int g = 1; g < G; g <<= 1) {
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc.v[q] += __shfl_xor(acc.v[q], KL * g, kWave);
+    }
+    if (live && part == 0 && colok) spmm_store<V, VE>(a, r0 + rr, col, acc);
+  }
+}
+
 // Y[r] += alpha * (sum of the carries of r), one wave per partition: the
 // wave holding the first carry of a row sums that row's carries in
 // partition order (they are contiguous) and updates the row once.
@@ -320,7 +412,12 @@ hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s) {
   const size_t lds = (size_t)kWavesPerBlock * spmm_wave_lds(a.cap, sizeof(V));
   // bytes from X to the end of its last row's k columns
   const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
-  if (xspan < (1ull << 32))
+  const bool off32 = xspan < (1ull << 32);
+  if (a.stream && off32)
+    hipLaunchKernelGGL((spmm_rows_kernel<V, KL, VE, true>), dim3(blocks), dim3(kBlock), lds, s, a);
+  else if (a.stream)
+    hipLaunchKernelGGL((spmm_rows_kernel<V, KL, VE, false>), dim3(blocks), dim3(kBlock), lds, s, a);
+  else if (off32)
     hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, true>), dim3(blocks), dim3(kBlock), lds, s, a);
   else
     hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, false>), dim3(blocks), dim3(kBlock), lds, s,
