@@ -38,6 +38,15 @@
  *      inputs, identity, 2-D Laplacian closed forms per column, and exact
  *      alpha/beta arithmetic.
  *
+ *  oracle_spmv_coo_f32 / _f64:
+ *      the same product for a matrix given as COO entries (row, column,
+ *      value), PPoPP'23 page, Section 3.1 (atoms named by their row): each
+ *      entry, in storage order, adds its product to its row's fp64 sum;
+ *      then the same alpha/beta update and scale. Rows with no entry give
+ *      beta * y_old. No ordering of the entries is assumed. Pinned by
+ *      tests/pins.py: dense brute force, integer sums of shuffled entries,
+ *      empty rows, out-of-order entries.
+ *
  *  oracle_merge_splits:
  *      merge-path partition, PPoPP'23 page, Section 5.2.1: every nonzero and
  *      every row counts as one unit of work; units are split evenly. Written
@@ -149,6 +158,50 @@ int oracle_spmm_f64(int64_t M, const int32_t* row_ptr, const int32_t* col_idx,
       scale[i * k + c] = s;
     }
   }
+  return 0;
+}
+
+/* ---- COO SpMV: y_ref = alpha * (A x) + beta * y_old, fp64 ---------------- */
+
+int oracle_spmv_coo_f32(int64_t M, int64_t nnz, const int32_t* row_idx,
+                        const int32_t* col_idx, const float* values, const float* x,
+                        double alpha, double beta, const float* y_old, double* ref,
+                        double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    ref[i] = 0.0;
+    scale[i] = 0.0;
+  }
+  for (int64_t e = 0; e < nnz; ++e) {
+    int64_t i = row_idx[e];
+    if (i < 0 || i >= M) return -2;
+    double p = (double)values[e] * (double)x[col_idx[e]];
+    ref[i] = ref[i] + p;
+    scale[i] = scale[i] + fabs(p);
+  }
+  for (int64_t i = 0; i < M; ++i)
+    ref[i] = alpha * ref[i] + (beta != 0.0 ? beta * (double)y_old[i] : 0.0);
+  return 0;
+}
+
+int oracle_spmv_coo_f64(int64_t M, int64_t nnz, const int32_t* row_idx,
+                        const int32_t* col_idx, const double* values, const double* x,
+                        double alpha, double beta, const double* y_old, double* ref,
+                        double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    ref[i] = 0.0;
+    scale[i] = 0.0;
+  }
+  for (int64_t e = 0; e < nnz; ++e) {
+    int64_t i = row_idx[e];
+    if (i < 0 || i >= M) return -2;
+    double p = values[e] * x[col_idx[e]];
+    ref[i] = ref[i] + p;
+    scale[i] = scale[i] + fabs(p);
+  }
+  for (int64_t i = 0; i < M; ++i)
+    ref[i] = alpha * ref[i] + (beta != 0.0 ? beta * y_old[i] : 0.0);
   return 0;
 }
 

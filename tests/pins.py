@@ -344,7 +344,39 @@ def pin_spmm_alpha_beta(o):
         assert not np.array_equal(rb, base), "spmm beta term present"
 
 
+def pin_coo(o):
+    """COO entries of a dense matrix (row-major scan) give the dense product
+    bit for bit; shuffled entries with small-integer values give the exact
+    integer row sums; rows without entries give beta * y_old exactly."""
+    rng = np.random.default_rng(21)
+    for trial in range(8):
+        M, N = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        dt = F32 if trial % 2 == 0 else F64
+        A = np.where(rng.random((M, N)) < 0.3, rng.uniform(-1, 1, (M, N)), 0.0).astype(dt)
+        A[rng.random(M) < 0.3, :] = 0
+        x = rng.uniform(-1, 1, N).astype(dt)
+        rows, cols = np.nonzero(A)
+        ref, scale = o.spmv_coo(M, rows, cols, A[rows, cols], x)
+        want, wscale = _dense_matvec_ascending(A, x)
+        assert np.array_equal(ref, want) and np.array_equal(scale, wscale), ("coo dense", trial)
+    M, N, nnz = 400, 300, 5000
+    rows = rng.integers(0, M, nnz)
+    rows[rows % 7 == 0] = 1                       # rows that are multiples of 7 stay empty
+    cols = rng.integers(0, N, nnz)
+    perm = rng.permutation(nnz)
+    for dt in (F32, F64):
+        ints = rng.choice(np.array([-1, 1, 2, 4]), nnz).astype(dt)
+        y0 = rng.uniform(-1, 1, M).astype(dt)
+        ref, _ = o.spmv_coo(M, rows[perm], cols[perm], ints[perm], np.ones(N, dt), 1.0, 0.5, y0)
+        want = np.zeros(M)
+        np.add.at(want, rows, ints.astype(np.float64))
+        want = want + 0.5 * y0.astype(np.float64)
+        assert np.array_equal(ref, want), "coo integer sums, shuffled"
+        empty = np.setdiff1d(np.arange(M), rows)
+        assert empty.size > 0 and np.array_equal(ref[empty], 0.5 * y0[empty].astype(np.float64))
+
+
 ALL_PINS = [pin_dense_bruteforce, pin_identity, pin_diagonal, pin_integer_row_sums,
             pin_laplacian_closed_forms, pin_alpha_beta, pin_scale, pin_rows_subset,
             pin_merge_splits, pin_bins, pin_spmm_dense, pin_spmm_identity_and_laplacian,
-            pin_spmm_alpha_beta]
+            pin_spmm_alpha_beta, pin_coo]

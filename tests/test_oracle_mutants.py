@@ -38,6 +38,10 @@ MUTANTS = [
      "ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * (double)Y_old[i + c] : 0.0);"),
     ("spmm alpha dropped", "ref[i * k + c] = alpha * t + (beta != 0.0 ? beta * Y_old[i * ldy + c] : 0.0);",
      "ref[i * k + c] = t + (beta != 0.0 ? beta * Y_old[i * ldy + c] : 0.0);"),
+    ("coo value of the next entry", "    double p = (double)values[e] * (double)x[col_idx[e]];\n    ref[i] = ref[i] + p;",
+     "    double p = (double)values[e + (e + 1 < nnz)] * (double)x[col_idx[e]];\n    ref[i] = ref[i] + p;"),
+    ("coo beta dropped", "    ref[i] = alpha * ref[i] + (beta != 0.0 ? beta * y_old[i] : 0.0);",
+     "    ref[i] = alpha * ref[i];"),
     ("bins reversed order", "bins[fill[b]] = (int32_t)r;", "bins[offsets[b + 1] - 1 - (fill[b] - offsets[b])] = (int32_t)r;"),
 ]
 
