@@ -105,7 +105,7 @@ def load_traffic(workload: str, kernel: str, files=KERNEL_SOURCES):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float, y_gpu):
+def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
     """The oracle as it stands, on one host core, repeated on the whole
     workload until the budget is spent (at least once). Its result also
     checks the GPU's first exec (every row, the acceptance bound)."""
@@ -115,10 +115,16 @@ def cpu_baseline(w, budget_s: float, y_gpu):
     except (AttributeError, OSError):
         pass
     times = []
+    rows = (np.repeat(np.arange(w.M, dtype=np.int32), np.diff(w.row_ptr))
+            if fmt == "coo" else None)
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
-        ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
+        if fmt == "coo":
+            ref, scale = oracle.spmv_coo(w.M, rows, w.col_idx, w.values, w.x, w.alpha, w.beta,
+                                         w.y0)
+        else:
+            ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 50:
             break
@@ -338,6 +344,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--format", default="csr", choices=["csr", "coo"],
+                    help="coo: plan from row-sorted COO entries (row offsets derived on the device)")
     ap.add_argument("--rhs", type=int, default=1, metavar="K",
                     help="K > 1: time the multi-vector form (SpMM) with K right-hand sides")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -376,15 +384,23 @@ def main():
     torch.cuda.synchronize()
 
     # planning cost (separate from the steps): median of 5 plan/destroy cycles
+    popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread)
+    if args.format == "coo":
+        rows = torch.from_numpy(np.repeat(np.arange(w.M, dtype=np.int32),
+                                          np.diff(w.row_ptr))).to(dev)
+
+        def make_plan():
+            return lb.Plan.coo(rows, col, val, (w.M, w.N), **popts)
+    else:
+        def make_plan():
+            return lb.Plan(rp, col, val, (w.M, w.N), **popts)
     plan_ms = []
     for _ in range(5):
         t0 = time.perf_counter()
-        p = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
-                    items_per_thread=args.items_per_thread)
+        p = make_plan()
         plan_ms.append((time.perf_counter() - t0) * 1e3)
         p.destroy()
-    plan = lb.Plan(rp, col, val, (w.M, w.N), strategy=args.strategy,
-                   items_per_thread=args.items_per_thread)
+    plan = make_plan()
     info = plan.info
 
     # first exec on fresh inputs; the cpu_baseline leg checks it against the oracle
@@ -477,7 +493,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
                    "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha, "beta": w.beta,
-                   "seed": w.seed, "strategy": info["strategy"],
+                   "seed": w.seed, "format": args.format, "strategy": info["strategy"],
                    "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
                    "items_per_wave": info["items_per_wave"],
                    "cache": "warm" if flush is None else
@@ -507,7 +523,7 @@ def main():
     ok = True
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"], ok, worst = cpu_baseline(w, args.cpu_seconds, y_first)
+        out["cpu_baseline"], ok, worst = cpu_baseline(w, args.cpu_seconds, y_first, args.format)
         out["cpu_baseline"]["gpu_speedup"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
         out["parity"] = {"ok": ok, "worst_over_bound": round(worst, 5),
                          "checked": "first exec vs the oracle, every row"}

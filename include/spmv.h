@@ -178,6 +178,27 @@ SPMV_API spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int6
                            const spmv_plan_options_t* options,
                            hipStream_t stream);
 
+/* Build a plan for A given in COO form: entry e is (row_idx[e], col_idx[e],
+ * values[e]), e < nnz, sorted by row (non-decreasing row_idx; any order
+ * within a row, repeated positions add up). "A Programming Model for GPU
+ * Load Balancing" (PPoPP'23), Section 3.1: the same atoms (nonzeros) and
+ * tiles (rows) as CSR, named by a row index per atom. The plan derives the
+ * CSR row offsets on the device (row r starts at the first entry whose row
+ * index is >= r), keeps them in an allocation of its own, and then plans and
+ * executes exactly as spmv_plan_ex would; spmv_exec and spmv_exec_multi
+ * apply unchanged.
+ *
+ * row_idx  device int32[nnz], each in [0, M), sorted; read only during this
+ *          call (it may be freed afterwards). Out of range or out of order
+ *          gives SPMV_ERR_INVALID_MATRIX (checked on the device).
+ * col_idx, values, dtype, options, stream: as for spmv_plan_ex (borrowed).
+ * One more device allocation (the row offsets), freed by spmv_destroy; one
+ * more stream synchronisation (the order check). */
+SPMV_API spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                                     const int32_t* row_idx, const int32_t* col_idx,
+                                     const void* values, spmv_dtype_t dtype,
+                                     const spmv_plan_options_t* options, hipStream_t stream);
+
 /* y = alpha * A * x + beta * y.
  *
  * x  device array of N elements of the plan's dtype.

@@ -25,7 +25,7 @@ STRATEGY = {"auto": 0, "merge": 1, "binned": 2}
 STRATEGY_NAME = {v: k for k, v in STRATEGY.items()}
 MAX_BINS = 8
 
-EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_exec", "spmv_exec_events", "spmv_destroy",
+EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
@@ -79,6 +79,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p]
     lib.spmv_plan_ex.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32,
                                  ctypes.POINTER(PlanOptions), p]
+    lib.spmv_plan_coo.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
     lib.spmv_exec.argtypes = [p, p, p, d, d, p]
     lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
     lib.spmv_destroy.argtypes = [p]
@@ -171,6 +172,26 @@ def spmv_plan(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor
         _check(lib.spmv_plan(*args, _stream(stream)), "spmv_plan")
     else:
         _check(lib.spmv_plan_ex(*args, ctypes.byref(options), _stream(stream)), "spmv_plan_ex")
+    return h.value
+
+
+def spmv_plan_coo(row_idx: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor, M: int,
+                  N: int, options: Optional[PlanOptions] = None, stream=None) -> int:
+    """Plan handle for a COO matrix sorted by row (device int32 row_idx /
+    col_idx, fp32/fp64 values). col_idx and values are borrowed; row_idx is
+    read only during the call."""
+    lib = load()
+    nnz = int(col_idx.numel())
+    if int(row_idx.numel()) != nnz:
+        raise ValueError("row_idx and col_idx must have the same length")
+    h = ctypes.c_void_p()
+    _check(lib.spmv_plan_coo(ctypes.byref(h), M, N, nnz,
+                             _dev_ptr(row_idx, "row_idx", (torch.int32,)),
+                             _dev_ptr(col_idx, "col_idx", (torch.int32,)),
+                             _dev_ptr(values, "values", (torch.float32, torch.float64)),
+                             _dtype_code(values),
+                             ctypes.byref(options) if options is not None else None,
+                             _stream(stream)), "spmv_plan_coo")
     return h.value
 
 
@@ -308,6 +329,17 @@ class Plan:
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
                                 merge_reduce, stream_lanes, x_window)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
+
+    @classmethod
+    def coo(cls, row_idx, col_idx, values, shape, stream=None, **opts):
+        """Plan for a COO matrix sorted by row (see spmv_plan_coo); the same
+        options as the CSR constructor."""
+        self = cls.__new__(cls)
+        self.M, self.N = int(shape[0]), int(shape[1])
+        self._keep = (col_idx, values)
+        o = make_options(**opts) if opts else None
+        self.handle = spmv_plan_coo(row_idx, col_idx, values, self.M, self.N, o, stream)
+        return self
 
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):
         spmv_exec(self.handle, x, y, alpha, beta, stream)

@@ -92,6 +92,7 @@ struct spmv_plan_st {
   void* carry_val;
   int32_t* bins;
   int32_t* win_span;
+  void* owned_row_ptr;   // COO plans: the row offsets derived from row_idx
 };
 
 namespace {
@@ -570,6 +571,55 @@ spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   return spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, nullptr, stream);
 }
 
+spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                            const int32_t* row_idx, const int32_t* col_idx, const void* values,
+                            spmv_dtype_t dtype, const spmv_plan_options_t* options,
+                            hipStream_t stream) {
+  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (M < 0 || N < 0 || nnz < 0)
+    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
+                (long long)N, (long long)nnz);
+  if (nnz > 0 && !row_idx) return fail(SPMV_ERR_INVALID_ARG, "row_idx is NULL");
+  if (M == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "M = 0 needs nnz = 0");
+  if (nnz > kInt32Max || M >= kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
+  // row offsets (M + 1) and a flag, in one allocation the plan keeps
+  const size_t off_flag = align256(sizeof(int32_t) * (size_t)(M + 1));
+  void* buf = nullptr;
+  hipError_t err = hipMalloc(&buf, off_flag + 256);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SPMV_ERR_ALLOC, "hipMalloc for the COO row offsets failed: %s",
+                hipGetErrorString(err));
+  }
+  int32_t* row_ptr = static_cast<int32_t*>(buf);
+  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + off_flag);
+  int32_t host_flag = 0;
+  if ((err = hipMemsetAsync(flag, 0, sizeof(int32_t), stream)) != hipSuccess ||
+      (err = launch_coo_row_ptr(row_idx, nnz, M, row_ptr, flag, stream)) != hipSuccess ||
+      (err = hipMemcpyAsync(&host_flag, flag, sizeof host_flag, hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess ||
+      (err = hipStreamSynchronize(stream)) != hipSuccess) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(buf);
+    return hip_fail(err, "spmv_plan_coo: row offsets");
+  }
+  if (host_flag) {
+    (void)hipFree(buf);
+    return fail(SPMV_ERR_INVALID_MATRIX,
+                "COO row indices must lie in [0, M) and be sorted in non-decreasing order");
+  }
+  spmv_status_t st = spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, options,
+                                  stream);
+  if (st != SPMV_SUCCESS) {
+    (void)hipFree(buf);
+    return st;
+  }
+  (*out)->owned_row_ptr = buf;
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink, hipStream_t stream) {
   if (!data || !sink || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(data) & 15) ||
       (reinterpret_cast<uintptr_t>(sink) & 3))
@@ -609,6 +659,10 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
   }
   p->magic = 0;
   hipError_t err = hipFree(p->ws);
+  if (p->owned_row_ptr) {
+    const hipError_t e2 = hipFree(p->owned_row_ptr);
+    if (err == hipSuccess) err = e2;
+  }
   delete p;
   if (err != hipSuccess) return hip_fail(err, "spmv_destroy: hipFree");
   return SPMV_SUCCESS;

@@ -74,6 +74,10 @@ hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, i
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
+// row_ptr[0..M] from row indices sorted by row (COO); *flag |= 1 when an
+// index is outside [0, M) or out of order (flag zeroed by the caller).
+hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, int32_t* row_ptr,
+                              int32_t* flag, hipStream_t s);
 // Per group of `group` consecutive partitions: up to kWinIntervals
 // chunk-aligned column intervals covering the group's quads within
 // cap_bytes (kWinTable int32 per group, win_span holds win_span_ints);

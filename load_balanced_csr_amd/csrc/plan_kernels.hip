@@ -22,6 +22,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 namespace spmv {
 namespace {
 
@@ -388,6 +390,39 @@ __global__ __launch_bounds__(kBlock) void window_count_kernel(const int32_t* __r
   }
 }
 
+// COO input, "A Programming Model for GPU Load Balancing" (PPoPP'23),
+// Section 3.1: the same atoms (nonzeros) and tiles (rows), given one row
+// index per atom instead of row offsets. With the row indices sorted, row r's
+// atoms start at the first index >= r: row_ptr[r] = lower_bound(row_idx, r),
+// one binary search per row, and every CSR step then applies unchanged.
+__global__ __launch_bounds__(kBlock) void coo_row_ptr_kernel(const int32_t* __restrict__ row_idx,
+                                                             int32_t nnz, int32_t M,
+                                                             int32_t* __restrict__ row_ptr) {
+  const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (r > M) return;
+  int lo = 0, hi = nnz;
+  while (lo < hi) {
+    const int mid = (int)(((int64_t)lo + hi) >> 1);
+    if (row_idx[mid] < r) lo = mid + 1;
+    else hi = mid;
+  }
+  row_ptr[r] = lo;
+}
+
+// flag |= 1 when a row index is outside [0, M) or smaller than its
+// predecessor (the offsets above need them sorted)
+__global__ __launch_bounds__(kBlock) void coo_check_kernel(const int32_t* __restrict__ row_idx,
+                                                           int64_t nnz, int32_t M,
+                                                           int32_t* flag) {
+  bool bad = false;
+  for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < nnz;
+       e += (int64_t)gridDim.x * kBlock) {
+    const int32_t r = row_idx[e];
+    bad |= r < 0 || r >= M || (e + 1 < nnz && row_idx[e + 1] < r);
+  }
+  if (__ballot(bad) != 0 && lane_id() == 0) atomicOr(flag, 1);
+}
+
 int n_blocks(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
 
 }  // namespace
@@ -450,6 +485,20 @@ hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(window_count_kernel, dim3((int)std::min<int64_t>(n_blocks(groups, kBlock), 64)),
                      dim3(kBlock), 0, s, win_span, (int32_t)groups, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, int32_t* row_ptr,
+                              int32_t* flag, hipStream_t s) {
+  if (nnz > 0) {
+    const int blocks = (int)std::min<int64_t>(n_blocks(nnz, kBlock), 8192);
+    hipLaunchKernelGGL(coo_check_kernel, dim3(blocks), dim3(kBlock), 0, s, row_idx, nnz,
+                       (int32_t)M, flag);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(coo_row_ptr_kernel, dim3(n_blocks(M + 1, kBlock)), dim3(kBlock), 0, s,
+                     row_idx, (int32_t)nnz, (int32_t)M, row_ptr);
   return hipGetLastError();
 }
 
