@@ -59,6 +59,10 @@ class OracleLib:
             f = getattr(lib, name)
             f.argtypes = [i64, i64, p, p, p, p, d, d, p, p, p]
             f.restype = ctypes.c_int
+        for name in ("oracle_spmv_t_f32", "oracle_spmv_t_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [i64, i64, p, p, p, p, d, d, p, p, p]
+            f.restype = ctypes.c_int
         lib.oracle_merge_splits.argtypes = [i64, i64, p, i64, p, p]
         lib.oracle_merge_splits.restype = i64
         lib.oracle_bins.argtypes = [i64, p, i32, p, p, p, p]
@@ -156,6 +160,28 @@ class OracleLib:
         assert rc == 0, rc
         return ref, scale
 
+    def spmv_t(self, N: int, row_ptr, col_idx, values, x, alpha: float = 1.0,
+               beta: float = 0.0, y_old=None) -> Tuple[np.ndarray, np.ndarray]:
+        """y = alpha * A^T x + beta * y_old for the CSR matrix A (M x N):
+        x has M entries, the result N."""
+        values = np.asarray(values)
+        dt = values.dtype
+        if dt not in (np.float32, np.float64):
+            raise TypeError("values must be float32 or float64")
+        if beta != 0.0 and y_old is None:
+            raise ValueError("beta != 0 needs y_old")
+        rp, col = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+        val, xx = _c(values, dt), _c(x, dt)
+        yo = _c(y_old, dt) if beta != 0.0 else None
+        M = rp.size - 1
+        ref = np.empty(N, dtype=np.float64)
+        scale = np.empty(N, dtype=np.float64)
+        f = self.lib.oracle_spmv_t_f32 if dt == np.float32 else self.lib.oracle_spmv_t_f64
+        rc = f(M, N, _ptr(rp), _ptr(col), _ptr(val), _ptr(xx), float(alpha), float(beta),
+               _ptr(yo), _ptr(ref), _ptr(scale))
+        assert rc == 0
+        return ref, scale
+
     def merge_splits(self, row_ptr, T: int) -> Tuple[np.ndarray, np.ndarray]:
         """Merge-path split coordinates (rows ended, nonzeros consumed) at
         every multiple of T items and at the end, by walking the items."""
@@ -216,6 +242,10 @@ def spmm(*args, **kw):
 
 def spmv_coo(*args, **kw):
     return _default().spmv_coo(*args, **kw)
+
+
+def spmv_t(*args, **kw):
+    return _default().spmv_t(*args, **kw)
 
 
 def merge_splits(*args, **kw):

@@ -47,6 +47,15 @@
  *      tests/pins.py: dense brute force, integer sums of shuffled entries,
  *      empty rows, out-of-order entries.
  *
+ *  oracle_spmv_t_f32 / _f64:
+ *      the transposed product y = alpha * A^T x + beta * y_old for A in
+ *      CSR (M x N; x has M entries, y has N), PPoPP'23 page, Section 3.1
+ *      read with rows and columns exchanged: entry (i, j) adds a_ij * x_i
+ *      to column j's fp64 sum; entries are taken in storage order (rows
+ *      ascending), then the same alpha/beta update and scale. Pinned by
+ *      tests/pins.py: dense brute force of A^T x, the adjoint identity
+ *      z . (A x) = x . (A^T z) on small integers, a symmetric matrix.
+ *
  *  oracle_merge_splits:
  *      merge-path partition, PPoPP'23 page, Section 5.2.1: every nonzero and
  *      every row counts as one unit of work; units are split evenly. Written
@@ -202,6 +211,50 @@ int oracle_spmv_coo_f64(int64_t M, int64_t nnz, const int32_t* row_idx,
   }
   for (int64_t i = 0; i < M; ++i)
     ref[i] = alpha * ref[i] + (beta != 0.0 ? beta * y_old[i] : 0.0);
+  return 0;
+}
+
+/* ---- transposed SpMV: y_ref = alpha * (A^T x) + beta * y_old, fp64 ------- */
+
+int oracle_spmv_t_f32(int64_t M, int64_t N, const int32_t* row_ptr, const int32_t* col_idx,
+                      const float* values, const float* x, double alpha, double beta,
+                      const float* y_old, double* ref, double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t j = 0; j < N; ++j) {
+    ref[j] = 0.0;
+    scale[j] = 0.0;
+  }
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      int64_t j = col_idx[e];
+      double p = (double)values[e] * (double)x[i];
+      ref[j] = ref[j] + p;
+      scale[j] = scale[j] + fabs(p);
+    }
+  }
+  for (int64_t j = 0; j < N; ++j)
+    ref[j] = alpha * ref[j] + (beta != 0.0 ? beta * (double)y_old[j] : 0.0);
+  return 0;
+}
+
+int oracle_spmv_t_f64(int64_t M, int64_t N, const int32_t* row_ptr, const int32_t* col_idx,
+                      const double* values, const double* x, double alpha, double beta,
+                      const double* y_old, double* ref, double* scale) {
+  if (beta != 0.0 && y_old == NULL) return -1;
+  for (int64_t j = 0; j < N; ++j) {
+    ref[j] = 0.0;
+    scale[j] = 0.0;
+  }
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      int64_t j = col_idx[e];
+      double p = values[e] * x[i];
+      ref[j] = ref[j] + p;
+      scale[j] = scale[j] + fabs(p);
+    }
+  }
+  for (int64_t j = 0; j < N; ++j)
+    ref[j] = alpha * ref[j] + (beta != 0.0 ? beta * y_old[j] : 0.0);
   return 0;
 }
 

@@ -376,7 +376,40 @@ def pin_coo(o):
         assert empty.size > 0 and np.array_equal(ref[empty], 0.5 * y0[empty].astype(np.float64))
 
 
+def pin_transposed(o):
+    """A^T x equals the hand-written dense product with A transposed, bit for
+    bit (rows ascending), on non-square matrices; z . (A x) = x . (A^T z)
+    exactly for small integers; the 5-point Laplacian (symmetric, columns of
+    a row in the order its rows reach a column) gives A^T x = A x bit for bit."""
+    rng = np.random.default_rng(22)
+    for trial in range(10):
+        M, N = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        if M == N:
+            N += 3
+        dt = F32 if trial % 2 == 0 else F64
+        A = np.where(rng.random((M, N)) < 0.3, rng.uniform(-1, 1, (M, N)), 0.0).astype(dt)
+        A[:, rng.random(N) < 0.3] = 0                 # empty columns of A: rows of A^T
+        x = rng.uniform(-1, 1, M).astype(dt)
+        rp, col, val = _csr_from_dense(A)
+        ref, scale = o.spmv_t(N, rp, col, val, x)
+        want, wscale = _dense_matvec_ascending(np.ascontiguousarray(A.T), x)
+        assert np.array_equal(ref, want) and np.array_equal(scale, wscale), ("A^T x", trial)
+    M, N = 300, 200
+    L = rng.integers(0, 15, M)
+    rp = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    col = np.concatenate([np.sort(rng.choice(N, l, replace=False)) for l in L]).astype(np.int32)
+    ints = rng.choice(np.array([-2, -1, 1, 3]), rp[-1]).astype(F64)
+    x = rng.integers(-3, 4, N).astype(F64)
+    z = rng.integers(-3, 4, M).astype(F64)
+    ax, _ = o.spmv(rp, col, ints, x)
+    atz, _ = o.spmv_t(N, rp, col, ints, z)
+    assert float(np.dot(z, ax)) == float(np.dot(x, atz)), "adjoint identity"
+    rp, col, val = _laplacian(9)
+    xx = rng.uniform(-1, 1, 81)
+    assert np.array_equal(o.spmv_t(81, rp, col, val, xx)[0], o.spmv(rp, col, val, xx)[0])
+
+
 ALL_PINS = [pin_dense_bruteforce, pin_identity, pin_diagonal, pin_integer_row_sums,
             pin_laplacian_closed_forms, pin_alpha_beta, pin_scale, pin_rows_subset,
             pin_merge_splits, pin_bins, pin_spmm_dense, pin_spmm_identity_and_laplacian,
-            pin_spmm_alpha_beta, pin_coo]
+            pin_spmm_alpha_beta, pin_coo, pin_transposed]

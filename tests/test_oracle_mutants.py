@@ -42,6 +42,10 @@ MUTANTS = [
      "    double p = (double)values[e + (e + 1 < nnz)] * (double)x[col_idx[e]];\n    ref[i] = ref[i] + p;"),
     ("coo beta dropped", "    ref[i] = alpha * ref[i] + (beta != 0.0 ? beta * y_old[i] : 0.0);",
      "    ref[i] = alpha * ref[i];"),
+    ("transposed: x indexed by column", "double p = (double)values[e] * (double)x[i];",
+     "double p = (double)values[e] * (double)x[j];"),
+    ("transposed: sum into the row", "      double p = values[e] * x[i];\n      ref[j] = ref[j] + p;",
+     "      double p = values[e] * x[i];\n      ref[i % N] = ref[i % N] + p;"),
     ("bins reversed order", "bins[fill[b]] = (int32_t)r;", "bins[offsets[b + 1] - 1 - (fill[b] - offsets[b])] = (int32_t)r;"),
 ]
 
