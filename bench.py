@@ -123,6 +123,9 @@ def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
         if fmt == "coo":
             ref, scale = oracle.spmv_coo(w.M, rows, w.col_idx, w.values, w.x, w.alpha, w.beta,
                                          w.y0)
+        elif fmt == "transpose":
+            ref, scale = oracle.spmv_t(w.N, w.row_ptr, w.col_idx, w.values, w.x, w.alpha,
+                                       w.beta, w.y0)
         else:
             ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
         times.append(time.perf_counter() - t0)
@@ -130,7 +133,7 @@ def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
             break
     t = statistics.median(times)
     ok, worst, _ = oracle.within_tolerance(y_gpu, ref, scale, w.alpha, w.beta, w.y0,
-                                           row_ptr=w.row_ptr)
+                                           row_ptr=w.row_ptr if fmt != "transpose" else None)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -344,8 +347,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--format", default="csr", choices=["csr", "coo"],
-                    help="coo: plan from row-sorted COO entries (row offsets derived on the device)")
+    ap.add_argument("--format", default="csr", choices=["csr", "coo", "transpose"],
+                    help="coo: plan from row-sorted COO entries (row offsets derived on the "
+                         "device); transpose: y = alpha A^T x + beta y (plan-time transpose)")
     ap.add_argument("--rhs", type=int, default=1, metavar="K",
                     help="K > 1: time the multi-vector form (SpMM) with K right-hand sides")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -391,6 +395,11 @@ def main():
 
         def make_plan():
             return lb.Plan.coo(rows, col, val, (w.M, w.N), **popts)
+    elif args.format == "transpose":
+        assert w.M == w.N, "the transposed benchmark uses square workloads"
+
+        def make_plan():
+            return lb.Plan.transpose(rp, col, val, (w.M, w.N), **popts)
     else:
         def make_plan():
             return lb.Plan(rp, col, val, (w.M, w.N), **popts)

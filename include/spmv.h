@@ -199,6 +199,40 @@ SPMV_API spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int
                                      const void* values, spmv_dtype_t dtype,
                                      const spmv_plan_options_t* options, hipStream_t stream);
 
+/* Build a plan whose spmv_exec computes y = alpha * A^T * x + beta * y for
+ * the CSR matrix A (M x N): x has M entries, y has N; the plan's shape is
+ * N x M. The transpose is built once here: a stable device radix sort of
+ * the column indices with their entry positions, then A^T's column indices
+ * (A's rows) and values gathered in that order, which is CSR of A^T with
+ * each row's entries in ascending column order; its row offsets are
+ * derived as for spmv_plan_coo. "A Programming Model for GPU Load
+ * Balancing" (PPoPP'23), Section 3.1 (atoms and tiles of a CSC layout).
+ * Then it plans and executes as spmv_plan_ex would (spmv_exec_multi too).
+ *
+ * row_ptr, col_idx, values, dtype, options, stream: A as for spmv_plan_ex;
+ * all three are read only during this call. The plan keeps its own copy of
+ * A^T's indices and values (nnz * (4 + value size) bytes plus the offsets),
+ * so later changes to A's values do not reach it. SPMV_ERR_INVALID_MATRIX
+ * when row_ptr is malformed or a column index is outside [0, N). Scratch of
+ * about 8 * nnz bytes plus the sort's is allocated and freed here; two more
+ * stream synchronisations than spmv_plan_ex. */
+SPMV_API spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N,
+                                           int64_t nnz, const int32_t* row_ptr,
+                                           const int32_t* col_idx, const void* values,
+                                           spmv_dtype_t dtype,
+                                           const spmv_plan_options_t* options,
+                                           hipStream_t stream);
+
+/* Build a plan for y = alpha * A * x + beta * y with A (M x N) given in CSC:
+ * col_ptr int32[N+1], row_idx int32[nnz] (each in [0, M)), values[nnz]. The
+ * CSC arrays of A are the CSR arrays of A^T, so this is
+ * spmv_plan_transpose of that N x M matrix; the same copies, checks and
+ * errors apply. */
+SPMV_API spmv_status_t spmv_plan_csc(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                                     const int32_t* col_ptr, const int32_t* row_idx,
+                                     const void* values, spmv_dtype_t dtype,
+                                     const spmv_plan_options_t* options, hipStream_t stream);
+
 /* y = alpha * A * x + beta * y.
  *
  * x  device array of N elements of the plan's dtype.

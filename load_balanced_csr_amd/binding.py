@@ -25,7 +25,8 @@ STRATEGY = {"auto": 0, "merge": 1, "binned": 2}
 STRATEGY_NAME = {v: k for k, v in STRATEGY.items()}
 MAX_BINS = 8
 
-EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_exec", "spmv_exec_events", "spmv_destroy",
+EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
+            "spmv_plan_csc", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
@@ -80,6 +81,8 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_ex.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32,
                                  ctypes.POINTER(PlanOptions), p]
     lib.spmv_plan_coo.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
+    lib.spmv_plan_transpose.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
+    lib.spmv_plan_csc.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
     lib.spmv_exec.argtypes = [p, p, p, d, d, p]
     lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
     lib.spmv_destroy.argtypes = [p]
@@ -193,6 +196,33 @@ def spmv_plan_coo(row_idx: torch.Tensor, col_idx: torch.Tensor, values: torch.Te
                              ctypes.byref(options) if options is not None else None,
                              _stream(stream)), "spmv_plan_coo")
     return h.value
+
+
+def _plan_other(fn: str, ptr: torch.Tensor, idx: torch.Tensor, values: torch.Tensor, M: int,
+                N: int, options: Optional[PlanOptions], stream) -> int:
+    lib = load()
+    h = ctypes.c_void_p()
+    _check(getattr(lib, fn)(ctypes.byref(h), M, N, int(idx.numel()),
+                            _dev_ptr(ptr, "offsets", (torch.int32,)),
+                            _dev_ptr(idx, "indices", (torch.int32,)),
+                            _dev_ptr(values, "values", (torch.float32, torch.float64)),
+                            _dtype_code(values),
+                            ctypes.byref(options) if options is not None else None,
+                            _stream(stream)), fn)
+    return h.value
+
+
+def spmv_plan_transpose(row_ptr, col_idx, values, M: int, N: int,
+                        options: Optional[PlanOptions] = None, stream=None) -> int:
+    """Plan computing y = alpha * A^T x + beta * y for the CSR matrix A (M x N);
+    the plan keeps its own copy of A^T (A's tensors are read only here)."""
+    return _plan_other("spmv_plan_transpose", row_ptr, col_idx, values, M, N, options, stream)
+
+
+def spmv_plan_csc(col_ptr, row_idx, values, M: int, N: int,
+                  options: Optional[PlanOptions] = None, stream=None) -> int:
+    """Plan computing y = alpha * A x + beta * y for A (M x N) in CSC form."""
+    return _plan_other("spmv_plan_csc", col_ptr, row_idx, values, M, N, options, stream)
 
 
 def spmv_exec(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
@@ -339,6 +369,28 @@ class Plan:
         self._keep = (col_idx, values)
         o = make_options(**opts) if opts else None
         self.handle = spmv_plan_coo(row_idx, col_idx, values, self.M, self.N, o, stream)
+        return self
+
+    @classmethod
+    def transpose(cls, row_ptr, col_idx, values, shape, stream=None, **opts):
+        """Plan for y = alpha * A^T x + beta * y, A (shape = (M, N)) in CSR;
+        the plan's own shape is (N, M)."""
+        self = cls.__new__(cls)
+        self.M, self.N = int(shape[1]), int(shape[0])
+        self._keep = ()
+        o = make_options(**opts) if opts else None
+        self.handle = spmv_plan_transpose(row_ptr, col_idx, values, int(shape[0]),
+                                          int(shape[1]), o, stream)
+        return self
+
+    @classmethod
+    def csc(cls, col_ptr, row_idx, values, shape, stream=None, **opts):
+        """Plan for y = alpha * A x + beta * y, A (shape = (M, N)) in CSC."""
+        self = cls.__new__(cls)
+        self.M, self.N = int(shape[0]), int(shape[1])
+        self._keep = ()
+        o = make_options(**opts) if opts else None
+        self.handle = spmv_plan_csc(col_ptr, row_idx, values, self.M, self.N, o, stream)
         return self
 
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):

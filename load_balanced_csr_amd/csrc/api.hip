@@ -93,6 +93,7 @@ struct spmv_plan_st {
   int32_t* bins;
   int32_t* win_span;
   void* owned_row_ptr;   // COO plans: the row offsets derived from row_idx
+  void* owned_entries;   // transposed plans: the column indices and values of A^T
 };
 
 namespace {
@@ -620,6 +621,100 @@ spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   return SPMV_SUCCESS;
 }
 
+spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  const void* values, spmv_dtype_t dtype,
+                                  const spmv_plan_options_t* options, hipStream_t stream) {
+  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (M < 0 || N < 0 || nnz < 0)
+    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
+                (long long)N, (long long)nnz);
+  if (dtype != SPMV_F32 && dtype != SPMV_F64)
+    return fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (M > 0 && !row_ptr) return fail(SPMV_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (nnz > 0 && (!col_idx || !values))
+    return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
+  if ((M == 0 || N == 0) && nnz != 0)
+    return fail(SPMV_ERR_INVALID_ARG, "M = 0 or N = 0 needs nnz = 0");
+  if (nnz > kInt32Max || M >= kInt32Max || N >= kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
+  const size_t vs = dtype == SPMV_F32 ? 4 : 8;
+  int bits = 1;
+  while (bits < 31 && (int64_t(1) << bits) < N) ++bits;
+  // owned by the plan: A^T's column indices (rows of A) and values
+  const size_t o_val = align256(sizeof(int32_t) * (size_t)nnz);
+  void* owned = nullptr;
+  hipError_t err = hipMalloc(&owned, o_val + align256(vs * (size_t)nnz) + 256);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SPMV_ERR_ALLOC, "hipMalloc for the transposed entries failed: %s",
+                hipGetErrorString(err));
+  }
+  int32_t* col_t = static_cast<int32_t*>(owned);
+  void* val_t = static_cast<char*>(owned) + o_val;
+  // scratch for this call: sorted keys (A^T's row indices), positions, a
+  // flag and the sort's own scratch
+  size_t sort_bytes = 0;
+  if (nnz > 0 &&
+      (err = sort_columns(nullptr, &sort_bytes, col_idx, nullptr, nullptr, nnz, bits, stream)) !=
+          hipSuccess) {
+    (void)hipFree(owned);
+    return hip_fail(err, "spmv_plan_transpose: sort size");
+  }
+  const size_t o_perm = align256(sizeof(int32_t) * (size_t)nnz);
+  const size_t o_flag = o_perm + align256(sizeof(int32_t) * (size_t)nnz);
+  const size_t o_sort = o_flag + 256;
+  void* scratch = nullptr;
+  if ((err = hipMalloc(&scratch, o_sort + align256(sort_bytes) + 256)) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(owned);
+    return fail(SPMV_ERR_ALLOC, "hipMalloc for the transpose scratch failed: %s",
+                hipGetErrorString(err));
+  }
+  int32_t* keys_t = static_cast<int32_t*>(scratch);
+  int32_t* perm = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + o_perm);
+  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + o_flag);
+  void* sort_tmp = static_cast<char*>(scratch) + o_sort;
+  auto release = [&](spmv_status_t st) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(scratch);
+    if (st != SPMV_SUCCESS) (void)hipFree(owned);
+    return st;
+  };
+  int32_t host_flag = 0;
+  if (M > 0 &&
+      ((err = hipMemsetAsync(flag, 0, sizeof(int32_t), stream)) != hipSuccess ||
+       (err = launch_csr_check(row_ptr, M, nnz, flag, stream)) != hipSuccess ||
+       (err = hipMemcpyAsync(&host_flag, flag, sizeof host_flag, hipMemcpyDeviceToHost,
+                             stream)) != hipSuccess ||
+       (err = hipStreamSynchronize(stream)) != hipSuccess))
+    return release(hip_fail(err, "spmv_plan_transpose: row_ptr check"));
+  if (host_flag)
+    return release(fail(SPMV_ERR_INVALID_MATRIX,
+                        "row_ptr must start at 0, never decrease and end at nnz"));
+  if (nnz > 0 &&
+      ((err = sort_columns(sort_tmp, &sort_bytes, col_idx, keys_t, perm, nnz, bits, stream)) !=
+           hipSuccess ||
+       (err = launch_transpose_gather(row_ptr, M, perm, values, (int)vs, nnz, col_t, val_t,
+                                      stream)) != hipSuccess))
+    return release(hip_fail(err, "spmv_plan_transpose: transpose"));
+  // A^T as COO sorted by its rows (A's columns); out-of-range columns of A
+  // show up there as out-of-range or unsorted rows
+  spmv_status_t st = spmv_plan_coo(out, N, M, nnz, keys_t, col_t, val_t, dtype, options, stream);
+  if (st != SPMV_SUCCESS) return release(st);
+  (*out)->owned_entries = owned;
+  return release(SPMV_SUCCESS);
+}
+
+spmv_status_t spmv_plan_csc(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                            const int32_t* col_ptr, const int32_t* row_idx, const void* values,
+                            spmv_dtype_t dtype, const spmv_plan_options_t* options,
+                            hipStream_t stream) {
+  // the CSC arrays of A (M x N) are the CSR arrays of A^T (N x M)
+  return spmv_plan_transpose(out, N, M, nnz, col_ptr, row_idx, values, dtype, options, stream);
+}
+
 spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink, hipStream_t stream) {
   if (!data || !sink || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(data) & 15) ||
       (reinterpret_cast<uintptr_t>(sink) & 3))
@@ -659,8 +754,9 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
   }
   p->magic = 0;
   hipError_t err = hipFree(p->ws);
-  if (p->owned_row_ptr) {
-    const hipError_t e2 = hipFree(p->owned_row_ptr);
+  for (void* q : {p->owned_row_ptr, p->owned_entries}) {
+    if (!q) continue;
+    const hipError_t e2 = hipFree(q);
     if (err == hipSuccess) err = e2;
   }
   delete p;

@@ -78,6 +78,18 @@ hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
 // index is outside [0, M) or out of order (flag zeroed by the caller).
 hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, int32_t* row_ptr,
                               int32_t* flag, hipStream_t s);
+// *flag |= 1 unless row_ptr is a valid CSR row pointer array for nnz entries.
+hipError_t launch_csr_check(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t* flag,
+                            hipStream_t s);
+// col_t[t] = row of A holding entry perm[t]; val_t[t] = values[perm[t]].
+hipError_t launch_transpose_gather(const int32_t* row_ptr, int64_t M, const int32_t* perm,
+                                   const void* values, int vbytes, int64_t nnz, int32_t* col_t,
+                                   void* val_t, hipStream_t s);
+// Stable sort of nnz column indices (keys < 2^bits) carrying their entry
+// positions: keys_out sorted, perm_out[t] = position of the t-th key.
+// temp == nullptr: *temp_bytes receives the scratch size needed.
+hipError_t sort_columns(void* temp, size_t* temp_bytes, const int32_t* keys, int32_t* keys_out,
+                        int32_t* perm_out, int64_t nnz, int bits, hipStream_t s);
 // Per group of `group` consecutive partitions: up to kWinIntervals
 // chunk-aligned column intervals covering the group's quads within
 // cap_bytes (kWinTable int32 per group, win_span holds win_span_ints);

@@ -423,6 +423,40 @@ __global__ __launch_bounds__(kBlock) void coo_check_kernel(const int32_t* __rest
   if (__ballot(bad) != 0 && lane_id() == 0) atomicOr(flag, 1);
 }
 
+// flag |= 1 unless row_ptr[0] = 0, row_ptr[M] = nnz and row_ptr never
+// decreases
+__global__ __launch_bounds__(kBlock) void csr_check_kernel(const int32_t* __restrict__ row_ptr,
+                                                           int64_t M, int64_t nnz, int32_t* flag) {
+  bool bad = false;
+  for (int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x; r <= M;
+       r += (int64_t)gridDim.x * kBlock) {
+    const int32_t v = row_ptr[r];
+    bad |= (r == 0 && v != 0) || (r == M && v != nnz) || (r < M && row_ptr[r + 1] < v);
+  }
+  if (__ballot(bad) != 0 && lane_id() == 0) atomicOr(flag, 1);
+}
+
+// Entries of A^T in column order of A: entry t of the sorted order is A's
+// entry perm[t]; its column in A^T is the row of A holding it (the last row
+// whose start is <= the entry), its value is copied.
+template <typename V>
+__global__ __launch_bounds__(kBlock) void transpose_gather_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t M, const int32_t* __restrict__ perm,
+    const V* __restrict__ values, int64_t nnz, int32_t* __restrict__ col_t, V* __restrict__ val_t) {
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < nnz;
+       t += (int64_t)gridDim.x * kBlock) {
+    const int32_t e = perm[t];
+    int lo = 0, hi = M;   // last row r with row_ptr[r] <= e
+    while (lo < hi) {
+      const int mid = (int)(((int64_t)lo + hi + 1) >> 1);
+      if (row_ptr[mid] <= e) lo = mid;
+      else hi = mid - 1;
+    }
+    col_t[t] = lo;
+    val_t[t] = values[e];
+  }
+}
+
 int n_blocks(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
 
 }  // namespace
@@ -499,6 +533,29 @@ hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, in
   }
   hipLaunchKernelGGL(coo_row_ptr_kernel, dim3(n_blocks(M + 1, kBlock)), dim3(kBlock), 0, s,
                      row_idx, (int32_t)nnz, (int32_t)M, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr_check(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t* flag,
+                            hipStream_t s) {
+  const int blocks = (int)std::min<int64_t>(n_blocks(M + 1, kBlock), 8192);
+  hipLaunchKernelGGL(csr_check_kernel, dim3(blocks), dim3(kBlock), 0, s, row_ptr, M, nnz, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_gather(const int32_t* row_ptr, int64_t M, const int32_t* perm,
+                                   const void* values, int vbytes, int64_t nnz, int32_t* col_t,
+                                   void* val_t, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>(n_blocks(nnz, kBlock), 65536);
+  if (vbytes == 4)
+    hipLaunchKernelGGL(transpose_gather_kernel<float>, dim3(blocks), dim3(kBlock), 0, s, row_ptr,
+                       (int32_t)M, perm, static_cast<const float*>(values), nnz, col_t,
+                       static_cast<float*>(val_t));
+  else
+    hipLaunchKernelGGL(transpose_gather_kernel<double>, dim3(blocks), dim3(kBlock), 0, s,
+                       row_ptr, (int32_t)M, perm, static_cast<const double*>(values), nnz,
+                       col_t, static_cast<double*>(val_t));
   return hipGetLastError();
 }
 
