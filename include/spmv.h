@@ -87,8 +87,8 @@ typedef struct spmv_plan_options {
                                  T = 64 * items_per_thread items per wavefront.
                                  0: env SPMV_ITEMS_PER_THREAD, else chosen from
                                  the row lengths: 4 when every row has <= 32
-                                 entries and the mean is < 12, 8 when every row
-                                 has <= 64, otherwise 16 (fp32) or 8 (fp64) */
+                                 entries and the mean is < 12, otherwise 16
+                                 (fp32) or 8 (fp64) */
   int32_t n_bins;             /* 1..SPMV_MAX_BINS; 0 = default bins */
   int32_t validate_columns;   /* 1: also check 0 <= col_idx < N at plan time
                                  (one pass over col_idx); env SPMV_VALIDATE=1 */

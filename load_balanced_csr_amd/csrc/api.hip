@@ -454,8 +454,9 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     return bail(hip_fail(err, "plan: bin scatter"));
   if (auto_ipt) {
     // row lengths decide T: short rows (every row <= 32, mean < 12) take
-    // T = 256, rows up to 64 take T = 512 (both then use the stream
-    // reduction); longer rows take the walk with T = 1024 (fp32) or 512
+    // T = 256; otherwise T = 1024 for fp32 (stream reduction up to rows of
+    // 128, walk beyond) and T = 512 for fp64 (its staging and window need
+    // twice the LDS per unit)
     if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
                               stream)) != hipSuccess ||
         (err = hipStreamSynchronize(stream)) != hipSuccess)
@@ -464,7 +465,6 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
       const int64_t max_len = host_stats[kStatMaxLen];
       const double avg = M > 0 ? (double)nnz / (double)M : 0.0;
       if (max_len <= 32 && avg < 12.0) p->ipt = 4;
-      else if (max_len <= 64) p->ipt = 8;
       else p->ipt = dtype == SPMV_F32 ? 16 : 8;
       p->T = kWave * p->ipt;
       p->P = (W + p->T - 1) / p->T;
