@@ -63,6 +63,8 @@ class OracleLib:
             f = getattr(lib, name)
             f.argtypes = [i64, i64, p, p, p, p, d, d, p, p, p]
             f.restype = ctypes.c_int
+        lib.oracle_rgcsr_stored.argtypes = [i64, p, i64]
+        lib.oracle_rgcsr_stored.restype = i64
         lib.oracle_merge_splits.argtypes = [i64, i64, p, i64, p, p]
         lib.oracle_merge_splits.restype = i64
         lib.oracle_bins.argtypes = [i64, p, i32, p, p, p, p]
@@ -182,6 +184,11 @@ class OracleLib:
         assert rc == 0
         return ref, scale
 
+    def rgcsr_stored(self, row_ptr, G: int) -> int:
+        """Entries a row-grouped CSR layout with groups of G rows stores."""
+        rp = _c(row_ptr, np.int32)
+        return int(self.lib.oracle_rgcsr_stored(rp.size - 1, _ptr(rp), int(G)))
+
     def merge_splits(self, row_ptr, T: int) -> Tuple[np.ndarray, np.ndarray]:
         """Merge-path split coordinates (rows ended, nonzeros consumed) at
         every multiple of T items and at the end, by walking the items."""
@@ -246,6 +253,10 @@ def spmv_coo(*args, **kw):
 
 def spmv_t(*args, **kw):
     return _default().spmv_t(*args, **kw)
+
+
+def rgcsr_stored(*args, **kw):
+    return _default().rgcsr_stored(*args, **kw)
 
 
 def merge_splits(*args, **kw):

@@ -56,6 +56,13 @@
  *      tests/pins.py: dense brute force of A^T x, the adjoint identity
  *      z . (A x) = x . (A^T z) on small integers, a symmetric matrix.
  *
+ *  oracle_rgcsr_stored:
+ *      entries the row-grouped CSR layout stores (arXiv 1012.2270,
+ *      Section 4): rows in groups of G consecutive rows, each group as wide
+ *      as its longest row, so width x (rows in the group), summed. Pinned by
+ *      the page's worked example (7 artificial zeros with groups of four;
+ *      11 for ELLPACK, one group of all rows) and brute force.
+ *
  *  oracle_merge_splits:
  *      merge-path partition, PPoPP'23 page, Section 5.2.1: every nonzero and
  *      every row counts as one unit of work; units are split evenly. Written
@@ -256,6 +263,22 @@ int oracle_spmv_t_f64(int64_t M, int64_t N, const int32_t* row_ptr, const int32_
   for (int64_t j = 0; j < N; ++j)
     ref[j] = alpha * ref[j] + (beta != 0.0 ? beta * y_old[j] : 0.0);
   return 0;
+}
+
+/* ---- row-grouped CSR: stored entries ---------------------------------------- */
+
+int64_t oracle_rgcsr_stored(int64_t M, const int32_t* row_ptr, int64_t G) {
+  int64_t stored = 0;
+  for (int64_t g0 = 0; g0 < M; g0 += G) {
+    int64_t g1 = g0 + G < M ? g0 + G : M;
+    int64_t width = 0;
+    for (int64_t i = g0; i < g1; ++i) {
+      int64_t L = row_ptr[i + 1] - row_ptr[i];
+      if (L > width) width = L;
+    }
+    stored += width * (g1 - g0);
+  }
+  return stored;
 }
 
 /* The same definition evaluated only on the rows listed in rows[0..n). */

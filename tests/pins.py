@@ -409,7 +409,26 @@ def pin_transposed(o):
     assert np.array_equal(o.spmv_t(81, rp, col, val, xx)[0], o.spmv(rp, col, val, xx)[0])
 
 
+def pin_rgcsr_stored(o):
+    """The worked example: groups of four rows store 7 artificial zeros
+    beside the 13 entries, one group of all eight rows (ELLPACK) 11; random
+    row lengths against a numpy reshape-and-max."""
+    g = read_golden("rgcsr_worked_example.txt")
+    rp = np.array(g["row_ptr"], dtype=np.int32)
+    nnz = int(g["nnz"][0])
+    assert o.rgcsr_stored(rp, int(g["rgcsr_group_size"][0])) - nnz == int(g["rgcsr_artificial_zeros"][0])
+    assert o.rgcsr_stored(rp, 8) - nnz == int(g["ellpack_artificial_zeros"][0])
+    rng = np.random.default_rng(23)
+    for G in (1, 3, 4, 64, 100):
+        L = rng.integers(0, 50, 1000)
+        rp = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        pad = (-L.size) % G
+        Lp = np.concatenate([L, np.full(pad, -1)]).reshape(-1, G)
+        rows = np.concatenate([np.full(Lp.shape[0] - 1, G), [G - pad]])
+        assert o.rgcsr_stored(rp, G) == int((Lp.max(1) * rows).sum()), ("rgcsr stored", G)
+
+
 ALL_PINS = [pin_dense_bruteforce, pin_identity, pin_diagonal, pin_integer_row_sums,
             pin_laplacian_closed_forms, pin_alpha_beta, pin_scale, pin_rows_subset,
             pin_merge_splits, pin_bins, pin_spmm_dense, pin_spmm_identity_and_laplacian,
-            pin_spmm_alpha_beta, pin_coo, pin_transposed]
+            pin_spmm_alpha_beta, pin_coo, pin_transposed, pin_rgcsr_stored]

@@ -46,6 +46,8 @@ MUTANTS = [
      "double p = (double)values[e] * (double)x[j];"),
     ("transposed: sum into the row", "      double p = values[e] * x[i];\n      ref[j] = ref[j] + p;",
      "      double p = values[e] * x[i];\n      ref[i % N] = ref[i % N] + p;"),
+    ("rgcsr width from the first row", "      if (L > width) width = L;", "      if (i == g0) width = L;"),
+    ("rgcsr full groups only", "    stored += width * (g1 - g0);", "    stored += width * G;"),
     ("bins reversed order", "bins[fill[b]] = (int32_t)r;", "bins[offsets[b + 1] - 1 - (fill[b] - offsets[b])] = (int32_t)r;"),
 ]
 
