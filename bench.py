@@ -342,7 +342,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="laplacian", choices=list(WORKLOADS))
-    ap.add_argument("--strategy", default="auto", choices=["auto", "merge", "binned"])
+    ap.add_argument("--strategy", default="auto", choices=["auto", "merge", "binned", "rgcsr"])
+    ap.add_argument("--rg-group", type=int, default=0,
+                    help="rows per group of the row-grouped CSR copy (--strategy rgcsr; 0 = 64)")
     ap.add_argument("--items-per-thread", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -389,7 +391,12 @@ def main():
 
     # planning cost (separate from the steps): median of 5 plan/destroy cycles
     popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread)
-    if args.format == "coo":
+    if args.strategy == "rgcsr":
+        assert args.format == "csr", "the row-grouped copy is built from CSR"
+
+        def make_plan():
+            return lb.Plan.rgcsr(rp, col, val, (w.M, w.N), group_rows=args.rg_group)
+    elif args.format == "coo":
         rows = torch.from_numpy(np.repeat(np.arange(w.M, dtype=np.int32),
                                           np.diff(w.row_ptr))).to(dev)
 
@@ -483,6 +490,8 @@ def main():
     gbps_exec = Bc / (mean_exec * 1e-3) / 1e9
     if info["strategy"] == "binned":
         kernel = "binned_spmv_kernel"
+    elif info["strategy"] == "rgcsr":
+        kernel = "rg_spmv_kernel"
     else:
         kernel = "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
     achieved = Bc / (mean_kern * 1e-3) / 1e9
@@ -528,6 +537,15 @@ def main():
         "plan_ms": round(statistics.median(plan_ms), 3),
         "kernel_source_hash": kernel_source_hash(),
     }
+    if info["strategy"] == "rgcsr":
+        s_ = w.values.dtype.itemsize
+        G = info["rgcsr_group"]
+        out["config"]["rgcsr_group"] = G
+        out["rgcsr_stored"] = info["rgcsr_stored"]
+        # bytes the row-grouped layout itself moves: padded entries, row
+        # lengths, group bases, x and y (the metric keeps the CSR bytes)
+        out["format_bytes"] = (info["rgcsr_stored"] * (4 + s_) + 4 * w.M + 8 * (w.M // G + 2)
+                               + (w.N + w.M) * s_ + (w.M * s_ if w.beta != 0.0 else 0))
     plan.destroy()
     ok = True
     if not args.no_cpu:

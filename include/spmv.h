@@ -70,7 +70,8 @@ typedef enum spmv_dtype { SPMV_F32 = 0, SPMV_F64 = 1 } spmv_dtype_t;
 typedef enum spmv_strategy {
   SPMV_STRATEGY_AUTO = 0,
   SPMV_STRATEGY_MERGE = 1,
-  SPMV_STRATEGY_BINNED = 2
+  SPMV_STRATEGY_BINNED = 2,
+  SPMV_STRATEGY_RGCSR = 3     /* row-grouped CSR copy (spmv_plan_rgcsr only) */
 } spmv_strategy_t;
 
 #define SPMV_MAX_BINS 8
@@ -139,6 +140,10 @@ typedef struct spmv_plan_info {
   int64_t max_row_len;
   int64_t n_empty_rows;
   int64_t workspace_bytes;    /* size of the plan's single device allocation */
+  int32_t rgcsr_group;        /* rows per group of the row-grouped copy (0: none) */
+  int32_t pad1;
+  int64_t rgcsr_stored;       /* entries that copy stores for existing rows
+                                 (group width x rows, summed): nnz + padding */
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).
@@ -233,6 +238,27 @@ SPMV_API spmv_status_t spmv_plan_csc(spmv_plan_t* out, int64_t M, int64_t N, int
                                      const void* values, spmv_dtype_t dtype,
                                      const spmv_plan_options_t* options, hipStream_t stream);
 
+/* spmv_plan_ex, then a row-grouped CSR copy of A that spmv_exec uses
+ * ("New Row-grouped CSR format for storing the sparse matrices on GPU with
+ * implementation in CUDA", arXiv 1012.2270, Section 4): rows in groups of
+ * group_rows consecutive rows; inside a group, entry k of the group's row i
+ * is stored at groupPointers[group] + k * group_rows + i, to the width of
+ * the group's longest row (shorter rows padded with value 0), with the row
+ * lengths beside. One lane per row, the group's lanes reading consecutive
+ * addresses.
+ *
+ * group_rows  1..1024; 0 = 64 (one wavefront).
+ * The copy is taken here: later changes to values do not reach spmv_exec
+ * while the plan's strategy is SPMV_STRATEGY_RGCSR (spmv_plan_set_strategy
+ * may switch it to MERGE or BINNED, which read the borrowed arrays, and
+ * back). It is kept in one more device allocation of about
+ * rgcsr_stored * (4 + value size) bytes (spmv_plan_info), freed by
+ * spmv_destroy. spmv_exec_multi uses the merge-path partitions as always. */
+SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                                       const int32_t* row_ptr, const int32_t* col_idx,
+                                       const void* values, spmv_dtype_t dtype,
+                                       int32_t group_rows, hipStream_t stream);
+
 /* y = alpha * A * x + beta * y.
  *
  * x  device array of N elements of the plan's dtype.
@@ -296,7 +322,8 @@ SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const
  * as long as its memory has not been reused. */
 SPMV_API spmv_status_t spmv_destroy(spmv_plan_t plan);
 
-/* Switch a live plan between MERGE and BINNED (both are always built). */
+/* Switch a live plan between MERGE and BINNED (both are always built), or to
+ * RGCSR when the plan has the row-grouped copy (spmv_plan_rgcsr). */
 SPMV_API spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
 
 /* Fill *info (host struct). */

@@ -21,12 +21,12 @@ SPMV_SUCCESS = 0
 STATUS_NAMES = {0: "SUCCESS", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALLOC", 4: "HIP",
                 5: "INVALID_PLAN", 6: "INVALID_MATRIX"}
 SPMV_F32, SPMV_F64 = 0, 1
-STRATEGY = {"auto": 0, "merge": 1, "binned": 2}
+STRATEGY = {"auto": 0, "merge": 1, "binned": 2, "rgcsr": 3}
 STRATEGY_NAME = {v: k for k, v in STRATEGY.items()}
 MAX_BINS = 8
 
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
-            "spmv_plan_csc", "spmv_exec", "spmv_exec_events", "spmv_destroy",
+            "spmv_plan_csc", "spmv_plan_rgcsr", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
@@ -58,7 +58,9 @@ class PlanInfo(ctypes.Structure):
                 ("bin_identity", ctypes.c_int32), ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
                 ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
-                ("n_empty_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("n_empty_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("rgcsr_group", ctypes.c_int32), ("pad1", ctypes.c_int32),
+                ("rgcsr_stored", ctypes.c_int64)]
 
 
 _lib = None
@@ -83,6 +85,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_coo.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
     lib.spmv_plan_transpose.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
     lib.spmv_plan_csc.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, p, p]
+    lib.spmv_plan_rgcsr.argtypes = [ctypes.POINTER(p), i64, i64, i64, p, p, p, i32, i32, p]
     lib.spmv_exec.argtypes = [p, p, p, d, d, p]
     lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
     lib.spmv_destroy.argtypes = [p]
@@ -225,6 +228,21 @@ def spmv_plan_csc(col_ptr, row_idx, values, M: int, N: int,
     return _plan_other("spmv_plan_csc", col_ptr, row_idx, values, M, N, options, stream)
 
 
+def spmv_plan_rgcsr(row_ptr, col_idx, values, M: int, N: int, group_rows: int = 0,
+                    stream=None) -> int:
+    """Plan whose spmv_exec runs on a row-grouped CSR copy of A (groups of
+    group_rows rows, 0 = 64); the copy is taken here."""
+    lib = load()
+    h = ctypes.c_void_p()
+    _check(lib.spmv_plan_rgcsr(ctypes.byref(h), M, N, int(col_idx.numel()),
+                               _dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
+                               _dev_ptr(col_idx, "col_idx", (torch.int32,)),
+                               _dev_ptr(values, "values", (torch.float32, torch.float64)),
+                               _dtype_code(values), int(group_rows), _stream(stream)),
+           "spmv_plan_rgcsr")
+    return h.value
+
+
 def spmv_exec(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
               beta: float = 0.0, stream=None) -> None:
     """y = alpha * A x + beta * y, enqueued on the stream (asynchronous)."""
@@ -311,7 +329,8 @@ def spmv_plan_info(plan: int) -> dict:
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
-            "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes}
+            "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes,
+            "rgcsr_group": info.rgcsr_group, "rgcsr_stored": info.rgcsr_stored}
 
 
 def spmv_plan_copy_splits(plan: int):
@@ -391,6 +410,17 @@ class Plan:
         self._keep = ()
         o = make_options(**opts) if opts else None
         self.handle = spmv_plan_csc(col_ptr, row_idx, values, self.M, self.N, o, stream)
+        return self
+
+    @classmethod
+    def rgcsr(cls, row_ptr, col_idx, values, shape, group_rows: int = 0, stream=None):
+        """Plan running on a row-grouped CSR copy of A (groups of group_rows
+        rows, 0 = 64)."""
+        self = cls.__new__(cls)
+        self.M, self.N = int(shape[0]), int(shape[1])
+        self._keep = (row_ptr, col_idx, values)
+        self.handle = spmv_plan_rgcsr(row_ptr, col_idx, values, self.M, self.N, group_rows,
+                                      stream)
         return self
 
     def __call__(self, x, y, alpha: float = 1.0, beta: float = 0.0, stream=None):

@@ -94,6 +94,15 @@ struct spmv_plan_st {
   int32_t* win_span;
   void* owned_row_ptr;   // COO plans: the row offsets derived from row_idx
   void* owned_entries;   // transposed plans: the column indices and values of A^T
+  // row-grouped copy (spmv_plan_rgcsr): metadata and entries, own allocations
+  void* owned_rg_meta;
+  void* owned_rg_data;
+  int32_t rg_group;
+  int64_t rg_stored;
+  const int32_t* rg_rl;
+  const int64_t* rg_base;
+  const int32_t* rg_col;
+  const void* rg_val;
 };
 
 namespace {
@@ -180,7 +189,22 @@ template <typename V>
 spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, double beta,
                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t err = hipSuccess;
-  if (p->strategy == SPMV_STRATEGY_MERGE) {
+  if (p->strategy == SPMV_STRATEGY_RGCSR) {
+    RgArgs<V> a;
+    std::memset(&a, 0, sizeof a);
+    a.rl = p->rg_rl;
+    a.base = p->rg_base;
+    a.col = p->rg_col;
+    a.val = static_cast<const V*>(p->rg_val);
+    a.x = static_cast<const V*>(x);
+    a.y = static_cast<V*>(y);
+    a.alpha = (V)alpha;
+    a.beta = (V)beta;
+    a.beta_nonzero = beta != 0.0;
+    a.M = (int32_t)p->M;
+    a.G = p->rg_group;
+    err = launch_rg_spmv<V>(a, stream, ev0, ev1);
+  } else if (p->strategy == SPMV_STRATEGY_MERGE) {
     MergeArgs<V> a;
     a.row_ptr = p->row_ptr;
     a.col_idx = p->col_idx;
@@ -715,6 +739,75 @@ spmv_status_t spmv_plan_csc(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   return spmv_plan_transpose(out, N, M, nnz, col_ptr, row_idx, values, dtype, options, stream);
 }
 
+spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                              const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                              spmv_dtype_t dtype, int32_t group_rows, hipStream_t stream) {
+  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (group_rows < 0 || group_rows > 1024)
+    return fail(SPMV_ERR_INVALID_ARG, "group_rows = %d outside 0..1024", group_rows);
+  const int32_t G = group_rows ? group_rows : kWave;
+  spmv_status_t st = spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, nullptr,
+                                  stream);
+  if (st != SPMV_SUCCESS) return st;
+  spmv_plan_st* p = *out;
+  auto undo = [&](spmv_status_t s2) {
+    (void)hipStreamSynchronize(stream);
+    (void)spmv_destroy(p);
+    *out = nullptr;
+    return s2;
+  };
+  const int64_t ngroups = (M + G - 1) / G;
+  // metadata: group widths, group bases (+1), row lengths, the stored count
+  const size_t o_base = align256(sizeof(int32_t) * (size_t)ngroups);
+  const size_t o_rl = o_base + align256(sizeof(int64_t) * (size_t)(ngroups + 1));
+  const size_t o_cnt = o_rl + align256(sizeof(int32_t) * (size_t)M);
+  hipError_t err = hipMalloc(&p->owned_rg_meta, o_cnt + 256);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    p->owned_rg_meta = nullptr;
+    return undo(fail(SPMV_ERR_ALLOC, "hipMalloc for the row-grouped metadata failed"));
+  }
+  char* meta = static_cast<char*>(p->owned_rg_meta);
+  int32_t* gw = reinterpret_cast<int32_t*>(meta);
+  int64_t* base = reinterpret_cast<int64_t*>(meta + o_base);
+  int32_t* rl = reinterpret_cast<int32_t*>(meta + o_rl);
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(meta + o_cnt);
+  int64_t host[2] = {0, 0};   // total slots, stored entries
+  if (M > 0 &&
+      ((err = hipMemsetAsync(cnt, 0, sizeof *cnt, stream)) != hipSuccess ||
+       (err = launch_rg_widths(row_ptr, M, G, gw, base, cnt, stream)) != hipSuccess ||
+       (err = hipMemcpyAsync(&host[0], base + ngroups, sizeof(int64_t), hipMemcpyDeviceToHost,
+                             stream)) != hipSuccess ||
+       (err = hipMemcpyAsync(&host[1], cnt, sizeof(int64_t), hipMemcpyDeviceToHost, stream)) !=
+           hipSuccess ||
+       (err = hipStreamSynchronize(stream)) != hipSuccess))
+    return undo(hip_fail(err, "spmv_plan_rgcsr: widths"));
+  const size_t vs = dtype == SPMV_F32 ? 4 : 8;
+  const size_t o_val = align256(sizeof(int32_t) * (size_t)host[0]);
+  if ((err = hipMalloc(&p->owned_rg_data, o_val + align256(vs * (size_t)host[0]) + 256)) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    p->owned_rg_data = nullptr;
+    return undo(fail(SPMV_ERR_ALLOC, "hipMalloc of %lld row-grouped slots failed",
+                     (long long)host[0]));
+  }
+  int32_t* col_rg = static_cast<int32_t*>(p->owned_rg_data);
+  void* val_rg = static_cast<char*>(p->owned_rg_data) + o_val;
+  if ((err = launch_rg_build(row_ptr, col_idx, values, (int)vs, M, G, gw, base, rl, col_rg,
+                             val_rg, stream)) != hipSuccess ||
+      (err = hipStreamSynchronize(stream)) != hipSuccess)
+    return undo(hip_fail(err, "spmv_plan_rgcsr: copy"));
+  p->rg_group = G;
+  p->rg_stored = host[1];
+  p->rg_rl = rl;
+  p->rg_base = base;
+  p->rg_col = col_rg;
+  p->rg_val = val_rg;
+  p->strategy = SPMV_STRATEGY_RGCSR;
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink, hipStream_t stream) {
   if (!data || !sink || bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(data) & 15) ||
       (reinterpret_cast<uintptr_t>(sink) & 3))
@@ -754,7 +847,7 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
   }
   p->magic = 0;
   hipError_t err = hipFree(p->ws);
-  for (void* q : {p->owned_row_ptr, p->owned_entries}) {
+  for (void* q : {p->owned_row_ptr, p->owned_entries, p->owned_rg_meta, p->owned_rg_data}) {
     if (!q) continue;
     const hipError_t e2 = hipFree(q);
     if (err == hipSuccess) err = e2;
@@ -770,6 +863,10 @@ spmv_status_t spmv_plan_set_strategy(spmv_plan_t p, spmv_strategy_t strategy) {
   if (strategy == SPMV_STRATEGY_AUTO) p->strategy = choose_strategy(p);
   else if (strategy == SPMV_STRATEGY_MERGE || strategy == SPMV_STRATEGY_BINNED)
     p->strategy = strategy;
+  else if (strategy == SPMV_STRATEGY_RGCSR && p->rg_group > 0)
+    p->strategy = strategy;
+  else if (strategy == SPMV_STRATEGY_RGCSR)
+    return fail(SPMV_ERR_INVALID_ARG, "the plan has no row-grouped copy (spmv_plan_rgcsr)");
   else return fail(SPMV_ERR_INVALID_ARG, "unknown strategy %d", (int)strategy);
   return SPMV_SUCCESS;
 }
@@ -788,6 +885,8 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->items_per_wave = p->T;
   info->n_partitions = p->P;
   info->merge_reduce = p->merge_reduce;
+  info->rgcsr_group = p->rg_group;
+  info->rgcsr_stored = p->rg_stored;
   info->stream_lanes = p->stream_lanes;
   info->x_window = p->x_window;
   info->n_bins = p->edges.n_bins;

@@ -175,6 +175,32 @@ size_t spmm_lds_bytes(int vbytes, int T);
 template <typename V>
 hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s);
 
+// ---- row-grouped CSR --------------------------------------------------------------
+template <typename V>
+struct RgArgs {
+  const int32_t* rl;       // entries per row
+  const int64_t* base;     // first slot of each group
+  const int32_t* col;      // column-interleaved column indices
+  const V* val;            // and values
+  const V* x;
+  V* y;
+  V alpha;
+  V beta;
+  int32_t beta_nonzero;
+  int32_t M;
+  int32_t G;               // rows per group
+};
+// group widths gw[ceil(M/G)], group bases base[ngroups + 1] (the last the
+// total slots) and *stored += sum of width x rows over groups
+hipError_t launch_rg_widths(const int32_t* row_ptr, int64_t M, int32_t G, int32_t* gw,
+                            int64_t* base, unsigned long long* stored, hipStream_t s);
+// row lengths and the column-interleaved copy of col_idx / values
+hipError_t launch_rg_build(const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                           int vbytes, int64_t M, int32_t G, int32_t* gw, int64_t* base,
+                           int32_t* rl, int32_t* col_rg, void* val_rg, hipStream_t s);
+template <typename V>
+hipError_t launch_rg_spmv(const RgArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
 // ---- binned exec ----------------------------------------------------------------
 struct BinLaunch {
   int32_t block_begin;   // first workgroup of this bin in the fused grid
