@@ -342,7 +342,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="laplacian", choices=list(WORKLOADS))
-    ap.add_argument("--strategy", default="auto", choices=["auto", "merge", "binned", "rgcsr"])
+    ap.add_argument("--strategy", default="auto",
+                    choices=["auto", "merge", "binned", "rgcsr", "group"])
     ap.add_argument("--rg-group", type=int, default=0,
                     help="rows per group of the row-grouped CSR copy (--strategy rgcsr; 0 = 64)")
     ap.add_argument("--items-per-thread", type=int, default=0)
@@ -492,6 +493,8 @@ def main():
         kernel = "binned_spmv_kernel"
     elif info["strategy"] == "rgcsr":
         kernel = "rg_spmv_kernel"
+    elif info["strategy"] == "group":
+        kernel = "group_spmv_kernel"
     else:
         kernel = "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
     achieved = Bc / (mean_kern * 1e-3) / 1e9

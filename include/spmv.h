@@ -66,12 +66,21 @@ typedef enum spmv_dtype { SPMV_F32 = 0, SPMV_F64 = 1 } spmv_dtype_t;
  *  BINNED: rows grouped into row-length bins (OpSparse, Sec. 5.1); each bin
  *          runs a thread-, lane-group-, wavefront- or workgroup-per-row variant
  *          (PPoPP'23 page, Secs. 4.2 and 5.2.2), longest bins dispatched first.
- *  AUTO  : the planner picks one of the two from the row-length statistics. */
+ *  AUTO  : the planner picks MERGE or BINNED from the matrix size and row
+ *          lengths (a switch fitted on MI355X: BINNED below 3,000,000
+ *          nonzeros when some row is longer than T/8, below 200,000 when
+ *          none is; MERGE above). */
 typedef enum spmv_strategy {
   SPMV_STRATEGY_AUTO = 0,
   SPMV_STRATEGY_MERGE = 1,
   SPMV_STRATEGY_BINNED = 2,
-  SPMV_STRATEGY_RGCSR = 3     /* row-grouped CSR copy (spmv_plan_rgcsr only) */
+  SPMV_STRATEGY_RGCSR = 3,    /* row-grouped CSR copy (spmv_plan_rgcsr only) */
+  SPMV_STRATEGY_GROUP = 4     /* group-mapped (PPoPP'23 page, Sec. 5.2.3): a
+                                 workgroup of 1, 2 or 4 wavefronts takes an
+                                 equal share of rows; its threads take the
+                                 share's nonzeros in turn, each finding its
+                                 row by a binary search in the rows' prefix
+                                 sum (spmv_plan_set_group) */
 } spmv_strategy_t;
 
 #define SPMV_MAX_BINS 8
@@ -144,6 +153,8 @@ typedef struct spmv_plan_info {
   int32_t pad1;
   int64_t rgcsr_stored;       /* entries that copy stores for existing rows
                                  (group width x rows, summed): nnz + padding */
+  int32_t group_waves;        /* group-mapped schedule: wavefronts per group */
+  int32_t group_rows;         /* ... and rows per group */
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).
@@ -325,6 +336,14 @@ SPMV_API spmv_status_t spmv_destroy(spmv_plan_t plan);
 /* Switch a live plan between MERGE and BINNED (both are always built), or to
  * RGCSR when the plan has the row-grouped copy (spmv_plan_rgcsr). */
 SPMV_API spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
+
+/* Select the group-mapped schedule (SPMV_STRATEGY_GROUP) for a live plan:
+ * group_waves 1, 2 or 4 wavefronts per group (0 = 4), rows_per_group
+ * 1..256 * group_waves (0 = 512 * group_waves nonzeros' worth of rows at the
+ * mean row length). Results do not depend on either. SPMV_ERR_INVALID_ARG
+ * outside those ranges. */
+SPMV_API spmv_status_t spmv_plan_set_group(spmv_plan_t plan, int32_t group_waves,
+                                           int32_t rows_per_group);
 
 /* Fill *info (host struct). */
 SPMV_API spmv_status_t spmv_plan_info(spmv_plan_t plan, spmv_plan_info_t* info);

@@ -21,13 +21,14 @@ SPMV_SUCCESS = 0
 STATUS_NAMES = {0: "SUCCESS", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALLOC", 4: "HIP",
                 5: "INVALID_PLAN", 6: "INVALID_MATRIX"}
 SPMV_F32, SPMV_F64 = 0, 1
-STRATEGY = {"auto": 0, "merge": 1, "binned": 2, "rgcsr": 3}
+STRATEGY = {"auto": 0, "merge": 1, "binned": 2, "rgcsr": 3, "group": 4}
 STRATEGY_NAME = {v: k for k, v in STRATEGY.items()}
 MAX_BINS = 8
 
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
             "spmv_plan_csc", "spmv_plan_rgcsr", "spmv_exec", "spmv_exec_events", "spmv_destroy",
-            "spmv_plan_set_strategy", "spmv_plan_info", "spmv_plan_copy_splits",
+            "spmv_plan_set_strategy", "spmv_plan_set_group", "spmv_plan_info",
+            "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
             "spmv_last_error")
@@ -60,7 +61,8 @@ class PlanInfo(ctypes.Structure):
                 ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
                 ("n_empty_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("rgcsr_group", ctypes.c_int32), ("pad1", ctypes.c_int32),
-                ("rgcsr_stored", ctypes.c_int64)]
+                ("rgcsr_stored", ctypes.c_int64), ("group_waves", ctypes.c_int32),
+                ("group_rows", ctypes.c_int32)]
 
 
 _lib = None
@@ -90,6 +92,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
     lib.spmv_destroy.argtypes = [p]
     lib.spmv_plan_set_strategy.argtypes = [p, i32]
+    lib.spmv_plan_set_group.argtypes = [p, i32, i32]
     lib.spmv_plan_info.argtypes = [p, ctypes.POINTER(PlanInfo)]
     lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
     lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
@@ -315,6 +318,12 @@ def spmv_plan_set_strategy(plan: int, strategy: str) -> None:
     _check(load().spmv_plan_set_strategy(plan, STRATEGY[strategy]), "spmv_plan_set_strategy")
 
 
+def spmv_plan_set_group(plan: int, group_waves: int = 0, rows_per_group: int = 0) -> None:
+    """Select the group-mapped schedule (0 = defaults)."""
+    _check(load().spmv_plan_set_group(plan, int(group_waves), int(rows_per_group)),
+           "spmv_plan_set_group")
+
+
 def spmv_plan_info(plan: int) -> dict:
     info = PlanInfo()
     _check(load().spmv_plan_info(plan, ctypes.byref(info)), "spmv_plan_info")
@@ -330,7 +339,8 @@ def spmv_plan_info(plan: int) -> dict:
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
             "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes,
-            "rgcsr_group": info.rgcsr_group, "rgcsr_stored": info.rgcsr_stored}
+            "rgcsr_group": info.rgcsr_group, "rgcsr_stored": info.rgcsr_stored,
+            "group_waves": info.group_waves, "group_rows": info.group_rows}
 
 
 def spmv_plan_copy_splits(plan: int):
@@ -443,6 +453,9 @@ class Plan:
 
     def set_strategy(self, strategy: str):
         spmv_plan_set_strategy(self.handle, strategy)
+
+    def set_group(self, group_waves: int = 0, rows_per_group: int = 0):
+        spmv_plan_set_group(self.handle, group_waves, rows_per_group)
 
     @property
     def info(self) -> dict:

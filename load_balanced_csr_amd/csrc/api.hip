@@ -103,6 +103,8 @@ struct spmv_plan_st {
   const int64_t* rg_base;
   const int32_t* rg_col;
   const void* rg_val;
+  int32_t group_waves;    // group-mapped schedule
+  int32_t group_rows;
 };
 
 namespace {
@@ -129,8 +131,8 @@ spmv_status_t check_plan(spmv_plan_t p) {
 
 spmv_status_t check_options(const spmv_plan_options_t* o) {
   if (!o) return SPMV_SUCCESS;
-  if (o->strategy < 0 || o->strategy > SPMV_STRATEGY_BINNED)
-    return fail(SPMV_ERR_INVALID_ARG, "options.strategy %d unknown", o->strategy);
+  if (o->strategy < 0 || o->strategy > SPMV_STRATEGY_GROUP || o->strategy == SPMV_STRATEGY_RGCSR)
+    return fail(SPMV_ERR_INVALID_ARG, "options.strategy %d unknown here", o->strategy);
   if (o->items_per_thread != 0 && o->items_per_thread != 4 && o->items_per_thread != 7 &&
       o->items_per_thread != 8 && o->items_per_thread != 16)
     return fail(SPMV_ERR_INVALID_ARG, "options.items_per_thread must be 4, 7, 8 or 16");
@@ -176,20 +178,53 @@ void build_binned_launch(spmv_plan_st* p) {
   p->binned_blocks = next;
 }
 
-// The schedule used when none is forced. Merge-path is the general case;
-// rows that are all short and of similar length (one bin) run binned.
-int32_t choose_strategy(const spmv_plan_st*) {
+// Rows per group of the group-mapped schedule: one LDS chunk of nonzeros
+// (512 per wavefront) at the mean row length, between 1 and the group's cap.
+int32_t default_group_rows(const spmv_plan_st* p, int waves) {
+  const double avg = p->M > 0 ? (double)p->nnz / (double)p->M : 0.0;
+  const double r = kGroupChunkPerWave * waves / (avg + 1.0);
+  return (int32_t)std::max(1.0, std::min((double)(kGroupRowsPerWave * waves), r));
+}
+
+// The schedule used when none is forced: the analogue, measured on MI355X,
+// of the PPoPP'23 page's size switch (Section 6.2), which leaves merge-path
+// for small matrices. Small matrices are launch-bound, and the binned
+// schedule is one launch while merge-path with the walk reduction is two
+// (main kernel and carry fix-up): binned below kBinnedMaxNnzWalk nonzeros
+// when rows cross partitions, below kBinnedMaxNnzStream when they do not,
+// merge-path above (a sweep of 42 synthetic matrices, 167 to 29M nonzeros,
+// uniform and skewed rows; the group-mapped schedule was never the fastest).
+constexpr int64_t kBinnedMaxNnzWalk = 3000000;
+constexpr int64_t kBinnedMaxNnzStream = 200000;
+
+int32_t choose_strategy(const spmv_plan_st* p) {
   const char* env = std::getenv("SPMV_STRATEGY");
   if (env && !std::strcmp(env, "merge")) return SPMV_STRATEGY_MERGE;
   if (env && !std::strcmp(env, "binned")) return SPMV_STRATEGY_BINNED;
-  return SPMV_STRATEGY_MERGE;
+  if (env && !std::strcmp(env, "group")) return SPMV_STRATEGY_GROUP;
+  const int64_t cap = p->merge_reduce == 2 ? kBinnedMaxNnzStream : kBinnedMaxNnzWalk;
+  return p->nnz < cap ? SPMV_STRATEGY_BINNED : SPMV_STRATEGY_MERGE;
 }
 
 template <typename V>
 spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, double beta,
                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t err = hipSuccess;
-  if (p->strategy == SPMV_STRATEGY_RGCSR) {
+  if (p->strategy == SPMV_STRATEGY_GROUP) {
+    GroupArgs<V> a;
+    std::memset(&a, 0, sizeof a);
+    a.row_ptr = p->row_ptr;
+    a.col_idx = p->col_idx;
+    a.val = static_cast<const V*>(p->values);
+    a.x = static_cast<const V*>(x);
+    a.y = static_cast<V*>(y);
+    a.alpha = (V)alpha;
+    a.beta = (V)beta;
+    a.beta_nonzero = beta != 0.0;
+    a.M = (int32_t)p->M;
+    a.rows_per_group = p->group_rows;
+    err = launch_group<V>(a, p->group_waves, stream, ev0, ev1);
+  } else if (p->strategy == SPMV_STRATEGY_RGCSR) {
     RgArgs<V> a;
     std::memset(&a, 0, sizeof a);
     a.rl = p->rg_rl;
@@ -571,13 +606,15 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     else if (room && xw == 0 && S > 0 && 2 * F1 >= S) p->x_window = 1;
     else if (room && xw == 0 && S > 0 && 2 * FM >= S) p->x_window = kWinIntervals;
   }
+  p->group_waves = 4;
+  p->group_rows = default_group_rows(p, 4);
   p->strategy = forced ? forced : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))
     std::fprintf(stderr,
                  "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d xwin=%d T=%d "
                  "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu\n",
                  (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
-                 p->strategy == SPMV_STRATEGY_MERGE ? "merge" : "binned",
+                 p->strategy == SPMV_STRATEGY_MERGE ? "merge" : p->strategy == SPMV_STRATEGY_GROUP ? "group" : "binned",
                  p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->x_window, p->T,
                  (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
                  p->edges.n_bins, p->identity, p->ws_bytes);
@@ -867,6 +904,8 @@ spmv_status_t spmv_plan_set_strategy(spmv_plan_t p, spmv_strategy_t strategy) {
     p->strategy = strategy;
   else if (strategy == SPMV_STRATEGY_RGCSR)
     return fail(SPMV_ERR_INVALID_ARG, "the plan has no row-grouped copy (spmv_plan_rgcsr)");
+  else if (strategy == SPMV_STRATEGY_GROUP)
+    p->strategy = strategy;
   else return fail(SPMV_ERR_INVALID_ARG, "unknown strategy %d", (int)strategy);
   return SPMV_SUCCESS;
 }
@@ -887,6 +926,8 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->merge_reduce = p->merge_reduce;
   info->rgcsr_group = p->rg_group;
   info->rgcsr_stored = p->rg_stored;
+  info->group_waves = p->group_waves;
+  info->group_rows = p->group_rows;
   info->stream_lanes = p->stream_lanes;
   info->x_window = p->x_window;
   info->n_bins = p->edges.n_bins;
@@ -899,6 +940,21 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->max_row_len = p->max_len;
   info->n_empty_rows = p->n_empty;
   info->workspace_bytes = (int64_t)p->ws_bytes;
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_plan_set_group(spmv_plan_t p, int32_t group_waves, int32_t rows_per_group) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (group_waves != 0 && group_waves != 1 && group_waves != 2 && group_waves != 4)
+    return fail(SPMV_ERR_INVALID_ARG, "group_waves = %d (1, 2 or 4)", group_waves);
+  const int waves = group_waves ? group_waves : 4;
+  if (rows_per_group < 0 || rows_per_group > kGroupRowsPerWave * waves)
+    return fail(SPMV_ERR_INVALID_ARG, "rows_per_group = %d outside 0..%d", rows_per_group,
+                kGroupRowsPerWave * waves);
+  p->group_waves = waves;
+  p->group_rows = rows_per_group ? rows_per_group : default_group_rows(p, waves);
+  p->strategy = SPMV_STRATEGY_GROUP;
   return SPMV_SUCCESS;
 }
 

@@ -175,6 +175,26 @@ size_t spmm_lds_bytes(int vbytes, int T);
 template <typename V>
 hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s);
 
+// ---- group-mapped exec ----------------------------------------------------------------
+constexpr int kGroupRowsPerWave = 256;  // rows (tiles) a group may take, per wavefront
+constexpr int kGroupChunkPerWave = 512; // nonzeros per LDS chunk, per wavefront
+template <typename V>
+struct GroupArgs {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const V* val;
+  const V* x;
+  V* y;
+  V alpha;
+  V beta;
+  int32_t beta_nonzero;
+  int32_t M;
+  int32_t rows_per_group;   // 1..kGroupRowsPerWave * wavefronts per group
+};
+template <typename V>
+hipError_t launch_group(const GroupArgs<V>& a, int group_waves, hipStream_t s, hipEvent_t ev0,
+                        hipEvent_t ev1);
+
 // ---- row-grouped CSR --------------------------------------------------------------
 template <typename V>
 struct RgArgs {
