@@ -279,6 +279,9 @@ def run_spmm(args, w, torch, lb, dev):
                                             Y_first.view(np.uint8)))
     mean_ms = statistics.fmean(ms)
     Bc = spmm_bytes(w, k)
+    # stream plans (partitions own whole rows) run the row-slot kernel, walk
+    # plans the merge-slot kernel followed by the carry fix-up
+    kern = "spmm_rows_kernel" if info["merge_reduce"] == "stream" else "spmm_merge_kernel"
     gbps = Bc / (mean_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC_SPMM,
@@ -296,10 +299,10 @@ def run_spmm(args, w, torch, lb, dev):
         "achieved_GBps": round(gbps, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "compulsory_bytes": Bc,
-        "roofline": {"bound": "hbm", "kernel": "spmm_merge_kernel", "achieved": round(gbps, 2),
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel_ms": round(mean_ms, 5),
-                     "traffic": load_traffic("%s_k%d" % (args.workload, k), "spmm_merge_kernel",
+                     "traffic": load_traffic("%s_k%d" % (args.workload, k), kern,
                                              SPMM_SOURCES),
                      "timed": "events around the exec's launches (main kernel%s)"
                               % ("" if info["merge_reduce"] == "stream" else " + carry fix-up")},
