@@ -350,6 +350,8 @@ def main():
     ap.add_argument("--rg-group", type=int, default=0,
                     help="rows per group of the row-grouped CSR copy (--strategy rgcsr; 0 = 64)")
     ap.add_argument("--items-per-thread", type=int, default=0)
+    ap.add_argument("--bin-streams", type=int, default=0,
+                    help="binned schedule: one launch per bin over N streams (0 = one grid)")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -394,7 +396,8 @@ def main():
     torch.cuda.synchronize()
 
     # planning cost (separate from the steps): median of 5 plan/destroy cycles
-    popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread)
+    popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread,
+                 bin_streams=args.bin_streams)
     if args.strategy == "rgcsr":
         assert args.format == "csr", "the row-grouped copy is built from CSR"
 
@@ -520,6 +523,7 @@ def main():
                    "seed": w.seed, "format": args.format, "strategy": info["strategy"],
                    "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
                    "items_per_wave": info["items_per_wave"],
+                   "bin_streams": info["bin_streams"],
                    "cache": "warm" if flush is None else
                    "flushed before every step (1 GiB fill + 1 GiB cached read)"},
         "achieved_GBps": round(gbps_exec, 2),

@@ -120,7 +120,18 @@ typedef struct spmv_plan_options {
                                  outside them gathers from global x. Auto: on
                                  when at least half the workgroups fit. Needs a
                                  16-byte aligned x at exec time (else off) */
-  int32_t pad0;
+  int32_t bin_streams;        /* binned schedule: 0 = all bins in one grid,
+                                 longest rows first (default; env
+                                 SPMV_BIN_STREAMS). n in 1..SPMV_MAX_BINS: one
+                                 launch per bin, longest first, dealt round
+                                 robin over the caller's stream and n - 1
+                                 streams the plan creates (OpSparse page,
+                                 Sec. 5.1, runs its bins on concurrent
+                                 streams); spmv_exec forks them from the
+                                 caller's stream and joins them back with
+                                 events, so the call stays asynchronous and
+                                 capturable. Same per-row arithmetic, so y is
+                                 bitwise equal to the single-grid result. */
   int64_t bin_max_len[SPMV_MAX_BINS];
                               /* inclusive upper row length of bins 0..n_bins-2,
                                  strictly increasing; the last bin is unbounded */
@@ -140,7 +151,8 @@ typedef struct spmv_plan_info {
   int32_t stream_lanes;
   int32_t x_window;           /* stream kernel's LDS x window: 0 none, 1 one
                                  column interval, 3 up to three */
-  int32_t pad0;
+  int32_t bin_streams;        /* binned exec: streams its per-bin launches use
+                                 (0: one grid for all bins) */
   int32_t n_bins;
   int32_t bin_identity;       /* 1: every row fell in one bin, no row-id array */
   int64_t bin_max_len[SPMV_MAX_BINS];

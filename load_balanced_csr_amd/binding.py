@@ -44,7 +44,7 @@ class PlanOptions(ctypes.Structure):
     _fields_ = [("strategy", ctypes.c_int32), ("items_per_thread", ctypes.c_int32),
                 ("n_bins", ctypes.c_int32), ("validate_columns", ctypes.c_int32),
                 ("merge_reduce", ctypes.c_int32), ("stream_lanes", ctypes.c_int32),
-                ("x_window", ctypes.c_int32), ("pad0", ctypes.c_int32),
+                ("x_window", ctypes.c_int32), ("bin_streams", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS)]
 
@@ -55,7 +55,7 @@ class PlanInfo(ctypes.Structure):
                 ("items_per_thread", ctypes.c_int32), ("items_per_wave", ctypes.c_int32),
                 ("n_partitions", ctypes.c_int64), ("merge_reduce", ctypes.c_int32),
                 ("stream_lanes", ctypes.c_int32), ("x_window", ctypes.c_int32),
-                ("pad0", ctypes.c_int32), ("n_bins", ctypes.c_int32),
+                ("bin_streams", ctypes.c_int32), ("n_bins", ctypes.c_int32),
                 ("bin_identity", ctypes.c_int32), ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
                 ("bin_count", ctypes.c_int64 * MAX_BINS), ("max_row_len", ctypes.c_int64),
@@ -150,8 +150,11 @@ MERGE_REDUCE_NAME = {1: "walk", 2: "stream"}
 
 def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
-                 stream_lanes: int = 0, x_window: str = "auto") -> PlanOptions:
-    """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored."""
+                 stream_lanes: int = 0, x_window: str = "auto",
+                 bin_streams: int = 0) -> PlanOptions:
+    """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored.
+    bin_streams: 0 runs the binned schedule as one grid; n >= 1 launches each
+    bin on its own, dealt over the caller's stream and n - 1 plan streams."""
     o = PlanOptions()
     o.strategy = STRATEGY[strategy]
     o.items_per_thread = items_per_thread
@@ -159,6 +162,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.merge_reduce = MERGE_REDUCE[merge_reduce]
     o.stream_lanes = stream_lanes
     o.x_window = {"auto": 0, "off": 1, "on": 2}[x_window]
+    o.bin_streams = bin_streams
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -334,7 +338,7 @@ def spmv_plan_info(plan: int) -> dict:
             "items_per_wave": info.items_per_wave, "n_partitions": info.n_partitions,
             "merge_reduce": MERGE_REDUCE_NAME.get(info.merge_reduce, "none"),
             "stream_lanes": info.stream_lanes, "x_window": bool(info.x_window),
-            "x_window_intervals": info.x_window,
+            "x_window_intervals": info.x_window, "bin_streams": info.bin_streams,
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
@@ -379,14 +383,14 @@ class Plan:
     def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
                  merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
-                 stream=None):
+                 bin_streams: int = 0, stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
-                or merge_reduce != "auto" or stream_lanes or x_window != "auto"):
+                or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
-                                merge_reduce, stream_lanes, x_window)
+                                merge_reduce, stream_lanes, x_window, bin_streams)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     @classmethod

@@ -105,6 +105,13 @@ struct spmv_plan_st {
   const void* rg_val;
   int32_t group_waves;    // group-mapped schedule
   int32_t group_rows;
+  // per-bin launches (options.bin_streams): bins dealt over the caller's
+  // stream and n_side streams of the plan, forked and joined by events
+  int32_t bin_streams;
+  int32_t n_side;
+  hipStream_t side[kMaxBins];
+  hipEvent_t fork_ev;
+  hipEvent_t join_ev[kMaxBins];
 };
 
 namespace {
@@ -143,6 +150,8 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
   if (o->stream_lanes != 0 && (o->stream_lanes < 1 || o->stream_lanes > 64 ||
                                (o->stream_lanes & (o->stream_lanes - 1))))
     return fail(SPMV_ERR_INVALID_ARG, "options.stream_lanes must be a power of two <= 64");
+  if (o->bin_streams < 0 || o->bin_streams > SPMV_MAX_BINS)
+    return fail(SPMV_ERR_INVALID_ARG, "options.bin_streams must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
     return fail(SPMV_ERR_INVALID_ARG, "options.n_bins must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins > 0) {
@@ -178,6 +187,33 @@ void build_binned_launch(spmv_plan_st* p) {
   p->binned_blocks = next;
 }
 
+// Streams and events of the per-bin launches (none when the bins share one
+// grid or there is one bin).
+void release_bin_streams(spmv_plan_st* p) {
+  for (int i = 0; i < p->n_side; ++i) {
+    if (p->join_ev[i]) (void)hipEventDestroy(p->join_ev[i]);
+    if (p->side[i]) (void)hipStreamDestroy(p->side[i]);
+    p->join_ev[i] = nullptr;
+    p->side[i] = nullptr;
+  }
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  p->fork_ev = nullptr;
+  p->n_side = 0;
+}
+
+hipError_t create_bin_streams(spmv_plan_st* p) {
+  const int want = std::min<int>(p->bin_streams, p->n_launch) - 1;
+  if (want <= 0) return hipSuccess;
+  hipError_t err = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming);
+  for (int i = 0; err == hipSuccess && i < want; ++i) {
+    // default priority, like every stream of this library
+    err = hipStreamCreateWithFlags(&p->side[i], hipStreamNonBlocking);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&p->join_ev[i], hipEventDisableTiming);
+    p->n_side = i + 1;
+  }
+  return err;
+}
+
 // Rows per group of the group-mapped schedule: one LDS chunk of nonzeros
 // (512 per wavefront) at the mean row length, between 1 and the group's cap.
 int32_t default_group_rows(const spmv_plan_st* p, int waves) {
@@ -204,6 +240,38 @@ int32_t choose_strategy(const spmv_plan_st* p) {
   if (env && !std::strcmp(env, "group")) return SPMV_STRATEGY_GROUP;
   const int64_t cap = p->merge_reduce == 2 ? kBinnedMaxNnzStream : kBinnedMaxNnzWalk;
   return p->nnz < cap ? SPMV_STRATEGY_BINNED : SPMV_STRATEGY_MERGE;
+}
+
+// One launch per bin, longest rows first, dealt round robin over the
+// caller's stream and the plan's side streams; the side streams wait for
+// the work queued before the call (fork) and the caller's stream waits for
+// them (join), so the call orders like one launch on the caller's stream.
+template <typename V>
+hipError_t launch_binned_per_bin(const spmv_plan_st* p, const BinnedArgs<V>& all,
+                                 hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t err;
+  if (ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess) return err;
+  const int ns = p->n_side + 1;
+  if (p->n_side > 0) {
+    if ((err = hipEventRecord(p->fork_ev, stream)) != hipSuccess) return err;
+    for (int i = 0; i < p->n_side; ++i)
+      if ((err = hipStreamWaitEvent(p->side[i], p->fork_ev, 0)) != hipSuccess) return err;
+  }
+  for (int d = 0; d < p->n_launch; ++d) {
+    BinnedArgs<V> one = all;
+    one.n_launch = 1;
+    one.bin[0] = p->launch[d];
+    one.bin[0].block_begin = 0;
+    const hipStream_t s = d % ns == 0 ? stream : p->side[d % ns - 1];
+    if ((err = launch_binned<V>(one, one.bin[0].n_blocks, s, nullptr, nullptr)) != hipSuccess)
+      return err;
+  }
+  for (int i = 0; i < p->n_side; ++i) {
+    if ((err = hipEventRecord(p->join_ev[i], p->side[i])) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(stream, p->join_ev[i], 0)) != hipSuccess) return err;
+  }
+  if (ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess) return err;
+  return hipSuccess;
 }
 
 template <typename V>
@@ -280,7 +348,10 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.n_launch = p->n_launch;
     a.xcd_remap = p->xcd_remap;
     for (int i = 0; i < p->n_launch; ++i) a.bin[i] = p->launch[i];
-    err = launch_binned<V>(a, p->binned_blocks, stream, ev0, ev1);
+    if (p->bin_streams > 0 && p->n_launch > 1)
+      err = launch_binned_per_bin<V>(p, a, stream, ev0, ev1);
+    else
+      err = launch_binned<V>(a, p->binned_blocks, stream, ev0, ev1);
   }
   if (err != hipSuccess) return hip_fail(err, "spmv_exec launch");
   return SPMV_SUCCESS;
@@ -497,6 +568,7 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   auto bail = [&](spmv_status_t s) {
     (void)hipStreamSynchronize(stream);
     (void)hipFree(p->ws);
+    release_bin_streams(p);
     delete p;
     return s;
   };
@@ -562,6 +634,11 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   build_binned_launch(p);
   if ((int64_t)p->binned_blocks * kBlock > 0xffffffffll)
     return bail(fail(SPMV_ERR_UNSUPPORTED, "binned grid exceeds 2^32 work-items"));
+  p->bin_streams = options && options->bin_streams ? options->bin_streams
+                                                   : env_int("SPMV_BIN_STREAMS", 0);
+  if (p->bin_streams < 0 || p->bin_streams > kMaxBins) p->bin_streams = 0;
+  if ((err = create_bin_streams(p)) != hipSuccess)
+    return bail(hip_fail(err, "plan: bin streams"));
 
   // merge-path reduction: stream when every row fits an eighth of a partition
   {
@@ -883,6 +960,7 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
     if (!g_plans.erase(p)) return fail(SPMV_ERR_INVALID_PLAN, "not a live plan handle");
   }
   p->magic = 0;
+  release_bin_streams(p);
   hipError_t err = hipFree(p->ws);
   for (void* q : {p->owned_row_ptr, p->owned_entries, p->owned_rg_meta, p->owned_rg_data}) {
     if (!q) continue;
@@ -930,6 +1008,7 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->group_rows = p->group_rows;
   info->stream_lanes = p->stream_lanes;
   info->x_window = p->x_window;
+  info->bin_streams = p->bin_streams;
   info->n_bins = p->edges.n_bins;
   info->bin_identity = p->identity;
   for (int b = 0; b < p->edges.n_bins; ++b) {
