@@ -524,6 +524,7 @@ def main():
                    "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
                    "items_per_wave": info["items_per_wave"],
                    "bin_streams": info["bin_streams"],
+                   "dispatch_order": info["dispatch_order"],
                    "cache": "warm" if flush is None else
                    "flushed before every step (1 GiB fill + 1 GiB cached read)"},
         "achieved_GBps": round(gbps_exec, 2),

@@ -138,6 +138,22 @@ typedef struct spmv_plan_options {
   int32_t bin_lanes[SPMV_MAX_BINS];
                               /* lanes per row of each bin: 1,2,4,...,64, or 256
                                  (one 256-thread workgroup per row) */
+  int32_t dispatch_order;     /* merge-path with the walk reduction: the order
+                                 in which partitions are dealt to wavefronts.
+                                 0 auto (env SPMV_DISPATCH_ORDER =
+                                 partition|column; else column order when at
+                                 least 1/8 of the partitions lie inside one
+                                 row and every row has < N/4 entries),
+                                 1 partition order, 2 column
+                                 order: partitions sorted by the column of
+                                 their middle nonzero, so the four waves of a
+                                 workgroup gather over the same columns (long
+                                 rows: parts of different rows) and each XCD,
+                                 which takes a contiguous run of workgroups,
+                                 from a narrow part of x. Same partitions,
+                                 carries and fix-up: y is bitwise equal
+                                 either way. */
+  int32_t pad1;
 } spmv_plan_options_t;
 
 typedef struct spmv_plan_info {
@@ -167,6 +183,9 @@ typedef struct spmv_plan_info {
                                  (group width x rows, summed): nnz + padding */
   int32_t group_waves;        /* group-mapped schedule: wavefronts per group */
   int32_t group_rows;         /* ... and rows per group */
+  int32_t dispatch_order;     /* walk kernel's partition order: 1 partition,
+                                 2 column */
+  int32_t pad2;
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).

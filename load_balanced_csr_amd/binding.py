@@ -46,7 +46,8 @@ class PlanOptions(ctypes.Structure):
                 ("merge_reduce", ctypes.c_int32), ("stream_lanes", ctypes.c_int32),
                 ("x_window", ctypes.c_int32), ("bin_streams", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
-                ("bin_lanes", ctypes.c_int32 * MAX_BINS)]
+                ("bin_lanes", ctypes.c_int32 * MAX_BINS),
+                ("dispatch_order", ctypes.c_int32), ("pad1", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -62,7 +63,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_empty_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("rgcsr_group", ctypes.c_int32), ("pad1", ctypes.c_int32),
                 ("rgcsr_stored", ctypes.c_int64), ("group_waves", ctypes.c_int32),
-                ("group_rows", ctypes.c_int32)]
+                ("group_rows", ctypes.c_int32), ("dispatch_order", ctypes.c_int32),
+                ("pad2", ctypes.c_int32)]
 
 
 _lib = None
@@ -145,16 +147,20 @@ def _dtype_code(values: torch.Tensor) -> int:
 
 
 MERGE_REDUCE = {"auto": 0, "walk": 1, "stream": 2}
+DISPATCH_ORDER = {"auto": 0, "partition": 1, "column": 2}
+DISPATCH_ORDER_NAME = {1: "partition", 2: "column"}
 MERGE_REDUCE_NAME = {1: "walk", 2: "stream"}
 
 
 def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
                  stream_lanes: int = 0, x_window: str = "auto",
-                 bin_streams: int = 0) -> PlanOptions:
+                 bin_streams: int = 0, dispatch_order: str = "auto") -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored.
     bin_streams: 0 runs the binned schedule as one grid; n >= 1 launches each
-    bin on its own, dealt over the caller's stream and n - 1 plan streams."""
+    bin on its own, dealt over the caller's stream and n - 1 plan streams.
+    dispatch_order: "partition" or "column" (walk plans: workgroups sorted by
+    the column of their middle nonzero), "auto" the library's choice."""
     o = PlanOptions()
     o.strategy = STRATEGY[strategy]
     o.items_per_thread = items_per_thread
@@ -163,6 +169,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.stream_lanes = stream_lanes
     o.x_window = {"auto": 0, "off": 1, "on": 2}[x_window]
     o.bin_streams = bin_streams
+    o.dispatch_order = DISPATCH_ORDER[dispatch_order]
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -339,6 +346,7 @@ def spmv_plan_info(plan: int) -> dict:
             "merge_reduce": MERGE_REDUCE_NAME.get(info.merge_reduce, "none"),
             "stream_lanes": info.stream_lanes, "x_window": bool(info.x_window),
             "x_window_intervals": info.x_window, "bin_streams": info.bin_streams,
+            "dispatch_order": DISPATCH_ORDER_NAME.get(info.dispatch_order, "partition"),
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
@@ -383,14 +391,16 @@ class Plan:
     def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
                  merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
-                 bin_streams: int = 0, stream=None):
+                 bin_streams: int = 0, dispatch_order: str = "auto", stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
-                or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams):
+                or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams
+                or dispatch_order != "auto"):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
-                                merge_reduce, stream_lanes, x_window, bin_streams)
+                                merge_reduce, stream_lanes, x_window, bin_streams,
+                                dispatch_order)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     @classmethod

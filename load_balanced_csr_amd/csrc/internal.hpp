@@ -49,7 +49,8 @@ enum StatSlot : int {
   kStatWindowSamples = 5,  // stream workgroups examined
   kStatWindowFitsMulti = 6,  // ... that fit kWinIntervals intervals
   kStatBinOffset = 7,      // kMaxBins + 1 entries
-  kStatCount = kStatBinOffset + kMaxBins + 1
+  kStatInterior = kStatBinOffset + kMaxBins + 1,  // partitions inside one row
+  kStatCount = kStatInterior + 1
 };
 
 struct BinEdges {
@@ -68,9 +69,11 @@ hipError_t launch_bin_scan(int64_t M, const BinEdges& edges, int32_t* counts,
 hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges& edges,
                               const int32_t* offsets, const int64_t* stats,
                               int32_t* bins, hipStream_t s);
+// Also counts, into stats[kStatInterior], the partitions no row ends in
+// (every item a nonzero of one row).
 hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
                                int64_t P, int32_t* split_row, int32_t* split_nz,
-                               int32_t* row_bounds, hipStream_t s);
+                               int32_t* row_bounds, int64_t* stats, hipStream_t s);
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
@@ -125,12 +128,19 @@ struct MergeArgs {
   int32_t stream_lanes;  // lanes per row in the stream reduction
   int32_t x_window;      // stream kernel's x window: 0 none, 1 one interval, 3 up to three
   const int32_t* win_span;  // per stream workgroup: kWinTable int32 (window intervals)
+  const int32_t* part_order;  // walk kernel: dispatch slot -> partition (null: identity)
 };
 
 // Streaming read of `bytes` (multiple of 16) at data; the xor of each 4 KiB
 // block is stored to the 4-byte sink only when it equals key.
 hipError_t launch_read_probe(const void* data, int64_t bytes, int32_t key, int32_t* sink,
                              hipStream_t s);
+
+// Sort key of each group of `group` consecutive partitions for the column
+// dispatch order: the column of the group's middle nonzero (0 for a group
+// without nonzeros).
+hipError_t launch_group_keys(const int32_t* split_nz, const int32_t* col_idx, int32_t P,
+                             int32_t group, int32_t* keys, hipStream_t s);
 
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,

@@ -40,8 +40,11 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  const int p = blk * kWavesPerBlock + wave;
+  int p = blk * kWavesPerBlock + wave;
   if (p >= a.P) return;
+  // column dispatch order: the plan's permutation of the partitions (a
+  // uniform read of a table nothing here writes)
+  if (a.part_order) p = a.part_order[p];
 
   const int r0 = a.split_row[p], r1 = a.split_row[p + 1];
   const int n0 = a.split_nz[p], n1 = a.split_nz[p + 1];

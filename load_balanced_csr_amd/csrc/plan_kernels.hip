@@ -191,23 +191,63 @@ __global__ __launch_bounds__(kBlock) void bin_scatter_kernel(
 // nonzeros = d - rows_ended.
 // Also writes, per boundary, the row and that row's first nonzero, the
 // boundaries of the stream reduction (rows never cross its partitions).
-__global__ __launch_bounds__(kBlock) void split_search_kernel(
-    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int32_t T, int32_t P,
-    int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz,
-    int32_t* __restrict__ row_bounds) {
-  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (p > P) return;
-  const int64_t W = (int64_t)M + nnz;
-  const int64_t d = min(p * T, W);
+__device__ __forceinline__ int64_t split_at(const int32_t* __restrict__ row_ptr, int32_t M,
+                                            int32_t nnz, int64_t d) {
   int64_t lo = max((int64_t)0, d - nnz), hi = min(d, (int64_t)M);
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) >> 1;
     if ((int64_t)row_ptr[mid] + mid <= d) lo = mid; else hi = mid - 1;
   }
-  split_row[p] = (int32_t)lo;
-  split_nz[p] = (int32_t)(d - lo);
-  row_bounds[2 * p] = (int32_t)lo;
-  row_bounds[2 * p + 1] = row_ptr[lo];
+  return lo;
+}
+
+__global__ __launch_bounds__(kBlock) void split_search_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int32_t T, int32_t P,
+    int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz,
+    int32_t* __restrict__ row_bounds, int64_t* __restrict__ stats) {
+  __shared__ int64_t s_lo[kBlock + 1];
+  __shared__ int s_cnt[kWavesPerBlock];
+  const int t = threadIdx.x;
+  const int64_t p = (int64_t)blockIdx.x * kBlock + t;
+  const int64_t W = (int64_t)M + nnz;
+  int64_t lo = -1;
+  if (p <= P) {
+    const int64_t d = min(p * T, W);
+    lo = split_at(row_ptr, M, nnz, d);
+    split_row[p] = (int32_t)lo;
+    split_nz[p] = (int32_t)(d - lo);
+    row_bounds[2 * p] = (int32_t)lo;
+    row_bounds[2 * p + 1] = row_ptr[lo];
+  }
+  s_lo[t] = lo;
+  // the next block's first boundary, for this block's last partition
+  if (t == kBlock - 1) s_lo[kBlock] = p + 1 <= P ? split_at(row_ptr, M, nnz, min((p + 1) * T, W)) : -1;
+  __syncthreads();
+  // partition p is interior when no row ends in it (same split row at both ends)
+  const bool interior = p < P && s_lo[t + 1] == lo;
+  const int c = __popcll(__ballot(interior));
+  if (lane_id() == 0) s_cnt[t / kWave] = c;
+  __syncthreads();
+  if (t == 0) {
+    int total = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) total += s_cnt[w];
+    if (total) atomicAdd((unsigned long long*)&stats[kStatInterior], (unsigned long long)total);
+  }
+}
+
+// Column dispatch order: key of each group of `group` consecutive walk
+// partitions (the column of its middle nonzero; 0 when it has none). The
+// plan sorts single partitions (group 1).
+__global__ __launch_bounds__(kBlock) void group_keys_kernel(const int32_t* __restrict__ split_nz,
+                                                            const int32_t* __restrict__ col_idx,
+                                                            int32_t P, int32_t group,
+                                                            int32_t* __restrict__ keys) {
+  const int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t G = ((int64_t)P + group - 1) / group;
+  if (g >= G) return;
+  const int64_t p0 = g * group, p1 = min(p0 + group, (int64_t)P);
+  const int n0 = split_nz[p0], n1 = split_nz[p1];
+  keys[g] = n1 > n0 ? col_idx[n0 + (n1 - n0) / 2] : 0;
 }
 
 __global__ __launch_bounds__(kBlock) void check_columns_kernel(
@@ -494,12 +534,21 @@ hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges&
   return hipGetLastError();
 }
 
+hipError_t launch_group_keys(const int32_t* split_nz, const int32_t* col_idx, int32_t P,
+                             int32_t group, int32_t* keys, hipStream_t s) {
+  const int64_t G = ((int64_t)P + group - 1) / group;
+  if (G <= 0) return hipSuccess;
+  hipLaunchKernelGGL(group_keys_kernel, dim3(n_blocks(G, kBlock)), dim3(kBlock), 0, s, split_nz,
+                     col_idx, P, group, keys);
+  return hipGetLastError();
+}
+
 hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
                                int64_t P, int32_t* split_row, int32_t* split_nz,
-                               int32_t* row_bounds, hipStream_t s) {
+                               int32_t* row_bounds, int64_t* stats, hipStream_t s) {
   hipLaunchKernelGGL(split_search_kernel, dim3(n_blocks(P + 1, kBlock)), dim3(kBlock), 0, s,
                      row_ptr, (int32_t)M, (int32_t)nnz, T, (int32_t)P, split_row, split_nz,
-                     row_bounds);
+                     row_bounds, stats);
   return hipGetLastError();
 }
 
