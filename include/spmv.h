@@ -184,8 +184,9 @@ typedef struct spmv_plan_info {
   int32_t group_waves;        /* group-mapped schedule: wavefronts per group */
   int32_t group_rows;         /* ... and rows per group */
   int32_t dispatch_order;     /* walk kernel's partition order: 1 partition,
-                                 2 column */
-  int32_t pad2;
+                                 2 column (spmv_exec_multi follows it when at
+                                 least half the partitions are interior) */
+  int32_t interior_partitions;  /* partitions no row ends in */
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).

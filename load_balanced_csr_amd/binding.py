@@ -64,7 +64,7 @@ class PlanInfo(ctypes.Structure):
                 ("rgcsr_group", ctypes.c_int32), ("pad1", ctypes.c_int32),
                 ("rgcsr_stored", ctypes.c_int64), ("group_waves", ctypes.c_int32),
                 ("group_rows", ctypes.c_int32), ("dispatch_order", ctypes.c_int32),
-                ("pad2", ctypes.c_int32)]
+                ("interior_partitions", ctypes.c_int32)]
 
 
 _lib = None
@@ -347,6 +347,7 @@ def spmv_plan_info(plan: int) -> dict:
             "stream_lanes": info.stream_lanes, "x_window": bool(info.x_window),
             "x_window_intervals": info.x_window, "bin_streams": info.bin_streams,
             "dispatch_order": DISPATCH_ORDER_NAME.get(info.dispatch_order, "partition"),
+            "interior_partitions": info.interior_partitions,
             "n_bins": nb, "bin_identity": bool(info.bin_identity),
             "bin_max_len": list(info.bin_max_len[:nb]), "bin_lanes": list(info.bin_lanes[:nb]),
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,

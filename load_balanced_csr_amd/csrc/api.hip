@@ -110,6 +110,7 @@ struct spmv_plan_st {
   // walk kernel's dispatch order (options.dispatch_order): 1 partition
   // order, 2 column order through part_order (in owned_order)
   int32_t dispatch_order;
+  int64_t interior;       // partitions no row ends in
   const int32_t* part_order;
   void* owned_order;
   int32_t bin_streams;
@@ -431,6 +432,11 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
   a.cap = spmm_stage_cap(p->T);
   a.stream = p->merge_reduce == 2;
   a.xcd_remap = p->xcd_remap;
+  // the column order pays for SpMM only where most partitions lie inside
+  // long rows (measured: -37% on the bimodal matrix at k = 8, +9% on the
+  // power-law one, where a fifth do)
+  a.part_order = !a.stream && p->dispatch_order == 2 && 2 * p->interior >= p->P ? p->part_order
+                                                                                : nullptr;
   hipError_t err = hipSuccess;
   if (ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");
@@ -738,8 +744,8 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     // inside one row and the longest row covers under a quarter of the
     // columns (long, sparse rows: a partition's gathers span a wide range of
     // x; measured -9% to -13% on such inputs, +2% to +6% on others)
-    if (d == 0)
-      d = 8 * host_stats[kStatInterior] >= p->P && 4 * p->max_len < N ? 2 : 1;
+    p->interior = host_stats[kStatInterior];
+    if (d == 0) d = 8 * p->interior >= p->P && 4 * p->max_len < N ? 2 : 1;
     p->dispatch_order = p->merge_reduce == 1 && p->P > 0 && nnz > 0 ? d : 1;
     if (p->dispatch_order == 2 && (err = build_column_order(p, stream)) != hipSuccess)
       return bail(hip_fail(err, "plan: column dispatch order"));
@@ -1073,6 +1079,7 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->x_window = p->x_window;
   info->bin_streams = p->bin_streams;
   info->dispatch_order = p->dispatch_order;
+  info->interior_partitions = (int32_t)p->interior;
   info->n_bins = p->edges.n_bins;
   info->bin_identity = p->identity;
   for (int b = 0; b < p->edges.n_bins; ++b) {

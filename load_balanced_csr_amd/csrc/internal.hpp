@@ -174,6 +174,7 @@ struct SpmmArgs {
   int32_t cap;               // staged entries per array and wave
   int32_t stream;            // 1: partitions end at row ends (no carries)
   int32_t xcd_remap;
+  const int32_t* part_order;  // walk plans: dispatch slot -> partition (null: identity)
 };
 
 // Staging room per array for partitions of T units (at most T + T/8 rows or

@@ -125,8 +125,10 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  const int p = blk * kWavesPerBlock + wave;
+  int p = blk * kWavesPerBlock + wave;
   if (p >= a.P) return;
+  // the plan's column dispatch order (walk plans), as in the SpMV kernel
+  if (a.part_order) p = a.part_order[p];
 
   // partition p: rows [r0, r1) end inside it; nonzeros [n0, n1). In the
   // stream layout the nonzeros start and stop at row boundaries; otherwise

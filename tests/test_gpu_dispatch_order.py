@@ -115,3 +115,47 @@ def test_dispatch_order_option_check():
     with pytest.raises(lb.SpmvError) as e:
         lb.spmv_plan(dev(w.row_ptr), dev(w.col_idx), dev(w.values), w.M, w.N, o, None)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("k", [3, 8, 16])
+def test_column_order_spmm(k):
+    # SpMM over walk plans takes the same order: bitwise equal to the
+    # partition order, within the bound of the oracle column by column
+    w = CASES["bimodal"]()
+    m = DevMatrix.of(w)
+    rng = np.random.default_rng(k)
+    X_h = rng.uniform(-1, 1, (w.N, k)).astype(np.float32)
+    Y0_h = rng.uniform(-1, 1, (w.M, k)).astype(np.float32)
+    X = dev(X_h)
+    outs = []
+    for order in ("partition", "column"):
+        p = m.plan(None, strategy="merge", merge_reduce="walk", dispatch_order=order)
+        assert p.info["dispatch_order"] == order
+        # most partitions lie inside the long rows, so SpMM takes the order too
+        assert 2 * p.info["interior_partitions"] >= p.info["n_partitions"]
+        Y = dev(Y0_h)
+        p.exec_multi(X, Y, 1.5, 0.5)
+        torch.cuda.synchronize()
+        outs.append(Y.cpu().numpy())
+        p.destroy()
+    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8))
+    for c in (0, k - 1):
+        check(outs[1][:, c].copy(), w.row_ptr, w.col_idx, w.values, X_h[:, c].copy(), 1.5, 0.5,
+              Y0_h[:, c].copy(), "spmm col %d" % c)
+
+
+@pytest.mark.parametrize("case", ["powerlaw", "bimodal", "tiny", "laplacian_walk"])
+def test_interior_partition_count(case):
+    # partitions with the same split row at both ends, from the merge-path
+    # split computed on the host
+    w = CASES[case]()
+    m = DevMatrix.of(w)
+    p = m.plan(None, strategy="merge", merge_reduce="walk", items_per_thread=8)
+    T, P = p.info["items_per_wave"], p.info["n_partitions"]
+    rp = w.row_ptr.astype(np.int64)
+    W = w.M + int(rp[-1])
+    d = np.minimum(np.arange(P + 1, dtype=np.int64) * T, W)
+    i = np.searchsorted(rp + np.arange(w.M + 1), d, side="right") - 1
+    want = int(np.count_nonzero(i[:-1] == i[1:]))
+    assert p.info["interior_partitions"] == want, (case, p.info["interior_partitions"], want)
+    p.destroy()
