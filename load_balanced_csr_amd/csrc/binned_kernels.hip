@@ -39,8 +39,10 @@ __device__ __forceinline__ void group_rows(const BinnedArgs<V>& a, const BinLaun
   const int r = a.identity ? L.row_begin + idx : a.bins[L.row_begin + idx];
   const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
   V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
-  int k = s + gl;
-  for (; k + 3 * G < e; k += 4 * G) {
+  // unsigned: with nnz near 2^31 the stride past the row end must not wrap
+  unsigned k = (unsigned)(s + gl);
+  const unsigned ue = (unsigned)e;
+  for (; k + 3u * G < ue; k += 4u * G) {
     const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + G);
     const int c2 = ld_stream(a.col_idx + k + 2 * G), c3 = ld_stream(a.col_idx + k + 3 * G);
     const V v0 = ld_stream(a.val + k), v1 = ld_stream(a.val + k + G);
@@ -50,7 +52,7 @@ __device__ __forceinline__ void group_rows(const BinnedArgs<V>& a, const BinLaun
     acc2 = fma(v2, a.x[c2], acc2);
     acc3 = fma(v3, a.x[c3], acc3);
   }
-  for (; k < e; k += G) acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
+  for (; k < ue; k += G) acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
   V acc = (acc0 + acc1) + (acc2 + acc3);
   if (G > 1) acc = group_sum<G>(acc);
   if (gl == 0) store_row(a, r, acc);
@@ -64,8 +66,9 @@ __device__ __forceinline__ void block_row(const BinnedArgs<V>& a, const BinLaunc
   const int r = a.identity ? L.row_begin + tile : a.bins[L.row_begin + tile];
   const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
   V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
-  int k = s + (int)threadIdx.x;
-  for (; k + 3 * kBlock < e; k += 4 * kBlock) {
+  unsigned k = (unsigned)s + threadIdx.x;   // unsigned: no wrap near 2^31
+  const unsigned ue = (unsigned)e;
+  for (; k + 3u * kBlock < ue; k += 4u * kBlock) {
     const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + kBlock);
     const int c2 = ld_stream(a.col_idx + k + 2 * kBlock);
     const int c3 = ld_stream(a.col_idx + k + 3 * kBlock);
@@ -76,7 +79,7 @@ __device__ __forceinline__ void block_row(const BinnedArgs<V>& a, const BinLaunc
     acc2 = fma(v2, a.x[c2], acc2);
     acc3 = fma(v3, a.x[c3], acc3);
   }
-  for (; k < e; k += kBlock)
+  for (; k < ue; k += kBlock)
     acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
   V acc = group_sum<kWave>((acc0 + acc1) + (acc2 + acc3));
   if (lane_id() == 0) s_part[threadIdx.x / kWave] = acc;

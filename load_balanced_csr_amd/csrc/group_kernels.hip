@@ -58,7 +58,10 @@ __global__ __launch_bounds__(GW * kWave) void group_spmv_kernel(const GroupArgs<
     return lo;
   };
 
-  for (int base = 0; base < A; base += CH) {
+  // chunks counted, not strided: base + CH must not wrap for A near 2^31
+  const int nchunks = A / CH + (A % CH != 0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int base = c * CH;
     const int cnt = min(CH, A - base);
     // products of the chunk's atoms, coalesced
     for (int j = t; j < cnt; j += NT) {

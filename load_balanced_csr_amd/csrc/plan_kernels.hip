@@ -286,13 +286,14 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
   const int g = blockIdx.x;
   const int t = threadIdx.x;
   const int p0 = g * group, p1 = min(p0 + group, P);
-  int k0 = row_ptr[split_row[p0]], k1 = row_ptr[split_row[p1]];
+  // 64-bit positions: strides past nnz near 2^31 must not wrap
+  int64_t k0 = row_ptr[split_row[p0]], k1 = row_ptr[split_row[p1]];
   if (k1 > k0) {
-    k0 &= ~3;
-    k1 = min((k1 + 3) & ~3, nnz);
+    k0 &= ~int64_t(3);
+    k1 = min((k1 + 3) & ~int64_t(3), (int64_t)nnz);
   }
   int lo = INT_MAX, hi = INT_MIN;
-  for (int k = k0 + t; k < k1; k += kBlock) {
+  for (int64_t k = k0 + t; k < k1; k += kBlock) {
     const int c = col_idx[k];
     lo = min(lo, c);
     hi = max(hi, c);
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
   // buckets of width w over [lo, hi] (hi - lo < 2^31: columns are int32 and
   // non-negative); mark the ones that hold a column
   const unsigned w = ((unsigned)(hi - lo) + NB) / NB;
-  for (int k = k0 + t; k < k1; k += kBlock) s_flag[(unsigned)(col_idx[k] - lo) / w] = 1;
+  for (int64_t k = k0 + t; k < k1; k += kBlock) s_flag[(unsigned)(col_idx[k] - lo) / w] = 1;
   __syncthreads();
   // runs of marked buckets: run id by a block scan of the run starts
   const int start = s_flag[t] && (t == 0 || !s_flag[t - 1]);
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
       rlo[q] = INT_MAX;
       rhi[q] = INT_MIN;
     }
-    for (int k = k0 + t; k < k1; k += kBlock) {
+    for (int64_t k = k0 + t; k < k1; k += kBlock) {
       const int c = col_idx[k];
       const int r = s_run[(unsigned)(c - lo) / w] - 1;
 #pragma unroll

@@ -103,10 +103,11 @@ __global__ __launch_bounds__(kBlock) void rg_spmv_kernel(const RgArgs<V> a) {
   const bool live = r64 < a.M;
   const int r = live ? (int)r64 : a.M - 1;
   const int g = r / a.G;
-  const int L = live ? a.rl[r] : 0;
+  // unsigned: stepping past a row of nearly 2^31 entries must not wrap
+  const unsigned L = live ? (unsigned)a.rl[r] : 0u;
   const int64_t at = a.base[g] + (r - (int64_t)g * a.G);
   V acc = V(0);
-  for (int k = 0; __ballot(k < L) != 0; k += U) {
+  for (unsigned k = 0; __ballot(k < L) != 0; k += U) {
     int c[U];
     V v[U];
 #pragma unroll
