@@ -98,7 +98,10 @@ typedef struct spmv_plan_options {
                                  0: env SPMV_ITEMS_PER_THREAD, else chosen from
                                  the row lengths: 4 when every row has <= 32
                                  entries and the mean is < 12, otherwise 16
-                                 (fp32) or 8 (fp64) */
+                                 (fp32) or 8 (fp64) -- but 4 again when rows
+                                 cross those partitions, x is larger than
+                                 4 MiB (one XCD's L2) and fewer than half the
+                                 partitions lie inside one row */
   int32_t n_bins;             /* 1..SPMV_MAX_BINS; 0 = default bins */
   int32_t validate_columns;   /* 1: also check 0 <= col_idx < N at plan time
                                  (one pass over col_idx); env SPMV_VALIDATE=1 */

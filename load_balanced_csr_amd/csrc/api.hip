@@ -649,24 +649,48 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
       p->P = (W + p->T - 1) / p->T;
     }
   }
-  if (p->P > 0 && (err = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row,
-                                             p->split_nz, p->row_bounds, p->stats, stream)) !=
-                     hipSuccess)
-    return bail(hip_fail(err, "plan: split search"));
-  if (p->P > 0 && nnz > 0 &&
-      (err = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
-                                 kWavesPerBlock, window_bytes(p->ipt, (int)vs, kWavesPerBlock),
-                                 p->win_span, win_ints, p->stats, stream)) !=
-          hipSuccess)
-    return bail(hip_fail(err, "plan: window spans"));
+  // merge-path splits at T and the stream workgroups' x windows (their
+  // counters in the stats block start from zero)
+  auto split_and_spans = [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    if (p->P > 0)
+      e = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row, p->split_nz,
+                              p->row_bounds, p->stats, stream);
+    if (e == hipSuccess && p->P > 0 && nnz > 0)
+      e = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
+                              kWavesPerBlock, window_bytes(p->ipt, (int)vs, kWavesPerBlock),
+                              p->win_span, win_ints, p->stats, stream);
+    return e;
+  };
+  auto read_stats = [&]() -> hipError_t {
+    hipError_t e = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats,
+                                  hipMemcpyDeviceToHost, stream);
+    return e == hipSuccess ? hipStreamSynchronize(stream) : e;
+  };
+  if ((err = split_and_spans()) != hipSuccess) return bail(hip_fail(err, "plan: split search"));
   if (validate_cols &&
       (err = launch_check_columns(col_idx, nnz, N, p->stats, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: column check"));
-  if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
-                            stream)) != hipSuccess)
-    return bail(hip_fail(err, "plan: stats copy"));
-  if ((err = hipStreamSynchronize(stream)) != hipSuccess)
-    return bail(hip_fail(err, "plan: synchronize"));
+  if ((err = read_stats()) != hipSuccess) return bail(hip_fail(err, "plan: stats copy"));
+  // Rows that cross partitions, an x larger than one XCD's L2 and most
+  // partitions holding row ends (not the insides of long rows): the gathers
+  // are bound by how many L1 misses are in flight, and T = 256 runs twice the
+  // waves per CU of T = 1024 (measured on MI355X: -4% to -29% on power-law
+  // and skewed matrices of 4M columns; no gain where the column order keeps
+  // long rows' x in L2). Split again at T = 256.
+  if (auto_ipt && p->ipt > 4 && !(host_stats[kStatError] & 3) &&
+      host_stats[kStatMaxLen] > p->T / 8 && N * (int64_t)vs > kXcdL2Bytes &&
+      2 * host_stats[kStatInterior] < p->P) {
+    p->ipt = 4;
+    p->T = kWave * p->ipt;
+    p->P = (W + p->T - 1) / p->T;
+    if ((err = hipMemsetAsync(p->stats + kStatWindowFits, 0, 3 * sizeof(int64_t), stream)) !=
+            hipSuccess ||
+        (err = hipMemsetAsync(p->stats + kStatInterior, 0, sizeof(int64_t), stream)) !=
+            hipSuccess ||
+        (err = split_and_spans()) != hipSuccess || (err = read_stats()) != hipSuccess)
+      return bail(hip_fail(err, "plan: split search at T = 256"));
+  }
 
   if (host_stats[kStatError] & 1)
     return bail(fail(SPMV_ERR_INVALID_MATRIX,

@@ -11,6 +11,7 @@ constexpr int kWave = 64;             // CDNA4 wavefront
 constexpr int kBlock = 256;           // threads per workgroup (4 waves)
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
+constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;   // L2 of one XCD
 constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
 constexpr int kWindowBytes = 12288;      // cap of the staged x window (register form)

@@ -159,3 +159,32 @@ def test_interior_partition_count(case):
     want = int(np.count_nonzero(i[:-1] == i[1:]))
     assert p.info["interior_partitions"] == want, (case, p.info["interior_partitions"], want)
     p.destroy()
+
+
+def test_auto_partition_size_for_wide_x():
+    # rows crossing partitions, x of 6 MB (> one XCD's L2), few interior
+    # partitions: the plan splits again at T = 256; its interior count is
+    # that of the final split
+    w = synth.powerlaw(M=1_500_000, max_len=50_000)
+    m = DevMatrix.of(w)
+    p = m.plan(None, strategy="merge")
+    assert p.info["merge_reduce"] == "walk"
+    assert p.info["items_per_wave"] == 256, p.info["items_per_wave"]
+    T, P = 256, p.info["n_partitions"]
+    rp = w.row_ptr.astype(np.int64)
+    assert P == (w.M + int(rp[-1]) + T - 1) // T
+    d = np.minimum(np.arange(P + 1, dtype=np.int64) * T, w.M + int(rp[-1]))
+    i = np.searchsorted(rp + np.arange(w.M + 1), d, side="right") - 1
+    assert p.info["interior_partitions"] == int(np.count_nonzero(i[:-1] == i[1:]))
+    x = dev(w.x)
+    y0 = dev(w.y0)
+    y = y0.clone()
+    p(x, y, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    check(y.cpu().numpy(), w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0, "T=256")
+    p.destroy()
+    # x within one L2: the default partition size stays
+    w = CASES["bimodal"]()
+    p = DevMatrix.of(w).plan(None, strategy="merge")
+    assert p.info["items_per_wave"] == 1024
+    p.destroy()
