@@ -181,8 +181,6 @@ struct SpmmArgs {
 // Staging room per array for partitions of T units (at most T + T/8 rows or
 // nonzeros, plus quad alignment).
 constexpr int spmm_stage_cap(int T) { return T + T / 8 + 8; }
-// Dynamic LDS of one SpMM workgroup.
-size_t spmm_lds_bytes(int vbytes, int T);
 
 template <typename V>
 hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s);

@@ -43,6 +43,18 @@ __host__ __device__ constexpr int spmm_wave_lds(int cap, int vbytes) {
                                                        : kSpmmRecordBytes;
 }
 
+// LDS of one wave of the merge-slot kernel (walk plans): a walk partition
+// holds at most T <= cap - 8 rows plus nonzeros, and staging an array of n
+// words takes at most n + 7, so the row pointers and the column indices
+// share one region of cap + 12 words (the columns start at the first 16-byte
+// boundary past the row pointers); the values follow it. The records of the
+// slot combine overlay the same space. Half the footprint of three separate
+// regions: twice the waves per CU for this gather-bound kernel.
+__host__ __device__ constexpr int spmm_walk_wave_lds(int cap, int vbytes) {
+  return (cap + 12) * 4 + cap * vbytes > kSpmmRecordBytes ? (cap + 12) * 4 + cap * vbytes
+                                                          : kSpmmRecordBytes;
+}
+
 // VE consecutive elements of V (a 16-byte vector when VE * sizeof(V) = 16).
 template <typename V, int VE>
 struct Vec {
@@ -148,10 +160,13 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   }
   const int R = r1 - r0, nloc = n1 - n0, tot = R + nloc;
 
-  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V));
+  // every partition holds at most cap - 8 rows plus nonzeros (walk: T; stream:
+  // T + T/8), which the shared LDS region relies on; never stage past it
+  if (tot > a.cap - 8) return;
+  unsigned char* base = s_dyn + (size_t)wave * spmm_walk_wave_lds(a.cap, sizeof(V));
   int32_t* s_rp = reinterpret_cast<int32_t*>(base);
-  int32_t* s_col = s_rp + a.cap;
-  int32_t* s_val = s_col + a.cap;   // cap entries of V, staged as int32 words
+  int32_t* s_col = s_rp + ((R + 8 + 3) & ~3);
+  int32_t* s_val = s_rp + (a.cap + 12);   // cap entries of V, staged as int32 words
 
   // row pointers rp[r0 .. r1] (row r1's start ends the last closed row), the
   // partition's column indices and values: coalesced 16-byte loads
@@ -411,7 +426,8 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
 template <typename V, int KL, int VE>
 hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  const size_t lds = (size_t)kWavesPerBlock * spmm_wave_lds(a.cap, sizeof(V));
+  const size_t lds = (size_t)kWavesPerBlock * (a.stream ? spmm_wave_lds(a.cap, sizeof(V))
+                                                        : spmm_walk_wave_lds(a.cap, sizeof(V)));
   // bytes from X to the end of its last row's k columns
   const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
   const bool off32 = xspan < (1ull << 32);
@@ -441,10 +457,6 @@ hipError_t launch_ve(const SpmmArgs<V>& a, hipStream_t s) {
 }
 
 }  // namespace
-
-size_t spmm_lds_bytes(int vbytes, int T) {
-  return (size_t)kWavesPerBlock * spmm_wave_lds(spmm_stage_cap(T), vbytes);
-}
 
 template <typename V>
 hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s) {
