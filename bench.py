@@ -107,8 +107,9 @@ def load_traffic(workload: str, kernel: str, files=KERNEL_SOURCES):
 
 def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
     """The oracle as it stands, on one host core, repeated on the whole
-    workload until the budget is spent (at least once). Its result also
-    checks the GPU's first exec (every row, the acceptance bound)."""
+    workload until the time budget is spent (at least once; the budget, 10 s
+    by default, bounds the sample). Its result also checks the GPU's first
+    exec (every row, the acceptance bound)."""
     import oracle
     try:
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
@@ -129,7 +130,7 @@ def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
         else:
             ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 50:
+        if time.perf_counter() > t_end or len(times) >= 2000:
             break
     t = statistics.median(times)
     ok, worst, _ = oracle.within_tolerance(y_gpu, ref, scale, w.alpha, w.beta, w.y0,
