@@ -231,14 +231,27 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
   Quad<V> v[NN > 0 ? NN : 1];
+  // wave-uniform bases and 32-bit byte offsets; all column quads, then all
+  // value quads, then the row ends (needed last)
+  const int32_t* cb = col + 4 * (int64_t)qn0;
+  const V* vbase = val + 4 * (int64_t)qn0;
+  const int32_t* eb = row_ptr + 4 * (int64_t)qr0;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) e[r] = load_quad<false>(row_ptr, qr0 + min(lane + kWave * r, nqr - 1), 0);
+  for (int r = 0; r < NN; ++r)
+    c[r] = ld_stream_at<i32x4>(cb, 16u * (uint32_t)min(lane + kWave * r, nqn - 1));
 #pragma unroll
   for (int r = 0; r < NN; ++r) {
-    const int q = qn0 + min(lane + kWave * r, nqn - 1);
-    c[r] = load_quad<false>(col, q, 0);
-    v[r] = load_quad<false>(val, q, 0);
+    const uint32_t off = 16u * (uint32_t)min(lane + kWave * r, nqn - 1);
+    if constexpr (sizeof(V) == 4) {
+      v[r].v = ld_stream_at<f32x4>(vbase, off);
+    } else {
+      v[r].lo = ld_stream_at<f64x2>(vbase, 2 * off);
+      v[r].hi = ld_stream_at<f64x2>(vbase, 2 * off + 16);
+    }
   }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    e[r] = ld_stream_at<i32x4>(eb, 16u * (uint32_t)min(lane + kWave * r, nqr - 1));
   bool from_lds = false;
   if (WIN) {
     w.commit();
