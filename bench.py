@@ -535,7 +535,10 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "kernel_ms": round(mean_kern, 5),
-                     "traffic": load_traffic(args.workload, kernel)},
+                     # counters were taken on the CSR plan; a COO plan runs the
+                     # same kernels on the same matrix, a transposed one on A^T
+                     "traffic": load_traffic(args.workload, kernel)
+                                if args.format in ("csr", "coo") else None},
         "exec_ms_median": round(statistics.median(exec_ms), 5),
         "exec_ms_min": round(min(exec_ms), 5),
         "exec_ms_max": round(max(exec_ms), 5),
