@@ -69,7 +69,8 @@ typedef enum spmv_dtype { SPMV_F32 = 0, SPMV_F64 = 1 } spmv_dtype_t;
  *  AUTO  : the planner picks MERGE or BINNED from the matrix size and row
  *          lengths (a switch fitted on MI355X: BINNED below 3,000,000
  *          nonzeros when some row is longer than T/8, below 200,000 when
- *          none is; MERGE above). */
+ *          none is and T = 1024; MERGE above, and whenever every row fits
+ *          T/8 with T = 256). */
 typedef enum spmv_strategy {
   SPMV_STRATEGY_AUTO = 0,
   SPMV_STRATEGY_MERGE = 1,

@@ -279,6 +279,10 @@ int32_t choose_strategy(const spmv_plan_st* p) {
   if (env && !std::strcmp(env, "merge")) return SPMV_STRATEGY_MERGE;
   if (env && !std::strcmp(env, "binned")) return SPMV_STRATEGY_BINNED;
   if (env && !std::strcmp(env, "group")) return SPMV_STRATEGY_GROUP;
+  // short rows (T = 256) give small stream plans enough partitions to fill
+  // the launch, and merge-path wins or ties there (tiny workload: 7.5 against
+  // 8.2 us); with T = 1024 a small plan is a few long-lived waves
+  if (p->merge_reduce == 2 && p->ipt == 4) return SPMV_STRATEGY_MERGE;
   const int64_t cap = p->merge_reduce == 2 ? kBinnedMaxNnzStream : kBinnedMaxNnzWalk;
   return p->nnz < cap ? SPMV_STRATEGY_BINNED : SPMV_STRATEGY_MERGE;
 }
