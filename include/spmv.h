@@ -52,7 +52,8 @@ typedef enum spmv_status {
   SPMV_SUCCESS = 0,
   SPMV_ERR_INVALID_ARG = 1,    /* null/aliased pointer, negative size, bad enum */
   SPMV_ERR_UNSUPPORTED = 2,    /* sizes beyond the int32 item model, see spmv_plan */
-  SPMV_ERR_ALLOC = 3,          /* the one workspace hipMalloc failed */
+  SPMV_ERR_ALLOC = 3,          /* a plan-time device allocation failed (the
+                                  workspace, or a copy a plan_* call owns) */
   SPMV_ERR_HIP = 4,            /* a HIP launch or runtime call failed */
   SPMV_ERR_INVALID_PLAN = 5,   /* NULL, destroyed or foreign handle */
   SPMV_ERR_INVALID_MATRIX = 6  /* row_ptr (or, when validated, col_idx) malformed */
@@ -209,15 +210,18 @@ typedef struct spmv_plan_info {
  * between spmv_exec calls (the plan samples col_idx once to choose a kernel
  * variant; results never depend on that choice). row_ptr, col_idx and values
  * must be 16-byte aligned (any hipMalloc allocation is), else
- * SPMV_ERR_INVALID_ARG. The plan owns exactly one device allocation, made
- * here and freed by spmv_destroy.
+ * SPMV_ERR_INVALID_ARG. The plan owns one device workspace, plus the column
+ * dispatch order when it uses one and the streams and events of per-bin
+ * launches when asked for; all are made here and freed by spmv_destroy.
  *
  * Work: row-length statistics and per-workgroup bin counts kept in LDS, an
  * exclusive scan of the bin counts, a stable scatter of row ids into bins,
- * and one merge-path binary search per wavefront partition; then one
- * device-to-host copy of a small statistics block and one stream
- * synchronisation. Returns SPMV_ERR_UNSUPPORTED if M + nnz > 2^31 - 1.
- * M == 0 or nnz == 0 is allowed. */
+ * one merge-path binary search per wavefront partition and the stream
+ * workgroups' x windows; device-to-host copies of a small statistics block
+ * with a stream synchronisation each (one to three: before choosing the
+ * partition size, after the split, after a second split), and one more when
+ * the column dispatch order is sorted. Returns SPMV_ERR_UNSUPPORTED if
+ * M + nnz > 2^31 - 1. M == 0 or nnz == 0 is allowed. */
 SPMV_API spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                         const int32_t* row_ptr, const int32_t* col_idx,
                         const void* values, spmv_dtype_t dtype,
@@ -312,10 +316,12 @@ SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, i
  * y  device array of M elements; read only when beta != 0. Must not alias x.
  * alpha, beta are converted once to the plan's dtype.
  *
- * Asynchronous: only enqueues kernels on stream; never allocates, frees or
- * synchronises. Rows with no entries give exactly beta*y (0 when beta == 0).
- * For a fixed plan the result is bitwise reproducible (no float atomics).
- * One plan must not run concurrently on two streams (its carry buffer is
+ * Asynchronous: only enqueues work on stream (with per-bin launches, event
+ * records and waits that fork the plan's streams from it and join them back);
+ * never allocates, frees or synchronises, so it can be captured in a HIP
+ * graph. Rows with no entries give exactly beta*y (0 when beta == 0). For a
+ * fixed plan the result is bitwise reproducible (no float atomics). One plan
+ * must not run concurrently on two streams (its carry buffer and events are
  * per plan); distinct plans are independent. */
 SPMV_API spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
                         double alpha, double beta, hipStream_t stream);
