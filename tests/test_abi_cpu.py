@@ -77,6 +77,15 @@ def test_bad_options_rejected():
         st = lib.spmv_plan_ex(ctypes.byref(h), 10, 10, 20, 0x1000, 0x2000, 0x3000, 0,
                               ctypes.byref(o), None)
         assert st == 1, kw
+    # per-bin streams beyond the bin count, dispatch orders that do not exist
+    for field, bad in (("bin_streams", 9), ("bin_streams", -1), ("dispatch_order", 3),
+                       ("dispatch_order", -1)):
+        o = lb.make_options()
+        setattr(o, field, bad)
+        st = lib.spmv_plan_ex(ctypes.byref(h), 10, 10, 20, 0x1000, 0x2000, 0x3000, 0,
+                              ctypes.byref(o), None)
+        assert st == 1, (field, bad)
+        assert field in lb.spmv_last_error()
 
 
 def test_exec_and_destroy_reject_foreign_handles():
@@ -99,3 +108,35 @@ def test_library_has_no_undefined_symbols_of_its_own():
     out = subprocess.check_output(["nm", "-D", "--undefined-only", lb.LIB_PATH]).decode()
     own = [l for l in out.splitlines() if "spmv" in l]
     assert not own, own[:5]
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # sizes and field offsets of the option and info structs as the C
+    # compiler lays them out, against the binding's ctypes mirrors
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("no C compiler or ROCm headers")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spmv.h"', 'int main(void) {']
+    for cname, py in (("spmv_plan_options_t", binding.PlanOptions),
+                      ("spmv_plan_info_t", binding.PlanInfo)):
+        lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for fname, _ in py._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, fname, cname, fname))
+    lines += ["return 0; }"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("header does not compile as C here: " + r.stderr[:200])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for cname, py in (("spmv_plan_options_t", binding.PlanOptions),
+                      ("spmv_plan_info_t", binding.PlanInfo)):
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
