@@ -171,3 +171,25 @@ def test_full_size_laplacian_k8():
     launch the SpMM benchmark times, against the oracle on every row."""
     w = synth.laplacian()
     _case(w, "auto", (8,))
+
+
+@pytest.mark.parametrize("kind", ["binned", "binned_streams", "group", "rgcsr"])
+def test_spmm_on_other_schedules(kind):
+    # spmv_exec_multi runs on the plan's merge-path partitions whatever
+    # schedule spmv_exec uses: the SpMV schedule must not change the result
+    w = synth.bimodal(M=20_000, n_long=15, long_len=4000)
+    m = DevMatrix.of(w)
+    if kind == "rgcsr":
+        plan = lb.Plan.rgcsr(m.rp, m.col, m.val, (w.M, w.N), group_rows=32)
+    elif kind == "binned_streams":
+        plan = m.plan(None, strategy="binned", bin_streams=3)
+    else:
+        plan = m.plan(None, strategy=kind)
+    rng = np.random.default_rng(11)
+    for k, beta in ((1, 0.0), (6, 0.5), (40, -1.0)):
+        X = rng.uniform(-1, 1, (w.N, k)).astype(np.float32)
+        Y0 = rng.uniform(-1, 1, (w.M, k)).astype(np.float32)
+        log("spmm on", kind, "k", k)
+        Y = _run(m, plan, X, 1.5, beta, Y0)
+        _check(Y, m, X, 1.5, beta, Y0, "%s k=%d" % (kind, k))
+    plan.destroy()
