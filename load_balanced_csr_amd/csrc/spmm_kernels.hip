@@ -63,7 +63,7 @@ struct Vec {
 template <typename V, int VE>
 __device__ __forceinline__ Vec<V, VE> vec_load(const V* p) {
   Vec<V, VE> r;
-  if constexpr (VE * sizeof(V) == 16) {
+  if constexpr (VE > 1 && (VE * sizeof(V) == 16 || VE * sizeof(V) == 8)) {
     typedef V v4 __attribute__((ext_vector_type(VE)));
     const v4 t = *reinterpret_cast<const v4*>(p);
 #pragma unroll
@@ -113,7 +113,7 @@ __device__ __forceinline__ void spmm_store(const SpmmArgs<V>& a, int row, int co
 #pragma unroll
     for (int q = 0; q < VE; ++q) out.v[q] = a.alpha * acc.v[q];
   }
-  if constexpr (VE * sizeof(V) == 16) {
+  if constexpr (VE > 1 && (VE * sizeof(V) == 16 || VE * sizeof(V) == 8)) {
     typedef V v4 __attribute__((ext_vector_type(VE)));
     v4 t;
 #pragma unroll
@@ -463,11 +463,20 @@ hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s) {
   if (a.P <= 0 || a.k <= 0) return hipSuccess;
   if (a.k > kWave || a.cap < spmm_stage_cap(a.T)) return hipErrorInvalidValue;
   // 16-byte lanes when every row of X and Y starts 16-byte aligned and k
-  // fills whole vectors; otherwise one element per lane
+  // fills whole vectors; for fp32, 8-byte lanes (two columns) when k, the
+  // strides and the 8-byte alignment allow; otherwise one element per lane
   constexpr int VE = 16 / sizeof(V);
-  const bool vec = a.k % VE == 0 && a.ldx % VE == 0 && a.ldy % VE == 0 &&
-                   ((reinterpret_cast<uintptr_t>(a.X) | reinterpret_cast<uintptr_t>(a.Y)) & 15) == 0;
-  hipError_t err = vec ? launch_ve<V, VE>(a, s) : launch_ve<V, 1>(a, s);
+  const uintptr_t xy = reinterpret_cast<uintptr_t>(a.X) | reinterpret_cast<uintptr_t>(a.Y);
+  const bool vec = a.k % VE == 0 && a.ldx % VE == 0 && a.ldy % VE == 0 && (xy & 15) == 0;
+  hipError_t err;
+  if (vec) {
+    err = launch_ve<V, VE>(a, s);
+  } else if constexpr (VE == 4) {
+    const bool vec2 = a.k % 2 == 0 && a.ldx % 2 == 0 && a.ldy % 2 == 0 && (xy & 7) == 0;
+    err = vec2 ? launch_ve<V, 2>(a, s) : launch_ve<V, 1>(a, s);
+  } else {
+    err = launch_ve<V, 1>(a, s);
+  }
   if (err != hipSuccess || a.stream || a.P <= 1) return err;
   hipLaunchKernelGGL((spmm_fixup_kernel<V>), dim3((a.P + kWavesPerBlock - 1) / kWavesPerBlock),
                      dim3(kBlock), 0, s, a);
