@@ -35,6 +35,22 @@
  *  - beta == 0 means y is write-only: it is never read, so it may hold NaN.
  *  - Nothing here allocates after spmv_plan returns, except spmv_plan_* calls
  *    that are documented as copying to host.
+ *
+ * Environment (read at plan time; an explicit option wins; for tuning and
+ * tests, never needed for correct results):
+ *   SPMV_STRATEGY=merge|binned|group   schedule when options leave it AUTO
+ *   SPMV_ITEMS_PER_THREAD=4|7|8|16     merge-path items per lane
+ *   SPMV_MERGE_REDUCE=walk|stream      merge-path reduction
+ *   SPMV_STREAM_LANES=G                lanes per row in the stream reduction
+ *   SPMV_X_WINDOW=0|1                  stream kernel's x window off / on
+ *   SPMV_DISPATCH_ORDER=partition|column   walk kernel's partition order
+ *   SPMV_BIN_STREAMS=n                 binned schedule: launches per bin
+ *   SPMV_XCD_REMAP=0                   plain workgroup order (default 1:
+ *                                      each XCD takes a contiguous run)
+ *   SPMV_VALIDATE=1                    check 0 <= col_idx < N at plan time
+ *   SPMV_LOG=1                         one line per plan on stderr
+ *   SPMV_TEST_FAIL_ALLOC=1             make the workspace allocation fail
+ *                                      (tests of the error path)
  */
 #ifndef SPMV_H_
 #define SPMV_H_
