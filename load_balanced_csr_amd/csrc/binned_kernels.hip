@@ -114,12 +114,8 @@ template <typename V>
 hipError_t launch_binned(const BinnedArgs<V>& a, int total_blocks, hipStream_t s,
                          hipEvent_t ev0, hipEvent_t ev1) {
   if (total_blocks <= 0) return hipSuccess;
-  hipError_t err;
-  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((binned_spmv_kernel<V>), dim3(total_blocks), dim3(kBlock), 0, s, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-  return hipSuccess;
+  launch_timed(binned_spmv_kernel<V>, dim3(total_blocks), dim3(kBlock), 0, s, ev0, ev1, a);
+  return hipGetLastError();
 }
 
 template hipError_t launch_binned<float>(const BinnedArgs<float>&, int, hipStream_t, hipEvent_t,

@@ -108,26 +108,22 @@ hipError_t launch_group(const GroupArgs<V>& a, int group_waves, hipStream_t s, h
   if (a.rows_per_group < 1 || a.rows_per_group > kGroupRowsPerWave * group_waves)
     return hipErrorInvalidValue;
   const int64_t groups = ((int64_t)a.M + a.rows_per_group - 1) / a.rows_per_group;
-  hipError_t err;
-  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
   switch (group_waves) {
     case 1:
-      hipLaunchKernelGGL((group_spmv_kernel<V, 1>), dim3((unsigned)groups), dim3(kWave), 0, s, a);
+      launch_timed(group_spmv_kernel<V, 1>, dim3((unsigned)groups), dim3(kWave), 0, s, ev0, ev1, a);
       break;
     case 2:
-      hipLaunchKernelGGL((group_spmv_kernel<V, 2>), dim3((unsigned)groups), dim3(2 * kWave), 0, s,
-                         a);
+      launch_timed(group_spmv_kernel<V, 2>, dim3((unsigned)groups), dim3(2 * kWave), 0, s, ev0,
+                   ev1, a);
       break;
     case 4:
-      hipLaunchKernelGGL((group_spmv_kernel<V, 4>), dim3((unsigned)groups), dim3(4 * kWave), 0, s,
-                         a);
+      launch_timed(group_spmv_kernel<V, 4>, dim3((unsigned)groups), dim3(4 * kWave), 0, s, ev0,
+                   ev1, a);
       break;
     default:
       return hipErrorInvalidValue;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 template hipError_t launch_group<float>(const GroupArgs<float>&, int, hipStream_t, hipEvent_t,

@@ -3,9 +3,22 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace spmv {
+
+// Launch a kernel; with timing events, the dispatch itself records them at
+// the kernel's start and end (AMD's extended launch), so they bracket the
+// kernel alone, as a kernel trace does. Without events, a plain launch.
+template <typename... Args, typename F = void (*)(Args...)>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                         hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev0, ev1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 constexpr int kWave = 64;             // CDNA4 wavefront
 constexpr int kBlock = 256;           // threads per workgroup (4 waves)

@@ -490,28 +490,29 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
 }
 
 template <typename V, int IPT, int WK>
-hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s) {
+hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int WPB = kWavesPerBlock;
   if constexpr (stream_window_bytes(IPT, sizeof(V), WPB) > 0) {
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, WK, WPB>), dim3((a.P + WPB - 1) / WPB),
-                       dim3(WPB * kWave), 0, s, a, a.row_bounds, a.win_span);
+    launch_timed(merge_stream_kernel<V, IPT, WK, WPB>, dim3((a.P + WPB - 1) / WPB),
+                 dim3(WPB * kWave), 0, s, ev0, ev1, a, a.row_bounds, a.win_span);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;   // the plan never asks for it
 }
 
 template <typename V, int IPT>
-hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s) {
+hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
   if (a.stream && a.x_window == 1) {
-    return launch_window<V, IPT, 1>(a, s);
+    return launch_window<V, IPT, 1>(a, s, ev0, ev1);
   } else if (a.stream && a.x_window > 1) {
-    return launch_window<V, IPT, kWinIntervals>(a, s);
+    return launch_window<V, IPT, kWinIntervals>(a, s, ev0, ev1);
   } else if (a.stream) {
-    hipLaunchKernelGGL((merge_stream_kernel<V, IPT, 0, kWavesPerBlock>), dim3(blocks),
-                       dim3(kBlock), 0, s, a, a.row_bounds, a.win_span);
-  } else
-    hipLaunchKernelGGL((merge_spmv_kernel<V, IPT>), dim3(blocks), dim3(kBlock), 0, s, a);
+    launch_timed(merge_stream_kernel<V, IPT, 0, kWavesPerBlock>, dim3(blocks), dim3(kBlock), 0,
+                 s, ev0, ev1, a, a.row_bounds, a.win_span);
+  } else {
+    launch_timed(merge_spmv_kernel<V, IPT>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
+  }
   return hipGetLastError();
 }
 
@@ -522,16 +523,15 @@ hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_
                         hipEvent_t ev1) {
   if (a.P <= 0) return hipSuccess;
   hipError_t err;
-  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+  // ev0 / ev1 bracket the main kernel alone (recorded by its dispatch)
   switch (ipt) {
-    case 4: err = launch_main<V, 4>(a, s); break;
-    case 7: err = launch_main<V, 7>(a, s); break;
-    case 8: err = launch_main<V, 8>(a, s); break;
-    case 16: err = launch_main<V, 16>(a, s); break;
+    case 4: err = launch_main<V, 4>(a, s, ev0, ev1); break;
+    case 7: err = launch_main<V, 7>(a, s, ev0, ev1); break;
+    case 8: err = launch_main<V, 8>(a, s, ev0, ev1); break;
+    case 16: err = launch_main<V, 16>(a, s, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
   if (a.P > 1 && !a.stream) {
     const int64_t chunks = ((int64_t)a.P + kWave - 1) / kWave;
     const int blocks = (int)((chunks + kWavesPerBlock - 1) / kWavesPerBlock);

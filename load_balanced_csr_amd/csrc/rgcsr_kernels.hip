@@ -159,12 +159,9 @@ hipError_t launch_rg_widths(const int32_t* row_ptr, int64_t M, int32_t G, int32_
 template <typename V>
 hipError_t launch_rg_spmv(const RgArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.M == 0) return hipSuccess;
-  hipError_t err;
-  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL(rg_spmv_kernel<V>, dim3((a.M + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-  return hipSuccess;
+  launch_timed(rg_spmv_kernel<V>, dim3((a.M + kBlock - 1) / kBlock), dim3(kBlock), 0, s, ev0, ev1,
+               a);
+  return hipGetLastError();
 }
 
 template hipError_t launch_rg_spmv<float>(const RgArgs<float>&, hipStream_t, hipEvent_t,
