@@ -297,15 +297,27 @@ def run_spmm(args, w, torch, lb, dev):
         step()
     kb = [hip.create() for _ in range(K)]
     ke = [hip.create() for _ in range(K)]
+    xb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    xe = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # timed region: K steps, events around each exec (every launch of it)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
             flush()
-        step(kb[i], ke[i])
+        xb[i].record()
+        step()
+        xe[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
+    ms = [xb[i].elapsed_time(xe[i]) for i in range(K)]
+    # second pass: the library's events, recorded by the main kernel's dispatch
+    for i in range(K):
+        if flush is not None:
+            flush()
+        step(kb[i], ke[i])
+    torch.cuda.synchronize()
+    kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
     for e in kb + ke:
         hip.destroy(e)
     deterministic = None
@@ -313,11 +325,13 @@ def run_spmm(args, w, torch, lb, dev):
         deterministic = bool(np.array_equal(Y.cpu().numpy().view(np.uint8),
                                             Y_first.view(np.uint8)))
     mean_ms = statistics.fmean(ms)
+    mean_kern = statistics.fmean(kern_ms)
     Bc = spmm_bytes(w, k)
     # stream plans (partitions own whole rows) run the row-slot kernel, walk
     # plans the merge-slot kernel followed by the carry fix-up
     kern = "spmm_rows_kernel" if info["merge_reduce"] == "stream" else "spmm_merge_kernel"
     gbps = Bc / (mean_ms * 1e-3) / 1e9
+    kern_gbps = Bc / (mean_kern * 1e-3) / 1e9
     out = {
         "metric": METRIC_SPMM,
         "value": round(2.0 * w.nnz * k / (mean_ms * 1e-3) / 1e9, 3),
@@ -334,13 +348,15 @@ def run_spmm(args, w, torch, lb, dev):
         "achieved_GBps": round(gbps, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "compulsory_bytes": Bc,
-        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(gbps, 2),
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(kern_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel_ms": round(mean_ms, 5),
+                     "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
+                     "kernel_ms": round(mean_kern, 5),
                      "traffic": load_traffic("%s_k%d" % (args.workload, k), kern,
                                              SPMM_SOURCES),
-                     "timed": "events around the exec's launches (main kernel%s)"
-                              % ("" if info["merge_reduce"] == "stream" else " + carry fix-up")},
+                     "timed": "events recorded by the main kernel's dispatch%s"
+                              % ("" if info["merge_reduce"] == "stream"
+                                 else " (the carry fix-up after it is outside)")},
         "exec_ms_median": round(statistics.median(ms), 5),
         "deterministic": deterministic,
         "wall_ms_per_step": round(wall * 1e3 / K, 5),

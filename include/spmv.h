@@ -342,10 +342,12 @@ SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, i
 SPMV_API spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
                         double alpha, double beta, hipStream_t stream);
 
-/* spmv_exec that also records ev_begin just before and ev_end just after the
- * dominant kernel (the merge-path main kernel or the fused binned kernel), on
- * the same stream, so a caller can time that kernel alone. Either event may
- * be NULL. */
+/* spmv_exec that also has the dispatch of the dominant kernel (the
+ * merge-path main kernel, the fused binned kernel, the group-mapped or the
+ * row-grouped kernel) record ev_begin at its start and ev_end at its end, on
+ * the same stream, so a caller can time that kernel alone. With bins on
+ * several streams they bracket the fork and the join instead. Either event
+ * may be NULL; a call with M = 0 launches nothing and records neither. */
 SPMV_API spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y,
                                double alpha, double beta, hipStream_t stream,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
@@ -377,9 +379,11 @@ SPMV_API spmv_status_t spmv_exec_multi(spmv_plan_t plan, int64_t k, const void* 
                                        double beta, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
-/* spmv_exec_multi that also records ev_begin before its first launch and
- * ev_end after its last (main kernel and, for plans whose partitions cut
- * rows, the carry fix-up), on the same stream. Either event may be NULL. */
+/* spmv_exec_multi that also records ev_begin and ev_end on the same stream:
+ * for k <= 64 the main kernel's dispatch records them at its start and end
+ * (the carry fix-up that follows is outside); for k > 64 they bracket every
+ * launch of the call. Either event may be NULL; a call with k = 0 or M = 0
+ * launches nothing and records neither. */
 SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const void* X,
                                               int64_t ldx, void* Y, int64_t ldy, double alpha,
                                               double beta, void* workspace,

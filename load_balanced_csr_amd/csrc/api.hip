@@ -441,17 +441,20 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
   // power-law one, where a fifth do)
   a.part_order = !a.stream && p->dispatch_order == 2 && 2 * p->interior >= p->P ? p->part_order
                                                                                 : nullptr;
+  // one column block: the main kernel's dispatch records the events; more
+  // than one: they bracket the whole loop
+  const bool one = k <= kWave;
   hipError_t err = hipSuccess;
-  if (ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess)
+  if (!one && ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");
   for (int64_t kb = 0; kb < k; kb += kWave) {
     a.k = (int32_t)std::min<int64_t>(kWave, k - kb);
     a.X = static_cast<const V*>(X) + kb;
     a.Y = static_cast<V*>(Y) + kb;
-    if ((err = launch_spmm<V>(a, stream)) != hipSuccess)
+    if ((err = launch_spmm<V>(a, stream, one ? ev0 : nullptr, one ? ev1 : nullptr)) != hipSuccess)
       return hip_fail(err, "spmv_exec_multi launch");
   }
-  if (ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess)
+  if (!one && ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");
   return SPMV_SUCCESS;
 }

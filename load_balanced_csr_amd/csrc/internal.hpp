@@ -195,8 +195,9 @@ struct SpmmArgs {
 // nonzeros, plus quad alignment).
 constexpr int spmm_stage_cap(int T) { return T + T / 8 + 8; }
 
+// ev0/ev1 (either may be null) are recorded by the main kernel's dispatch
 template <typename V>
-hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s);
+hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 // ---- group-mapped exec ----------------------------------------------------------------
 constexpr int kGroupRowsPerWave = 256;  // rows (tiles) a group may take, per wavefront

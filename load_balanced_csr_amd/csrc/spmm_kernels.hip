@@ -406,60 +406,120 @@ __global__ __launch_bounds__(kBlock) void spmm_rows_kernel(const SpmmArgs<V> a) 
   }
 }
 
-// Y[r] += alpha * (sum of the carries of r), one wave per partition: the
-// wave holding the first carry of a row sums that row's carries in
-// partition order (they are contiguous) and updates the row once.
+// Y[r] += alpha * (sum of the carries of r) for every row that partitions
+// left open. kl lanes per partition (the power of two covering k, lane c
+// taking column c), so a wave holds G = 64 / kl consecutive partitions. A
+// row's carries are contiguous: a segmented scan over the wave's groups sums
+// each row's carries inside the chunk, and the group holding a segment's
+// last carry updates the row, unless the segment began in an earlier chunk
+// (that chunk's wave owns it). A segment owned here that runs past the chunk
+// is read on by the whole wave, kFixupSlices slices of G partitions per step
+// with every load of a step in flight together, until the step where it
+// ends; the groups' sums are then added across the wave. The order of the
+// adds depends only on the plan and k.
+constexpr int kFixupSlices = 8;
+
 template <typename V>
 __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a) {
   const int lane = lane_id();
-  const int p = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (p >= a.P) return;
-  const int r = a.carry_row[p];
-  if (r >= a.M || (p > 0 && a.carry_row[p - 1] == r)) return;
-  if (lane >= a.k) return;
-  V sum = V(0);
-  for (int q = p; q < a.P && a.carry_row[q] == r; ++q) sum += a.carry_vec[(int64_t)q * a.k + lane];
-  V* yp = a.Y + (int64_t)r * a.ldy + lane;
-  *yp = fma(a.alpha, sum, *yp);
+  const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));   // log2 kl
+  const int G = kWave >> lg;
+  const int c = lane & ((1 << lg) - 1);
+  const int g = lane >> lg;
+  const bool col = c < a.k;
+  const int64_t base =
+      ((int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) *
+      G;
+  if (base >= a.P) return;
+  const int64_t p = base + g;
+  const int key = p < a.P ? a.carry_row[p] : INT_MAX;
+  V s = p < a.P && col ? a.carry_vec[p * a.k + c] : V(0);
+  // inclusive segmented scan over the groups, same column
+  for (int d = 1; d < G; d <<= 1) {
+    const int src = lane - (d << lg);
+    const V up = __shfl(s, src < 0 ? lane : src, kWave);
+    const int kup = __shfl(key, src < 0 ? lane : src, kWave);
+    if (src >= 0 && kup == key) s += up;
+  }
+  const int dn = lane + (1 << lg);
+  int next = __shfl(key, dn < kWave ? dn : lane, kWave);
+  if (g == G - 1) next = base + G < a.P ? a.carry_row[base + G] : INT_MAX - 1;
+  const int key0 = __shfl(key, 0, kWave);
+  const int prev0 = base > 0 ? a.carry_row[base - 1] : -1;
+  const bool owned = !(key == key0 && prev0 == key0);
+  const bool tail = next != key;
+  if (tail && owned && key < a.M && col) {
+    V* yp = a.Y + (int64_t)key * a.ldy + c;
+    *yp = fma(a.alpha, s, *yp);
+  }
+  // the last group's segment, when it is owned here and goes on
+  const int last = (G - 1) << lg;
+  const int r = __shfl(key, last, kWave);
+  const bool cont = __shfl((int)(!tail && owned), last, kWave) != 0;
+  if (!cont || r >= a.M) return;
+  V extra = V(0);
+  for (int64_t q = base + G;; q += (int64_t)G * kFixupSlices) {
+    int kq[kFixupSlices];
+#pragma unroll
+    for (int u = 0; u < kFixupSlices; ++u) {
+      const int64_t pp = q + u * G + g;
+      kq[u] = pp < a.P ? a.carry_row[pp] : -1;
+    }
+    V v[kFixupSlices];
+#pragma unroll
+    for (int u = 0; u < kFixupSlices; ++u) {
+      const int64_t pp = q + u * G + g;
+      v[u] = kq[u] == r && col ? a.carry_vec[pp * a.k + c] : V(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kFixupSlices; ++u) extra += v[u];
+    // the row's carries are a prefix of the step: it goes on only if the
+    // step's last partition is still the row's
+    if (__ballot(kq[kFixupSlices - 1] == r) != ~0ull) break;
+  }
+  for (int d = 1 << lg; d < kWave; d <<= 1) extra += __shfl_xor(extra, d, kWave);
+  if (g != G - 1 || !col) return;
+  V* yp = a.Y + (int64_t)r * a.ldy + c;
+  *yp = fma(a.alpha, s + extra, *yp);
 }
 
 template <typename V, int KL, int VE>
-hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s) {
+hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
   const size_t lds = (size_t)kWavesPerBlock * (a.stream ? spmm_wave_lds(a.cap, sizeof(V))
                                                         : spmm_walk_wave_lds(a.cap, sizeof(V)));
   // bytes from X to the end of its last row's k columns
   const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
   const bool off32 = xspan < (1ull << 32);
+  const dim3 g(blocks), b(kBlock);
   if (a.stream && off32)
-    hipLaunchKernelGGL((spmm_rows_kernel<V, KL, VE, true>), dim3(blocks), dim3(kBlock), lds, s, a);
+    launch_timed(spmm_rows_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
   else if (a.stream)
-    hipLaunchKernelGGL((spmm_rows_kernel<V, KL, VE, false>), dim3(blocks), dim3(kBlock), lds, s, a);
+    launch_timed(spmm_rows_kernel<V, KL, VE, false>, g, b, lds, s, ev0, ev1, a);
   else if (off32)
-    hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, true>), dim3(blocks), dim3(kBlock), lds, s, a);
+    launch_timed(spmm_merge_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
   else
-    hipLaunchKernelGGL((spmm_merge_kernel<V, KL, VE, false>), dim3(blocks), dim3(kBlock), lds, s,
-                       a);
+    launch_timed(spmm_merge_kernel<V, KL, VE, false>, g, b, lds, s, ev0, ev1, a);
   return hipGetLastError();
 }
 
 // lanes per slot: the smallest power of two covering k columns, VE per lane
 template <typename V, int VE>
-hipError_t launch_ve(const SpmmArgs<V>& a, hipStream_t s) {
+hipError_t launch_ve(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int lanes = (a.k + VE - 1) / VE;
-  if (lanes <= 1) return launch_kl<V, 1, VE>(a, s);
-  if (lanes <= 2) return launch_kl<V, 2, VE>(a, s);
-  if (lanes <= 4) return launch_kl<V, 4, VE>(a, s);
-  if (lanes <= 8) return launch_kl<V, 8, VE>(a, s);
-  if (lanes <= 16) return launch_kl<V, 16, VE>(a, s);
-  if (lanes <= 32) return launch_kl<V, 32, VE>(a, s);
-  return launch_kl<V, 64, VE>(a, s);
+  if (lanes <= 1) return launch_kl<V, 1, VE>(a, s, ev0, ev1);
+  if (lanes <= 2) return launch_kl<V, 2, VE>(a, s, ev0, ev1);
+  if (lanes <= 4) return launch_kl<V, 4, VE>(a, s, ev0, ev1);
+  if (lanes <= 8) return launch_kl<V, 8, VE>(a, s, ev0, ev1);
+  if (lanes <= 16) return launch_kl<V, 16, VE>(a, s, ev0, ev1);
+  if (lanes <= 32) return launch_kl<V, 32, VE>(a, s, ev0, ev1);
+  return launch_kl<V, 64, VE>(a, s, ev0, ev1);
 }
 
 }  // namespace
 
 template <typename V>
-hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s) {
+hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.P <= 0 || a.k <= 0) return hipSuccess;
   if (a.k > kWave || a.cap < spmm_stage_cap(a.T)) return hipErrorInvalidValue;
   // 16-byte lanes when every row of X and Y starts 16-byte aligned and k
@@ -470,20 +530,26 @@ hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s) {
   const bool vec = a.k % VE == 0 && a.ldx % VE == 0 && a.ldy % VE == 0 && (xy & 15) == 0;
   hipError_t err;
   if (vec) {
-    err = launch_ve<V, VE>(a, s);
+    err = launch_ve<V, VE>(a, s, ev0, ev1);
   } else if constexpr (VE == 4) {
     const bool vec2 = a.k % 2 == 0 && a.ldx % 2 == 0 && a.ldy % 2 == 0 && (xy & 7) == 0;
-    err = vec2 ? launch_ve<V, 2>(a, s) : launch_ve<V, 1>(a, s);
+    err = vec2 ? launch_ve<V, 2>(a, s, ev0, ev1) : launch_ve<V, 1>(a, s, ev0, ev1);
   } else {
-    err = launch_ve<V, 1>(a, s);
+    err = launch_ve<V, 1>(a, s, ev0, ev1);
   }
   if (err != hipSuccess || a.stream || a.P <= 1) return err;
-  hipLaunchKernelGGL((spmm_fixup_kernel<V>), dim3((a.P + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(kBlock), 0, s, a);
+  // one wave per 64 / kl partitions
+  const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));
+  const int64_t waves = ((int64_t)a.P + (kWave >> lg) - 1) / (kWave >> lg);
+  hipLaunchKernelGGL((spmm_fixup_kernel<V>),
+                     dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
+                     0, s, a);
   return hipGetLastError();
 }
 
-template hipError_t launch_spmm<float>(const SpmmArgs<float>&, hipStream_t);
-template hipError_t launch_spmm<double>(const SpmmArgs<double>&, hipStream_t);
+template hipError_t launch_spmm<float>(const SpmmArgs<float>&, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+template hipError_t launch_spmm<double>(const SpmmArgs<double>&, hipStream_t, hipEvent_t,
+                                        hipEvent_t);
 
 }  // namespace spmv

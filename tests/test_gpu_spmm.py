@@ -193,3 +193,18 @@ def test_spmm_on_other_schedules(kind):
         Y = _run(m, plan, X, 1.5, beta, Y0)
         _check(Y, m, X, 1.5, beta, Y0, "%s k=%d" % (kind, k))
     plan.destroy()
+
+
+def test_carry_chains_around_step_sizes():
+    """Walk plan, rows whose carries run over n partitions for n just below,
+    at and above the fix-up's step sizes (8 slices of 64 / kl partitions,
+    kl the power of two covering k): chains that end inside a step, at its
+    last partition and one past it, for k = 1, 8, 33, 64."""
+    T = 512                                   # items_per_thread 8
+    Ls = []
+    for n in (7, 8, 9, 63, 64, 65, 511, 512, 513):
+        for d in (-1, 0, 1):
+            Ls += [T * n + d, 3, 0, 3]
+    L = np.asarray(Ls)
+    w = synth.random_csr(len(L), 300_000, L, 11)
+    _case(w, "merge8_walk", (1, 8, 33, 64))
