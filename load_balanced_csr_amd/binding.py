@@ -295,8 +295,8 @@ def spmv_exec_multi(plan: int, X: torch.Tensor, Y: torch.Tensor, alpha: float = 
     """Y = alpha * A X + beta * Y for the k = X.shape[1] columns of X (N x k)
     and Y (M x k), both row-major; ``workspace`` is a device tensor of at
     least spmv_spmm_workspace_size(plan, k) bytes (None when that is 0).
-    ev_begin / ev_end: optional hipEvent_t handles recorded around the
-    launches."""
+    ev_begin / ev_end: optional hipEvent_t handles, recorded by the main
+    kernel's dispatch for k <= 64 and around every launch for k > 64."""
     dts = (torch.float32, torch.float64)
     if X.shape[1] != Y.shape[1]:
         raise ValueError("X and Y must have the same number of columns")
