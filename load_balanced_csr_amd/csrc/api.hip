@@ -105,14 +105,14 @@ struct spmv_plan_st {
   const void* rg_val;
   int32_t group_waves;    // group-mapped schedule
   int32_t group_rows;
-  // per-bin launches (options.bin_streams): bins dealt over the caller's
-  // stream and n_side streams of the plan, forked and joined by events
   // walk kernel's dispatch order (options.dispatch_order): 1 partition
   // order, 2 column order through part_order (in owned_order)
   int32_t dispatch_order;
   int64_t interior;       // partitions no row ends in
   const int32_t* part_order;
   void* owned_order;
+  // per-bin launches (options.bin_streams): bins dealt over the caller's
+  // stream and n_side streams of the plan, forked and joined by events
   int32_t bin_streams;
   int32_t n_side;
   hipStream_t side[kMaxBins];
