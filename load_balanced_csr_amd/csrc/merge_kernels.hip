@@ -448,8 +448,8 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 
 // Adds alpha * sum(carries) to every row that partitions left open. One wave
 // handles 64 consecutive partitions; a row's carries are contiguous, so they
 // form a segment of equal keys. The wave that holds a segment's first carry
-// owns it and, if the segment runs past its 64 partitions, keeps reading
-// until the key changes.
+// owns it and, if the segment runs past its 64 partitions, keeps reading,
+// eight windows of 64 per step, until the step where the key changes.
 template <typename V>
 __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
     const int32_t* __restrict__ carry_row, const V* __restrict__ carry_val, int32_t P,
@@ -476,12 +476,25 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
   const int key63 = __shfl(key, kWave - 1, kWave);
   const bool cont63 = __shfl((int)(!tail && owned), kWave - 1, kWave);
   if (cont63 && key63 < M) {
+    // kFixupWindows windows of 64 partitions per step, every load of a step
+    // in flight together; the row's carries are a prefix of the step, so it
+    // goes on only if the step's last window is still all the row's
+    constexpr int kFixupWindows = 8;
     V extra = V(0);
-    for (int64_t q = base + kWave;; q += kWave) {
-      const int64_t pp = q + lane;
-      const bool match = pp < P && carry_row[pp] == key63;
-      extra += match ? carry_val[pp] : V(0);
-      if (__ballot(match) != ~0ull) break;
+    for (int64_t q = base + kWave;; q += kWave * kFixupWindows) {
+      int kq[kFixupWindows];
+#pragma unroll
+      for (int u = 0; u < kFixupWindows; ++u) {
+        const int64_t pp = q + kWave * u + lane;
+        kq[u] = pp < P ? carry_row[pp] : -1;
+      }
+      V v[kFixupWindows];
+#pragma unroll
+      for (int u = 0; u < kFixupWindows; ++u)
+        v[u] = kq[u] == key63 ? carry_val[q + kWave * u + lane] : V(0);
+#pragma unroll
+      for (int u = 0; u < kFixupWindows; ++u) extra += v[u];
+      if (__ballot(kq[kFixupWindows - 1] == key63) != ~0ull) break;
     }
     extra = group_sum<kWave>(extra);
     const V s63 = __shfl(s, kWave - 1, kWave);
