@@ -343,3 +343,29 @@ def test_read_probe_runs_and_leaves_the_sink():
     assert int(sink.item()) == 7
     with pytest.raises(lb.SpmvError):
         lb.spmv_read_probe(buf[1:], sink)       # 4-byte offset: misaligned
+
+
+@pytest.mark.parametrize("order", ["partition", "column"])
+def test_walk_carry_chains_around_step_sizes(order):
+    """Walk plan at T = 512: rows whose carries run over n partitions for n
+    just below, at and above 64 (one fix-up wave's chunk) and 64 + 512 (one
+    chunk and one continuation step of eight 64-partition windows), so a
+    row's chain ends inside a step, at its last partition and one past it."""
+    T = 512
+    Ls = []
+    for n in (63, 64, 65, 575, 576, 577, 1087, 1088, 1089):
+        for d in (-1, 0, 1):
+            Ls += [T * n + d, 2, 0, 5]
+    L = np.asarray(Ls)
+    w = synth.random_csr(len(L), 700_000, L, 13)
+    m = DevMatrix.of(w)
+    plan = m.plan(None, strategy="merge", merge_reduce="walk", items_per_thread=8,
+                  dispatch_order=order)
+    assert plan.info["items_per_wave"] == T
+    for alpha, beta in ((1.0, 0.0), (-0.5, 2.0)):
+        y0 = synth.uniform(w.M, 3, synth.S_Y, np.float32)
+        log("chains", order, "nnz=%d" % len(w.col_idx), alpha, beta)
+        y = run(plan, w.x, alpha, beta, y0)
+        check(y, w.row_ptr, w.col_idx, w.values, w.x, alpha, beta,
+              y0 if beta != 0 else None, "chains %s" % order)
+    plan.destroy()
