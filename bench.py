@@ -3,7 +3,12 @@
 
 One step = one spmv_exec (y = alpha*A*x + beta*y, the whole hot path: the
 merge-path kernel and, where rows cross partitions, its carry fix-up, or the
-fused binned kernel) over the workload resident in HBM. Before every step
+fused binned kernel) over the workload resident in HBM. The headline
+workload (``--workload``, default: the 32M-row banded decay matrix, the
+largest of the five) gives the JSON line's ``value``; the same steps are then
+run on the other four workloads, each reported under ``per_config`` with its
+own timing, roofline fraction, parity and CPU-oracle figures
+(``--no-per-config`` skips them). Before every step
 the caches are flushed on the same stream: a 1 GiB buffer is zero-filled,
 then another 1 GiB buffer is summed with ordinary (cached) loads. The fill
 alone would leave up to 256 MiB of dirty lines in the Infinity Cache whose
@@ -105,7 +110,7 @@ def load_traffic(workload: str, kernel: str, files=KERNEL_SOURCES):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
+def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr", allcores: bool = True):
     """The oracle as it stands, on one host core, repeated on the whole
     workload until the time budget is spent (at least once; the budget, 10 s
     by default, bounds the sample). Its result also checks the GPU's first
@@ -150,8 +155,10 @@ def cpu_baseline(w, budget_s: float, y_gpu, fmt: str = "csr"):
            "sample": "whole workload (%d nnz), %d runs, median %.1f ms, fp64 accumulation"
                      % (w.nnz, len(times), t * 1e3),
            "GBps": round(compulsory_bytes(w) / t / 1e9, 3)}
-    if fmt == "csr" and all_cpus:
+    if fmt == "csr" and all_cpus and allcores:
         res["allcores"] = cpu_allcores(w, all_cpus)
+    elif all_cpus:
+        os.sched_setaffinity(0, all_cpus)
     return res, bool(ok), worst
 
 
@@ -390,12 +397,270 @@ def run_spmm(args, w, torch, lb, dev):
         sys.exit(3)
 
 
+TARGET_FRAC = {"laplacian": 0.70, "banded": 0.70, "powerlaw": 0.50, "bimodal": 0.50}
+
+
+def kernel_of(info) -> str:
+    if info["strategy"] == "binned":
+        return "binned_spmv_kernel"
+    if info["strategy"] == "rgcsr":
+        return "rg_spmv_kernel"
+    if info["strategy"] == "group":
+        return "group_spmv_kernel"
+    return "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
+
+
+def timed_median(torch, flush, reps, fn):
+    """Median ms of fn() over reps calls, each flushed and event-timed."""
+    ts = []
+    for r in range(reps + 2):
+        if flush is not None:
+            flush()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        fn()
+        b_.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(a_.elapsed_time(b_))
+    return statistics.median(ts)
+
+
+def probes(lb, torch, flush, w, tensors, ipt, reps):
+    """The two measurement aids on this workload's own arrays: the gather
+    probe (col_idx read once, x gathered at every column) and the stream
+    probe (row_ptr, col_idx, values streamed in partitions of 64 * ipt units,
+    y written; no x), flushed and event-timed like the steps."""
+    rp, col, val, x = tensors
+    s = w.values.dtype.itemsize
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty(w.M, dtype=val.dtype, device="cuda")
+    g_ms = timed_median(torch, flush, reps, lambda: lb.spmv_gather_probe(col, x, sink))
+    ipt = ipt if ipt in (4, 8, 16) else 8
+    s_ms = timed_median(torch, flush, reps,
+                        lambda: lb.spmv_stream_probe(rp, col, val, y, ipt))
+    s_bytes = 4 * (w.M + 1) + w.nnz * (4 + s) + w.M * s
+    del y, sink
+    return {"gather_probe_ms": round(g_ms, 5),
+            "gather_probe_Ggathers_per_s": round(w.nnz / (g_ms * 1e-3) / 1e9, 2),
+            "stream_probe_ms": round(s_ms, 5),
+            "stream_probe_GBps": round(s_bytes / (s_ms * 1e-3) / 1e9, 1),
+            "stream_probe_items_per_wave": 64 * ipt,
+            "probes": "gather: col_idx read once and x gathered at every column in storage "
+                      "order, nothing else; stream: row_ptr/col_idx/values streamed in the "
+                      "plan's partition size and y written, no x (bytes: the compulsory ones "
+                      "minus x)"}
+
+
+def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
+    """Plan, parity, K flushed event-timed steps, the library's kernel events,
+    determinism, the probes and the CPU oracle for one workload. Returns the
+    full record (the headline's JSON line) and the per-config summary."""
+    dt = torch.float32 if w.values.dtype == np.float32 else torch.float64
+    rp = torch.from_numpy(w.row_ptr).to(dev)
+    col = torch.from_numpy(w.col_idx).to(dev)
+    val = torch.from_numpy(w.values).to(dev)
+    x = torch.from_numpy(w.x).to(dev)
+    y0 = torch.from_numpy(w.y0).to(dev) if w.y0 is not None else None
+    y = torch.empty(w.M, dtype=dt, device=dev)
+    torch.cuda.synchronize()
+
+    popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread,
+                 bin_streams=args.bin_streams)
+    if args.strategy == "rgcsr":
+        assert args.format == "csr", "the row-grouped copy is built from CSR"
+
+        def make_plan():
+            return lb.Plan.rgcsr(rp, col, val, (w.M, w.N), group_rows=args.rg_group)
+    elif args.format == "coo":
+        rows = torch.from_numpy(np.repeat(np.arange(w.M, dtype=np.int32),
+                                          np.diff(w.row_ptr))).to(dev)
+
+        def make_plan():
+            return lb.Plan.coo(rows, col, val, (w.M, w.N), **popts)
+    elif args.format == "transpose":
+        assert w.M == w.N, "the transposed benchmark uses square workloads"
+
+        def make_plan():
+            return lb.Plan.transpose(rp, col, val, (w.M, w.N), **popts)
+    else:
+        def make_plan():
+            return lb.Plan(rp, col, val, (w.M, w.N), **popts)
+    # planning cost (separate from the steps): median of 5 plan/destroy cycles
+    plan_ms = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        p_ = make_plan()
+        plan_ms.append((time.perf_counter() - t0) * 1e3)
+        p_.destroy()
+    plan = make_plan()
+    info = plan.info
+
+    # first exec on fresh inputs; checked against the oracle below
+    if y0 is not None:
+        y.copy_(y0)
+    else:
+        y.fill_(float("nan"))
+    plan(x, y, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    y_first = y.cpu().numpy()
+
+    hip = HipEvents()
+    kb = [hip.create() for _ in range(K)]
+    ke = [hip.create() for _ in range(K)]
+    xb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    xe = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    if y0 is not None:
+        y.copy_(y0)
+    for _ in range(W):
+        if flush is not None:
+            flush()
+        plan(x, y, w.alpha, w.beta)
+    # timed region: K steps, events around each exec only
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush()
+        xb[i].record()
+        plan(x, y, w.alpha, w.beta)
+        xe[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    exec_ms = [xb[i].elapsed_time(xe[i]) for i in range(K)]
+    # second pass: the library's events around its dominant kernel
+    for i in range(K):
+        if flush is not None:
+            flush()
+        lb.spmv_exec_events(plan.handle, x, y, w.alpha, w.beta, kb[i], ke[i])
+    torch.cuda.synchronize()
+    kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
+    for e in kb + ke:
+        hip.destroy(e)
+    # beta = 0: every call must reproduce the first one bit for bit
+    deterministic = None
+    if w.beta == 0.0:
+        deterministic = bool(np.array_equal(y.cpu().numpy().view(np.uint8),
+                                            y_first.view(np.uint8)))
+    # secondary figure: warm steps (no flush), events around each exec
+    warm = []
+    for i in range(min(K, 20)):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        plan(x, y, w.alpha, w.beta)
+        b_.record()
+        warm.append((a_, b_))
+    torch.cuda.synchronize()
+    warm_ms = [a_.elapsed_time(b_) for a_, b_ in warm]
+    plan.destroy()
+    pr = probes(lb, torch, flush, w, (rp, col, val, x), info["items_per_thread"], min(K, 10)) \
+        if args.format == "csr" and w.nnz > 0 else {}
+    del rp, col, val, x, y0, y
+    torch.cuda.empty_cache()
+
+    mean_exec = statistics.fmean(exec_ms)
+    mean_kern = statistics.fmean(kern_ms)
+    Bc = compulsory_bytes(w)
+    gflops = 2.0 * w.nnz / (mean_exec * 1e-3) / 1e9
+    gbps_exec = Bc / (mean_exec * 1e-3) / 1e9
+    kernel = kernel_of(info)
+    achieved = Bc / (mean_kern * 1e-3) / 1e9
+    traffic = load_traffic(args.workload if headline else w.name, kernel) \
+        if args.format in ("csr", "coo") else None
+    out = {
+        "metric": METRIC,
+        "value": round(gflops, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(mean_exec, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if dt == torch.float32 else "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": WORKLOADS[w.name],
+                   "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha, "beta": w.beta,
+                   "seed": w.seed, "format": args.format, "strategy": info["strategy"],
+                   "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
+                   "items_per_wave": info["items_per_wave"],
+                   "bin_streams": info["bin_streams"],
+                   "dispatch_order": info["dispatch_order"],
+                   "cache": "warm" if flush is None else
+                   "flushed before every step (1 GiB fill + 1 GiB cached read)"},
+        "achieved_GBps": round(gbps_exec, 2),
+        "pct_hbm_peak": round(100.0 * gbps_exec / HBM_PEAK_GBPS, 2),
+        "compulsory_bytes": Bc,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "kernel_ms": round(mean_kern, 5),
+                     # counters were taken on the CSR plan; a COO plan runs the
+                     # same kernels on the same matrix, a transposed one on A^T
+                     "traffic": traffic},
+        "exec_ms_median": round(statistics.median(exec_ms), 5),
+        "exec_ms_min": round(min(exec_ms), 5),
+        "exec_ms_max": round(max(exec_ms), 5),
+        "warm_exec_ms_median": round(statistics.median(warm_ms), 5),
+        "warm_pct_hbm_peak": round(100.0 * Bc / (statistics.median(warm_ms) * 1e-3) / 1e9
+                                   / HBM_PEAK_GBPS, 2),
+        "deterministic": deterministic,
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "plan_ms": round(statistics.median(plan_ms), 3),
+        "plan_allocs": info["plan_allocs"],
+        "plan_syncs": info["plan_syncs"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    out.update(pr)
+    if info["strategy"] == "rgcsr":
+        s_ = w.values.dtype.itemsize
+        G = info["rgcsr_group"]
+        out["config"]["rgcsr_group"] = G
+        out["rgcsr_stored"] = info["rgcsr_stored"]
+        # bytes the row-grouped layout itself moves: padded entries, row
+        # lengths, group bases, x and y (the metric keeps the CSR bytes)
+        out["format_bytes"] = (info["rgcsr_stored"] * (4 + s_) + 4 * w.M + 8 * (w.M // G + 2)
+                               + (w.N + w.M) * s_ + (w.M * s_ if w.beta != 0.0 else 0))
+    ok = True
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline: %s" % w.name, file=sys.stderr, flush=True)
+        out["cpu_baseline"], ok, worst = cpu_baseline(w, cpu_seconds, y_first, args.format,
+                                                      allcores=headline)
+        out["cpu_baseline"]["gpu_speedup"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
+        out["parity"] = {"ok": ok, "worst_over_bound": round(worst, 5),
+                         "checked": "first exec vs the oracle, every row"}
+    summary = {k: out[k] for k in ("dtype", "ms_per_step", "exec_ms_median", "achieved_GBps",
+                                   "pct_hbm_peak", "deterministic", "plan_ms", "plan_allocs",
+                                   "plan_syncs")}
+    summary.update({"M": w.M, "nnz": w.nnz, "GFLOPs": out["value"],
+                    "strategy": info["strategy"], "merge_reduce": info["merge_reduce"],
+                    "items_per_wave": info["items_per_wave"],
+                    "dispatch_order": info["dispatch_order"], "kernel": kernel,
+                    "kernel_ms": out["roofline"]["kernel_ms"],
+                    "roofline_frac": out["roofline"]["frac"],
+                    "target_frac": TARGET_FRAC.get(w.name),
+                    "traffic": traffic,
+                    "traffic_over_bytes": round(traffic / Bc, 3) if traffic else None})
+    for k in ("gather_probe_ms", "gather_probe_Ggathers_per_s", "stream_probe_ms",
+              "stream_probe_GBps"):
+        if k in out:
+            summary[k] = out[k]
+    if "parity" in out:
+        summary["parity_ok"] = out["parity"]["ok"]
+        summary["worst_over_bound"] = out["parity"]["worst_over_bound"]
+        summary["cpu_oracle_GFLOPs"] = out["cpu_baseline"]["value"]
+    return out, summary, ok and deterministic is not False
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="laplacian", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="banded", choices=list(WORKLOADS))
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time the headline workload only")
     ap.add_argument("--strategy", default="auto",
                     choices=["auto", "merge", "binned", "rgcsr", "group"])
     ap.add_argument("--rg-group", type=int, default=0,
@@ -436,191 +701,34 @@ def main():
     w = synth.CONFIGS[args.workload]()
     if args.rhs > 1:
         return run_spmm(args, w, torch, lb, dev)
-    dt = torch.float32 if w.values.dtype == np.float32 else torch.float64
-
-    rp = torch.from_numpy(w.row_ptr).to(dev)
-    col = torch.from_numpy(w.col_idx).to(dev)
-    val = torch.from_numpy(w.values).to(dev)
-    x = torch.from_numpy(w.x).to(dev)
-    y0 = torch.from_numpy(w.y0).to(dev) if w.y0 is not None else None
-    y = torch.empty(w.M, dtype=dt, device=dev)
-    torch.cuda.synchronize()
-
-    # planning cost (separate from the steps): median of 5 plan/destroy cycles
-    popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread,
-                 bin_streams=args.bin_streams)
-    if args.strategy == "rgcsr":
-        assert args.format == "csr", "the row-grouped copy is built from CSR"
-
-        def make_plan():
-            return lb.Plan.rgcsr(rp, col, val, (w.M, w.N), group_rows=args.rg_group)
-    elif args.format == "coo":
-        rows = torch.from_numpy(np.repeat(np.arange(w.M, dtype=np.int32),
-                                          np.diff(w.row_ptr))).to(dev)
-
-        def make_plan():
-            return lb.Plan.coo(rows, col, val, (w.M, w.N), **popts)
-    elif args.format == "transpose":
-        assert w.M == w.N, "the transposed benchmark uses square workloads"
-
-        def make_plan():
-            return lb.Plan.transpose(rp, col, val, (w.M, w.N), **popts)
-    else:
-        def make_plan():
-            return lb.Plan(rp, col, val, (w.M, w.N), **popts)
-    plan_ms = []
-    for _ in range(5):
-        t0 = time.perf_counter()
-        p = make_plan()
-        plan_ms.append((time.perf_counter() - t0) * 1e3)
-        p.destroy()
-    plan = make_plan()
-    info = plan.info
-
-    # first exec on fresh inputs; the cpu_baseline leg checks it against the oracle
-    if y0 is not None:
-        y.copy_(y0)
-    else:
-        y.fill_(float("nan"))
-    plan(x, y, w.alpha, w.beta)
-    torch.cuda.synchronize()
-    y_first = y.cpu().numpy()
-
     flush = None if args.no_flush else CacheFlush(torch, dev)
-    hip = HipEvents()
     K, W = args.steps, args.warmup
-    kb = [hip.create() for _ in range(K)]
-    ke = [hip.create() for _ in range(K)]
-    xb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    xe = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    if y0 is not None:
-        y.copy_(y0)
-
-    for _ in range(W):
-        if flush is not None:
-            flush()
-        plan(x, y, w.alpha, w.beta)
-    # timed region: K steps, events around each exec only
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        if flush is not None:
-            flush()
-        xb[i].record()
-        plan(x, y, w.alpha, w.beta)
-        xe[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    exec_ms = [xb[i].elapsed_time(xe[i]) for i in range(K)]
-
-    # second pass: the library's events around its dominant kernel
-    for i in range(K):
-        if flush is not None:
-            flush()
-        lb.spmv_exec_events(plan.handle, x, y, w.alpha, w.beta, kb[i], ke[i])
-    torch.cuda.synchronize()
-    kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
-    for e in kb + ke:
-        hip.destroy(e)
-    # beta = 0: every call must reproduce the first one bit for bit
-    deterministic = None
-    if w.beta == 0.0:
-        deterministic = bool(np.array_equal(y.cpu().numpy().view(np.uint8),
-                                            y_first.view(np.uint8)))
-
-    # secondary figure: warm steps (no flush), events around each exec
-    warm_ms = []
-    for i in range(min(K, 20)):
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        plan(x, y, w.alpha, w.beta)
-        b_.record()
-        warm_ms.append((a_, b_))
-    torch.cuda.synchronize()
-    warm_ms = [a_.elapsed_time(b_) for a_, b_ in warm_ms]
-
+    print("[bench] %s: %d rows, %d nonzeros" % (w.name, w.M, w.nnz), file=sys.stderr, flush=True)
+    out, summary, ok = spmv_leg(args, w, torch, lb, dev, flush, K, W, args.cpu_seconds, True)
+    del w
     # achievable streaming-read bandwidth on this GPU, same flush and timing
     ceiling = read_ceiling(lb, torch, flush)
-    mean_exec = statistics.fmean(exec_ms)
-    mean_kern = statistics.fmean(kern_ms)
-    Bc = compulsory_bytes(w)
-    gflops = 2.0 * w.nnz / (mean_exec * 1e-3) / 1e9
-    gbps_exec = Bc / (mean_exec * 1e-3) / 1e9
-    if info["strategy"] == "binned":
-        kernel = "binned_spmv_kernel"
-    elif info["strategy"] == "rgcsr":
-        kernel = "rg_spmv_kernel"
-    elif info["strategy"] == "group":
-        kernel = "group_spmv_kernel"
-    else:
-        kernel = "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
-    achieved = Bc / (mean_kern * 1e-3) / 1e9
-
-    out = {
-        "metric": METRIC,
-        "value": round(gflops, 3),
-        "unit": "GFLOP/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(mean_exec, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if dt == torch.float32 else "f64",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
-                   "M": w.M, "N": w.N, "nnz": w.nnz, "alpha": w.alpha, "beta": w.beta,
-                   "seed": w.seed, "format": args.format, "strategy": info["strategy"],
-                   "merge_reduce": info["merge_reduce"], "stream_lanes": info["stream_lanes"],
-                   "items_per_wave": info["items_per_wave"],
-                   "bin_streams": info["bin_streams"],
-                   "dispatch_order": info["dispatch_order"],
-                   "cache": "warm" if flush is None else
-                   "flushed before every step (1 GiB fill + 1 GiB cached read)"},
-        "achieved_GBps": round(gbps_exec, 2),
-        "pct_hbm_peak": round(100.0 * gbps_exec / HBM_PEAK_GBPS, 2),
-        "compulsory_bytes": Bc,
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "kernel_ms": round(mean_kern, 5),
-                     # counters were taken on the CSR plan; a COO plan runs the
-                     # same kernels on the same matrix, a transposed one on A^T
-                     "traffic": load_traffic(args.workload, kernel)
-                                if args.format in ("csr", "coo") else None},
-        "exec_ms_median": round(statistics.median(exec_ms), 5),
-        "exec_ms_min": round(min(exec_ms), 5),
-        "exec_ms_max": round(max(exec_ms), 5),
-        "warm_exec_ms_median": round(statistics.median(warm_ms), 5),
-        "warm_pct_hbm_peak": round(100.0 * Bc / (statistics.median(warm_ms) * 1e-3) / 1e9
-                                   / HBM_PEAK_GBPS, 2),
-        "read_ceiling_GBps": ceiling,
-        "pct_of_read_ceiling": round(100.0 * gbps_exec / ceiling, 2) if ceiling else None,
-        "deterministic": deterministic,
-        "wall_ms_per_step": round(wall * 1e3 / K, 5),
-        "plan_ms": round(statistics.median(plan_ms), 3),
-        "kernel_source_hash": kernel_source_hash(),
-    }
-    if info["strategy"] == "rgcsr":
-        s_ = w.values.dtype.itemsize
-        G = info["rgcsr_group"]
-        out["config"]["rgcsr_group"] = G
-        out["rgcsr_stored"] = info["rgcsr_stored"]
-        # bytes the row-grouped layout itself moves: padded entries, row
-        # lengths, group bases, x and y (the metric keeps the CSR bytes)
-        out["format_bytes"] = (info["rgcsr_stored"] * (4 + s_) + 4 * w.M + 8 * (w.M // G + 2)
-                               + (w.N + w.M) * s_ + (w.M * s_ if w.beta != 0.0 else 0))
-    plan.destroy()
-    ok = True
-    if not args.no_cpu:
-        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"], ok, worst = cpu_baseline(w, args.cpu_seconds, y_first, args.format)
-        out["cpu_baseline"]["gpu_speedup"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
-        out["parity"] = {"ok": ok, "worst_over_bound": round(worst, 5),
-                         "checked": "first exec vs the oracle, every row"}
+    out["read_ceiling_GBps"] = ceiling
+    out["pct_of_read_ceiling"] = round(100.0 * out["achieved_GBps"] / ceiling, 2) if ceiling else None
+    per = {args.workload: summary}
+    if not args.no_per_config and args.format == "csr" and args.strategy == "auto":
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            print("[bench] per-config leg: %s" % name, file=sys.stderr, flush=True)
+            try:
+                wk = synth.CONFIGS[name]()
+                _, summ, ok_k = spmv_leg(args, wk, torch, lb, dev, flush, K, W,
+                                         min(args.cpu_seconds, 2.0), False)
+                del wk
+                ok = ok and ok_k
+            except Exception as e:  # reported, and the run fails below
+                summ = {"error": "%s: %s" % (type(e).__name__, e)}
+                ok = False
+            per[name] = summ
+    out["per_config"] = {k: per[k] for k in WORKLOADS if k in per}
     print(json.dumps(out), flush=True)
-    if not ok or deterministic is False:
+    if not ok:
         sys.exit(3)
 
 

@@ -33,8 +33,10 @@
  *    stays allocated and *out handles are set to NULL. spmv_last_error()
  *    gives a thread-local text with the detail of the last failure.
  *  - beta == 0 means y is write-only: it is never read, so it may hold NaN.
- *  - Nothing here allocates after spmv_plan returns, except spmv_plan_* calls
- *    that are documented as copying to host.
+ *  - Nothing here allocates device memory after a plan is built; the
+ *    spmv_plan_copy_* calls copy to host memory the caller provides.
+ *  - Where no page defines a point (error codes, introspection), the
+ *    declaration says "library convention".
  *
  * Environment (read at plan time; an explicit option wins; for tuning and
  * tests, never needed for correct results):
@@ -66,8 +68,10 @@ extern "C" {
 
 typedef enum spmv_status {
   SPMV_SUCCESS = 0,
-  SPMV_ERR_INVALID_ARG = 1,    /* null/aliased pointer, negative size, bad enum */
-  SPMV_ERR_UNSUPPORTED = 2,    /* sizes beyond the int32 item model, see spmv_plan */
+  SPMV_ERR_INVALID_ARG = 1,    /* null/aliased pointer, negative size, nnz
+                                  beyond int32 indices, bad enum */
+  SPMV_ERR_UNSUPPORTED = 2,    /* M or N beyond int32 indices, or M + nnz
+                                  beyond the int32 item model (spmv_plan) */
   SPMV_ERR_ALLOC = 3,          /* a plan-time device allocation failed (the
                                   workspace, or a copy a plan_* call owns) */
   SPMV_ERR_HIP = 4,            /* a HIP launch or runtime call failed */
@@ -208,9 +212,19 @@ typedef struct spmv_plan_info {
                                  2 column (spmv_exec_multi follows it when at
                                  least half the partitions are interior) */
   int32_t interior_partitions;  /* partitions no row ends in */
+  int32_t plan_allocs;        /* device allocations the plan's construction
+                                 made (1 for spmv_plan / _ex / _coo) */
+  int32_t plan_syncs;         /* host synchronisations it made (1 for
+                                 spmv_plan / _ex / _coo) */
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).
+ * Sources: CSR as the RgCSR page, Section 3 and Fig. 1, defines it (row
+ * pointers ending in nnz, 32-bit indices); the plan's steps are the PPoPP'23
+ * page's Section 5.2.1 (merge-path split of rows + nonzeros, one binary
+ * search per partition) and the OpSparse page's Section 5.1 (row-length bins
+ * counted in shared memory, exclusive sum, scatter; one allocation for all
+ * metadata, no synchronisation mid-pipeline).
  *
  * row_ptr  device int32[M+1]; row_ptr[0] == 0, non-decreasing,
  *          row_ptr[M] == nnz (RgCSR page, Sec. 3). Checked on the device;
@@ -226,18 +240,25 @@ typedef struct spmv_plan_info {
  * between spmv_exec calls (the plan samples col_idx once to choose a kernel
  * variant; results never depend on that choice). row_ptr, col_idx and values
  * must be 16-byte aligned (any hipMalloc allocation is), else
- * SPMV_ERR_INVALID_ARG. The plan owns one device workspace, plus the column
- * dispatch order when it uses one and the streams and events of per-bin
- * launches when asked for; all are made here and freed by spmv_destroy.
+ * SPMV_ERR_INVALID_ARG. The plan owns one device workspace (all of its
+ * metadata, the column dispatch order included), plus the streams and events
+ * of per-bin launches when asked for; all are made here and freed by
+ * spmv_destroy.
  *
- * Work: row-length statistics and per-workgroup bin counts kept in LDS, an
- * exclusive scan of the bin counts, a stable scatter of row ids into bins,
- * one merge-path binary search per wavefront partition and the stream
- * workgroups' x windows; device-to-host copies of a small statistics block
- * with a stream synchronisation each (one to three: before choosing the
- * partition size, after the split, after a second split), and one more when
- * the column dispatch order is sorted. Returns SPMV_ERR_UNSUPPORTED if
- * M + nnz > 2^31 - 1. M == 0 or nnz == 0 is allowed. */
+ * Work, all enqueued on `stream` back to back: row-length statistics and
+ * per-workgroup bin counts kept in LDS, an exclusive scan of the bin counts,
+ * a stable scatter of row ids into bins, the partition size chosen on the
+ * device from the counted rows, one merge-path binary search per wavefront
+ * partition (a second pass at T = 256 when the device decides so), the
+ * stream workgroups' x windows, and for walk plans that take the column
+ * dispatch order the partitions' keys and a radix sort of them. Then one
+ * device-to-host copy of a small statistics block and one stream
+ * synchronisation: exactly one allocation and one synchronisation
+ * (spmv_plan_info reports both). Errors: SPMV_ERR_INVALID_ARG for a NULL
+ * out, a NULL or misaligned array, a negative size or nnz > 2^31 - 1;
+ * SPMV_ERR_UNSUPPORTED for M >= 2^31 - 1, N > 2^31 - 1 or
+ * M + nnz > 2^31 - 1; SPMV_ERR_ALLOC when the workspace allocation fails;
+ * SPMV_ERR_INVALID_MATRIX as above. M == 0 or nnz == 0 is allowed. */
 SPMV_API spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                         const int32_t* row_ptr, const int32_t* col_idx,
                         const void* values, spmv_dtype_t dtype,
@@ -264,8 +285,9 @@ SPMV_API spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int6
  *          call (it may be freed afterwards). Out of range or out of order
  *          gives SPMV_ERR_INVALID_MATRIX (checked on the device).
  * col_idx, values, dtype, options, stream: as for spmv_plan_ex (borrowed).
- * One more device allocation (the row offsets), freed by spmv_destroy; one
- * more stream synchronisation (the order check). */
+ * The row offsets live in the plan's one workspace; the order check joins
+ * the plan's statistics, so this too makes one allocation and one
+ * synchronisation. */
 SPMV_API spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                                      const int32_t* row_idx, const int32_t* col_idx,
                                      const void* values, spmv_dtype_t dtype,
@@ -283,11 +305,14 @@ SPMV_API spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int
  *
  * row_ptr, col_idx, values, dtype, options, stream: A as for spmv_plan_ex;
  * all three are read only during this call. The plan keeps its own copy of
- * A^T's indices and values (nnz * (4 + value size) bytes plus the offsets),
- * so later changes to A's values do not reach it. SPMV_ERR_INVALID_MATRIX
- * when row_ptr is malformed or a column index is outside [0, N). Scratch of
- * about 8 * nnz bytes plus the sort's is allocated and freed here; two more
- * stream synchronisations than spmv_plan_ex. */
+ * A^T's indices and values (nnz * (4 + value size) bytes plus the offsets,
+ * in its one workspace), so later changes to A's values do not reach it.
+ * SPMV_ERR_INVALID_MATRIX when row_ptr is malformed or a column index is
+ * outside [0, N). The sort's scratch (about 16 * nnz bytes) is a second
+ * allocation, freed before the call returns, after one more stream
+ * synchronisation (two allocations and two synchronisations in all). The
+ * sort is the library's own (sort_kernels.hip: LSD radix, 8-bit digits,
+ * stable). */
 SPMV_API spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N,
                                            int64_t nnz, const int32_t* row_ptr,
                                            const int32_t* col_idx, const void* values,
@@ -327,9 +352,16 @@ SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, i
                                        int32_t group_rows, hipStream_t stream);
 
 /* y = alpha * A * x + beta * y.
+ * Sources: the product of the RgCSR page, Section 3 (sequential CSR loop,
+ * 2 flops per stored entry) and the PPoPP'23 page, Section 4.3, Listing 3
+ * (each row's atoms summed, then y[row] written), load-balanced as its
+ * Section 5.2.1 and Sidebar 1 describe (merge-path partitions, segmented
+ * fix-up of rows cut between them); the alpha/beta form is the SpAMM page's
+ * background section (C = alpha A B + beta C).
  *
  * x  device array of N elements of the plan's dtype.
- * y  device array of M elements; read only when beta != 0. Must not alias x.
+ * y  device array of M elements; read only when beta != 0. The byte ranges
+ *    of x and y must not overlap (SPMV_ERR_INVALID_ARG).
  * alpha, beta are converted once to the plan's dtype.
  *
  * Asynchronous: only enqueues work on stream (with per-bin launches, event
@@ -342,7 +374,8 @@ SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, i
 SPMV_API spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
                         double alpha, double beta, hipStream_t stream);
 
-/* spmv_exec that also has the dispatch of the dominant kernel (the
+/* Library convention (measurement): spmv_exec that also has the dispatch of
+ * the dominant kernel (the
  * merge-path main kernel, the fused binned kernel, the group-mapped or the
  * row-grouped kernel) record ev_begin at its start and ev_end at its end, on
  * the same stream, so a caller can time that kernel alone. With bins on
@@ -391,12 +424,18 @@ SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const
                                               hipEvent_t ev_begin, hipEvent_t ev_end);
 
 /* Release the plan's workspace (hipFree, which synchronises the device).
- * NULL is a no-op; a destroyed or foreign handle gives SPMV_ERR_INVALID_PLAN
- * as long as its memory has not been reused. */
+ * The OpSparse page, Section 5.1, frees its metadata only at the end of the
+ * pipeline, since a free synchronises; the plan's memory is freed here and
+ * nowhere else. NULL is a no-op; a destroyed or foreign handle gives
+ * SPMV_ERR_INVALID_PLAN (library convention: live handles are tracked, so a
+ * stale one is never dereferenced). */
 SPMV_API spmv_status_t spmv_destroy(spmv_plan_t plan);
 
-/* Switch a live plan between MERGE and BINNED (both are always built), or to
- * RGCSR when the plan has the row-grouped copy (spmv_plan_rgcsr). */
+/* Switch a live plan between MERGE (PPoPP'23 page, Sec. 5.2.1) and BINNED
+ * (OpSparse page, Sec. 5.1; PPoPP'23 page, Secs. 4.2 and 5.2.2) -- both are
+ * always built -- or to RGCSR when the plan has the row-grouped copy (RgCSR
+ * page, Sec. 4). Library convention: SPMV_ERR_INVALID_ARG for an unknown
+ * strategy or RGCSR without the copy. */
 SPMV_API spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t strategy);
 
 /* Select the group-mapped schedule (SPMV_STRATEGY_GROUP) for a live plan:
@@ -407,19 +446,25 @@ SPMV_API spmv_status_t spmv_plan_set_strategy(spmv_plan_t plan, spmv_strategy_t 
 SPMV_API spmv_status_t spmv_plan_set_group(spmv_plan_t plan, int32_t group_waves,
                                            int32_t rows_per_group);
 
-/* Fill *info (host struct). */
+/* Library convention (introspection for tests and reports): fill *info
+ * (host struct) with the plan's choices, sizes and bin counts.
+ * SPMV_ERR_INVALID_PLAN for a dead handle, SPMV_ERR_INVALID_ARG for NULL. */
 SPMV_API spmv_status_t spmv_plan_info(spmv_plan_t plan, spmv_plan_info_t* info);
 
-/* Copy the merge-path split coordinates to host arrays of cap >= P+1 entries:
- * rows_host[p] = rows whose end item precedes diagonal min(p*T, M+nnz),
- * nnz_host[p] = nonzeros before it. Synchronous (stream-ordered on the null
- * stream after the plan's work). */
+/* Copy the merge-path split coordinates to host arrays of cap >= P+1 entries
+ * (PPoPP'23 page, Sec. 5.2.1: the coordinates of each worker's start on the
+ * merge path): rows_host[p] = rows whose end item precedes diagonal
+ * min(p*T, M+nnz), nnz_host[p] = nonzeros before it. Synchronous
+ * (stream-ordered on the null stream after the plan's work). Library
+ * convention: SPMV_ERR_INVALID_ARG for NULL buffers or cap < P + 1. */
 SPMV_API spmv_status_t spmv_plan_copy_splits(spmv_plan_t plan, int32_t* rows_host,
                                     int32_t* nnz_host, int64_t cap);
 
-/* Copy the binning result to host: bins_host[M] (row ids grouped by bin,
- * ascending within a bin; the identity when bin_identity is set) and
- * offsets_host[n_bins+1]. Synchronous. */
+/* Copy the binning result to host (OpSparse page, Sec. 5.1: the row ids
+ * grouped by bin and the bins' offsets from the exclusive sum):
+ * bins_host[M] (ascending within a bin; the identity when bin_identity is
+ * set) and offsets_host[n_bins+1]. Synchronous. Library convention:
+ * SPMV_ERR_INVALID_ARG for NULL buffers or bins_cap < M. */
 SPMV_API spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
                                   int64_t bins_cap, int64_t* offsets_host);
 
@@ -435,7 +480,35 @@ SPMV_API spmv_status_t spmv_plan_copy_bins(spmv_plan_t plan, int32_t* bins_host,
 SPMV_API spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink,
                                        hipStream_t stream);
 
+/* Measurement aid, not part of the SpMV: read col_idx[0..nnz) once, in
+ * storage order (16-byte loads, 1,024 indices per wavefront), and gather
+ * x[col_idx[k]] for every k, nothing else; the x-gather cost of an SpMV of
+ * that matrix, with its own column locality (the RgCSR page, Section 3,
+ * counts an x element per nonzero in its bandwidth estimate; caching x is
+ * what its results improve). col_idx 16-byte aligned; x of n_x elements
+ * (0 < n_x < 2^32) of `dtype`; columns are clamped to [0, n_x), so any
+ * col_idx is safe. `sink` (device int32) keeps the loads live. Asynchronous. */
+SPMV_API spmv_status_t spmv_gather_probe(const int32_t* col_idx, int64_t nnz, const void* x,
+                                         int64_t n_x, spmv_dtype_t dtype, void* sink,
+                                         hipStream_t stream);
+
+/* Measurement aid, not part of the SpMV: the merge-path kernels' access
+ * pattern without x. The M + nnz units are cut into P = ceil((M + nnz) / T)
+ * equal partitions, T = 64 * items_per_thread (4, 8 or 16); each 64-lane
+ * wavefront streams its partition's share of row_ptr, col_idx and values
+ * (16-byte non-temporal loads, all issued first, clamped to the arrays) and
+ * writes its share of y (M elements of `dtype`) with a value folded from the
+ * loads. Timed, it gives what plain streaming of the CSR arrays and y
+ * reaches on this device. Arrays 16-byte aligned; M > 0, M + nnz < 2^31.
+ * Asynchronous. */
+SPMV_API spmv_status_t spmv_stream_probe(const int32_t* row_ptr, const int32_t* col_idx,
+                                         const void* values, int64_t M, int64_t nnz,
+                                         spmv_dtype_t dtype, int32_t items_per_thread, void* y,
+                                         hipStream_t stream);
+
+/* Library convention: a fixed text for each status. */
 SPMV_API const char* spmv_status_string(spmv_status_t status);
+/* Library convention: the calling thread's text of its last failure. */
 SPMV_API const char* spmv_last_error(void);
 
 #ifdef __cplusplus

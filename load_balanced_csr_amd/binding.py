@@ -29,7 +29,8 @@ EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
             "spmv_plan_csc", "spmv_plan_rgcsr", "spmv_exec", "spmv_exec_events", "spmv_destroy",
             "spmv_plan_set_strategy", "spmv_plan_set_group", "spmv_plan_info",
             "spmv_plan_copy_splits",
-            "spmv_plan_copy_bins", "spmv_read_probe", "spmv_spmm_workspace_size",
+            "spmv_plan_copy_bins", "spmv_read_probe", "spmv_gather_probe",
+            "spmv_stream_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
             "spmv_last_error")
 
@@ -64,7 +65,8 @@ class PlanInfo(ctypes.Structure):
                 ("rgcsr_group", ctypes.c_int32), ("pad1", ctypes.c_int32),
                 ("rgcsr_stored", ctypes.c_int64), ("group_waves", ctypes.c_int32),
                 ("group_rows", ctypes.c_int32), ("dispatch_order", ctypes.c_int32),
-                ("interior_partitions", ctypes.c_int32)]
+                ("interior_partitions", ctypes.c_int32), ("plan_allocs", ctypes.c_int32),
+                ("plan_syncs", ctypes.c_int32)]
 
 
 _lib = None
@@ -99,6 +101,8 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
     lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
     lib.spmv_read_probe.argtypes = [p, i64, p, p]
+    lib.spmv_gather_probe.argtypes = [p, i64, p, i64, i32, p, p]
+    lib.spmv_stream_probe.argtypes = [p, p, p, i64, i64, i32, i32, p, p]
     lib.spmv_spmm_workspace_size.argtypes = [p, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.spmv_exec_multi.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p]
     lib.spmv_exec_multi_events.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p,
@@ -146,6 +150,49 @@ def _dtype_code(values: torch.Tensor) -> int:
     return SPMV_F32 if values.dtype == torch.float32 else SPMV_F64
 
 
+# Shape and value type of every plan made through this module (handle ->
+# (M, N, torch dtype)): the C ABI takes bare pointers and cannot see a
+# tensor's length, so the sizes are checked here, before any call that
+# would read or write past a short tensor.
+_plans: dict = {}
+_TORCH_DTYPE = {SPMV_F32: torch.float32, SPMV_F64: torch.float64}
+
+
+def _register(handle: int, M: int, N: int, dtype_code: int) -> int:
+    _plans[handle] = (int(M), int(N), _TORCH_DTYPE[dtype_code])
+    return handle
+
+
+def _plan_shape(plan: int):
+    """(M, N, dtype) of a plan; asks the library for handles made elsewhere
+    (an invalid handle raises there)."""
+    got = _plans.get(plan)
+    if got is not None:
+        return got
+    info = PlanInfo()
+    _check(load().spmv_plan_info(plan, ctypes.byref(info)), "spmv_plan_info")
+    return int(info.M), int(info.N), _TORCH_DTYPE[info.dtype]
+
+
+def _check_vec(t: torch.Tensor, name: str, n: int, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, the plan's values are %s" % (name, t.dtype, dtype))
+    if t.numel() < n:
+        raise ValueError("%s has %d elements, the plan needs %d" % (name, t.numel(), n))
+
+
+def _check_csr(row_ptr, col_idx, values, M: int, N: int) -> None:
+    if int(M) < 0 or int(N) < 0:
+        raise ValueError("negative shape (%d, %d)" % (M, N))
+    if row_ptr is not None and int(row_ptr.numel()) != int(M) + 1 and int(M) > 0:
+        raise ValueError("row_ptr has %d entries, M + 1 = %d" % (row_ptr.numel(), int(M) + 1))
+    if int(values.numel()) != int(col_idx.numel()):
+        raise ValueError("values (%d) and col_idx (%d) differ in length"
+                         % (values.numel(), col_idx.numel()))
+
+
 MERGE_REDUCE = {"auto": 0, "walk": 1, "stream": 2}
 DISPATCH_ORDER = {"auto": 0, "partition": 1, "column": 2}
 DISPATCH_ORDER_NAME = {1: "partition", 2: "column"}
@@ -183,6 +230,7 @@ def spmv_plan(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor
     """Plan handle for the CSR matrix (device int32 row_ptr/col_idx, fp32/fp64
     values). The tensors are borrowed: keep them alive until spmv_destroy."""
     lib = load()
+    _check_csr(row_ptr, col_idx, values, M, N)
     nnz = int(col_idx.numel())
     h = ctypes.c_void_p()
     args = (ctypes.byref(h), M, N, nnz, _dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
@@ -192,7 +240,7 @@ def spmv_plan(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor
         _check(lib.spmv_plan(*args, _stream(stream)), "spmv_plan")
     else:
         _check(lib.spmv_plan_ex(*args, ctypes.byref(options), _stream(stream)), "spmv_plan_ex")
-    return h.value
+    return _register(h.value, M, N, _dtype_code(values))
 
 
 def spmv_plan_coo(row_idx: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor, M: int,
@@ -204,6 +252,7 @@ def spmv_plan_coo(row_idx: torch.Tensor, col_idx: torch.Tensor, values: torch.Te
     nnz = int(col_idx.numel())
     if int(row_idx.numel()) != nnz:
         raise ValueError("row_idx and col_idx must have the same length")
+    _check_csr(None, col_idx, values, M, N)
     h = ctypes.c_void_p()
     _check(lib.spmv_plan_coo(ctypes.byref(h), M, N, nnz,
                              _dev_ptr(row_idx, "row_idx", (torch.int32,)),
@@ -212,13 +261,17 @@ def spmv_plan_coo(row_idx: torch.Tensor, col_idx: torch.Tensor, values: torch.Te
                              _dtype_code(values),
                              ctypes.byref(options) if options is not None else None,
                              _stream(stream)), "spmv_plan_coo")
-    return h.value
+    return _register(h.value, M, N, _dtype_code(values))
 
 
 def _plan_other(fn: str, ptr: torch.Tensor, idx: torch.Tensor, values: torch.Tensor, M: int,
                 N: int, options: Optional[PlanOptions], stream) -> int:
     lib = load()
     h = ctypes.c_void_p()
+    # fn's offsets cover the rows of the stored matrix: M for a transpose
+    # (A is M x N in CSR), N for CSC (A^T is N x M)
+    _check_csr(ptr, idx, values, M if fn == "spmv_plan_transpose" else N,
+               N if fn == "spmv_plan_transpose" else M)
     _check(getattr(lib, fn)(ctypes.byref(h), M, N, int(idx.numel()),
                             _dev_ptr(ptr, "offsets", (torch.int32,)),
                             _dev_ptr(idx, "indices", (torch.int32,)),
@@ -226,7 +279,10 @@ def _plan_other(fn: str, ptr: torch.Tensor, idx: torch.Tensor, values: torch.Ten
                             _dtype_code(values),
                             ctypes.byref(options) if options is not None else None,
                             _stream(stream)), fn)
-    return h.value
+    # the plan computes with A^T for a transpose (shape N x M), with A for CSC
+    if fn == "spmv_plan_transpose":
+        return _register(h.value, N, M, _dtype_code(values))
+    return _register(h.value, M, N, _dtype_code(values))
 
 
 def spmv_plan_transpose(row_ptr, col_idx, values, M: int, N: int,
@@ -247,6 +303,7 @@ def spmv_plan_rgcsr(row_ptr, col_idx, values, M: int, N: int, group_rows: int = 
     """Plan whose spmv_exec runs on a row-grouped CSR copy of A (groups of
     group_rows rows, 0 = 64); the copy is taken here."""
     lib = load()
+    _check_csr(row_ptr, col_idx, values, M, N)
     h = ctypes.c_void_p()
     _check(lib.spmv_plan_rgcsr(ctypes.byref(h), M, N, int(col_idx.numel()),
                                _dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
@@ -254,13 +311,16 @@ def spmv_plan_rgcsr(row_ptr, col_idx, values, M: int, N: int, group_rows: int = 
                                _dev_ptr(values, "values", (torch.float32, torch.float64)),
                                _dtype_code(values), int(group_rows), _stream(stream)),
            "spmv_plan_rgcsr")
-    return h.value
+    return _register(h.value, M, N, _dtype_code(values))
 
 
 def spmv_exec(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
               beta: float = 0.0, stream=None) -> None:
     """y = alpha * A x + beta * y, enqueued on the stream (asynchronous)."""
     dts = (torch.float32, torch.float64)
+    M, N, dt = _plan_shape(plan)
+    _check_vec(x, "x", N, dt)
+    _check_vec(y, "y", M, dt)
     _check(load().spmv_exec(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts), float(alpha),
                             float(beta), _stream(stream)), "spmv_exec")
 
@@ -269,6 +329,9 @@ def spmv_exec_events(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float, 
                      ev_begin: int, ev_end: int, stream=None) -> None:
     """spmv_exec recording two hipEvent_t handles around the dominant kernel."""
     dts = (torch.float32, torch.float64)
+    M, N, dt = _plan_shape(plan)
+    _check_vec(x, "x", N, dt)
+    _check_vec(y, "y", M, dt)
     _check(load().spmv_exec_events(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts),
                                    float(alpha), float(beta), _stream(stream), ev_begin, ev_end),
            "spmv_exec_events")
@@ -298,6 +361,14 @@ def spmv_exec_multi(plan: int, X: torch.Tensor, Y: torch.Tensor, alpha: float = 
     ev_begin / ev_end: optional hipEvent_t handles, recorded by the main
     kernel's dispatch for k <= 64 and around every launch for k > 64."""
     dts = (torch.float32, torch.float64)
+    M, N, dt = _plan_shape(plan)
+    for t, name, rows in ((X, "X", N), (Y, "Y", M)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % name)
+        if t.dtype != dt:
+            raise TypeError("%s has dtype %s, the plan's values are %s" % (name, t.dtype, dt))
+        if t.dim() != 2 or t.shape[0] < rows:
+            raise ValueError("%s must be 2-D with at least %d rows" % (name, rows))
     if X.shape[1] != Y.shape[1]:
         raise ValueError("X and Y must have the same number of columns")
     ldx, ldy = _row_major(X, "X"), _row_major(Y, "Y")
@@ -321,8 +392,37 @@ def spmv_read_probe(data: torch.Tensor, sink: torch.Tensor, stream=None) -> None
                                   sink.data_ptr(), _stream(stream)), "spmv_read_probe")
 
 
+def spmv_gather_probe(col_idx: torch.Tensor, x: torch.Tensor, sink: torch.Tensor,
+                      stream=None) -> None:
+    """Read col_idx once and gather x at every column, nothing else
+    (measurement aid, see the header)."""
+    if not (col_idx.is_cuda and x.is_cuda and sink.is_cuda and sink.dtype == torch.int32
+            and col_idx.dtype == torch.int32 and x.dtype in (torch.float32, torch.float64)):
+        raise ValueError("spmv_gather_probe needs device tensors: int32 col_idx, fp32/fp64 x, "
+                         "int32 sink")
+    _check(load().spmv_gather_probe(col_idx.data_ptr(), col_idx.numel(), x.data_ptr(), x.numel(),
+                                    _dtype_code(x), sink.data_ptr(), _stream(stream)),
+           "spmv_gather_probe")
+
+
+def spmv_stream_probe(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor,
+                      y: torch.Tensor, items_per_thread: int, stream=None) -> None:
+    """Stream the CSR arrays in partitions of 64 * items_per_thread units and
+    write y, with no x and no arithmetic (measurement aid, see the header)."""
+    M = int(row_ptr.numel()) - 1
+    _check_csr(row_ptr, col_idx, values, M, 1)
+    _check_vec(y, "y", M, values.dtype)
+    _check(load().spmv_stream_probe(_dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
+                                    _dev_ptr(col_idx, "col_idx", (torch.int32,)),
+                                    _dev_ptr(values, "values", (torch.float32, torch.float64)),
+                                    M, int(col_idx.numel()), _dtype_code(values),
+                                    int(items_per_thread), y.data_ptr(), _stream(stream)),
+           "spmv_stream_probe")
+
+
 def spmv_destroy(plan: Optional[int]) -> None:
     _check(load().spmv_destroy(plan), "spmv_destroy")
+    _plans.pop(plan, None)
 
 
 def spmv_plan_set_strategy(plan: int, strategy: str) -> None:
@@ -353,7 +453,8 @@ def spmv_plan_info(plan: int) -> dict:
             "bin_count": list(info.bin_count[:nb]), "max_row_len": info.max_row_len,
             "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes,
             "rgcsr_group": info.rgcsr_group, "rgcsr_stored": info.rgcsr_stored,
-            "group_waves": info.group_waves, "group_rows": info.group_rows}
+            "group_waves": info.group_waves, "group_rows": info.group_rows,
+            "plan_allocs": info.plan_allocs, "plan_syncs": info.plan_syncs}
 
 
 def spmv_plan_copy_splits(plan: int):

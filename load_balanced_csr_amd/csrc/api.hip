@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <new>
 #include <string>
@@ -92,8 +93,6 @@ struct spmv_plan_st {
   void* carry_val;
   int32_t* bins;
   int32_t* win_span;
-  void* owned_row_ptr;   // COO plans: the row offsets derived from row_idx
-  void* owned_entries;   // transposed plans: the column indices and values of A^T
   // row-grouped copy (spmv_plan_rgcsr): metadata and entries, own allocations
   void* owned_rg_meta;
   void* owned_rg_data;
@@ -106,11 +105,13 @@ struct spmv_plan_st {
   int32_t group_waves;    // group-mapped schedule
   int32_t group_rows;
   // walk kernel's dispatch order (options.dispatch_order): 1 partition
-  // order, 2 column order through part_order (in owned_order)
+  // order, 2 column order through part_order (in the workspace)
   int32_t dispatch_order;
   int64_t interior;       // partitions no row ends in
   const int32_t* part_order;
-  void* owned_order;
+  // device allocations and host synchronisations the plan's construction made
+  int32_t plan_allocs;
+  int32_t plan_syncs;
   // per-bin launches (options.bin_streams): bins dealt over the caller's
   // stream and n_side streams of the plan, forked and joined by events
   int32_t bin_streams;
@@ -121,11 +122,6 @@ struct spmv_plan_st {
 };
 
 namespace {
-
-// The stream kernel's x window for these parameters (0: none).
-int window_bytes(int ipt, int vbytes, int wpb) {
-  return stream_window_bytes(ipt, vbytes, wpb);
-}
 
 // Live plans. A handle is only dereferenced after it is found here, so a
 // destroyed or foreign handle is rejected without touching its memory.
@@ -220,39 +216,6 @@ hipError_t create_bin_streams(spmv_plan_st* p) {
     p->n_side = i + 1;
   }
   return err;
-}
-
-// Column dispatch order of the walk kernel: the partitions stably sorted by
-// the column of their middle nonzero. A workgroup takes four consecutive
-// entries of the order -- with long rows, parts of different rows over the
-// same columns, so its waves share x lines in L1 -- and XCD x the x-th
-// eighth of the workgroups (the kernel's XCD remap), so each XCD's L2 serves
-// a narrow range of x. Plan time only: keys, a radix sort, one sync.
-hipError_t build_column_order(spmv_plan_st* p, hipStream_t stream) {
-  const int64_t P = p->P;
-  int bits = 1;
-  while (bits < 31 && (int64_t(1) << bits) < p->N) ++bits;
-  size_t temp_bytes = 0;
-  hipError_t err = sort_columns(nullptr, &temp_bytes, nullptr, nullptr, nullptr, P, bits, stream);
-  if (err != hipSuccess) return err;
-  const size_t ints = align256(sizeof(int32_t) * P);
-  if ((err = hipMalloc(&p->owned_order, 3 * ints + align256(temp_bytes))) != hipSuccess) {
-    p->owned_order = nullptr;
-    return err;
-  }
-  char* b = static_cast<char*>(p->owned_order);
-  int32_t* order = reinterpret_cast<int32_t*>(b);
-  int32_t* keys = reinterpret_cast<int32_t*>(b + ints);
-  int32_t* keys_out = reinterpret_cast<int32_t*>(b + 2 * ints);
-  void* temp = b + 3 * ints;
-  if ((err = launch_group_keys(p->split_nz, p->col_idx, (int32_t)P, 1, keys, stream)) !=
-          hipSuccess ||
-      (err = sort_columns(temp, &temp_bytes, keys, keys_out, order, P, bits, stream)) !=
-          hipSuccess ||
-      (err = hipStreamSynchronize(stream)) != hipSuccess)
-    return err;
-  p->part_order = order;
-  return hipSuccess;
 }
 
 // Rows per group of the group-mapped schedule: one LDS chunk of nonzeros
@@ -514,30 +477,40 @@ spmv_status_t spmv_exec_multi(spmv_plan_t p, int64_t k, const void* X, int64_t l
                                 stream, nullptr, nullptr);
 }
 
-spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
-                           const int32_t* row_ptr, const int32_t* col_idx, const void* values,
-                           spmv_dtype_t dtype, const spmv_plan_options_t* options,
-                           hipStream_t stream) {
-  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  if (M < 0 || N < 0 || nnz < 0)
-    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
-                (long long)N, (long long)nnz);
-  if (dtype != SPMV_F32 && dtype != SPMV_F64)
-    return fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (M > 0 && !row_ptr) return fail(SPMV_ERR_INVALID_ARG, "row_ptr is NULL");
-  if (nnz > 0 && (!col_idx || !values))
-    return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
-  if (M == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "M = 0 needs nnz = 0");
-  if ((reinterpret_cast<uintptr_t>(row_ptr) | reinterpret_cast<uintptr_t>(col_idx) |
-       reinterpret_cast<uintptr_t>(values)) & 15)
-    return fail(SPMV_ERR_INVALID_ARG, "row_ptr, col_idx and values must be 16-byte aligned");
-  if (N == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "N = 0 needs nnz = 0");
-  if (nnz > kInt32Max || M >= kInt32Max || N > kInt32Max)
-    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
-  if (M + nnz > kInt32Max)
-    return fail(SPMV_ERR_UNSUPPORTED, "M + nnz = %lld exceeds 2^31 - 1 work units",
-                (long long)(M + nnz));
+}  // extern "C"
+
+namespace {
+
+// ---- plan construction ----------------------------------------------------------
+// Every plan is built by one routine: one workspace allocation, the planning
+// kernels enqueued back to back (the decisions that depend on the counted
+// rows are taken on the device, see plan_choose_kernel), one read-back of the
+// statistics block and one stream synchronisation. The OpSparse page,
+// Section 5.1, keeps all metadata in one allocation and avoids frees and
+// synchronisations in the middle of its pipeline; this follows it.
+
+// What one build starts from: CSR (row_ptr) or row-sorted COO (row_idx),
+// plus an optional region of the workspace the caller fills in `prologue`
+// (launched on the stream after the statistics block is cleared and before
+// any kernel reads the matrix).
+struct PlanSource {
+  int64_t M = 0, N = 0, nnz = 0;
+  const int32_t* row_ptr = nullptr;
+  bool coo = false;                  // derive row_ptr from row_idx (read by this call only)
+  const int32_t* row_idx = nullptr;  // may be null when nnz = 0
+  const int32_t* col_idx = nullptr;
+  const void* values = nullptr;
+  spmv_dtype_t dtype = SPMV_F32;
+  size_t extra_bytes = 0;
+  std::function<hipError_t(spmv_plan_st*, void* extra, hipStream_t)> prologue;
+  int32_t allocs_before = 0;   // allocations the caller made for this plan
+};
+
+spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
+                         const spmv_plan_options_t* options, hipStream_t stream,
+                         void** extra_out) {
+  const int64_t M = src.M, N = src.N, nnz = src.nnz;
+  const spmv_dtype_t dtype = src.dtype;
   spmv_status_t st = check_options(options);
   if (st != SPMV_SUCCESS) return st;
 
@@ -548,21 +521,21 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   p->N = N;
   p->nnz = nnz;
   p->dtype = dtype;
-  p->row_ptr = row_ptr;
-  p->col_idx = col_idx;
-  p->values = values;
+  p->row_ptr = src.row_ptr;
+  p->col_idx = src.col_idx;
+  p->values = src.values;
   p->xcd_remap = env_int("SPMV_XCD_REMAP", 1) != 0;
+  p->plan_allocs = src.allocs_before;
 
-  const int forced = options ? options->strategy : 0;
-  // items per lane: given, or chosen from the row lengths once they are
-  // counted (the partition arrays are sized for the smallest candidate, 4)
-  p->ipt = options && options->items_per_thread ? options->items_per_thread
-                                                 : env_int("SPMV_ITEMS_PER_THREAD", 0);
-  const bool auto_ipt = p->ipt != 4 && p->ipt != 7 && p->ipt != 8 && p->ipt != 16;
-  if (auto_ipt) p->ipt = 4;
-  p->T = kWave * p->ipt;
+  // items per lane: given (options, then environment), else chosen on the
+  // device from the row lengths; the partition arrays are sized for the
+  // smallest partition the plan may choose (T = 256 unless forced)
+  int forced_ipt = options && options->items_per_thread ? options->items_per_thread
+                                                         : env_int("SPMV_ITEMS_PER_THREAD", 0);
+  if (forced_ipt != 4 && forced_ipt != 7 && forced_ipt != 8 && forced_ipt != 16) forced_ipt = 0;
   const int64_t W = M + nnz;
-  p->P = (W + p->T - 1) / p->T;
+  const int64_t t_min = (int64_t)kWave * (forced_ipt ? forced_ipt : 4);
+  const int64_t p_max = (W + t_min - 1) / t_min;
 
   if (options && options->n_bins > 0) {
     p->edges.n_bins = options->n_bins;
@@ -575,30 +548,60 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   }
   const bool validate_cols =
       (options && options->validate_columns) || env_int("SPMV_VALIDATE", 0) != 0;
+  int reduce_req = options ? options->merge_reduce : 0;
+  if (reduce_req == 0) {
+    const char* e = std::getenv("SPMV_MERGE_REDUCE");
+    if (e && !std::strcmp(e, "walk")) reduce_req = 1;
+    else if (e && !std::strcmp(e, "stream")) reduce_req = 2;
+  }
+  int order_req = options ? options->dispatch_order : 0;
+  if (order_req == 0) {
+    const char* e = std::getenv("SPMV_DISPATCH_ORDER");
+    if (e && !std::strcmp(e, "partition")) order_req = 1;
+    else if (e && !std::strcmp(e, "column")) order_req = 2;
+  }
+  const size_t vs = dtype == SPMV_F32 ? 4 : 8;
+  PlanCtl ctl;
+  std::memset(&ctl, 0, sizeof ctl);
+  ctl.M = M;
+  ctl.N = N;
+  ctl.nnz = nnz;
+  ctl.vbytes = (int32_t)vs;
+  ctl.forced_ipt = forced_ipt;
+  ctl.wide_x = N * (int64_t)vs > kXcdL2Bytes;
+  ctl.reduce_req = reduce_req;
+  ctl.order_req = order_req;
+  int key_bits = 1;
+  while (key_bits < 31 && (int64_t(1) << key_bits) < N) ++key_bits;
 
   // ---- the one workspace allocation -------------------------------------------
-  const size_t vs = dtype == SPMV_F32 ? 4 : 8;
   const int64_t n_wg = (M + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  const int64_t groups_max = (p_max + kWavesPerBlock - 1) / kWavesPerBlock;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t o_stats = take(sizeof(int64_t) * kStatCount);
   const size_t o_counts = take(sizeof(int32_t) * kMaxBins * n_wg);
   const size_t o_wgmax = take(sizeof(int32_t) * n_wg);
   const size_t o_wgemp = take(sizeof(int32_t) * n_wg);
-  const size_t o_srow = take(sizeof(int32_t) * (p->P + 1));
-  const size_t o_snz = take(sizeof(int32_t) * (p->P + 1));
-  const size_t o_rb = take(sizeof(int32_t) * 2 * (p->P + 1));
-  const size_t o_crow = take(sizeof(int32_t) * p->P);
-  const size_t o_cval = take(vs * p->P);
+  const size_t o_srow = take(sizeof(int32_t) * (p_max + 1));
+  const size_t o_snz = take(sizeof(int32_t) * (p_max + 1));
+  const size_t o_rb = take(sizeof(int32_t) * 2 * (p_max + 1));
+  const size_t o_crow = take(sizeof(int32_t) * std::max<int64_t>(p_max, 1));
+  const size_t o_cval = take(vs * std::max<int64_t>(p_max, 1));
   const size_t o_bins = take(sizeof(int32_t) * M);
-  const int64_t win_ints = (int64_t)kWinTable * ((p->P + kWavesPerBlock - 1) / kWavesPerBlock);
-  const size_t o_wins = take(sizeof(int32_t) * win_ints);
+  const size_t o_wins = take(sizeof(int32_t) * kWinTable * groups_max);
+  const size_t o_order = take(sizeof(int32_t) * std::max<int64_t>(p_max, 1));
+  const size_t o_order2 = take(sizeof(int32_t) * std::max<int64_t>(p_max, 1));
+  const size_t o_sort = take(radix_sort_temp_bytes(std::max<int64_t>(p_max, 1)));
+  const size_t o_rowptr = src.coo ? take(sizeof(int32_t) * (M + 1)) : 0;
+  const size_t o_extra = src.extra_bytes ? take(src.extra_bytes) : 0;
   p->ws_bytes = off;
   if (env_int("SPMV_TEST_FAIL_ALLOC", 0)) {
     delete p;
     return fail(SPMV_ERR_ALLOC, "workspace allocation failed (forced by SPMV_TEST_FAIL_ALLOC)");
   }
   hipError_t err = hipMalloc(&p->ws, p->ws_bytes);
+  ++p->plan_allocs;
   if (err != hipSuccess) {
     delete p;
     (void)hipGetLastError();
@@ -616,98 +619,87 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   p->carry_val = base + o_cval;
   p->bins = reinterpret_cast<int32_t*>(base + o_bins);
   p->win_span = reinterpret_cast<int32_t*>(base + o_wins);
+  int32_t* order0 = reinterpret_cast<int32_t*>(base + o_order);
+  int32_t* order1 = reinterpret_cast<int32_t*>(base + o_order2);
+  void* extra = src.extra_bytes ? base + o_extra : nullptr;
+  int32_t* coo_row_ptr = src.coo ? reinterpret_cast<int32_t*>(base + o_rowptr) : nullptr;
+  if (src.coo) p->row_ptr = coo_row_ptr;
+  const int32_t* row_ptr = p->row_ptr;
 
-  // ---- planning kernels, one read-back, one synchronisation ---------------------
-  int64_t host_stats[kStatCount] = {0};
   auto bail = [&](spmv_status_t s) {
     (void)hipStreamSynchronize(stream);
     (void)hipFree(p->ws);
-    if (p->owned_order) (void)hipFree(p->owned_order);
     release_bin_streams(p);
     delete p;
     return s;
   };
+
+  // ---- planning kernels, back to back --------------------------------------------
+  int sort_result = 0;
   if ((err = launch_clear_stats(p->stats, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: clear"));
+  if (src.prologue && (err = src.prologue(p, extra, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: prologue"));
+  if (src.coo &&
+      (err = launch_coo_row_ptr(src.row_idx, nnz, M, coo_row_ptr, p->stats, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: COO row offsets"));
   if ((err = launch_bin_count(row_ptr, M, nnz, p->edges, p->counts, p->wg_max, p->wg_empty,
-                              p->stats, stream)) != hipSuccess)
-    return bail(hip_fail(err, "plan: bin count"));
-  if ((err = launch_bin_scan(M, p->edges, p->counts, p->wg_max, p->wg_empty, p->stats,
-                             stream)) != hipSuccess)
-    return bail(hip_fail(err, "plan: bin scan"));
-  if ((err = launch_bin_scatter(row_ptr, M, p->edges, p->counts, p->stats, p->bins, stream)) !=
-      hipSuccess)
-    return bail(hip_fail(err, "plan: bin scatter"));
-  if (auto_ipt) {
-    // row lengths decide T: short rows (every row <= 32, mean < 12) take
-    // T = 256; otherwise T = 1024 for fp32 (stream reduction up to rows of
-    // 128, walk beyond) and T = 512 for fp64 (its staging and window need
-    // twice the LDS per unit)
-    if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
-                              stream)) != hipSuccess ||
-        (err = hipStreamSynchronize(stream)) != hipSuccess)
-      return bail(hip_fail(err, "plan: row-length read-back"));
-    if (!(host_stats[kStatError] & 1)) {
-      const int64_t max_len = host_stats[kStatMaxLen];
-      const double avg = M > 0 ? (double)nnz / (double)M : 0.0;
-      if (max_len <= 32 && avg < 12.0) p->ipt = 4;
-      else p->ipt = dtype == SPMV_F32 ? 16 : 8;
-      p->T = kWave * p->ipt;
-      p->P = (W + p->T - 1) / p->T;
-    }
-  }
-  // merge-path splits at T and the stream workgroups' x windows (their
-  // counters in the stats block start from zero)
-  auto split_and_spans = [&]() -> hipError_t {
-    hipError_t e = hipSuccess;
-    if (p->P > 0)
-      e = launch_split_search(row_ptr, M, nnz, p->T, p->P, p->split_row, p->split_nz,
-                              p->row_bounds, p->stats, stream);
-    if (e == hipSuccess && p->P > 0 && nnz > 0)
-      e = launch_window_spans(row_ptr, col_idx, p->split_row, p->P, nnz, N, (int32_t)vs,
-                              kWavesPerBlock, window_bytes(p->ipt, (int)vs, kWavesPerBlock),
-                              p->win_span, win_ints, p->stats, stream);
-    return e;
-  };
-  auto read_stats = [&]() -> hipError_t {
-    hipError_t e = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats,
-                                  hipMemcpyDeviceToHost, stream);
-    return e == hipSuccess ? hipStreamSynchronize(stream) : e;
-  };
-  if ((err = split_and_spans()) != hipSuccess) return bail(hip_fail(err, "plan: split search"));
+                              p->stats, stream)) != hipSuccess ||
+      (err = launch_bin_scan(M, p->edges, p->counts, p->wg_max, p->wg_empty, p->stats,
+                             stream)) != hipSuccess ||
+      (err = launch_bin_scatter(row_ptr, M, p->edges, p->counts, p->stats, p->bins, stream)) !=
+          hipSuccess)
+    return bail(hip_fail(err, "plan: bins"));
   if (validate_cols &&
-      (err = launch_check_columns(col_idx, nnz, N, p->stats, stream)) != hipSuccess)
+      (err = launch_check_columns(p->col_idx, nnz, N, p->stats, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: column check"));
-  if ((err = read_stats()) != hipSuccess) return bail(hip_fail(err, "plan: stats copy"));
-  // Rows that cross partitions, an x larger than one XCD's L2 and most
-  // partitions holding row ends (not the insides of long rows): the gathers
-  // are bound by how many L1 misses are in flight, and T = 256 runs twice the
-  // waves per CU of T = 1024 (measured on MI355X: -4% to -29% on power-law
-  // and skewed matrices of 4M columns; no gain where the column order keeps
-  // long rows' x in L2). Split again at T = 256.
-  if (auto_ipt && p->ipt > 4 && !(host_stats[kStatError] & 3) &&
-      host_stats[kStatMaxLen] > p->T / 8 && N * (int64_t)vs > kXcdL2Bytes &&
-      2 * host_stats[kStatInterior] < p->P) {
-    p->ipt = 4;
-    p->T = kWave * p->ipt;
-    p->P = (W + p->T - 1) / p->T;
-    if ((err = hipMemsetAsync(p->stats + kStatWindowFits, 0, 3 * sizeof(int64_t), stream)) !=
-            hipSuccess ||
-        (err = hipMemsetAsync(p->stats + kStatInterior, 0, sizeof(int64_t), stream)) !=
-            hipSuccess ||
-        (err = split_and_spans()) != hipSuccess || (err = read_stats()) != hipSuccess)
-      return bail(hip_fail(err, "plan: split search at T = 256"));
-  }
+  if ((err = launch_plan_choose(ctl, p->stats, 0, stream)) != hipSuccess ||
+      (err = launch_split_search(row_ptr, M, nnz, p_max, 0, p->split_row, p->split_nz,
+                                 p->row_bounds, p->stats, stream)) != hipSuccess ||
+      (err = launch_plan_choose(ctl, p->stats, 1, stream)) != hipSuccess ||
+      (err = launch_split_search(row_ptr, M, nnz, p_max, 1, p->split_row, p->split_nz,
+                                 p->row_bounds, p->stats, stream)) != hipSuccess ||
+      (err = launch_plan_choose(ctl, p->stats, 2, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: merge-path split"));
+  if ((err = launch_window_spans(ctl, row_ptr, p->col_idx, p->split_row, p_max, p->win_span,
+                                 p->stats, stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: x windows"));
+  // column dispatch order (walk plans that chose it; every launch checks
+  // the flag): keys in the carry-row array, sorted with their partition ids
+  // (ping-pong through the carry-value array, which has room for P ints)
+  if (p_max > 0 &&
+      ((err = launch_partition_keys(p->split_nz, p->col_idx, p_max, p->stats, p->carry_row,
+                                    stream)) != hipSuccess ||
+       (err = radix_sort_pairs(p->carry_row, nullptr, order0,
+                               reinterpret_cast<int32_t*>(p->carry_val), order1, base + o_sort,
+                               p_max, p->stats + kStatParts, p->stats + kStatOrder, key_bits,
+                               stream, &sort_result)) != hipSuccess))
+    return bail(hip_fail(err, "plan: column dispatch order"));
 
-  if (host_stats[kStatError] & 1)
+  // ---- the one read-back and synchronisation -----------------------------------------
+  int64_t host_stats[kStatCount] = {0};
+  if ((err = hipMemcpyAsync(host_stats, p->stats, sizeof host_stats, hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess ||
+      (err = hipStreamSynchronize(stream)) != hipSuccess)
+    return bail(hip_fail(err, "plan: statistics read-back"));
+  ++p->plan_syncs;
+
+  if (host_stats[kStatError] & kErrCooRows)
+    return bail(fail(SPMV_ERR_INVALID_MATRIX,
+                     "COO row indices must lie in [0, M) and be sorted in non-decreasing order"));
+  if (host_stats[kStatError] & kErrRowPtr)
     return bail(fail(SPMV_ERR_INVALID_MATRIX,
                      "row_ptr is not a CSR row pointer array (row_ptr[0] = 0, "
                      "non-decreasing, row_ptr[M] = nnz)"));
-  if (host_stats[kStatError] & 2)
+  if (host_stats[kStatError] & kErrColumn)
     return bail(fail(SPMV_ERR_INVALID_MATRIX, "a column index is outside [0, N)"));
 
+  p->ipt = (int32_t)host_stats[kStatIpt];
+  p->T = kWave * p->ipt;
+  p->P = host_stats[kStatParts];
   p->max_len = host_stats[kStatMaxLen];
   p->n_empty = host_stats[kStatEmpty];
+  p->interior = host_stats[kStatInterior];
   for (int b = 0; b <= p->edges.n_bins; ++b)
     p->bin_offset[b] = M > 0 ? host_stats[kStatBinOffset + b] : 0;
   p->identity = M == 0 || host_stats[kStatNonEmptyBins] <= 1;
@@ -723,17 +715,11 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
   // merge-path reduction: stream when every row fits an eighth of a partition
   {
     const bool eligible = p->max_len <= p->T / 8;
-    int req = options ? options->merge_reduce : 0;
-    if (req == 0) {
-      const char* e = std::getenv("SPMV_MERGE_REDUCE");
-      if (e && !std::strcmp(e, "walk")) req = 1;
-      else if (e && !std::strcmp(e, "stream")) req = 2;
-    }
-    if (req == 2 && !eligible)
+    if (reduce_req == 2 && !eligible)
       return bail(fail(SPMV_ERR_INVALID_ARG,
                        "stream reduction needs every row <= T/8 = %d entries (longest: %lld)",
                        p->T / 8, (long long)p->max_len));
-    p->merge_reduce = req ? req : (eligible ? 2 : 1);
+    p->merge_reduce = reduce_req ? reduce_req : (eligible ? 2 : 1);
     int g = options ? options->stream_lanes : 0;
     if (g == 0) g = env_int("SPMV_STREAM_LANES", 0);
     if (g == 0) {
@@ -744,7 +730,6 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     }
     if (g < 1 || g > 64 || (g & (g - 1))) g = 1;
     p->stream_lanes = g;
-    // x window: where at least half of the stream workgroups' column spans fit
     int xw = options ? options->x_window : 0;
     if (xw == 0) {
       const int e = env_int("SPMV_X_WINDOW", -1);
@@ -757,50 +742,88 @@ spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
     const int64_t S = host_stats[kStatWindowSamples];
     const int64_t F1 = host_stats[kStatWindowFits], FM = host_stats[kStatWindowFitsMulti];
     const bool room = p->merge_reduce == 2 && nnz > 0 &&
-                      window_bytes(p->ipt, (int)vs, kWavesPerBlock) > 0;
+                      stream_window_bytes(p->ipt, (int)vs, kWavesPerBlock) > 0 && S > 0;
     p->x_window = 0;
     if (room && xw == 2) p->x_window = FM > F1 ? kWinIntervals : 1;
-    else if (room && xw == 0 && S > 0 && 2 * F1 >= S) p->x_window = 1;
-    else if (room && xw == 0 && S > 0 && 2 * FM >= S) p->x_window = kWinIntervals;
+    else if (room && xw == 0 && 2 * F1 >= S) p->x_window = 1;
+    else if (room && xw == 0 && 2 * FM >= S) p->x_window = kWinIntervals;
   }
-  // walk kernel's dispatch order
-  {
-    int d = options ? options->dispatch_order : 0;
-    if (d == 0) {
-      const char* e = std::getenv("SPMV_DISPATCH_ORDER");
-      if (e && !std::strcmp(e, "partition")) d = 1;
-      else if (e && !std::strcmp(e, "column")) d = 2;
-    }
-    // auto: column order where at least an eighth of the partitions lie
-    // inside one row and the longest row covers under a quarter of the
-    // columns (long, sparse rows: a partition's gathers span a wide range of
-    // x; measured -9% to -13% on such inputs, +2% to +6% on others)
-    p->interior = host_stats[kStatInterior];
-    if (d == 0) d = 8 * p->interior >= p->P && 4 * p->max_len < N ? 2 : 1;
-    p->dispatch_order = p->merge_reduce == 1 && p->P > 0 && nnz > 0 ? d : 1;
-    if (p->dispatch_order == 2 && (err = build_column_order(p, stream)) != hipSuccess)
-      return bail(hip_fail(err, "plan: column dispatch order"));
-  }
+  // walk kernel's dispatch order, as chosen and sorted on the device
+  p->dispatch_order = host_stats[kStatOrder] ? 2 : 1;
+  p->part_order = p->dispatch_order == 2 ? (sort_result ? order1 : order0) : nullptr;
   p->group_waves = 4;
   p->group_rows = default_group_rows(p, 4);
-  p->strategy = forced ? forced : choose_strategy(p);
+  p->strategy = options && options->strategy ? options->strategy : choose_strategy(p);
   if (env_int("SPMV_LOG", 0))
     std::fprintf(stderr,
                  "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d xwin=%d T=%d "
-                 "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu order=%s\n",
+                 "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu order=%s allocs=%d "
+                 "syncs=%d\n",
                  (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
                  p->strategy == SPMV_STRATEGY_MERGE ? "merge" : p->strategy == SPMV_STRATEGY_GROUP ? "group" : "binned",
                  p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->x_window, p->T,
                  (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
                  p->edges.n_bins, p->identity, p->ws_bytes,
-                 p->dispatch_order == 2 ? "column" : "partition");
+                 p->dispatch_order == 2 ? "column" : "partition", p->plan_allocs, p->plan_syncs);
   p->magic = kMagic;
   {
     std::lock_guard<std::mutex> lk(g_plans_mu);
     g_plans.insert(p);
   }
+  if (extra_out) *extra_out = extra;
   *out = p;
   return SPMV_SUCCESS;
+}
+
+// Argument checks shared by the CSR, COO and transposed entry points.
+spmv_status_t check_sizes(int64_t M, int64_t N, int64_t nnz, spmv_dtype_t dtype) {
+  if (M < 0 || N < 0 || nnz < 0)
+    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
+                (long long)N, (long long)nnz);
+  if (dtype != SPMV_F32 && dtype != SPMV_F64)
+    return fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((M == 0 || N == 0) && nnz != 0)
+    return fail(SPMV_ERR_INVALID_ARG, "M = 0 or N = 0 needs nnz = 0");
+  if (nnz > kInt32Max)
+    return fail(SPMV_ERR_INVALID_ARG, "nnz = %lld exceeds the int32 index range",
+                (long long)nnz);
+  if (M >= kInt32Max || N > kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "M = %lld or N = %lld beyond int32 indices",
+                (long long)M, (long long)N);
+  if (M + nnz > kInt32Max)
+    return fail(SPMV_ERR_UNSUPPORTED, "M + nnz = %lld exceeds 2^31 - 1 work units",
+                (long long)(M + nnz));
+  return SPMV_SUCCESS;
+}
+
+bool aligned16(const void* a) { return (reinterpret_cast<uintptr_t>(a) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+spmv_status_t spmv_plan_ex(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
+                           const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                           spmv_dtype_t dtype, const spmv_plan_options_t* options,
+                           hipStream_t stream) {
+  if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  spmv_status_t st = check_sizes(M, N, nnz, dtype);
+  if (st != SPMV_SUCCESS) return st;
+  if (M > 0 && !row_ptr) return fail(SPMV_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (nnz > 0 && (!col_idx || !values))
+    return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
+  if (!aligned16(row_ptr) || !aligned16(col_idx) || !aligned16(values))
+    return fail(SPMV_ERR_INVALID_ARG, "row_ptr, col_idx and values must be 16-byte aligned");
+  PlanSource src;
+  src.M = M;
+  src.N = N;
+  src.nnz = nnz;
+  src.row_ptr = row_ptr;
+  src.col_idx = col_idx;
+  src.values = values;
+  src.dtype = dtype;
+  return plan_build(out, src, options, stream, nullptr);
 }
 
 spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
@@ -815,47 +838,24 @@ spmv_status_t spmv_plan_coo(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                             hipStream_t stream) {
   if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (M < 0 || N < 0 || nnz < 0)
-    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
-                (long long)N, (long long)nnz);
-  if (nnz > 0 && !row_idx) return fail(SPMV_ERR_INVALID_ARG, "row_idx is NULL");
-  if (M == 0 && nnz != 0) return fail(SPMV_ERR_INVALID_ARG, "M = 0 needs nnz = 0");
-  if (nnz > kInt32Max || M >= kInt32Max)
-    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
-  // row offsets (M + 1) and a flag, in one allocation the plan keeps
-  const size_t off_flag = align256(sizeof(int32_t) * (size_t)(M + 1));
-  void* buf = nullptr;
-  hipError_t err = hipMalloc(&buf, off_flag + 256);
-  if (err != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(SPMV_ERR_ALLOC, "hipMalloc for the COO row offsets failed: %s",
-                hipGetErrorString(err));
-  }
-  int32_t* row_ptr = static_cast<int32_t*>(buf);
-  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(buf) + off_flag);
-  int32_t host_flag = 0;
-  if ((err = hipMemsetAsync(flag, 0, sizeof(int32_t), stream)) != hipSuccess ||
-      (err = launch_coo_row_ptr(row_idx, nnz, M, row_ptr, flag, stream)) != hipSuccess ||
-      (err = hipMemcpyAsync(&host_flag, flag, sizeof host_flag, hipMemcpyDeviceToHost,
-                            stream)) != hipSuccess ||
-      (err = hipStreamSynchronize(stream)) != hipSuccess) {
-    (void)hipStreamSynchronize(stream);
-    (void)hipFree(buf);
-    return hip_fail(err, "spmv_plan_coo: row offsets");
-  }
-  if (host_flag) {
-    (void)hipFree(buf);
-    return fail(SPMV_ERR_INVALID_MATRIX,
-                "COO row indices must lie in [0, M) and be sorted in non-decreasing order");
-  }
-  spmv_status_t st = spmv_plan_ex(out, M, N, nnz, row_ptr, col_idx, values, dtype, options,
-                                  stream);
-  if (st != SPMV_SUCCESS) {
-    (void)hipFree(buf);
-    return st;
-  }
-  (*out)->owned_row_ptr = buf;
-  return SPMV_SUCCESS;
+  spmv_status_t st = check_sizes(M, N, nnz, dtype);
+  if (st != SPMV_SUCCESS) return st;
+  if (nnz > 0 && (!row_idx || !col_idx || !values))
+    return fail(SPMV_ERR_INVALID_ARG, "row_idx, col_idx or values is NULL");
+  if (!aligned16(col_idx) || !aligned16(values))
+    return fail(SPMV_ERR_INVALID_ARG, "col_idx and values must be 16-byte aligned");
+  // the row offsets are derived into the plan's workspace; row_idx is read
+  // only by this call's kernels (not at all when nnz = 0: every offset is 0)
+  PlanSource src;
+  src.M = M;
+  src.N = N;
+  src.nnz = nnz;
+  src.coo = true;
+  src.row_idx = row_idx;
+  src.col_idx = col_idx;
+  src.values = values;
+  src.dtype = dtype;
+  return plan_build(out, src, options, stream, nullptr);
 }
 
 spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
@@ -864,84 +864,79 @@ spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N, int64_
                                   const spmv_plan_options_t* options, hipStream_t stream) {
   if (!out) return fail(SPMV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (M < 0 || N < 0 || nnz < 0)
-    return fail(SPMV_ERR_INVALID_ARG, "negative size (M=%lld N=%lld nnz=%lld)", (long long)M,
-                (long long)N, (long long)nnz);
-  if (dtype != SPMV_F32 && dtype != SPMV_F64)
-    return fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  spmv_status_t st = check_sizes(N, M, nnz, dtype);
+  if (st != SPMV_SUCCESS) return st;
   if (M > 0 && !row_ptr) return fail(SPMV_ERR_INVALID_ARG, "row_ptr is NULL");
   if (nnz > 0 && (!col_idx || !values))
     return fail(SPMV_ERR_INVALID_ARG, "col_idx or values is NULL");
-  if ((M == 0 || N == 0) && nnz != 0)
-    return fail(SPMV_ERR_INVALID_ARG, "M = 0 or N = 0 needs nnz = 0");
-  if (nnz > kInt32Max || M >= kInt32Max || N >= kInt32Max)
-    return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond int32 indices");
+  if (M >= kInt32Max) return fail(SPMV_ERR_UNSUPPORTED, "M beyond int32 indices");
   const size_t vs = dtype == SPMV_F32 ? 4 : 8;
   int bits = 1;
   while (bits < 31 && (int64_t(1) << bits) < N) ++bits;
-  // owned by the plan: A^T's column indices (rows of A) and values
-  const size_t o_val = align256(sizeof(int32_t) * (size_t)nnz);
-  void* owned = nullptr;
-  hipError_t err = hipMalloc(&owned, o_val + align256(vs * (size_t)nnz) + 256);
+  // scratch for this call (freed before it returns): the sort's keys and
+  // positions in two ping-pong pairs, its counts, and a flag for A's row_ptr
+  const size_t n1 = std::max<int64_t>(nnz, 1);
+  const size_t o_k1 = align256(sizeof(int32_t) * n1);
+  const size_t o_v0 = o_k1 + align256(sizeof(int32_t) * n1);
+  const size_t o_v1 = o_v0 + align256(sizeof(int32_t) * n1);
+  const size_t o_flag = o_v1 + align256(sizeof(int32_t) * n1);
+  const size_t o_temp = o_flag + 256;
+  void* scratch = nullptr;
+  hipError_t err = hipMalloc(&scratch, o_temp + radix_sort_temp_bytes((int64_t)n1));
   if (err != hipSuccess) {
     (void)hipGetLastError();
-    return fail(SPMV_ERR_ALLOC, "hipMalloc for the transposed entries failed: %s",
-                hipGetErrorString(err));
-  }
-  int32_t* col_t = static_cast<int32_t*>(owned);
-  void* val_t = static_cast<char*>(owned) + o_val;
-  // scratch for this call: sorted keys (A^T's row indices), positions, a
-  // flag and the sort's own scratch
-  size_t sort_bytes = 0;
-  if (nnz > 0 &&
-      (err = sort_columns(nullptr, &sort_bytes, col_idx, nullptr, nullptr, nnz, bits, stream)) !=
-          hipSuccess) {
-    (void)hipFree(owned);
-    return hip_fail(err, "spmv_plan_transpose: sort size");
-  }
-  const size_t o_perm = align256(sizeof(int32_t) * (size_t)nnz);
-  const size_t o_flag = o_perm + align256(sizeof(int32_t) * (size_t)nnz);
-  const size_t o_sort = o_flag + 256;
-  void* scratch = nullptr;
-  if ((err = hipMalloc(&scratch, o_sort + align256(sort_bytes) + 256)) != hipSuccess) {
-    (void)hipGetLastError();
-    (void)hipFree(owned);
     return fail(SPMV_ERR_ALLOC, "hipMalloc for the transpose scratch failed: %s",
                 hipGetErrorString(err));
   }
-  int32_t* keys_t = static_cast<int32_t*>(scratch);
-  int32_t* perm = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + o_perm);
-  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + o_flag);
-  void* sort_tmp = static_cast<char*>(scratch) + o_sort;
-  auto release = [&](spmv_status_t st) {
+  char* sb = static_cast<char*>(scratch);
+  int32_t* k0 = reinterpret_cast<int32_t*>(sb);
+  int32_t* k1 = reinterpret_cast<int32_t*>(sb + o_k1);
+  int32_t* v0 = reinterpret_cast<int32_t*>(sb + o_v0);
+  int32_t* v1 = reinterpret_cast<int32_t*>(sb + o_v1);
+  int32_t* flag = reinterpret_cast<int32_t*>(sb + o_flag);
+  int which = 0;
+  auto release = [&](spmv_status_t s2) {
     (void)hipStreamSynchronize(stream);
     (void)hipFree(scratch);
-    if (st != SPMV_SUCCESS) (void)hipFree(owned);
-    return st;
+    return s2;
   };
-  int32_t host_flag = 0;
-  if (M > 0 &&
-      ((err = hipMemsetAsync(flag, 0, sizeof(int32_t), stream)) != hipSuccess ||
-       (err = launch_csr_check(row_ptr, M, nnz, flag, stream)) != hipSuccess ||
-       (err = hipMemcpyAsync(&host_flag, flag, sizeof host_flag, hipMemcpyDeviceToHost,
-                             stream)) != hipSuccess ||
-       (err = hipStreamSynchronize(stream)) != hipSuccess))
-    return release(hip_fail(err, "spmv_plan_transpose: row_ptr check"));
-  if (host_flag)
-    return release(fail(SPMV_ERR_INVALID_MATRIX,
-                        "row_ptr must start at 0, never decrease and end at nnz"));
-  if (nnz > 0 &&
-      ((err = sort_columns(sort_tmp, &sort_bytes, col_idx, keys_t, perm, nnz, bits, stream)) !=
-           hipSuccess ||
-       (err = launch_transpose_gather(row_ptr, M, perm, values, (int)vs, nnz, col_t, val_t,
-                                      stream)) != hipSuccess))
-    return release(hip_fail(err, "spmv_plan_transpose: transpose"));
-  // A^T as COO sorted by its rows (A's columns); out-of-range columns of A
-  // show up there as out-of-range or unsorted rows
-  spmv_status_t st = spmv_plan_coo(out, N, M, nnz, keys_t, col_t, val_t, dtype, options, stream);
-  if (st != SPMV_SUCCESS) return release(st);
-  (*out)->owned_entries = owned;
-  return release(SPMV_SUCCESS);
+  // A's row_ptr check, and the stable sort of (column, position)
+  if ((err = hipMemsetAsync(flag, 0, sizeof(int32_t), stream)) != hipSuccess ||
+      (M > 0 && (err = launch_csr_check(row_ptr, M, nnz, flag, stream)) != hipSuccess) ||
+      (nnz > 0 && (err = hipMemcpyAsync(k0, col_idx, sizeof(int32_t) * nnz,
+                                        hipMemcpyDeviceToDevice, stream)) != hipSuccess) ||
+      (nnz > 0 && (err = radix_sort_pairs(k0, nullptr, v0, k1, v1, sb + o_temp, nnz, nullptr,
+                                          nullptr, bits, stream, &which)) != hipSuccess))
+    return release(hip_fail(err, "spmv_plan_transpose: sort"));
+  const int32_t* keys_t = which ? k1 : k0;
+  const int32_t* perm = which ? v1 : v0;
+  // A^T as COO sorted by its rows (A's columns); its column indices and
+  // values live in the plan's workspace. Out-of-range columns of A show up
+  // as out-of-range or unsorted rows of A^T.
+  const size_t o_val = align256(sizeof(int32_t) * n1);
+  PlanSource src;
+  src.M = N;
+  src.N = M;
+  src.nnz = nnz;
+  src.coo = true;
+  src.row_idx = keys_t;
+  src.dtype = dtype;
+  src.extra_bytes = o_val + align256(vs * n1);
+  src.allocs_before = 1;
+  src.prologue = [&](spmv_plan_st* p, void* extra, hipStream_t s) -> hipError_t {
+    int32_t* col_t = static_cast<int32_t*>(extra);
+    void* val_t = static_cast<char*>(extra) + o_val;
+    p->col_idx = col_t;
+    p->values = val_t;
+    hipError_t e = launch_fold_flag(flag, kErrRowPtr, p->stats, s);
+    if (e == hipSuccess && nnz > 0)
+      e = launch_transpose_gather(row_ptr, M, perm, values, (int)vs, nnz, col_t, val_t, s);
+    return e;
+  };
+  st = plan_build(out, src, options, stream, nullptr);
+  st = release(st);
+  if (st == SPMV_SUCCESS) ++(*out)->plan_syncs;   // the wait before the scratch is freed
+  return st;
 }
 
 spmv_status_t spmv_plan_csc(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
@@ -976,6 +971,7 @@ spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nn
   const size_t o_rl = o_base + align256(sizeof(int64_t) * (size_t)(ngroups + 1));
   const size_t o_cnt = o_rl + align256(sizeof(int32_t) * (size_t)M);
   hipError_t err = hipMalloc(&p->owned_rg_meta, o_cnt + 256);
+  ++p->plan_allocs;
   if (err != hipSuccess) {
     (void)hipGetLastError();
     p->owned_rg_meta = nullptr;
@@ -996,10 +992,12 @@ spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nn
            hipSuccess ||
        (err = hipStreamSynchronize(stream)) != hipSuccess))
     return undo(hip_fail(err, "spmv_plan_rgcsr: widths"));
+  ++p->plan_syncs;
   const size_t vs = dtype == SPMV_F32 ? 4 : 8;
   const size_t o_val = align256(sizeof(int32_t) * (size_t)host[0]);
-  if ((err = hipMalloc(&p->owned_rg_data, o_val + align256(vs * (size_t)host[0]) + 256)) !=
-      hipSuccess) {
+  err = hipMalloc(&p->owned_rg_data, o_val + align256(vs * (size_t)host[0]) + 256);
+  ++p->plan_allocs;
+  if (err != hipSuccess) {
     (void)hipGetLastError();
     p->owned_rg_data = nullptr;
     return undo(fail(SPMV_ERR_ALLOC, "hipMalloc of %lld row-grouped slots failed",
@@ -1011,6 +1009,7 @@ spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nn
                              val_rg, stream)) != hipSuccess ||
       (err = hipStreamSynchronize(stream)) != hipSuccess)
     return undo(hip_fail(err, "spmv_plan_rgcsr: copy"));
+  ++p->plan_syncs;
   p->rg_group = G;
   p->rg_stored = host[1];
   p->rg_rl = rl;
@@ -1033,6 +1032,40 @@ spmv_status_t spmv_read_probe(const void* data, int64_t bytes, void* sink, hipSt
   return SPMV_SUCCESS;
 }
 
+spmv_status_t spmv_gather_probe(const int32_t* col_idx, int64_t nnz, const void* x, int64_t n_x,
+                                spmv_dtype_t dtype, void* sink, hipStream_t stream) {
+  if (dtype != SPMV_F32 && dtype != SPMV_F64)
+    return fail(SPMV_ERR_INVALID_ARG, "gather probe: unknown dtype %d", (int)dtype);
+  if (nnz < 0 || n_x <= 0 || n_x > 0xffffffffll || (nnz > 0 && (!col_idx || !x)) || !sink ||
+      (reinterpret_cast<uintptr_t>(col_idx) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(SPMV_ERR_INVALID_ARG, "gather probe: col_idx 16-byte aligned, 0 < n_x < 2^32, "
+                                      "sink 4-byte aligned");
+  const hipError_t err = launch_gather_probe(col_idx, nnz, x, n_x, dtype == SPMV_F32 ? 4 : 8,
+                                             0x5bd1e995, static_cast<int32_t*>(sink), stream);
+  if (err != hipSuccess) return hip_fail(err, "gather probe launch");
+  return SPMV_SUCCESS;
+}
+
+spmv_status_t spmv_stream_probe(const int32_t* row_ptr, const int32_t* col_idx,
+                                const void* values, int64_t M, int64_t nnz, spmv_dtype_t dtype,
+                                int32_t items_per_thread, void* y, hipStream_t stream) {
+  if (dtype != SPMV_F32 && dtype != SPMV_F64)
+    return fail(SPMV_ERR_INVALID_ARG, "stream probe: unknown dtype %d", (int)dtype);
+  if (items_per_thread != 4 && items_per_thread != 8 && items_per_thread != 16)
+    return fail(SPMV_ERR_INVALID_ARG, "stream probe: items_per_thread must be 4, 8 or 16");
+  if (M <= 0 || nnz < 0 || M + nnz > kInt32Max || !row_ptr || !y ||
+      (nnz > 0 && (!col_idx || !values)) ||
+      ((reinterpret_cast<uintptr_t>(row_ptr) | reinterpret_cast<uintptr_t>(col_idx) |
+        reinterpret_cast<uintptr_t>(values)) & 15))
+    return fail(SPMV_ERR_INVALID_ARG, "stream probe: M > 0, M + nnz < 2^31, arrays 16-byte "
+                                      "aligned");
+  const hipError_t err = launch_stream_probe(row_ptr, col_idx, values, M, nnz,
+                                             dtype == SPMV_F32 ? 4 : 8, items_per_thread, y,
+                                             stream);
+  if (err != hipSuccess) return hip_fail(err, "stream probe launch");
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_exec_events(spmv_plan_t p, const void* x, void* y, double alpha,
                                double beta, hipStream_t stream, hipEvent_t ev_begin,
                                hipEvent_t ev_end) {
@@ -1040,7 +1073,13 @@ spmv_status_t spmv_exec_events(spmv_plan_t p, const void* x, void* y, double alp
   if (st != SPMV_SUCCESS) return st;
   if (p->M > 0 && !y) return fail(SPMV_ERR_INVALID_ARG, "y is NULL");
   if (p->N > 0 && p->nnz > 0 && !x) return fail(SPMV_ERR_INVALID_ARG, "x is NULL");
-  if (x && y && x == y) return fail(SPMV_ERR_INVALID_ARG, "x and y must not alias");
+  if (x && y && p->N > 0 && p->M > 0) {
+    // byte ranges [x, x + N vs) and [y, y + M vs) must be disjoint
+    const uintptr_t vs = p->dtype == SPMV_F32 ? 4 : 8;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), x1 = x0 + (uintptr_t)p->N * vs;
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uintptr_t)p->M * vs;
+    if (x0 < y1 && y0 < x1) return fail(SPMV_ERR_INVALID_ARG, "x and y overlap");
+  }
   if (p->M == 0) return SPMV_SUCCESS;
   return p->dtype == SPMV_F32
              ? exec_typed<float>(p, x, y, alpha, beta, stream, ev_begin, ev_end)
@@ -1061,8 +1100,7 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
   p->magic = 0;
   release_bin_streams(p);
   hipError_t err = hipFree(p->ws);
-  for (void* q : {p->owned_row_ptr, p->owned_entries, p->owned_rg_meta, p->owned_rg_data,
-                  p->owned_order}) {
+  for (void* q : {p->owned_rg_meta, p->owned_rg_data}) {
     if (!q) continue;
     const hipError_t e2 = hipFree(q);
     if (err == hipSuccess) err = e2;
@@ -1121,6 +1159,8 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->max_row_len = p->max_len;
   info->n_empty_rows = p->n_empty;
   info->workspace_bytes = (int64_t)p->ws_bytes;
+  info->plan_allocs = p->plan_allocs;
+  info->plan_syncs = p->plan_syncs;
   return SPMV_SUCCESS;
 }
 

@@ -188,45 +188,12 @@ __device__ __forceinline__ void store_quad(double* lds, int i, const Quad<double
 // compile time, lane quads clamped into range (a clamped lane repeats the
 // last quad, which costs no extra cache lines), so the code is straight-line
 // and every load is issued before the first use.
-// Optional x window shared by the 4 waves of a workgroup. The plan records,
-// per workgroup, the span [lo, lo + len) of the columns its entries use
-// (len = 0 when the span does not fit kWindowBytes). At kernel start every
-// thread issues its share of the coalesced loads of x[lo, lo + len) together
-// with its partition's own loads; the values go to LDS, one __syncthreads(),
-// and the gathers read LDS. A random 64-lane global gather costs about one L1
-// line lookup per lane; an LDS gather a few bank cycles. A lane whose column
-// falls outside the recorded span (col_idx changed after planning) makes its
-// wave gather from HBM instead, so results never depend on the window.
-template <typename V>
-struct XWindow {
-  static constexpr int kCap = kWindowBytes / sizeof(V);
-  static constexpr int kIters = kCap / kBlock;
-  V* lds;        // kCap entries
-  int lo, len;   // block-uniform
-  V t[kIters];   // this thread's share, in flight until commit()
-
-  __device__ __forceinline__ void issue(const V* __restrict__ x) {
-    if (len > 0) {
-#pragma unroll
-      for (int j = 0; j < kIters; ++j) t[j] = x[lo + min((int)threadIdx.x + kBlock * j, len - 1)];
-    }
-  }
-  // every thread of the block calls this exactly once
-  __device__ __forceinline__ void commit() {
-    if (len > 0) {
-#pragma unroll
-      for (int j = 0; j < kIters; ++j) lds[min((int)threadIdx.x + kBlock * j, len - 1)] = t[j];
-    }
-    __syncthreads();
-  }
-};
-
-template <typename V, int NR, int NN, bool WIN>
+template <typename V, int NR, int NN>
 __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, int qr0, int nqr,
                                            int sub, const int32_t* __restrict__ col,
                                            const V* __restrict__ val,
                                            const V* __restrict__ x, int qn0, int nqn,
-                                           int32_t* ends, V* prods, XWindow<V>& w) {
+                                           int32_t* ends, V* prods) {
   const int lane = lane_id();
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
@@ -252,27 +219,10 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
 #pragma unroll
   for (int r = 0; r < NR; ++r)
     e[r] = ld_stream_at<i32x4>(eb, 16u * (uint32_t)min(lane + kWave * r, nqr - 1));
-  bool from_lds = false;
-  if (WIN) {
-    w.commit();
-    bool inside = true;
 #pragma unroll
-    for (int r = 0; r < NN; ++r)
+  for (int r = 0; r < NN; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) inside &= (unsigned)(c[r][j] - w.lo) < (unsigned)w.len;
-    from_lds = __ballot(!inside) == 0;
-  }
-  if (from_lds) {
-#pragma unroll
-    for (int r = 0; r < NN; ++r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * w.lds[c[r][j] - w.lo]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < NN; ++r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
-  }
+    for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
   // clamped lanes rewrite the last quad with the same values: unconditional
   // stores keep the loads from being sunk into (and serialised by) branches
 #pragma unroll
@@ -284,14 +234,12 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
 
 // Slow path for the one partition that reaches an array's last, partial
 // quad: element-wise guarded loads, exec-masked rounds.
-template <typename V, int RQR, int RQN, bool WIN>
+template <typename V, int RQR, int RQN>
 __device__ __forceinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int m, int qr0,
                                         int nqr, int sub, const int32_t* __restrict__ col,
                                         const V* __restrict__ val, const V* __restrict__ x,
-                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods,
-                                        XWindow<V>& w) {
+                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods) {
   const int lane = lane_id();
-  if (WIN) w.commit();  // joins the block's barrier; this wave gathers from HBM
   for (int r = 0; r < RQR; ++r)
     if (lane + kWave * r < nqr) {
       const i32x4 e = load_quad<true>(row_ptr, qr0 + lane + kWave * r, m);
@@ -306,93 +254,178 @@ __device__ __forceinline__ void stage_safe(const int32_t* __restrict__ row_ptr, 
     }
 }
 
-template <typename V, int NR, int RQN, bool WIN>
+template <typename V, int NR, int RQN>
 __device__ __forceinline__ void stage_dispatch_nn(const int32_t* row_ptr, int qr0, int nqr,
                                                   int sub, const int32_t* col, const V* val,
                                                   const V* x, int qn0, int nqn, int32_t* ends,
-                                                  V* prods, XWindow<V>& w) {
+                                                  V* prods) {
   const int rounds = (nqn + kWave - 1) / kWave;
   if (rounds == 0)
-    stage_fast<V, NR, 0, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, w);
+    stage_fast<V, NR, 0>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rounds == 1 || RQN < 2)
-    stage_fast<V, NR, 1, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, w);
+    stage_fast<V, NR, 1>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rounds == 2 || RQN < 3)
-    stage_fast<V, NR, (RQN < 2 ? 1 : 2), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods, w);
+    stage_fast<V, NR, (RQN < 2 ? 1 : 2)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rounds == 3 || RQN < 4)
-    stage_fast<V, NR, (RQN < 3 ? 1 : 3), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods, w);
+    stage_fast<V, NR, (RQN < 3 ? 1 : 3)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rounds == 4 || RQN < 5)
-    stage_fast<V, NR, (RQN < 4 ? 1 : 4), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods, w);
+    stage_fast<V, NR, (RQN < 4 ? 1 : 4)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rounds == 5 || RQN < 6)
-    stage_fast<V, NR, (RQN < 5 ? 1 : 5), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods, w);
+    stage_fast<V, NR, (RQN < 5 ? 1 : 5)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else
-    stage_fast<V, NR, (RQN < 6 ? 1 : 6), WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                         prods, w);
+    stage_fast<V, NR, (RQN < 6 ? 1 : 6)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
 }
 
 // Stage one partition (see stage_fast). RQR / RQN bound the rounds.
-template <typename V, int RQR, int RQN, bool WIN>
+template <typename V, int RQR, int RQN>
 __device__ __forceinline__ void stage_partition(const int32_t* __restrict__ row_ptr, int m,
                                                 int qr0, int nqr, int sub,
                                                 const int32_t* __restrict__ col,
                                                 const V* __restrict__ val,
                                                 const V* __restrict__ x, int nnz, int qn0,
-                                                int nqn, int32_t* ends, V* prods,
-                                                XWindow<V>& w) {
+                                                int nqn, int32_t* ends, V* prods) {
   static_assert(RQN <= 6, "at most 6 nonzero rounds");
   // does this partition reach an array's last, partial quad? (wave-uniform)
   const bool tail = (nqr > 0 && (m & 3) && qr0 + nqr - 1 == (m - 1) >> 2) ||
                     (nqn > 0 && (nnz & 3) && qn0 + nqn - 1 == (nnz - 1) >> 2);
   if (tail) {
-    stage_safe<V, RQR, RQN, WIN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends,
-                                 prods, w);
+    stage_safe<V, RQR, RQN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends, prods);
     return;
   }
   const int rrounds = (nqr + kWave - 1) / kWave;
   if (rrounds == 0)
-    stage_dispatch_nn<V, 0, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                      prods, w);
+    stage_dispatch_nn<V, 0, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else if (rrounds == 1 || RQR < 2)
-    stage_dispatch_nn<V, 1, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                      prods, w);
+    stage_dispatch_nn<V, 1, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
   else
-    stage_dispatch_nn<V, RQR, RQN, WIN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends,
-                                        prods, w);
+    stage_dispatch_nn<V, RQR, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
 }
 
-// Segmented inclusive scan across the wave: lanes with equal `key` that are
-// contiguous form a segment (keys must be non-decreasing across lanes).
+// ---- cross-lane moves in DPP form (gfx9 encodings) ---------------------------
+// A DPP move reads another lane's register as an operand modifier of a VALU
+// instruction: no LDS traffic and no wait, unlike a ds_bpermute shuffle.
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15 - i within 16
+constexpr int kDppWaveShl1 = 0x130;       // lane i <- lane i + 1 (lane 63: none)
+constexpr int kDppWaveShr1 = 0x138;       // lane i <- lane i - 1 (lane 0: none)
+constexpr int kDppRowBcast15 = 0x142;     // rows 1, 3 <- lane 15 of rows 0, 2
+constexpr int kDppRowBcast31 = 0x143;     // rows 2, 3 <- lane 31
+constexpr int dpp_row_shr(int n) { return 0x110 + n; }  // lane i <- i - n in its row of 16
+
+// this lane's copy of lane src(CTRL)'s v; lanes that CTRL gives no source
+// (or whose row is outside ROWS) keep `old`. Callers never rely on `old` for
+// those lanes: they test the lane position themselves. Every lane of the
+// wave must execute the move (never call it under a condition or on one
+// side of || or ?:): a lane reading from a lane masked off gets no value.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(dpp_i32<CTRL, ROWS>(0, __float_as_int(v)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_move(double v) {
+  const int64_t b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROWS>(0, (int)(uint32_t)b);
+  const int hi = dpp_i32<CTRL, ROWS>(0, (int)(b >> 32));
+  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// lane l - 1's value (lane 0: `first`) and lane l + 1's (lane 63: `last`)
+__device__ __forceinline__ int lane_prev(int v, int first) {
+  const int t = dpp_i32<kDppWaveShr1>(first, v);
+  return lane_id() == 0 ? first : t;
+}
+__device__ __forceinline__ int lane_next(int v, int last) {
+  const int t = dpp_i32<kDppWaveShl1>(last, v);
+  return lane_id() == kWave - 1 ? last : t;
+}
 template <typename V>
-__device__ __forceinline__ V wave_segscan(V v, int key) {
+__device__ __forceinline__ V lane_prev(V v) {
+  const V t = dpp_move<kDppWaveShr1>(v);
+  return lane_id() == 0 ? V(0) : t;
+}
+
+// One step of a segmented inclusive scan (Hillis-Steele over (value, head
+// flag) pairs): when the lane's covered range holds no segment head, the
+// range just before it (from lane src(CTRL)) is added, and the flags merge.
+// `valid` says whether CTRL gives this lane a source in this step.
+template <int CTRL, int ROWS, typename V>
+__device__ __forceinline__ void segscan_step(V& v, int& f, bool valid) {
+  // selects, not branches: every lane executes the moves
+  const V t = dpp_move<CTRL, ROWS>(v);
+  const int tf = dpp_i32<CTRL, ROWS>(0, f);
+  v = valid && !f ? v + t : v;
+  f = valid ? (f | tf) : f;
+}
+
+// Segmented inclusive scan across the wave, entirely in DPP moves: a segment
+// starts at every lane whose `head` is set (and at lane 0). Shifts of 1, 2, 4
+// and 8 lanes inside each row of 16, then the last lane of row 0 (2) into
+// row 1 (3), then lane 31 into rows 2 and 3: after the six steps lane l holds
+// the sum from the last head at or before l up to l. This is the wave-level
+// form of the segmented reduction the PPoPP'23 load-balancing page's
+// Sidebar 1 describes for the carry fix-up.
+template <typename V>
+__device__ __forceinline__ V wave_segscan(V v, bool head) {
   const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const V t = __shfl_up(v, o, kWave);
-    const int kt = __shfl_up(key, o, kWave);
-    if (lane >= o && kt == key) v += t;
-  }
+  const int r = lane & 15, row = lane >> 4;
+  int f = head || lane == 0;
+  segscan_step<dpp_row_shr(1), 0xF>(v, f, r >= 1);
+  segscan_step<dpp_row_shr(2), 0xF>(v, f, r >= 2);
+  segscan_step<dpp_row_shr(4), 0xF>(v, f, r >= 4);
+  segscan_step<dpp_row_shr(8), 0xF>(v, f, r >= 8);
+  segscan_step<kDppRowBcast15, 0xA>(v, f, (row & 1) != 0);
+  segscan_step<kDppRowBcast31, 0xC>(v, f, row >= 2);
   return v;
 }
 
-// DPP lane permutations inside a row of 16 lanes (gfx9 encodings).
-constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
-constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
-constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15 - i within 16
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+// Segments given by a key that does not decrease across the lanes: a lane
+// heads a segment when its key differs from the previous lane's.
+template <typename V>
+__device__ __forceinline__ V wave_segscan_keys(V v, int key) {
+  return wave_segscan(v, lane_prev(key, key) != key);
 }
-template <int CTRL>
-__device__ __forceinline__ double dpp_move(double v) {
-  const int64_t b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+
+// Inclusive prefix sum of an int across the wave in DPP moves (integer
+// sums: exact in any order).
+__device__ __forceinline__ int wave_scan_i32(int x) {
+  const int lane = lane_id();
+  const int r = lane & 15, row = lane >> 4;
+  int t;
+  t = dpp_i32<dpp_row_shr(1)>(0, x);
+  x += r >= 1 ? t : 0;
+  t = dpp_i32<dpp_row_shr(2)>(0, x);
+  x += r >= 2 ? t : 0;
+  t = dpp_i32<dpp_row_shr(4)>(0, x);
+  x += r >= 4 ? t : 0;
+  t = dpp_i32<dpp_row_shr(8)>(0, x);
+  x += r >= 8 ? t : 0;
+  t = dpp_i32<kDppRowBcast15, 0xA>(0, x);
+  x += (row & 1) ? t : 0;
+  t = dpp_i32<kDppRowBcast31, 0xC>(0, x);
+  x += row >= 2 ? t : 0;
+  return x;
+}
+
+// Sum over the whole wave in DPP moves; the total lands in lane 63 (rows of
+// 16 first, then row 0 into 1 and 2 into 3, then lane 31 into rows 2 and 3).
+template <typename V>
+__device__ __forceinline__ V wave_sum_to_last(V v) {
+  const int row = lane_id() >> 4;
+  v += dpp_move<kDppQuadXor1>(v);
+  v += dpp_move<kDppQuadXor2>(v);
+  v += dpp_move<kDppRowHalfMirror>(v);
+  v += dpp_move<kDppRowMirror>(v);
+  const V a = dpp_move<kDppRowBcast15, 0xA>(v);
+  v = (row & 1) ? v + a : v;
+  const V b = dpp_move<kDppRowBcast31, 0xC>(v);
+  v = row >= 2 ? v + b : v;
+  return v;
 }
 
 // Sum over aligned groups of G lanes, G in {1, 2, 4, 8, 16}, with DPP moves

@@ -64,7 +64,28 @@ enum StatSlot : int {
   kStatWindowFitsMulti = 6,  // ... that fit kWinIntervals intervals
   kStatBinOffset = 7,      // kMaxBins + 1 entries
   kStatInterior = kStatBinOffset + kMaxBins + 1,  // partitions inside one row
-  kStatCount = kStatInterior + 1
+  kStatIpt = kStatInterior + 1,      // merge-path items per lane the plan chose
+  kStatParts = kStatIpt + 1,         // P at that partition size
+  kStatResplit = kStatParts + 1,     // 1: the second split pass runs (T = 256)
+  kStatOrder = kStatResplit + 1,     // 1: walk partitions dealt in column order
+  kStatCount = kStatOrder + 1
+};
+
+// Error bits of stats[kStatError].
+constexpr int64_t kErrRowPtr = 1;     // row_ptr is not a CSR row pointer array
+constexpr int64_t kErrColumn = 2;     // a column index outside [0, N) (validated)
+constexpr int64_t kErrCooRows = 4;    // COO row indices out of range or order
+
+// What the planning kernels decide on the device from the counted rows
+// (host-known inputs of those decisions).
+struct PlanCtl {
+  int64_t M, N, nnz;
+  int32_t vbytes;       // 4 or 8
+  int32_t forced_ipt;   // items per lane given by the caller (0: chosen here)
+  int32_t wide_x;       // x is larger than one XCD's L2
+  int32_t reduce_req;   // 0 auto, 1 walk, 2 stream
+  int32_t order_req;    // 0 auto, 1 partition order, 2 column order
+  int32_t pad;
 };
 
 struct BinEdges {
@@ -83,18 +104,24 @@ hipError_t launch_bin_scan(int64_t M, const BinEdges& edges, int32_t* counts,
 hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges& edges,
                               const int32_t* offsets, const int64_t* stats,
                               int32_t* bins, hipStream_t s);
-// Also counts, into stats[kStatInterior], the partitions no row ends in
-// (every item a nonzero of one row).
-hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
-                               int64_t P, int32_t* split_row, int32_t* split_nz,
+// Planning decisions on the device, one thread (stage 0: items per lane
+// from the row lengths; 1: whether to split again at T = 256; 2: whether
+// the walk partitions take the column dispatch order). See plan_kernels.hip.
+hipError_t launch_plan_choose(const PlanCtl& c, int64_t* stats, int stage, hipStream_t s);
+// Merge-path split at the partition size in stats[kStatIpt] (pass 1 runs
+// only when stats[kStatResplit] is set); p_max bounds the partitions of any
+// size the plan may choose. Also counts, into stats[kStatInterior], the
+// partitions no row ends in (every item a nonzero of one row).
+hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int64_t p_max,
+                               int pass, int32_t* split_row, int32_t* split_nz,
                                int32_t* row_bounds, int64_t* stats, hipStream_t s);
 hipError_t launch_check_columns(const int32_t* col_idx, int64_t nnz, int64_t N,
                                 int64_t* stats, hipStream_t s);
 hipError_t launch_clear_stats(int64_t* stats, hipStream_t s);
-// row_ptr[0..M] from row indices sorted by row (COO); *flag |= 1 when an
-// index is outside [0, M) or out of order (flag zeroed by the caller).
+// row_ptr[0..M] from row indices sorted by row (COO); stats[kStatError]
+// gets kErrCooRows when an index is outside [0, M) or out of order.
 hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, int32_t* row_ptr,
-                              int32_t* flag, hipStream_t s);
+                              int64_t* stats, hipStream_t s);
 // *flag |= 1 unless row_ptr is a valid CSR row pointer array for nnz entries.
 hipError_t launch_csr_check(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t* flag,
                             hipStream_t s);
@@ -102,21 +129,29 @@ hipError_t launch_csr_check(const int32_t* row_ptr, int64_t M, int64_t nnz, int3
 hipError_t launch_transpose_gather(const int32_t* row_ptr, int64_t M, const int32_t* perm,
                                    const void* values, int vbytes, int64_t nnz, int32_t* col_t,
                                    void* val_t, hipStream_t s);
-// Stable sort of nnz column indices (keys < 2^bits) carrying their entry
-// positions: keys_out sorted, perm_out[t] = position of the t-th key.
-// temp == nullptr: *temp_bytes receives the scratch size needed.
-hipError_t sort_columns(void* temp, size_t* temp_bytes, const int32_t* keys, int32_t* keys_out,
-                        int32_t* perm_out, int64_t nnz, int bits, hipStream_t s);
-// Per group of `group` consecutive partitions: up to kWinIntervals
-// chunk-aligned column intervals covering the group's quads within
-// cap_bytes (kWinTable int32 per group, win_span holds win_span_ints);
-// counts groups and fitting groups in stats. hipErrorInvalidValue, and no
-// launch, when the table does not hold every group.
-hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
-                               const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t group, int32_t cap_bytes,
-                               int32_t* win_span, int64_t win_span_ints, int64_t* stats,
-                               hipStream_t s);
+// Stable LSD radix sort (8-bit digits) of (key, value) pairs by the keys'
+// low `bits` bits (keys >= 0). Pass 0 reads keys0 and vals_in (nullptr: the
+// value of key i is i) and writes keys1 / vals1; later passes ping-pong;
+// *result = 0 when the sorted pairs end in keys0 / vals0, 1 in keys1 /
+// vals1. The element count is n_dev[0] when n_dev is set (at most n_max),
+// else n_max; with `enable` set, every launch does nothing while *enable is
+// 0. temp holds radix_sort_temp_bytes(n_max) bytes.
+size_t radix_sort_temp_bytes(int64_t n_max);
+hipError_t radix_sort_pairs(int32_t* keys0, const int32_t* vals_in, int32_t* vals0,
+                            int32_t* keys1, int32_t* vals1, void* temp, int64_t n_max,
+                            const int64_t* n_dev, const int64_t* enable, int bits, hipStream_t s,
+                            int* result);
+// Per group of kWavesPerBlock consecutive stream partitions at the plan's
+// chosen partition size: up to kWinIntervals chunk-aligned column intervals
+// covering the group's quads within the stream kernel's window for that
+// size (kWinTable int32 per group; win_span holds the groups of p_max
+// partitions); counts groups and fitting groups in stats. Nothing for walk
+// plans or a malformed row_ptr.
+hipError_t launch_window_spans(const PlanCtl& c, const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* split_row, int64_t p_max, int32_t* win_span,
+                               int64_t* stats, hipStream_t s);
+// stats[kError] |= bits when *flag != 0
+hipError_t launch_fold_flag(const int32_t* flag, int64_t bits, int64_t* stats, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>
@@ -150,11 +185,17 @@ struct MergeArgs {
 hipError_t launch_read_probe(const void* data, int64_t bytes, int32_t key, int32_t* sink,
                              hipStream_t s);
 
-// Sort key of each group of `group` consecutive partitions for the column
-// dispatch order: the column of the group's middle nonzero (0 for a group
-// without nonzeros).
-hipError_t launch_group_keys(const int32_t* split_nz, const int32_t* col_idx, int32_t P,
-                             int32_t group, int32_t* keys, hipStream_t s);
+// Sort key of each walk partition for the column dispatch order: the column
+// of its middle nonzero (0 for a partition without nonzeros); P from stats,
+// nothing unless stats[kStatOrder] is set. p_max bounds P.
+hipError_t launch_partition_keys(const int32_t* split_nz, const int32_t* col_idx, int64_t p_max,
+                                 const int64_t* stats, int32_t* keys, hipStream_t s);
+// Measurement aids (probe_kernels.hip).
+hipError_t launch_gather_probe(const int32_t* col_idx, int64_t nnz, const void* x, int64_t n_x,
+                               int vbytes, int32_t key, int32_t* sink, hipStream_t s);
+hipError_t launch_stream_probe(const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                               int64_t M, int64_t nnz, int vbytes, int ipt, void* y,
+                               hipStream_t s);
 
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,

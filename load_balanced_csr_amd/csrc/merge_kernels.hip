@@ -63,10 +63,8 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   V* vb = s_val[wave];
   V* prod_q = vb + (T + 8 - 4 * nqn);
   V* prod = prod_q + (n0 & 3);
-  XWindow<V> nowin;
-  nowin.len = 0;
-  stage_partition<V, RQ, RQ, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
-                                    a.nnz, qn0, nqn, s_end[wave], prod_q, nowin);
+  stage_partition<V, RQ, RQ>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x, a.nnz,
+                             qn0, nqn, s_end[wave], prod_q);
   wave_sync();
 
   // ---- 2. per-lane start by binary search, then walk IPT units --------------
@@ -99,10 +97,11 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
 
   // ---- 3. combine open-row sums across lanes ---------------------------------
   // Lane l starts inside the row lane l-1 ended in, so the sum flowing into
-  // lane l's first finished row is the segmented scan value of lane l-1.
-  const V s = wave_segscan(acc, ri);
-  V incoming = __shfl_up(s, 1, kWave);
-  if (lane == 0) incoming = V(0);
+  // lane l's first finished row is the segmented scan value of lane l-1
+  // (DPP moves only: the scan keys are the lanes' open rows, which never
+  // decrease across the lanes).
+  const V s = wave_segscan_keys(acc, ri);
+  const V incoming = lane_prev(s);
   if (first_row >= 0) vb[first_row] += incoming;
   wave_sync();
 
@@ -299,24 +298,32 @@ __device__ __forceinline__ void stream_reduce_g(const MergeArgs<V>& a, int r0, i
   }
 }
 
-// Wider groups (32, 64 lanes per row): shuffles for the butterfly.
-template <typename V>
+// Wider groups (32, 64 lanes per row): the group's partial sums meet in its
+// last lane by DPP moves (rows of 16, then row 0 into 1 and 2 into 3; for 64
+// lanes also lane 31 into rows 2 and 3).
+template <typename V, int G>
 __device__ __forceinline__ void stream_reduce_wide(const MergeArgs<V>& a, int r0, int nrows,
                                                    const int32_t* re, const V* prod) {
+  static_assert(G == 32 || G == 64, "wide groups");
   const int lane = lane_id();
-  const int G = a.stream_lanes;
   const int gl = lane & (G - 1);
-  const int rows_per_round = kWave / G;
+  constexpr int RPR = kWave / G;
   const int grp = lane / G;
-  for (int base = 0; base < nrows; base += rows_per_round) {
+  for (int base = 0; base < nrows; base += RPR) {
     const int k = base + grp;
     V acc = V(0);
     if (k < nrows) {
       const int s = k > 0 ? re[k - 1] : 0, t = re[k];
       for (int i = s + gl; i < t; i += G) acc += prod[i];
     }
-    for (int o = G >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    if (k < nrows && gl == 0) {
+    if (G == 64) {
+      acc = wave_sum_to_last(acc);
+    } else {
+      acc = group_sum_dpp<16>(acc);
+      const V up = dpp_move<kDppRowBcast15, 0xA>(acc);
+      acc = ((lane >> 4) & 1) ? acc + up : acc;
+    }
+    if (k < nrows && gl == G - 1) {
       V out = a.alpha * acc;
       if (a.beta_nonzero) out = fma(a.beta, a.y[r0 + k], out);
       a.y[r0 + k] = out;
@@ -333,7 +340,8 @@ __device__ __forceinline__ void stream_reduce(const MergeArgs<V>& a, int r0, int
     case 4: stream_reduce_g<V, 4>(a, r0, nrows, re, prod); break;
     case 8: stream_reduce_g<V, 8>(a, r0, nrows, re, prod); break;
     case 16: stream_reduce_g<V, 16>(a, r0, nrows, re, prod); break;
-    default: stream_reduce_wide(a, r0, nrows, re, prod); break;
+    case 32: stream_reduce_wide<V, 32>(a, r0, nrows, re, prod); break;
+    default: stream_reduce_wide<V, 64>(a, r0, nrows, re, prod); break;
   }
 }
 
@@ -428,10 +436,8 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 
       wait_vmem();
       __syncthreads();
     }
-    XWindow<V> nowin;
-    nowin.len = 0;
-    stage_safe<V, RQR, RQN, false>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
-                                   a.nnz, qn0, nqn, ends_q, buf, nowin);
+    stage_safe<V, RQR, RQN>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x, a.nnz,
+                            qn0, nqn, ends_q, buf);
   } else if (nqr == 0) {
     stream_stage<V, 0, 0, WK>(a, qr0, nqr, n0, qn0, nqn, ends_q, buf, s_x, s_win);
   } else if (nqr <= kWave || RQR < 2) {
@@ -447,9 +453,11 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 
 
 // Adds alpha * sum(carries) to every row that partitions left open. One wave
 // handles 64 consecutive partitions; a row's carries are contiguous, so they
-// form a segment of equal keys. The wave that holds a segment's first carry
-// owns it and, if the segment runs past its 64 partitions, keeps reading,
-// eight windows of 64 per step, until the step where the key changes.
+// form a segment of equal keys, summed by the wave's DPP segmented scan. The
+// wave that holds a segment's first carry owns it and, if the segment runs
+// past its 64 partitions, keeps reading, eight windows of 64 per step, until
+// the step where the key changes. Every lane of the wave stays active up to
+// the scans (the early return is wave-uniform).
 template <typename V>
 __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
     const int32_t* __restrict__ carry_row, const V* __restrict__ carry_val, int32_t P,
@@ -461,11 +469,12 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
   const int64_t p = base + lane;
   const int key = p < P ? carry_row[p] : INT_MAX;
   const V v = p < P ? carry_val[p] : V(0);
-  const V s = wave_segscan(v, key);
+  const V s = wave_segscan_keys(v, key);
 
-  int next_key = __shfl_down(key, 1, kWave);
-  if (lane == kWave - 1) next_key = p + 1 < P ? carry_row[p + 1] : INT_MAX - 1;
-  const int key0 = __shfl(key, 0, kWave);
+  // the key after this lane's (the next chunk's first for lane 63)
+  const int next_key = lane_next(key, base + kWave < P ? carry_row[base + kWave] : INT_MAX - 1);
+  // wave-uniform: the chunk's first key and the key before the chunk
+  const int key0 = __builtin_amdgcn_readfirstlane(key);
   const int prev0 = base > 0 ? carry_row[base - 1] : -1;
   // a segment is owned here unless it starts at lane 0 and continues from
   // the previous chunk
@@ -473,8 +482,8 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
   const bool tail = next_key != key;
   if (tail && owned && key < M) y[key] += alpha * s;
 
-  const int key63 = __shfl(key, kWave - 1, kWave);
-  const bool cont63 = __shfl((int)(!tail && owned), kWave - 1, kWave);
+  const int key63 = __builtin_amdgcn_readlane(key, kWave - 1);
+  const bool cont63 = __builtin_amdgcn_readlane((int)(!tail && owned), kWave - 1) != 0;
   if (cont63 && key63 < M) {
     // kFixupWindows windows of 64 partitions per step, every load of a step
     // in flight together; the row's carries are a prefix of the step, so it
@@ -488,17 +497,17 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
         const int64_t pp = q + kWave * u + lane;
         kq[u] = pp < P ? carry_row[pp] : -1;
       }
-      V v[kFixupWindows];
+      V w[kFixupWindows];
 #pragma unroll
       for (int u = 0; u < kFixupWindows; ++u)
-        v[u] = kq[u] == key63 ? carry_val[q + kWave * u + lane] : V(0);
+        w[u] = kq[u] == key63 ? carry_val[q + kWave * u + lane] : V(0);
 #pragma unroll
-      for (int u = 0; u < kFixupWindows; ++u) extra += v[u];
+      for (int u = 0; u < kFixupWindows; ++u) extra += w[u];
       if (__ballot(kq[kFixupWindows - 1] == key63) != ~0ull) break;
     }
-    extra = group_sum<kWave>(extra);
-    const V s63 = __shfl(s, kWave - 1, kWave);
-    if (lane == 0) y[key63] += alpha * (s63 + extra);
+    // lane 63 holds both the wave's total and the chunk's part of the row
+    extra = wave_sum_to_last(extra);
+    if (lane == kWave - 1) y[key63] += alpha * (s + extra);
   }
 }
 

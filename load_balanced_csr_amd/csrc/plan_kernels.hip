@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void bin_count_kernel(
     atomicMax(&s_max, my_max);
     atomicAdd(&s_empty, my_empty);
   }
-  if (bad) atomicOr((unsigned long long*)&stats[kStatError], 1ull);
+  if (bad) atomicOr((unsigned long long*)&stats[kStatError], (unsigned long long)kErrRowPtr);
   __syncthreads();
   if (tid < edges.n_bins) counts[(int64_t)tid * gridDim.x + blockIdx.x] = s_cnt[tid];
   if (tid == 0) {
@@ -201,10 +201,62 @@ __device__ __forceinline__ int64_t split_at(const int32_t* __restrict__ row_ptr,
   return lo;
 }
 
+// Decisions the plan takes on the device, so that the host reads the
+// statistics back once, at the end. One thread.
+//  stage 0 -- items per lane: given by the caller, else from the row lengths:
+//    4 (T = 256) when every row has <= 32 entries and the mean is < 12 (short
+//    rows: more, smaller partitions keep the tail of the launch short), else
+//    16 for fp32 and 8 for fp64 (whose staging needs twice the LDS per unit).
+//  stage 1 -- after the split at that size: walk plans (some row longer than
+//    T/8) whose x is larger than one XCD's L2 and whose partitions mostly
+//    hold row ends are split again at T = 256 (their gathers are bound by the
+//    L1 misses in flight, and T = 256 runs twice the waves per CU).
+//  stage 2 -- walk plans deal their partitions in column order when at least
+//    an eighth of them lie inside one row and every row covers under a
+//    quarter of the columns (or when the caller asks for it).
+__global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_t* stats,
+                                                         int stage) {
+  if (threadIdx.x != 0) return;
+  const int64_t W = c.M + c.nnz;
+  const int64_t err = stats[kStatError];
+  const int64_t max_len = stats[kStatMaxLen];
+  if (stage == 0) {
+    int ipt = c.forced_ipt;
+    if (ipt == 0) {
+      const double avg = c.M > 0 ? (double)c.nnz / (double)c.M : 0.0;
+      ipt = (err & kErrRowPtr) ? 4 : (max_len <= 32 && avg < 12.0) ? 4 : c.vbytes == 4 ? 16 : 8;
+    }
+    stats[kStatIpt] = ipt;
+    stats[kStatParts] = (W + kWave * ipt - 1) / (kWave * ipt);
+    stats[kStatResplit] = 0;
+    stats[kStatOrder] = 0;
+  } else if (stage == 1) {
+    const int64_t ipt = stats[kStatIpt];
+    const int64_t T = kWave * ipt;
+    if (c.forced_ipt == 0 && ipt > 4 && !(err & (kErrRowPtr | kErrColumn)) && max_len > T / 8 &&
+        c.wide_x && 2 * stats[kStatInterior] < stats[kStatParts]) {
+      stats[kStatIpt] = 4;
+      stats[kStatParts] = (W + kWave * 4 - 1) / (kWave * 4);
+      stats[kStatResplit] = 1;
+      stats[kStatInterior] = 0;
+    }
+  } else {
+    const int64_t T = kWave * stats[kStatIpt], P = stats[kStatParts];
+    const bool walk = c.reduce_req == 1 || (c.reduce_req == 0 && max_len > T / 8);
+    int d = c.order_req;
+    if (d == 0) d = 8 * stats[kStatInterior] >= P && 4 * max_len < c.N ? 2 : 1;
+    stats[kStatOrder] = walk && P > 0 && c.nnz > 0 && !(err & kErrRowPtr) && d == 2;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void split_search_kernel(
-    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int32_t T, int32_t P,
+    const int32_t* __restrict__ row_ptr, int32_t M, int32_t nnz, int pass,
     int32_t* __restrict__ split_row, int32_t* __restrict__ split_nz,
     int32_t* __restrict__ row_bounds, int64_t* __restrict__ stats) {
+  if (pass == 1 && stats[kStatResplit] == 0) return;
+  const int64_t T = kWave * stats[kStatIpt];
+  const int64_t P = stats[kStatParts];
+  if ((int64_t)blockIdx.x * kBlock > P) return;   // workgroup-uniform
   __shared__ int64_t s_lo[kBlock + 1];
   __shared__ int s_cnt[kWavesPerBlock];
   const int t = threadIdx.x;
@@ -235,19 +287,16 @@ __global__ __launch_bounds__(kBlock) void split_search_kernel(
   }
 }
 
-// Column dispatch order: key of each group of `group` consecutive walk
-// partitions (the column of its middle nonzero; 0 when it has none). The
-// plan sorts single partitions (group 1).
-__global__ __launch_bounds__(kBlock) void group_keys_kernel(const int32_t* __restrict__ split_nz,
-                                                            const int32_t* __restrict__ col_idx,
-                                                            int32_t P, int32_t group,
-                                                            int32_t* __restrict__ keys) {
-  const int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t G = ((int64_t)P + group - 1) / group;
-  if (g >= G) return;
-  const int64_t p0 = g * group, p1 = min(p0 + group, (int64_t)P);
-  const int n0 = split_nz[p0], n1 = split_nz[p1];
-  keys[g] = n1 > n0 ? col_idx[n0 + (n1 - n0) / 2] : 0;
+// Column dispatch order: key of each walk partition, the column of its
+// middle nonzero (0 when it has none). Only when the plan chose that order.
+__global__ __launch_bounds__(kBlock) void partition_keys_kernel(
+    const int32_t* __restrict__ split_nz, const int32_t* __restrict__ col_idx,
+    const int64_t* __restrict__ stats, int32_t* __restrict__ keys) {
+  if (stats[kStatOrder] == 0) return;
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= stats[kStatParts]) return;
+  const int n0 = split_nz[p], n1 = split_nz[p + 1];
+  keys[p] = n1 > n0 ? col_idx[n0 + (n1 - n0) / 2] : 0;
 }
 
 __global__ __launch_bounds__(kBlock) void check_columns_kernel(
@@ -258,7 +307,7 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
     const int32_t c = col_idx[k];
     bad |= (c < 0) | ((int64_t)c >= N);
   }
-  if (bad) atomicOr((unsigned long long*)&stats[kStatError], 2ull);
+  if (bad) atomicOr((unsigned long long*)&stats[kStatError], (unsigned long long)kErrColumn);
 }
 
 // x window of each group of `group` consecutive stream partitions: up to
@@ -274,11 +323,27 @@ __global__ __launch_bounds__(kBlock) void check_columns_kernel(
 // interval, bit 1: they fit the intervals). This only prepares a
 // kernel variant: the exec kernel checks every column against the intervals
 // again and gathers from global x when one is outside.
+// Whether the plan's stream kernel has a window at all (stream reduction,
+// a window at this partition size, a well-formed row_ptr), and its
+// capacity in elements.
+__device__ __forceinline__ int window_cap(const PlanCtl& c, const int64_t* stats) {
+  const int64_t ipt = stats[kStatIpt];
+  const bool stream = c.reduce_req == 2 ||
+                      (c.reduce_req == 0 && stats[kStatMaxLen] <= kWave * ipt / 8);
+  if (!stream || c.nnz == 0 || (stats[kStatError] & kErrRowPtr)) return 0;
+  return stream_window_bytes((int)ipt, c.vbytes, kWavesPerBlock) / c.vbytes;
+}
+
 __global__ __launch_bounds__(kBlock) void window_span_kernel(
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    const int32_t* __restrict__ split_row, int32_t P, int32_t nnz, int32_t N, int32_t e,
-    int32_t cap, int32_t group, int32_t* __restrict__ win_span) {
+    const PlanCtl ctl, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ split_row, const int64_t* __restrict__ stats,
+    int32_t* __restrict__ win_span) {
   constexpr int NB = kBlock;            // buckets
+  const int cap = window_cap(ctl, stats);
+  const int group = kWavesPerBlock;
+  const int P = (int)stats[kStatParts];
+  if (cap == 0 || (int64_t)blockIdx.x * group >= P) return;   // workgroup-uniform
+  const int nnz = (int)ctl.nnz, N = (int)ctl.N, e = 16 / ctl.vbytes;
   __shared__ int32_t s_lo[kWavesPerBlock], s_hi[kWavesPerBlock];
   __shared__ int32_t s_flag[NB], s_run[NB];
   __shared__ int32_t s_rlo[NB], s_rhi[NB];
@@ -406,8 +471,11 @@ __global__ __launch_bounds__(kBlock) void window_span_kernel(
 // groups that fit one interval, groups that fit the intervals. A grid-stride
 // pass with one global atomic per workgroup and counter (thousands of groups
 // each adding to one address would serialise on it).
-__global__ __launch_bounds__(kBlock) void window_count_kernel(const int32_t* __restrict__ win_span,
-                                                              int32_t groups, int64_t* stats) {
+__global__ __launch_bounds__(kBlock) void window_count_kernel(const PlanCtl ctl,
+                                                              const int32_t* __restrict__ win_span,
+                                                              int64_t* stats) {
+  if (window_cap(ctl, stats) == 0) return;
+  const int groups = (int)((stats[kStatParts] + kWavesPerBlock - 1) / kWavesPerBlock);
   __shared__ int s_sum[3][kWavesPerBlock];
   int cnt[3] = {0, 0, 0};   // groups, fit one interval, fit the intervals
   for (int g = blockIdx.x * kBlock + threadIdx.x; g < groups; g += gridDim.x * kBlock) {
@@ -454,14 +522,21 @@ __global__ __launch_bounds__(kBlock) void coo_row_ptr_kernel(const int32_t* __re
 // predecessor (the offsets above need them sorted)
 __global__ __launch_bounds__(kBlock) void coo_check_kernel(const int32_t* __restrict__ row_idx,
                                                            int64_t nnz, int32_t M,
-                                                           int32_t* flag) {
+                                                           int64_t* stats) {
   bool bad = false;
   for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < nnz;
        e += (int64_t)gridDim.x * kBlock) {
     const int32_t r = row_idx[e];
     bad |= r < 0 || r >= M || (e + 1 < nnz && row_idx[e + 1] < r);
   }
-  if (__ballot(bad) != 0 && lane_id() == 0) atomicOr(flag, 1);
+  if (__ballot(bad) != 0 && lane_id() == 0)
+    atomicOr((unsigned long long*)&stats[kStatError], (unsigned long long)kErrCooRows);
+}
+
+__global__ __launch_bounds__(64) void fold_flag_kernel(const int32_t* flag, int64_t bits,
+                                                       int64_t* stats) {
+  if (threadIdx.x == 0 && *flag != 0)
+    atomicOr((unsigned long long*)&stats[kStatError], (unsigned long long)bits);
 }
 
 // flag |= 1 unless row_ptr[0] = 0, row_ptr[M] = nnz and row_ptr never
@@ -535,49 +610,53 @@ hipError_t launch_bin_scatter(const int32_t* row_ptr, int64_t M, const BinEdges&
   return hipGetLastError();
 }
 
-hipError_t launch_group_keys(const int32_t* split_nz, const int32_t* col_idx, int32_t P,
-                             int32_t group, int32_t* keys, hipStream_t s) {
-  const int64_t G = ((int64_t)P + group - 1) / group;
-  if (G <= 0) return hipSuccess;
-  hipLaunchKernelGGL(group_keys_kernel, dim3(n_blocks(G, kBlock)), dim3(kBlock), 0, s, split_nz,
-                     col_idx, P, group, keys);
+hipError_t launch_plan_choose(const PlanCtl& c, int64_t* stats, int stage, hipStream_t s) {
+  hipLaunchKernelGGL(plan_choose_kernel, dim3(1), dim3(64), 0, s, c, stats, stage);
   return hipGetLastError();
 }
 
-hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int32_t T,
-                               int64_t P, int32_t* split_row, int32_t* split_nz,
+hipError_t launch_partition_keys(const int32_t* split_nz, const int32_t* col_idx, int64_t p_max,
+                                 const int64_t* stats, int32_t* keys, hipStream_t s) {
+  if (p_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(partition_keys_kernel, dim3(n_blocks(p_max, kBlock)), dim3(kBlock), 0, s,
+                     split_nz, col_idx, stats, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_search(const int32_t* row_ptr, int64_t M, int64_t nnz, int64_t p_max,
+                               int pass, int32_t* split_row, int32_t* split_nz,
                                int32_t* row_bounds, int64_t* stats, hipStream_t s) {
-  hipLaunchKernelGGL(split_search_kernel, dim3(n_blocks(P + 1, kBlock)), dim3(kBlock), 0, s,
-                     row_ptr, (int32_t)M, (int32_t)nnz, T, (int32_t)P, split_row, split_nz,
-                     row_bounds, stats);
+  hipLaunchKernelGGL(split_search_kernel, dim3(n_blocks(p_max + 1, kBlock)), dim3(kBlock), 0, s,
+                     row_ptr, (int32_t)M, (int32_t)nnz, pass, split_row, split_nz, row_bounds,
+                     stats);
   return hipGetLastError();
 }
 
-hipError_t launch_window_spans(const int32_t* row_ptr, const int32_t* col_idx,
-                               const int32_t* split_row, int64_t P, int64_t nnz, int64_t N,
-                               int32_t elem_bytes, int32_t group, int32_t cap_bytes,
-                               int32_t* win_span, int64_t win_span_ints, int64_t* stats,
-                               hipStream_t s) {
-  if (P <= 0 || cap_bytes <= 0) return hipSuccess;
-  if (group <= 0) return hipErrorInvalidValue;
-  const int64_t groups = (P + group - 1) / group;
-  if (groups * kWinTable > win_span_ints) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(window_span_kernel, dim3((int)groups), dim3(kBlock), 0, s, row_ptr,
-                     col_idx, split_row, (int32_t)P, (int32_t)nnz, (int32_t)N, 16 / elem_bytes,
-                     cap_bytes / elem_bytes, group, win_span);
+hipError_t launch_window_spans(const PlanCtl& c, const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* split_row, int64_t p_max, int32_t* win_span,
+                               int64_t* stats, hipStream_t s) {
+  if (p_max <= 0 || c.nnz == 0) return hipSuccess;
+  const int64_t groups = (p_max + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(window_span_kernel, dim3((unsigned)groups), dim3(kBlock), 0, s, c, row_ptr,
+                     col_idx, split_row, stats, win_span);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(window_count_kernel, dim3((int)std::min<int64_t>(n_blocks(groups, kBlock), 64)),
-                     dim3(kBlock), 0, s, win_span, (int32_t)groups, stats);
+                     dim3(kBlock), 0, s, c, win_span, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_flag(const int32_t* flag, int64_t bits, int64_t* stats, hipStream_t s) {
+  hipLaunchKernelGGL(fold_flag_kernel, dim3(1), dim3(64), 0, s, flag, bits, stats);
   return hipGetLastError();
 }
 
 hipError_t launch_coo_row_ptr(const int32_t* row_idx, int64_t nnz, int64_t M, int32_t* row_ptr,
-                              int32_t* flag, hipStream_t s) {
+                              int64_t* stats, hipStream_t s) {
   if (nnz > 0) {
     const int blocks = (int)std::min<int64_t>(n_blocks(nnz, kBlock), 8192);
     hipLaunchKernelGGL(coo_check_kernel, dim3(blocks), dim3(kBlock), 0, s, row_idx, nnz,
-                       (int32_t)M, flag);
+                       (int32_t)M, stats);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

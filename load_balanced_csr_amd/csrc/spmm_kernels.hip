@@ -407,16 +407,19 @@ __global__ __launch_bounds__(kBlock) void spmm_rows_kernel(const SpmmArgs<V> a) 
 }
 
 // Y[r] += alpha * (sum of the carries of r) for every row that partitions
-// left open. kl lanes per partition (the power of two covering k, lane c
-// taking column c), so a wave holds G = 64 / kl consecutive partitions. A
-// row's carries are contiguous: a segmented scan over the wave's groups sums
-// each row's carries inside the chunk, and the group holding a segment's
-// last carry updates the row, unless the segment began in an earlier chunk
-// (that chunk's wave owns it). A segment owned here that runs past the chunk
-// is read on by the whole wave, kFixupSlices slices of G partitions per step
+// left open. A wave holds G = 64 / kl consecutive partitions (kl the power
+// of two covering k), laid out column by column: lane c * G + g takes
+// partition base + g, column c, so each column's G partitions are adjacent
+// lanes. A row's carries are contiguous: one DPP segmented scan over the
+// wave (a segment starts at g = 0 and where the row changes) sums each row's
+// carries inside the chunk, and the lane holding a segment's last carry
+// updates the row, unless the segment began in an earlier chunk (that
+// chunk's wave owns it). A segment owned here that runs past the chunk is
+// read on by the whole wave, kFixupSlices slices of G partitions per step
 // with every load of a step in flight together, until the step where it
-// ends; the groups' sums are then added across the wave. The order of the
-// adds depends only on the plan and k.
+// ends; a second segmented scan (a segment per column) then adds the slices
+// up in each column's last lane. The order of the adds depends only on the
+// plan and k.
 constexpr int kFixupSlices = 8;
 
 template <typename V>
@@ -424,38 +427,37 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   const int lane = lane_id();
   const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));   // log2 kl
   const int G = kWave >> lg;
-  const int c = lane & ((1 << lg) - 1);
-  const int g = lane >> lg;
+  const int g = lane & (G - 1);
+  const int c = lane >> (6 - lg);
   const bool col = c < a.k;
   const int64_t base =
       ((int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) *
       G;
-  if (base >= a.P) return;
+  if (base >= a.P) return;   // wave-uniform: every lane takes part in the scans below
   const int64_t p = base + g;
   const int key = p < a.P ? a.carry_row[p] : INT_MAX;
   V s = p < a.P && col ? a.carry_vec[p * a.k + c] : V(0);
-  // inclusive segmented scan over the groups, same column
-  for (int d = 1; d < G; d <<= 1) {
-    const int src = lane - (d << lg);
-    const V up = __shfl(s, src < 0 ? lane : src, kWave);
-    const int kup = __shfl(key, src < 0 ? lane : src, kWave);
-    if (src >= 0 && kup == key) s += up;
-  }
-  const int dn = lane + (1 << lg);
-  int next = __shfl(key, dn < kWave ? dn : lane, kWave);
-  if (g == G - 1) next = base + G < a.P ? a.carry_row[base + G] : INT_MAX - 1;
-  const int key0 = __shfl(key, 0, kWave);
+  // wave-uniform: the chunk's first row, the row before the chunk, the row
+  // after it
+  const int key0 = a.carry_row[base];
   const int prev0 = base > 0 ? a.carry_row[base - 1] : -1;
+  const int after = base + G < a.P ? a.carry_row[base + G] : INT_MAX - 1;
+  // the neighbours' rows, read by DPP moves that every lane executes (a move
+  // under a lane mask would read stale values from the masked lanes)
+  const int key_prev = lane_prev(key, key);
+  const int key_next = lane_next(key, after);
+  s = wave_segscan(s, g == 0 || key_prev != key);
+  const int next = g == G - 1 ? after : key_next;
   const bool owned = !(key == key0 && prev0 == key0);
   const bool tail = next != key;
   if (tail && owned && key < a.M && col) {
     V* yp = a.Y + (int64_t)key * a.ldy + c;
     *yp = fma(a.alpha, s, *yp);
   }
-  // the last group's segment, when it is owned here and goes on
-  const int last = (G - 1) << lg;
-  const int r = __shfl(key, last, kWave);
-  const bool cont = __shfl((int)(!tail && owned), last, kWave) != 0;
+  // the last partition's segment, when it is owned here and goes on
+  // (wave-uniform)
+  const int r = base + G - 1 < a.P ? a.carry_row[base + G - 1] : INT_MAX;
+  const bool cont = after == r && !(r == key0 && prev0 == key0);
   if (!cont || r >= a.M) return;
   V extra = V(0);
   for (int64_t q = base + G;; q += (int64_t)G * kFixupSlices) {
@@ -477,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
     // step's last partition is still the row's
     if (__ballot(kq[kFixupSlices - 1] == r) != ~0ull) break;
   }
-  for (int d = 1 << lg; d < kWave; d <<= 1) extra += __shfl_xor(extra, d, kWave);
+  extra = wave_segscan(extra, g == 0);   // column totals in each column's last lane
   if (g != G - 1 || !col) return;
   V* yp = a.Y + (int64_t)r * a.ldy + c;
   *yp = fma(a.alpha, s + extra, *yp);
