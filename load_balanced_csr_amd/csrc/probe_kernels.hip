@@ -74,8 +74,9 @@ __global__ __launch_bounds__(kBlock) void gather_probe_kernel(const int32_t* __r
   if (fold_bits(s) == key) sink[0] = key;
 }
 
-// One wavefront per partition of T = 64 * IPT units: rows [M p / P,
-// M (p+1) / P) and nonzeros [nnz p / P, nnz (p+1) / P), P = ceil((M + nnz) / T).
+// One wavefront per partition of T = 64 * IPT units, P = ceil((M + nnz) / T):
+// rows [p R, (p+1) R) and nonzeros [p Z, (p+1) Z), R = ceil(M / P) and
+// Z = ceil(nnz / P), clipped to the arrays.
 // Every quad of the three arrays is loaded first (16-byte non-temporal loads,
 // clamped to the arrays' full quads: a partial last quad is read as the full
 // one before it, since the probe times bytes, not values), then the rows of y
@@ -84,13 +85,15 @@ __global__ __launch_bounds__(kBlock) void gather_probe_kernel(const int32_t* __r
 template <typename V, int IPT>
 __global__ __launch_bounds__(kBlock) void stream_probe_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-    const V* __restrict__ val, int64_t M, int64_t nnz, int64_t P, V* __restrict__ y) {
+    const V* __restrict__ val, int64_t M, int64_t nnz, int64_t P, int64_t rows_per,
+    int64_t nnz_per, V* __restrict__ y) {
   constexpr int RQ = (kWave * IPT / 4 + 2 + kWave - 1) / kWave;
   const int64_t p = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
   if (p >= P) return;
   const int lane = lane_id();
-  const int64_t r0 = M * p / P, r1 = M * (p + 1) / P;
-  const int64_t n0 = nnz * p / P, n1 = nnz * (p + 1) / P;
+  // equal shares (the last one shorter), no division on the device
+  const int64_t r0 = min(M, p * rows_per), r1 = min(M, r0 + rows_per);
+  const int64_t n0 = min(nnz, p * nnz_per), n1 = min(nnz, n0 + nnz_per);
   const int64_t nqn = nnz / 4, nqr = (M + 1) / 4;
   const int64_t qn0 = n0 / 4, qn1 = max(qn0 + 1, (n1 + 3) / 4);
   const int64_t qr0 = r0 / 4, qr1 = (r1 + 4) / 4;
@@ -147,11 +150,12 @@ hipError_t launch_stream_probe_t(const int32_t* row_ptr, const int32_t* col, con
   const int64_t blocks = (P + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+  const int64_t R = (M + P - 1) / P, Z = (nnz + P - 1) / P;   // R + Z <= T + 2
   const dim3 g((unsigned)blocks), b(kBlock);
   switch (ipt) {
-    case 4: hipLaunchKernelGGL((stream_probe_kernel<V, 4>), g, b, 0, s, row_ptr, col, val, M, nnz, P, y); break;
-    case 8: hipLaunchKernelGGL((stream_probe_kernel<V, 8>), g, b, 0, s, row_ptr, col, val, M, nnz, P, y); break;
-    case 16: hipLaunchKernelGGL((stream_probe_kernel<V, 16>), g, b, 0, s, row_ptr, col, val, M, nnz, P, y); break;
+    case 4: hipLaunchKernelGGL((stream_probe_kernel<V, 4>), g, b, 0, s, row_ptr, col, val, M, nnz, P, R, Z, y); break;
+    case 8: hipLaunchKernelGGL((stream_probe_kernel<V, 8>), g, b, 0, s, row_ptr, col, val, M, nnz, P, R, Z, y); break;
+    case 16: hipLaunchKernelGGL((stream_probe_kernel<V, 16>), g, b, 0, s, row_ptr, col, val, M, nnz, P, R, Z, y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
