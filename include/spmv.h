@@ -506,6 +506,29 @@ SPMV_API spmv_status_t spmv_stream_probe(const int32_t* row_ptr, const int32_t* 
                                          spmv_dtype_t dtype, int32_t items_per_thread, void* y,
                                          hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * y = alpha * A * x + beta * y with A given directly in CSR (no plan), as
+ * spmv_plan_ex + spmv_exec compute it for a merge-path walk plan with
+ * items_per_thread 16 (fp32) or 8 (fp64) in partition order -- the same
+ * partitions, kernels and fix-up, so the same y bit for bit. The split
+ * coordinates and carries live in a 32 MiB device array of the library,
+ * one per GPU, held until the process ends: nothing is allocated, freed or
+ * synchronised, and every step is enqueued on `stream`.
+ *
+ * Arguments and conventions as for spmv_plan_ex and spmv_exec (row_ptr,
+ * col_idx, values 16-byte aligned; x and y must not overlap; beta == 0
+ * means y is not read). row_ptr is not validated (that needs a read-back);
+ * a malformed row_ptr gives an undefined y but no access outside the
+ * arrays' declared sizes. SPMV_ERR_UNSUPPORTED when M + nnz needs more
+ * partitions than the scratch holds (about 1.19M: M + nnz up to ~1.2e9 for
+ * fp32, ~0.6e9 for fp64). Calls that overlap on one GPU (two streams, or
+ * two host threads) share that scratch and race: serialise them. */
+SPMV_API spmv_status_t spmv_exec_noalloc(int64_t M, int64_t N, int64_t nnz,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         const void* values, spmv_dtype_t dtype, const void* x,
+                                         void* y, double alpha, double beta, hipStream_t stream);
+
 /* Library convention: a fixed text for each status. */
 SPMV_API const char* spmv_status_string(spmv_status_t status);
 /* Library convention: the calling thread's text of its last failure. */

@@ -31,8 +31,8 @@ EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
             "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_gather_probe",
             "spmv_stream_probe", "spmv_spmm_workspace_size",
-            "spmv_exec_multi", "spmv_exec_multi_events", "spmv_status_string",
-            "spmv_last_error")
+            "spmv_exec_multi", "spmv_exec_multi_events", "spmv_exec_noalloc",
+            "spmv_status_string", "spmv_last_error")
 
 
 class SpmvError(RuntimeError):
@@ -103,6 +103,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_read_probe.argtypes = [p, i64, p, p]
     lib.spmv_gather_probe.argtypes = [p, i64, p, i64, i32, p, p]
     lib.spmv_stream_probe.argtypes = [p, p, p, i64, i64, i32, i32, p, p]
+    lib.spmv_exec_noalloc.argtypes = [i64, i64, i64, p, p, p, i32, p, p, d, d, p]
     lib.spmv_spmm_workspace_size.argtypes = [p, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.spmv_exec_multi.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p]
     lib.spmv_exec_multi_events.argtypes = [p, i64, p, i64, p, i64, d, d, p, ctypes.c_size_t, p,
@@ -335,6 +336,23 @@ def spmv_exec_events(plan: int, x: torch.Tensor, y: torch.Tensor, alpha: float, 
     _check(load().spmv_exec_events(plan, _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts),
                                    float(alpha), float(beta), _stream(stream), ev_begin, ev_end),
            "spmv_exec_events")
+
+
+def spmv_exec_noalloc(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor,
+                      M: int, N: int, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
+                      beta: float = 0.0, stream=None) -> None:
+    """One y = alpha * A x + beta * y with no plan and no device allocation
+    (the library's own scratch array holds the partition data)."""
+    _check_csr(row_ptr, col_idx, values, M, N)
+    _check_vec(x, "x", N, values.dtype)
+    _check_vec(y, "y", M, values.dtype)
+    dts = (torch.float32, torch.float64)
+    _check(load().spmv_exec_noalloc(int(M), int(N), int(col_idx.numel()),
+                                    _dev_ptr(row_ptr, "row_ptr", (torch.int32,)),
+                                    _dev_ptr(col_idx, "col_idx", (torch.int32,)),
+                                    _dev_ptr(values, "values", dts), _dtype_code(values),
+                                    _dev_ptr(x, "x", dts), _dev_ptr(y, "y", dts), float(alpha),
+                                    float(beta), _stream(stream)), "spmv_exec_noalloc")
 
 
 def spmv_spmm_workspace_size(plan: int, k: int) -> int:

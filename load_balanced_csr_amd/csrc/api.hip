@@ -55,6 +55,11 @@ const int32_t kDefaultLanes[kMaxBins] = {1, 2, 4, 8, 16, 32, 64, 256};
 
 }  // namespace
 
+namespace spmv {
+// other sources of the library report their failures through the same text
+void set_last_error(const char* text) { g_last_error = text; }
+}  // namespace spmv
+
 struct spmv_plan_st {
   uint64_t magic;
   int64_t M, N, nnz;

@@ -53,6 +53,7 @@ def _plan_raw(M, N, nnz, rp=0x1000, col=0x2000, val=0x3000, dtype=0, out=True):
     (dict(M=5, N=5, nnz=3, out=False), 1),
     (dict(M=2 ** 31, N=5, nnz=3), 2),
     (dict(M=2 ** 30, N=5, nnz=2 ** 30 + 5), 2),
+    (dict(M=5, N=5, nnz=2 ** 31), 1),          # nnz beyond int32 indices
 ])
 def test_plan_rejects_bad_arguments(args, status):
     st, h = _plan_raw(**args)
@@ -140,3 +141,24 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def _noalloc_raw(M, N, nnz, dtype=0, rp=0x1000, col=0x2000, val=0x3000, x=0x4000, y=0x8000):
+    lib = lb.load()
+    return lib.spmv_exec_noalloc(M, N, nnz, rp, col, val, dtype, x, y, 1.0, 0.0, None)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1, N=5, nnz=0), 1),
+    (dict(M=5, N=5, nnz=3, dtype=9), 1),
+    (dict(M=5, N=5, nnz=2 ** 31), 1),
+    (dict(M=5, N=5, nnz=3, rp=None), 1),
+    (dict(M=5, N=5, nnz=3, rp=0x1004), 1),                 # misaligned
+    (dict(M=5, N=5, nnz=3, x=0x8008), 1),                  # x overlaps y
+    (dict(M=2 ** 31 - 100, N=5, nnz=0), 2),                # beyond the scratch (fp32)
+    (dict(M=700_000_000, N=5, nnz=0, dtype=1), 2),         # beyond the scratch (fp64)
+])
+def test_noalloc_rejects_before_any_device_call(args, status):
+    """Sizes and pointers are checked on the host first; none of these
+    reaches a HIP call (this container has no GPU)."""
+    assert _noalloc_raw(**args) == status, lb.spmv_last_error()
