@@ -228,10 +228,16 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def _default() -> OracleLib:
+    """The oracle library: liboracle.so, or the copy ORACLE_LIB names (a
+    sanitizer build of the same oracle.c, made by tests/test_sanitizers.py)."""
     global _lib
     if _lib is None:
-        build()
-        _lib = OracleLib(_LIB)
+        alt = os.environ.get("ORACLE_LIB")
+        if alt:
+            _lib = OracleLib(alt)
+        else:
+            build()
+            _lib = OracleLib(_LIB)
     return _lib
 
 

@@ -51,10 +51,14 @@ def build(force: bool = False) -> str:
 
 
 def _load():
+    """libsynth.so, or the copy SYNTH_LIB names (a sanitizer build of the
+    same gen.c, made by tests/test_sanitizers.py)."""
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        alt = os.environ.get("SYNTH_LIB")
+        if not alt:
+            build()
+        lib = ctypes.CDLL(alt or _LIB)
         i64, u64, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32
         p = ctypes.c_void_p
         lib.synth_hash.argtypes = [u64, u64, u64, u64]
