@@ -178,7 +178,14 @@ typedef struct spmv_plan_options {
                                  from a narrow part of x. Same partitions,
                                  carries and fix-up: y is bitwise equal
                                  either way. */
-  int32_t pad1;
+  int32_t long_row_tiles;     /* merge-path walk plans: 0 auto, 1 off (env
+                                 SPMV_TILES=0). Auto: the interior nonzeros
+                                 of rows long enough to hold, on average,
+                                 >= 64 nonzeros per block of 16 KiB of x
+                                 (4096 fp32 / 2048 fp64 columns) are summed
+                                 by column-blocked tiles (x staged in LDS)
+                                 instead of the walk kernel; needs x larger
+                                 than one block and the partition order */
 } spmv_plan_options_t;
 
 typedef struct spmv_plan_info {
@@ -216,6 +223,11 @@ typedef struct spmv_plan_info {
                                  made (1 for spmv_plan / _ex / _coo) */
   int32_t plan_syncs;         /* host synchronisations it made (1 for
                                  spmv_plan / _ex / _coo) */
+  int32_t tile_rows;          /* long rows summed by column-blocked tiles */
+  int32_t tile_blocks;        /* column blocks of those tiles */
+  int32_t walk_partitions;    /* partitions the walk kernel runs (P without
+                                 tiles; those the tiles leave with them) */
+  int32_t pad2;
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).
@@ -510,8 +522,9 @@ SPMV_API spmv_status_t spmv_stream_probe(const int32_t* row_ptr, const int32_t* 
  * capture, tight serving loops, harnesses that forbid hipMalloc): one
  * y = alpha * A * x + beta * y with A given directly in CSR (no plan), as
  * spmv_plan_ex + spmv_exec compute it for a merge-path walk plan with
- * items_per_thread 16 (fp32) or 8 (fp64) in partition order -- the same
- * partitions, kernels and fix-up, so the same y bit for bit. The split
+ * items_per_thread 16 (fp32) or 8 (fp64) in partition order and without
+ * long-row tiles -- the same partitions, kernels and fix-up, so the same y
+ * bit for bit. The split
  * coordinates and carries live in a 32 MiB device array of the library,
  * one per GPU, held until the process ends: nothing is allocated, freed or
  * synchronised, and every step is enqueued on `stream`.

@@ -48,7 +48,7 @@ class PlanOptions(ctypes.Structure):
                 ("x_window", ctypes.c_int32), ("bin_streams", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
-                ("dispatch_order", ctypes.c_int32), ("pad1", ctypes.c_int32)]
+                ("dispatch_order", ctypes.c_int32), ("long_row_tiles", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -66,7 +66,9 @@ class PlanInfo(ctypes.Structure):
                 ("rgcsr_stored", ctypes.c_int64), ("group_waves", ctypes.c_int32),
                 ("group_rows", ctypes.c_int32), ("dispatch_order", ctypes.c_int32),
                 ("interior_partitions", ctypes.c_int32), ("plan_allocs", ctypes.c_int32),
-                ("plan_syncs", ctypes.c_int32)]
+                ("plan_syncs", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_blocks", ctypes.c_int32), ("walk_partitions", ctypes.c_int32),
+                ("pad2", ctypes.c_int32)]
 
 
 _lib = None
@@ -203,7 +205,8 @@ MERGE_REDUCE_NAME = {1: "walk", 2: "stream"}
 def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
                  stream_lanes: int = 0, x_window: str = "auto",
-                 bin_streams: int = 0, dispatch_order: str = "auto") -> PlanOptions:
+                 bin_streams: int = 0, dispatch_order: str = "auto",
+                 long_row_tiles: str = "auto") -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored.
     bin_streams: 0 runs the binned schedule as one grid; n >= 1 launches each
     bin on its own, dealt over the caller's stream and n - 1 plan streams.
@@ -218,6 +221,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.x_window = {"auto": 0, "off": 1, "on": 2}[x_window]
     o.bin_streams = bin_streams
     o.dispatch_order = DISPATCH_ORDER[dispatch_order]
+    o.long_row_tiles = {"auto": 0, "off": 1}[long_row_tiles]
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -472,7 +476,9 @@ def spmv_plan_info(plan: int) -> dict:
             "n_empty_rows": info.n_empty_rows, "workspace_bytes": info.workspace_bytes,
             "rgcsr_group": info.rgcsr_group, "rgcsr_stored": info.rgcsr_stored,
             "group_waves": info.group_waves, "group_rows": info.group_rows,
-            "plan_allocs": info.plan_allocs, "plan_syncs": info.plan_syncs}
+            "plan_allocs": info.plan_allocs, "plan_syncs": info.plan_syncs,
+            "tile_rows": info.tile_rows, "tile_blocks": info.tile_blocks,
+            "walk_partitions": info.walk_partitions}
 
 
 def spmv_plan_copy_splits(plan: int):
@@ -511,16 +517,17 @@ class Plan:
     def __init__(self, row_ptr, col_idx, values, shape, strategy: str = "auto",
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
                  merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
-                 bin_streams: int = 0, dispatch_order: str = "auto", stream=None):
+                 bin_streams: int = 0, dispatch_order: str = "auto",
+                 long_row_tiles: str = "auto", stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
                 or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams
-                or dispatch_order != "auto"):
+                or dispatch_order != "auto" or long_row_tiles != "auto"):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
                                 merge_reduce, stream_lanes, x_window, bin_streams,
-                                dispatch_order)
+                                dispatch_order, long_row_tiles)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     @classmethod

@@ -117,6 +117,15 @@ struct spmv_plan_st {
   // device allocations and host synchronisations the plan's construction made
   int32_t plan_allocs;
   int32_t plan_syncs;
+  // column-blocked tiles of long rows (walk plans): tile rows, their segment
+  // bounds and block partials, and the walk kernel's list of the partitions
+  // the tiles leave (part_order, n_dispatch entries)
+  int32_t n_tile_rows;
+  int32_t tile_nb;
+  int32_t n_dispatch;
+  const int32_t* tile_rows;
+  const int32_t* tile_seg;
+  void* tile_partial;
   // per-bin launches (options.bin_streams): bins dealt over the caller's
   // stream and n_side streams of the plan, forked and joined by events
   int32_t bin_streams;
@@ -159,6 +168,8 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
     return fail(SPMV_ERR_INVALID_ARG, "options.stream_lanes must be a power of two <= 64");
   if (o->dispatch_order < 0 || o->dispatch_order > 2)
     return fail(SPMV_ERR_INVALID_ARG, "options.dispatch_order %d unknown", o->dispatch_order);
+  if (o->long_row_tiles < 0 || o->long_row_tiles > 1)
+    return fail(SPMV_ERR_INVALID_ARG, "options.long_row_tiles %d unknown", o->long_row_tiles);
   if (o->bin_streams < 0 || o->bin_streams > SPMV_MAX_BINS)
     return fail(SPMV_ERR_INVALID_ARG, "options.bin_streams must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
@@ -344,8 +355,31 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     // the window's 16-byte direct-to-LDS loads need a 16-byte aligned x
     a.x_window = (reinterpret_cast<uintptr_t>(x) & 15) == 0 ? p->x_window : 0;
     a.win_span = p->win_span;
-    a.part_order = p->dispatch_order == 2 ? p->part_order : nullptr;
-    err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
+    a.part_order = p->dispatch_order == 2 || p->n_tile_rows > 0 ? p->part_order : nullptr;
+    a.n_dispatch = p->n_tile_rows > 0 ? p->n_dispatch : 0;
+    err = launch_merge<V>(a, p->ipt, stream, ev0, p->n_tile_rows > 0 ? nullptr : ev1);
+    if (err == hipSuccess && p->n_tile_rows > 0) {
+      // the tile kernel and, after the walk kernel's fix-up, the reduction
+      // that adds each tile row's block partials (ev1 marks its end)
+      TileArgs<V> t;
+      std::memset(&t, 0, sizeof t);
+      t.rows = p->tile_rows;
+      t.seg = p->tile_seg;
+      t.col_idx = p->col_idx;
+      t.val = static_cast<const V*>(p->values);
+      t.x = static_cast<const V*>(x);
+      t.y = static_cast<V*>(y);
+      t.partial = static_cast<V*>(p->tile_partial);
+      t.alpha = (V)alpha;
+      t.n_rows = p->n_tile_rows;
+      t.nb = p->tile_nb;
+      t.ngroups = (p->n_tile_rows + kTileRows - 1) / kTileRows;
+      t.N = (int32_t)p->N;
+      t.nnz = (int32_t)p->nnz;
+      t.x_aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+      err = launch_tiles<V>(t, stream);
+      if (err == hipSuccess) err = launch_tile_reduce<V>(t, stream, ev1);
+    }
   } else {
     BinnedArgs<V> a;
     std::memset(&a, 0, sizeof a);
@@ -576,6 +610,16 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   ctl.wide_x = N * (int64_t)vs > kXcdL2Bytes;
   ctl.reduce_req = reduce_req;
   ctl.order_req = order_req;
+  ctl.tiles_req = (options && options->long_row_tiles) ? options->long_row_tiles
+                  : env_int("SPMV_TILES", -1) == 0 ? 1 : 0;
+  // column-blocked tiles of long rows: blocks of kTileBytes of x; at most
+  // one tile row per kTileMinPerBlock * nb nonzeros (and one per partition)
+  const int32_t tile_bc = kTileBytes / (int32_t)vs;
+  const int64_t tile_nb = (N + tile_bc - 1) / tile_bc;
+  const int64_t tile_cap =
+      (ctl.tiles_req == 1 || tile_nb < 2 || nnz == 0)
+          ? 0
+          : std::min<int64_t>(p_max, nnz / (kTileMinPerBlock * tile_nb) + 1);
   int key_bits = 1;
   while (key_bits < 31 && (int64_t(1) << key_bits) < N) ++key_bits;
 
@@ -597,7 +641,14 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   const size_t o_wins = take(sizeof(int32_t) * kWinTable * groups_max);
   const size_t o_order = take(sizeof(int32_t) * std::max<int64_t>(p_max, 1));
   const size_t o_order2 = take(sizeof(int32_t) * std::max<int64_t>(p_max, 1));
-  const size_t o_sort = take(radix_sort_temp_bytes(std::max<int64_t>(p_max, 1)));
+  const size_t o_sort = take(std::max(radix_sort_temp_bytes(std::max<int64_t>(p_max, 1)),
+                                      scan_temp_bytes(p_max)));
+  // tiles: their rows, segment bounds and partials; their plan-time flags,
+  // skip marks and the walk list reuse the x-window table and the column
+  // order arrays, which a plan with tiles (walk, partition order) never uses
+  const size_t o_trows = take(sizeof(int32_t) * kTileRowInts * std::max<int64_t>(tile_cap, 1));
+  const size_t o_tseg = take(sizeof(int32_t) * std::max<int64_t>(tile_cap, 1) * (tile_nb + 1));
+  const size_t o_tpart = take(vs * std::max<int64_t>(tile_cap, 1) * std::max<int64_t>(tile_nb, 1));
   const size_t o_rowptr = src.coo ? take(sizeof(int32_t) * (M + 1)) : 0;
   const size_t o_extra = src.extra_bytes ? take(src.extra_bytes) : 0;
   p->ws_bytes = off;
@@ -626,6 +677,22 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   p->win_span = reinterpret_cast<int32_t*>(base + o_wins);
   int32_t* order0 = reinterpret_cast<int32_t*>(base + o_order);
   int32_t* order1 = reinterpret_cast<int32_t*>(base + o_order2);
+  TilePlan tp;
+  std::memset(&tp, 0, sizeof tp);
+  tp.cap = (int32_t)tile_cap;
+  tp.nb = (int32_t)tile_nb;
+  tp.bc = tile_bc;
+  tp.min_entries = (int64_t)kTileMinPerBlock * tile_nb;
+  tp.rows = reinterpret_cast<int32_t*>(base + o_trows);
+  tp.seg = reinterpret_cast<int32_t*>(base + o_tseg);
+  tp.skip = p->win_span;          // 8 ints per 4 partitions: room for p_max
+  tp.scan = order1;
+  tp.list = order0;
+  tp.scan_temp = base + o_sort;
+  p->tile_rows = tp.rows;
+  p->tile_seg = tp.seg;
+  p->tile_partial = base + o_tpart;
+  p->tile_nb = tp.nb;
   void* extra = src.extra_bytes ? base + o_extra : nullptr;
   int32_t* coo_row_ptr = src.coo ? reinterpret_cast<int32_t*>(base + o_rowptr) : nullptr;
   if (src.coo) p->row_ptr = coo_row_ptr;
@@ -669,6 +736,11 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   if ((err = launch_window_spans(ctl, row_ptr, p->col_idx, p->split_row, p_max, p->win_span,
                                  p->stats, stream)) != hipSuccess)
     return bail(hip_fail(err, "plan: x windows"));
+  // tiles of long rows (walk plans; gated on the device), then the order
+  if ((err = launch_tile_plan(tp, p->split_row, p->split_nz, p->col_idx, M, nnz, p_max,
+                              p->stats, p->carry_row, p->carry_val, (int)vs, stream)) !=
+      hipSuccess)
+    return bail(hip_fail(err, "plan: long-row tiles"));
   // column dispatch order (walk plans that chose it; every launch checks
   // the flag): keys in the carry-row array, sorted with their partition ids
   // (ping-pong through the carry-value array, which has room for P ints)
@@ -756,6 +828,15 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   // walk kernel's dispatch order, as chosen and sorted on the device
   p->dispatch_order = host_stats[kStatOrder] ? 2 : 1;
   p->part_order = p->dispatch_order == 2 ? (sort_result ? order1 : order0) : nullptr;
+  p->n_tile_rows = p->merge_reduce == 1 ? (int32_t)host_stats[kStatTileRows] : 0;
+  // every tile row leaves its row-end partition to the walk kernel, so the
+  // list is never empty; were it, the plain walk (all partitions, which
+  // rewrites every carry) stays correct
+  if (host_stats[kStatWalkParts] <= 0) p->n_tile_rows = 0;
+  if (p->n_tile_rows > 0) {
+    p->part_order = tp.list;
+    p->n_dispatch = (int32_t)host_stats[kStatWalkParts];
+  }
   p->group_waves = 4;
   p->group_rows = default_group_rows(p, 4);
   p->strategy = options && options->strategy ? options->strategy : choose_strategy(p);
@@ -1166,6 +1247,9 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->workspace_bytes = (int64_t)p->ws_bytes;
   info->plan_allocs = p->plan_allocs;
   info->plan_syncs = p->plan_syncs;
+  info->tile_rows = p->n_tile_rows;
+  info->tile_blocks = p->n_tile_rows > 0 ? p->tile_nb : 0;
+  info->walk_partitions = p->n_tile_rows > 0 ? p->n_dispatch : (int32_t)p->P;
   return SPMV_SUCCESS;
 }
 

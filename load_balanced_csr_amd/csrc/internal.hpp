@@ -68,8 +68,64 @@ enum StatSlot : int {
   kStatParts = kStatIpt + 1,         // P at that partition size
   kStatResplit = kStatParts + 1,     // 1: the second split pass runs (T = 256)
   kStatOrder = kStatResplit + 1,     // 1: walk partitions dealt in column order
-  kStatCount = kStatOrder + 1
+  kStatTileOk = kStatOrder + 1,      // 1: the plan may tile long rows (walk, x > one block)
+  kStatTileRows = kStatTileOk + 1,   // tile rows found (0: no tiles)
+  kStatWalkParts = kStatTileRows + 1,  // partitions the walk kernel still runs, with tiles
+  kStatTileEntries = kStatWalkParts + 1,  // nonzeros in the tile rows' interior runs
+  kStatCount = kStatTileEntries + 1
 };
+
+// ---- column-blocked tiles of long rows (tile_kernels.hip) ------------------------
+constexpr int kTileBytes = 16384;   // x block of one tile in LDS: 4096 fp32 / 2048 fp64
+constexpr int kTileRows = 64;       // tile rows one workgroup takes per column block
+constexpr int kTileRowInts = 8;     // per tile row: row, first / end nonzero, first / end partition
+constexpr int kTileMinPerBlock = 64;  // a row is tiled when its interior run holds this many
+                                      // nonzeros per column block on average
+
+// Plan-time buffers of the tiles (all in the plan's workspace).
+struct TilePlan {
+  int32_t cap;            // tile rows the buffers hold
+  int32_t nb;             // column blocks
+  int32_t bc;             // columns per block
+  int64_t min_entries;    // kTileMinPerBlock * nb
+  int32_t* rows;          // cap x kTileRowInts
+  int32_t* seg;           // cap x (nb + 1): segment bounds
+  int32_t* skip;          // p_max: 1 where the walk kernel skips the partition
+  int32_t* scan;          // p_max: flags, then their prefix sums
+  int32_t* list;          // p_max: the walk kernel's dispatch list
+  void* scan_temp;        // scan_temp_bytes(p_max)
+};
+// Tile rows, segments, skipped partitions (carries zeroed) and the walk
+// dispatch list, every launch gated by the statistics (kStatTileOk, then
+// kStatTileRows). Tiles are kept only when their runs hold at least half of
+// the nnz nonzeros; a plan that keeps them takes the partition order.
+hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const int32_t* split_nz,
+                            const int32_t* col_idx, int64_t M, int64_t nnz, int64_t p_max,
+                            int64_t* stats, int32_t* carry_row, void* carry_val, int vbytes,
+                            hipStream_t s);
+
+template <typename V>
+struct TileArgs {
+  const int32_t* rows;    // kTileRowInts per tile row
+  const int32_t* seg;     // n_rows x (nb + 1)
+  const int32_t* col_idx;
+  const V* val;
+  const V* x;
+  V* y;
+  V* partial;             // n_rows x nb
+  V alpha;
+  int32_t n_rows;
+  int32_t nb;
+  int32_t ngroups;        // ceil(n_rows / kTileRows)
+  int32_t N;
+  int32_t nnz;
+  int32_t x_aligned;      // x is 16-byte aligned (direct-to-LDS staging)
+};
+template <typename V>
+hipError_t launch_tiles(const TileArgs<V>& a, hipStream_t s);
+// ev_end (may be null) is recorded by the reduction's dispatch at its end
+template <typename V>
+hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s, hipEvent_t ev_end);
 
 // Error bits of stats[kStatError].
 constexpr int64_t kErrRowPtr = 1;     // row_ptr is not a CSR row pointer array
@@ -85,7 +141,7 @@ struct PlanCtl {
   int32_t wide_x;       // x is larger than one XCD's L2
   int32_t reduce_req;   // 0 auto, 1 walk, 2 stream
   int32_t order_req;    // 0 auto, 1 partition order, 2 column order
-  int32_t pad;
+  int32_t tiles_req;    // 0 auto, 1 off
 };
 
 struct BinEdges {
@@ -137,6 +193,12 @@ hipError_t launch_transpose_gather(const int32_t* row_ptr, int64_t M, const int3
 // else n_max; with `enable` set, every launch does nothing while *enable is
 // 0. temp holds radix_sort_temp_bytes(n_max) bytes.
 size_t radix_sort_temp_bytes(int64_t n_max);
+// Exclusive prefix sum, in place, of n_max int32 (sum < 2^31); nothing while
+// *enable is 0 (enable may be null). n_max <= 8192 * 4096. temp holds
+// scan_temp_bytes(n_max) bytes.
+size_t scan_temp_bytes(int64_t n_max);
+hipError_t exclusive_scan_i32(int32_t* data, int64_t n_max, const int64_t* enable, void* temp,
+                              hipStream_t s);
 hipError_t radix_sort_pairs(int32_t* keys0, const int32_t* vals_in, int32_t* vals0,
                             int32_t* keys1, int32_t* vals1, void* temp, int64_t n_max,
                             const int64_t* n_dev, const int64_t* enable, int bits, hipStream_t s,
@@ -178,6 +240,7 @@ struct MergeArgs {
   int32_t x_window;      // stream kernel's x window: 0 none, 1 one interval, 3 up to three
   const int32_t* win_span;  // per stream workgroup: kWinTable int32 (window intervals)
   const int32_t* part_order;  // walk kernel: dispatch slot -> partition (null: identity)
+  int32_t n_dispatch;    // walk kernel: dispatch slots (0: P)
 };
 
 // Streaming read of `bytes` (multiple of 16) at data; the xor of each 4 KiB

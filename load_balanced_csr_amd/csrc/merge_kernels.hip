@@ -41,9 +41,9 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
   int p = blk * kWavesPerBlock + wave;
-  if (p >= a.P) return;
-  // column dispatch order: the plan's permutation of the partitions (a
-  // uniform read of a table nothing here writes)
+  if (p >= (a.n_dispatch ? a.n_dispatch : a.P)) return;
+  // column dispatch order, or the partitions that long-row tiles leave: the
+  // plan's list of partitions (a uniform read of a table nothing here writes)
   if (a.part_order) p = a.part_order[p];
 
   const int r0 = a.split_row[p], r1 = a.split_row[p + 1];
@@ -524,7 +524,8 @@ hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, h
 
 template <typename V, int IPT>
 hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int slots = a.stream || !a.n_dispatch ? a.P : a.n_dispatch;
+  const int blocks = (slots + kWavesPerBlock - 1) / kWavesPerBlock;
   if (a.stream && a.x_window == 1) {
     return launch_window<V, IPT, 1>(a, s, ev0, ev1);
   } else if (a.stream && a.x_window > 1) {

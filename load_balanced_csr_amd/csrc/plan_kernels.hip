@@ -213,7 +213,10 @@ __device__ __forceinline__ int64_t split_at(const int32_t* __restrict__ row_ptr,
 //    L1 misses in flight, and T = 256 runs twice the waves per CU).
 //  stage 2 -- walk plans deal their partitions in column order when at least
 //    an eighth of them lie inside one row and every row covers under a
-//    quarter of the columns (or when the caller asks for it).
+//    quarter of the columns (or when the caller asks for it); and walk plans
+//    whose x spans more than one tile block may tile their long rows (the
+//    tile plan keeps them, and the partition order, when they hold at least
+//    half of the nonzeros).
 __global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_t* stats,
                                                          int stage) {
   if (threadIdx.x != 0) return;
@@ -240,12 +243,17 @@ __global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_
       stats[kStatResplit] = 1;
       stats[kStatInterior] = 0;
     }
-  } else {
+  } else if (stage == 2) {
     const int64_t T = kWave * stats[kStatIpt], P = stats[kStatParts];
     const bool walk = c.reduce_req == 1 || (c.reduce_req == 0 && max_len > T / 8);
     int d = c.order_req;
     if (d == 0) d = 8 * stats[kStatInterior] >= P && 4 * max_len < c.N ? 2 : 1;
     stats[kStatOrder] = walk && P > 0 && c.nnz > 0 && !(err & kErrRowPtr) && d == 2;
+    // long rows may be tiled by column block (walk plans whose x spans more
+    // than one block; their runs are found next)
+    const int64_t bc = kTileBytes / c.vbytes;
+    stats[kStatTileOk] = walk && c.tiles_req != 1 && c.order_req != 2 && P > 0 && c.nnz > 0 &&
+                         !(err & kErrRowPtr) && c.N > bc;
   }
 }
 

@@ -214,6 +214,24 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 }  // namespace
 
+size_t scan_temp_bytes(int64_t n_max) {
+  return align256(sizeof(int32_t) * (size_t)((std::max<int64_t>(n_max, 1) + kScanChunk - 1) /
+                                             kScanChunk));
+}
+
+hipError_t exclusive_scan_i32(int32_t* data, int64_t n_max, const int64_t* enable, void* temp,
+                              hipStream_t s) {
+  const int64_t chunks = (std::max<int64_t>(n_max, 1) + kScanChunk - 1) / kScanChunk;
+  if (chunks > kScanTopMax) return hipErrorInvalidValue;
+  int32_t* sums = static_cast<int32_t*>(temp);
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)chunks), dim3(kSortThreads), 0, s, data,
+                     n_max, enable, sums);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, s, sums, (int32_t)chunks, enable);
+  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)chunks), dim3(kSortThreads), 0, s, data,
+                     n_max, enable, sums);
+  return hipGetLastError();
+}
+
 size_t radix_sort_temp_bytes(int64_t n_max) {
   const SortGeometry g = sort_geometry(n_max);
   return align256(sizeof(int32_t) * (size_t)g.count_elems) +

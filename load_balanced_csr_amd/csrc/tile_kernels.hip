@@ -1,0 +1,339 @@
+// Column-blocked tiles for the long rows of a merge-path walk plan.
+//
+// Merge-path ("A Programming Model for GPU Load Balancing", PPoPP'23,
+// Section 5.2.1) cuts a row of 50,000 nonzeros into ~50 partitions of
+// T = 1024 units, each a run of the row's consecutive nonzeros. With columns
+// spread over all of x, every such partition gathers x from a wide span, one
+// cache line per product: on MI355X those gathers, not HBM, bind (the RgCSR
+// page's results section reports the same effect of caching x, 1.81x on its
+// GPU). Here the partitions that lie entirely inside one row (no row end in
+// them) are regrouped by column: a long row's interior nonzeros are cut at
+// fixed column-block boundaries (BC columns, 16 KiB of x), and a workgroup
+// (a tile) takes one column block and the segments of up to kTileRows long
+// rows in it: it stages that block of x in LDS once and gathers from LDS.
+// Every segment's sum goes to partial[row][block]; a reduction adds
+// alpha * sum over blocks, in block order, to each row's y after the walk
+// kernel and the carry fix-up. The walk kernel skips those partitions (their
+// carries are 0), so every nonzero is summed exactly once and the result is
+// bitwise reproducible for a fixed plan.
+//
+// Correctness never depends on the columns: segments partition each row's
+// interior range whatever col_idx holds, and a column outside the tile's
+// block is gathered from global x.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+#include <limits.h>
+
+#include <algorithm>
+
+namespace spmv {
+namespace {
+
+// ---- plan: interior runs of long rows ---------------------------------------------
+
+// The partition just past row r's interior run starting at p (its row-end
+// partition): the first q > p with split_row[q + 1] > r, by binary search.
+__device__ __forceinline__ int64_t run_end(const int32_t* __restrict__ split_row, int64_t p,
+                                           int64_t P, int32_t r) {
+  int64_t lo = p + 1, hi = P;   // split_row[P] = M > r
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (split_row[mid] > r) hi = mid; else lo = mid + 1;
+  }
+  return lo - 1;
+}
+
+// flags[p] = 1 when partition p starts an interior run whose nonzeros reach
+// min_entries (0 past P); nothing unless the plan allows tiles.
+__global__ __launch_bounds__(kBlock) void tile_flags_kernel(
+    const int32_t* __restrict__ split_row, const int32_t* __restrict__ split_nz, int64_t p_max,
+    int32_t M, int64_t min_entries, const int64_t* __restrict__ stats, int32_t* __restrict__ flags) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= p_max || stats[kStatTileOk] == 0) return;
+  const int64_t P = stats[kStatParts];
+  int f = 0;
+  if (p < P) {
+    const int32_t r = split_row[p];
+    if (r < M && split_row[p + 1] == r && (p == 0 || split_row[p - 1] != r)) {
+      const int64_t q = run_end(split_row, p, P, r);
+      f = (int64_t)split_nz[q] - split_nz[p] >= min_entries;
+    }
+  }
+  flags[p] = f;
+}
+
+// After the exclusive scan of the flags: the tile-row table (row, first and
+// end nonzero of the interior run, first and end partition), at most cap
+// rows; stats[kStatTileRows] = their number.
+__global__ __launch_bounds__(kBlock) void tile_rows_kernel(
+    const int32_t* __restrict__ split_row, const int32_t* __restrict__ split_nz, int64_t p_max,
+    int32_t M, int64_t min_entries, int32_t cap, const int32_t* __restrict__ scan,
+    int64_t* __restrict__ stats, int32_t* __restrict__ rows) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= p_max || stats[kStatTileOk] == 0) return;
+  const int64_t P = stats[kStatParts];
+  if (p >= P) return;
+  const int32_t r = split_row[p];
+  int64_t q = -1;
+  bool f = false;
+  if (r < M && split_row[p + 1] == r && (p == 0 || split_row[p - 1] != r)) {
+    q = run_end(split_row, p, P, r);
+    f = (int64_t)split_nz[q] - split_nz[p] >= min_entries;
+  }
+  const int32_t i = scan[p];
+  if (f && i < cap) {
+    int32_t* t = rows + (int64_t)kTileRowInts * i;
+    t[0] = r;
+    t[1] = split_nz[p];
+    t[2] = split_nz[q];
+    t[3] = (int32_t)p;
+    t[4] = (int32_t)q;
+    atomicAdd((unsigned long long*)&stats[kStatTileEntries],
+              (unsigned long long)((int64_t)split_nz[q] - split_nz[p]));
+  }
+  if (p == P - 1) stats[kStatTileRows] = min((int64_t)cap, (int64_t)i + (f ? 1 : 0));
+}
+
+// Tiles are worth their extra launches and their partition order only when
+// their runs hold at least half of the nonzeros; a plan that keeps them
+// deals the walk kernel's partitions in partition order.
+__global__ __launch_bounds__(64) void tile_gate_kernel(int64_t nnz, int64_t* stats) {
+  if (threadIdx.x != 0) return;
+  if (2 * stats[kStatTileEntries] < nnz) stats[kStatTileRows] = 0;
+  if (stats[kStatTileRows] > 0) stats[kStatOrder] = 0;
+}
+
+// seg[i][b] = first interior nonzero of tile row i whose column is >= b * bc
+// (b = 0..nb; the ends are the run's bounds), made non-decreasing in b so
+// that the segments always partition the run.
+__global__ __launch_bounds__(kBlock) void tile_seg_kernel(const int32_t* __restrict__ rows,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          int32_t nb, int32_t bc, int64_t n_max,
+                                                          const int64_t* __restrict__ stats,
+                                                          int32_t* __restrict__ seg) {
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= n_max * (nb + 1)) return;
+  const int64_t i = t / (nb + 1);
+  const int b = (int)(t - i * (nb + 1));
+  if (i >= stats[kStatTileRows]) return;
+  const int32_t* row = rows + kTileRowInts * i;
+  const int32_t a = row[1], e = row[2];
+  int32_t pos;
+  if (b == 0) {
+    pos = a;
+  } else if (b == nb) {
+    pos = e;
+  } else {
+    const int64_t c = (int64_t)b * bc;
+    int32_t lo = a, hi = e;
+    while (lo < hi) {
+      const int32_t mid = (int32_t)(((int64_t)lo + hi) >> 1);
+      if (col_idx[mid] < c) lo = mid + 1; else hi = mid;
+    }
+    pos = lo;
+  }
+  seg[i * (nb + 1) + b] = pos;
+}
+
+// Running maximum along each tile row's boundaries (only changes anything
+// when a row's interior columns are not sorted), then the row's partitions
+// marked as skipped by the walk kernel, with zero carries that the fix-up
+// adds to the row harmlessly. One thread per tile row.
+__global__ __launch_bounds__(kBlock) void tile_finish_kernel(const int32_t* __restrict__ rows,
+                                                             int32_t nb, int64_t n_max,
+                                                             const int64_t* __restrict__ stats,
+                                                             int32_t* __restrict__ seg,
+                                                             int32_t* __restrict__ skip,
+                                                             int32_t* __restrict__ carry_row,
+                                                             void* carry_val, int vbytes) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n_max || i >= stats[kStatTileRows]) return;
+  int32_t* s = seg + i * (nb + 1);
+  int32_t run = s[0];
+  for (int b = 1; b <= nb; ++b) {
+    run = max(run, s[b]);
+    s[b] = run;
+  }
+  const int32_t* row = rows + kTileRowInts * i;
+  for (int32_t p = row[3]; p < row[4]; ++p) {
+    skip[p] = 1;
+    carry_row[p] = row[0];
+    if (vbytes == 4) static_cast<float*>(carry_val)[p] = 0.f;
+    else static_cast<double*>(carry_val)[p] = 0.0;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* __restrict__ a, int64_t n,
+                                                          int32_t v, const int64_t* enable) {
+  if (enable && *enable == 0) return;
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < n;
+       k += (int64_t)gridDim.x * kBlock)
+    a[k] = v;
+}
+
+// keep[p] = 1 for the partitions the walk kernel still runs (0 past P)
+__global__ __launch_bounds__(kBlock) void tile_keep_kernel(const int32_t* __restrict__ skip,
+                                                           int64_t p_max,
+                                                           const int64_t* __restrict__ stats,
+                                                           int32_t* __restrict__ keep) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= p_max || stats[kStatTileRows] == 0) return;
+  keep[p] = p < stats[kStatParts] && skip[p] == 0;
+}
+
+// the walk kernel's dispatch list: the kept partitions in partition order
+__global__ __launch_bounds__(kBlock) void tile_list_kernel(const int32_t* __restrict__ skip,
+                                                           const int32_t* __restrict__ scan,
+                                                           int64_t p_max,
+                                                           int64_t* __restrict__ stats,
+                                                           int32_t* __restrict__ list) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= p_max || stats[kStatTileRows] == 0) return;
+  const int64_t P = stats[kStatParts];
+  if (p >= P) return;
+  const bool kept = skip[p] == 0;
+  if (kept) list[scan[p]] = (int32_t)p;
+  if (p == P - 1) stats[kStatWalkParts] = scan[p] + (kept ? 1 : 0);
+}
+
+// ---- exec ------------------------------------------------------------------------
+
+template <typename V>
+__device__ __forceinline__ V tile_x(const V* xs, const V* __restrict__ x, int c, int64_t c0,
+                                    int clen) {
+  const unsigned lc = (unsigned)((int64_t)c - c0);
+  return lc < (unsigned)clen ? xs[lc] : x[c];
+}
+
+// One workgroup per tile (column block b, group g of kTileRows tile rows):
+// the block of x staged in LDS (direct-to-LDS 16-byte loads when x is 16-byte
+// aligned), then each wave takes every fourth row of the group and streams
+// its segment in 16-byte quads (entries outside the segment masked), sums
+// the products lane-wise and across the wave by DPP moves; lane 63 writes
+// partial[row][b].
+template <typename V>
+__global__ __launch_bounds__(kBlock) void tile_spmv_kernel(const TileArgs<V> a) {
+  constexpr int BC = kTileBytes / (int)sizeof(V);
+  constexpr int E = 16 / (int)sizeof(V);   // elements per 16-byte chunk
+  __shared__ __attribute__((aligned(16))) V xs[BC];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = xcd_tile(blockIdx.x, 0, gridDim.x);
+  const int b = t / a.ngroups, g = t - b * a.ngroups;
+  const int64_t c0 = (int64_t)b * BC;
+  const int clen = (int)min((int64_t)BC, (int64_t)a.N - c0);
+  if (a.x_aligned) {
+    const int nch = clen / E;
+#pragma unroll
+    for (int r = 0; r < BC / E / kBlock; ++r) {
+      const int first = r * kBlock + wave * kWave;
+      if (first < nch && first + lane < nch) lds_dma16(a.x + c0 + E * (first + lane), xs + E * first);
+    }
+    if ((int)threadIdx.x < clen - E * nch) xs[E * nch + threadIdx.x] = a.x[c0 + E * nch + threadIdx.x];
+  } else {
+    for (int k = threadIdx.x; k < clen; k += kBlock) xs[k] = a.x[c0 + k];
+  }
+  wait_vmem();
+  __syncthreads();
+  const int end = min(g * kTileRows + kTileRows, a.n_rows);
+  for (int i = g * kTileRows + wave; i < end; i += kWavesPerBlock) {
+    const int32_t s0 = a.seg[(int64_t)i * (a.nb + 1) + b];
+    const int32_t s1 = a.seg[(int64_t)i * (a.nb + 1) + b + 1];
+    const int q1 = (s1 + 3) >> 2;
+    V acc = V(0);
+    for (int q = (s0 >> 2) + lane; q < q1; q += kWave) {
+      // the array's last quad may be partial: element loads for it alone
+      const bool full = 4 * q + 3 < a.nnz;
+      const i32x4 c = full ? ld_stream(reinterpret_cast<const i32x4*>(a.col_idx) + q)
+                           : load_quad<true>(a.col_idx, q, a.nnz);
+      const Quad<V> v = full ? load_quad<false>(a.val, q, 0) : load_quad<true>(a.val, q, a.nnz);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * q + j;
+        if (k >= s0 && k < s1) acc += v[j] * tile_x(xs, a.x, c[j], c0, clen);
+      }
+    }
+    acc = wave_sum_to_last(acc);
+    if (lane == kWave - 1) a.partial[(int64_t)i * a.nb + b] = acc;
+  }
+}
+
+// y[row] += alpha * (sum of the row's block partials, in block order), one
+// wave per tile row.
+template <typename V>
+__global__ __launch_bounds__(kBlock) void tile_reduce_kernel(const TileArgs<V> a) {
+  const int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  if (i >= a.n_rows) return;   // wave-uniform
+  const int lane = lane_id();
+  V acc = V(0);
+  for (int b = lane; b < a.nb; b += kWave) acc += a.partial[i * a.nb + b];
+  acc = wave_sum_to_last(acc);
+  if (lane == kWave - 1) {
+    const int32_t r = a.rows[kTileRowInts * i];
+    a.y[r] += a.alpha * acc;
+  }
+}
+
+unsigned grid_for(int64_t n, int64_t per) {
+  return (unsigned)std::max<int64_t>(1, (n + per - 1) / per);
+}
+
+}  // namespace
+
+hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const int32_t* split_nz,
+                            const int32_t* col_idx, int64_t M, int64_t nnz, int64_t p_max,
+                            int64_t* stats, int32_t* carry_row, void* carry_val, int vbytes,
+                            hipStream_t s) {
+  if (tp.cap <= 0 || p_max <= 0) return hipSuccess;
+  const dim3 blk(kBlock);
+  hipLaunchKernelGGL(tile_flags_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, split_row,
+                     split_nz, p_max, (int32_t)M, tp.min_entries, stats, tp.scan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = exclusive_scan_i32(tp.scan, p_max, stats + kStatTileOk, tp.scan_temp, s)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(tile_rows_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, split_row,
+                     split_nz, p_max, (int32_t)M, tp.min_entries, tp.cap, tp.scan, stats, tp.rows);
+  hipLaunchKernelGGL(tile_gate_kernel, dim3(1), dim3(64), 0, s, nnz, stats);
+  hipLaunchKernelGGL(tile_seg_kernel, dim3(grid_for((int64_t)tp.cap * (tp.nb + 1), kBlock)), blk,
+                     0, s, tp.rows, col_idx, tp.nb, tp.bc, (int64_t)tp.cap, stats, tp.seg);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max, 0,
+                     stats + kStatTileRows);
+  hipLaunchKernelGGL(tile_finish_kernel, dim3(grid_for(tp.cap, kBlock)), blk, 0, s, tp.rows,
+                     tp.nb, (int64_t)tp.cap, stats, tp.seg, tp.skip, carry_row, carry_val, vbytes);
+  hipLaunchKernelGGL(tile_keep_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max,
+                     stats, tp.scan);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = exclusive_scan_i32(tp.scan, p_max, stats + kStatTileRows, tp.scan_temp, s)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(tile_list_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, tp.scan,
+                     p_max, stats, tp.list);
+  return hipGetLastError();
+}
+
+template <typename V>
+hipError_t launch_tiles(const TileArgs<V>& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int64_t tiles = (int64_t)a.ngroups * a.nb;
+  if (tiles > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_spmv_kernel<V>, dim3((unsigned)tiles), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename V>
+hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s, hipEvent_t ev_end) {
+  if (a.n_rows <= 0) return hipSuccess;
+  launch_timed(tile_reduce_kernel<V>,
+               dim3((unsigned)(((int64_t)a.n_rows * kWave + kBlock - 1) / kBlock)), dim3(kBlock),
+               0, s, nullptr, ev_end, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_tiles<float>(const TileArgs<float>&, hipStream_t);
+template hipError_t launch_tiles<double>(const TileArgs<double>&, hipStream_t);
+template hipError_t launch_tile_reduce<float>(const TileArgs<float>&, hipStream_t, hipEvent_t);
+template hipError_t launch_tile_reduce<double>(const TileArgs<double>&, hipStream_t, hipEvent_t);
+
+}  // namespace spmv

@@ -50,8 +50,10 @@ def test_column_order_bitwise_equal(case, ipt):
     dt = w.values.dtype.type
     x = dev(w.x)
     y0 = dev(synth.uniform(w.M, 4, synth.S_Y, dt))
+    # long-row tiles change the summation order, so they stay off here: this
+    # compares the two dispatch orders of the same partitions
     base = m.plan(None, strategy="merge", items_per_thread=ipt, merge_reduce="walk",
-                  dispatch_order="partition")
+                  dispatch_order="partition", long_row_tiles="off")
     col = m.plan(None, strategy="merge", items_per_thread=ipt, merge_reduce="walk",
                  dispatch_order="column")
     assert base.info["dispatch_order"] == "partition"
@@ -94,7 +96,11 @@ def test_auto_order():
     # long sparse rows fill most partitions: column order; short rows: not
     w = CASES["bimodal"]()
     m = DevMatrix.of(w)
+    # by default these long rows go to column-blocked tiles (partition order)
     p = m.plan(None, strategy="merge", merge_reduce="walk")
+    assert p.info["tile_rows"] > 0 and p.info["dispatch_order"] == "partition"
+    p.destroy()
+    p = m.plan(None, strategy="merge", merge_reduce="walk", long_row_tiles="off")
     assert p.info["dispatch_order"] == "column"
     x = dev(w.x)
     y = torch.full((w.M,), float("nan"), device="cuda")

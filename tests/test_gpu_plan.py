@@ -24,7 +24,7 @@ EXPECTED = {
     "tiny": (256, "stream", "partition"),
     "laplacian": (256, "stream", "partition"),
     "powerlaw": (256, "walk", "column"),
-    "bimodal": (1024, "walk", "column"),
+    "bimodal": (1024, "walk", "partition"),   # its long rows go to tiles
     "banded": (1024, "stream", "partition"),
 }
 
@@ -40,6 +40,7 @@ def test_one_allocation_one_sync(name):
     assert (info["items_per_wave"], info["merge_reduce"], info["dispatch_order"]) == \
         EXPECTED[name], info
     assert info["n_partitions"] == -(-(w.M + w.nnz) // info["items_per_wave"])
+    assert (info["tile_rows"] > 0) == (name == "bimodal"), info
     plan.destroy()
     del m
     torch.cuda.empty_cache()

@@ -1,8 +1,8 @@
 """spmv_exec_noalloc (no plan, no device allocation: the library's own
 scratch array) against the entry points it stands in for, spmv_plan_ex +
 spmv_exec on a merge-path walk plan at the same partition size in partition
-order: the same partitions, kernels and fix-up, so y must be equal bit for
-bit; and within the oracle's bound. Two calls in a row, the second on a
+order without long-row tiles: the same partitions, kernels and fix-up, so y
+must be equal bit for bit; and within the oracle's bound. Two calls in a row, the second on a
 smaller input (the scratch keeps the first call's contents)."""
 import numpy as np
 import pytest
@@ -36,7 +36,7 @@ def _both(w, alpha, beta, y0):
     x = dev(w.x)
     ipt = 16 if w.values.dtype == np.float32 else 8
     plan = m.plan(None, strategy="merge", merge_reduce="walk", items_per_thread=ipt,
-                  dispatch_order="partition")
+                  dispatch_order="partition", long_row_tiles="off")
     y_plan = _y_start(w, beta, y0, tdt)
     plan(x, y_plan, alpha, beta)
     y_na = _y_start(w, beta, y0, tdt)
