@@ -52,7 +52,8 @@ WORKLOADS = {
     "bimodal": "fp32 bimodal rows, 1,000,000^2: 1,000 x 50,000 + 5% empty + 3 per row",
     "banded": "fp32 banded decay matrix, 32,000,000 rows, 24..40 entries within |i-j| <= 1000",
 }
-KERNEL_SOURCES = ["merge_kernels.hip", "binned_kernels.hip", "device_common.hpp", "internal.hpp"]
+KERNEL_SOURCES = ["merge_kernels.hip", "tile_exec.hpp", "binned_kernels.hip", "device_common.hpp",
+                  "internal.hpp"]
 SPMM_SOURCES = ["spmm_kernels.hip", "device_common.hpp", "internal.hpp"]
 
 
@@ -407,7 +408,11 @@ def kernel_of(info) -> str:
         return "rg_spmv_kernel"
     if info["strategy"] == "group":
         return "group_spmv_kernel"
-    return "merge_stream_kernel" if info["merge_reduce"] == "stream" else "merge_spmv_kernel"
+    if info["merge_reduce"] == "stream":
+        return "merge_stream_kernel"
+    # long rows in column-blocked tiles: one grid walks the other partitions
+    # and runs the tiles
+    return "walk_tile_kernel" if info["tile_rows"] > 0 else "merge_spmv_kernel"
 
 
 def timed_median(torch, flush, reps, fn):

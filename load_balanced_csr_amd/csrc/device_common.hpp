@@ -177,6 +177,24 @@ __device__ __forceinline__ void store_quad(double* lds, int i, const Quad<double
   reinterpret_cast<f64x2*>(lds + 4 * i)[1] = v.hi;
 }
 
+// p when `in`, else exactly +0 (whatever p is: NaN and infinities too), by
+// clearing its bits rather than by a select the compiler could turn into a
+// branch.
+__device__ __forceinline__ float mask_zero(bool in, float p) {
+  return __int_as_float(__float_as_int(p) & (in ? -1 : 0));
+}
+__device__ __forceinline__ double mask_zero(bool in, double p) {
+  return __longlong_as_double(__double_as_longlong(p) & (in ? -1ll : 0ll));
+}
+
+// val * x[col] when `in`, else exactly +0, without a branch: a gather under
+// a branch is waited for before the branch joins, which would serialise a
+// partition's gathers. Masked lanes read x[0] (one cache line for all).
+template <typename V>
+__device__ __forceinline__ V masked_product(bool in, V v, const V* __restrict__ x, int col) {
+  return mask_zero(in, v * x[in ? col : 0]);
+}
+
 // Stage, with 16-byte loads, the row ends and the products of one partition:
 //   ends[4 * (q - qr0) + j] = row_ptr[4q + j] - sub     for quads [qr0, qr0 + nqr)
 //   prods[4 * (q - qn0) + j] = val[k] * x[col[k]], k = 4q + j, for [qn0, qn0 + nqn)
@@ -188,12 +206,14 @@ __device__ __forceinline__ void store_quad(double* lds, int i, const Quad<double
 // compile time, lane quads clamped into range (a clamped lane repeats the
 // last quad, which costs no extra cache lines), so the code is straight-line
 // and every load is issued before the first use.
-template <typename V, int NR, int NN>
+// MASK: the products of nonzeros k outside [lo, hi) are 0, without a gather
+// (nonzeros another kernel sums).
+template <typename V, int NR, int NN, bool MASK>
 __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, int qr0, int nqr,
                                            int sub, const int32_t* __restrict__ col,
                                            const V* __restrict__ val,
                                            const V* __restrict__ x, int qn0, int nqn,
-                                           int32_t* ends, V* prods) {
+                                           int32_t* ends, V* prods, int lo, int hi) {
   const int lane = lane_id();
   i32x4 e[NR > 0 ? NR : 1];
   i32x4 c[NN > 0 ? NN : 1];
@@ -222,7 +242,14 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
 #pragma unroll
   for (int r = 0; r < NN; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[r].set(j, v[r][j] * x[c[r][j]]);
+    for (int j = 0; j < 4; ++j) {
+      if (MASK) {
+        const int k = 4 * (qn0 + min(lane + kWave * r, nqn - 1)) + j;
+        v[r].set(j, masked_product(k >= lo && k < hi, v[r][j], x, c[r][j]));
+      } else {
+        v[r].set(j, v[r][j] * x[c[r][j]]);
+      }
+    }
   // clamped lanes rewrite the last quad with the same values: unconditional
   // stores keep the loads from being sunk into (and serialised by) branches
 #pragma unroll
@@ -234,11 +261,12 @@ __device__ __forceinline__ void stage_fast(const int32_t* __restrict__ row_ptr, 
 
 // Slow path for the one partition that reaches an array's last, partial
 // quad: element-wise guarded loads, exec-masked rounds.
-template <typename V, int RQR, int RQN>
+template <typename V, int RQR, int RQN, bool MASK = false>
 __device__ __forceinline__ void stage_safe(const int32_t* __restrict__ row_ptr, int m, int qr0,
                                         int nqr, int sub, const int32_t* __restrict__ col,
                                         const V* __restrict__ val, const V* __restrict__ x,
-                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods) {
+                                        int nnz, int qn0, int nqn, int32_t* ends, V* prods,
+                                        int lo = 0, int hi = INT_MAX) {
   const int lane = lane_id();
   for (int r = 0; r < RQR; ++r)
     if (lane + kWave * r < nqr) {
@@ -249,56 +277,61 @@ __device__ __forceinline__ void stage_safe(const int32_t* __restrict__ row_ptr, 
     if (lane + kWave * r < nqn) {
       const i32x4 c = load_quad<true>(col, qn0 + lane + kWave * r, nnz);
       Quad<V> v = load_quad<true>(val, qn0 + lane + kWave * r, nnz);
-      for (int j = 0; j < 4; ++j) v.set(j, v[j] * x[c[j]]);
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * (qn0 + lane + kWave * r) + j;
+        v.set(j, MASK ? masked_product(k >= lo && k < hi, v[j], x, c[j]) : v[j] * x[c[j]]);
+      }
       store_quad(prods, lane + kWave * r, v);
     }
 }
 
-template <typename V, int NR, int RQN>
+template <typename V, int NR, int RQN, bool MASK>
 __device__ __forceinline__ void stage_dispatch_nn(const int32_t* row_ptr, int qr0, int nqr,
                                                   int sub, const int32_t* col, const V* val,
                                                   const V* x, int qn0, int nqn, int32_t* ends,
-                                                  V* prods) {
+                                                  V* prods, int lo, int hi) {
   const int rounds = (nqn + kWave - 1) / kWave;
   if (rounds == 0)
-    stage_fast<V, NR, 0>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, 0, MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rounds == 1 || RQN < 2)
-    stage_fast<V, NR, 1>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, 1, MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rounds == 2 || RQN < 3)
-    stage_fast<V, NR, (RQN < 2 ? 1 : 2)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, (RQN < 2 ? 1 : 2), MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rounds == 3 || RQN < 4)
-    stage_fast<V, NR, (RQN < 3 ? 1 : 3)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, (RQN < 3 ? 1 : 3), MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rounds == 4 || RQN < 5)
-    stage_fast<V, NR, (RQN < 4 ? 1 : 4)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, (RQN < 4 ? 1 : 4), MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rounds == 5 || RQN < 6)
-    stage_fast<V, NR, (RQN < 5 ? 1 : 5)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, (RQN < 5 ? 1 : 5), MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else
-    stage_fast<V, NR, (RQN < 6 ? 1 : 6)>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_fast<V, NR, (RQN < 6 ? 1 : 6), MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
 }
 
 // Stage one partition (see stage_fast). RQR / RQN bound the rounds.
-template <typename V, int RQR, int RQN>
+template <typename V, int RQR, int RQN, bool MASK = false>
 __device__ __forceinline__ void stage_partition(const int32_t* __restrict__ row_ptr, int m,
                                                 int qr0, int nqr, int sub,
                                                 const int32_t* __restrict__ col,
                                                 const V* __restrict__ val,
                                                 const V* __restrict__ x, int nnz, int qn0,
-                                                int nqn, int32_t* ends, V* prods) {
+                                                int nqn, int32_t* ends, V* prods, int lo = 0,
+                                                int hi = INT_MAX) {
   static_assert(RQN <= 6, "at most 6 nonzero rounds");
   // does this partition reach an array's last, partial quad? (wave-uniform)
   const bool tail = (nqr > 0 && (m & 3) && qr0 + nqr - 1 == (m - 1) >> 2) ||
                     (nqn > 0 && (nnz & 3) && qn0 + nqn - 1 == (nnz - 1) >> 2);
   if (tail) {
-    stage_safe<V, RQR, RQN>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends, prods);
+    stage_safe<V, RQR, RQN, MASK>(row_ptr, m, qr0, nqr, sub, col, val, x, nnz, qn0, nqn, ends,
+                                  prods, lo, hi);
     return;
   }
   const int rrounds = (nqr + kWave - 1) / kWave;
   if (rrounds == 0)
-    stage_dispatch_nn<V, 0, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, 0, RQN, MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else if (rrounds == 1 || RQR < 2)
-    stage_dispatch_nn<V, 1, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, 1, RQN, MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
   else
-    stage_dispatch_nn<V, RQR, RQN>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods);
+    stage_dispatch_nn<V, RQR, RQN, MASK>(row_ptr, qr0, nqr, sub, col, val, x, qn0, nqn, ends, prods, lo, hi);
 }
 
 // ---- cross-lane moves in DPP form (gfx9 encodings) ---------------------------

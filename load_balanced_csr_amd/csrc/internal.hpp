@@ -78,6 +78,7 @@ enum StatSlot : int {
 // ---- column-blocked tiles of long rows (tile_kernels.hip) ------------------------
 constexpr int kTileBytes = 16384;   // x block of one tile in LDS: 4096 fp32 / 2048 fp64
 constexpr int kTileRows = 64;       // tile rows one workgroup takes per column block
+constexpr int kTileBatch = 4;      // tile rows whose quads a wave requests together
 constexpr int kTileRowInts = 8;     // per tile row: row, first / end nonzero, first / end partition
 constexpr int kTileMinPerBlock = 64;  // a row is tiled when its interior run holds this many
                                       // nonzeros per column block on average
@@ -93,12 +94,16 @@ struct TilePlan {
   int32_t* skip;          // p_max: 1 where the walk kernel skips the partition
   int32_t* scan;          // p_max: flags, then their prefix sums
   int32_t* list;          // p_max: the walk kernel's dispatch list
+  int32_t* mask_end;      // p_max: the walk kernel ignores nonzeros below this
+  int32_t* mask_start;    // p_max: ... and from this one on (tile rows' ends)
+  const int32_t* row_ptr;
   void* scan_temp;        // scan_temp_bytes(p_max)
 };
-// Tile rows, segments, skipped partitions (carries zeroed) and the walk
-// dispatch list, every launch gated by the statistics (kStatTileOk, then
-// kStatTileRows). Tiles are kept only when their runs hold at least half of
-// the nnz nonzeros; a plan that keeps them takes the partition order.
+// Tile rows (whole rows: their interior partitions skipped with zero
+// carries, their nonzeros in the first and last partition masked off for
+// the walk kernel), segments and the walk dispatch list, every launch gated
+// by the statistics (kStatTileOk, then kStatTileRows). Tiles are kept only
+// when their rows hold at least half of the nnz nonzeros.
 hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const int32_t* split_nz,
                             const int32_t* col_idx, int64_t M, int64_t nnz, int64_t p_max,
                             int64_t* stats, int32_t* carry_row, void* carry_val, int vbytes,
@@ -122,10 +127,7 @@ struct TileArgs {
   int32_t x_aligned;      // x is 16-byte aligned (direct-to-LDS staging)
 };
 template <typename V>
-hipError_t launch_tiles(const TileArgs<V>& a, hipStream_t s);
-// ev_end (may be null) is recorded by the reduction's dispatch at its end
-template <typename V>
-hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s, hipEvent_t ev_end);
+hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s);
 
 // Error bits of stats[kStatError].
 constexpr int64_t kErrRowPtr = 1;     // row_ptr is not a CSR row pointer array
@@ -241,6 +243,10 @@ struct MergeArgs {
   const int32_t* win_span;  // per stream workgroup: kWinTable int32 (window intervals)
   const int32_t* part_order;  // walk kernel: dispatch slot -> partition (null: identity)
   int32_t n_dispatch;    // walk kernel: dispatch slots (0: P)
+  // walk kernel with long-row tiles: per partition, the nonzeros it leaves
+  // to the tiles ([n0, mask_end) and [mask_start, n1)); null without tiles
+  const int32_t* mask_end;
+  const int32_t* mask_start;
 };
 
 // Streaming read of `bytes` (multiple of 16) at data; the xor of each 4 KiB
@@ -260,9 +266,13 @@ hipError_t launch_stream_probe(const int32_t* row_ptr, const int32_t* col_idx, c
                                int64_t M, int64_t nnz, int vbytes, int ipt, void* y,
                                hipStream_t s);
 
+// The walk or stream kernel (with tiles, for plans that have long-row
+// tiles: the walk over the partitions they leave and the tiles, one grid),
+// then the walk's carry fix-up. ev0 / ev1 (may be null) are recorded by the
+// main kernel's dispatch at its start and end.
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,
-                        hipEvent_t ev1);
+                        hipEvent_t ev1, const TileArgs<V>* tiles = nullptr);
 
 // ---- multi-vector exec (SpMM) -------------------------------------------------------
 // Y = alpha * A X + beta * Y, X N x k and Y M x k row-major (k <= 64 per

@@ -24,23 +24,29 @@
 // row's carries with a wave segmented scan, deterministically.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "tile_exec.hpp"
 
 #include <limits.h>
 
 namespace spmv {
 namespace {
 
+// LDS of one wave's partition: row ends (int32) and sums / products (V),
+// T + 8 of each.
 template <typename V, int IPT>
-__global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a) {
+constexpr int walk_lds_bytes() { return kWavesPerBlock * (kWave * IPT + 8) * (4 + (int)sizeof(V)); }
+
+// One wave walks partition slot `slot` of the dispatch (all P partitions,
+// or the n_dispatch of the plan's list), with its LDS at s_end / s_val.
+// MASK: with long-row tiles, a partition leaves the nonzeros outside
+// [mask_end[p], mask_start[p]) to them (their products are 0 here).
+template <typename V, int IPT, bool MASK>
+__device__ __forceinline__ void walk_partition(const MergeArgs<V>& a, int slot, int32_t* s_end,
+                                               V* s_val) {
   constexpr int T = kWave * IPT;
   constexpr int RQ = (T / 4 + 2 + kWave - 1) / kWave;   // quad rounds per array
-  __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
-  __shared__ __attribute__((aligned(16))) V s_val[kWavesPerBlock][T + 8];
-
   const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  int p = blk * kWavesPerBlock + wave;
+  int p = slot;
   if (p >= (a.n_dispatch ? a.n_dispatch : a.P)) return;
   // column dispatch order, or the partitions that long-row tiles leave: the
   // plan's list of partitions (a uniform read of a table nothing here writes)
@@ -59,12 +65,14 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   const int nqr = nrows > 0 ? ((r1 >> 2) - qr0 + 1) : 0;
   const int qn0 = n0 >> 2;
   const int nqn = nnzc > 0 ? (((n1 - 1) >> 2) - qn0 + 1) : 0;
-  int32_t* re = s_end[wave] + ((r0 + 1) & 3);
-  V* vb = s_val[wave];
+  int32_t* re = s_end + ((r0 + 1) & 3);
+  V* vb = s_val;
   V* prod_q = vb + (T + 8 - 4 * nqn);
   V* prod = prod_q + (n0 & 3);
-  stage_partition<V, RQ, RQ>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x, a.nnz,
-                             qn0, nqn, s_end[wave], prod_q);
+  const int mlo = MASK ? a.mask_end[p] : 0;
+  const int mhi = MASK ? a.mask_start[p] : INT_MAX;
+  stage_partition<V, RQ, RQ, MASK>(a.row_ptr, a.M + 1, qr0, nqr, n0, a.col_idx, a.val, a.x,
+                                   a.nnz, qn0, nqn, s_end, prod_q, mlo, mhi);
   wave_sync();
 
   // ---- 2. per-lane start by binary search, then walk IPT units --------------
@@ -114,6 +122,42 @@ __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a
   if (lane == kWave - 1) {
     a.carry_row[p] = r1;
     a.carry_val[p] = s;
+  }
+}
+
+template <typename V, int IPT, bool MASK>
+__global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a) {
+  constexpr int T = kWave * IPT;
+  __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
+  __shared__ __attribute__((aligned(16))) V s_val[kWavesPerBlock][T + 8];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
+  walk_partition<V, IPT, MASK>(a, blk * kWavesPerBlock + wave, s_end[wave], s_val[wave]);
+}
+
+// The walk over the partitions long-row tiles leave and the tiles
+// themselves, in one grid: workgroups [0, walk_blocks) walk (one partition
+// per wave, masked), the rest each take one tile. The two share no output
+// (tiles write only their block partials). Workgroups are dispatched about
+// in index order, so the walk of the short rows runs first, with the tiles
+// filling the CUs as its workgroups end, in one launch. One LDS buffer
+// serves either role.
+template <typename V, int IPT>
+__global__ __launch_bounds__(kBlock) void walk_tile_kernel(const MergeArgs<V> a,
+                                                           const TileArgs<V> t, int walk_blocks) {
+  constexpr int T = kWave * IPT;
+  constexpr int LDS = walk_lds_bytes<V, IPT>() > kTileBytes ? walk_lds_bytes<V, IPT>() : kTileBytes;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  const int b = blockIdx.x;
+  if (b < walk_blocks) {   // workgroup-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int blk = a.xcd_remap ? xcd_tile(b, 0, walk_blocks) : b;
+    int32_t* ends = reinterpret_cast<int32_t*>(lds) + wave * (T + 8);
+    V* vals = reinterpret_cast<V*>(lds + kWavesPerBlock * (T + 8) * 4) + wave * (T + 8);
+    walk_partition<V, IPT, true>(a, blk * kWavesPerBlock + wave, ends, vals);
+  } else {
+    tile_block<V>(t, xcd_tile(b, walk_blocks, (int)gridDim.x - walk_blocks),
+                  reinterpret_cast<V*>(lds));
   }
 }
 
@@ -523,18 +567,27 @@ hipError_t launch_window(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, h
 }
 
 template <typename V, int IPT>
-hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_main(const MergeArgs<V>& a, const TileArgs<V>* tiles, hipStream_t s,
+                       hipEvent_t ev0, hipEvent_t ev1) {
   const int slots = a.stream || !a.n_dispatch ? a.P : a.n_dispatch;
   const int blocks = (slots + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (a.stream && a.x_window == 1) {
+  if (tiles) {
+    if (a.stream || !a.mask_end || !a.n_dispatch) return hipErrorInvalidValue;
+    const int64_t n_tiles = (int64_t)tiles->ngroups * tiles->nb;
+    if (n_tiles + blocks > 0x7fffffffll) return hipErrorInvalidValue;
+    launch_timed(walk_tile_kernel<V, IPT>, dim3((unsigned)(blocks + n_tiles)), dim3(kBlock), 0, s,
+                 ev0, ev1, a, *tiles, blocks);
+  } else if (a.stream && a.x_window == 1) {
     return launch_window<V, IPT, 1>(a, s, ev0, ev1);
   } else if (a.stream && a.x_window > 1) {
     return launch_window<V, IPT, kWinIntervals>(a, s, ev0, ev1);
   } else if (a.stream) {
     launch_timed(merge_stream_kernel<V, IPT, 0, kWavesPerBlock>, dim3(blocks), dim3(kBlock), 0,
                  s, ev0, ev1, a, a.row_bounds, a.win_span);
+  } else if (a.mask_end) {
+    launch_timed(merge_spmv_kernel<V, IPT, true>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
   } else {
-    launch_timed(merge_spmv_kernel<V, IPT>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
+    launch_timed(merge_spmv_kernel<V, IPT, false>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
   }
   return hipGetLastError();
 }
@@ -543,15 +596,15 @@ hipError_t launch_main(const MergeArgs<V>& a, hipStream_t s, hipEvent_t ev0, hip
 
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,
-                        hipEvent_t ev1) {
+                        hipEvent_t ev1, const TileArgs<V>* tiles) {
   if (a.P <= 0) return hipSuccess;
   hipError_t err;
   // ev0 / ev1 bracket the main kernel alone (recorded by its dispatch)
   switch (ipt) {
-    case 4: err = launch_main<V, 4>(a, s, ev0, ev1); break;
-    case 7: err = launch_main<V, 7>(a, s, ev0, ev1); break;
-    case 8: err = launch_main<V, 8>(a, s, ev0, ev1); break;
-    case 16: err = launch_main<V, 16>(a, s, ev0, ev1); break;
+    case 4: err = launch_main<V, 4>(a, tiles, s, ev0, ev1); break;
+    case 7: err = launch_main<V, 7>(a, tiles, s, ev0, ev1); break;
+    case 8: err = launch_main<V, 8>(a, tiles, s, ev0, ev1); break;
+    case 16: err = launch_main<V, 16>(a, tiles, s, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
@@ -566,8 +619,8 @@ hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_
 }
 
 template hipError_t launch_merge<float>(const MergeArgs<float>&, int, hipStream_t, hipEvent_t,
-                                        hipEvent_t);
+                                        hipEvent_t, const TileArgs<float>*);
 template hipError_t launch_merge<double>(const MergeArgs<double>&, int, hipStream_t,
-                                         hipEvent_t, hipEvent_t);
+                                         hipEvent_t, hipEvent_t, const TileArgs<double>*);
 
 }  // namespace spmv

@@ -8,14 +8,19 @@
 // page's results section reports the same effect of caching x, 1.81x on its
 // GPU). Here the partitions that lie entirely inside one row (no row end in
 // them) are regrouped by column: a long row's interior nonzeros are cut at
-// fixed column-block boundaries (BC columns, 16 KiB of x), and a workgroup
-// (a tile) takes one column block and the segments of up to kTileRows long
-// rows in it: it stages that block of x in LDS once and gathers from LDS.
-// Every segment's sum goes to partial[row][block]; a reduction adds
-// alpha * sum over blocks, in block order, to each row's y after the walk
-// kernel and the carry fix-up. The walk kernel skips those partitions (their
-// carries are 0), so every nonzero is summed exactly once and the result is
-// bitwise reproducible for a fixed plan.
+// fixed column-block boundaries (BC columns, 16 KiB of x) -- all of such a
+// row's nonzeros, those in its first and last partition too --, and a
+// workgroup (a tile) takes one column block and the segments of up to
+// kTileRows long rows in it: it stages that block of x in LDS once and
+// gathers from LDS. Every segment's sum goes to partial[row][block]; a
+// reduction adds alpha * sum over blocks, in block order, to each row's y
+// after the walk and the carry fix-up. The walk skips the rows' interior
+// partitions (their carries are 0) and leaves the rows' nonzeros in their
+// first and last partition out (masked), so every nonzero is summed exactly
+// once and the result is bitwise reproducible for a fixed plan. The walk
+// and the tiles run in one grid (merge_kernels.hip; the tiles' device code
+// is in tile_exec.hpp); this file builds the plan's tables and holds the
+// reduction.
 //
 // Correctness never depends on the columns: segments partition each row's
 // interior range whatever col_idx holds, and a column outside the tile's
@@ -63,13 +68,15 @@ __global__ __launch_bounds__(kBlock) void tile_flags_kernel(
   flags[p] = f;
 }
 
-// After the exclusive scan of the flags: the tile-row table (row, first and
-// end nonzero of the interior run, first and end partition), at most cap
-// rows; stats[kStatTileRows] = their number.
+// After the exclusive scan of the flags: the tile-row table (row, its first
+// and end nonzero -- the whole row --, the first interior partition and the
+// row's end partition), at most cap rows; stats[kStatTileRows] = their
+// number, stats[kStatTileEntries] = their nonzeros.
 __global__ __launch_bounds__(kBlock) void tile_rows_kernel(
-    const int32_t* __restrict__ split_row, const int32_t* __restrict__ split_nz, int64_t p_max,
-    int32_t M, int64_t min_entries, int32_t cap, const int32_t* __restrict__ scan,
-    int64_t* __restrict__ stats, int32_t* __restrict__ rows) {
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ split_row,
+    const int32_t* __restrict__ split_nz, int64_t p_max, int32_t M, int64_t min_entries,
+    int32_t cap, const int32_t* __restrict__ scan, int64_t* __restrict__ stats,
+    int32_t* __restrict__ rows) {
   const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (p >= p_max || stats[kStatTileOk] == 0) return;
   const int64_t P = stats[kStatParts];
@@ -85,28 +92,26 @@ __global__ __launch_bounds__(kBlock) void tile_rows_kernel(
   if (f && i < cap) {
     int32_t* t = rows + (int64_t)kTileRowInts * i;
     t[0] = r;
-    t[1] = split_nz[p];
-    t[2] = split_nz[q];
+    t[1] = row_ptr[r];
+    t[2] = row_ptr[r + 1];
     t[3] = (int32_t)p;
     t[4] = (int32_t)q;
     atomicAdd((unsigned long long*)&stats[kStatTileEntries],
-              (unsigned long long)((int64_t)split_nz[q] - split_nz[p]));
+              (unsigned long long)((int64_t)row_ptr[r + 1] - row_ptr[r]));
   }
   if (p == P - 1) stats[kStatTileRows] = min((int64_t)cap, (int64_t)i + (f ? 1 : 0));
 }
 
-// Tiles are worth their extra launches and their partition order only when
-// their runs hold at least half of the nonzeros; a plan that keeps them
-// deals the walk kernel's partitions in partition order.
+// Tiles are worth their extra launches only when their rows hold at least
+// half of the nonzeros.
 __global__ __launch_bounds__(64) void tile_gate_kernel(int64_t nnz, int64_t* stats) {
   if (threadIdx.x != 0) return;
   if (2 * stats[kStatTileEntries] < nnz) stats[kStatTileRows] = 0;
-  if (stats[kStatTileRows] > 0) stats[kStatOrder] = 0;
 }
 
-// seg[i][b] = first interior nonzero of tile row i whose column is >= b * bc
-// (b = 0..nb; the ends are the run's bounds), made non-decreasing in b so
-// that the segments always partition the run.
+// seg[i][b] = first nonzero of tile row i whose column is >= b * bc
+// (b = 0..nb; the ends are the row's bounds), made non-decreasing in b so
+// that the segments always partition the row.
 __global__ __launch_bounds__(kBlock) void tile_seg_kernel(const int32_t* __restrict__ rows,
                                                           const int32_t* __restrict__ col_idx,
                                                           int32_t nb, int32_t bc, int64_t n_max,
@@ -137,16 +142,18 @@ __global__ __launch_bounds__(kBlock) void tile_seg_kernel(const int32_t* __restr
 }
 
 // Running maximum along each tile row's boundaries (only changes anything
-// when a row's interior columns are not sorted), then the row's partitions
-// marked as skipped by the walk kernel, with zero carries that the fix-up
-// adds to the row harmlessly. One thread per tile row.
-__global__ __launch_bounds__(kBlock) void tile_finish_kernel(const int32_t* __restrict__ rows,
-                                                             int32_t nb, int64_t n_max,
-                                                             const int64_t* __restrict__ stats,
-                                                             int32_t* __restrict__ seg,
-                                                             int32_t* __restrict__ skip,
-                                                             int32_t* __restrict__ carry_row,
-                                                             void* carry_val, int vbytes) {
+// when a row's columns are not sorted); the row's interior partitions marked
+// as skipped by the walk kernel, with zero carries that the fix-up adds to
+// the row harmlessly; and the row's nonzeros in its first and last
+// partition masked off for the walk kernel (so its carry there is 0 and its
+// y gets beta * y only). A partition holds at most one tile row's start and
+// one tile row's end, so no two threads write the same mask. One thread per
+// tile row.
+__global__ __launch_bounds__(kBlock) void tile_finish_kernel(
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ split_nz, int32_t nb,
+    int64_t n_max, const int64_t* __restrict__ stats, int32_t* __restrict__ seg,
+    int32_t* __restrict__ skip, int32_t* __restrict__ mask_end, int32_t* __restrict__ mask_start,
+    int32_t* __restrict__ carry_row, void* carry_val, int vbytes) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= n_max || i >= stats[kStatTileRows]) return;
   int32_t* s = seg + i * (nb + 1);
@@ -156,12 +163,17 @@ __global__ __launch_bounds__(kBlock) void tile_finish_kernel(const int32_t* __re
     s[b] = run;
   }
   const int32_t* row = rows + kTileRowInts * i;
-  for (int32_t p = row[3]; p < row[4]; ++p) {
+  const int32_t p_first = row[3], p_end = row[4];
+  for (int32_t p = p_first; p < p_end; ++p) {
     skip[p] = 1;
     carry_row[p] = row[0];
     if (vbytes == 4) static_cast<float*>(carry_val)[p] = 0.f;
     else static_cast<double*>(carry_val)[p] = 0.0;
   }
+  // the row's start, in the partition before its interior run
+  if (p_first > 0 && row[1] < split_nz[p_first]) mask_start[p_first - 1] = row[1];
+  // the row's end partition
+  if (row[2] > split_nz[p_end]) mask_end[p_end] = row[2];
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* __restrict__ a, int64_t n,
@@ -199,66 +211,6 @@ __global__ __launch_bounds__(kBlock) void tile_list_kernel(const int32_t* __rest
 
 // ---- exec ------------------------------------------------------------------------
 
-template <typename V>
-__device__ __forceinline__ V tile_x(const V* xs, const V* __restrict__ x, int c, int64_t c0,
-                                    int clen) {
-  const unsigned lc = (unsigned)((int64_t)c - c0);
-  return lc < (unsigned)clen ? xs[lc] : x[c];
-}
-
-// One workgroup per tile (column block b, group g of kTileRows tile rows):
-// the block of x staged in LDS (direct-to-LDS 16-byte loads when x is 16-byte
-// aligned), then each wave takes every fourth row of the group and streams
-// its segment in 16-byte quads (entries outside the segment masked), sums
-// the products lane-wise and across the wave by DPP moves; lane 63 writes
-// partial[row][b].
-template <typename V>
-__global__ __launch_bounds__(kBlock) void tile_spmv_kernel(const TileArgs<V> a) {
-  constexpr int BC = kTileBytes / (int)sizeof(V);
-  constexpr int E = 16 / (int)sizeof(V);   // elements per 16-byte chunk
-  __shared__ __attribute__((aligned(16))) V xs[BC];
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = xcd_tile(blockIdx.x, 0, gridDim.x);
-  const int b = t / a.ngroups, g = t - b * a.ngroups;
-  const int64_t c0 = (int64_t)b * BC;
-  const int clen = (int)min((int64_t)BC, (int64_t)a.N - c0);
-  if (a.x_aligned) {
-    const int nch = clen / E;
-#pragma unroll
-    for (int r = 0; r < BC / E / kBlock; ++r) {
-      const int first = r * kBlock + wave * kWave;
-      if (first < nch && first + lane < nch) lds_dma16(a.x + c0 + E * (first + lane), xs + E * first);
-    }
-    if ((int)threadIdx.x < clen - E * nch) xs[E * nch + threadIdx.x] = a.x[c0 + E * nch + threadIdx.x];
-  } else {
-    for (int k = threadIdx.x; k < clen; k += kBlock) xs[k] = a.x[c0 + k];
-  }
-  wait_vmem();
-  __syncthreads();
-  const int end = min(g * kTileRows + kTileRows, a.n_rows);
-  for (int i = g * kTileRows + wave; i < end; i += kWavesPerBlock) {
-    const int32_t s0 = a.seg[(int64_t)i * (a.nb + 1) + b];
-    const int32_t s1 = a.seg[(int64_t)i * (a.nb + 1) + b + 1];
-    const int q1 = (s1 + 3) >> 2;
-    V acc = V(0);
-    for (int q = (s0 >> 2) + lane; q < q1; q += kWave) {
-      // the array's last quad may be partial: element loads for it alone
-      const bool full = 4 * q + 3 < a.nnz;
-      const i32x4 c = full ? ld_stream(reinterpret_cast<const i32x4*>(a.col_idx) + q)
-                           : load_quad<true>(a.col_idx, q, a.nnz);
-      const Quad<V> v = full ? load_quad<false>(a.val, q, 0) : load_quad<true>(a.val, q, a.nnz);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 4 * q + j;
-        if (k >= s0 && k < s1) acc += v[j] * tile_x(xs, a.x, c[j], c0, clen);
-      }
-    }
-    acc = wave_sum_to_last(acc);
-    if (lane == kWave - 1) a.partial[(int64_t)i * a.nb + b] = acc;
-  }
-}
-
 // y[row] += alpha * (sum of the row's block partials, in block order), one
 // wave per tile row.
 template <typename V>
@@ -293,15 +245,22 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
   if (e != hipSuccess) return e;
   if ((e = exclusive_scan_i32(tp.scan, p_max, stats + kStatTileOk, tp.scan_temp, s)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(tile_rows_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, split_row,
-                     split_nz, p_max, (int32_t)M, tp.min_entries, tp.cap, tp.scan, stats, tp.rows);
+  hipLaunchKernelGGL(tile_rows_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.row_ptr,
+                     split_row, split_nz, p_max, (int32_t)M, tp.min_entries, tp.cap, tp.scan,
+                     stats, tp.rows);
   hipLaunchKernelGGL(tile_gate_kernel, dim3(1), dim3(64), 0, s, nnz, stats);
   hipLaunchKernelGGL(tile_seg_kernel, dim3(grid_for((int64_t)tp.cap * (tp.nb + 1), kBlock)), blk,
                      0, s, tp.rows, col_idx, tp.nb, tp.bc, (int64_t)tp.cap, stats, tp.seg);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max, 0,
+  const unsigned fill_blocks = std::min<unsigned>(grid_for(p_max, kBlock), 4096);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.skip, p_max, 0,
                      stats + kStatTileRows);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.mask_end, p_max, 0,
+                     stats + kStatTileRows);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.mask_start, p_max,
+                     INT_MAX, stats + kStatTileRows);
   hipLaunchKernelGGL(tile_finish_kernel, dim3(grid_for(tp.cap, kBlock)), blk, 0, s, tp.rows,
-                     tp.nb, (int64_t)tp.cap, stats, tp.seg, tp.skip, carry_row, carry_val, vbytes);
+                     split_nz, tp.nb, (int64_t)tp.cap, stats, tp.seg, tp.skip, tp.mask_end,
+                     tp.mask_start, carry_row, carry_val, vbytes);
   hipLaunchKernelGGL(tile_keep_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max,
                      stats, tp.scan);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -314,26 +273,15 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
 }
 
 template <typename V>
-hipError_t launch_tiles(const TileArgs<V>& a, hipStream_t s) {
+hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  const int64_t tiles = (int64_t)a.ngroups * a.nb;
-  if (tiles > 0x7fffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tile_spmv_kernel<V>, dim3((unsigned)tiles), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(tile_reduce_kernel<V>,
+                     dim3((unsigned)(((int64_t)a.n_rows * kWave + kBlock - 1) / kBlock)),
+                     dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename V>
-hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s, hipEvent_t ev_end) {
-  if (a.n_rows <= 0) return hipSuccess;
-  launch_timed(tile_reduce_kernel<V>,
-               dim3((unsigned)(((int64_t)a.n_rows * kWave + kBlock - 1) / kBlock)), dim3(kBlock),
-               0, s, nullptr, ev_end, a);
-  return hipGetLastError();
-}
-
-template hipError_t launch_tiles<float>(const TileArgs<float>&, hipStream_t);
-template hipError_t launch_tiles<double>(const TileArgs<double>&, hipStream_t);
-template hipError_t launch_tile_reduce<float>(const TileArgs<float>&, hipStream_t, hipEvent_t);
-template hipError_t launch_tile_reduce<double>(const TileArgs<double>&, hipStream_t, hipEvent_t);
+template hipError_t launch_tile_reduce<float>(const TileArgs<float>&, hipStream_t);
+template hipError_t launch_tile_reduce<double>(const TileArgs<double>&, hipStream_t);
 
 }  // namespace spmv

@@ -16,11 +16,13 @@ from gpu_util import DevMatrix, check, dev, log, run
 pytestmark = pytest.mark.gpu
 
 
-def _long_rows(M, N, n_long, long_len, seed, dt=np.float32, short=3):
+def _long_rows(M, N, n_long, long_len, seed, dt=np.float32, short=3, last_long=False):
     rng = np.random.default_rng(seed)
     L = np.full(M, short, np.int64)
     L[rng.choice(M, n_long, replace=False)] = long_len
     L[rng.choice(M, M // 20, replace=False)] = 0
+    if last_long:
+        L[-1] = long_len     # the array's last (partial) quad in a tile row
     w = synth.random_csr(M, N, L, seed + 1)
     if dt != np.float32:
         w = synth.Workload("long_f64", M, N, w.row_ptr, w.col_idx, w.values.astype(dt),
@@ -34,6 +36,10 @@ CASES = {
     "many_blocks": lambda: _long_rows(20_000, 200_000, 30, 60_000, 2),
     "odd_nnz": lambda: _long_rows(5001, 50_003, 11, 24_001, 3, short=5),
     "f64": lambda: _long_rows(8000, 24_000, 25, 15_000, 4, np.float64),
+    # more tile rows than one workgroup's group, the last row among them,
+    # an odd entry count
+    "two_groups_last_row": lambda: _long_rows(4003, 40_000, 70, 12_345, 6, last_long=True),
+    "f64_last_row": lambda: _long_rows(3001, 9_001, 9, 7_001, 7, np.float64, last_long=True),
 }
 
 
