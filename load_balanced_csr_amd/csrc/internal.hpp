@@ -22,6 +22,7 @@ inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStrea
 
 constexpr int kWave = 64;             // CDNA4 wavefront
 constexpr int kBlock = 256;           // threads per workgroup (4 waves)
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU, the most one workgroup may take
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
 constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;   // L2 of one XCD

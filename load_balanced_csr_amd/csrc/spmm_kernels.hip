@@ -33,24 +33,18 @@ namespace {
 
 constexpr int kSpmmBatch = 4;
 
-// LDS of one wave (bytes): the staged row pointers, column indices and
-// values (cap entries each, 16-byte aligned); once the walk is done the same
-// bytes hold the head / tail vectors (64 lanes x 16 bytes each) and the
-// per-slot records (5 x 64 int32).
+// Bytes of the per-slot records of the merge kernel's slot combine (head /
+// tail vectors, 64 lanes x 16 bytes each, and 5 x 64 int32), which overlay
+// the staged partition once the walk is done.
 constexpr int kSpmmRecordBytes = 2 * kWave * 16 + 5 * kWave * 4;
-__host__ __device__ constexpr int spmm_wave_lds(int cap, int vbytes) {
-  return 2 * cap * 4 + cap * vbytes > kSpmmRecordBytes ? 2 * cap * 4 + cap * vbytes
-                                                       : kSpmmRecordBytes;
-}
 
-// LDS of one wave of the merge-slot kernel (walk plans): a walk partition
-// holds at most T <= cap - 8 rows plus nonzeros, and staging an array of n
-// words takes at most n + 7, so the row pointers and the column indices
-// share one region of cap + 12 words (the columns start at the first 16-byte
-// boundary past the row pointers); the values follow it. The records of the
-// slot combine overlay the same space. Half the footprint of three separate
-// regions: twice the waves per CU for this gather-bound kernel.
-__host__ __device__ constexpr int spmm_walk_wave_lds(int cap, int vbytes) {
+// LDS of one wave's partition (bytes), both kernels: a partition holds at
+// most cap - 8 rows plus nonzeros (walk: T; stream: T + T/8), and staging an
+// array of n words takes at most n + 7, so the row pointers and the column
+// indices share one region of cap + 12 words (the columns start at the
+// first 16-byte boundary past the row pointers); the values follow it.
+// Two thirds of the footprint of three separate regions.
+__host__ __device__ constexpr int spmm_wave_lds(int cap, int vbytes) {
   return (cap + 12) * 4 + cap * vbytes > kSpmmRecordBytes ? (cap + 12) * 4 + cap * vbytes
                                                           : kSpmmRecordBytes;
 }
@@ -163,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   // every partition holds at most cap - 8 rows plus nonzeros (walk: T; stream:
   // T + T/8), which the shared LDS region relies on; never stage past it
   if (tot > a.cap - 8) return;
-  unsigned char* base = s_dyn + (size_t)wave * spmm_walk_wave_lds(a.cap, sizeof(V));
+  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V));
   int32_t* s_rp = reinterpret_cast<int32_t*>(base);
   int32_t* s_col = s_rp + ((R + 8 + 3) & ~3);
   int32_t* s_val = s_rp + (a.cap + 12);   // cap entries of V, staged as int32 words
@@ -315,35 +309,47 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
 }
 
 // The same product for plans whose partitions hold whole rows (every row
-// <= T/8 entries, the stream layout). Rows go to slots instead of equal
-// runs: G slots share a row when the partition has fewer rows than slots
-// (G the largest power of two with rows * G <= slots), each taking every
-// G-th of the row's nonzeros in batches of 8 (all X-row loads first), and
-// meet by cross-lane adds. A round finishes S / G rows at once, so Y rows
-// are written together (coalesced) and no slot walks a row end alone.
-template <typename V, int KL, int VE, bool OFF32>
-__global__ __launch_bounds__(kBlock) void spmm_rows_kernel(const SpmmArgs<V> a) {
+// <= T/8 entries, the stream layout): one wave per partition, staging its
+// row pointers, columns and values in LDS (direct-to-LDS loads; row
+// pointers and columns share one region). Rows go to slots instead of
+// equal runs: G slots share a row when the partition has fewer rows than
+// slots (G the largest power of two with rows * G <= slots), each taking
+// every G-th of the row's nonzeros in batches of 8 (all X-row loads first),
+// and meet by cross-lane adds. A round finishes S / G rows at once, so Y
+// rows are written together (coalesced) and no slot walks a row end alone.
+// The kernel is bound by the rate of X-row gathers that miss the CU's L1:
+// a workgroup holds PPB consecutive partitions, so the waves of a CU walk
+// neighbouring rows together and share the X rows around them in L1
+// (banded, 8 RHS: 1 partition per workgroup 5.0 ms, 4: 4.2 ms, 8: 3.2 ms).
+template <typename V, int KL, int VE, bool OFF32, int PPB>
+__global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V> a) {
   constexpr int S = kWave / KL;   // slots per wave
   constexpr int B = 8;
   typedef Vec<V, VE> VV;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
 
   const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wave = PPB == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  const int p = blk * kWavesPerBlock + wave;
-  if (p >= a.P) return;
+  const int p = blk * PPB + wave;
+  if (p >= a.P) return;   // wave-uniform; the waves never wait for each other
   const int r0 = a.row_bounds[2 * p];
   const int n0 = a.row_bounds[2 * p + 1];
   const int r1 = a.row_bounds[2 * p + 2];
   const int n1 = a.row_bounds[2 * p + 3];
   const int R = r1 - r0, nloc = n1 - n0;
   if (R == 0) return;
+  // a stream partition holds at most T + T/8 = cap - 8 rows plus nonzeros,
+  // which the shared LDS region relies on; never stage past it
+  if (R + nloc > a.cap - 8) return;
 
-  unsigned char* base = s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V));
-  int32_t* s_rp = reinterpret_cast<int32_t*>(base);
-  int32_t* s_col = s_rp + a.cap;
-  int32_t* s_val = s_col + a.cap;
+  // row pointers, then the columns from the next 16-byte boundary (rows +
+  // nonzeros <= cap - 8, each staged array takes at most its count + 7
+  // words), in one region of cap + 12 words; the values after it
+  int32_t* s_rp =
+      reinterpret_cast<int32_t*>(s_dyn + (size_t)wave * spmm_wave_lds(a.cap, sizeof(V)));
+  int32_t* s_col = s_rp + ((R + 1 + 7 + 3) & ~3);
+  int32_t* s_val = s_rp + a.cap + 12;
   constexpr int W = sizeof(V) / 4;
   stage_dma(s_rp, a.row_ptr, r0, R + 1, a.M + 1);
   stage_dma(s_col, a.col_idx, n0, nloc, a.nnz);
@@ -372,12 +378,12 @@ __global__ __launch_bounds__(kBlock) void spmm_rows_kernel(const SpmmArgs<V> a) 
   for (int rb = 0; rb < R; rb += rpr) {
     const int rr = rb + grp;
     const bool live = rr < R;
-    const int ra = live ? rpl[rr] - n0 : 0;
+    const int rs = live ? rpl[rr] - n0 : 0;
     const int re = live ? rpl[rr + 1] - n0 : 0;
     VV acc;
 #pragma unroll
     for (int q = 0; q < VE; ++q) acc.v[q] = V(0);
-    for (int jb = ra + part; jb < re; jb += G * B) {
+    for (int jb = rs + part; jb < re; jb += G * B) {
       int cs[B];
 #pragma unroll
       for (int u = 0; u < B; ++u) cs[u] = coll[min(jb + G * u, re - 1)];
@@ -485,20 +491,38 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   *yp = fma(a.alpha, s + extra, *yp);
 }
 
+template <typename V, int KL, int VE, bool OFF32>
+void launch_rows(const SpmmArgs<V>& a, int ppb, size_t lds_wave, hipStream_t s, hipEvent_t ev0,
+                 hipEvent_t ev1) {
+  const dim3 g((a.P + ppb - 1) / ppb);
+  const size_t lds = (size_t)ppb * lds_wave;
+  switch (ppb) {
+    case 8: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 8>, g, dim3(8 * kWave), lds, s, ev0, ev1, a); break;
+    case 4: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 4>, g, dim3(4 * kWave), lds, s, ev0, ev1, a); break;
+    case 2: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 2>, g, dim3(2 * kWave), lds, s, ev0, ev1, a); break;
+    default: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 1>, g, dim3(kWave), lds, s, ev0, ev1, a); break;
+  }
+}
+
 template <typename V, int KL, int VE>
 hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  const int blocks = (a.P + kWavesPerBlock - 1) / kWavesPerBlock;
-  const size_t lds = (size_t)kWavesPerBlock * (a.stream ? spmm_wave_lds(a.cap, sizeof(V))
-                                                        : spmm_walk_wave_lds(a.cap, sizeof(V)));
   // bytes from X to the end of its last row's k columns
   const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
   const bool off32 = xspan < (1ull << 32);
-  const dim3 g(blocks), b(kBlock);
-  if (a.stream && off32)
-    launch_timed(spmm_rows_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
-  else if (a.stream)
-    launch_timed(spmm_rows_kernel<V, KL, VE, false>, g, b, lds, s, ev0, ev1, a);
-  else if (off32)
+  const size_t lds_wave = (size_t)spmm_wave_lds(a.cap, sizeof(V));
+  if (a.stream) {
+    // up to 8 consecutive partitions per workgroup, as many as one CU's LDS
+    // holds (16 measured no better: banded 3.15 against 3.19 ms, fp64
+    // Laplacian 0.186 against 0.171 ms)
+    int ppb = 8;
+    while (ppb > 1 && (size_t)ppb * lds_wave > (size_t)kLdsBytes) ppb >>= 1;
+    if (off32) launch_rows<V, KL, VE, true>(a, ppb, lds_wave, s, ev0, ev1);
+    else launch_rows<V, KL, VE, false>(a, ppb, lds_wave, s, ev0, ev1);
+    return hipGetLastError();
+  }
+  const dim3 g((a.P + kWavesPerBlock - 1) / kWavesPerBlock), b(kBlock);
+  const size_t lds = (size_t)kWavesPerBlock * lds_wave;
+  if (off32)
     launch_timed(spmm_merge_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
   else
     launch_timed(spmm_merge_kernel<V, KL, VE, false>, g, b, lds, s, ev0, ev1, a);

@@ -173,6 +173,18 @@ def test_full_size_laplacian_k8():
     _case(w, "auto", (8,))
 
 
+@pytest.mark.parametrize("name", ["powerlaw", "bimodal", "banded"])
+def test_full_size_k8(name):
+    """The full-size power-law (walk layout, column order), bimodal (walk
+    layout, long-row tiles in its SpMV plan) and banded (stream layout, one
+    workgroup per partition) matrices with 8 right-hand sides and the default
+    plan, the launch the SpMM benchmark times: every row against the oracle."""
+    log("generate", name)
+    w = synth.CONFIGS[name]()
+    _case(w, "auto", (8,))
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("kind", ["binned", "binned_streams", "group", "rgcsr"])
 def test_spmm_on_other_schedules(kind):
     # spmv_exec_multi runs on the plan's merge-path partitions whatever
