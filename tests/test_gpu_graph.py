@@ -25,6 +25,9 @@ def _spmv_cases():
                                           dispatch_order="partition")),
         "merge_walk_column": (bi, dict(strategy="merge", merge_reduce="walk",
                                        dispatch_order="column")),
+        # long rows in column-blocked tiles: the walk+tile grid, the fix-up
+        # and the tile reduction, three launches per exec
+        "merge_walk_tiles": (bi, dict(strategy="merge", merge_reduce="walk")),
         "binned": (pw, dict(strategy="binned")),
         "group": (pw, dict(strategy="group")),
         "rgcsr": (lap, None),
@@ -54,6 +57,8 @@ def _capture(fn):
 def test_spmv_graph_replays(case):
     w, opts = _spmv_cases()[case]
     m, plan = _plan(w, opts)
+    if case == "merge_walk_tiles":
+        assert plan.info["tile_rows"] > 0, plan.info
     dt = w.values.dtype.type
     x = dev(w.x)
     y0 = dev(synth.uniform(w.M, 12, synth.S_Y, dt))
