@@ -80,7 +80,10 @@ __device__ __forceinline__ void tile_block(const TileArgs<V>& a, int t, V* xs) {
   static_assert(2 * RW <= kWave && RW % NB == 0, "segment bounds of a wave's rows in one register");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int b = t / a.ngroups, g = t - b * a.ngroups;
+  // group-major: consecutive tiles take consecutive blocks of the same
+  // rows, so a run of tiles streams each row's segments in memory order
+  // (block-major, sharing one x block instead, measured 2% slower)
+  const int g = t / a.nb, b = t - g * a.nb;
   const int c0 = b * BC;   // < N
   const int clen = min(BC, a.N - c0);
   // lane 2k + e: seg[row k of this wave][b + e] (rows past the end clamped
