@@ -371,6 +371,15 @@ def run_spmm(args, w, torch, lb, dev):
         "workspace_bytes": need,
         "kernel_source_hash": kernel_source_hash(SPMM_SOURCES),
     }
+    # the X-row gathers alone (each nonzero's row of X, nothing else), in the
+    # kernels' lane grouping, flushed and timed like the steps
+    row_bytes = k * X.element_size()
+    if row_bytes in (16, 32, 64, 128, 256) and X.is_contiguous() and w.nnz > 0:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        g_ms = timed_median(torch, flush, min(K, 10),
+                            lambda: lb.spmv_gather_rows_probe(col, X, sink))
+        out["gather_rows_probe_ms"] = round(g_ms, 5)
+        out["gather_rows_probe_G_per_s"] = round(w.nnz / (g_ms * 1e-3) / 1e9, 2)
     plan.destroy()
     ok = True
     if not args.no_cpu:

@@ -504,6 +504,20 @@ SPMV_API spmv_status_t spmv_gather_probe(const int32_t* col_idx, int64_t nnz, co
                                          int64_t n_x, spmv_dtype_t dtype, void* sink,
                                          hipStream_t stream);
 
+/* Measurement aid, not part of the SpMV: the X-row gathers of a
+ * multi-vector product (the PPoPP'23 page, Section 5.3, Listing 4: a row of
+ * the dense operand per nonzero), nothing else. Reads col_idx[0..nnz) once
+ * and, for every k, the row col_idx[k] of X, a dense array of n_rows rows of
+ * row_bytes bytes each (16, 32, 64, 128 or 256; rows contiguous), with
+ * 16-byte lanes grouped as the SpMM kernels group them (row_bytes / 16 lanes
+ * per row, 8 rows per lane group in flight). Rows are clamped to
+ * [0, n_rows), so any col_idx is safe. X 16-byte aligned, 0 < n_rows < 2^32;
+ * `sink` (device int32) keeps the loads live. Asynchronous;
+ * SPMV_ERR_INVALID_ARG on a bad size or pointer. */
+SPMV_API spmv_status_t spmv_gather_rows_probe(const int32_t* col_idx, int64_t nnz, const void* X,
+                                              int64_t n_rows, int32_t row_bytes, void* sink,
+                                              hipStream_t stream);
+
 /* Measurement aid, not part of the SpMV: the merge-path kernels' access
  * pattern without x. The M + nnz units are cut into P = ceil((M + nnz) / T)
  * equal partitions, T = 64 * items_per_thread (4, 8 or 16); each 64-lane

@@ -13,8 +13,8 @@ from .binding import (EXPORTED, LIB_PATH, Plan, PlanOptions, SpmvError, load, ma
                       spmv_plan_set_strategy, spmv_read_probe, spmv_status_string,
                       spmv_exec_multi, spmv_spmm_workspace_size, spmv_plan_coo,
                       spmv_plan_transpose, spmv_plan_csc, spmv_plan_rgcsr,
-                      spmv_plan_set_group, spmv_gather_probe, spmv_stream_probe,
-                      spmv_exec_noalloc)
+                      spmv_plan_set_group, spmv_gather_probe, spmv_gather_rows_probe,
+                      spmv_stream_probe, spmv_exec_noalloc)
 
 __all__ = ["EXPORTED", "LIB_PATH", "Plan", "PlanOptions", "SpmvError", "load", "make_options",
            "spmv_destroy", "spmv_exec", "spmv_exec_events", "spmv_last_error", "spmv_plan",
@@ -22,5 +22,5 @@ __all__ = ["EXPORTED", "LIB_PATH", "Plan", "PlanOptions", "SpmvError", "load", "
            "spmv_plan_set_strategy", "spmv_read_probe", "spmv_status_string",
            "spmv_exec_multi", "spmv_spmm_workspace_size", "spmv_plan_coo",
            "spmv_plan_transpose", "spmv_plan_csc", "spmv_plan_rgcsr",
-           "spmv_plan_set_group", "spmv_gather_probe", "spmv_stream_probe",
-           "spmv_exec_noalloc"]
+           "spmv_plan_set_group", "spmv_gather_probe", "spmv_gather_rows_probe",
+           "spmv_stream_probe", "spmv_exec_noalloc"]

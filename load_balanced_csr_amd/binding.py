@@ -30,6 +30,7 @@ EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
             "spmv_plan_set_strategy", "spmv_plan_set_group", "spmv_plan_info",
             "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_gather_probe",
+            "spmv_gather_rows_probe",
             "spmv_stream_probe", "spmv_spmm_workspace_size",
             "spmv_exec_multi", "spmv_exec_multi_events", "spmv_exec_noalloc",
             "spmv_status_string", "spmv_last_error")
@@ -104,6 +105,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_plan_copy_bins.argtypes = [p, p, i64, p]
     lib.spmv_read_probe.argtypes = [p, i64, p, p]
     lib.spmv_gather_probe.argtypes = [p, i64, p, i64, i32, p, p]
+    lib.spmv_gather_rows_probe.argtypes = [p, i64, p, i64, i32, p, p]
     lib.spmv_stream_probe.argtypes = [p, p, p, i64, i64, i32, i32, p, p]
     lib.spmv_exec_noalloc.argtypes = [i64, i64, i64, p, p, p, i32, p, p, d, d, p]
     lib.spmv_spmm_workspace_size.argtypes = [p, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -425,6 +427,20 @@ def spmv_gather_probe(col_idx: torch.Tensor, x: torch.Tensor, sink: torch.Tensor
     _check(load().spmv_gather_probe(col_idx.data_ptr(), col_idx.numel(), x.data_ptr(), x.numel(),
                                     _dtype_code(x), sink.data_ptr(), _stream(stream)),
            "spmv_gather_probe")
+
+
+def spmv_gather_rows_probe(col_idx: torch.Tensor, X: torch.Tensor, sink: torch.Tensor,
+                           stream=None) -> None:
+    """Read col_idx once and gather the row of X (2-D, contiguous) at every
+    column, nothing else (measurement aid, see the header)."""
+    if not (col_idx.is_cuda and X.is_cuda and sink.is_cuda and sink.dtype == torch.int32
+            and col_idx.dtype == torch.int32 and X.dim() == 2 and X.is_contiguous()):
+        raise ValueError("spmv_gather_rows_probe needs device tensors: int32 col_idx, a "
+                         "contiguous 2-D X, int32 sink")
+    _check(load().spmv_gather_rows_probe(col_idx.data_ptr(), col_idx.numel(), X.data_ptr(),
+                                         X.shape[0], X.shape[1] * X.element_size(),
+                                         sink.data_ptr(), _stream(stream)),
+           "spmv_gather_rows_probe")
 
 
 def spmv_stream_probe(row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor,

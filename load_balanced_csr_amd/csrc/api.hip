@@ -1159,6 +1159,22 @@ spmv_status_t spmv_gather_probe(const int32_t* col_idx, int64_t nnz, const void*
   return SPMV_SUCCESS;
 }
 
+spmv_status_t spmv_gather_rows_probe(const int32_t* col_idx, int64_t nnz, const void* X,
+                                     int64_t n_rows, int32_t row_bytes, void* sink,
+                                     hipStream_t stream) {
+  const bool rb_ok = row_bytes == 16 || row_bytes == 32 || row_bytes == 64 || row_bytes == 128 ||
+                     row_bytes == 256;
+  if (!rb_ok || nnz < 0 || n_rows <= 0 || n_rows > 0xffffffffll ||
+      (nnz > 0 && (!col_idx || !X)) || !sink || (reinterpret_cast<uintptr_t>(X) & 15) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(SPMV_ERR_INVALID_ARG, "gather rows probe: row_bytes 16/32/64/128/256, X 16-byte "
+                                      "aligned, 0 < n_rows < 2^32, sink 4-byte aligned");
+  const hipError_t err = launch_gather_rows_probe(col_idx, nnz, X, n_rows, row_bytes, 0x5bd1e995,
+                                                  static_cast<int32_t*>(sink), stream);
+  if (err != hipSuccess) return hip_fail(err, "gather rows probe launch");
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_stream_probe(const int32_t* row_ptr, const int32_t* col_idx,
                                 const void* values, int64_t M, int64_t nnz, spmv_dtype_t dtype,
                                 int32_t items_per_thread, void* y, hipStream_t stream) {

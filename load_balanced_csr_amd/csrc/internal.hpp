@@ -263,6 +263,9 @@ hipError_t launch_partition_keys(const int32_t* split_nz, const int32_t* col_idx
 // Measurement aids (probe_kernels.hip).
 hipError_t launch_gather_probe(const int32_t* col_idx, int64_t nnz, const void* x, int64_t n_x,
                                int vbytes, int32_t key, int32_t* sink, hipStream_t s);
+hipError_t launch_gather_rows_probe(const int32_t* col_idx, int64_t nnz, const void* X,
+                                    int64_t n_rows, int row_bytes, int32_t key, int32_t* sink,
+                                    hipStream_t s);
 hipError_t launch_stream_probe(const int32_t* row_ptr, const int32_t* col_idx, const void* values,
                                int64_t M, int64_t nnz, int vbytes, int ipt, void* y,
                                hipStream_t s);

@@ -74,6 +74,40 @@ __global__ __launch_bounds__(kBlock) void gather_probe_kernel(const int32_t* __r
   if (fold_bits(s) == key) sink[0] = key;
 }
 
+// X-row gathers as the SpMM kernels issue them: a wavefront is 64 / KL
+// slots of KL lanes, a slot takes one column index per round and its lanes
+// read the 16-byte parts of that row of X (rows of 16 KL bytes); 8 rounds,
+// every load in flight before the first use. The column indices come
+// straight from global memory (one line per round for the whole wave).
+template <int KL>
+__global__ __launch_bounds__(kBlock) void gather_rows_probe_kernel(const int32_t* __restrict__ col,
+                                                                   int64_t nnz,
+                                                                   const char* __restrict__ X,
+                                                                   uint32_t n_rows, int32_t key,
+                                                                   int32_t* sink) {
+  constexpr int S = kWave / KL, U = 8;
+  const int64_t w = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  const int lane = lane_id();
+  const int s = lane / KL, part = lane % KL;
+  const int64_t base = w * S * U;
+  int c[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t e = base + (int64_t)S * u + s;
+    c[u] = e < nnz ? col[e] : 0;
+  }
+  i32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t r = min((uint32_t)c[u], n_rows - 1);
+    v[u] = *reinterpret_cast<const i32x4*>(X + (r * KL + part) * 16);
+  }
+  int32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  if (acc == key) sink[0] = key;
+}
+
 // One wavefront per partition of T = 64 * IPT units, P = ceil((M + nnz) / T):
 // rows [p R, (p+1) R) and nonzeros [p Z, (p+1) Z), R = ceil(M / P) and
 // Z = ceil(nnz / P), clipped to the arrays.
@@ -139,6 +173,28 @@ hipError_t launch_gather_probe(const int32_t* col_idx, int64_t nnz, const void* 
   else
     hipLaunchKernelGGL(gather_probe_kernel<double>, dim3((unsigned)blocks), dim3(kBlock), 0, s,
                        col_idx, nnz, static_cast<const double*>(x), (uint32_t)n_x, key, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_probe(const int32_t* col_idx, int64_t nnz, const void* X,
+                                    int64_t n_rows, int row_bytes, int32_t key, int32_t* sink,
+                                    hipStream_t s) {
+  const int kl = row_bytes / 16;
+  const int64_t per_wave = (int64_t)(kWave / kl) * 8;
+  const int64_t waves = (nnz + per_wave - 1) / per_wave;
+  const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffll || n_rows <= 0 || n_rows > 0xffffffffll) return hipErrorInvalidValue;
+  const dim3 g((unsigned)blocks), b(kBlock);
+  const char* xb = static_cast<const char*>(X);
+  switch (kl) {
+    case 1: hipLaunchKernelGGL(gather_rows_probe_kernel<1>, g, b, 0, s, col_idx, nnz, xb, (uint32_t)n_rows, key, sink); break;
+    case 2: hipLaunchKernelGGL(gather_rows_probe_kernel<2>, g, b, 0, s, col_idx, nnz, xb, (uint32_t)n_rows, key, sink); break;
+    case 4: hipLaunchKernelGGL(gather_rows_probe_kernel<4>, g, b, 0, s, col_idx, nnz, xb, (uint32_t)n_rows, key, sink); break;
+    case 8: hipLaunchKernelGGL(gather_rows_probe_kernel<8>, g, b, 0, s, col_idx, nnz, xb, (uint32_t)n_rows, key, sink); break;
+    case 16: hipLaunchKernelGGL(gather_rows_probe_kernel<16>, g, b, 0, s, col_idx, nnz, xb, (uint32_t)n_rows, key, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

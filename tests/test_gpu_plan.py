@@ -134,3 +134,10 @@ def test_probes_run_and_keep_their_sink():
     assert bool(torch.isfinite(y).all().item())      # every row of y written
     with pytest.raises(lb.SpmvError):
         lb.spmv_stream_probe(rp, col, val, y, 7)      # items per thread 4, 8 or 16
+    for k, dt in ((4, torch.float32), (8, torch.float32), (8, torch.float64), (64, torch.float32)):
+        X = torch.ones((w.N, k), dtype=dt, device="cuda")
+        lb.spmv_gather_rows_probe(col, X, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    with pytest.raises(lb.SpmvError):                 # 12-byte rows
+        lb.spmv_gather_rows_probe(col, torch.ones((w.N, 3), device="cuda"), sink)
