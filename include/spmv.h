@@ -269,7 +269,8 @@ typedef struct spmv_plan_info {
  * (spmv_plan_info reports both). Errors: SPMV_ERR_INVALID_ARG for a NULL
  * out, a NULL or misaligned array, a negative size or nnz > 2^31 - 1;
  * SPMV_ERR_UNSUPPORTED for M >= 2^31 - 1, N > 2^31 - 1 or
- * M + nnz > 2^31 - 1; SPMV_ERR_ALLOC when the workspace allocation fails;
+ * M + nnz > 2^31 - 65 (the kernels keep 64 units of int32 headroom past the
+ * last one); SPMV_ERR_ALLOC when the workspace allocation fails;
  * SPMV_ERR_INVALID_MATRIX as above. M == 0 or nnz == 0 is allowed. */
 SPMV_API spmv_status_t spmv_plan(spmv_plan_t* out, int64_t M, int64_t N, int64_t nnz,
                         const int32_t* row_ptr, const int32_t* col_idx,

@@ -24,6 +24,10 @@ namespace {
 
 constexpr uint64_t kMagic = 0x53504d5650414e31ull;  // "SPMVPAN1"
 constexpr int64_t kInt32Max = 2147483647ll;
+// M + nnz at most 2^31 - 65: the kernels index the quads and partition ends
+// past the last unit in int32 (a quad's last entry, a lane's clamped
+// start), so 64 units of headroom stay below 2^31.
+constexpr int64_t kMaxUnits = kInt32Max - 64;
 
 thread_local std::string g_last_error;
 
@@ -903,8 +907,8 @@ spmv_status_t check_sizes(int64_t M, int64_t N, int64_t nnz, spmv_dtype_t dtype)
   if (M >= kInt32Max || N > kInt32Max)
     return fail(SPMV_ERR_UNSUPPORTED, "M = %lld or N = %lld beyond int32 indices",
                 (long long)M, (long long)N);
-  if (M + nnz > kInt32Max)
-    return fail(SPMV_ERR_UNSUPPORTED, "M + nnz = %lld exceeds 2^31 - 1 work units",
+  if (M + nnz > kMaxUnits)
+    return fail(SPMV_ERR_UNSUPPORTED, "M + nnz = %lld exceeds 2^31 - 65 work units",
                 (long long)(M + nnz));
   return SPMV_SUCCESS;
 }

@@ -127,7 +127,8 @@ template <> struct Quad<double> {
   }
 };
 
-// Elements [4q, 4q + 4) of a 16-byte aligned array of n elements, streamed.
+// Elements [4q, 4q + 4) of a 16-byte aligned array of n elements, streamed
+// (n < 2^31; the bound is compared unsigned, since 4q + 3 may pass 2^31 - 1).
 // SAFE = false: the caller guarantees 4q + 3 < n (one or two 16-byte loads).
 // SAFE = true: elements at or past n read as 0 and nothing past the array is
 // touched (element-wise loads); used only by the wave that holds the array's
@@ -138,7 +139,7 @@ __device__ __forceinline__ i32x4 load_quad(const int32_t* a, int q, int n) {
   i32x4 r = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (4 * q + j < n) r[j] = a[4 * q + j];
+    if (4u * (uint32_t)q + j < (uint32_t)n) r[j] = a[4 * (int64_t)q + j];
   return r;
 }
 template <bool SAFE>
@@ -150,7 +151,7 @@ __device__ __forceinline__ Quad<float> load_quad(const float* a, int q, int n) {
     r.v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (4 * q + j < n) r.v[j] = a[4 * q + j];
+      if (4u * (uint32_t)q + j < (uint32_t)n) r.v[j] = a[4 * (int64_t)q + j];
   }
   return r;
 }
@@ -165,7 +166,7 @@ __device__ __forceinline__ Quad<double> load_quad(const double* a, int q, int n)
     r.hi = f64x2{0.0, 0.0};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (4 * q + j < n) r.set(j, a[4 * q + j]);
+      if (4u * (uint32_t)q + j < (uint32_t)n) r.set(j, a[4 * (int64_t)q + j]);
   }
   return r;
 }

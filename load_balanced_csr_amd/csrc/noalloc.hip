@@ -67,7 +67,7 @@ spmv_status_t spmv_exec_noalloc(int64_t M, int64_t N, int64_t nnz, const int32_t
   if ((M == 0 || N == 0) && nnz != 0)
     return fail(SPMV_ERR_INVALID_ARG, "M = 0 or N = 0 needs nnz = 0");
   if (nnz > 2147483647ll) return fail(SPMV_ERR_INVALID_ARG, "nnz beyond int32 indices");
-  if (M >= 2147483647ll || N > 2147483647ll || M + nnz > 2147483647ll)
+  if (M >= 2147483647ll || N > 2147483647ll || M + nnz > 2147483647ll - 64)
     return fail(SPMV_ERR_UNSUPPORTED, "sizes beyond the int32 item model");
   if (M == 0) return SPMV_SUCCESS;
   if (!row_ptr || !y || (nnz > 0 && (!col_idx || !values || !x)))

@@ -36,6 +36,16 @@ __device__ __forceinline__ void tile_x4(V (&xv)[4], const i32x4& c, const bool (
   }
 }
 
+// Quads covering entries [s0, s1): the end quad, (s1 + 3) / 4, and whether
+// entry 4q + e lies in [s0, s1), in unsigned arithmetic (nnz may come within
+// a few entries of 2^31, where 4q + e overflows int32; as unsigned it stays
+// below 2^32).
+__device__ __forceinline__ int quad_end(int32_t s1) { return (int)(((uint32_t)s1 + 3u) >> 2); }
+__device__ __forceinline__ bool in_segment(int q, int e, int32_t s0, int32_t s1) {
+  const uint32_t k = 4u * (uint32_t)q + (uint32_t)e;
+  return k >= (uint32_t)s0 && k < (uint32_t)s1;
+}
+
 // One tile row's segment in one column block, one quad per lane per step,
 // for a segment that holds the array's last, partial quad (element loads
 // there, nothing past the array touched). Returns the sum in lane 63.
@@ -43,15 +53,17 @@ template <typename V>
 __device__ V tile_segment_safe(const TileArgs<V>& a, const V* xs, int32_t s0, int32_t s1, int c0,
                                int clen) {
   const int lane = lane_id();
+  const int q1 = quad_end(s1);
   V acc = V(0);
-  for (int q = (s0 >> 2) + lane; q < ((s1 + 3) >> 2); q += kWave) {
-    const bool full = 4 * q + 3 < a.nnz;
+  for (int q = (s0 >> 2) + lane; q < q1; q += kWave) {
+    // q < q1 <= 2^29: 4q + 3 < 2^31 + 3, compared unsigned
+    const bool full = 4u * (uint32_t)q + 3u < (uint32_t)a.nnz;
     const i32x4 c = full ? ld_stream(reinterpret_cast<const i32x4*>(a.col_idx) + q)
                          : load_quad<true>(a.col_idx, q, a.nnz);
     const Quad<V> v = full ? load_quad<false>(a.val, q, 0) : load_quad<true>(a.val, q, a.nnz);
     bool in[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) in[e] = 4 * q + e >= s0 && 4 * q + e < s1;
+    for (int e = 0; e < 4; ++e) in[e] = in_segment(q, e, s0, s1);
     V xv[4];
     tile_x4(xv, c, in, xs, a.x, c0, clen);
 #pragma unroll
@@ -60,10 +72,10 @@ __device__ V tile_segment_safe(const TileArgs<V>& a, const V* xs, int32_t s0, in
   return wave_sum_to_last(acc);
 }
 
-// One workgroup's tile t (column block b, group g of kTileRows tile rows),
-// the block of x in xs (kTileBytes of LDS):
-// the block of x staged in LDS (direct-to-LDS 16-byte loads when x is 16-byte
-// aligned) while each wave loads the segment bounds of its rows (every
+// One workgroup's tile t (column block b, group g of kTileRows tile rows):
+// the block of x staged in xs, kTileBytes of LDS (direct-to-LDS 16-byte
+// loads when x is 16-byte aligned), while each wave loads the segment bounds
+// of its rows (every
 // kWavesPerBlock-th row of the group) into one register; then each wave
 // streams the segments of kTileBatch rows at a time in 16-byte quads, the
 // quads of all of them requested before any is used (indices clamped into
@@ -115,9 +127,9 @@ __device__ __forceinline__ void tile_block(const TileArgs<V>& a, int t, V* xs) {
       s0[j] = __builtin_amdgcn_readlane(sb, 2 * (m + j));
       s1[j] = row ? __builtin_amdgcn_readlane(sb, 2 * (m + j) + 1) : s0[j];
       q0[j] = s0[j] >> 2;
-      q1[j] = (s1[j] + 3) >> 2;
+      q1[j] = quad_end(s1[j]);
       nit = max(nit, (q1[j] - q0[j] + kWave - 1) / kWave);
-      full = full && 4 * max(q1[j], 1) <= a.nnz;
+      full = full && 4u * (uint32_t)max(q1[j], 1) <= (uint32_t)a.nnz;
     }
     V acc[NB];
     if (full) {
@@ -137,7 +149,7 @@ __device__ __forceinline__ void tile_block(const TileArgs<V>& a, int t, V* xs) {
           const int q = q0[j] + it * kWave + lane;
           bool in[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) in[e] = 4 * q + e >= s0[j] && 4 * q + e < s1[j];
+          for (int e = 0; e < 4; ++e) in[e] = in_segment(q, e, s0[j], s1[j]);
           V xv[4];
           tile_x4(xv, c[j], in, xs, a.x, c0, clen);
 #pragma unroll

@@ -54,6 +54,7 @@ def _plan_raw(M, N, nnz, rp=0x1000, col=0x2000, val=0x3000, dtype=0, out=True):
     (dict(M=2 ** 31, N=5, nnz=3), 2),
     (dict(M=2 ** 30, N=5, nnz=2 ** 30 + 5), 2),
     (dict(M=5, N=5, nnz=2 ** 31), 1),          # nnz beyond int32 indices
+    (dict(M=5, N=5, nnz=2 ** 31 - 64 - 5), 2),  # M + nnz = 2^31 - 64: past the limit
 ])
 def test_plan_rejects_bad_arguments(args, status):
     st, h = _plan_raw(**args)
