@@ -425,10 +425,24 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
   return SPMV_SUCCESS;
 }
 
+// Sub-blocks per SpMV tile block when a k-column product runs the plan's
+// long-row tiles, else 0 (no tiles in the plan, or X rows too wide).
+int spmm_tile_m(const spmv_plan_st* p, int64_t k) {
+  if (p->n_tile_rows <= 0 || k <= 0 || k > kWave) return 0;
+  const int vs = p->dtype == SPMV_F32 ? 4 : 8;
+  return spmm_tile_split((int)k, vs, kTileBytes / vs);
+}
+
 size_t spmm_workspace(const spmv_plan_st* p, int64_t k) {
   if (p->merge_reduce == 2 || p->P <= 0 || k <= 0) return 0;
   const size_t vs = p->dtype == SPMV_F32 ? 4 : 8;
-  return align256((size_t)p->P * (size_t)std::min<int64_t>(k, kWave) * vs);
+  size_t bytes = align256((size_t)p->P * (size_t)std::min<int64_t>(k, kWave) * vs);
+  const int m = spmm_tile_m(p, k);
+  if (m > 0)
+    bytes += p->dtype == SPMV_F32
+                 ? spmm_tile_workspace<float>(p->n_tile_rows, p->tile_nb, m, (int)k)
+                 : spmm_tile_workspace<double>(p->n_tile_rows, p->tile_nb, m, (int)k);
+  return bytes;
 }
 
 template <typename V>
@@ -463,12 +477,55 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
   // power-law one, where a fifth do)
   a.part_order = !a.stream && p->dispatch_order == 2 && 2 * p->interior >= p->P ? p->part_order
                                                                                 : nullptr;
-  // one column block: the main kernel's dispatch records the events; more
-  // than one: they bracket the whole loop
-  const bool one = k <= kWave;
+  // long-row tiles, when the plan has them and X rows are narrow enough:
+  // the merge kernel leaves the tiled rows' entries to them
+  // (16-byte lanes: X and Y aligned, row strides whole lanes, as the vector
+  // path of the merge kernel needs too)
+  constexpr int VE = 16 / (int)sizeof(V);
+  const bool vec = k % VE == 0 && ldx % VE == 0 && ldy % VE == 0 &&
+                   ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y)) & 15) == 0;
+  const int tm = vec ? spmm_tile_m(p, k) : 0;
+  SpmmTileArgs<V> t;
+  std::memset(&t, 0, sizeof t);
+  if (tm > 0) {
+    const int vs = (int)sizeof(V);
+    a.part_order = p->tile_list;   // the partitions the tiles leave, in order
+    a.n_dispatch = p->n_dispatch;
+    a.mask_end = p->tile_mask_end;
+    a.mask_start = p->tile_mask_start;
+    char* ws = static_cast<char*>(workspace) + align256((size_t)p->P * (size_t)k * vs);
+    t.rows = p->tile_rows;
+    t.seg = p->tile_seg;
+    t.partial = reinterpret_cast<V*>(ws);
+    t.carry_vec = static_cast<V*>(workspace);
+    t.col_idx = p->col_idx;
+    t.val = static_cast<const V*>(p->values);
+    t.X = static_cast<const V*>(X);
+    t.Y = static_cast<V*>(Y);
+    t.ldx = ldx;
+    t.ldy = ldy;
+    t.alpha = (V)alpha;
+    t.k = (int32_t)k;
+    t.n_rows = p->n_tile_rows;
+    t.nb = p->tile_nb;
+    t.m = tm;
+    t.bc = kTileBytes / vs;
+    t.bck = t.bc / tm;
+    t.ngroups = 0;   // chosen by launch_spmm_tiles
+    t.N = (int32_t)p->N;
+    t.nnz = (int32_t)p->nnz;
+    t.x_dma = ldx == k && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (k * vs) % 16 == 0;
+  }
+  // one column block without tiles: the main kernel's dispatch records the
+  // events; otherwise they bracket the whole call
+  const bool one = k <= kWave && tm == 0;
   hipError_t err = hipSuccess;
   if (!one && ev0 && (err = hipEventRecord(ev0, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");
+  // the tiles first: they zero the carries of the partitions they cover,
+  // which the merge kernel's fix-up reads
+  if (tm > 0 && (err = launch_spmm_tiles<V>(t, stream)) != hipSuccess)
+    return hip_fail(err, "spmv_exec_multi tiles");
   for (int64_t kb = 0; kb < k; kb += kWave) {
     a.k = (int32_t)std::min<int64_t>(kWave, k - kb);
     a.X = static_cast<const V*>(X) + kb;
@@ -476,6 +533,9 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
     if ((err = launch_spmm<V>(a, stream, one ? ev0 : nullptr, one ? ev1 : nullptr)) != hipSuccess)
       return hip_fail(err, "spmv_exec_multi launch");
   }
+  // after the merge kernel's fix-up, the tiles' partials into Y
+  if (tm > 0 && (err = launch_spmm_tile_reduce<V>(t, stream)) != hipSuccess)
+    return hip_fail(err, "spmv_exec_multi tiles");
   if (!one && ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");
   return SPMV_SUCCESS;
@@ -668,7 +728,8 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   // of the partitions they leave and its masks; their plan-time skip marks
   // reuse the x-window table, which walk plans never use
   const size_t o_trows = take(sizeof(int32_t) * kTileRowInts * std::max<int64_t>(tile_cap, 1));
-  const size_t o_tseg = take(sizeof(int32_t) * std::max<int64_t>(tile_cap, 1) * (tile_nb + 1));
+  const size_t o_tseg =
+      take(sizeof(int32_t) * std::max<int64_t>(tile_cap, 1) * (tile_nb * kTileSub + 1));
   const size_t o_tpart = take(vs * std::max<int64_t>(tile_cap, 1) * std::max<int64_t>(tile_nb, 1));
   const int64_t tile_p = tile_cap > 0 ? std::max<int64_t>(p_max, 1) : 1;
   const size_t o_tscan = take(sizeof(int32_t) * tile_p);

@@ -80,6 +80,7 @@ enum StatSlot : int {
 constexpr int kTileBytes = 16384;   // x block of one tile in LDS: 4096 fp32 / 2048 fp64
 constexpr int kTileRows = 64;       // tile rows one workgroup takes per column block
 constexpr int kTileBatch = 4;      // tile rows whose quads a wave requests together
+constexpr int kTileSub = 4;        // segment bounds per column block (quarter blocks)
 constexpr int kTileRowInts = 8;     // per tile row: row, first / end nonzero, first / end partition
 constexpr int kTileMinPerBlock = 64;  // a row is tiled when its interior run holds this many
                                       // nonzeros per column block on average
@@ -91,7 +92,7 @@ struct TilePlan {
   int32_t bc;             // columns per block
   int64_t min_entries;    // kTileMinPerBlock * nb
   int32_t* rows;          // cap x kTileRowInts
-  int32_t* seg;           // cap x (nb + 1): segment bounds
+  int32_t* seg;           // cap x (nb kTileSub + 1): bounds at every quarter block
   int32_t* skip;          // p_max: 1 where the walk kernel skips the partition
   int32_t* scan;          // p_max: flags, then their prefix sums
   int32_t* list;          // p_max: the walk kernel's dispatch list
@@ -113,7 +114,7 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
 template <typename V>
 struct TileArgs {
   const int32_t* rows;    // kTileRowInts per tile row
-  const int32_t* seg;     // n_rows x (nb + 1)
+  const int32_t* seg;     // n_rows x (nb kTileSub + 1), quarter-block bounds
   const int32_t* col_idx;
   const V* val;
   const V* x;
@@ -307,7 +308,58 @@ struct SpmmArgs {
   int32_t stream;            // 1: partitions end at row ends (no carries)
   int32_t xcd_remap;
   const int32_t* part_order;  // walk plans: dispatch slot -> partition (null: identity)
+  // plans with long-row tiles, when the tiles run for this k (else null / 0):
+  // the first n_dispatch slots of part_order are the partitions the tiles
+  // leave (the tiles zero the others' carries), and the masks of the
+  // partitions a tile row starts or ends in (entries outside
+  // [mask_end[p], mask_start[p]) belong to the tiles)
+  int32_t n_dispatch;
+  const int32_t* mask_end;
+  const int32_t* mask_start;
 };
+
+// Long-row tiles of a multi-vector product: a tile is one sub-block of
+// bck X rows (k-wide, staged in LDS, at most kSpmmTileBytes) and the
+// segments of up to kSpmmTileWaves x 32 tile rows in it (8, 16 or 32 a
+// wave: the most that leaves kSpmmTileMinGrid tiles). Sub-blocks split the plan's
+// SpMV column blocks (bc columns) in m equal parts, m dividing kTileSub, so
+// their bounds are among the plan's quarter-block bounds.
+constexpr int kSpmmTileBytes = 65536;
+constexpr int kSpmmTileWaves = 8;       // waves of one SpMM tile workgroup (two fit a CU)
+constexpr int kSpmmTileMinGrid = 1024;  // tiles wanted before a tile takes more rows
+template <typename V>
+struct SpmmTileArgs {
+  const int32_t* rows;        // plan: kTileRowInts per tile row
+  const int32_t* seg;         // plan: n_rows x (nb kTileSub + 1) quarter-block bounds
+  const int32_t* col_idx;
+  const V* val;
+  const V* X;
+  V* Y;
+  V* partial;                 // workspace: n_rows x nb m x k
+  V* carry_vec;               // the merge kernel's carries (P x k): the tiles zero
+                              // those of the partitions they cover
+  int64_t ldx, ldy;
+  V alpha;
+  int32_t k;
+  int32_t n_rows;
+  int32_t nb, m, bc, bck;     // SpMV blocks, sub-blocks per block, their widths (columns)
+  int32_t ngroups;            // row groups of one tile (set by launch_spmm_tiles)
+  int32_t N;
+  int32_t nnz;
+  int32_t x_dma;              // X rows contiguous (ldx == k) and 16-byte aligned
+};
+// Sub-blocks per SpMV block for k columns of vbytes each: the power of two m
+// with bc / m X rows in kSpmmTileBytes; 0 when the tiles do not apply (k
+// not a multiple of a 16-byte lane, or X rows wider than 32 bytes).
+int spmm_tile_split(int k, int vbytes, int bc);
+template <typename V>
+size_t spmm_tile_workspace(int n_rows, int nb, int m, int k);
+// The tiles (before the merge kernel, whose fix-up reads the carries they
+// zero), and, after the fix-up, the reduction of the partials into Y.
+template <typename V>
+hipError_t launch_spmm_tiles(const SpmmTileArgs<V>& t, hipStream_t s);
+template <typename V>
+hipError_t launch_spmm_tile_reduce(const SpmmTileArgs<V>& t, hipStream_t s);
 
 // Staging room per array for partitions of T units (at most T + T/8 rows or
 // nonzeros, plus quad alignment).

@@ -125,14 +125,14 @@ __device__ __forceinline__ void walk_partition(const MergeArgs<V>& a, int slot, 
   }
 }
 
-template <typename V, int IPT, bool MASK>
+template <typename V, int IPT>
 __global__ __launch_bounds__(kBlock) void merge_spmv_kernel(const MergeArgs<V> a) {
   constexpr int T = kWave * IPT;
   __shared__ __attribute__((aligned(16))) int32_t s_end[kWavesPerBlock][T + 8];
   __shared__ __attribute__((aligned(16))) V s_val[kWavesPerBlock][T + 8];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
-  walk_partition<V, IPT, MASK>(a, blk * kWavesPerBlock + wave, s_end[wave], s_val[wave]);
+  walk_partition<V, IPT, false>(a, blk * kWavesPerBlock + wave, s_end[wave], s_val[wave]);
 }
 
 // The walk over the partitions long-row tiles leave and the tiles
@@ -585,9 +585,9 @@ hipError_t launch_main(const MergeArgs<V>& a, const TileArgs<V>* tiles, hipStrea
     launch_timed(merge_stream_kernel<V, IPT, 0, kWavesPerBlock>, dim3(blocks), dim3(kBlock), 0,
                  s, ev0, ev1, a, a.row_bounds, a.win_span);
   } else if (a.mask_end) {
-    launch_timed(merge_spmv_kernel<V, IPT, true>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
+    return hipErrorInvalidValue;   // masked partitions run only beside their tiles
   } else {
-    launch_timed(merge_spmv_kernel<V, IPT, false>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
+    launch_timed(merge_spmv_kernel<V, IPT>, dim3(blocks), dim3(kBlock), 0, s, ev0, ev1, a);
   }
   return hipGetLastError();
 }

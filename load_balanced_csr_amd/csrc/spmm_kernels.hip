@@ -132,8 +132,9 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int blk = a.xcd_remap ? xcd_tile(blockIdx.x, 0, gridDim.x) : (int)blockIdx.x;
   int p = blk * kWavesPerBlock + wave;
-  if (p >= a.P) return;
-  // the plan's column dispatch order (walk plans), as in the SpMV kernel
+  if (p >= (a.n_dispatch ? a.n_dispatch : a.P)) return;
+  // the plan's column dispatch order (walk plans), as in the SpMV kernel,
+  // or the partitions long-row tiles leave
   if (a.part_order) p = a.part_order[p];
 
   // partition p: rows [r0, r1) end inside it; nonzeros [n0, n1). In the
@@ -176,6 +177,24 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   const int32_t* coll = s_col + (n0 & 3);  // coll[t] = col_idx[n0 + t]
   const V* vall = reinterpret_cast<const V*>(s_val + ((W * n0) & 3));   // vall[t] = val[n0 + t]
   // (W * n0 may wrap in int32 for fp64; its low two bits are still right)
+  // a partition a tiled row starts or ends in: that row's entries belong to
+  // the tiles, so their staged values become 0 and their columns 0 (one X
+  // row for all of them)
+  if (a.mask_end) {
+    const int mlo = a.mask_end[p], mhi = a.mask_start[p];
+    if (mlo > n0 || mhi < n1) {   // wave-uniform
+      V* vw = reinterpret_cast<V*>(s_val + ((W * n0) & 3));
+      int32_t* cw = s_col + (n0 & 3);
+      for (int t = lane; t < nloc; t += kWave) {
+        const int gk = n0 + t;
+        if (gk < mlo || gk >= mhi) {
+          vw[t] = V(0);
+          cw[t] = 0;
+        }
+      }
+      wave_sync();
+    }
+  }
 
   const int s = lane / KL;
   const int col = (lane % KL) * VE;          // first output column of this lane
@@ -491,6 +510,252 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   *yp = fma(a.alpha, s + extra, *yp);
 }
 
+// ---- long-row tiles (plans with tiles, X rows of at most 32 bytes) --------------
+
+// The end quad of entries [., s1), (s1 + 3) / 4, and whether entry 4q + e
+// lies in [s0, s1), in unsigned arithmetic (4q + e may pass 2^31 - 1).
+__device__ __forceinline__ int quad_end(int32_t s1) { return (int)(((uint32_t)s1 + 3u) >> 2); }
+__device__ __forceinline__ bool in_segment_u(int q, int e, int32_t s0, int32_t s1) {
+  const uint32_t k = 4u * (uint32_t)q + (uint32_t)e;
+  return k >= (uint32_t)s0 && k < (uint32_t)s1;
+}
+
+// The 16-byte quad (columns or values) of the partner lane (this lane xor
+// 1): one DPP move per word.
+__device__ __forceinline__ i32x4 quad_of_partner(const i32x4& v) {
+  i32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = dpp_i32<kDppQuadXor1>(0, v[j]);
+  return r;
+}
+template <typename V>
+__device__ __forceinline__ Quad<V> quad_of_partner(const Quad<V>& v) {
+  Quad<V> r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.set(j, dpp_move<kDppQuadXor1>(v[j]));
+  return r;
+}
+
+// acc += the products of quad q (entries 4q..4q+3, those in [s0, s1)) with
+// this lane's VE columns of their X rows: from the staged block in LDS, or,
+// for a column outside it (only in a row with unsorted columns), from
+// global X, in a branch the wave takes only when one of its lanes needs it.
+// An entry outside the segment reads the zero row past the block (row
+// zrow) and its value is taken as 0, so its FMAs add exactly 0 whatever X
+// and the values hold elsewhere.
+template <typename V, int VE>
+__device__ __forceinline__ void tile_quad_products(Vec<V, VE>& acc, const i32x4& c,
+                                                   const Quad<V>& v, int q, int32_t s0,
+                                                   int32_t s1, const V* xs,
+                                                   const SpmmTileArgs<V>& t, int64_t c0,
+                                                   int clen, int zrow, int lcol) {
+  bool in[4], out = false;
+  Vec<V, VE> xv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    in[e] = in_segment_u(q, e, s0, s1);
+    const unsigned lc = (unsigned)((int64_t)c[e] - c0);
+    const bool inb = lc < (unsigned)clen;
+    xv[e] = vec_load<V, VE>(xs + (int64_t)(in[e] && inb ? lc : (unsigned)zrow) * t.k + lcol);
+    out = out || (in[e] && !inb);
+  }
+  if (__builtin_amdgcn_ballot_w64(out) != 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (in[e] && (unsigned)((int64_t)c[e] - c0) >= (unsigned)clen)
+        xv[e] = vec_load<V, VE>(t.X + (int64_t)c[e] * t.ldx + lcol);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const V ve = in[e] ? v[e] : V(0);
+#pragma unroll
+    for (int r = 0; r < VE; ++r) acc.v[r] = fma(ve, xv[e].v[r], acc.v[r]);
+  }
+}
+
+// One workgroup of W waves per tile: sub-block b of bck X rows, group g of
+// TR = W RW tile rows, taken block-major (an XCD's run of tiles then reads
+// its own run of X blocks into its L2; X of k columns does not fit one L2
+// whole). The tiles of sub-block 0 first zero the carries of their rows'
+// interior partitions, which the merge kernel does not walk but its fix-up
+// reads. The block's X rows are staged in LDS (direct-to-LDS loads when
+// they are contiguous and aligned), with one zero row past them. Each wave
+// takes every W-th row of the group, two at a time, one per half-wave, NP
+// such pairs per batch: a lane loads one 16-byte quad of its row's segment
+// (columns and values; 32 quads per half and step); with KL = 2 lanes a
+// slot (X rows of 32 bytes), partners swap their quads by DPP, and each
+// lane multiplies all 4 KL entries by its VE columns of their X rows (from
+// LDS). The NP pairs' loads are all requested before any is used. Eight waves a workgroup and at most
+// 128 registers let two workgroups share a CU (LDS allows two): measured
+// on the bimodal matrix at k = 8, 4 waves of 16 rows took 237 us, 8 waves
+// of 16 rows 155 us, and 8 of 32 rows less again (X staged half as often).
+// Each lane adds in a fixed order; the half's slots then meet by a
+// butterfly of cross-lane adds, and its first slot writes
+// partial[row][b][columns].
+template <typename V, int KL, int VE, int W, int RW>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2 * W / 4)))
+void spmm_tile_kernel(const SpmmTileArgs<V> t) {
+  constexpr int TR = W * RW;                       // rows per tile
+  constexpr int NT = W * kWave;                    // threads per workgroup
+  constexpr int HL = kWave / 2;                    // lanes per row (a half-wave)
+  // row pairs per batch: as many as fit 128 registers (two workgroups a CU)
+  constexpr int NP = (KL == 2 && sizeof(V) == 8) ? 1 : 2;
+  static_assert(2 * RW <= kWave && KL <= 2 && (RW / 2) % NP == 0, "tile layout");
+  typedef Vec<V, VE> VV;
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+  V* xs = reinterpret_cast<V*>(s_dyn);
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nbs = t.nb * t.m;
+  const int sub = kTileSub / t.m;   // quarter-block bounds per sub-block
+  const int tile = xcd_tile(blockIdx.x, 0, gridDim.x);
+  const int b = tile / t.ngroups, g = tile - b * t.ngroups;
+  if (b == 0) {   // workgroup-uniform
+    for (int r = 0; r < TR; ++r) {
+      const int i = g * TR + r;
+      if (i >= t.n_rows) break;
+      const int32_t pf = t.rows[kTileRowInts * i + 3], pe = t.rows[kTileRowInts * i + 4];
+      const int64_t n = (int64_t)(pe - pf) * t.k;
+      for (int64_t e = threadIdx.x; e < n; e += NT) t.carry_vec[(int64_t)pf * t.k + e] = V(0);
+    }
+  }
+  const int64_t c0 = (int64_t)b * t.bck;
+  const int clen = (int)max((int64_t)0, min((int64_t)t.bck, (int64_t)t.N - c0));
+  // lane 2r + e: the bound of sub-block b + e of row r of this wave (rows
+  // past the end clamped to the last; their bounds are not used)
+  const int i0 = g * TR + wave;
+  const int ri = min(i0 + W * min(lane >> 1, RW - 1), t.n_rows - 1);
+  const int32_t sb = t.seg[(int64_t)ri * (t.nb * kTileSub + 1) + sub * (b + (lane & 1))];
+  const int64_t nel = (int64_t)clen * t.k;
+  if (t.x_dma) {
+    // k values of a row are a whole number of 16-byte chunks
+    const int nch = (int)(nel * (int64_t)sizeof(V) / 16);
+    const char* src = reinterpret_cast<const char*>(t.X + c0 * t.k);
+    for (int first = wave * kWave; first < nch; first += NT)
+      if (first + lane < nch)
+        lds_dma16(src + 16 * (int64_t)(first + lane), reinterpret_cast<char*>(xs) + 16 * first);
+  } else {
+    for (int64_t e = threadIdx.x; e < nel; e += NT) {
+      const int64_t r = e / t.k;
+      xs[e] = t.X[(c0 + r) * t.ldx + (e - r * t.k)];
+    }
+  }
+  // the zero row past the block, for the entries outside a segment
+  const int zrow = t.bck;
+  for (int e = threadIdx.x; e < t.k; e += NT) xs[(int64_t)zrow * t.k + e] = V(0);
+  wait_vmem();
+  __syncthreads();
+  const int h = lane / HL, hl = lane % HL;
+  const int col = (hl % KL) * VE;
+  const bool colok = col < t.k;
+  const int lcol = colok ? col : 0;
+  for (int pb = 0; pb < RW / 2; pb += NP) {
+    if (i0 + W * 2 * pb >= t.n_rows) break;   // wave-uniform
+    int32_t s0[NP], s1[NP];
+    int nit = 0;
+    bool full = true;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int ra = 2 * (pb + j), rb = ra + 1;   // rows of the pair, in this wave
+      const bool va = i0 + W * ra < t.n_rows;
+      const bool vb = i0 + W * rb < t.n_rows;
+      const int32_t a0 = __builtin_amdgcn_readlane(sb, 2 * ra);
+      const int32_t a1 = va ? __builtin_amdgcn_readlane(sb, 2 * ra + 1) : a0;
+      const int32_t b0 = __builtin_amdgcn_readlane(sb, 2 * rb);
+      const int32_t b1 = vb ? __builtin_amdgcn_readlane(sb, 2 * rb + 1) : b0;
+      s0[j] = h ? b0 : a0;
+      s1[j] = h ? b1 : a1;
+      const int qa = quad_end(a1) - (a0 >> 2), qb = quad_end(b1) - (b0 >> 2);
+      nit = max(nit, (max(qa, qb) + HL - 1) / HL);
+      full = full && 4u * (uint32_t)max(quad_end(max(a1, b1)), 1) <= (uint32_t)t.nnz;
+    }
+    VV acc[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int r = 0; r < VE; ++r) acc[j].v[r] = V(0);
+    for (int it = 0; it < nit; ++it) {
+      i32x4 cq[NP];
+      Quad<V> vq[NP];
+      int qb0[NP];   // quad of lane hl = 0 of this half at this step
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        qb0[j] = (s0[j] >> 2) + it * HL;
+        const int qc = max(min(qb0[j] + hl, quad_end(s1[j]) - 1), 0);
+        if (full) {
+          cq[j] = ld_stream(reinterpret_cast<const i32x4*>(t.col_idx) + qc);
+          vq[j] = load_quad<false>(t.val, qc, 0);
+        } else {   // the array's last, partial quad is among them
+          cq[j] = load_quad<true>(t.col_idx, qc, t.nnz);
+          vq[j] = load_quad<true>(t.val, qc, t.nnz);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        tile_quad_products<V, VE>(acc[j], cq[j], vq[j], qb0[j] + hl, s0[j], s1[j], xs, t, c0,
+                                  clen, zrow, lcol);
+        if (KL == 2)
+          tile_quad_products<V, VE>(acc[j], quad_of_partner(cq[j]), quad_of_partner(vq[j]),
+                                    qb0[j] + (hl ^ 1), s0[j], s1[j], xs, t, c0, clen, zrow,
+                                    lcol);
+      }
+    }
+    // the half's slots meet (offsets below HL keep each half apart)
+    for (int off = KL; off < HL; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int r = 0; r < VE; ++r) acc[j].v[r] += __shfl_xor(acc[j].v[r], off, kWave);
+    }
+    if (hl < KL && colok) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int i = i0 + W * (2 * (pb + j) + h);
+        if (i < t.n_rows) {
+          V* dst = t.partial + ((int64_t)i * nbs + b) * t.k + col;
+#pragma unroll
+          for (int r = 0; r < VE; ++r) dst[r] = acc[j].v[r];
+        }
+      }
+    }
+  }
+}
+
+// Y[row][c] += alpha * (sum of the row's sub-block partials of column c),
+// one wave per tile row: lane l takes column l % KC (KC the power of two
+// covering k) and sub-blocks l / KC, l / KC + 64 / KC, ...; the lanes of a
+// column then meet by a butterfly of cross-lane adds (a fixed order).
+template <typename V>
+__global__ __launch_bounds__(kBlock) void spmm_tile_reduce_kernel(const SpmmTileArgs<V> t,
+                                                                  int kc) {
+  const int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  if (i >= t.n_rows) return;   // wave-uniform
+  const int lane = lane_id();
+  const int c = lane % kc, bl = lane / kc, nbl = kWave / kc;
+  const int nbs = t.nb * t.m;
+  // eight running sums, so eight loads are in flight; added in a fixed order
+  V a8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a8[u] = V(0);
+  if (c < t.k) {
+    const V* pr = t.partial + (int64_t)i * nbs * t.k + c;
+    int b = bl;
+    for (; b + 7 * nbl < nbs; b += 8 * nbl) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a8[u] += pr[(int64_t)(b + u * nbl) * t.k];
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (b + u * nbl < nbs) a8[u] += pr[(int64_t)(b + u * nbl) * t.k];
+  }
+  V acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
+  for (int off = kc; off < kWave; off <<= 1) acc += __shfl_xor(acc, off, kWave);
+  if (bl == 0 && c < t.k) {
+    V* yp = t.Y + (int64_t)t.rows[kTileRowInts * i] * t.ldy + c;
+    *yp += t.alpha * acc;
+  }
+}
+
 template <typename V, int KL, int VE, bool OFF32>
 void launch_rows(const SpmmArgs<V>& a, int ppb, size_t lds_wave, hipStream_t s, hipEvent_t ev0,
                  hipEvent_t ev1) {
@@ -520,7 +785,8 @@ hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEve
     else launch_rows<V, KL, VE, false>(a, ppb, lds_wave, s, ev0, ev1);
     return hipGetLastError();
   }
-  const dim3 g((a.P + kWavesPerBlock - 1) / kWavesPerBlock), b(kBlock);
+  const int slots = a.n_dispatch ? a.n_dispatch : a.P;
+  const dim3 g((slots + kWavesPerBlock - 1) / kWavesPerBlock), b(kBlock);
   const size_t lds = (size_t)kWavesPerBlock * lds_wave;
   if (off32)
     launch_timed(spmm_merge_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
@@ -577,5 +843,85 @@ template hipError_t launch_spmm<float>(const SpmmArgs<float>&, hipStream_t, hipE
                                        hipEvent_t);
 template hipError_t launch_spmm<double>(const SpmmArgs<double>&, hipStream_t, hipEvent_t,
                                         hipEvent_t);
+
+int spmm_tile_split(int k, int vbytes, int bc) {
+  const int ve = 16 / vbytes;
+  // X rows of at most 32 bytes: at 64 (fp32 k = 16) a row's segment in a
+  // sub-block fills under half of a half-wave's quads, and the bimodal
+  // matrix measured 0.45 ms tiled against 0.38 ms untiled
+  if (k <= 0 || k % ve != 0 || k * vbytes > 32) return 0;
+  int m = 1;
+  while ((int64_t)(bc / m) * k * vbytes > kSpmmTileBytes) m *= 2;
+  return m <= kTileSub ? m : 0;   // the plan keeps bounds at quarter blocks
+}
+
+template <typename V>
+size_t spmm_tile_workspace(int n_rows, int nb, int m, int k) {
+  return (sizeof(V) * (size_t)n_rows * nb * m * k + 255) & ~size_t(255);
+}
+
+template <typename V, int W, int RW>
+hipError_t launch_spmm_tiles_w(const SpmmTileArgs<V>& t, hipStream_t s);
+
+int spmm_tile_rows_per_wave(int n_rows, int nb, int m) {
+  for (int rw = 32; rw > 8; rw /= 2) {
+    const int64_t tr = (int64_t)kSpmmTileWaves * rw;
+    if ((n_rows + tr - 1) / tr * nb * m >= kSpmmTileMinGrid) return rw;
+  }
+  return 8;
+}
+template <typename V>
+hipError_t launch_spmm_tiles(const SpmmTileArgs<V>& t, hipStream_t s) {
+  if (t.n_rows <= 0 || t.m <= 0) return hipSuccess;
+  if (kTileSub % t.m != 0) return hipErrorInvalidValue;
+  // the most rows per wave that still leaves kSpmmTileMinGrid tiles (more
+  // rows a tile stage its X block fewer times)
+  const int rw = spmm_tile_rows_per_wave(t.n_rows, t.nb, t.m);
+  if (rw == 32) return launch_spmm_tiles_w<V, kSpmmTileWaves, 32>(t, s);
+  if (rw == 16) return launch_spmm_tiles_w<V, kSpmmTileWaves, 16>(t, s);
+  return launch_spmm_tiles_w<V, kSpmmTileWaves, 8>(t, s);
+}
+template <typename V, int W, int RW>
+hipError_t launch_spmm_tiles_w(const SpmmTileArgs<V>& t, hipStream_t s) {
+  SpmmTileArgs<V> u = t;
+  u.ngroups = (t.n_rows + W * RW - 1) / (W * RW);
+  const int64_t tiles = (int64_t)u.ngroups * t.nb * t.m;
+  if (tiles > 0x7fffffffll) return hipErrorInvalidValue;
+  constexpr int VE = 16 / (int)sizeof(V);
+  const int lanes = t.k / VE;   // k is a multiple of VE (spmm_tile_split)
+  // the block's X rows and one zero row (just past 64 KiB at the widest)
+  const size_t lds = ((size_t)t.bck + 1) * t.k * sizeof(V);
+  const dim3 g((unsigned)tiles), b(W * kWave);
+  auto go = [&](auto kern) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kSpmmTileBytes + 64 * (int)sizeof(V));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, g, b, lds, s, u);
+    return hipGetLastError();
+  };
+  if (lanes <= 1) return go(spmm_tile_kernel<V, 1, VE, W, RW>);
+  if (lanes <= 2) return go(spmm_tile_kernel<V, 2, VE, W, RW>);
+  return hipErrorInvalidValue;
+}
+
+template <typename V>
+hipError_t launch_spmm_tile_reduce(const SpmmTileArgs<V>& t, hipStream_t s) {
+  if (t.n_rows <= 0 || t.m <= 0) return hipSuccess;
+  int kc = 1;
+  while (kc < t.k) kc *= 2;
+  if (kc > kWave) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(spmm_tile_reduce_kernel<V>,
+                     dim3((unsigned)(((int64_t)t.n_rows * kWave + kBlock - 1) / kBlock)),
+                     dim3(kBlock), 0, s, t, kc);
+  return hipGetLastError();
+}
+
+template size_t spmm_tile_workspace<float>(int, int, int, int);
+template size_t spmm_tile_workspace<double>(int, int, int, int);
+template hipError_t launch_spmm_tiles<float>(const SpmmTileArgs<float>&, hipStream_t);
+template hipError_t launch_spmm_tiles<double>(const SpmmTileArgs<double>&, hipStream_t);
+template hipError_t launch_spmm_tile_reduce<float>(const SpmmTileArgs<float>&, hipStream_t);
+template hipError_t launch_spmm_tile_reduce<double>(const SpmmTileArgs<double>&, hipStream_t);
 
 }  // namespace spmv

@@ -98,11 +98,12 @@ __device__ __forceinline__ void tile_block(const TileArgs<V>& a, int t, V* xs) {
   const int g = t / a.nb, b = t - g * a.nb;
   const int c0 = b * BC;   // < N
   const int clen = min(BC, a.N - c0);
-  // lane 2k + e: seg[row k of this wave][b + e] (rows past the end clamped
-  // to the last; their bounds are not used)
+  // lane 2k + e: the bound of block b + e of row k of this wave (every
+  // kTileSub-th of the row's quarter-block bounds; rows past the end clamped
+  // to the last, their bounds not used)
   const int i0 = g * kTileRows + wave;
   const int ri = min(i0 + kWavesPerBlock * min(lane >> 1, RW - 1), a.n_rows - 1);
-  const int32_t sb = a.seg[(int64_t)ri * (a.nb + 1) + b + (lane & 1)];
+  const int32_t sb = a.seg[(int64_t)ri * (a.nb * kTileSub + 1) + kTileSub * (b + (lane & 1))];
   if (a.x_aligned) {
     const int nch = clen / E;
 #pragma unroll

@@ -249,8 +249,11 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
                      split_row, split_nz, p_max, (int32_t)M, tp.min_entries, tp.cap, tp.scan,
                      stats, tp.rows);
   hipLaunchKernelGGL(tile_gate_kernel, dim3(1), dim3(64), 0, s, nnz, stats);
-  hipLaunchKernelGGL(tile_seg_kernel, dim3(grid_for((int64_t)tp.cap * (tp.nb + 1), kBlock)), blk,
-                     0, s, tp.rows, col_idx, tp.nb, tp.bc, (int64_t)tp.cap, stats, tp.seg);
+  // segment bounds at every quarter block (a multi-vector product's tiles
+  // take narrower blocks of x; the SpMV tiles read every fourth bound)
+  const int32_t nq = tp.nb * kTileSub;
+  hipLaunchKernelGGL(tile_seg_kernel, dim3(grid_for((int64_t)tp.cap * (nq + 1), kBlock)), blk, 0,
+                     s, tp.rows, col_idx, nq, tp.bc / kTileSub, (int64_t)tp.cap, stats, tp.seg);
   const unsigned fill_blocks = std::min<unsigned>(grid_for(p_max, kBlock), 4096);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.skip, p_max, 0,
                      stats + kStatTileRows);
@@ -259,7 +262,7 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
   hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.mask_start, p_max,
                      INT_MAX, stats + kStatTileRows);
   hipLaunchKernelGGL(tile_finish_kernel, dim3(grid_for(tp.cap, kBlock)), blk, 0, s, tp.rows,
-                     split_nz, tp.nb, (int64_t)tp.cap, stats, tp.seg, tp.skip, tp.mask_end,
+                     split_nz, nq, (int64_t)tp.cap, stats, tp.seg, tp.skip, tp.mask_end,
                      tp.mask_start, carry_row, carry_val, vbytes);
   hipLaunchKernelGGL(tile_keep_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max,
                      stats, tp.scan);

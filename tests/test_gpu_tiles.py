@@ -99,23 +99,96 @@ def test_tiles_with_unsorted_columns_and_misaligned_x():
     plan(x, yd, 1.0, 0.0)
     torch.cuda.synchronize()
     check(yd.cpu().numpy(), w.row_ptr, col, w.values, w.x, 1.0, 0.0, None, "misaligned x")
+    # SpMM tiles over the unsorted rows (columns outside a tile's X block
+    # come from global X) and with X at a 4-byte offset (no tiles then)
+    X = rng.uniform(-1, 1, (w.N, 8)).astype(np.float32)
+    for off in (0, 1):
+        Xb = torch.zeros(w.N * 8 + off, dtype=torch.float32, device="cuda")
+        Xb[off:] = dev(X.reshape(-1))
+        Xd = Xb[off:].view(w.N, 8)
+        Y = torch.full((w.M, 8), float("nan"), device="cuda")
+        plan.exec_multi(Xd, Y, 1.0, 0.0)
+        torch.cuda.synchronize()
+        ref, scale = oracle.spmm(w.row_ptr, col, w.values, X, 1.0, 0.0, None)
+        ok, worst, idx = oracle.within_tolerance(Y.cpu().numpy(), ref, scale, 1.0, 0.0, None,
+                                                 row_ptr=w.row_ptr)
+        assert ok, ("unsorted spmm", off, divmod(idx, 8), worst)
     plan.destroy()
 
 
-def test_spmm_over_a_tiled_plan():
-    w = CASES["small"]()
+@pytest.mark.parametrize("case", list(CASES))
+def test_spmm_over_a_tiled_plan(case):
+    """SpMM on a plan with long-row tiles: k where the tiles run (16-byte
+    lanes, X rows of at most 32 bytes) and where they do not, row strides
+    past k, beta != 0, against the oracle on every element; then the SpMV of
+    the same plan still right."""
+    w = CASES[case]()
+    dt = w.values.dtype.type
     m = DevMatrix.of(w)
     plan = m.plan(None, strategy="merge", merge_reduce="walk")
     assert plan.info["tile_rows"] > 0
-    X = synth.uniform(w.N * 4, 3, synth.S_X, np.float32).reshape(w.N, 4)
-    Y = torch.full((w.M, 4), float("nan"), device="cuda")
-    plan.exec_multi(dev(X), Y, 1.0, 0.0)
-    torch.cuda.synchronize()
-    Yh = Y.cpu().numpy()
-    for c in range(4):
-        check(Yh[:, c].copy(), w.row_ptr, w.col_idx, w.values, X[:, c].copy(), 1.0, 0.0, None,
-              "spmm col %d" % c)
+    ks = (1, 3, 4, 8, 12, 16, 20) if dt == np.float32 else (1, 2, 4, 6, 8, 10)
+    rng = np.random.default_rng(7)
+    for k in ks:
+        for ld_extra, beta in ((0, 0.0), (4, 0.5)):
+            X = rng.uniform(-1, 1, (w.N, k)).astype(dt)
+            Y0 = rng.uniform(-1, 1, (w.M, k)).astype(dt)
+            tdt = torch.float32 if dt == np.float32 else torch.float64
+            Xb = torch.full((w.N, k + ld_extra), float("nan"), dtype=tdt, device="cuda")
+            Xb[:, :k] = dev(X)
+            Yb = torch.full((w.M, k + ld_extra), float("nan"), dtype=tdt, device="cuda")
+            if beta != 0:
+                Yb[:, :k] = dev(Y0)
+            log("spmm tiles", case, "k", k, "ld+", ld_extra, "beta", beta)
+            plan.exec_multi(Xb[:, :k], Yb[:, :k], 1.5, beta)
+            torch.cuda.synchronize()
+            out = Yb.cpu().numpy()
+            assert np.all(np.isnan(out[:, k:])), "columns past k written"
+            ref, scale = oracle.spmm(w.row_ptr, w.col_idx, w.values, X, 1.5, beta,
+                                     Y0 if beta != 0 else None)
+            ok, worst, idx = oracle.within_tolerance(out[:, :k], ref, scale, 1.5, beta,
+                                                     Y0 if beta != 0 else None,
+                                                     row_ptr=w.row_ptr)
+            assert ok, (case, k, ld_extra, beta, divmod(idx, k), worst)
     # and the SpMV after it still right (the SpMM rewrote the carry rows)
-    y = run(plan, w.x, 1.0, 0.0)
+    y = run(plan, w.x, 1.0, 0.0, None, dt)
     check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "spmv after spmm")
+    plan.destroy()
+
+
+def test_spmm_tile_row_groups():
+    """The SpMM tile kernel takes 8, 16 or 32 rows a wave (the most that
+    still leaves 1024 tiles). The cases above have few tiles (8 a wave); a
+    matrix of ~190 long rows over 2.2M columns takes 16 at k = 4 (one
+    sub-block a column block) and 32 at k = 8 (two), each against the
+    oracle on every element, beta zero and not."""
+    w = _long_rows(20_000, 2_200_000, 200, 45_000, 8)
+    m = DevMatrix.of(w)
+    plan = m.plan(None, strategy="merge", merge_reduce="walk")
+    info = plan.info
+    n, nb = info["tile_rows"], info["tile_blocks"]
+    assert 128 < n <= 200, info   # some long rows fall among the empty ones
+
+    def rows_per_wave(sub):
+        for rw in (32, 16):
+            if -(-n // (8 * rw)) * nb * sub >= 1024:
+                return rw
+        return 8
+
+    assert (rows_per_wave(1), rows_per_wave(2)) == (16, 32), (n, nb)
+    rng = np.random.default_rng(11)
+    for k in (4, 8):
+        X = rng.uniform(-1, 1, (w.N, k)).astype(np.float32)
+        Y0 = rng.uniform(-1, 1, (w.M, k)).astype(np.float32)
+        for beta in (0.0, 0.5):
+            Y = dev(Y0.copy())
+            log("spmm tile groups k", k, "beta", beta)
+            plan.exec_multi(dev(X), Y, -0.75, beta)
+            torch.cuda.synchronize()
+            ref, scale = oracle.spmm(w.row_ptr, w.col_idx, w.values, X, -0.75, beta,
+                                     Y0 if beta != 0 else None)
+            ok, worst, idx = oracle.within_tolerance(Y.cpu().numpy(), ref, scale, -0.75, beta,
+                                                     Y0 if beta != 0 else None,
+                                                     row_ptr=w.row_ptr)
+            assert ok, (k, beta, divmod(idx, k), worst)
     plan.destroy()
