@@ -141,39 +141,66 @@ __global__ __launch_bounds__(kBlock) void tile_seg_kernel(const int32_t* __restr
   seg[i * (nb + 1) + b] = pos;
 }
 
+// Inclusive running maximum of an int across the wave, in DPP moves (the
+// steps of wave_scan_i32 with max in place of +).
+__device__ __forceinline__ int wave_max_scan_i32(int x) {
+  const int lane = lane_id();
+  const int r = lane & 15, row = lane >> 4;
+  int t;
+  t = dpp_i32<dpp_row_shr(1)>(0, x);
+  x = r >= 1 ? max(x, t) : x;
+  t = dpp_i32<dpp_row_shr(2)>(0, x);
+  x = r >= 2 ? max(x, t) : x;
+  t = dpp_i32<dpp_row_shr(4)>(0, x);
+  x = r >= 4 ? max(x, t) : x;
+  t = dpp_i32<dpp_row_shr(8)>(0, x);
+  x = r >= 8 ? max(x, t) : x;
+  t = dpp_i32<kDppRowBcast15, 0xA>(0, x);
+  x = (row & 1) ? max(x, t) : x;
+  t = dpp_i32<kDppRowBcast31, 0xC>(0, x);
+  x = row >= 2 ? max(x, t) : x;
+  return x;
+}
+
 // Running maximum along each tile row's boundaries (only changes anything
 // when a row's columns are not sorted); the row's interior partitions marked
 // as skipped by the walk kernel, with zero carries that the fix-up adds to
 // the row harmlessly; and the row's nonzeros in its first and last
 // partition masked off for the walk kernel (so its carry there is 0 and its
 // y gets beta * y only). A partition holds at most one tile row's start and
-// one tile row's end, so no two threads write the same mask. One thread per
-// tile row.
+// one tile row's end, so no two threads write the same mask. One wave per
+// tile row (a row's bounds and interior partitions number in the
+// thousands: one thread per row took 0.5 ms on the bimodal matrix).
 __global__ __launch_bounds__(kBlock) void tile_finish_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ split_nz, int32_t nb,
     int64_t n_max, const int64_t* __restrict__ stats, int32_t* __restrict__ seg,
     int32_t* __restrict__ skip, int32_t* __restrict__ mask_end, int32_t* __restrict__ mask_start,
     int32_t* __restrict__ carry_row, void* carry_val, int vbytes) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= n_max || i >= stats[kStatTileRows]) return;
+  const int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  if (i >= n_max || i >= stats[kStatTileRows]) return;   // wave-uniform
+  const int lane = lane_id();
   int32_t* s = seg + i * (nb + 1);
   int32_t run = s[0];
-  for (int b = 1; b <= nb; ++b) {
-    run = max(run, s[b]);
-    s[b] = run;
+  for (int b0 = 0; b0 <= nb; b0 += kWave) {
+    const int b = b0 + lane;
+    const int32_t v = max(wave_max_scan_i32(b <= nb ? s[b] : INT_MIN), run);
+    if (b <= nb) s[b] = v;
+    run = __builtin_amdgcn_readlane(v, kWave - 1);
   }
   const int32_t* row = rows + kTileRowInts * i;
   const int32_t p_first = row[3], p_end = row[4];
-  for (int32_t p = p_first; p < p_end; ++p) {
+  for (int32_t p = p_first + lane; p < p_end; p += kWave) {
     skip[p] = 1;
     carry_row[p] = row[0];
     if (vbytes == 4) static_cast<float*>(carry_val)[p] = 0.f;
     else static_cast<double*>(carry_val)[p] = 0.0;
   }
-  // the row's start, in the partition before its interior run
-  if (p_first > 0 && row[1] < split_nz[p_first]) mask_start[p_first - 1] = row[1];
-  // the row's end partition
-  if (row[2] > split_nz[p_end]) mask_end[p_end] = row[2];
+  if (lane == 0) {
+    // the row's start, in the partition before its interior run
+    if (p_first > 0 && row[1] < split_nz[p_first]) mask_start[p_first - 1] = row[1];
+    // the row's end partition
+    if (row[2] > split_nz[p_end]) mask_end[p_end] = row[2];
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* __restrict__ a, int64_t n,
@@ -261,7 +288,8 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
                      stats + kStatTileRows);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_blocks), blk, 0, s, tp.mask_start, p_max,
                      INT_MAX, stats + kStatTileRows);
-  hipLaunchKernelGGL(tile_finish_kernel, dim3(grid_for(tp.cap, kBlock)), blk, 0, s, tp.rows,
+  hipLaunchKernelGGL(tile_finish_kernel, dim3(grid_for((int64_t)tp.cap * kWave, kBlock)), blk, 0,
+                     s, tp.rows,
                      split_nz, nq, (int64_t)tp.cap, stats, tp.seg, tp.skip, tp.mask_end,
                      tp.mask_start, carry_row, carry_val, vbytes);
   hipLaunchKernelGGL(tile_keep_kernel, dim3(grid_for(p_max, kBlock)), blk, 0, s, tp.skip, p_max,
