@@ -28,7 +28,6 @@ constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
 constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;   // L2 of one XCD
 constexpr int kMaxBins = 8;
 constexpr int kBinRowsPerBlock = 1024;   // rows one binning workgroup owns
-constexpr int kWindowBytes = 12288;      // cap of the staged x window (register form)
 constexpr int kWinIntervals = 3;         // column intervals of one x window
 constexpr int kWinTable = 8;             // int32 per window: {lo, len} x 3, total, flags
 

@@ -893,10 +893,6 @@ hipError_t launch_spmm_tiles_w(const SpmmTileArgs<V>& t, hipStream_t s) {
   const size_t lds = ((size_t)t.bck + 1) * t.k * sizeof(V);
   const dim3 g((unsigned)tiles), b(W * kWave);
   auto go = [&](auto kern) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-        kSpmmTileBytes + 64 * (int)sizeof(V));
-    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(kern, g, b, lds, s, u);
     return hipGetLastError();
   };

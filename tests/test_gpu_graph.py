@@ -86,8 +86,10 @@ def test_spmv_graph_replays(case):
     plan.destroy()
 
 
-@pytest.mark.parametrize("case", ["stream", "walk"])
+@pytest.mark.parametrize("case", ["stream", "walk", "walk_tiles_k8"])
 def test_spmm_graph_replays(case):
+    # the walk cases run the SpMM long-row tiles too (X rows of 16 and 32
+    # bytes): tiles, merge walk, fix-up and tile reduction, four launches
     if case == "stream":
         w = synth.laplacian(n=150)
         opts = dict(strategy="merge")
@@ -95,9 +97,11 @@ def test_spmm_graph_replays(case):
     else:
         w = synth.bimodal(M=30_000, n_long=20, long_len=6000)
         opts = dict(strategy="merge", merge_reduce="walk")
-        k = 4
+        k = 4 if case == "walk" else 8
     m = DevMatrix.of(w)
     plan = m.plan(None, **opts)
+    if case != "stream":
+        assert plan.info["tile_rows"] > 0, plan.info
     dt = w.values.dtype
     rng = np.random.default_rng(5)
     X = dev(rng.uniform(-1, 1, (w.N, k)).astype(dt))
