@@ -409,8 +409,13 @@ SPMV_API spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y
  * workspace, workspace_bytes: device memory of at least
  *    spmv_spmm_workspace_size(plan, k) bytes for the k-wide carries of rows
  *    cut between partitions (0 bytes, NULL allowed, when the plan's
- *    partitions end at row ends: merge_reduce = stream). Owned by the caller;
- *    its contents need no initialisation and are scratch after the call.
+ *    partitions end at row ends: merge_reduce = stream), plus, on a plan
+ *    with long-row tiles and X rows of 16 or 32 bytes, the tiles' partial
+ *    sums per row, X sub-block and column. Owned by the caller; its
+ *    contents need no initialisation and are scratch after the call.
+ *    (The tiles run when X and Y are 16-byte aligned and ldx, ldy and k
+ *    are whole 16-byte lanes; otherwise the merge-path walk takes every
+ *    row. Results differ by rounding order only.)
  * k = 0 or M = 0 does nothing. k > 64 runs in column blocks of 64.
  *
  * Uses the plan's merge-path partitions whatever its SpMV strategy.
@@ -427,8 +432,8 @@ SPMV_API spmv_status_t spmv_exec_multi(spmv_plan_t plan, int64_t k, const void* 
 
 /* spmv_exec_multi that also records ev_begin and ev_end on the same stream:
  * for k <= 64 the main kernel's dispatch records them at its start and end
- * (the carry fix-up that follows is outside); for k > 64 they bracket every
- * launch of the call. Either event may be NULL; a call with k = 0 or M = 0
+ * (the carry fix-up that follows is outside); for k > 64, and when the
+ * long-row tiles run, they bracket every launch of the call. Either event may be NULL; a call with k = 0 or M = 0
  * launches nothing and records neither. */
 SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const void* X,
                                               int64_t ldx, void* Y, int64_t ldy, double alpha,
