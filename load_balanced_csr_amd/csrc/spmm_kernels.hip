@@ -28,6 +28,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 namespace spmv {
 namespace {
 
@@ -178,19 +180,15 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   const V* vall = reinterpret_cast<const V*>(s_val + ((W * n0) & 3));   // vall[t] = val[n0 + t]
   // (W * n0 may wrap in int32 for fp64; its low two bits are still right)
   // a partition a tiled row starts or ends in: that row's entries belong to
-  // the tiles, so their staged values become 0 and their columns 0 (one X
-  // row for all of them)
+  // the tiles, so their staged columns become -1: the walk reads X row 0 for
+  // them and adds nothing (whatever X row 0 holds)
   if (a.mask_end) {
     const int mlo = a.mask_end[p], mhi = a.mask_start[p];
     if (mlo > n0 || mhi < n1) {   // wave-uniform
-      V* vw = reinterpret_cast<V*>(s_val + ((W * n0) & 3));
       int32_t* cw = s_col + (n0 & 3);
       for (int t = lane; t < nloc; t += kWave) {
         const int gk = n0 + t;
-        if (gk < mlo || gk >= mhi) {
-          vw[t] = V(0);
-          cw[t] = 0;
-        }
+        if (gk < mlo || gk >= mhi) cw[t] = -1;
       }
       wave_sync();
     }
@@ -251,26 +249,30 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
   const uint32_t xcol_bytes = (uint32_t)lcol * (uint32_t)sizeof(V);
   for (int jb = jbeg; jb < jend; jb += B) {
     // the batch's column indices first (LDS), then every X-row load: past the
-    // run's end a lane re-reads its last nonzero's row and adds 0 for it
+    // run's end a lane re-reads its last nonzero's row, and a masked entry
+    // (column -1) reads row 0; neither adds anything (a select, not a
+    // product with 0, so an Inf or NaN in X stays out of other rows)
     int cs[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) cs[u] = coll[min(jb + u, jend - 1)];
     VV xv[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
+      const uint32_t c = (uint32_t)max(cs[u], 0);
       if (OFF32)
         xv[u] = vec_load<V, VE>(
-            reinterpret_cast<const V*>(xbase + ((uint32_t)cs[u] * xrow_bytes + xcol_bytes)));
+            reinterpret_cast<const V*>(xbase + (c * xrow_bytes + xcol_bytes)));
       else
-        xv[u] = vec_load<V, VE>(xcol + (int64_t)cs[u] * a.ldx);
+        xv[u] = vec_load<V, VE>(xcol + (int64_t)c * a.ldx);
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const int jj = jb + u;
       finish_rows(jj);
-      const V v = jj < jend ? vall[min(jj, jend - 1)] : V(0);
+      const bool live = jj < jend && cs[u] >= 0;
+      const V v = vall[min(jj, jend - 1)];
 #pragma unroll
-      for (int q = 0; q < VE; ++q) acc.v[q] = fma(v, xv[u].v[q], acc.v[q]);
+      for (int q = 0; q < VE; ++q) acc.v[q] = live ? fma(v, xv[u].v[q], acc.v[q]) : acc.v[q];
     }
   }
   finish_rows(jend);
@@ -402,7 +404,12 @@ __global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V
     VV acc;
 #pragma unroll
     for (int q = 0; q < VE; ++q) acc.v[q] = V(0);
-    for (int jb = rs + part; jb < re; jb += G * B) {
+    // one batch of B of the row's nonzeros (every G-th): all X-row loads
+    // first, then the FMAs. Only a row's last batch runs past its end; there
+    // a lane re-reads the row's last nonzero and adds nothing for it (a
+    // select, so an Inf or NaN in that X row does not turn the sum into
+    // NaN), the full batches before it need no select.
+    auto batch = [&](int jb, auto tail) {
       int cs[B];
 #pragma unroll
       for (int u = 0; u < B; ++u) cs[u] = coll[min(jb + G * u, re - 1)];
@@ -418,11 +425,19 @@ __global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V
 #pragma unroll
       for (int u = 0; u < B; ++u) {
         const int jj = jb + G * u;
-        const V v = jj < re ? vall[min(jj, re - 1)] : V(0);
+        const V v = vall[min(jj, re - 1)];
 #pragma unroll
-        for (int q = 0; q < VE; ++q) acc.v[q] = fma(v, xv[u].v[q], acc.v[q]);
+        for (int q = 0; q < VE; ++q) {
+          if (decltype(tail)::value)
+            acc.v[q] = jj < re ? fma(v, xv[u].v[q], acc.v[q]) : acc.v[q];
+          else
+            acc.v[q] = fma(v, xv[u].v[q], acc.v[q]);
+        }
       }
-    }
+    };
+    int jb = rs + part;
+    for (; jb + G * (B - 1) < re; jb += G * B) batch(jb, std::false_type{});
+    if (jb < re) batch(jb, std::true_type{});
     for (int g = 1; g < G; g <<= 1) {
 #pragma unroll
       for (int q = 0; q < VE; ++q) acc.v[q] += __shfl_xor(acc.v[q], KL * g, kWave);
