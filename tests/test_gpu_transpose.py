@@ -93,3 +93,37 @@ def test_transpose_checks_and_empty():
     y = run(plan, np.ones(5, np.float32), 1.0, 0.0)
     assert np.array_equal(y, np.zeros(9, np.float32))
     plan.destroy()
+
+
+def test_transpose_long_columns_take_tiles():
+    """A with 40 columns of 8,000 entries: A^T has long rows, so the
+    transposed plan takes the long-row tiles (SpMV and SpMM). A is built
+    from B = A^T (a bimodal matrix) on the host; y = A^T x = B x."""
+    Bw = synth.bimodal(M=20_000, n_long=40, long_len=8000)
+    rows = np.repeat(np.arange(Bw.M, dtype=np.int64), np.diff(Bw.row_ptr))
+    order = np.lexsort((rows, Bw.col_idx))
+    a_col = rows[order].astype(np.int32)
+    a_val = Bw.values[order]
+    a_rp = np.zeros(Bw.N + 1, np.int32)
+    a_rp[1:] = np.cumsum(np.bincount(Bw.col_idx, minlength=Bw.N))
+    plan = lb.Plan.transpose(dev(a_rp), dev(a_col), dev(a_val), (Bw.N, Bw.M),
+                             strategy="merge", merge_reduce="walk")
+    assert plan.M == Bw.M and plan.N == Bw.N
+    assert plan.info["tile_rows"] > 0, plan.info
+    y0 = synth.uniform(Bw.M, 6, synth.S_Y, np.float32)
+    for alpha, beta in ((1.0, 0.0), (-1.5, 0.5)):
+        log("transpose tiles", alpha, beta)
+        y = run(plan, Bw.x, alpha, beta, y0 if beta != 0 else None)
+        _check_t(y, a_rp, a_col, a_val, Bw.M, Bw.x, alpha, beta, y0, "transpose tiles")
+    rng = np.random.default_rng(12)
+    for k in (4, 8):
+        X = rng.uniform(-1, 1, (Bw.N, k)).astype(np.float32)
+        Y = torch.full((Bw.M, k), float("nan"), device="cuda")
+        log("transpose tiles spmm k", k)
+        plan.exec_multi(dev(X), Y)
+        torch.cuda.synchronize()
+        ref, scale = oracle.spmm(Bw.row_ptr, Bw.col_idx, Bw.values, X, 1.0, 0.0, None)
+        ok, worst, idx = oracle.within_tolerance(Y.cpu().numpy(), ref, scale, 1.0, 0.0, None,
+                                                 row_ptr=Bw.row_ptr)
+        assert ok, (k, divmod(idx, k), worst)
+    plan.destroy()
