@@ -89,7 +89,7 @@ typedef enum spmv_dtype { SPMV_F32 = 0, SPMV_F64 = 1 } spmv_dtype_t;
  *          (PPoPP'23 page, Secs. 4.2 and 5.2.2), longest bins dispatched first.
  *  AUTO  : the planner picks MERGE or BINNED from the matrix size and row
  *          lengths (a switch fitted on MI355X: BINNED below 3,000,000
- *          nonzeros when some row is longer than T/8, below 200,000 when
+ *          nonzeros when some row is longer than T/8, below 2,000,000 when
  *          none is and T = 1024; MERGE above, and whenever every row fits
  *          T/8 with T = 256). */
 typedef enum spmv_strategy {

@@ -55,7 +55,9 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Default row-length bins: inclusive upper lengths and lanes per row.
 const int64_t kDefaultMaxLen[kMaxBins - 1] = {2, 8, 16, 32, 128, 512, 4096};
-const int32_t kDefaultLanes[kMaxBins] = {1, 2, 4, 8, 16, 32, 64, 256};
+// measured with the quad-load row sums (laplacian, power-law, bimodal,
+// banded): rows of 17..32 on 4 lanes and 33..128 on 8 beat 8 and 16
+const int32_t kDefaultLanes[kMaxBins] = {1, 2, 4, 4, 8, 32, 64, 256};
 
 }  // namespace
 
@@ -257,9 +259,12 @@ int32_t default_group_rows(const spmv_plan_st* p, int waves) {
 // (main kernel and carry fix-up): binned below kBinnedMaxNnzWalk nonzeros
 // when rows cross partitions, below kBinnedMaxNnzStream when they do not,
 // merge-path above (a sweep of 42 synthetic matrices, 167 to 29M nonzeros,
-// uniform and skewed rows; the group-mapped schedule was never the fastest).
+// uniform and skewed rows; the group-mapped schedule was never the fastest;
+// re-run when the binned rows went to 16-byte quad loads, which moved the
+// stream cap from 200,000 to 2,000,000: 479,464 nonzeros 9.6 against
+// 12.7 us, 1.9M 18.8 against 19.0, 9.6M 65.2 against 59.6).
 constexpr int64_t kBinnedMaxNnzWalk = 3000000;
-constexpr int64_t kBinnedMaxNnzStream = 200000;
+constexpr int64_t kBinnedMaxNnzStream = 2000000;
 
 int32_t choose_strategy(const spmv_plan_st* p) {
   const char* env = std::getenv("SPMV_STRATEGY");
@@ -415,6 +420,7 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.identity = p->identity;
     a.n_launch = p->n_launch;
     a.xcd_remap = p->xcd_remap;
+    a.nnz = (int32_t)p->nnz;
     for (int i = 0; i < p->n_launch; ++i) a.bin[i] = p->launch[i];
     if (p->bin_streams > 0 && p->n_launch > 1)
       err = launch_binned_per_bin<V>(p, a, stream, ev0, ev1);

@@ -28,6 +28,48 @@ __device__ __forceinline__ void store_row(const BinnedArgs<V>& a, int r, V acc) 
   a.y[r] = out;
 }
 
+// The sum over row entries [s, e) of the quads q0 + t, q0 + t + G, ...
+// (q0 = s / 4, t = this lane's place among the G lanes of the row), NQ
+// quads a step (one for rows of up to 8 entries on 1 or 2 lanes, two
+// otherwise): 16-byte loads of columns and values (element loads for the
+// array's last, partial quad), then the x gathers; entries of a quad outside
+// [s, e) are masked to exactly 0 (their gather reads x[0]). Four running
+// sums, one per entry of a quad, added in a fixed order.
+template <typename V, int G>
+__device__ __forceinline__ V quad_row_sum(const BinnedArgs<V>& a, int32_t s, int32_t e, int t) {
+  // unsigned: 4q + 3 may pass 2^31 - 1 near the largest nnz
+  const uint32_t q1 = ((uint32_t)e + 3u) >> 2;
+  const uint32_t nnz = (uint32_t)a.nnz;
+  constexpr int NQ = G <= 2 ? 1 : 2;
+  V acc[4] = {V(0), V(0), V(0), V(0)};
+  for (uint32_t q = ((uint32_t)s >> 2) + (uint32_t)t; q < q1; q += (uint32_t)(NQ * G)) {
+    uint32_t qq[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) qq[h] = min(q + (uint32_t)(h * G), q1 - 1u);
+    i32x4 c[NQ];
+    Quad<V> v[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      const bool full = 4u * qq[h] + 3u < nnz;
+      c[h] = full ? load_quad<false>(a.col_idx, (int)qq[h], 0)
+                  : load_quad<true>(a.col_idx, (int)qq[h], (int)nnz);
+      v[h] = full ? load_quad<false>(a.val, (int)qq[h], 0)
+                  : load_quad<true>(a.val, (int)qq[h], (int)nnz);
+    }
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      const bool live = q + (uint32_t)(h * G) < q1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = 4u * qq[h] + (uint32_t)j;
+        const bool in = live && k >= (uint32_t)s && k < (uint32_t)e;
+        acc[j] += masked_product(in, v[h][j], a.x, c[h][j]);
+      }
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // G lanes per row (G = 1, 2, ..., 64), 256 / G rows per workgroup.
 template <typename V, int G>
 __device__ __forceinline__ void group_rows(const BinnedArgs<V>& a, const BinLaunch& L,
@@ -38,22 +80,7 @@ __device__ __forceinline__ void group_rows(const BinnedArgs<V>& a, const BinLaun
   if (idx >= L.n_rows) return;  // whole groups leave together
   const int r = a.identity ? L.row_begin + idx : a.bins[L.row_begin + idx];
   const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
-  V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
-  // unsigned: with nnz near 2^31 the stride past the row end must not wrap
-  unsigned k = (unsigned)(s + gl);
-  const unsigned ue = (unsigned)e;
-  for (; k + 3u * G < ue; k += 4u * G) {
-    const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + G);
-    const int c2 = ld_stream(a.col_idx + k + 2 * G), c3 = ld_stream(a.col_idx + k + 3 * G);
-    const V v0 = ld_stream(a.val + k), v1 = ld_stream(a.val + k + G);
-    const V v2 = ld_stream(a.val + k + 2 * G), v3 = ld_stream(a.val + k + 3 * G);
-    acc0 = fma(v0, a.x[c0], acc0);
-    acc1 = fma(v1, a.x[c1], acc1);
-    acc2 = fma(v2, a.x[c2], acc2);
-    acc3 = fma(v3, a.x[c3], acc3);
-  }
-  for (; k < ue; k += G) acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
-  V acc = (acc0 + acc1) + (acc2 + acc3);
+  V acc = quad_row_sum<V, G>(a, s, e, gl);
   if (G > 1) acc = group_sum<G>(acc);
   if (gl == 0) store_row(a, r, acc);
 }
@@ -65,23 +92,7 @@ __device__ __forceinline__ void block_row(const BinnedArgs<V>& a, const BinLaunc
   __shared__ V s_part[kWavesPerBlock];
   const int r = a.identity ? L.row_begin + tile : a.bins[L.row_begin + tile];
   const int s = a.row_ptr[r], e = a.row_ptr[r + 1];
-  V acc0 = V(0), acc1 = V(0), acc2 = V(0), acc3 = V(0);
-  unsigned k = (unsigned)s + threadIdx.x;   // unsigned: no wrap near 2^31
-  const unsigned ue = (unsigned)e;
-  for (; k + 3u * kBlock < ue; k += 4u * kBlock) {
-    const int c0 = ld_stream(a.col_idx + k), c1 = ld_stream(a.col_idx + k + kBlock);
-    const int c2 = ld_stream(a.col_idx + k + 2 * kBlock);
-    const int c3 = ld_stream(a.col_idx + k + 3 * kBlock);
-    const V v0 = ld_stream(a.val + k), v1 = ld_stream(a.val + k + kBlock);
-    const V v2 = ld_stream(a.val + k + 2 * kBlock), v3 = ld_stream(a.val + k + 3 * kBlock);
-    acc0 = fma(v0, a.x[c0], acc0);
-    acc1 = fma(v1, a.x[c1], acc1);
-    acc2 = fma(v2, a.x[c2], acc2);
-    acc3 = fma(v3, a.x[c3], acc3);
-  }
-  for (; k < ue; k += kBlock)
-    acc0 = fma(ld_stream(a.val + k), a.x[ld_stream(a.col_idx + k)], acc0);
-  V acc = group_sum<kWave>((acc0 + acc1) + (acc2 + acc3));
+  V acc = group_sum<kWave>(quad_row_sum<V, kBlock>(a, s, e, threadIdx.x));
   if (lane_id() == 0) s_part[threadIdx.x / kWave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) store_row(a, r, (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));

@@ -438,6 +438,7 @@ struct BinnedArgs {
   int32_t identity;
   int32_t n_launch;
   int32_t xcd_remap;
+  int32_t nnz;           // the arrays' length (their last quad may be partial)
   BinLaunch bin[kMaxBins];
 };
 
