@@ -63,10 +63,26 @@ __global__ __launch_bounds__(GW * kWave) void group_spmv_kernel(const GroupArgs<
   for (int c = 0; c < nchunks; ++c) {
     const int base = c * CH;
     const int cnt = min(CH, A - base);
-    // products of the chunk's atoms, coalesced
-    for (int j = t; j < cnt; j += NT) {
-      const int64_t e = n0 + base + j;
-      s_prod[j] = a.val[e] * a.x[a.col_idx[e]];
+    // products of the chunk's atoms, coalesced: a thread's CH / NT atoms
+    // (t, t + NT, ...) are loaded together, then gathered together, before
+    // the first product is stored (atoms past the chunk re-read its last one
+    // and store nothing)
+    {
+      constexpr int U = CH / NT;
+      int cu[U];
+      V vu[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = n0 + base + min(t + u * NT, cnt - 1);
+        cu[u] = ld_stream(a.col_idx + e);
+        vu[u] = ld_stream(a.val + e);
+      }
+      V xu[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) xu[u] = a.x[cu[u]];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t + u * NT < cnt) s_prod[t + u * NT] = vu[u] * xu[u];
     }
     __syncthreads();
     // rows whose atoms meet this chunk: [first, last]
