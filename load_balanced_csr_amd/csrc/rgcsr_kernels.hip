@@ -116,9 +116,13 @@ __global__ __launch_bounds__(kBlock) void rg_spmv_kernel(const RgArgs<V> a) {
       c[u] = ok ? ld_stream(a.col + at + (int64_t)(k + u) * a.G) : 0;
       v[u] = ok ? ld_stream(a.val + at + (int64_t)(k + u) * a.G) : V(0);
     }
+    // every gather in flight before the first FMA; a padded step reads x[0]
+    // and adds nothing (a select, not 0 * x)
+    V xv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (k + u < L) acc = fma(v[u], a.x[c[u]], acc);
+    for (int u = 0; u < U; ++u) xv[u] = a.x[c[u]];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = k + u < L ? fma(v[u], xv[u], acc) : acc;
   }
   if (!live) return;
   V out = a.alpha * acc;
