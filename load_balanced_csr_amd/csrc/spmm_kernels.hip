@@ -95,6 +95,25 @@ __device__ __forceinline__ void stage_dma(int32_t* dst, const int32_t* a, int64_
   }
 }
 
+// X addressing of the SpMM kernels (XA): 0, a 64-bit element offset; 1,
+// a 32-bit byte offset from a wave-uniform base (X spans < 4 GiB), the row
+// stride a run-time multiply; 2, the same with rows of exactly KL * VE
+// elements (contiguous X), so the stride is a shift (a 32-bit multiply is a
+// quarter-rate instruction, one per X-row load).
+constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+template <typename V, int KL, int VE, int XA>
+__device__ __forceinline__ Vec<V, VE> x_row(const char* xbase, const V* xcol, uint32_t c,
+                                            uint32_t xrow_bytes, uint32_t xcol_bytes,
+                                            int64_t ldx) {
+  constexpr int SH = ilog2c(KL * VE * (int)sizeof(V));
+  if constexpr (XA == 2)
+    return vec_load<V, VE>(reinterpret_cast<const V*>(xbase + ((c << SH) + xcol_bytes)));
+  else if constexpr (XA == 1)
+    return vec_load<V, VE>(reinterpret_cast<const V*>(xbase + (c * xrow_bytes + xcol_bytes)));
+  else
+    return vec_load<V, VE>(xcol + (int64_t)c * ldx);
+}
+
 // Y[row, col .. col + VE) = alpha * acc + beta * Y (Y not read when beta = 0)
 template <typename V, int VE>
 __device__ __forceinline__ void spmm_store(const SpmmArgs<V>& a, int row, int col,
@@ -121,9 +140,10 @@ __device__ __forceinline__ void spmm_store(const SpmmArgs<V>& a, int row, int co
   }
 }
 
-// OFF32: X spans less than 4 GiB, so a row's address is the wave-uniform
-// base plus a 32-bit byte offset (one VGPR per address instead of two).
-template <typename V, int KL, int VE, bool OFF32>
+// XA: the X addressing (x_row): a 32-bit offset from a wave-uniform base
+// when X spans less than 4 GiB (one VGPR per address instead of two), a
+// shift for contiguous rows.
+template <typename V, int KL, int VE, int XA>
 __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a) {
   constexpr int S = kWave / KL;   // slots per wave
   constexpr int B = kSpmmBatch;
@@ -258,12 +278,8 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
     VV xv[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const uint32_t c = (uint32_t)max(cs[u], 0);
-      if (OFF32)
-        xv[u] = vec_load<V, VE>(
-            reinterpret_cast<const V*>(xbase + (c * xrow_bytes + xcol_bytes)));
-      else
-        xv[u] = vec_load<V, VE>(xcol + (int64_t)c * a.ldx);
+      xv[u] = x_row<V, KL, VE, XA>(xbase, xcol, (uint32_t)max(cs[u], 0), xrow_bytes,
+                                   xcol_bytes, a.ldx);
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const SpmmArgs<V> a)
 // a workgroup holds PPB consecutive partitions, so the waves of a CU walk
 // neighbouring rows together and share the X rows around them in L1
 // (banded, 8 RHS: 1 partition per workgroup 5.0 ms, 4: 4.2 ms, 8: 3.2 ms).
-template <typename V, int KL, int VE, bool OFF32, int PPB>
+template <typename V, int KL, int VE, int XA, int PPB>
 __global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V> a) {
   constexpr int S = kWave / KL;   // slots per wave
   constexpr int B = 8;
@@ -416,11 +432,8 @@ __global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V
       VV xv[B];
 #pragma unroll
       for (int u = 0; u < B; ++u) {
-        if (OFF32)
-          xv[u] = vec_load<V, VE>(
-              reinterpret_cast<const V*>(xbase + ((uint32_t)cs[u] * xrow_bytes + xcol_bytes)));
-        else
-          xv[u] = vec_load<V, VE>(xcol + (int64_t)cs[u] * a.ldx);
+        xv[u] = x_row<V, KL, VE, XA>(xbase, xcol, (uint32_t)cs[u], xrow_bytes, xcol_bytes,
+                                     a.ldx);
       }
 #pragma unroll
       for (int u = 0; u < B; ++u) {
@@ -771,16 +784,16 @@ __global__ __launch_bounds__(kBlock) void spmm_tile_reduce_kernel(const SpmmTile
   }
 }
 
-template <typename V, int KL, int VE, bool OFF32>
+template <typename V, int KL, int VE, int XA>
 void launch_rows(const SpmmArgs<V>& a, int ppb, size_t lds_wave, hipStream_t s, hipEvent_t ev0,
                  hipEvent_t ev1) {
   const dim3 g((a.P + ppb - 1) / ppb);
   const size_t lds = (size_t)ppb * lds_wave;
   switch (ppb) {
-    case 8: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 8>, g, dim3(8 * kWave), lds, s, ev0, ev1, a); break;
-    case 4: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 4>, g, dim3(4 * kWave), lds, s, ev0, ev1, a); break;
-    case 2: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 2>, g, dim3(2 * kWave), lds, s, ev0, ev1, a); break;
-    default: launch_timed(spmm_rows_kernel<V, KL, VE, OFF32, 1>, g, dim3(kWave), lds, s, ev0, ev1, a); break;
+    case 8: launch_timed(spmm_rows_kernel<V, KL, VE, XA, 8>, g, dim3(8 * kWave), lds, s, ev0, ev1, a); break;
+    case 4: launch_timed(spmm_rows_kernel<V, KL, VE, XA, 4>, g, dim3(4 * kWave), lds, s, ev0, ev1, a); break;
+    case 2: launch_timed(spmm_rows_kernel<V, KL, VE, XA, 2>, g, dim3(2 * kWave), lds, s, ev0, ev1, a); break;
+    default: launch_timed(spmm_rows_kernel<V, KL, VE, XA, 1>, g, dim3(kWave), lds, s, ev0, ev1, a); break;
   }
 }
 
@@ -789,6 +802,7 @@ hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEve
   // bytes from X to the end of its last row's k columns
   const uint64_t xspan = (uint64_t)a.ldx * sizeof(V) * (uint64_t)(a.N > 0 ? a.N : 1);
   const bool off32 = xspan < (1ull << 32);
+  const bool contig = off32 && a.ldx == KL * VE;   // rows of exactly KL * VE elements
   const size_t lds_wave = (size_t)spmm_wave_lds(a.cap, sizeof(V));
   if (a.stream) {
     // up to 8 consecutive partitions per workgroup, as many as one CU's LDS
@@ -796,17 +810,20 @@ hipError_t launch_kl(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEve
     // Laplacian 0.186 against 0.171 ms)
     int ppb = 8;
     while (ppb > 1 && (size_t)ppb * lds_wave > (size_t)kLdsBytes) ppb >>= 1;
-    if (off32) launch_rows<V, KL, VE, true>(a, ppb, lds_wave, s, ev0, ev1);
-    else launch_rows<V, KL, VE, false>(a, ppb, lds_wave, s, ev0, ev1);
+    if (contig) launch_rows<V, KL, VE, 2>(a, ppb, lds_wave, s, ev0, ev1);
+    else if (off32) launch_rows<V, KL, VE, 1>(a, ppb, lds_wave, s, ev0, ev1);
+    else launch_rows<V, KL, VE, 0>(a, ppb, lds_wave, s, ev0, ev1);
     return hipGetLastError();
   }
   const int slots = a.n_dispatch ? a.n_dispatch : a.P;
   const dim3 g((slots + kWavesPerBlock - 1) / kWavesPerBlock), b(kBlock);
   const size_t lds = (size_t)kWavesPerBlock * lds_wave;
-  if (off32)
-    launch_timed(spmm_merge_kernel<V, KL, VE, true>, g, b, lds, s, ev0, ev1, a);
+  if (contig)
+    launch_timed(spmm_merge_kernel<V, KL, VE, 2>, g, b, lds, s, ev0, ev1, a);
+  else if (off32)
+    launch_timed(spmm_merge_kernel<V, KL, VE, 1>, g, b, lds, s, ev0, ev1, a);
   else
-    launch_timed(spmm_merge_kernel<V, KL, VE, false>, g, b, lds, s, ev0, ev1, a);
+    launch_timed(spmm_merge_kernel<V, KL, VE, 0>, g, b, lds, s, ev0, ev1, a);
   return hipGetLastError();
 }
 
