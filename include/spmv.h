@@ -186,6 +186,28 @@ typedef struct spmv_plan_options {
                                  by column-blocked tiles (x staged in LDS)
                                  instead of the walk kernel; needs x larger
                                  than one block and the partition order */
+  int32_t x_slabs;            /* merge-path: 0 auto, 1 off, 2 on (env
+                                 SPMV_X_SLABS = 0 / 1). The columns are cut
+                                 into 8 slabs, one per XCD, and the plan keeps
+                                 a copy of A ordered slab-major (each row's run
+                                 of entries in slab 0, for every row, then
+                                 slab 1, ...): the walk over that copy hands
+                                 each XCD the partitions of one slab, so its
+                                 gathers stay within an eighth of x, and a
+                                 final kernel adds each row's slab sums in slab
+                                 order. Auto: walk plans whose x is larger than
+                                 4 MiB (one XCD's L2), split again at T = 256
+                                 (their partitions mostly hold row ends); on:
+                                 every plan. Either way only MERGE plans that
+                                 keep no long-row tiles (those win where both
+                                 apply). Needs columns sorted
+                                 within each row (checked; else no slabs) and
+                                 costs a second allocation the size of A. The
+                                 copy holds A's values as they were at plan
+                                 time: call spmv_plan_update_values after
+                                 changing them (spmv_plan_info.x_slabs tells
+                                 whether the plan took slabs). */
+  int32_t pad0;
 } spmv_plan_options_t;
 
 typedef struct spmv_plan_info {
@@ -227,7 +249,10 @@ typedef struct spmv_plan_info {
   int32_t tile_blocks;        /* column blocks of those tiles */
   int32_t walk_partitions;    /* partitions the walk kernel runs (P without
                                  tiles; those the tiles leave with them) */
-  int32_t pad2;
+  int32_t x_slabs;            /* 1: spmv_exec walks the plan's slab-major copy
+                                 of A (options.x_slabs) */
+  int64_t slab_segments;      /* that copy's (row, slab) runs: its rows */
+  int64_t slab_bytes;         /* size of the copy's allocation (0: none) */
 } spmv_plan_info_t;
 
 /* Build a plan for the CSR matrix A (M x N, nnz stored entries).
@@ -448,6 +473,20 @@ SPMV_API spmv_status_t spmv_exec_multi_events(spmv_plan_t plan, int64_t k, const
  * SPMV_ERR_INVALID_PLAN (library convention: live handles are tracked, so a
  * stale one is never dereferenced). */
 SPMV_API spmv_status_t spmv_destroy(spmv_plan_t plan);
+
+/* Library convention (the inspector-executor pattern: a plan may hold a
+ * copy of A made in its own layout): make the plan use `values` (device,
+ * fp32 or fp64 per the plan's dtype, nnz entries in the layout of the values
+ * given to spmv_plan / _ex / _coo, 16-byte aligned; the same array after its
+ * contents changed, or another one, which the plan then borrows) from the
+ * next spmv_exec on. Plans with x slabs (spmv_plan_info.x_slabs) rewrite
+ * their slab-major copy on `stream`, asynchronously; an exec of the plan on
+ * another stream must not overlap it. Other plans read values at every exec
+ * and only store the pointer. Errors: INVALID_PLAN; INVALID_ARG for a NULL
+ * (nnz > 0) or misaligned pointer; UNSUPPORTED for transposed, CSC and
+ * row-grouped plans (their copies are in another layout: plan again). */
+SPMV_API spmv_status_t spmv_plan_update_values(spmv_plan_t plan, const void* values,
+                                               hipStream_t stream);
 
 /* Switch a live plan between MERGE (PPoPP'23 page, Sec. 5.2.1) and BINNED
  * (OpSparse page, Sec. 5.1; PPoPP'23 page, Secs. 4.2 and 5.2.2) -- both are

@@ -27,7 +27,8 @@ MAX_BINS = 8
 
 EXPORTED = ("spmv_plan", "spmv_plan_ex", "spmv_plan_coo", "spmv_plan_transpose",
             "spmv_plan_csc", "spmv_plan_rgcsr", "spmv_exec", "spmv_exec_events", "spmv_destroy",
-            "spmv_plan_set_strategy", "spmv_plan_set_group", "spmv_plan_info",
+            "spmv_plan_set_strategy", "spmv_plan_set_group", "spmv_plan_update_values",
+            "spmv_plan_info",
             "spmv_plan_copy_splits",
             "spmv_plan_copy_bins", "spmv_read_probe", "spmv_gather_probe",
             "spmv_gather_rows_probe",
@@ -49,7 +50,8 @@ class PlanOptions(ctypes.Structure):
                 ("x_window", ctypes.c_int32), ("bin_streams", ctypes.c_int32),
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
-                ("dispatch_order", ctypes.c_int32), ("long_row_tiles", ctypes.c_int32)]
+                ("dispatch_order", ctypes.c_int32), ("long_row_tiles", ctypes.c_int32),
+                ("x_slabs", ctypes.c_int32), ("pad0", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -69,7 +71,8 @@ class PlanInfo(ctypes.Structure):
                 ("interior_partitions", ctypes.c_int32), ("plan_allocs", ctypes.c_int32),
                 ("plan_syncs", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("tile_blocks", ctypes.c_int32), ("walk_partitions", ctypes.c_int32),
-                ("pad2", ctypes.c_int32)]
+                ("x_slabs", ctypes.c_int32), ("slab_segments", ctypes.c_int64),
+                ("slab_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -99,6 +102,7 @@ def load(build_if_missing: bool = True):
     lib.spmv_exec_events.argtypes = [p, p, p, d, d, p, p, p]
     lib.spmv_destroy.argtypes = [p]
     lib.spmv_plan_set_strategy.argtypes = [p, i32]
+    lib.spmv_plan_update_values.argtypes = [p, p, p]
     lib.spmv_plan_set_group.argtypes = [p, i32, i32]
     lib.spmv_plan_info.argtypes = [p, ctypes.POINTER(PlanInfo)]
     lib.spmv_plan_copy_splits.argtypes = [p, p, p, i64]
@@ -208,7 +212,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
                  stream_lanes: int = 0, x_window: str = "auto",
                  bin_streams: int = 0, dispatch_order: str = "auto",
-                 long_row_tiles: str = "auto") -> PlanOptions:
+                 long_row_tiles: str = "auto", x_slabs: str = "auto") -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored.
     bin_streams: 0 runs the binned schedule as one grid; n >= 1 launches each
     bin on its own, dealt over the caller's stream and n - 1 plan streams.
@@ -224,6 +228,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.bin_streams = bin_streams
     o.dispatch_order = DISPATCH_ORDER[dispatch_order]
     o.long_row_tiles = {"auto": 0, "off": 1}[long_row_tiles]
+    o.x_slabs = {"auto": 0, "off": 1, "on": 2}[x_slabs]
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -467,6 +472,17 @@ def spmv_plan_set_strategy(plan: int, strategy: str) -> None:
     _check(load().spmv_plan_set_strategy(plan, STRATEGY[strategy]), "spmv_plan_set_strategy")
 
 
+def spmv_plan_update_values(plan: int, values: torch.Tensor, stream=None) -> None:
+    """Make the plan use `values` (nnz entries, the planned layout and dtype)
+    from the next exec on; a plan with x slabs rewrites its copy on `stream`."""
+    info = spmv_plan_info(plan)
+    _check_vec(values, "values", int(info["nnz"]),
+               torch.float32 if info["dtype"] == "f32" else torch.float64)
+    _check(load().spmv_plan_update_values(
+        plan, _dev_ptr(values, "values", (torch.float32, torch.float64)), _stream(stream)),
+        "spmv_plan_update_values")
+
+
 def spmv_plan_set_group(plan: int, group_waves: int = 0, rows_per_group: int = 0) -> None:
     """Select the group-mapped schedule (0 = defaults)."""
     _check(load().spmv_plan_set_group(plan, int(group_waves), int(rows_per_group)),
@@ -494,7 +510,8 @@ def spmv_plan_info(plan: int) -> dict:
             "group_waves": info.group_waves, "group_rows": info.group_rows,
             "plan_allocs": info.plan_allocs, "plan_syncs": info.plan_syncs,
             "tile_rows": info.tile_rows, "tile_blocks": info.tile_blocks,
-            "walk_partitions": info.walk_partitions}
+            "walk_partitions": info.walk_partitions, "x_slabs": info.x_slabs,
+            "slab_segments": info.slab_segments, "slab_bytes": info.slab_bytes}
 
 
 def spmv_plan_copy_splits(plan: int):
@@ -534,16 +551,16 @@ class Plan:
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
                  merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
                  bin_streams: int = 0, dispatch_order: str = "auto",
-                 long_row_tiles: str = "auto", stream=None):
+                 long_row_tiles: str = "auto", x_slabs: str = "auto", stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
                 or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams
-                or dispatch_order != "auto" or long_row_tiles != "auto"):
+                or dispatch_order != "auto" or long_row_tiles != "auto" or x_slabs != "auto"):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
                                 merge_reduce, stream_lanes, x_window, bin_streams,
-                                dispatch_order, long_row_tiles)
+                                dispatch_order, long_row_tiles, x_slabs)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     @classmethod
@@ -610,6 +627,12 @@ class Plan:
 
     def set_strategy(self, strategy: str):
         spmv_plan_set_strategy(self.handle, strategy)
+
+    def update_values(self, values, stream=None):
+        """Use `values` from the next call on (see spmv_plan_update_values)."""
+        spmv_plan_update_values(self.handle, values, stream)
+        if self._keep:
+            self._keep = self._keep[:-1] + (values,)
 
     def set_group(self, group_waves: int = 0, rows_per_group: int = 0):
         spmv_plan_set_group(self.handle, group_waves, rows_per_group)

@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libspmv.so")
 SOURCES = ["api.hip", "plan_kernels.hip", "merge_kernels.hip", "binned_kernels.hip",
            "probe_kernels.hip", "spmm_kernels.hip", "sort_kernels.hip", "rgcsr_kernels.hip",
            "group_kernels.hip", "noalloc.hip",
-           "tile_kernels.hip"]
+           "tile_kernels.hip", "slab_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -143,6 +143,26 @@ struct spmv_plan_st {
   hipStream_t side[kMaxBins];
   hipEvent_t fork_ev;
   hipEvent_t join_ev[kMaxBins];
+  // x slabs (walk plans whose x is wider than one XCD's L2): the row tables
+  // (in the workspace), and in a second allocation the slab-major copy A',
+  // its merge-path split and carries, and y' (one sum per segment)
+  int32_t x_slabs;          // 1: spmv_exec walks A' and combines
+  int32_t slab_ipt;
+  int64_t slab_P;
+  SlabRows slab_rows;
+  SlabMatrix slab_m;
+  void* owned_slab;
+  size_t slab_bytes;
+  int64_t* slab_stats;
+  int32_t* slab_split_row;
+  int32_t* slab_split_nz;
+  int32_t* slab_row_bounds;
+  int32_t* slab_carry_row;
+  void* slab_carry_val;
+  void* slab_y;
+  // values held as a copy made at plan time in another layout (transposed,
+  // CSC and row-grouped plans); spmv_plan_update_values refuses those
+  int32_t values_copied;
 };
 
 namespace {
@@ -180,6 +200,8 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
     return fail(SPMV_ERR_INVALID_ARG, "options.dispatch_order %d unknown", o->dispatch_order);
   if (o->long_row_tiles < 0 || o->long_row_tiles > 1)
     return fail(SPMV_ERR_INVALID_ARG, "options.long_row_tiles %d unknown", o->long_row_tiles);
+  if (o->x_slabs < 0 || o->x_slabs > 2)
+    return fail(SPMV_ERR_INVALID_ARG, "options.x_slabs %d unknown", o->x_slabs);
   if (o->bin_streams < 0 || o->bin_streams > SPMV_MAX_BINS)
     return fail(SPMV_ERR_INVALID_ARG, "options.bin_streams must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
@@ -344,6 +366,35 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.M = (int32_t)p->M;
     a.G = p->rg_group;
     err = launch_rg_spmv<V>(a, stream, ev0, ev1);
+  } else if (p->strategy == SPMV_STRATEGY_MERGE && p->x_slabs) {
+    // the walk over A' (partitions in contiguous eighths per XCD, so XCD s
+    // gathers from slab s of x) into one sum per segment, its fix-up, then
+    // the combine of each row's segment sums into y
+    MergeArgs<V> a;
+    std::memset(&a, 0, sizeof a);
+    a.row_ptr = p->slab_m.seg_ptr;
+    a.col_idx = p->slab_m.col;
+    a.val = static_cast<const V*>(p->slab_m.val);
+    a.x = static_cast<const V*>(x);
+    a.y = static_cast<V*>(p->slab_y);
+    a.split_row = p->slab_split_row;
+    a.split_nz = p->slab_split_nz;
+    a.row_bounds = p->slab_row_bounds;
+    a.carry_row = p->slab_carry_row;
+    a.carry_val = static_cast<V*>(p->slab_carry_val);
+    a.alpha = V(1);
+    a.beta = V(0);
+    a.beta_nonzero = 0;
+    a.P = (int32_t)p->slab_P;
+    a.M = (int32_t)p->slab_m.n_seg;
+    a.nnz = (int32_t)p->nnz;
+    a.xcd_remap = 1;
+    a.stream = 0;
+    err = launch_merge<V>(a, p->slab_ipt, stream, ev0, ev1);
+    if (err == hipSuccess)
+      err = launch_slab_combine<V>(p->slab_rows.rptr, p->slab_m.rseg, static_cast<const V*>(p->slab_y),
+                                   static_cast<V*>(y), (V)alpha, (V)beta, beta != 0.0, p->M,
+                                   stream);
   } else if (p->strategy == SPMV_STRATEGY_MERGE) {
     MergeArgs<V> a;
     a.row_ptr = p->row_ptr;
@@ -631,6 +682,68 @@ struct PlanSource {
   int32_t allocs_before = 0;   // allocations the caller made for this plan
 };
 
+// The x slabs' copy A' of the matrix (slab_kernels.hip), after the plan's
+// read-back gave its segment count: one more allocation (A', y', the split
+// and carries of its merge-path walk), then its kernels, enqueued without a
+// further synchronisation. A' takes partitions of T = 1024 units (fp32) or
+// 512 (fp64): its gathers stay in L2, so the walk favours fewer, longer
+// waves (power-law, fp32: 0.217 / 0.186 / 0.170 ms at T = 256 / 512 / 1024).
+// A failed allocation leaves the plan without slabs.
+spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, hipStream_t stream) {
+  const int64_t nnz = p->nnz;
+  const size_t vs = p->dtype == SPMV_F32 ? 4 : 8;
+  const int ipt = vs == 4 ? 16 : 8;
+  const int64_t T = (int64_t)kWave * ipt;
+  if (n_seg <= 0 || n_seg > nnz || n_seg + nnz > kMaxUnits) return SPMV_SUCCESS;
+  const int64_t P = (n_seg + nnz + T - 1) / T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t o_stats = take(sizeof(int64_t) * kStatCount);
+  const size_t o_segp = take(sizeof(int32_t) * (n_seg + 1));
+  const size_t o_col = take(sizeof(int32_t) * nnz);
+  const size_t o_val = take(vs * nnz);
+  const size_t o_rseg = take(sizeof(int32_t) * n_seg);
+  const size_t o_y = take(vs * n_seg);
+  const size_t o_srow = take(sizeof(int32_t) * (P + 1));
+  const size_t o_snz = take(sizeof(int32_t) * (P + 1));
+  const size_t o_rb = take(sizeof(int32_t) * 2 * (P + 1));
+  const size_t o_crow = take(sizeof(int32_t) * P);
+  const size_t o_cval = take(vs * P);
+  void* mem = nullptr;
+  hipError_t err = hipMalloc(&mem, off);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return SPMV_SUCCESS;
+  }
+  ++p->plan_allocs;
+  char* b = static_cast<char*>(mem);
+  p->owned_slab = mem;
+  p->slab_bytes = off;
+  p->slab_stats = reinterpret_cast<int64_t*>(b + o_stats);
+  p->slab_m.seg_ptr = reinterpret_cast<int32_t*>(b + o_segp);
+  p->slab_m.col = reinterpret_cast<int32_t*>(b + o_col);
+  p->slab_m.val = b + o_val;
+  p->slab_m.rseg = reinterpret_cast<int32_t*>(b + o_rseg);
+  p->slab_m.n_seg = n_seg;
+  p->slab_y = b + o_y;
+  p->slab_split_row = reinterpret_cast<int32_t*>(b + o_srow);
+  p->slab_split_nz = reinterpret_cast<int32_t*>(b + o_snz);
+  p->slab_row_bounds = reinterpret_cast<int32_t*>(b + o_rb);
+  p->slab_carry_row = reinterpret_cast<int32_t*>(b + o_crow);
+  p->slab_carry_val = b + o_cval;
+  p->slab_ipt = ipt;
+  p->slab_P = P;
+  if ((err = launch_slab_emit(p->slab_rows, p->slab_m, p->row_ptr, p->col_idx, p->values,
+                              (int)vs, p->M, p->N, nnz, stream)) != hipSuccess ||
+      (err = launch_slab_stats(p->slab_stats, ipt, P, stream)) != hipSuccess ||
+      (err = launch_split_search(p->slab_m.seg_ptr, n_seg, nnz, P, 0, p->slab_split_row,
+                                 p->slab_split_nz, p->slab_row_bounds, p->slab_stats,
+                                 stream)) != hipSuccess)
+    return hip_fail(err, "plan: x slabs");
+  p->x_slabs = 1;
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
                          const spmv_plan_options_t* options, hipStream_t stream,
                          void** extra_out) {
@@ -709,6 +822,13 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
           : std::min<int64_t>(p_max, nnz / (kTileMinPerBlock * tile_nb) + 1);
   int key_bits = 1;
   while (key_bits < 31 && (int64_t(1) << key_bits) < N) ++key_bits;
+  // x slabs: 0 auto, 1 off, 2 on (options, then env SPMV_X_SLABS = 0 / 1);
+  // the workspace reserves their row tables when they may be taken
+  ctl.slabs_req = options && options->x_slabs ? options->x_slabs
+                  : env_int("SPMV_X_SLABS", -1) == 0 ? 1
+                  : env_int("SPMV_X_SLABS", -1) == 1 ? 2 : 0;
+  ctl.slab_room = M > 0 && nnz > 0 && ctl.slabs_req != 1 && (ctl.slabs_req == 2 || ctl.wide_x) &&
+                  slab_scan_max(M) <= kScanMaxElems && 2 * nnz <= kMaxUnits;
 
   // ---- the one workspace allocation -------------------------------------------
   const int64_t n_wg = (M + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
@@ -742,6 +862,13 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   const size_t o_tlist = take(sizeof(int32_t) * tile_p);
   const size_t o_tmend = take(sizeof(int32_t) * tile_p);
   const size_t o_tmstart = take(sizeof(int32_t) * tile_p);
+  // x slabs' row tables
+  const int64_t slab_nt = ctl.slab_room ? slab_tiles(M) : 0;
+  const size_t o_srptr = ctl.slab_room ? take(sizeof(int32_t) * (M + 1)) : 0;
+  const size_t o_smask = ctl.slab_room ? take((size_t)M) : 0;
+  const size_t o_stile_e = ctl.slab_room ? take(sizeof(int32_t) * kSlabs * slab_nt) : 0;
+  const size_t o_stile_g = ctl.slab_room ? take(sizeof(int32_t) * kSlabs * slab_nt) : 0;
+  const size_t o_sscan = ctl.slab_room ? take(scan_temp_bytes(slab_scan_max(M))) : 0;
   const size_t o_rowptr = src.coo ? take(sizeof(int32_t) * (M + 1)) : 0;
   const size_t o_extra = src.extra_bytes ? take(src.extra_bytes) : 0;
   p->ws_bytes = off;
@@ -791,6 +918,14 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   p->tile_seg = tp.seg;
   p->tile_partial = base + o_tpart;
   p->tile_nb = tp.nb;
+  if (ctl.slab_room) {
+    p->slab_rows.rptr = reinterpret_cast<int32_t*>(base + o_srptr);
+    p->slab_rows.mask = reinterpret_cast<uint8_t*>(base + o_smask);
+    p->slab_rows.tile_e = reinterpret_cast<int32_t*>(base + o_stile_e);
+    p->slab_rows.tile_g = reinterpret_cast<int32_t*>(base + o_stile_g);
+    p->slab_rows.scan_temp = base + o_sscan;
+    p->slab_rows.n_tiles = slab_nt;
+  }
   void* extra = src.extra_bytes ? base + o_extra : nullptr;
   int32_t* coo_row_ptr = src.coo ? reinterpret_cast<int32_t*>(base + o_rowptr) : nullptr;
   if (src.coo) p->row_ptr = coo_row_ptr;
@@ -799,6 +934,7 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   auto bail = [&](spmv_status_t s) {
     (void)hipStreamSynchronize(stream);
     (void)hipFree(p->ws);
+    if (p->owned_slab) (void)hipFree(p->owned_slab);
     release_bin_streams(p);
     delete p;
     return s;
@@ -853,6 +989,11 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
                               p->stats, p->carry_row, p->carry_val, (int)vs, stream)) !=
       hipSuccess)
     return bail(hip_fail(err, "plan: long-row tiles"));
+  // x slabs' row tables (when stage 3 takes them)
+  if ((err = launch_plan_choose(ctl, p->stats, 3, stream)) != hipSuccess ||
+      (ctl.slab_room && (err = launch_slab_rows(p->slab_rows, row_ptr, p->col_idx, M, N, p->stats,
+                                                stream)) != hipSuccess))
+    return bail(hip_fail(err, "plan: x slab tables"));
 
   // ---- the one read-back and synchronisation -----------------------------------------
   int64_t host_stats[kStatCount] = {0};
@@ -938,17 +1079,25 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   p->group_waves = 4;
   p->group_rows = default_group_rows(p, 4);
   p->strategy = options && options->strategy ? options->strategy : choose_strategy(p);
+  // x slabs: taken on the device, kept when the columns are sorted within
+  // their rows and the plan runs merge-path
+  if (ctl.slab_room && host_stats[kStatSlabOk] && host_stats[kStatSlabDescents] == 0 &&
+      p->strategy == SPMV_STRATEGY_MERGE) {
+    st = build_slabs(p, host_stats[kStatSlabSegs], stream);
+    if (st != SPMV_SUCCESS) return bail(st);
+  }
   if (env_int("SPMV_LOG", 0))
     std::fprintf(stderr,
                  "[spmv] plan M=%lld N=%lld nnz=%lld dtype=%s strategy=%s reduce=%s G=%d xwin=%d T=%d "
                  "P=%lld max_len=%lld empty=%lld bins=%d identity=%d ws=%zu order=%s allocs=%d "
-                 "syncs=%d\n",
+                 "syncs=%d slabs=%d segs=%lld\n",
                  (long long)M, (long long)N, (long long)nnz, dtype == SPMV_F32 ? "f32" : "f64",
                  p->strategy == SPMV_STRATEGY_MERGE ? "merge" : p->strategy == SPMV_STRATEGY_GROUP ? "group" : "binned",
                  p->merge_reduce == 2 ? "stream" : "walk", p->stream_lanes, p->x_window, p->T,
                  (long long)p->P, (long long)p->max_len, (long long)p->n_empty,
                  p->edges.n_bins, p->identity, p->ws_bytes,
-                 p->dispatch_order == 2 ? "column" : "partition", p->plan_allocs, p->plan_syncs);
+                 p->dispatch_order == 2 ? "column" : "partition", p->plan_allocs, p->plan_syncs,
+                 p->x_slabs, (long long)p->slab_m.n_seg);
   p->magic = kMagic;
   {
     std::lock_guard<std::mutex> lk(g_plans_mu);
@@ -1112,6 +1261,7 @@ spmv_status_t spmv_plan_transpose(spmv_plan_t* out, int64_t M, int64_t N, int64_
     void* val_t = static_cast<char*>(extra) + o_val;
     p->col_idx = col_t;
     p->values = val_t;
+    p->values_copied = 1;
     hipError_t e = launch_fold_flag(flag, kErrRowPtr, p->stats, s);
     if (e == hipSuccess && nnz > 0)
       e = launch_transpose_gather(row_ptr, M, perm, values, (int)vs, nnz, col_t, val_t, s);
@@ -1143,6 +1293,7 @@ spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, int64_t nn
                                   stream);
   if (st != SPMV_SUCCESS) return st;
   spmv_plan_st* p = *out;
+  p->values_copied = 1;
   auto undo = [&](spmv_status_t s2) {
     (void)hipStreamSynchronize(stream);
     (void)spmv_destroy(p);
@@ -1291,6 +1442,24 @@ spmv_status_t spmv_exec(spmv_plan_t p, const void* x, void* y, double alpha, dou
   return spmv_exec_events(p, x, y, alpha, beta, stream, nullptr, nullptr);
 }
 
+spmv_status_t spmv_plan_update_values(spmv_plan_t p, const void* values, hipStream_t stream) {
+  spmv_status_t st = check_plan(p);
+  if (st != SPMV_SUCCESS) return st;
+  if (p->values_copied)
+    return fail(SPMV_ERR_UNSUPPORTED,
+                "transposed, CSC and row-grouped plans keep values in their own layout");
+  if (p->nnz > 0 && !values) return fail(SPMV_ERR_INVALID_ARG, "values is NULL");
+  if (!aligned16(values)) return fail(SPMV_ERR_INVALID_ARG, "values must be 16-byte aligned");
+  p->values = values;
+  if (p->x_slabs) {
+    const hipError_t err =
+        launch_slab_emit(p->slab_rows, p->slab_m, p->row_ptr, p->col_idx, values,
+                         p->dtype == SPMV_F32 ? 4 : 8, p->M, p->N, p->nnz, stream);
+    if (err != hipSuccess) return hip_fail(err, "spmv_plan_update_values");
+  }
+  return SPMV_SUCCESS;
+}
+
 spmv_status_t spmv_destroy(spmv_plan_t p) {
   if (!p) return SPMV_SUCCESS;
   {
@@ -1300,7 +1469,7 @@ spmv_status_t spmv_destroy(spmv_plan_t p) {
   p->magic = 0;
   release_bin_streams(p);
   hipError_t err = hipFree(p->ws);
-  for (void* q : {p->owned_rg_meta, p->owned_rg_data}) {
+  for (void* q : {p->owned_rg_meta, p->owned_rg_data, p->owned_slab}) {
     if (!q) continue;
     const hipError_t e2 = hipFree(q);
     if (err == hipSuccess) err = e2;
@@ -1364,6 +1533,9 @@ spmv_status_t spmv_plan_info(spmv_plan_t p, spmv_plan_info_t* info) {
   info->tile_rows = p->n_tile_rows;
   info->tile_blocks = p->n_tile_rows > 0 ? p->tile_nb : 0;
   info->walk_partitions = p->n_tile_rows > 0 ? p->n_dispatch : (int32_t)p->P;
+  info->x_slabs = p->x_slabs;
+  info->slab_segments = p->x_slabs ? p->slab_m.n_seg : 0;
+  info->slab_bytes = p->x_slabs ? (int64_t)p->slab_bytes : 0;
   return SPMV_SUCCESS;
 }
 

@@ -72,7 +72,10 @@ enum StatSlot : int {
   kStatTileRows = kStatTileOk + 1,   // tile rows found (0: no tiles)
   kStatWalkParts = kStatTileRows + 1,  // partitions the walk kernel still runs, with tiles
   kStatTileEntries = kStatWalkParts + 1,  // nonzeros in the tile rows' interior runs
-  kStatCount = kStatTileEntries + 1
+  kStatSlabOk = kStatTileEntries + 1,     // 1: the plan builds x slabs (unless columns descend)
+  kStatSlabDescents = kStatSlabOk + 1,    // entries whose column is below the previous one's in their row
+  kStatSlabSegs = kStatSlabDescents + 1,  // (row, slab) segments with at least one entry
+  kStatCount = kStatSlabSegs + 1
 };
 
 // ---- column-blocked tiles of long rows (tile_kernels.hip) ------------------------
@@ -145,6 +148,8 @@ struct PlanCtl {
   int32_t reduce_req;   // 0 auto, 1 walk, 2 stream
   int32_t order_req;    // 0 auto, 1 partition order, 2 column order
   int32_t tiles_req;    // 0 auto, 1 off
+  int32_t slabs_req;    // 0 auto, 1 off, 2 on
+  int32_t slab_room;    // the workspace holds the x slabs' row tables
 };
 
 struct BinEdges {
@@ -217,6 +222,61 @@ hipError_t launch_window_spans(const PlanCtl& c, const int32_t* row_ptr, const i
                                int64_t* stats, hipStream_t s);
 // stats[kError] |= bits when *flag != 0
 hipError_t launch_fold_flag(const int32_t* flag, int64_t bits, int64_t* stats, hipStream_t s);
+
+// ---- x slabs: one column slab of x per XCD (slab_kernels.hip) -----------------------
+// A walk plan whose x is larger than one XCD's L2 gathers most x entries from
+// beyond that L2. With x slabs the plan keeps a copy A' of A whose entries are
+// ordered slab-major: slab s (columns [ceil(s N / 8), ceil((s + 1) N / 8)))
+// holds, row after row, the run of each row's entries in those columns -- a
+// segment, one row of the CSR matrix A' (M' segments, nnz entries). The walk
+// over A' hands each XCD a contiguous eighth of its partitions, so XCD s
+// gathers from slab s of x; a combine kernel then adds each row's segment
+// sums, in slab order, into y with alpha and beta. Requires columns sorted
+// within each row (checked while the tables are built; otherwise no slabs).
+constexpr int kSlabs = kXcds;                    // one column slab per XCD
+constexpr int kSlabTileRows = kBlock / kSlabs;   // rows per planning workgroup (8 lanes a row)
+
+// Tables filled before the plan's read-back (inside its one workspace). Every
+// launch does nothing unless stats[kStatSlabOk] is set.
+struct SlabRows {
+  int32_t* rptr;     // M + 1: segments of each row, then their exclusive prefix sum
+  uint8_t* mask;     // M: bit s set when the row has an entry in slab s
+  int32_t* tile_e;   // kSlabs x n_tiles, slab-major: entries of (slab, row tile), then prefix
+  int32_t* tile_g;   // kSlabs x n_tiles: segments of (slab, row tile), then prefix
+  void* scan_temp;   // scan_temp_bytes(slab_scan_max(M))
+  int64_t n_tiles;   // ceil(M / kSlabTileRows)
+};
+constexpr int64_t kScanMaxElems = int64_t(8192) * 4096;   // exclusive_scan_i32's limit
+inline int64_t slab_tiles(int64_t M) { return (M + kSlabTileRows - 1) / kSlabTileRows; }
+inline int64_t slab_scan_max(int64_t M) {
+  return M + 1 > kSlabs * slab_tiles(M) ? M + 1 : kSlabs * slab_tiles(M);
+}
+// Segment counts and masks per row, the (slab, tile) counts, their prefix
+// sums; stats[kStatSlabDescents] += descending column pairs within rows,
+// stats[kStatSlabSegs] = M'.
+hipError_t launch_slab_rows(const SlabRows& t, const int32_t* row_ptr, const int32_t* col_idx,
+                            int64_t M, int64_t N, int64_t* stats, hipStream_t s);
+
+// A' (after the read-back, in the plan's second allocation).
+struct SlabMatrix {
+  int32_t* seg_ptr;   // M' + 1: A' row offsets
+  int32_t* col;       // nnz
+  void* val;          // nnz of the plan's dtype
+  int32_t* rseg;      // M': the segments of row r, slab order, at [rptr[r], rptr[r + 1])
+  int64_t n_seg;      // M'
+};
+// Copies col_idx / values into A' and writes seg_ptr and rseg (also the
+// values refresh of spmv_plan_update_values).
+hipError_t launch_slab_emit(const SlabRows& t, const SlabMatrix& m, const int32_t* row_ptr,
+                            const int32_t* col_idx, const void* values, int vbytes, int64_t M,
+                            int64_t N, int64_t nnz, hipStream_t s);
+// A statistics block for A's merge-path split: all zero but the items per
+// lane and the partition count.
+hipError_t launch_slab_stats(int64_t* stats, int ipt, int64_t P, hipStream_t s);
+// y[r] = alpha * (sum over the segments of row r of yp[segment]) + beta * y[r]
+template <typename V>
+hipError_t launch_slab_combine(const int32_t* rptr, const int32_t* rseg, const V* yp, V* y,
+                               V alpha, V beta, int beta_nonzero, int64_t M, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>

@@ -43,7 +43,8 @@ def test_full_size_row_lengths_exact(name):
     w = synth.CONFIGS[name]()
     L = np.diff(w.row_ptr).astype(np.float32)
     m = DevMatrix(w.row_ptr, w.col_idx, np.ones(w.nnz, np.float32), w.M, w.N)
-    for variant in ("merge8", "merge8_walk", "binned"):
+    # None: the default plan (power-law: x slabs)
+    for variant in (None, "merge8", "merge8_walk", "binned"):
         log("lengths", name, variant)
         plan = m.plan(variant)
         y = run(plan, np.ones(w.N, np.float32), 1.0, 0.0)

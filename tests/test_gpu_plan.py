@@ -1,10 +1,12 @@
 """Planning contract and the binding's argument checks.
 
-* A plan is built with one device allocation and one host synchronisation
-  (the OpSparse page, Section 5.1: all metadata in one allocation, no
-  synchronisation mid-pipeline); the choices the device takes from the
-  counted rows (partition size, stream or walk, column dispatch order) are
-  the ones the five workloads are benchmarked with.
+* A plan is built with one device allocation for its metadata and one host
+  synchronisation (the OpSparse page, Section 5.1: all metadata in one
+  allocation, no synchronisation mid-pipeline); a plan that takes x slabs
+  makes one more allocation, for its slab-major copy of the matrix, and no
+  further synchronisation. The choices the device takes from the counted
+  rows (partition size, stream or walk, column dispatch order, tiles,
+  slabs) are the ones the five workloads are benchmarked with.
 * The Python binding rejects, before any launch, tensors too short or of the
   wrong type for the plan; the C ABI rejects x and y whose bytes overlap.
 * The measurement aids run, touch only their own outputs, and keep the sink.
@@ -19,13 +21,14 @@ from gpu_util import DevMatrix, dev, log
 
 pytestmark = pytest.mark.gpu
 
-# workload -> (items per wave, reduction, dispatch order) of the default plan
+# workload -> (items per wave, reduction, dispatch order, x slabs) of the
+# default plan
 EXPECTED = {
-    "tiny": (256, "stream", "partition"),
-    "laplacian": (256, "stream", "partition"),
-    "powerlaw": (256, "walk", "column"),
-    "bimodal": (1024, "walk", "partition"),   # its long rows go to tiles
-    "banded": (1024, "stream", "partition"),
+    "tiny": (256, "stream", "partition", 0),
+    "laplacian": (256, "stream", "partition", 0),
+    "powerlaw": (256, "walk", "column", 1),   # x of 16 MB: slabs
+    "bimodal": (1024, "walk", "partition", 0),   # its long rows go to tiles
+    "banded": (1024, "stream", "partition", 0),
 }
 
 
@@ -36,9 +39,9 @@ def test_one_allocation_one_sync(name):
     m = DevMatrix.of(w)
     plan = m.plan(None)
     info = plan.info
-    assert info["plan_allocs"] == 1 and info["plan_syncs"] == 1, info
-    assert (info["items_per_wave"], info["merge_reduce"], info["dispatch_order"]) == \
-        EXPECTED[name], info
+    assert info["plan_allocs"] == 1 + info["x_slabs"] and info["plan_syncs"] == 1, info
+    assert (info["items_per_wave"], info["merge_reduce"], info["dispatch_order"],
+            info["x_slabs"]) == EXPECTED[name], info
     assert info["n_partitions"] == -(-(w.M + w.nnz) // info["items_per_wave"])
     assert (info["tile_rows"] > 0) == (name == "bimodal"), info
     plan.destroy()

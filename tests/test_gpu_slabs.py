@@ -1,0 +1,234 @@
+"""x slabs: merge-path walk over a slab-major copy of A (one column slab of x
+per XCD), then the combine of each row's slab sums. Every row against the
+oracle, bitwise reproducibility, exact row lengths, the auto choice on a
+wide-x power-law matrix, the cases the slabs must survive (empty rows, rows
+in every slab, N smaller than the slab count, fp64, beta != 0), the plans
+that must decline them (columns not sorted within a row), the values
+refresh, and the other entry points over a slab plan (SpMM, other
+schedules)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DevMatrix, check, dev, log, run
+
+pytestmark = pytest.mark.gpu
+
+
+def _random(M, N, L, seed, dt=np.float32):
+    w = synth.random_csr(M, N, np.asarray(L), seed)
+    if dt != np.float32:
+        w = synth.Workload("random_f64", M, N, w.row_ptr, w.col_idx, w.values.astype(dt),
+                           w.x.astype(dt), None, 1.0, 0.0, seed)
+    return w
+
+
+def _mixed_lengths(M, N, seed, long_len):
+    rng = np.random.default_rng(seed)
+    L = rng.integers(0, 12, M)
+    L[rng.choice(M, M // 10, replace=False)] = 0
+    L[rng.choice(M, 12, replace=False)] = long_len   # rows over every slab
+    L[-1] = 0
+    return np.minimum(L, N)
+
+
+CASES = {
+    "powerlaw": lambda: synth.powerlaw(M=30_000, max_len=8_000),
+    "wide_x": lambda: _random(20_000, 3_000_000, _mixed_lengths(20_000, 3_000_000, 1, 4_000), 2),
+    "f64": lambda: _random(25_000, 400_000, _mixed_lengths(25_000, 400_000, 3, 9_000), 4,
+                           np.float64),
+    "narrow_N": lambda: _random(3_000, 5, np.random.default_rng(5).integers(0, 6, 3_000), 6),
+    "one_column": lambda: _random(2_000, 1, np.random.default_rng(7).integers(0, 2, 2_000), 8),
+    "last_row_long": lambda: _random(4_097, 70_001,
+                                     np.r_[np.random.default_rng(9).integers(1, 9, 4_096),
+                                           [50_001]], 10),
+}
+
+
+def _slab_plan(m, **kw):
+    return m.plan(None, strategy="merge", x_slabs="on", **kw)
+
+
+# cases whose long rows the long-row tiles would take (tiles win over slabs)
+NO_TILES = {"last_row_long"}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_slab_plans_match_the_oracle(case):
+    w = CASES[case]()
+    dt = w.values.dtype.type
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m, long_row_tiles="off") if case in NO_TILES else _slab_plan(m)
+    info = plan.info
+    assert info["x_slabs"] == 1 and info["slab_segments"] > 0, info
+    assert info["slab_segments"] <= w.nnz
+    assert info["plan_allocs"] == 2 and info["plan_syncs"] == 1, info
+    y0 = synth.uniform(w.M, 11, synth.S_Y, dt)
+    for alpha, beta in ((1.0, 0.0), (-1.5, 0.5)):
+        log("slabs", case, info["slab_segments"], alpha, beta)
+        yo = y0 if beta != 0 else None
+        y = run(plan, w.x, alpha, beta, yo, dt)
+        check(y, w.row_ptr, w.col_idx, w.values, w.x, alpha, beta, yo, "slabs %s" % case)
+        y2 = run(plan, w.x, alpha, beta, yo, dt)
+        assert np.array_equal(y.view(np.uint8), y2.view(np.uint8)), "not reproducible"
+    plan.destroy()
+
+
+def test_tiles_take_precedence():
+    """A plan whose long rows the column-blocked tiles take keeps no slabs,
+    even when asked for them."""
+    w = CASES["last_row_long"]()
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m, merge_reduce="walk")
+    info = plan.info
+    assert info["tile_rows"] > 0 and info["x_slabs"] == 0 and info["plan_allocs"] == 1, info
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "tiles over slabs")
+    plan.destroy()
+
+
+def test_slab_segment_count():
+    """A row has one segment per slab its columns reach: the count the plan
+    reports equals the count from the columns (slab of column c: 8c // N)."""
+    w = CASES["wide_x"]()
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m)
+    slab = (w.col_idx.astype(np.int64) * 8) // w.N
+    row = np.repeat(np.arange(w.M), np.diff(w.row_ptr))
+    expect = len(np.unique(row * 8 + slab))
+    assert plan.info["slab_segments"] == expect
+    plan.destroy()
+
+
+def test_slab_row_lengths_exact():
+    w = CASES["wide_x"]()
+    m = DevMatrix(w.row_ptr, w.col_idx, np.ones(w.nnz, np.float32), w.M, w.N)
+    plan = _slab_plan(m)
+    assert plan.info["x_slabs"] == 1
+    y = run(plan, np.ones(w.N, np.float32), 1.0, 0.0)
+    assert np.array_equal(y, np.diff(w.row_ptr).astype(np.float32))
+    plan.destroy()
+
+
+def test_auto_takes_slabs_on_wide_powerlaw():
+    """A power-law matrix whose x (6 MB) is wider than one XCD's L2: the
+    automatic plan walks at T = 256 and takes slabs; off when asked."""
+    w = synth.powerlaw(M=1_500_000, max_len=20_000)
+    m = DevMatrix.of(w)
+    plan = m.plan(None)
+    info = plan.info
+    log("auto slabs", info["x_slabs"], info["items_per_wave"], info["merge_reduce"],
+        info["slab_segments"], info["plan_allocs"], info["plan_syncs"])
+    assert info["strategy"] == "merge" and info["merge_reduce"] == "walk", info
+    assert info["x_slabs"] == 1 and info["plan_allocs"] == 2 and info["plan_syncs"] == 1, info
+    y0 = w.y0
+    y = run(plan, w.x, w.alpha, w.beta, y0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, y0, "auto slabs")
+    off = m.plan(None, x_slabs="off")
+    assert off.info["x_slabs"] == 0 and off.info["plan_allocs"] == 1
+    y = run(off, w.x, w.alpha, w.beta, y0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, y0, "slabs off")
+    off.destroy()
+    plan.destroy()
+
+
+def test_unsorted_columns_decline_slabs():
+    w = CASES["wide_x"]()
+    rng = np.random.default_rng(12)
+    col = w.col_idx.copy()
+    for r in np.nonzero(np.diff(w.row_ptr) > 100)[0][:5]:
+        a, b = w.row_ptr[r], w.row_ptr[r + 1]
+        col[a:b] = rng.permutation(col[a:b])
+    m = DevMatrix(w.row_ptr, col, w.values, w.M, w.N)
+    plan = _slab_plan(m)
+    info = plan.info
+    assert info["x_slabs"] == 0 and info["plan_allocs"] == 1, info
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, col, w.values, w.x, 1.0, 0.0, None, "unsorted")
+    plan.destroy()
+
+
+def test_repeated_columns_keep_slabs():
+    """Equal neighbouring columns are sorted (non-decreasing): slabs stay on
+    and the repeats add."""
+    M, N = 2_000, 100_000
+    rng = np.random.default_rng(13)
+    L = rng.integers(1, 10, M)
+    rp = synth.row_ptr_from_lengths(L.astype(np.int32))
+    col = np.sort(rng.integers(0, N, int(rp[-1])).astype(np.int32))   # placeholder order
+    for r in range(M):
+        a, b = rp[r], rp[r + 1]
+        c = np.sort(rng.integers(0, N, b - a))
+        if b - a > 1:
+            c[1] = c[0]
+        col[a:b] = c
+    val = rng.uniform(-1, 1, int(rp[-1])).astype(np.float32)
+    x = rng.uniform(-1, 1, N).astype(np.float32)
+    m = DevMatrix(rp, col, val, M, N)
+    plan = _slab_plan(m)
+    assert plan.info["x_slabs"] == 1
+    y = run(plan, x, 1.0, 0.0)
+    check(y, rp, col, val, x, 1.0, 0.0, None, "repeats")
+    plan.destroy()
+
+
+def test_update_values():
+    """The slab copy holds the values of plan time until
+    spmv_plan_update_values; then the new ones, bitwise as a fresh plan."""
+    w = CASES["powerlaw"]()
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m)
+    assert plan.info["x_slabs"] == 1
+    v2 = synth.uniform(w.nnz, 14, synth.S_VAL, np.float32)
+    m.val.copy_(dev(v2))
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "before the refresh")
+    plan.update_values(m.val)
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, w.col_idx, v2, w.x, 1.0, 0.0, None, "after the refresh")
+    fresh = _slab_plan(m)
+    y2 = run(fresh, w.x, 1.0, 0.0)
+    assert np.array_equal(y.view(np.uint8), y2.view(np.uint8))
+    # another array, on a plan without slabs too
+    v3 = dev(synth.uniform(w.nnz, 15, synth.S_VAL, np.float32))
+    for p in (plan, m.plan(None, strategy="merge", x_slabs="off")):
+        p.update_values(v3)
+        y = run(p, w.x, 1.0, 0.0)
+        check(y, w.row_ptr, w.col_idx, v3.cpu().numpy(), w.x, 1.0, 0.0, None, "other array")
+        p.destroy()
+    fresh.destroy()
+
+
+def test_update_values_refused_for_copies_in_other_layouts():
+    w = CASES["narrow_N"]()
+    m = DevMatrix.of(w)
+    t = __import__("load_balanced_csr_amd").Plan.transpose(m.rp, m.col, m.val, (w.M, w.N))
+    with pytest.raises(Exception):
+        t.update_values(m.val)
+    t.destroy()
+
+
+def test_other_entry_points_over_a_slab_plan():
+    """SpMM and the other schedules run on the plan's own arrays: right
+    whether or not the plan took slabs."""
+    w = CASES["powerlaw"]()
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m)
+    assert plan.info["x_slabs"] == 1
+    rng = np.random.default_rng(16)
+    k = 4
+    X = rng.uniform(-1, 1, (w.N, k)).astype(np.float32)
+    Y = torch.full((w.M, k), float("nan"), device="cuda")
+    plan.exec_multi(dev(X), Y, 1.0, 0.0)
+    torch.cuda.synchronize()
+    ref, scale = oracle.spmm(w.row_ptr, w.col_idx, w.values, X, 1.0, 0.0, None)
+    ok, worst, idx = oracle.within_tolerance(Y.cpu().numpy(), ref, scale, 1.0, 0.0, None,
+                                             row_ptr=w.row_ptr)
+    assert ok, ("spmm over slabs", idx, worst)
+    for s in ("binned", "group", "merge"):
+        plan.set_strategy(s)
+        y = run(plan, w.x, 1.0, 0.0)
+        check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "slab plan as " + s)
+    plan.destroy()
