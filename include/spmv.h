@@ -200,9 +200,15 @@ typedef struct spmv_plan_options {
                                  (their partitions mostly hold row ends); on:
                                  every plan. Either way only MERGE plans that
                                  keep no long-row tiles (those win where both
-                                 apply). Needs columns sorted
-                                 within each row (checked; else no slabs) and
-                                 costs a second allocation the size of A. The
+                                 apply). Each row's entries are
+                                 cut into slab runs by binary search over its
+                                 columns: results are right in any column
+                                 order, but the x locality needs the columns
+                                 sorted within rows, so auto keeps no slabs
+                                 when a run's middle entry lies outside its
+                                 slab or below the entry before it. Costs a
+                                 second allocation
+                                 the size of A. The
                                  copy holds A's values as they were at plan
                                  time: call spmv_plan_update_values after
                                  changing them (spmv_plan_info.x_slabs tells

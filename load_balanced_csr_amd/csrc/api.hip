@@ -392,7 +392,7 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
     a.stream = 0;
     err = launch_merge<V>(a, p->slab_ipt, stream, ev0, ev1);
     if (err == hipSuccess)
-      err = launch_slab_combine<V>(p->slab_rows.rptr, p->slab_m.rseg, static_cast<const V*>(p->slab_y),
+      err = launch_slab_combine<V>(p->slab_rows, static_cast<const V*>(p->slab_y),
                                    static_cast<V*>(y), (V)alpha, (V)beta, beta != 0.0, p->M,
                                    stream);
   } else if (p->strategy == SPMV_STRATEGY_MERGE) {
@@ -689,12 +689,14 @@ struct PlanSource {
 // 512 (fp64): its gathers stay in L2, so the walk favours fewer, longer
 // waves (power-law, fp32: 0.217 / 0.186 / 0.170 ms at T = 256 / 512 / 1024).
 // A failed allocation leaves the plan without slabs.
-spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, hipStream_t stream) {
+spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, int64_t n_chunks, hipStream_t stream) {
   const int64_t nnz = p->nnz;
   const size_t vs = p->dtype == SPMV_F32 ? 4 : 8;
   const int ipt = vs == 4 ? 16 : 8;
   const int64_t T = (int64_t)kWave * ipt;
-  if (n_seg <= 0 || n_seg > nnz || n_seg + nnz > kMaxUnits) return SPMV_SUCCESS;
+  if (n_seg <= 0 || n_seg > nnz || n_seg + nnz > kMaxUnits || n_chunks <= 0 ||
+      n_chunks > 0x7fffffffll)
+    return SPMV_SUCCESS;
   const int64_t P = (n_seg + nnz + T - 1) / T;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
@@ -702,7 +704,6 @@ spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, hipStream_t stream) {
   const size_t o_segp = take(sizeof(int32_t) * (n_seg + 1));
   const size_t o_col = take(sizeof(int32_t) * nnz);
   const size_t o_val = take(vs * nnz);
-  const size_t o_rseg = take(sizeof(int32_t) * n_seg);
   const size_t o_y = take(vs * n_seg);
   const size_t o_srow = take(sizeof(int32_t) * (P + 1));
   const size_t o_snz = take(sizeof(int32_t) * (P + 1));
@@ -723,8 +724,8 @@ spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, hipStream_t stream) {
   p->slab_m.seg_ptr = reinterpret_cast<int32_t*>(b + o_segp);
   p->slab_m.col = reinterpret_cast<int32_t*>(b + o_col);
   p->slab_m.val = b + o_val;
-  p->slab_m.rseg = reinterpret_cast<int32_t*>(b + o_rseg);
   p->slab_m.n_seg = n_seg;
+  p->slab_m.n_chunks = n_chunks;
   p->slab_y = b + o_y;
   p->slab_split_row = reinterpret_cast<int32_t*>(b + o_srow);
   p->slab_split_nz = reinterpret_cast<int32_t*>(b + o_snz);
@@ -864,10 +865,10 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   const size_t o_tmstart = take(sizeof(int32_t) * tile_p);
   // x slabs' row tables
   const int64_t slab_nt = ctl.slab_room ? slab_tiles(M) : 0;
-  const size_t o_srptr = ctl.slab_room ? take(sizeof(int32_t) * (M + 1)) : 0;
   const size_t o_smask = ctl.slab_room ? take((size_t)M) : 0;
-  const size_t o_stile_e = ctl.slab_room ? take(sizeof(int32_t) * kSlabs * slab_nt) : 0;
-  const size_t o_stile_g = ctl.slab_room ? take(sizeof(int32_t) * kSlabs * slab_nt) : 0;
+  const size_t o_stile_e = ctl.slab_room ? take(sizeof(int32_t) * (kSlabs * slab_nt + 1)) : 0;
+  const size_t o_stile_g = ctl.slab_room ? take(sizeof(int32_t) * (kSlabs * slab_nt + 1)) : 0;
+  const size_t o_stile_c = ctl.slab_room ? take(sizeof(int32_t) * (slab_nt + 1)) : 0;
   const size_t o_sscan = ctl.slab_room ? take(scan_temp_bytes(slab_scan_max(M))) : 0;
   const size_t o_rowptr = src.coo ? take(sizeof(int32_t) * (M + 1)) : 0;
   const size_t o_extra = src.extra_bytes ? take(src.extra_bytes) : 0;
@@ -919,10 +920,10 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   p->tile_partial = base + o_tpart;
   p->tile_nb = tp.nb;
   if (ctl.slab_room) {
-    p->slab_rows.rptr = reinterpret_cast<int32_t*>(base + o_srptr);
     p->slab_rows.mask = reinterpret_cast<uint8_t*>(base + o_smask);
     p->slab_rows.tile_e = reinterpret_cast<int32_t*>(base + o_stile_e);
     p->slab_rows.tile_g = reinterpret_cast<int32_t*>(base + o_stile_g);
+    p->slab_rows.tile_c = reinterpret_cast<int32_t*>(base + o_stile_c);
     p->slab_rows.scan_temp = base + o_sscan;
     p->slab_rows.n_tiles = slab_nt;
   }
@@ -991,8 +992,8 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
     return bail(hip_fail(err, "plan: long-row tiles"));
   // x slabs' row tables (when stage 3 takes them)
   if ((err = launch_plan_choose(ctl, p->stats, 3, stream)) != hipSuccess ||
-      (ctl.slab_room && (err = launch_slab_rows(p->slab_rows, row_ptr, p->col_idx, M, N, p->stats,
-                                                stream)) != hipSuccess))
+      (ctl.slab_room && (err = launch_slab_rows(p->slab_rows, row_ptr, p->col_idx, M, N, nnz,
+                                                p->stats, stream)) != hipSuccess))
     return bail(hip_fail(err, "plan: x slab tables"));
 
   // ---- the one read-back and synchronisation -----------------------------------------
@@ -1079,11 +1080,12 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   p->group_waves = 4;
   p->group_rows = default_group_rows(p, 4);
   p->strategy = options && options->strategy ? options->strategy : choose_strategy(p);
-  // x slabs: taken on the device, kept when the columns are sorted within
-  // their rows and the plan runs merge-path
-  if (ctl.slab_room && host_stats[kStatSlabOk] && host_stats[kStatSlabDescents] == 0 &&
+  // x slabs: taken on the device; kept when the plan runs merge-path and,
+  // unless asked for, when every slab run's end columns lie in its slab
+  if (ctl.slab_room && host_stats[kStatSlabOk] &&
+      (ctl.slabs_req == 2 || host_stats[kStatSlabStray] == 0) &&
       p->strategy == SPMV_STRATEGY_MERGE) {
-    st = build_slabs(p, host_stats[kStatSlabSegs], stream);
+    st = build_slabs(p, host_stats[kStatSlabSegs], host_stats[kStatSlabChunks], stream);
     if (st != SPMV_SUCCESS) return bail(st);
   }
   if (env_int("SPMV_LOG", 0))

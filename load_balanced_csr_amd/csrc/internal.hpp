@@ -72,10 +72,11 @@ enum StatSlot : int {
   kStatTileRows = kStatTileOk + 1,   // tile rows found (0: no tiles)
   kStatWalkParts = kStatTileRows + 1,  // partitions the walk kernel still runs, with tiles
   kStatTileEntries = kStatWalkParts + 1,  // nonzeros in the tile rows' interior runs
-  kStatSlabOk = kStatTileEntries + 1,     // 1: the plan builds x slabs (unless columns descend)
-  kStatSlabDescents = kStatSlabOk + 1,    // entries whose column is below the previous one's in their row
-  kStatSlabSegs = kStatSlabDescents + 1,  // (row, slab) segments with at least one entry
-  kStatCount = kStatSlabSegs + 1
+  kStatSlabOk = kStatTileEntries + 1,     // 1: the plan builds x slabs (auto: unless runs stray)
+  kStatSlabStray = kStatSlabOk + 1,       // slab runs whose middle entry strays (rows not sorted)
+  kStatSlabSegs = kStatSlabStray + 1,     // (row, slab) segments with at least one entry
+  kStatSlabChunks = kStatSlabSegs + 1,    // workgroups of the copy into the slab-major order
+  kStatCount = kStatSlabChunks + 1
 };
 
 // ---- column-blocked tiles of long rows (tile_kernels.hip) ------------------------
@@ -238,45 +239,45 @@ constexpr int kSlabTileRows = kBlock / kSlabs;   // rows per planning workgroup 
 
 // Tables filled before the plan's read-back (inside its one workspace). Every
 // launch does nothing unless stats[kStatSlabOk] is set.
+constexpr int kSlabChunk = 4096;   // entries one workgroup copies into A'
 struct SlabRows {
-  int32_t* rptr;     // M + 1: segments of each row, then their exclusive prefix sum
   uint8_t* mask;     // M: bit s set when the row has an entry in slab s
-  int32_t* tile_e;   // kSlabs x n_tiles, slab-major: entries of (slab, row tile), then prefix
-  int32_t* tile_g;   // kSlabs x n_tiles: segments of (slab, row tile), then prefix
+  int32_t* tile_e;   // kSlabs x n_tiles + 1, slab-major: entries of (slab, row tile), then prefix
+  int32_t* tile_g;   // kSlabs x n_tiles + 1: segments of (slab, row tile), then prefix
+  int32_t* tile_c;   // n_tiles + 1: copy chunks of each tile, then prefix
   void* scan_temp;   // scan_temp_bytes(slab_scan_max(M))
   int64_t n_tiles;   // ceil(M / kSlabTileRows)
 };
 constexpr int64_t kScanMaxElems = int64_t(8192) * 4096;   // exclusive_scan_i32's limit
 inline int64_t slab_tiles(int64_t M) { return (M + kSlabTileRows - 1) / kSlabTileRows; }
-inline int64_t slab_scan_max(int64_t M) {
-  return M + 1 > kSlabs * slab_tiles(M) ? M + 1 : kSlabs * slab_tiles(M);
-}
-// Segment counts and masks per row, the (slab, tile) counts, their prefix
-// sums; stats[kStatSlabDescents] += descending column pairs within rows,
-// stats[kStatSlabSegs] = M'.
+inline int64_t slab_scan_max(int64_t M) { return kSlabs * slab_tiles(M) + 1; }
+// Slab masks of the rows, the (slab, tile) counts and the tiles' copy
+// chunks, their prefix sums; runs whose middle entry strays from the slab
+// into stats[kStatSlabStray]; stats[kStatSlabSegs] = M', [kStatSlabChunks].
 hipError_t launch_slab_rows(const SlabRows& t, const int32_t* row_ptr, const int32_t* col_idx,
-                            int64_t M, int64_t N, int64_t* stats, hipStream_t s);
+                            int64_t M, int64_t N, int64_t nnz, int64_t* stats, hipStream_t s);
 
 // A' (after the read-back, in the plan's second allocation).
 struct SlabMatrix {
   int32_t* seg_ptr;   // M' + 1: A' row offsets
   int32_t* col;       // nnz
   void* val;          // nnz of the plan's dtype
-  int32_t* rseg;      // M': the segments of row r, slab order, at [rptr[r], rptr[r + 1])
   int64_t n_seg;      // M'
+  int64_t n_chunks;   // workgroups of the copy
 };
-// Copies col_idx / values into A' and writes seg_ptr and rseg (also the
-// values refresh of spmv_plan_update_values).
+// Copies col_idx / values into A' and writes seg_ptr (also the values
+// refresh of spmv_plan_update_values).
 hipError_t launch_slab_emit(const SlabRows& t, const SlabMatrix& m, const int32_t* row_ptr,
                             const int32_t* col_idx, const void* values, int vbytes, int64_t M,
                             int64_t N, int64_t nnz, hipStream_t s);
 // A statistics block for A's merge-path split: all zero but the items per
 // lane and the partition count.
 hipError_t launch_slab_stats(int64_t* stats, int ipt, int64_t P, hipStream_t s);
-// y[r] = alpha * (sum over the segments of row r of yp[segment]) + beta * y[r]
+// y[r] = alpha * (sum over the slabs of row r of yp[segment]) + beta * y[r];
+// a segment's id follows from the row's mask and the tile prefix sums.
 template <typename V>
-hipError_t launch_slab_combine(const int32_t* rptr, const int32_t* rseg, const V* yp, V* y,
-                               V alpha, V beta, int beta_nonzero, int64_t M, hipStream_t s);
+hipError_t launch_slab_combine(const SlabRows& t, const V* yp, V* y, V alpha, V beta,
+                               int beta_nonzero, int64_t M, hipStream_t s);
 
 // ---- merge-path exec ----------------------------------------------------------
 template <typename V>

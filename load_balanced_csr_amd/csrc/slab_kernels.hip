@@ -15,16 +15,24 @@
 // runs over it unchanged and deals its partitions to the XCDs in contiguous
 // eighths (workgroup b runs on XCD b mod 8), so XCD s gathers only from slab
 // s, an eighth of x. A combine kernel then adds the segment sums of every
-// row, in slab order, and applies alpha and beta; every sum is taken in a
+// row over its slabs and applies alpha and beta; every sum is taken in a
 // fixed order, so the result is bitwise reproducible for the plan.
 //
-// Planning (before the plan's one read-back): per row, eight lanes find the
-// row's slab bounds by binary search over its columns (which must be sorted
-// within the row; descending pairs are counted and, if any, the plan keeps
-// no slabs), and each workgroup of 32 rows counts entries and segments per
-// slab. Prefix sums of those counts give every segment its id and its first
-// position in A'. After the read-back (M' known), the copy is written by
-// one workgroup per 32 rows.
+// Tables: rows are taken in tiles of 32, eight lanes a row, lane s for slab
+// s. Lane s finds the row's first entry in slab s by binary search over the
+// row's columns (which assumes them sorted within the row); the bounds are
+// made non-decreasing across the lanes, so the runs partition the row and
+// every entry is summed once whatever the columns' order -- only the x
+// locality depends on it. Runs whose middle entry lies outside their slab
+// or below its predecessor are counted, and the automatic choice keeps no
+// slabs if there are any. Per tile and slab the entries and segments are counted,
+// slab-major, and their prefix sums give every run its first position in A'
+// and every segment its id: segment (row r, slab s) is the tile's first
+// slab-s id plus the rows before r in the tile with an entry in slab s (the
+// rows' slab masks, one byte each). The combine finds the segments the same
+// way, so it needs no per-segment table. The copy into A' runs in chunks of
+// at most kSlabChunk entries of one tile, so a tile holding a long row is
+// shared out.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -58,16 +66,24 @@ struct SlabLane {
   uint32_t mask;
 };
 
-// Every lane of the wave must call this (shuffle and ballot); rows r >= M
-// read as empty at row_ptr[M].
+// Every lane of the wave must call this (shuffles and ballot); rows r >= M
+// read as empty at row_ptr[M]. The bounds are made non-decreasing across
+// the lanes (a running maximum), so [b, bn) partition [a, e) whatever the
+// columns' order.
 __device__ __forceinline__ SlabLane slab_lane(const int32_t* __restrict__ row_ptr,
                                               const int32_t* __restrict__ col, int64_t M,
                                               int64_t N, int64_t r, int s) {
   SlabLane l;
   l.a = row_ptr[r < M ? r : M];
   l.e = r < M ? row_ptr[r + 1] : l.a;
-  l.b = s == 0 ? l.a : first_col_at_least(col, l.a, l.e, slab_col0(s, N));
-  const int32_t up = __shfl_down(l.b, 1, kSlabs);
+  int32_t b = s == 0 ? l.a : first_col_at_least(col, l.a, l.e, slab_col0(s, N));
+#pragma unroll
+  for (int o = 1; o < kSlabs; o <<= 1) {
+    const int32_t lower = __shfl_up(b, o, kSlabs);
+    b = s >= o ? max(b, lower) : b;
+  }
+  l.b = b;
+  const int32_t up = __shfl_down(b, 1, kSlabs);
   l.bn = s == kSlabs - 1 ? l.e : up;
   const uint64_t ne = __ballot(l.bn > l.b);
   l.mask = (uint32_t)(ne >> (lane_id() & ~(kSlabs - 1))) & 0xffu;
@@ -76,37 +92,56 @@ __device__ __forceinline__ SlabLane slab_lane(const int32_t* __restrict__ row_pt
 
 __global__ __launch_bounds__(kBlock) void slab_rows_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int64_t M, int64_t N,
-    int32_t* __restrict__ rptr, uint8_t* __restrict__ mask, int32_t* __restrict__ tile_e,
-    int32_t* __restrict__ tile_g, int64_t n_tiles, int64_t* __restrict__ stats) {
+    uint8_t* __restrict__ mask, int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_g,
+    int32_t* __restrict__ tile_c, int64_t n_tiles, int64_t* __restrict__ stats) {
   if (stats[kStatSlabOk] == 0) return;   // workgroup-uniform
   __shared__ int s_e[kWavesPerBlock][kSlabs], s_g[kWavesPerBlock][kSlabs];
+  __shared__ int s_stray[kWavesPerBlock];
   const int s = threadIdx.x & (kSlabs - 1);
   const int64_t t = blockIdx.x;
   const int64_t r = t * kSlabTileRows + (threadIdx.x >> 3);
   const SlabLane l = slab_lane(row_ptr, col, M, N, r, s);
-  // descending neighbours inside the row (the bounds above assume none)
-  int desc = 0;
-  for (int64_t k = (int64_t)l.a + 1 + s; k < l.e; k += kSlabs) desc += col[k] < col[k - 1];
-  if (r < M && s == 0) {
-    rptr[r] = __popc(l.mask);
-    mask[r] = (uint8_t)l.mask;
+  // a run whose middle entry lies outside its slab or below its
+  // predecessor (a row whose columns are not sorted; the binary search
+  // alone keeps each run's first and last column inside the slab)
+  int stray = 0;
+  if (l.bn > l.b) {
+    const int32_t mid = l.b + ((l.bn - l.b) >> 1);
+    const int64_t c = col[mid];
+    stray = c < slab_col0(s, N) || (s + 1 < kSlabs && c >= slab_col0(s + 1, N)) ||
+            (mid > l.b && col[mid - 1] > c);
   }
-  if (t == 0 && threadIdx.x == 0) rptr[M] = 0;
+  if (r < M && s == 0) mask[r] = (uint8_t)l.mask;
+  if (t == 0 && threadIdx.x == 0) {
+    tile_e[kSlabs * n_tiles] = 0;
+    tile_g[kSlabs * n_tiles] = 0;
+    tile_c[n_tiles] = 0;
+  }
+  if (threadIdx.x == 0) {
+    const int64_t re = (t + 1) * kSlabTileRows < M ? (t + 1) * kSlabTileRows : M;
+    const int64_t n = (int64_t)row_ptr[re] - row_ptr[t * kSlabTileRows];
+    tile_c[t] = n > kSlabChunk ? (int32_t)((n + kSlabChunk - 1) / kSlabChunk) : 1;
+  }
   // entries and segments per slab over the wave's 8 rows (lanes s, s + 8, ...)
   int e = l.bn - l.b, g = l.bn > l.b ? 1 : 0;
   for (int o = kSlabs; o < kWave; o <<= 1) {
     e += __shfl_xor(e, o);
     g += __shfl_xor(g, o);
   }
-  for (int o = 1; o < kWave; o <<= 1) desc += __shfl_xor(desc, o);
   const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int wave_stray = __popcll(__ballot(stray != 0));
   if (lane < kSlabs) {
     s_e[wave][lane] = e;
     s_g[wave][lane] = g;
   }
-  if (lane == 0 && desc > 0)
-    atomicAdd((unsigned long long*)&stats[kStatSlabDescents], (unsigned long long)desc);
+  if (lane == 0) s_stray[wave] = wave_stray;
   __syncthreads();
+  // one atomic per workgroup, and only where a run strays
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) n += s_stray[w];
+    if (n > 0) atomicAdd((unsigned long long*)&stats[kStatSlabStray], (unsigned long long)n);
+  }
   if (threadIdx.x < kSlabs) {
     int te = 0, tg = 0;
     for (int w = 0; w < kWavesPerBlock; ++w) {
@@ -118,36 +153,49 @@ __global__ __launch_bounds__(kBlock) void slab_rows_kernel(
   }
 }
 
-__global__ __launch_bounds__(64) void slab_total_kernel(const int32_t* rptr, int64_t M,
+__global__ __launch_bounds__(64) void slab_total_kernel(const int32_t* tile_g,
+                                                        const int32_t* tile_c, int64_t n_tiles,
                                                         int64_t* stats) {
-  if (threadIdx.x == 0 && stats[kStatSlabOk] != 0) stats[kStatSlabSegs] = rptr[M];
+  if (threadIdx.x == 0 && stats[kStatSlabOk] != 0) {
+    stats[kStatSlabSegs] = tile_g[kSlabs * n_tiles];
+    stats[kStatSlabChunks] = tile_c[n_tiles];
+  }
 }
 
-// One workgroup per 32 rows: the rows' slab bounds (as in slab_rows_kernel),
-// each (row, slab) run's first position in A' and segment id from the
-// prefix sums, then the copy of the tile's entries, 256 at a time, each to
-// its run's position plus its offset in the run.
+// One workgroup per copy chunk (part i of tile t): the tile's rows' slab
+// bounds, each run's first position in A' and, in part 0, each segment's
+// first position into seg_ptr; then the chunk's entries, each to its run's
+// position plus its offset in the run. Positions and ids outside A' (only
+// if col_idx changed since the plan was made) are skipped.
 template <typename V>
 __global__ __launch_bounds__(kBlock) void slab_emit_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
     const V* __restrict__ val, int64_t M, int64_t N, int64_t nnz,
-    const int32_t* __restrict__ rptr, const int32_t* __restrict__ tile_e,
-    const int32_t* __restrict__ tile_g, int64_t n_tiles, int32_t* __restrict__ seg_ptr,
-    int32_t* __restrict__ col2, V* __restrict__ val2, int32_t* __restrict__ rseg,
-    int64_t n_seg) {
+    const int32_t* __restrict__ tile_e, const int32_t* __restrict__ tile_g,
+    const int32_t* __restrict__ tile_c, int64_t n_tiles, int32_t* __restrict__ seg_ptr,
+    int32_t* __restrict__ col2, V* __restrict__ val2, int64_t n_seg) {
   __shared__ int32_t s_rs[kSlabTileRows + 1];          // row starts
   __shared__ int32_t s_b[kSlabTileRows][kSlabs + 1];   // slab bounds of each row
   __shared__ int32_t s_len[kSlabs][kSlabTileRows];     // run lengths
   __shared__ int32_t s_pos[kSlabTileRows][kSlabs];     // first A' position of each run
+  // the tile whose chunks hold this workgroup: the last t with tile_c[t] <= b
+  const int64_t blk = blockIdx.x;
+  int64_t lo_t = 0, hi_t = n_tiles - 1;
+  while (lo_t < hi_t) {
+    const int64_t mid = (lo_t + hi_t + 1) >> 1;
+    if (tile_c[mid] <= blk) lo_t = mid;
+    else hi_t = mid - 1;
+  }
+  const int64_t t = lo_t, part = blk - tile_c[t];
   const int s = threadIdx.x & (kSlabs - 1);
   const int j = threadIdx.x >> 3;
-  const int64_t t = blockIdx.x;
   const int64_t r = t * kSlabTileRows + j;
   const SlabLane l = slab_lane(row_ptr, col, M, N, r, s);
   s_b[j][s] = l.b;
   if (s == kSlabs - 1) s_b[j][kSlabs] = l.e;
   if (s == 0) s_rs[j] = l.a;
-  if (threadIdx.x == 0) s_rs[kSlabTileRows] = row_ptr[(t + 1) * kSlabTileRows < M ? (t + 1) * kSlabTileRows : M];
+  if (threadIdx.x == 0)
+    s_rs[kSlabTileRows] = row_ptr[(t + 1) * kSlabTileRows < M ? (t + 1) * kSlabTileRows : M];
   s_len[s][j] = l.bn - l.b;
   __syncthreads();
   int32_t pos = tile_e[s * n_tiles + t], id = tile_g[s * n_tiles + t];
@@ -157,13 +205,11 @@ __global__ __launch_bounds__(kBlock) void slab_emit_kernel(
     id += n > 0 ? 1 : 0;
   }
   s_pos[j][s] = pos;
-  if (r < M && l.bn > l.b) {
-    seg_ptr[id] = pos;
-    rseg[rptr[r] + __popc(l.mask & ((1u << s) - 1u))] = id;
-  }
-  if (t == 0 && threadIdx.x == 0) seg_ptr[n_seg] = (int32_t)nnz;
+  if (part == 0 && r < M && l.bn > l.b && id < n_seg) seg_ptr[id] = pos;
+  if (blk == 0 && threadIdx.x == 0) seg_ptr[n_seg] = (int32_t)nnz;
   __syncthreads();
-  const int64_t e0 = s_rs[0], e1 = s_rs[kSlabTileRows];
+  const int64_t e0 = s_rs[0] + part * kSlabChunk;
+  const int64_t e1 = min((int64_t)s_rs[kSlabTileRows], e0 + kSlabChunk);
   for (int64_t k = e0 + threadIdx.x; k < e1; k += kBlock) {
     // the last row starting at or before k (rows of the tile past M start
     // at nnz > k and are never chosen), then the last slab bound <= k
@@ -177,8 +223,10 @@ __global__ __launch_bounds__(kBlock) void slab_emit_kernel(
 #pragma unroll
     for (int u = 1; u < kSlabs; ++u) q = s_b[lo][u] <= k ? u : q;
     const int64_t p2 = (int64_t)s_pos[lo][q] + (k - s_b[lo][q]);
-    col2[p2] = col[k];
-    val2[p2] = val[k];
+    if ((uint64_t)p2 < (uint64_t)nnz) {
+      col2[p2] = col[k];
+      val2[p2] = val[k];
+    }
   }
 }
 
@@ -191,27 +239,64 @@ __global__ __launch_bounds__(64) void slab_stats_kernel(int64_t* stats, int ipt,
   }
 }
 
-// One thread per row: its at most kSlabs segment sums, all requested before
-// the first is added, added in slab order.
+// Rows per thread of the combine: a wave takes 4 x 64 consecutive rows, 64
+// at a time, so more of its loads are in flight together.
+constexpr int kCombineSteps = 4;
+
+// A wave takes kCombineSteps runs of 64 rows (two tiles of 32 each), one
+// row per lane per run. The segment id of (row, slab s) is the tile's first
+// slab-s id plus the lanes of the tile before this one whose rows have an
+// entry in slab s (a ballot). First every lane's masks and old y and, in one
+// load, the first ids of the wave's 8 tiles x 8 slabs; then every segment
+// sum of the lane's rows; each row's sums are added in slab order.
 template <typename V>
 __global__ __launch_bounds__(kBlock) void slab_combine_kernel(
-    const int32_t* __restrict__ rptr, const int32_t* __restrict__ rseg, const V* __restrict__ yp,
-    V* __restrict__ y, V alpha, V beta, int beta_nonzero, int32_t M) {
-  const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (r >= M) return;
-  const int32_t t0 = rptr[r], n = rptr[r + 1] - t0;
-  int32_t sg[kSlabs];
+    const uint8_t* __restrict__ mask, const int32_t* __restrict__ tile_g, int64_t n_tiles,
+    const V* __restrict__ yp, V* __restrict__ y, V alpha, V beta, int beta_nonzero, int32_t M) {
+  constexpr int K = kCombineSteps;
+  constexpr int TPW = K * kWave / kSlabTileRows;   // tiles of a wave
+  static_assert(kWave == 2 * kSlabTileRows && TPW * kSlabs == kWave, "one id per lane");
+  const int lane = lane_id();
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t r0 = wave * K * kWave;             // the wave's first row (a tile start)
+  const int64_t t0 = r0 / kSlabTileRows;
+  // lane l: first id of slab l % 8 in tile t0 + l / 8
+  const int64_t tl = min(t0 + lane / kSlabs, n_tiles - 1);
+  const int32_t gl = tile_g[(lane % kSlabs) * n_tiles + tl];
+  uint32_t m[K];
+  V yold[K];
 #pragma unroll
-  for (int u = 0; u < kSlabs; ++u) sg[u] = u < n ? rseg[t0 + u] : -1;
-  V v[kSlabs];
+  for (int k = 0; k < K; ++k) {
+    const int64_t r = r0 + k * kWave + lane;
+    m[k] = r < M ? mask[r] : 0u;
+    yold[k] = beta_nonzero && r < M ? y[r] : V(0);
+  }
+  const uint64_t half = lane >= kSlabTileRows ? 0xffffffff00000000ull : 0x00000000ffffffffull;
+  const uint64_t below = ((1ull << lane) - 1ull) & half;
+  V v[K][kSlabs];
 #pragma unroll
-  for (int u = 0; u < kSlabs; ++u) v[u] = sg[u] >= 0 ? yp[sg[u]] : V(0);
-  V acc = V(0);
+  for (int k = 0; k < K; ++k) {
+    const int tile = 2 * k + (lane >= kSlabTileRows ? 1 : 0);
 #pragma unroll
-  for (int u = 0; u < kSlabs; ++u) acc += v[u];
-  V out = alpha * acc;
-  if (beta_nonzero) out = fma(beta, y[r], out);
-  y[r] = out;
+    for (int s = 0; s < kSlabs; ++s) {
+      const bool has = (m[k] >> s) & 1u;
+      const int before = __popcll(__ballot(has) & below);
+      const int32_t g = __shfl(gl, tile * kSlabs + s);
+      v[k][s] = has ? yp[g + before] : V(0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t r = r0 + k * kWave + lane;
+    V acc = V(0);
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s) acc += v[k][s];
+    if (r < M) {
+      V out = alpha * acc;
+      if (beta_nonzero) out = fma(beta, yold[k], out);
+      y[r] = out;
+    }
+  }
 }
 
 int blocks_for(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
@@ -219,35 +304,38 @@ int blocks_for(int64_t n, int64_t per) { return (int)((n + per - 1) / per); }
 }  // namespace
 
 hipError_t launch_slab_rows(const SlabRows& t, const int32_t* row_ptr, const int32_t* col_idx,
-                            int64_t M, int64_t N, int64_t* stats, hipStream_t s) {
+                            int64_t M, int64_t N, int64_t nnz, int64_t* stats, hipStream_t s) {
   if (M <= 0 || t.n_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(slab_rows_kernel, dim3((unsigned)t.n_tiles), dim3(kBlock), 0, s, row_ptr,
-                     col_idx, M, N, t.rptr, t.mask, t.tile_e, t.tile_g, t.n_tiles, stats);
+                     col_idx, M, N, t.mask, t.tile_e, t.tile_g, t.tile_c, t.n_tiles, stats);
   hipError_t err = hipGetLastError();
-  const int64_t* enable = stats + kStatSlabOk;
-  if (err == hipSuccess) err = exclusive_scan_i32(t.rptr, M + 1, enable, t.scan_temp, s);
-  if (err == hipSuccess)
-    err = exclusive_scan_i32(t.tile_e, kSlabs * t.n_tiles, enable, t.scan_temp, s);
-  if (err == hipSuccess)
-    err = exclusive_scan_i32(t.tile_g, kSlabs * t.n_tiles, enable, t.scan_temp, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(slab_total_kernel, dim3(1), dim3(64), 0, s, t.rptr, M, stats);
+  const int64_t* enable = stats + kStatSlabOk;
+  if ((err = exclusive_scan_i32(t.tile_e, kSlabs * t.n_tiles + 1, enable, t.scan_temp, s)) !=
+          hipSuccess ||
+      (err = exclusive_scan_i32(t.tile_g, kSlabs * t.n_tiles + 1, enable, t.scan_temp, s)) !=
+          hipSuccess ||
+      (err = exclusive_scan_i32(t.tile_c, t.n_tiles + 1, enable, t.scan_temp, s)) != hipSuccess)
+    return err;
+  hipLaunchKernelGGL(slab_total_kernel, dim3(1), dim3(64), 0, s, t.tile_g, t.tile_c, t.n_tiles,
+                     stats);
   return hipGetLastError();
 }
 
 hipError_t launch_slab_emit(const SlabRows& t, const SlabMatrix& m, const int32_t* row_ptr,
                             const int32_t* col_idx, const void* values, int vbytes, int64_t M,
                             int64_t N, int64_t nnz, hipStream_t s) {
-  if (M <= 0 || t.n_tiles <= 0) return hipSuccess;
-  const dim3 g((unsigned)t.n_tiles), b(kBlock);
+  if (M <= 0 || t.n_tiles <= 0 || m.n_chunks <= 0) return hipSuccess;
+  if (m.n_chunks > 0x7fffffffll) return hipErrorInvalidValue;
+  const dim3 g((unsigned)m.n_chunks), b(kBlock);
   if (vbytes == 4)
     hipLaunchKernelGGL(slab_emit_kernel<float>, g, b, 0, s, row_ptr, col_idx,
-                       static_cast<const float*>(values), M, N, nnz, t.rptr, t.tile_e, t.tile_g,
-                       t.n_tiles, m.seg_ptr, m.col, static_cast<float*>(m.val), m.rseg, m.n_seg);
+                       static_cast<const float*>(values), M, N, nnz, t.tile_e, t.tile_g, t.tile_c,
+                       t.n_tiles, m.seg_ptr, m.col, static_cast<float*>(m.val), m.n_seg);
   else
     hipLaunchKernelGGL(slab_emit_kernel<double>, g, b, 0, s, row_ptr, col_idx,
-                       static_cast<const double*>(values), M, N, nnz, t.rptr, t.tile_e,
-                       t.tile_g, t.n_tiles, m.seg_ptr, m.col, static_cast<double*>(m.val), m.rseg,
+                       static_cast<const double*>(values), M, N, nnz, t.tile_e, t.tile_g,
+                       t.tile_c, t.n_tiles, m.seg_ptr, m.col, static_cast<double*>(m.val),
                        m.n_seg);
   return hipGetLastError();
 }
@@ -258,18 +346,18 @@ hipError_t launch_slab_stats(int64_t* stats, int ipt, int64_t P, hipStream_t s) 
 }
 
 template <typename V>
-hipError_t launch_slab_combine(const int32_t* rptr, const int32_t* rseg, const V* yp, V* y,
-                               V alpha, V beta, int beta_nonzero, int64_t M, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(slab_combine_kernel<V>, dim3(blocks_for(M, kBlock)), dim3(kBlock), 0, s,
-                     rptr, rseg, yp, y, alpha, beta, beta_nonzero, (int32_t)M);
+hipError_t launch_slab_combine(const SlabRows& t, const V* yp, V* y, V alpha, V beta,
+                               int beta_nonzero, int64_t M, hipStream_t s) {
+  if (M <= 0 || t.n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slab_combine_kernel<V>, dim3(blocks_for(M, kBlock * kCombineSteps)),
+                     dim3(kBlock), 0, s,
+                     t.mask, t.tile_g, t.n_tiles, yp, y, alpha, beta, beta_nonzero, (int32_t)M);
   return hipGetLastError();
 }
 
-template hipError_t launch_slab_combine<float>(const int32_t*, const int32_t*, const float*,
-                                               float*, float, float, int, int64_t, hipStream_t);
-template hipError_t launch_slab_combine<double>(const int32_t*, const int32_t*, const double*,
-                                                double*, double, double, int, int64_t,
-                                                hipStream_t);
+template hipError_t launch_slab_combine<float>(const SlabRows&, const float*, float*, float,
+                                               float, int, int64_t, hipStream_t);
+template hipError_t launch_slab_combine<double>(const SlabRows&, const double*, double*, double,
+                                                double, int, int64_t, hipStream_t);
 
 }  // namespace spmv

@@ -134,20 +134,32 @@ def test_auto_takes_slabs_on_wide_powerlaw():
     plan.destroy()
 
 
-def test_unsorted_columns_decline_slabs():
+def test_unsorted_columns():
+    """Columns out of order inside some rows: the automatic choice keeps no
+    slabs (a run's end columns stray from its slab); forced on, the runs
+    still partition every row, so the result is right."""
     w = CASES["wide_x"]()
     rng = np.random.default_rng(12)
     col = w.col_idx.copy()
     for r in np.nonzero(np.diff(w.row_ptr) > 100)[0][:5]:
         a, b = w.row_ptr[r], w.row_ptr[r + 1]
         col[a:b] = rng.permutation(col[a:b])
+    sorted_auto = DevMatrix.of(w).plan(None, strategy="merge")
+    assert sorted_auto.info["x_slabs"] == 1, sorted_auto.info
+    sorted_auto.destroy()
     m = DevMatrix(w.row_ptr, col, w.values, w.M, w.N)
-    plan = _slab_plan(m)
-    info = plan.info
+    auto = m.plan(None, strategy="merge")
+    info = auto.info
     assert info["x_slabs"] == 0 and info["plan_allocs"] == 1, info
-    y = run(plan, w.x, 1.0, 0.0)
-    check(y, w.row_ptr, col, w.values, w.x, 1.0, 0.0, None, "unsorted")
-    plan.destroy()
+    y = run(auto, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, col, w.values, w.x, 1.0, 0.0, None, "unsorted, auto")
+    auto.destroy()
+    forced = _slab_plan(m)
+    assert forced.info["x_slabs"] == 1
+    y0 = synth.uniform(w.M, 17, synth.S_Y, np.float32)
+    y = run(forced, w.x, -0.5, 2.0, y0)
+    check(y, w.row_ptr, col, w.values, w.x, -0.5, 2.0, y0, "unsorted, slabs on")
+    forced.destroy()
 
 
 def test_repeated_columns_keep_slabs():
