@@ -53,7 +53,7 @@ WORKLOADS = {
     "banded": "fp32 banded decay matrix, 32,000,000 rows, 24..40 entries within |i-j| <= 1000",
 }
 KERNEL_SOURCES = ["merge_kernels.hip", "tile_exec.hpp", "binned_kernels.hip", "device_common.hpp",
-                  "internal.hpp"]
+                  "internal.hpp", "slab_kernels.hip"]
 SPMM_SOURCES = ["spmm_kernels.hip", "device_common.hpp", "internal.hpp"]
 
 
@@ -610,6 +610,9 @@ def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
                    "items_per_wave": info["items_per_wave"],
                    "bin_streams": info["bin_streams"],
                    "dispatch_order": info["dispatch_order"],
+                   # 1: the walk runs over the plan's slab-major copy of A
+                   # (one column slab of x per XCD), then the combine
+                   "x_slabs": info["x_slabs"], "slab_segments": info["slab_segments"],
                    "cache": "warm" if flush is None else
                    "flushed before every step (1 GiB fill + 1 GiB cached read)"},
         "achieved_GBps": round(gbps_exec, 2),
@@ -659,7 +662,8 @@ def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
     summary.update({"M": w.M, "nnz": w.nnz, "GFLOPs": out["value"],
                     "strategy": info["strategy"], "merge_reduce": info["merge_reduce"],
                     "items_per_wave": info["items_per_wave"],
-                    "dispatch_order": info["dispatch_order"], "kernel": kernel,
+                    "dispatch_order": info["dispatch_order"], "x_slabs": info["x_slabs"],
+                    "kernel": kernel,
                     "kernel_ms": out["roofline"]["kernel_ms"],
                     "roofline_frac": out["roofline"]["frac"],
                     "target_frac": TARGET_FRAC.get(w.name),
