@@ -232,6 +232,41 @@ def read_ceiling(lb, torch, flush, gib: int = 2, reps: int = 10):
     return round(nbytes / (statistics.median(ts) * 1e-3) / 1e9, 1)
 
 
+def gather_sweep(reps: int = 10):
+    """The x-gather ceiling of each layout the x slabs choose between: the
+    library's gather probe (col_idx read once, x gathered at every column,
+    nothing else) over 31M seeded uniform columns drawn from arrays of
+    16 / 8 / 4 / 2 MB of fp32, and from 16 MB where the columns of
+    workgroup b (4,096 consecutive entries) lie in slab b mod S of S
+    slabs; flushed and event-timed like the steps. One JSON line."""
+    import torch
+    import load_balanced_csr_amd as lb
+    dev = torch.device("cuda:0")
+    flush = CacheFlush(torch, dev)
+    nnz, N = 31 * 1024 * 1024, 4_000_000
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    x = torch.rand(N, device=dev, dtype=torch.float32, generator=g)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    rows = []
+
+    def one(name, col):
+        ms = timed_median(torch, flush, reps, lambda: lb.spmv_gather_probe(col, x, sink))
+        rows.append({"x": name, "ms": round(ms, 4), "Ggathers_per_s": round(nnz / ms / 1e6, 1)})
+
+    for nx in (N, N // 2, N // 4, N // 8):
+        col = torch.randint(0, nx, (nnz,), device=dev, dtype=torch.int32, generator=g)
+        one("uniform over %.0f MB" % (4 * nx / 1e6), col)
+    blk = torch.arange(nnz, device=dev, dtype=torch.int64) // 4096
+    for S in (8, 4, 16):
+        slab = N // S
+        col = (torch.randint(0, slab, (nnz,), device=dev, dtype=torch.int64, generator=g)
+               + (blk % S) * slab).to(torch.int32)
+        one("workgroup b in slab b mod %d (%.1f MB)" % (S, 4 * slab / 1e6), col)
+    print(json.dumps({"gather_sweep": rows, "gathers": nnz,
+                      "probe": "spmv_gather_probe, flushed, median of %d" % reps}), flush=True)
+
+
 def calibrate_copy(mib: int, steps: int):
     """A plain copy kernel of known size (torch's device copy): reads and
     writes exactly mib MiB per launch. Under rocprofv3 --pmc FETCH_SIZE /
@@ -705,10 +740,14 @@ def main():
                     help="K > 1: time the multi-vector form (SpMM) with K right-hand sides")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--gather-sweep", action="store_true",
+                    help="only run the x-gather probe over the layouts x slabs choose between")
     args = ap.parse_args()
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, args.steps)
+    if args.gather_sweep:
+        return gather_sweep()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
