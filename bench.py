@@ -267,6 +267,57 @@ def gather_sweep(reps: int = 10):
                       "probe": "spmv_gather_probe, flushed, median of %d" % reps}), flush=True)
 
 
+def slab_sweep(reps: int = 15):
+    """x slabs on and off (strategy merge) on seeded matrices whose x is
+    wider than one XCD's L2: the four the automatic rule takes them for
+    (power-law, uniform short rows with long spikes, skewed rows, random
+    short rows in a stream plan) and two it leaves (a stencil and a band,
+    whose gathers stay near the row); flushed and event-timed like the
+    steps. One JSON line."""
+    import numpy as np
+    import torch
+    import synth
+    import load_balanced_csr_amd as lb
+    dev = torch.device("cuda:0")
+    flush = CacheFlush(torch, dev)
+    rng = np.random.default_rng(3)
+
+    def mats():
+        yield "powerlaw (4M rows, fp32)", synth.powerlaw()
+        yield "powerlaw (2M rows, max 50,000)", synth.powerlaw(M=2_000_000, max_len=50_000)
+        L = rng.integers(1, 16, 4_000_000)
+        L[rng.choice(4_000_000, 2000, replace=False)] = 3000
+        yield "uniform 1..15 + 2,000 rows of 3,000 (4M rows)", synth.random_csr(4_000_000, 4_000_000, L, 7)
+        L = np.minimum((rng.pareto(1.5, 4_000_000) * 20 + 1).astype(np.int64), 5000)
+        yield "skewed, Pareto 1.5, mean 58 (4M rows)", synth.random_csr(4_000_000, 4_000_000, L, 8)
+        yield "uniform 5..15, stream plan (4M rows)", synth.random_csr(
+            4_000_000, 4_000_000, rng.integers(5, 16, 4_000_000), 11)
+        yield "uniform 20..40, stream plan (2M rows)", synth.random_csr(
+            2_000_000, 2_000_000, rng.integers(20, 41, 2_000_000), 12)
+        yield "laplacian (fp64, 2048^2 grid)", synth.laplacian()
+        yield "banded (4M rows)", synth.banded(M=4_000_000)
+
+    rows = []
+    for name, w in mats():
+        rp, col, val, x = (torch.from_numpy(a).to(dev) for a in (w.row_ptr, w.col_idx, w.values, w.x))
+        y = torch.zeros(w.M, device=dev, dtype=val.dtype)
+        r = {"matrix": name, "nnz": w.nnz}
+        for mode in ("auto", "off", "on"):
+            p = lb.Plan(rp, col, val, (w.M, w.N), x_slabs=mode, strategy="merge")
+            info = p.info
+            ms = timed_median(torch, flush, reps, lambda: p(x, y, 1.0, 0.0))
+            r[mode + "_ms"] = round(ms, 4)
+            if mode == "auto":
+                r["auto_takes_slabs"] = info["x_slabs"]
+                r["reduce"] = info["merge_reduce"]
+            p.destroy()
+        print("[bench] slab sweep %s" % json.dumps(r), file=sys.stderr, flush=True)
+        rows.append(r)
+        del rp, col, val, x, y
+        torch.cuda.empty_cache()
+    print(json.dumps({"slab_sweep": rows}), flush=True)
+
+
 def calibrate_copy(mib: int, steps: int):
     """A plain copy kernel of known size (torch's device copy): reads and
     writes exactly mib MiB per launch. Under rocprofv3 --pmc FETCH_SIZE /
@@ -742,8 +793,12 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--gather-sweep", action="store_true",
                     help="only run the x-gather probe over the layouts x slabs choose between")
+    ap.add_argument("--slab-sweep", action="store_true",
+                    help="only time x slabs on / off / auto on matrices with a wide x")
     args = ap.parse_args()
 
+    if args.slab_sweep:
+        return slab_sweep()
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, args.steps)
     if args.gather_sweep:

@@ -211,7 +211,8 @@ __device__ __forceinline__ int64_t split_at(const int32_t* __restrict__ row_ptr,
 //    T/8) whose x is larger than one XCD's L2 and whose partitions mostly
 //    hold row ends are split again at T = 256 (their gathers are bound by the
 //    L1 misses in flight, and T = 256 runs twice the waves per CU).
-//  stage 3 -- (after the tile plan) x slabs, see slab_kernels.hip.
+//  stage 3 -- (after the window spans and the tile plan) x slabs, see
+//    slab_kernels.hip.
 //  stage 2 -- walk plans deal their partitions in column order when at least
 //    an eighth of them lie inside one row and every row covers under a
 //    quarter of the columns (or when the caller asks for it); and walk plans
@@ -256,15 +257,21 @@ __global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_
     stats[kStatTileOk] = walk && c.tiles_req != 1 && c.order_req != 2 && P > 0 && c.nnz > 0 &&
                          !(err & kErrRowPtr) && c.N > bc;
   } else if (stage == 3) {
-    // after the tile plan: x slabs for walk plans that were split again at
-    // T = 256 (x wider than one XCD's L2, partitions mostly holding row ends)
-    // and keep no tiles; or whenever the caller asks for them
+    // after the window spans and the tile plan: x slabs where x is wider
+    // than one XCD's L2 and the gathers spread over it -- walk plans split
+    // again at T = 256 (partitions mostly holding row ends), stream plans
+    // whose workgroups' columns fit no x window -- and no tiles are kept;
+    // or whenever the caller asks for them
     const int64_t T = kWave * stats[kStatIpt], P = stats[kStatParts];
     const bool walk = c.reduce_req == 1 || (c.reduce_req == 0 && max_len > T / 8);
+    const int64_t S = stats[kStatWindowSamples];
+    const bool spread = !walk && S > 0 && 2 * stats[kStatWindowFits] < S &&
+                        2 * stats[kStatWindowFitsMulti] < S;
     const bool ok = c.slab_room && c.slabs_req != 1 && P > 0 && c.nnz > 0 &&
                     !(err & (kErrRowPtr | kErrColumn)) && stats[kStatTileRows] == 0;
     stats[kStatSlabOk] =
-        ok && (c.slabs_req == 2 || (walk && c.wide_x && stats[kStatResplit] != 0));
+        ok && (c.slabs_req == 2 ||
+               (c.wide_x && ((walk && stats[kStatResplit] != 0) || spread)));
   }
 }
 

@@ -134,6 +134,27 @@ def test_auto_takes_slabs_on_wide_powerlaw():
     plan.destroy()
 
 
+def test_auto_takes_slabs_on_wide_random_stream_plan():
+    """Short rows (a stream plan) with uniform columns over a 4.8 MB x: no
+    workgroup's columns fit an x window, so the automatic plan takes slabs;
+    a stencil keeps its window and no slabs (the five workloads' choices
+    are pinned in test_gpu_plan.py)."""
+    M = 1_200_000
+    w = synth.random_csr(M, M, np.random.default_rng(18).integers(5, 16, M), 19,
+                         beta=0.25)
+    m = DevMatrix.of(w)
+    plan = m.plan(None)
+    info = plan.info
+    log("auto slabs, stream", info["x_slabs"], info["merge_reduce"], info["items_per_wave"],
+        info["slab_segments"])
+    assert info["merge_reduce"] == "stream" and info["x_slabs"] == 1, info
+    y = run(plan, w.x, 1.0, 0.25, w.y0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.25, w.y0, "auto slabs, stream")
+    y2 = run(plan, w.x, 1.0, 0.25, w.y0)
+    assert np.array_equal(y.view(np.uint8), y2.view(np.uint8))
+    plan.destroy()
+
+
 def test_unsorted_columns():
     """Columns out of order inside some rows: the automatic choice keeps no
     slabs (a run's end columns stray from its slab); forced on, the runs
