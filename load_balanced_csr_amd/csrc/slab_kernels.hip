@@ -240,7 +240,8 @@ __global__ __launch_bounds__(64) void slab_stats_kernel(int64_t* stats, int ipt,
 }
 
 // Rows per thread of the combine: a wave takes 4 x 64 consecutive rows, 64
-// at a time, so more of its loads are in flight together.
+// at a time, so more of its loads are in flight together (power-law: 1 / 4 /
+// 8 rows a thread, 32 / 21 / 26 us).
 constexpr int kCombineSteps = 4;
 
 // A wave takes kCombineSteps runs of 64 rows (two tiles of 32 each), one
@@ -255,14 +256,19 @@ __global__ __launch_bounds__(kBlock) void slab_combine_kernel(
     const V* __restrict__ yp, V* __restrict__ y, V alpha, V beta, int beta_nonzero, int32_t M) {
   constexpr int K = kCombineSteps;
   constexpr int TPW = K * kWave / kSlabTileRows;   // tiles of a wave
-  static_assert(kWave == 2 * kSlabTileRows && TPW * kSlabs == kWave, "one id per lane");
+  constexpr int NG = TPW * kSlabs / kWave;          // first ids per lane
+  static_assert(kWave == 2 * kSlabTileRows && NG * kWave == TPW * kSlabs, "ids fill lanes");
   const int lane = lane_id();
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int64_t r0 = wave * K * kWave;             // the wave's first row (a tile start)
   const int64_t t0 = r0 / kSlabTileRows;
-  // lane l: first id of slab l % 8 in tile t0 + l / 8
-  const int64_t tl = min(t0 + lane / kSlabs, n_tiles - 1);
-  const int32_t gl = tile_g[(lane % kSlabs) * n_tiles + tl];
+  // gl[j] of lane l: first id of slab l % 8 in tile t0 + 8 j + l / 8
+  int32_t gl[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int64_t tl = min(t0 + (kWave / kSlabs) * j + lane / kSlabs, n_tiles - 1);
+    gl[j] = tile_g[(lane % kSlabs) * n_tiles + tl];
+  }
   uint32_t m[K];
   V yold[K];
 #pragma unroll
@@ -281,7 +287,8 @@ __global__ __launch_bounds__(kBlock) void slab_combine_kernel(
     for (int s = 0; s < kSlabs; ++s) {
       const bool has = (m[k] >> s) & 1u;
       const int before = __popcll(__ballot(has) & below);
-      const int32_t g = __shfl(gl, tile * kSlabs + s);
+      const int q = tile * kSlabs + s;   // q / 64 is fixed for each step k
+      const int32_t g = __shfl(gl[q / kWave], q % kWave);
       v[k][s] = has ? yp[g + before] : V(0);
     }
   }

@@ -28,6 +28,9 @@ def _spmv_cases():
         # long rows in column-blocked tiles: the walk+tile grid, the fix-up
         # and the tile reduction, three launches per exec
         "merge_walk_tiles": (bi, dict(strategy="merge", merge_reduce="walk")),
+        # x slabs: the walk over the slab-major copy, its fix-up and the
+        # combine, three launches per exec
+        "merge_x_slabs": (pw, dict(strategy="merge", x_slabs="on")),
         "binned": (pw, dict(strategy="binned")),
         "group": (pw, dict(strategy="group")),
         "rgcsr": (lap, None),
@@ -59,6 +62,8 @@ def test_spmv_graph_replays(case):
     m, plan = _plan(w, opts)
     if case == "merge_walk_tiles":
         assert plan.info["tile_rows"] > 0, plan.info
+    if case == "merge_x_slabs":
+        assert plan.info["x_slabs"] == 1, plan.info
     dt = w.values.dtype.type
     x = dev(w.x)
     y0 = dev(synth.uniform(w.M, 12, synth.S_Y, dt))
