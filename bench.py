@@ -268,12 +268,12 @@ def gather_sweep(reps: int = 10):
 
 
 def slab_sweep(reps: int = 15):
-    """x slabs on and off (strategy merge) on seeded matrices whose x is
-    wider than one XCD's L2: the four the automatic rule takes them for
-    (power-law, uniform short rows with long spikes, skewed rows, random
-    short rows in a stream plan) and two it leaves (a stencil and a band,
-    whose gathers stay near the row); flushed and event-timed like the
-    steps. One JSON line."""
+    """x slabs on, off and auto (strategy merge) on seeded matrices whose x
+    is wider than one XCD's L2 (power-law, uniform short rows with long
+    spikes, skewed rows, random short rows in stream plans, and a stencil
+    and a band, whose gathers stay near the row) or of 2..4 MB (random rows
+    of 5..80 entries); flushed and event-timed like the steps. One JSON
+    line."""
     import numpy as np
     import torch
     import synth
@@ -294,6 +294,12 @@ def slab_sweep(reps: int = 15):
             4_000_000, 4_000_000, rng.integers(5, 16, 4_000_000), 11)
         yield "uniform 20..40, stream plan (2M rows)", synth.random_csr(
             2_000_000, 2_000_000, rng.integers(20, 41, 2_000_000), 12)
+        yield "uniform 40..80, x of 3 MB (750K rows)", synth.random_csr(
+            750_000, 750_000, rng.integers(40, 81, 750_000), 13)
+        yield "uniform 24..40, x of 2 MB (500K rows)", synth.random_csr(
+            500_000, 500_000, rng.integers(24, 41, 500_000), 14)
+        yield "uniform 5..15, x of 4 MB (1M rows)", synth.random_csr(
+            1_000_000, 1_000_000, rng.integers(5, 16, 1_000_000), 15)
         yield "laplacian (fp64, 2048^2 grid)", synth.laplacian()
         yield "banded (4M rows)", synth.banded(M=4_000_000)
 

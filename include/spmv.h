@@ -195,12 +195,16 @@ typedef struct spmv_plan_options {
                                  each XCD the partitions of one slab, so its
                                  gathers stay within an eighth of x, and a
                                  final kernel adds each row's slab sums in slab
-                                 order. Auto: plans whose x is larger than
-                                 4 MiB (one XCD's L2) and whose gathers spread
-                                 over it: walk plans split again at T = 256
-                                 (their partitions mostly hold row ends), and
-                                 stream plans whose workgroups' columns fit no
-                                 x window (x_window above); on:
+                                 order. Auto: plans whose gathers spread over
+                                 an x larger than 4 MiB (one XCD's L2) -- walk
+                                 plans split again at T = 256 (their
+                                 partitions mostly hold row ends), stream
+                                 plans whose workgroups' columns fit no x
+                                 window (x_window above) -- or over an x of
+                                 1..4 MiB whose rows average at least
+                                 1e8 / (x bytes) entries (walk plans with
+                                 partitions mostly holding row ends, the same
+                                 stream plans); on:
                                  every plan. Either way only MERGE plans that
                                  keep no long-row tiles (those win where both
                                  apply). Each row's entries are

@@ -828,7 +828,16 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   ctl.slabs_req = options && options->x_slabs ? options->x_slabs
                   : env_int("SPMV_X_SLABS", -1) == 0 ? 1
                   : env_int("SPMV_X_SLABS", -1) == 1 ? 2 : 0;
-  ctl.slab_room = M > 0 && nnz > 0 && ctl.slabs_req != 1 && (ctl.slabs_req == 2 || ctl.wide_x) &&
+  // an x of 1..4 MiB takes slabs only when rows are long: measured, they pay
+  // where mean row length x x bytes >= 1e8 (uniform rows of 32 over 4 MB,
+  // of 90 over 2 MB; not rows of 32 over 2 MB nor of 18 over 4 MB)
+  {
+    const int64_t xb = N * (int64_t)vs;
+    ctl.mid_x = !ctl.wide_x && xb > (int64_t(1) << 20) && M > 0 &&
+                (double)nnz / (double)M * (double)xb >= 1e8;
+  }
+  ctl.slab_room = M > 0 && nnz > 0 && ctl.slabs_req != 1 &&
+                  (ctl.slabs_req == 2 || ctl.wide_x || ctl.mid_x) &&
                   slab_scan_max(M) <= kScanMaxElems && 2 * nnz <= kMaxUnits;
 
   // ---- the one workspace allocation -------------------------------------------

@@ -150,6 +150,7 @@ struct PlanCtl {
   int32_t order_req;    // 0 auto, 1 partition order, 2 column order
   int32_t tiles_req;    // 0 auto, 1 off
   int32_t slabs_req;    // 0 auto, 1 off, 2 on
+  int32_t mid_x;        // x of 1..4 MiB with mean row length x x bytes >= 1e8
   int32_t slab_room;    // the workspace holds the x slabs' row tables
 };
 

@@ -257,11 +257,13 @@ __global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_
     stats[kStatTileOk] = walk && c.tiles_req != 1 && c.order_req != 2 && P > 0 && c.nnz > 0 &&
                          !(err & kErrRowPtr) && c.N > bc;
   } else if (stage == 3) {
-    // after the window spans and the tile plan: x slabs where x is wider
-    // than one XCD's L2 and the gathers spread over it -- walk plans split
-    // again at T = 256 (partitions mostly holding row ends), stream plans
-    // whose workgroups' columns fit no x window -- and no tiles are kept;
-    // or whenever the caller asks for them
+    // after the window spans and the tile plan: x slabs where the gathers
+    // spread over an x wider than one XCD's L2 -- walk plans split again at
+    // T = 256 (partitions mostly holding row ends), stream plans whose
+    // workgroups' columns fit no x window -- or over an x of 1..4 MiB when
+    // rows are long enough to pay for the combine (mid_x: walk plans whose
+    // partitions mostly hold row ends, the same stream plans), and no tiles
+    // are kept; or whenever the caller asks for them
     const int64_t T = kWave * stats[kStatIpt], P = stats[kStatParts];
     const bool walk = c.reduce_req == 1 || (c.reduce_req == 0 && max_len > T / 8);
     const int64_t S = stats[kStatWindowSamples];
@@ -269,9 +271,9 @@ __global__ __launch_bounds__(64) void plan_choose_kernel(const PlanCtl c, int64_
                         2 * stats[kStatWindowFitsMulti] < S;
     const bool ok = c.slab_room && c.slabs_req != 1 && P > 0 && c.nnz > 0 &&
                     !(err & (kErrRowPtr | kErrColumn)) && stats[kStatTileRows] == 0;
-    stats[kStatSlabOk] =
-        ok && (c.slabs_req == 2 ||
-               (c.wide_x && ((walk && stats[kStatResplit] != 0) || spread)));
+    const bool wide = c.wide_x && ((walk && stats[kStatResplit] != 0) || spread);
+    const bool mid = c.mid_x && ((walk && 2 * stats[kStatInterior] < P) || spread);
+    stats[kStatSlabOk] = ok && (c.slabs_req == 2 || wide || mid);
   }
 }
 

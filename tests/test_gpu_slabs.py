@@ -155,6 +155,27 @@ def test_auto_takes_slabs_on_wide_random_stream_plan():
     plan.destroy()
 
 
+def test_auto_slabs_for_mid_x_and_long_rows():
+    """x of 1.1 MB, rows of 100..199 (mean length x x bytes >= 1e8): the
+    automatic plan takes slabs; the same rows over 2 MB but of 5..15
+    entries do not."""
+    M = 280_000
+    w = synth.random_csr(M, M, np.random.default_rng(20).integers(100, 200, M), 21)
+    m = DevMatrix.of(w)
+    plan = m.plan(None)
+    info = plan.info
+    log("auto slabs, mid x", info["x_slabs"], info["merge_reduce"], info["slab_segments"])
+    assert info["x_slabs"] == 1, info
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "auto slabs, mid x")
+    plan.destroy()
+    M = 500_000
+    w = synth.random_csr(M, M, np.random.default_rng(22).integers(5, 16, M), 23)
+    plan = DevMatrix.of(w).plan(None)
+    assert plan.info["x_slabs"] == 0, plan.info
+    plan.destroy()
+
+
 def test_unsorted_columns():
     """Columns out of order inside some rows: the automatic choice keeps no
     slabs (a run's end columns stray from its slab); forced on, the runs
