@@ -81,7 +81,7 @@ def test_bad_options_rejected():
         assert st == 1, kw
     # per-bin streams beyond the bin count, dispatch orders that do not exist
     for field, bad in (("bin_streams", 9), ("bin_streams", -1), ("dispatch_order", 3),
-                       ("dispatch_order", -1)):
+                       ("dispatch_order", -1), ("x_slabs", 3), ("x_slabs", -1)):
         o = lb.make_options()
         setattr(o, field, bad)
         st = lib.spmv_plan_ex(ctypes.byref(h), 10, 10, 20, 0x1000, 0x2000, 0x3000, 0,
@@ -96,6 +96,8 @@ def test_exec_and_destroy_reject_foreign_handles():
     assert lib.spmv_exec(0x12345678, 0x10, 0x20, 1.0, 0.0, None) == 5
     assert lib.spmv_destroy(0x12345678) == 5
     assert lib.spmv_destroy(None) == 0
+    assert lib.spmv_plan_update_values(None, 0x1000, None) == 5
+    assert lib.spmv_plan_update_values(0x12345678, 0x1000, None) == 5
     info = binding.PlanInfo()
     assert lib.spmv_plan_info(0x12345678, ctypes.byref(info)) == 5
     with pytest.raises(lb.SpmvError) as e:
