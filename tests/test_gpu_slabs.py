@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import load_balanced_csr_amd as lb
 import synth
 from gpu_util import DevMatrix, check, dev, log, run
 
@@ -258,7 +259,7 @@ def test_update_values():
 def test_update_values_refused_for_copies_in_other_layouts():
     w = CASES["narrow_N"]()
     m = DevMatrix.of(w)
-    t = __import__("load_balanced_csr_amd").Plan.transpose(m.rp, m.col, m.val, (w.M, w.N))
+    t = lb.Plan.transpose(m.rp, m.col, m.val, (w.M, w.N))
     with pytest.raises(Exception):
         t.update_values(m.val)
     t.destroy()
@@ -286,3 +287,33 @@ def test_other_entry_points_over_a_slab_plan():
         y = run(plan, w.x, 1.0, 0.0)
         check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "slab plan as " + s)
     plan.destroy()
+
+
+def test_slabs_in_the_other_input_forms():
+    """COO and transposed / CSC plans build through the same planning and
+    take slabs the same way: forced on, each against its oracle."""
+    w = CASES["powerlaw"]()
+    rows = np.repeat(np.arange(w.M, dtype=np.int32), np.diff(w.row_ptr))
+    m = DevMatrix.of(w)
+    coo = lb.Plan.coo(dev(rows), m.col, m.val, (w.M, w.N), strategy="merge", x_slabs="on")
+    assert coo.info["x_slabs"] == 1, coo.info
+    y = run(coo, w.x, 1.0, 0.0)
+    ref, scale = oracle.spmv_coo(w.M, rows, w.col_idx, w.values, w.x, 1.0, 0.0, None)
+    ok, worst, idx = oracle.within_tolerance(y, ref, scale, 1.0, 0.0, None, row_ptr=w.row_ptr)
+    assert ok, ("coo over slabs", idx, worst)
+    coo.destroy()
+    for kind in ("transpose", "csc"):
+        if kind == "transpose":
+            p = lb.Plan.transpose(m.rp, m.col, m.val, (w.M, w.N), strategy="merge",
+                                  x_slabs="on")
+        else:
+            # A's CSR arrays are the CSC arrays of A^T (N x M)
+            p = lb.Plan.csc(m.rp, m.col, m.val, (w.N, w.M), strategy="merge", x_slabs="on")
+        assert p.info["x_slabs"] == 1, (kind, p.info)
+        x = synth.uniform(w.M, 24, synth.S_X, np.float32)
+        y0 = synth.uniform(w.N, 25, synth.S_Y, np.float32)
+        y = run(p, x, 0.75, -0.5, y0)
+        ref, scale = oracle.spmv_t(w.N, w.row_ptr, w.col_idx, w.values, x, 0.75, -0.5, y0)
+        ok, worst, idx = oracle.within_tolerance(y, ref, scale, 0.75, -0.5, y0)
+        assert ok, (kind, "over slabs", idx, worst)
+        p.destroy()
