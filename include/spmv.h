@@ -420,8 +420,11 @@ SPMV_API spmv_status_t spmv_plan_rgcsr(spmv_plan_t* out, int64_t M, int64_t N, i
  * never allocates, frees or synchronises, so it can be captured in a HIP
  * graph. Rows with no entries give exactly beta*y (0 when beta == 0). For a
  * fixed plan the result is bitwise reproducible (no float atomics). One plan
- * must not run concurrently on two streams (its carry buffer and events are
- * per plan); distinct plans are independent. */
+ * must not run concurrently on two streams (its carry buffer, its x slabs'
+ * segment sums and its events are per plan); distinct plans are
+ * independent. A plan with x slabs (options.x_slabs) runs the walk over its
+ * slab-major copy, its fix-up and a combine of each row's slab sums: three
+ * launches, all on stream. */
 SPMV_API spmv_status_t spmv_exec(spmv_plan_t plan, const void* x, void* y,
                         double alpha, double beta, hipStream_t stream);
 
