@@ -2,9 +2,9 @@
 shape and row-length mix (uniform, Zipf tail, a few very long rows, many
 empty rows; duplicate and unsorted columns in some), random dtype, alpha and
 beta, run through every schedule and input form the library has -- auto,
-merge-path walk in both dispatch orders, stream where it applies, binned as
-one grid and per bin on streams, group-mapped, row-grouped, COO, transposed
--- and SpMM with a random k, each against the oracle."""
+merge-path walk in both dispatch orders, stream where it applies, x slabs,
+binned as one grid and per bin on streams, group-mapped, row-grouped, COO,
+transposed -- and SpMM with a random k, each against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -64,6 +64,9 @@ def _variants(rng):
         "binned": dict(strategy="binned"),
         "binned_streams": dict(strategy="binned", bin_streams=int(rng.integers(1, 5))),
         "group": dict(strategy="group"),
+        # x slabs forced on: the slab-major copy, its walk and the combine,
+        # whatever the column order (duplicates, unsorted rows)
+        "x_slabs": dict(strategy="merge", x_slabs="on"),
     }
     return v
 
