@@ -309,7 +309,8 @@ def slab_sweep(reps: int = 15):
         y = torch.zeros(w.M, device=dev, dtype=val.dtype)
         r = {"matrix": name, "nnz": w.nnz}
         for mode in ("auto", "off", "on"):
-            p = lb.Plan(rp, col, val, (w.M, w.N), x_slabs=mode, strategy="merge")
+            p = lb.Plan(rp, col, val, (w.M, w.N), x_slabs=mode, strategy="merge",
+                        static_matrix=True)
             info = p.info
             ms = timed_median(torch, flush, reps, lambda: p(x, y, 1.0, 0.0))
             r[mode + "_ms"] = round(ms, 4)
@@ -580,8 +581,10 @@ def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
     y = torch.empty(w.M, dtype=dt, device=dev)
     torch.cuda.synchronize()
 
+    # the benchmark's matrices never change after planning: it declares them
+    # static, which lets the plan keep a copy of A (x slabs) where it pays
     popts = dict(strategy=args.strategy, items_per_thread=args.items_per_thread,
-                 bin_streams=args.bin_streams)
+                 bin_streams=args.bin_streams, static_matrix=not args.mutable_matrix)
     if args.strategy == "rgcsr":
         assert args.format == "csr", "the row-grouped copy is built from CSR"
 
@@ -704,6 +707,7 @@ def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
                    "dispatch_order": info["dispatch_order"],
                    # 1: the walk runs over the plan's slab-major copy of A
                    # (one column slab of x per XCD), then the combine
+                   "static_matrix": not args.mutable_matrix,
                    "x_slabs": info["x_slabs"], "slab_segments": info["slab_segments"],
                    "cache": "warm" if flush is None else
                    "flushed before every step (1 GiB fill + 1 GiB cached read)"},
@@ -799,6 +803,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--gather-sweep", action="store_true",
                     help="only run the x-gather probe over the layouts x slabs choose between")
+    ap.add_argument("--mutable-matrix", action="store_true",
+                    help="plan without declaring the matrix static (no plan-time copy of A)")
     ap.add_argument("--slab-sweep", action="store_true",
                     help="only time x slabs on / off / auto on matrices with a wide x")
     args = ap.parse_args()

@@ -195,7 +195,9 @@ typedef struct spmv_plan_options {
                                  each XCD the partitions of one slab, so its
                                  gathers stay within an eighth of x, and a
                                  final kernel adds each row's slab sums in slab
-                                 order. Auto: plans whose gathers spread over
+                                 order. Auto (only with static_matrix below,
+                                 as the copy holds A's columns and values of
+                                 plan time): plans whose gathers spread over
                                  an x larger than 4 MiB (one XCD's L2) -- walk
                                  plans split again at T = 256 (their
                                  partitions mostly hold row ends), stream
@@ -220,7 +222,15 @@ typedef struct spmv_plan_options {
                                  time: call spmv_plan_update_values after
                                  changing them (spmv_plan_info.x_slabs tells
                                  whether the plan took slabs). */
-  int32_t pad0;
+  int32_t static_matrix;      /* 0 (default): the plan borrows row_ptr,
+                                 col_idx and values, and the contents of
+                                 col_idx and values may change between
+                                 spmv_exec calls (row_ptr may not). 1: the
+                                 caller keeps col_idx and values as they are
+                                 at plan time, or changes values only through
+                                 spmv_plan_update_values; the plan may then
+                                 hold a copy of A in another layout (x slabs,
+                                 auto). */
 } spmv_plan_options_t;
 
 typedef struct spmv_plan_info {

@@ -51,7 +51,7 @@ class PlanOptions(ctypes.Structure):
                 ("bin_max_len", ctypes.c_int64 * MAX_BINS),
                 ("bin_lanes", ctypes.c_int32 * MAX_BINS),
                 ("dispatch_order", ctypes.c_int32), ("long_row_tiles", ctypes.c_int32),
-                ("x_slabs", ctypes.c_int32), ("pad0", ctypes.c_int32)]
+                ("x_slabs", ctypes.c_int32), ("static_matrix", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -212,7 +212,8 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
                  validate_columns: bool = False, merge_reduce: str = "auto",
                  stream_lanes: int = 0, x_window: str = "auto",
                  bin_streams: int = 0, dispatch_order: str = "auto",
-                 long_row_tiles: str = "auto", x_slabs: str = "auto") -> PlanOptions:
+                 long_row_tiles: str = "auto", x_slabs: str = "auto",
+                 static_matrix: bool = False) -> PlanOptions:
     """bins: optional list of (max_len, lanes) pairs; the last max_len is ignored.
     bin_streams: 0 runs the binned schedule as one grid; n >= 1 launches each
     bin on its own, dealt over the caller's stream and n - 1 plan streams.
@@ -229,6 +230,7 @@ def make_options(strategy: str = "auto", items_per_thread: int = 0, bins=None,
     o.dispatch_order = DISPATCH_ORDER[dispatch_order]
     o.long_row_tiles = {"auto": 0, "off": 1}[long_row_tiles]
     o.x_slabs = {"auto": 0, "off": 1, "on": 2}[x_slabs]
+    o.static_matrix = int(bool(static_matrix))
     if bins:
         o.n_bins = len(bins)
         for k, (ml, lanes) in enumerate(bins):
@@ -551,16 +553,18 @@ class Plan:
                  items_per_thread: int = 0, bins=None, validate_columns: bool = False,
                  merge_reduce: str = "auto", stream_lanes: int = 0, x_window: str = "auto",
                  bin_streams: int = 0, dispatch_order: str = "auto",
-                 long_row_tiles: str = "auto", x_slabs: str = "auto", stream=None):
+                 long_row_tiles: str = "auto", x_slabs: str = "auto",
+                 static_matrix: bool = False, stream=None):
         self.M, self.N = int(shape[0]), int(shape[1])
         self._keep = (row_ptr, col_idx, values)
         opts = None
         if (strategy != "auto" or items_per_thread or bins or validate_columns
                 or merge_reduce != "auto" or stream_lanes or x_window != "auto" or bin_streams
-                or dispatch_order != "auto" or long_row_tiles != "auto" or x_slabs != "auto"):
+                or dispatch_order != "auto" or long_row_tiles != "auto" or x_slabs != "auto"
+                or static_matrix):
             opts = make_options(strategy, items_per_thread, bins, validate_columns,
                                 merge_reduce, stream_lanes, x_window, bin_streams,
-                                dispatch_order, long_row_tiles, x_slabs)
+                                dispatch_order, long_row_tiles, x_slabs, static_matrix)
         self.handle = spmv_plan(row_ptr, col_idx, values, self.M, self.N, opts, stream)
 
     @classmethod

@@ -202,6 +202,8 @@ spmv_status_t check_options(const spmv_plan_options_t* o) {
     return fail(SPMV_ERR_INVALID_ARG, "options.long_row_tiles %d unknown", o->long_row_tiles);
   if (o->x_slabs < 0 || o->x_slabs > 2)
     return fail(SPMV_ERR_INVALID_ARG, "options.x_slabs %d unknown", o->x_slabs);
+  if (o->static_matrix < 0 || o->static_matrix > 1)
+    return fail(SPMV_ERR_INVALID_ARG, "options.static_matrix %d unknown", o->static_matrix);
   if (o->bin_streams < 0 || o->bin_streams > SPMV_MAX_BINS)
     return fail(SPMV_ERR_INVALID_ARG, "options.bin_streams must be in [0, %d]", SPMV_MAX_BINS);
   if (o->n_bins < 0 || o->n_bins > SPMV_MAX_BINS)
@@ -824,10 +826,13 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   int key_bits = 1;
   while (key_bits < 31 && (int64_t(1) << key_bits) < N) ++key_bits;
   // x slabs: 0 auto, 1 off, 2 on (options, then env SPMV_X_SLABS = 0 / 1);
-  // the workspace reserves their row tables when they may be taken
+  // auto only for a static matrix (the copy holds A's columns and values of
+  // plan time); the workspace reserves their row tables when they may be
+  // taken
   ctl.slabs_req = options && options->x_slabs ? options->x_slabs
                   : env_int("SPMV_X_SLABS", -1) == 0 ? 1
                   : env_int("SPMV_X_SLABS", -1) == 1 ? 2 : 0;
+  if (ctl.slabs_req == 0 && !(options && options->static_matrix)) ctl.slabs_req = 1;
   // an x of 1..4 MiB takes slabs only when rows are long: measured, they pay
   // where mean row length x x bytes >= 1e8 (uniform rows of 32 over 4 MB,
   // of 90 over 2 MB; not rows of 32 over 2 MB nor of 18 over 4 MB)

@@ -29,6 +29,8 @@ VARIANTS = {
     "merge7": dict(strategy="merge", items_per_thread=7),
     "merge7_xwin": dict(strategy="merge", items_per_thread=7, x_window="on", stream_lanes=4),
     "merge16_xwin": dict(strategy="merge", items_per_thread=16, x_window="on", stream_lanes=8),
+    # declared static: the plan may keep a copy of A (x slabs where they pay)
+    "static": dict(static_matrix=True),
     "binned": dict(strategy="binned"),
     # other bin edges: correctness must not depend on them
     "binned_alt": dict(strategy="binned",

@@ -81,7 +81,8 @@ def test_bad_options_rejected():
         assert st == 1, kw
     # per-bin streams beyond the bin count, dispatch orders that do not exist
     for field, bad in (("bin_streams", 9), ("bin_streams", -1), ("dispatch_order", 3),
-                       ("dispatch_order", -1), ("x_slabs", 3), ("x_slabs", -1)):
+                       ("dispatch_order", -1), ("x_slabs", 3), ("x_slabs", -1),
+                       ("static_matrix", 2)):
         o = lb.make_options()
         setattr(o, field, bad)
         st = lib.spmv_plan_ex(ctypes.byref(h), 10, 10, 20, 0x1000, 0x2000, 0x3000, 0,

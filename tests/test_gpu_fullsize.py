@@ -21,7 +21,7 @@ def test_full_size_parity(name):
     dt = w.values.dtype.type
     ref, scale = oracle.spmv(w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, w.y0)
     m = DevMatrix.of(w)
-    for variant in (None, "merge8", "merge8_walk", "merge8_xwin", "merge7", "binned"):
+    for variant in (None, "static", "merge8", "merge8_walk", "merge8_xwin", "merge7", "binned"):
         log("run", name, variant or "auto", "M=%d nnz=%d" % (w.M, w.nnz))
         plan = m.plan(variant)
         y = run(plan, w.x, w.alpha, w.beta, w.y0, dt)
@@ -43,8 +43,8 @@ def test_full_size_row_lengths_exact(name):
     w = synth.CONFIGS[name]()
     L = np.diff(w.row_ptr).astype(np.float32)
     m = DevMatrix(w.row_ptr, w.col_idx, np.ones(w.nnz, np.float32), w.M, w.N)
-    # None: the default plan (power-law: x slabs)
-    for variant in (None, "merge8", "merge8_walk", "binned"):
+    # "static": the plan bench.py times (power-law: x slabs)
+    for variant in (None, "static", "merge8", "merge8_walk", "binned"):
         log("lengths", name, variant)
         plan = m.plan(variant)
         y = run(plan, np.ones(w.N, np.float32), 1.0, 0.0)

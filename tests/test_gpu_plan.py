@@ -37,13 +37,18 @@ def test_one_allocation_one_sync(name):
     log("plan contract", name)
     w = synth.CONFIGS[name]()
     m = DevMatrix.of(w)
-    plan = m.plan(None)
+    # planned as bench.py plans it: the matrix declared static
+    plan = m.plan(None, static_matrix=True)
     info = plan.info
     assert info["plan_allocs"] == 1 + info["x_slabs"] and info["plan_syncs"] == 1, info
     assert (info["items_per_wave"], info["merge_reduce"], info["dispatch_order"],
             info["x_slabs"]) == EXPECTED[name], info
     assert info["n_partitions"] == -(-(w.M + w.nnz) // info["items_per_wave"])
     assert (info["tile_rows"] > 0) == (name == "bimodal"), info
+    plan.destroy()
+    # not declared static, the plan borrows A and keeps no copy of it
+    plan = m.plan(None)
+    assert plan.info["x_slabs"] == 0 and plan.info["plan_allocs"] == 1, plan.info
     plan.destroy()
     del m
     torch.cuda.empty_cache()

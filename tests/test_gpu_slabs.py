@@ -114,11 +114,12 @@ def test_slab_row_lengths_exact():
 
 
 def test_auto_takes_slabs_on_wide_powerlaw():
-    """A power-law matrix whose x (6 MB) is wider than one XCD's L2: the
-    automatic plan walks at T = 256 and takes slabs; off when asked."""
+    """A power-law matrix whose x (6 MB) is wider than one XCD's L2, declared
+    static: the automatic plan walks at T = 256 and takes slabs; off when
+    asked, and never when the matrix is not declared static."""
     w = synth.powerlaw(M=1_500_000, max_len=20_000)
     m = DevMatrix.of(w)
-    plan = m.plan(None)
+    plan = m.plan(None, static_matrix=True)
     info = plan.info
     log("auto slabs", info["x_slabs"], info["items_per_wave"], info["merge_reduce"],
         info["slab_segments"], info["plan_allocs"], info["plan_syncs"])
@@ -127,8 +128,12 @@ def test_auto_takes_slabs_on_wide_powerlaw():
     y0 = w.y0
     y = run(plan, w.x, w.alpha, w.beta, y0)
     check(y, w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, y0, "auto slabs")
-    off = m.plan(None, x_slabs="off")
+    off = m.plan(None, x_slabs="off", static_matrix=True)
     assert off.info["x_slabs"] == 0 and off.info["plan_allocs"] == 1
+    # not declared static: no copy of A, whatever the gathers
+    borrowed = m.plan(None)
+    assert borrowed.info["x_slabs"] == 0 and borrowed.info["plan_allocs"] == 1
+    borrowed.destroy()
     y = run(off, w.x, w.alpha, w.beta, y0)
     check(y, w.row_ptr, w.col_idx, w.values, w.x, w.alpha, w.beta, y0, "slabs off")
     off.destroy()
@@ -144,7 +149,7 @@ def test_auto_takes_slabs_on_wide_random_stream_plan():
     w = synth.random_csr(M, M, np.random.default_rng(18).integers(5, 16, M), 19,
                          beta=0.25)
     m = DevMatrix.of(w)
-    plan = m.plan(None)
+    plan = m.plan(None, static_matrix=True)
     info = plan.info
     log("auto slabs, stream", info["x_slabs"], info["merge_reduce"], info["items_per_wave"],
         info["slab_segments"])
@@ -163,7 +168,7 @@ def test_auto_slabs_for_mid_x_and_long_rows():
     M = 280_000
     w = synth.random_csr(M, M, np.random.default_rng(20).integers(100, 200, M), 21)
     m = DevMatrix.of(w)
-    plan = m.plan(None)
+    plan = m.plan(None, static_matrix=True)
     info = plan.info
     log("auto slabs, mid x", info["x_slabs"], info["merge_reduce"], info["slab_segments"])
     assert info["x_slabs"] == 1, info
@@ -172,7 +177,7 @@ def test_auto_slabs_for_mid_x_and_long_rows():
     plan.destroy()
     M = 500_000
     w = synth.random_csr(M, M, np.random.default_rng(22).integers(5, 16, M), 23)
-    plan = DevMatrix.of(w).plan(None)
+    plan = DevMatrix.of(w).plan(None, static_matrix=True)
     assert plan.info["x_slabs"] == 0, plan.info
     plan.destroy()
 
@@ -187,11 +192,11 @@ def test_unsorted_columns():
     for r in np.nonzero(np.diff(w.row_ptr) > 100)[0][:5]:
         a, b = w.row_ptr[r], w.row_ptr[r + 1]
         col[a:b] = rng.permutation(col[a:b])
-    sorted_auto = DevMatrix.of(w).plan(None, strategy="merge")
+    sorted_auto = DevMatrix.of(w).plan(None, strategy="merge", static_matrix=True)
     assert sorted_auto.info["x_slabs"] == 1, sorted_auto.info
     sorted_auto.destroy()
     m = DevMatrix(w.row_ptr, col, w.values, w.M, w.N)
-    auto = m.plan(None, strategy="merge")
+    auto = m.plan(None, strategy="merge", static_matrix=True)
     info = auto.info
     assert info["x_slabs"] == 0 and info["plan_allocs"] == 1, info
     y = run(auto, w.x, 1.0, 0.0)
