@@ -325,6 +325,34 @@ def slab_sweep(reps: int = 15):
     print(json.dumps({"slab_sweep": rows}), flush=True)
 
 
+def read_sweep(reps: int = 10):
+    """The streaming-read ceiling against buffer size (the library's read
+    probe, each wavefront reading 4 KiB once, over 64 MiB .. 8 GiB) and a
+    plain device copy (read + write) at three sizes; flushed and event-timed
+    like the steps. One JSON line: the ceiling a kernel of a given size can
+    reach, e.g. the 320 MiB of the laplacian workload."""
+    import torch
+    import load_balanced_csr_amd as lb
+    dev = torch.device("cuda:0")
+    flush = CacheFlush(torch, dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    rows = []
+    for mib in (64, 128, 256, 320, 512, 1024, 2048, 8192):
+        buf = torch.ones(mib << 18, dtype=torch.int32, device=dev)
+        ms = timed_median(torch, flush, reps, lambda: lb.spmv_read_probe(buf, sink))
+        rows.append({"read_MiB": mib, "us": round(ms * 1e3, 2),
+                     "GBps": round(buf.numel() * 4 / ms / 1e6, 1)})
+        del buf
+    for mib in (32, 160, 320):
+        a = torch.ones(mib << 18, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        ms = timed_median(torch, flush, reps, lambda: b.copy_(a))
+        rows.append({"copy_MiB": mib, "us": round(ms * 1e3, 2),
+                     "GBps_read_plus_write": round(2 * a.numel() * 4 / ms / 1e6, 1)})
+        del a, b
+    print(json.dumps({"read_sweep": rows}), flush=True)
+
+
 def calibrate_copy(mib: int, steps: int):
     """A plain copy kernel of known size (torch's device copy): reads and
     writes exactly mib MiB per launch. Under rocprofv3 --pmc FETCH_SIZE /
@@ -803,6 +831,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--gather-sweep", action="store_true",
                     help="only run the x-gather probe over the layouts x slabs choose between")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="only run the streaming-read probe over buffer sizes (and a copy)")
     ap.add_argument("--mutable-matrix", action="store_true",
                     help="plan without declaring the matrix static (no plan-time copy of A)")
     ap.add_argument("--slab-sweep", action="store_true",
@@ -811,6 +841,8 @@ def main():
 
     if args.slab_sweep:
         return slab_sweep()
+    if args.read_sweep:
+        return read_sweep()
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, args.steps)
     if args.gather_sweep:
