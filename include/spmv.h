@@ -467,9 +467,12 @@ SPMV_API spmv_status_t spmv_exec_events(spmv_plan_t plan, const void* x, void* y
  *    (The tiles run when X and Y are 16-byte aligned and ldx, ldy and k
  *    are whole 16-byte lanes; otherwise the merge-path walk takes every
  *    row. Results differ by rounding order only.)
- * k = 0 or M = 0 does nothing. k > 64 runs in column blocks of 64.
+ * k = 0 or M = 0 does nothing. k > 64 runs in column blocks of 64. k = 1
+ * with ldx = ldy = 1 is an SpMV and runs as spmv_exec (the plan's strategy,
+ * tiles and x slabs; the workspace is then not touched).
  *
- * Uses the plan's merge-path partitions whatever its SpMV strategy.
+ * Otherwise uses the plan's merge-path partitions whatever its SpMV
+ * strategy.
  * Asynchronous like spmv_exec (no allocation, no synchronisation);
  * bitwise reproducible for a fixed plan and k; the plan's carry-row array
  * is shared with spmv_exec, so one plan must not run either call

@@ -641,6 +641,12 @@ spmv_status_t spmv_exec_multi_events(spmv_plan_t p, int64_t k, const void* X, in
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SPMV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
+  // one contiguous column is an SpMV: run it as one, with every schedule
+  // the plan has for that (stream or walk, tiles, x slabs)
+  if (k == 1 && ldx == 1 && ldy == 1)
+    return p->dtype == SPMV_F32
+               ? exec_typed<float>(p, X, Y, alpha, beta, stream, ev_begin, ev_end)
+               : exec_typed<double>(p, X, Y, alpha, beta, stream, ev_begin, ev_end);
   return p->dtype == SPMV_F32
              ? exec_multi_typed<float>(p, k, X, ldx, Y, ldy, alpha, beta, workspace, stream,
                                        ev_begin, ev_end)

@@ -322,3 +322,26 @@ def test_slabs_in_the_other_input_forms():
         ok, worst, idx = oracle.within_tolerance(y, ref, scale, 0.75, -0.5, y0)
         assert ok, (kind, "over slabs", idx, worst)
         p.destroy()
+
+
+def test_spmm_with_one_contiguous_column_is_the_spmv():
+    """exec_multi with k = 1 and unit strides runs as spmv_exec, so on a
+    slab plan it is bitwise the SpMV over the slab copy; a strided column
+    (ldx = 3) takes the SpMM kernels and stays within the bound."""
+    w = CASES["powerlaw"]()
+    m = DevMatrix.of(w)
+    plan = _slab_plan(m)
+    assert plan.info["x_slabs"] == 1
+    y = run(plan, w.x, 1.0, 0.0)
+    Y = torch.full((w.M, 1), float("nan"), device="cuda")
+    plan.exec_multi(dev(w.x).view(w.N, 1), Y, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy()[:, 0].view(np.uint8), y.view(np.uint8))
+    Xb = torch.full((w.N, 3), float("nan"), device="cuda")
+    Xb[:, 0] = dev(w.x)
+    Y2 = torch.full((w.M, 1), float("nan"), device="cuda")
+    plan.exec_multi(Xb[:, :1], Y2, 1.0, 0.0)
+    torch.cuda.synchronize()
+    check(Y2.cpu().numpy()[:, 0].copy(), w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None,
+          "strided column")
+    plan.destroy()
