@@ -449,10 +449,14 @@ def run_spmm(args, w, torch, lb, dev):
     kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
     for e in kb + ke:
         hip.destroy(e)
-    deterministic = None
-    if w.beta == 0.0:
-        deterministic = bool(np.array_equal(Y.cpu().numpy().view(np.uint8),
-                                            Y_first.view(np.uint8)))
+    # every call must reproduce the first one bit for bit (beta != 0: one
+    # more call from Y0)
+    if w.beta != 0.0:
+        Y.copy_(Y0)
+        step()
+        torch.cuda.synchronize()
+    deterministic = bool(np.array_equal(Y.cpu().numpy().view(np.uint8),
+                                        Y_first.view(np.uint8)))
     mean_ms = statistics.fmean(ms)
     mean_kern = statistics.fmean(kern_ms)
     Bc = spmm_bytes(w, k)
@@ -683,9 +687,15 @@ def spmv_leg(args, w, torch, lb, dev, flush, K, W, cpu_seconds, headline):
     kern_ms = [hip.elapsed_ms(kb[i], ke[i]) for i in range(K)]
     for e in kb + ke:
         hip.destroy(e)
-    # beta = 0: every call must reproduce the first one bit for bit
-    deterministic = None
+    # every call must reproduce the first one bit for bit: beta = 0, the
+    # last step's y; beta != 0 (y accumulates), one more call from y0
     if w.beta == 0.0:
+        deterministic = bool(np.array_equal(y.cpu().numpy().view(np.uint8),
+                                            y_first.view(np.uint8)))
+    else:
+        y.copy_(y0)
+        plan(x, y, w.alpha, w.beta)
+        torch.cuda.synchronize()
         deterministic = bool(np.array_equal(y.cpu().numpy().view(np.uint8),
                                             y_first.view(np.uint8)))
     # secondary figure: warm steps (no flush), events around each exec
