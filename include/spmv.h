@@ -53,6 +53,8 @@
  *   SPMV_LOG=1                         one line per plan on stderr
  *   SPMV_TEST_FAIL_ALLOC=1             make the workspace allocation fail
  *                                      (tests of the error path)
+ *   SPMV_TEST_FAIL_ALLOC=2             make the x-slab copy's allocation
+ *                                      fail (the plan is made without it)
  */
 #ifndef SPMV_H_
 #define SPMV_H_

@@ -718,6 +718,8 @@ spmv_status_t build_slabs(spmv_plan_st* p, int64_t n_seg, int64_t n_chunks, hipS
   const size_t o_rb = take(sizeof(int32_t) * 2 * (P + 1));
   const size_t o_crow = take(sizeof(int32_t) * P);
   const size_t o_cval = take(vs * P);
+  // a failed allocation leaves the plan without slabs (it stays valid)
+  if (env_int("SPMV_TEST_FAIL_ALLOC", 0) == 2) return SPMV_SUCCESS;
   void* mem = nullptr;
   hipError_t err = hipMalloc(&mem, off);
   if (err != hipSuccess) {
@@ -893,7 +895,7 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   const size_t o_rowptr = src.coo ? take(sizeof(int32_t) * (M + 1)) : 0;
   const size_t o_extra = src.extra_bytes ? take(src.extra_bytes) : 0;
   p->ws_bytes = off;
-  if (env_int("SPMV_TEST_FAIL_ALLOC", 0)) {
+  if (env_int("SPMV_TEST_FAIL_ALLOC", 0) == 1) {
     delete p;
     return fail(SPMV_ERR_ALLOC, "workspace allocation failed (forced by SPMV_TEST_FAIL_ALLOC)");
   }

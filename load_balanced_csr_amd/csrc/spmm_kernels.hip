@@ -543,10 +543,6 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
 // The end quad of entries [., s1), (s1 + 3) / 4, and whether entry 4q + e
 // lies in [s0, s1), in unsigned arithmetic (4q + e may pass 2^31 - 1).
 __device__ __forceinline__ int quad_end(int32_t s1) { return (int)(((uint32_t)s1 + 3u) >> 2); }
-__device__ __forceinline__ bool in_segment_u(int q, int e, int32_t s0, int32_t s1) {
-  const uint32_t k = 4u * (uint32_t)q + (uint32_t)e;
-  return k >= (uint32_t)s0 && k < (uint32_t)s1;
-}
 
 // The 16-byte quad (columns or values) of the partner lane (this lane xor
 // 1): one DPP move per word.
@@ -571,7 +567,7 @@ __device__ __forceinline__ Quad<V> quad_of_partner(const Quad<V>& v) {
 // An entry outside the segment reads the zero row past the block (row
 // zrow) and its value is taken as 0, so its FMAs add exactly 0 whatever X
 // and the values hold elsewhere.
-template <typename V, int VE>
+template <typename V, int VE, int K>
 __device__ __forceinline__ void tile_quad_products(Vec<V, VE>& acc, const i32x4& c,
                                                    const Quad<V>& v, int q, int32_t s0,
                                                    int32_t s1, const V* xs,
@@ -579,12 +575,16 @@ __device__ __forceinline__ void tile_quad_products(Vec<V, VE>& acc, const i32x4&
                                                    int clen, int zrow, int lcol) {
   bool in[4], out = false;
   Vec<V, VE> xv[4];
+  // entry 4q + e is in [s0, s1) when 4q + e - s0 < s1 - s0, unsigned (4q
+  // stays below 2^32: q is at most one segment's quads past the other's end)
+  const uint32_t d = 4u * (uint32_t)q - (uint32_t)s0, len = (uint32_t)(s1 - s0);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    in[e] = in_segment_u(q, e, s0, s1);
+    in[e] = d + (uint32_t)e < len;
     const unsigned lc = (unsigned)((int64_t)c[e] - c0);
     const bool inb = lc < (unsigned)clen;
-    xv[e] = vec_load<V, VE>(xs + (int64_t)(in[e] && inb ? lc : (unsigned)zrow) * t.k + lcol);
+    // X rows of K values in LDS: a compile-time row stride
+    xv[e] = vec_load<V, VE>(xs + (in[e] && inb ? lc : (unsigned)zrow) * (unsigned)K + lcol);
     out = out || (in[e] && !inb);
   }
   if (__builtin_amdgcn_ballot_w64(out) != 0) {
@@ -720,12 +720,12 @@ void spmm_tile_kernel(const SpmmTileArgs<V> t) {
       }
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
-        tile_quad_products<V, VE>(acc[j], cq[j], vq[j], qb0[j] + hl, s0[j], s1[j], xs, t, c0,
-                                  clen, zrow, lcol);
+        tile_quad_products<V, VE, KL * VE>(acc[j], cq[j], vq[j], qb0[j] + hl, s0[j], s1[j], xs,
+                                           t, c0, clen, zrow, lcol);
         if (KL == 2)
-          tile_quad_products<V, VE>(acc[j], quad_of_partner(cq[j]), quad_of_partner(vq[j]),
-                                    qb0[j] + (hl ^ 1), s0[j], s1[j], xs, t, c0, clen, zrow,
-                                    lcol);
+          tile_quad_products<V, VE, KL * VE>(acc[j], quad_of_partner(cq[j]),
+                                             quad_of_partner(vq[j]), qb0[j] + (hl ^ 1), s0[j],
+                                             s1[j], xs, t, c0, clen, zrow, lcol);
       }
     }
     // the half's slots meet (offsets below HL keep each half apart)
@@ -921,6 +921,8 @@ hipError_t launch_spmm_tiles_w(const SpmmTileArgs<V>& t, hipStream_t s) {
   if (tiles > 0x7fffffffll) return hipErrorInvalidValue;
   constexpr int VE = 16 / (int)sizeof(V);
   const int lanes = t.k / VE;   // k is a multiple of VE (spmm_tile_split)
+  // the kernel takes X rows of exactly KL * VE values
+  if (t.k % VE != 0 || lanes < 1 || lanes > 2) return hipErrorInvalidValue;
   // the block's X rows and one zero row (just past 64 KiB at the widest)
   const size_t lds = ((size_t)t.bck + 1) * t.k * sizeof(V);
   const dim3 g((unsigned)tiles), b(W * kWave);

@@ -90,6 +90,29 @@ def test_tiles_take_precedence():
     plan.destroy()
 
 
+def test_failed_slab_allocation_leaves_a_plain_plan(monkeypatch):
+    """When the slab copy cannot be allocated the plan is made without it:
+    one allocation, no slabs, and the result of the plain walk, bitwise."""
+    w = CASES["wide_x"]()
+    m = DevMatrix.of(w)
+    monkeypatch.setenv("SPMV_TEST_FAIL_ALLOC", "2")
+    plan = _slab_plan(m)
+    monkeypatch.delenv("SPMV_TEST_FAIL_ALLOC")
+    info = plan.info
+    assert info["x_slabs"] == 0 and info["slab_segments"] == 0, info
+    assert info["plan_allocs"] == 1 and info["plan_syncs"] == 1, info
+    plain = m.plan(None, strategy="merge", x_slabs="off")
+    for key in ("items_per_wave", "n_partitions", "merge_reduce", "dispatch_order"):
+        assert plain.info[key] == info[key], key
+    log("slabs", "failed allocation", info["items_per_wave"], info["n_partitions"])
+    y = run(plan, w.x, 1.0, 0.0)
+    check(y, w.row_ptr, w.col_idx, w.values, w.x, 1.0, 0.0, None, "no slab allocation")
+    yp = run(plain, w.x, 1.0, 0.0)
+    assert np.array_equal(y.view(np.uint8), yp.view(np.uint8))
+    plan.destroy()
+    plain.destroy()
+
+
 def test_slab_segment_count():
     """A row has one segment per slab its columns reach: the count the plan
     reports equals the count from the columns (slab of column c: 8c // N)."""
