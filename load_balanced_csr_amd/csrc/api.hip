@@ -131,6 +131,7 @@ struct spmv_plan_st {
   int32_t tile_nb;
   int32_t n_dispatch;
   const int32_t* tile_list;
+  const int32_t* tile_skip;   // per partition: 1 where the walk skips it (in win_span's room)
   const int32_t* tile_mask_end;
   const int32_t* tile_mask_start;
   const int32_t* tile_rows;
@@ -437,8 +438,8 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
       err = launch_merge<V>(a, p->ipt, stream, ev0, ev1);
     } else {
       // one grid for the walk over the partitions the tiles leave and the
-      // tiles (ev0 / ev1 bracket it), the walk's fix-up, then the reduction
-      // that adds each tile row's block partials into y
+      // tiles (ev0 / ev1 bracket it), then one for the walk's fix-up and the
+      // reduction that adds each tile row's block partials into y
       TileArgs<V> t;
       std::memset(&t, 0, sizeof t);
       t.rows = p->tile_rows;
@@ -448,6 +449,7 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
       t.x = static_cast<const V*>(x);
       t.y = static_cast<V*>(y);
       t.partial = static_cast<V*>(p->tile_partial);
+      t.skip = p->tile_skip;
       t.alpha = (V)alpha;
       t.n_rows = p->n_tile_rows;
       t.nb = p->tile_nb;
@@ -456,7 +458,6 @@ spmv_status_t exec_typed(spmv_plan_t p, const void* x, void* y, double alpha, do
       t.nnz = (int32_t)p->nnz;
       t.x_aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
       err = launch_merge<V>(a, p->ipt, stream, ev0, ev1, &t);
-      if (err == hipSuccess) err = launch_tile_reduce<V>(t, stream);
     }
   } else {
     BinnedArgs<V> a;
@@ -935,6 +936,7 @@ spmv_status_t plan_build(spmv_plan_t* out, const PlanSource& src,
   tp.mask_start = reinterpret_cast<int32_t*>(base + o_tmstart);
   tp.scan_temp = base + o_sort;
   p->tile_rows = tp.rows;
+  p->tile_skip = tp.skip;
   p->tile_list = tp.list;
   p->tile_mask_end = tp.mask_end;
   p->tile_mask_start = tp.mask_start;

@@ -123,6 +123,7 @@ struct TileArgs {
   const V* x;
   V* y;
   V* partial;             // n_rows x nb
+  const int32_t* skip;    // per partition: 1 where the walk skips it (P entries)
   V alpha;
   int32_t n_rows;
   int32_t nb;
@@ -131,8 +132,6 @@ struct TileArgs {
   int32_t nnz;
   int32_t x_aligned;      // x is 16-byte aligned (direct-to-LDS staging)
 };
-template <typename V>
-hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s);
 
 // Error bits of stats[kStatError].
 constexpr int64_t kErrRowPtr = 1;     // row_ptr is not a CSR row pointer array
@@ -334,7 +333,8 @@ hipError_t launch_stream_probe(const int32_t* row_ptr, const int32_t* col_idx, c
 
 // The walk or stream kernel (with tiles, for plans that have long-row
 // tiles: the walk over the partitions they leave and the tiles, one grid),
-// then the walk's carry fix-up. ev0 / ev1 (may be null) are recorded by the
+// then the walk's carry fix-up (with tiles, in one grid with the tiles'
+// reduction into y). ev0 / ev1 (may be null) are recorded by the
 // main kernel's dispatch at its start and end.
 template <typename V>
 hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_t ev0,

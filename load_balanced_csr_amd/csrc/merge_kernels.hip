@@ -502,24 +502,41 @@ __global__ __launch_bounds__(WPB * kWave, stream_min_waves(sizeof(V), IPT, WK > 
 // past its 64 partitions, keeps reading, eight windows of 64 per step, until
 // the step where the key changes. Every lane of the wave stays active up to
 // the scans (the early return is wave-uniform).
-template <typename V>
-__global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
-    const int32_t* __restrict__ carry_row, const V* __restrict__ carry_val, int32_t P,
-    int32_t M, V* __restrict__ y, V alpha) {
+// The row a partition's carry belongs to. On a plan with long-row tiles
+// (skip: 1 for the partitions the walk skips), the carries of a tile row --
+// those of its interior partitions, which the walk skips, and of the
+// partition just before them, whose open row it is -- are all 0 and are
+// keyed past the last row (M), so no fix-up writes a tile row's y: its
+// tiles' reduction does, in the same launch. The skip flags decide, not the
+// stored keys, which a multi-vector product without tiles rewrites.
+template <bool TILED>
+__device__ __forceinline__ int carry_key(const int32_t* __restrict__ carry_row,
+                                         const int32_t* __restrict__ skip, int64_t p,
+                                         int32_t P, int32_t M) {
+  if (TILED && (skip[p] != 0 || (p + 1 < P && skip[p + 1] != 0))) return M;
+  return carry_row[p];
+}
+
+template <typename V, bool TILED>
+__device__ __forceinline__ void fixup_chunks(const int32_t* __restrict__ carry_row,
+                                             const int32_t* __restrict__ skip,
+                                             const V* __restrict__ carry_val, int32_t P,
+                                             int32_t M, V* __restrict__ y, V alpha, int blk) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t base = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kWave;
+  const int64_t base = ((int64_t)blk * kWavesPerBlock + wave) * kWave;
   if (base >= P) return;
   const int64_t p = base + lane;
-  const int key = p < P ? carry_row[p] : INT_MAX;
+  const int key = p < P ? carry_key<TILED>(carry_row, skip, p, P, M) : INT_MAX;
   const V v = p < P ? carry_val[p] : V(0);
   const V s = wave_segscan_keys(v, key);
 
   // the key after this lane's (the next chunk's first for lane 63)
-  const int next_key = lane_next(key, base + kWave < P ? carry_row[base + kWave] : INT_MAX - 1);
+  const int next_key = lane_next(
+      key, base + kWave < P ? carry_key<TILED>(carry_row, skip, base + kWave, P, M) : INT_MAX - 1);
   // wave-uniform: the chunk's first key and the key before the chunk
   const int key0 = __builtin_amdgcn_readfirstlane(key);
-  const int prev0 = base > 0 ? carry_row[base - 1] : -1;
+  const int prev0 = base > 0 ? carry_key<TILED>(carry_row, skip, base - 1, P, M) : -1;
   // a segment is owned here unless it starts at lane 0 and continues from
   // the previous chunk
   const bool owned = !(key == key0 && prev0 == key0);
@@ -539,7 +556,7 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
 #pragma unroll
       for (int u = 0; u < kFixupWindows; ++u) {
         const int64_t pp = q + kWave * u + lane;
-        kq[u] = pp < P ? carry_row[pp] : -1;
+        kq[u] = pp < P ? carry_key<TILED>(carry_row, skip, pp, P, M) : -1;
       }
       V w[kFixupWindows];
 #pragma unroll
@@ -552,6 +569,38 @@ __global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
     // lane 63 holds both the wave's total and the chunk's part of the row
     extra = wave_sum_to_last(extra);
     if (lane == kWave - 1) y[key63] += alpha * (s + extra);
+  }
+}
+
+template <typename V>
+__global__ __launch_bounds__(kBlock) void merge_fixup_kernel(
+    const int32_t* __restrict__ carry_row, const V* __restrict__ carry_val, int32_t P,
+    int32_t M, V* __restrict__ y, V alpha) {
+  fixup_chunks<V, false>(carry_row, nullptr, carry_val, P, M, y, alpha, (int)blockIdx.x);
+}
+
+// The fix-up and, on a plan with long-row tiles, the tiles' reduction in
+// one launch: blocks [0, fix_blocks) take the carries as above (tile rows'
+// keyed past the last row), the others one wave per tile row, which adds
+// alpha * (the row's block partials, summed in a fixed order) to its y. So
+// the two parts write different rows.
+template <typename V>
+__global__ __launch_bounds__(kBlock) void fixup_tile_reduce_kernel(
+    const int32_t* __restrict__ carry_row, const V* __restrict__ carry_val, int32_t P,
+    int32_t M, V* __restrict__ y, V alpha, const TileArgs<V> t, int fix_blocks) {
+  if ((int)blockIdx.x < fix_blocks) {   // workgroup-uniform
+    fixup_chunks<V, true>(carry_row, t.skip, carry_val, P, M, y, alpha, (int)blockIdx.x);
+    return;
+  }
+  const int64_t i = ((int64_t)(blockIdx.x - fix_blocks) * kBlock + threadIdx.x) / kWave;
+  if (i >= t.n_rows) return;   // wave-uniform
+  const int lane = lane_id();
+  V acc = V(0);
+  for (int b = lane; b < t.nb; b += kWave) acc += t.partial[i * t.nb + b];
+  acc = wave_sum_to_last(acc);
+  if (lane == kWave - 1) {
+    const int32_t r = t.rows[kTileRowInts * i];
+    t.y[r] += t.alpha * acc;
   }
 }
 
@@ -608,10 +657,18 @@ hipError_t launch_merge(const MergeArgs<V>& a, int ipt, hipStream_t s, hipEvent_
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  if (a.P > 1 && !a.stream) {
-    const int64_t chunks = ((int64_t)a.P + kWave - 1) / kWave;
-    const int blocks = (int)((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((merge_fixup_kernel<V>), dim3(blocks), dim3(kBlock), 0, s,
+  const int64_t chunks = ((int64_t)a.P + kWave - 1) / kWave;
+  const int fix_blocks =
+      a.P > 1 && !a.stream ? (int)((chunks + kWavesPerBlock - 1) / kWavesPerBlock) : 0;
+  const int64_t red_blocks =
+      tiles && tiles->n_rows > 0 ? ((int64_t)tiles->n_rows * kWave + kBlock - 1) / kBlock : 0;
+  if (red_blocks > 0) {
+    hipLaunchKernelGGL((fixup_tile_reduce_kernel<V>), dim3((unsigned)(fix_blocks + red_blocks)),
+                       dim3(kBlock), 0, s, a.carry_row, a.carry_val, a.P, a.M, a.y, a.alpha,
+                       *tiles, fix_blocks);
+    err = hipGetLastError();
+  } else if (fix_blocks > 0) {
+    hipLaunchKernelGGL((merge_fixup_kernel<V>), dim3(fix_blocks), dim3(kBlock), 0, s,
                        a.carry_row, a.carry_val, a.P, a.M, a.y, a.alpha);
     err = hipGetLastError();
   }

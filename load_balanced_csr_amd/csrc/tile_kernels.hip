@@ -18,9 +18,9 @@
 // partitions (their carries are 0) and leaves the rows' nonzeros in their
 // first and last partition out (masked), so every nonzero is summed exactly
 // once and the result is bitwise reproducible for a fixed plan. The walk
-// and the tiles run in one grid (merge_kernels.hip; the tiles' device code
-// is in tile_exec.hpp); this file builds the plan's tables and holds the
-// reduction.
+// and the tiles run in one grid, the fix-up and the reduction in another
+// (merge_kernels.hip; the tiles' device code is in tile_exec.hpp); this file
+// builds the plan's tables.
 //
 // Correctness never depends on the columns: segments partition each row's
 // interior range whatever col_idx holds, and a column outside the tile's
@@ -240,20 +240,6 @@ __global__ __launch_bounds__(kBlock) void tile_list_kernel(const int32_t* __rest
 
 // y[row] += alpha * (sum of the row's block partials, in block order), one
 // wave per tile row.
-template <typename V>
-__global__ __launch_bounds__(kBlock) void tile_reduce_kernel(const TileArgs<V> a) {
-  const int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
-  if (i >= a.n_rows) return;   // wave-uniform
-  const int lane = lane_id();
-  V acc = V(0);
-  for (int b = lane; b < a.nb; b += kWave) acc += a.partial[i * a.nb + b];
-  acc = wave_sum_to_last(acc);
-  if (lane == kWave - 1) {
-    const int32_t r = a.rows[kTileRowInts * i];
-    a.y[r] += a.alpha * acc;
-  }
-}
-
 unsigned grid_for(int64_t n, int64_t per) {
   return (unsigned)std::max<int64_t>(1, (n + per - 1) / per);
 }
@@ -302,17 +288,5 @@ hipError_t launch_tile_plan(const TilePlan& tp, const int32_t* split_row, const 
                      p_max, stats, tp.list);
   return hipGetLastError();
 }
-
-template <typename V>
-hipError_t launch_tile_reduce(const TileArgs<V>& a, hipStream_t s) {
-  if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(tile_reduce_kernel<V>,
-                     dim3((unsigned)(((int64_t)a.n_rows * kWave + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, s, a);
-  return hipGetLastError();
-}
-
-template hipError_t launch_tile_reduce<float>(const TileArgs<float>&, hipStream_t);
-template hipError_t launch_tile_reduce<double>(const TileArgs<double>&, hipStream_t);
 
 }  // namespace spmv

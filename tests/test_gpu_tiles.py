@@ -156,6 +156,32 @@ def test_spmm_over_a_tiled_plan(case):
     plan.destroy()
 
 
+@pytest.mark.parametrize("case", ["small", "two_groups_last_row"])
+def test_spmv_unchanged_by_an_untiled_spmm(case):
+    """The fix-up and the tiles' reduction share one launch and must write
+    different rows; an SpMM without tiles (X rows of 12 bytes) walks every
+    partition and rewrites the carry rows of the tile rows' interior
+    partitions. The SpMV after it is bitwise the SpMV before it, every
+    time, and right."""
+    w = CASES[case]()
+    m = DevMatrix.of(w)
+    plan = m.plan(None, strategy="merge", merge_reduce="walk")
+    assert plan.info["tile_rows"] > 0
+    y0 = synth.uniform(w.M, 13, synth.S_Y, np.float32)
+    y_before = run(plan, w.x, -1.25, 0.5, y0)
+    check(y_before, w.row_ptr, w.col_idx, w.values, w.x, -1.25, 0.5, y0, "tiles before spmm")
+    rng = np.random.default_rng(3)
+    X = rng.uniform(-1, 1, (w.N, 3)).astype(np.float32)
+    Y = torch.zeros((w.M, 3), dtype=torch.float32, device="cuda")
+    log("tiles", case, "untiled spmm k 3, then spmv")
+    plan.exec_multi(dev(X), Y, 1.0, 0.0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y = run(plan, w.x, -1.25, 0.5, y0)
+        assert np.array_equal(y.view(np.uint8), y_before.view(np.uint8))
+    plan.destroy()
+
+
 def test_spmm_tile_row_groups():
     """The SpMM tile kernel takes 8, 16 or 32 rows a wave (the most that
     still leaves 1024 tiles). The cases above have few tiles (8 a wave); a
