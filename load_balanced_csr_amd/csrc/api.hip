@@ -558,6 +558,7 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
     t.seg = p->tile_seg;
     t.partial = reinterpret_cast<V*>(ws);
     t.carry_vec = static_cast<V*>(workspace);
+    t.skip = p->tile_skip;
     t.col_idx = p->col_idx;
     t.val = static_cast<const V*>(p->values);
     t.X = static_cast<const V*>(X);
@@ -590,11 +591,13 @@ spmv_status_t exec_multi_typed(spmv_plan_t p, int64_t k, const void* X, int64_t 
     a.k = (int32_t)std::min<int64_t>(kWave, k - kb);
     a.X = static_cast<const V*>(X) + kb;
     a.Y = static_cast<V*>(Y) + kb;
-    if ((err = launch_spmm<V>(a, stream, one ? ev0 : nullptr, one ? ev1 : nullptr)) != hipSuccess)
+    if ((err = launch_spmm<V>(a, stream, one ? ev0 : nullptr, one ? ev1 : nullptr, tm == 0)) !=
+        hipSuccess)
       return hip_fail(err, "spmv_exec_multi launch");
   }
-  // after the merge kernel's fix-up, the tiles' partials into Y
-  if (tm > 0 && (err = launch_spmm_tile_reduce<V>(t, stream)) != hipSuccess)
+  // with tiles (k <= 64: one column block, a as launched): the merge
+  // kernel's fix-up and the tiles' partials into Y, one launch
+  if (tm > 0 && (err = launch_spmm_fixup_tile_reduce<V>(a, t, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi tiles");
   if (!one && ev1 && (err = hipEventRecord(ev1, stream)) != hipSuccess)
     return hip_fail(err, "spmv_exec_multi event");

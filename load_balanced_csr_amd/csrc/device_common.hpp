@@ -485,4 +485,19 @@ __device__ __forceinline__ V group_sum(V v) {
   return v;
 }
 
+// The row a partition's carry belongs to. On a plan with long-row tiles
+// (skip: 1 for the partitions the walk skips), the carries of a tile row --
+// those of its interior partitions, which the walk skips, and of the
+// partition just before them, whose open row it is -- are all 0 and are
+// keyed past the last row (M), so no fix-up writes a tile row's y: its
+// tiles' reduction does, in the same launch. The skip flags decide, not the
+// stored keys, which a multi-vector product without tiles rewrites.
+template <bool TILED>
+__device__ __forceinline__ int carry_key(const int32_t* __restrict__ carry_row,
+                                         const int32_t* __restrict__ skip, int64_t p,
+                                         int32_t P, int32_t M) {
+  if (TILED && (skip[p] != 0 || (p + 1 < P && skip[p + 1] != 0))) return M;
+  return carry_row[p];
+}
+
 }  // namespace spmv

@@ -399,6 +399,7 @@ struct SpmmTileArgs {
   V* partial;                 // workspace: n_rows x nb m x k
   V* carry_vec;               // the merge kernel's carries (P x k): the tiles zero
                               // those of the partitions they cover
+  const int32_t* skip;        // plan: per partition, 1 where the walk skips it
   int64_t ldx, ldy;
   V alpha;
   int32_t k;
@@ -416,19 +417,23 @@ int spmm_tile_split(int k, int vbytes, int bc);
 template <typename V>
 size_t spmm_tile_workspace(int n_rows, int nb, int m, int k);
 // The tiles (before the merge kernel, whose fix-up reads the carries they
-// zero), and, after the fix-up, the reduction of the partials into Y.
+// zero), and, after the merge kernel (launched without its fix-up), the
+// fix-up and the reduction of the partials into Y in one launch.
 template <typename V>
 hipError_t launch_spmm_tiles(const SpmmTileArgs<V>& t, hipStream_t s);
 template <typename V>
-hipError_t launch_spmm_tile_reduce(const SpmmTileArgs<V>& t, hipStream_t s);
+hipError_t launch_spmm_fixup_tile_reduce(const SpmmArgs<V>& a, const SpmmTileArgs<V>& t,
+                                         hipStream_t s);
 
 // Staging room per array for partitions of T units (at most T + T/8 rows or
 // nonzeros, plus quad alignment).
 constexpr int spmm_stage_cap(int T) { return T + T / 8 + 8; }
 
-// ev0/ev1 (either may be null) are recorded by the main kernel's dispatch
+// ev0/ev1 (either may be null) are recorded by the main kernel's dispatch;
+// fixup false leaves the carry fix-up to launch_spmm_fixup_tile_reduce
 template <typename V>
-hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                       bool fixup = true);
 
 // ---- group-mapped exec ----------------------------------------------------------------
 constexpr int kGroupRowsPerWave = 256;  // rows (tiles) a group may take, per wavefront

@@ -475,8 +475,9 @@ __global__ __launch_bounds__(PPB * kWave) void spmm_rows_kernel(const SpmmArgs<V
 // plan and k.
 constexpr int kFixupSlices = 8;
 
-template <typename V>
-__global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a) {
+template <typename V, bool TILED>
+__device__ __forceinline__ void spmm_fixup_chunk(const SpmmArgs<V>& a, const int32_t* skip,
+                                                 int blk) {
   const int lane = lane_id();
   const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));   // log2 kl
   const int G = kWave >> lg;
@@ -484,17 +485,17 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   const int c = lane >> (6 - lg);
   const bool col = c < a.k;
   const int64_t base =
-      ((int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) *
-      G;
+      ((int64_t)blk * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) * G;
   if (base >= a.P) return;   // wave-uniform: every lane takes part in the scans below
+  const int32_t* cr = a.carry_row;
   const int64_t p = base + g;
-  const int key = p < a.P ? a.carry_row[p] : INT_MAX;
+  const int key = p < a.P ? carry_key<TILED>(cr, skip, p, a.P, a.M) : INT_MAX;
   V s = p < a.P && col ? a.carry_vec[p * a.k + c] : V(0);
   // wave-uniform: the chunk's first row, the row before the chunk, the row
   // after it
-  const int key0 = a.carry_row[base];
-  const int prev0 = base > 0 ? a.carry_row[base - 1] : -1;
-  const int after = base + G < a.P ? a.carry_row[base + G] : INT_MAX - 1;
+  const int key0 = carry_key<TILED>(cr, skip, base, a.P, a.M);
+  const int prev0 = base > 0 ? carry_key<TILED>(cr, skip, base - 1, a.P, a.M) : -1;
+  const int after = base + G < a.P ? carry_key<TILED>(cr, skip, base + G, a.P, a.M) : INT_MAX - 1;
   // the neighbours' rows, read by DPP moves that every lane executes (a move
   // under a lane mask would read stale values from the masked lanes)
   const int key_prev = lane_prev(key, key);
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   }
   // the last partition's segment, when it is owned here and goes on
   // (wave-uniform)
-  const int r = base + G - 1 < a.P ? a.carry_row[base + G - 1] : INT_MAX;
+  const int r = base + G - 1 < a.P ? carry_key<TILED>(cr, skip, base + G - 1, a.P, a.M) : INT_MAX;
   const bool cont = after == r && !(r == key0 && prev0 == key0);
   if (!cont || r >= a.M) return;
   V extra = V(0);
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
 #pragma unroll
     for (int u = 0; u < kFixupSlices; ++u) {
       const int64_t pp = q + u * G + g;
-      kq[u] = pp < a.P ? a.carry_row[pp] : -1;
+      kq[u] = pp < a.P ? carry_key<TILED>(cr, skip, pp, a.P, a.M) : -1;
     }
     V v[kFixupSlices];
 #pragma unroll
@@ -536,6 +537,11 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a)
   if (g != G - 1 || !col) return;
   V* yp = a.Y + (int64_t)r * a.ldy + c;
   *yp = fma(a.alpha, s + extra, *yp);
+}
+
+template <typename V>
+__global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(const SpmmArgs<V> a) {
+  spmm_fixup_chunk<V, false>(a, nullptr, (int)blockIdx.x);
 }
 
 // ---- long-row tiles (plans with tiles, X rows of at most 32 bytes) --------------
@@ -754,9 +760,8 @@ void spmm_tile_kernel(const SpmmTileArgs<V> t) {
 // covering k) and sub-blocks l / KC, l / KC + 64 / KC, ...; the lanes of a
 // column then meet by a butterfly of cross-lane adds (a fixed order).
 template <typename V>
-__global__ __launch_bounds__(kBlock) void spmm_tile_reduce_kernel(const SpmmTileArgs<V> t,
-                                                                  int kc) {
-  const int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+__device__ __forceinline__ void spmm_tile_reduce_rows(const SpmmTileArgs<V>& t, int kc, int blk) {
+  const int64_t i = ((int64_t)blk * kBlock + threadIdx.x) / kWave;
   if (i >= t.n_rows) return;   // wave-uniform
   const int lane = lane_id();
   const int c = lane % kc, bl = lane / kc, nbl = kWave / kc;
@@ -782,6 +787,20 @@ __global__ __launch_bounds__(kBlock) void spmm_tile_reduce_kernel(const SpmmTile
     V* yp = t.Y + (int64_t)t.rows[kTileRowInts * i] * t.ldy + c;
     *yp += t.alpha * acc;
   }
+}
+
+// The merge kernel's fix-up and the tiles' reduction in one launch: blocks
+// [0, fix_blocks) take the carries (those of tile rows keyed past the last
+// row, so skipped), the others the tile rows. The two write different rows.
+template <typename V>
+__global__ __launch_bounds__(kBlock) void spmm_fixup_tile_reduce_kernel(const SpmmArgs<V> a,
+                                                                        const SpmmTileArgs<V> t,
+                                                                        int fix_blocks, int kc) {
+  if ((int)blockIdx.x < fix_blocks) {   // workgroup-uniform
+    spmm_fixup_chunk<V, true>(a, t.skip, (int)blockIdx.x);
+    return;
+  }
+  spmm_tile_reduce_rows(t, kc, (int)blockIdx.x - fix_blocks);
 }
 
 template <typename V, int KL, int VE, int XA>
@@ -843,7 +862,17 @@ hipError_t launch_ve(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEve
 }  // namespace
 
 template <typename V>
-hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+int spmm_fixup_blocks(const SpmmArgs<V>& a) {
+  if (a.stream || a.P <= 1) return 0;
+  // one wave per 64 / kl partitions
+  const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));
+  const int64_t waves = ((int64_t)a.P + (kWave >> lg) - 1) / (kWave >> lg);
+  return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+template <typename V>
+hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                       bool fixup) {
   if (a.P <= 0 || a.k <= 0) return hipSuccess;
   if (a.k > kWave || a.cap < spmm_stage_cap(a.T)) return hipErrorInvalidValue;
   // 16-byte lanes when every row of X and Y starts 16-byte aligned and k
@@ -861,20 +890,16 @@ hipError_t launch_spmm(const SpmmArgs<V>& a, hipStream_t s, hipEvent_t ev0, hipE
   } else {
     err = launch_ve<V, 1>(a, s, ev0, ev1);
   }
-  if (err != hipSuccess || a.stream || a.P <= 1) return err;
-  // one wave per 64 / kl partitions
-  const int lg = a.k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.k - 1));
-  const int64_t waves = ((int64_t)a.P + (kWave >> lg) - 1) / (kWave >> lg);
-  hipLaunchKernelGGL((spmm_fixup_kernel<V>),
-                     dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
-                     0, s, a);
+  const int fb = spmm_fixup_blocks(a);
+  if (err != hipSuccess || !fixup || fb == 0) return err;
+  hipLaunchKernelGGL((spmm_fixup_kernel<V>), dim3((unsigned)fb), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template hipError_t launch_spmm<float>(const SpmmArgs<float>&, hipStream_t, hipEvent_t,
-                                       hipEvent_t);
+                                       hipEvent_t, bool);
 template hipError_t launch_spmm<double>(const SpmmArgs<double>&, hipStream_t, hipEvent_t,
-                                        hipEvent_t);
+                                        hipEvent_t, bool);
 
 int spmm_tile_split(int k, int vbytes, int bc) {
   const int ve = 16 / vbytes;
@@ -936,14 +961,16 @@ hipError_t launch_spmm_tiles_w(const SpmmTileArgs<V>& t, hipStream_t s) {
 }
 
 template <typename V>
-hipError_t launch_spmm_tile_reduce(const SpmmTileArgs<V>& t, hipStream_t s) {
+hipError_t launch_spmm_fixup_tile_reduce(const SpmmArgs<V>& a, const SpmmTileArgs<V>& t,
+                                         hipStream_t s) {
   if (t.n_rows <= 0 || t.m <= 0) return hipSuccess;
   int kc = 1;
   while (kc < t.k) kc *= 2;
-  if (kc > kWave) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(spmm_tile_reduce_kernel<V>,
-                     dim3((unsigned)(((int64_t)t.n_rows * kWave + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, s, t, kc);
+  if (kc > kWave || a.k != t.k || !t.skip) return hipErrorInvalidValue;
+  const int fb = spmm_fixup_blocks(a);
+  const int64_t rb = ((int64_t)t.n_rows * kWave + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(spmm_fixup_tile_reduce_kernel<V>, dim3((unsigned)(fb + rb)), dim3(kBlock), 0,
+                     s, a, t, fb, kc);
   return hipGetLastError();
 }
 
@@ -951,7 +978,10 @@ template size_t spmm_tile_workspace<float>(int, int, int, int);
 template size_t spmm_tile_workspace<double>(int, int, int, int);
 template hipError_t launch_spmm_tiles<float>(const SpmmTileArgs<float>&, hipStream_t);
 template hipError_t launch_spmm_tiles<double>(const SpmmTileArgs<double>&, hipStream_t);
-template hipError_t launch_spmm_tile_reduce<float>(const SpmmTileArgs<float>&, hipStream_t);
-template hipError_t launch_spmm_tile_reduce<double>(const SpmmTileArgs<double>&, hipStream_t);
+template hipError_t launch_spmm_fixup_tile_reduce<float>(const SpmmArgs<float>&,
+                                                         const SpmmTileArgs<float>&, hipStream_t);
+template hipError_t launch_spmm_fixup_tile_reduce<double>(const SpmmArgs<double>&,
+                                                          const SpmmTileArgs<double>&,
+                                                          hipStream_t);
 
 }  // namespace spmv
