@@ -25,8 +25,8 @@ def _spmv_cases():
                                           dispatch_order="partition")),
         "merge_walk_column": (bi, dict(strategy="merge", merge_reduce="walk",
                                        dispatch_order="column")),
-        # long rows in column-blocked tiles: the walk+tile grid, the fix-up
-        # and the tile reduction, three launches per exec
+        # long rows in column-blocked tiles: the walk+tile grid, then the
+        # fix-up and the tile reduction in one grid, two launches per exec
         "merge_walk_tiles": (bi, dict(strategy="merge", merge_reduce="walk")),
         # x slabs: the walk over the slab-major copy, its fix-up and the
         # combine, three launches per exec
@@ -94,7 +94,8 @@ def test_spmv_graph_replays(case):
 @pytest.mark.parametrize("case", ["stream", "walk", "walk_tiles_k8"])
 def test_spmm_graph_replays(case):
     # the walk cases run the SpMM long-row tiles too (X rows of 16 and 32
-    # bytes): tiles, merge walk, fix-up and tile reduction, four launches
+    # bytes): tiles, merge walk, then fix-up and tile reduction in one grid,
+    # three launches
     if case == "stream":
         w = synth.laplacian(n=150)
         opts = dict(strategy="merge")
